@@ -1,0 +1,222 @@
+"""ctypes wrapper of the CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The product path (the HIP library and its binding) never
+imports it.  Inputs and outputs are numpy arrays on the host.
+
+Citations of the operations wrapped here are in kvq_oracle.h.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+INT2, INT4, FP16 = 0, 1, 2
+F32, BF16, F16 = 0, 1, 2
+PAGES, SLOTS = 0, 1
+PAGE = 16
+HEAD_DIM = 128
+BLOCK_BYTES = {INT2: 1536, INT4: 2560, FP16: 8192}
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build  # noqa: WPS433 (build on first use)
+            _build.build()
+        _lib = ctypes.CDLL(LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("heads_per_page", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32 * 3),
+                ("pool", ctypes.c_void_p * 3),
+                ("sentinel_slot", ctypes.c_int32)]
+
+
+class _Range(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_int32), ("head", ctypes.c_int32),
+                ("cls", ctypes.c_int32), ("tok_begin", ctypes.c_int32),
+                ("tok_end", ctypes.c_int32)]
+
+
+RANGE_DTYPE = np.dtype([("table", "<i4"), ("head", "<i4"), ("cls", "<i4"),
+                        ("tok_begin", "<i4"), ("tok_end", "<i4")])
+
+
+def _declare(L):
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    L.orc_f16_down.argtypes = [ctypes.c_float]
+    L.orc_f16_down.restype = ctypes.c_uint16
+    L.orc_f16_up.argtypes = [ctypes.c_float]
+    L.orc_f16_up.restype = ctypes.c_uint16
+    L.orc_f16_nearest.argtypes = [ctypes.c_float]
+    L.orc_f16_nearest.restype = ctypes.c_uint16
+    L.orc_f16_value.argtypes = [ctypes.c_uint16]
+    L.orc_f16_value.restype = ctypes.c_double
+    L.orc_block_bytes.argtypes = [i32]
+    L.orc_block_bytes.restype = i64
+    L.orc_quantize.argtypes = [P, i32, i64, i32, P, P, P]
+    L.orc_quantize.restype = None
+    L.orc_route.argtypes = [P, i32, P, P, P, P]
+    L.orc_append.argtypes = [P, P, P, i32, i64, i64, i32, P, P, i32, P, P, i32, P, P]
+    L.orc_reorder.argtypes = [P, P, i32, i32, P, P]
+    L.orc_token.argtypes = [P, i32, i32, i32, P, P]
+    L.orc_attend.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, P, i32, P, P, i32]
+    L.orc_attend_ranges.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, P, i32, P, P, i32]
+    L.orc_merge.argtypes = [P, P, P, i32, i32, i32, P, P]
+    for name in ("orc_route", "orc_append", "orc_reorder", "orc_token", "orc_attend",
+                 "orc_attend_ranges", "orc_merge"):
+        getattr(L, name).restype = ctypes.c_int
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+def _c_array(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --- fp16 helpers ------------------------------------------------------------
+
+def f16_down(x: float) -> int:
+    return int(lib().orc_f16_down(float(x)))
+
+
+def f16_up(x: float) -> int:
+    return int(lib().orc_f16_up(float(x)))
+
+
+def f16_nearest(x: float) -> int:
+    return int(lib().orc_f16_nearest(float(x)))
+
+
+def f16_value(bits: int) -> float:
+    return float(lib().orc_f16_value(int(bits)))
+
+
+def quantize(x, bits: int):
+    """Quantize one group; returns (codes uint8[n], scale bits, zero bits)."""
+    x = _c_array(x, np.float32)
+    codes = np.zeros(x.shape[0], np.uint8)
+    s = ctypes.c_uint16()
+    z = ctypes.c_uint16()
+    lib().orc_quantize(_ptr(x), x.shape[0], 1, bits, _ptr(codes), ctypes.byref(s), ctypes.byref(z))
+    return codes, int(s.value), int(z.value)
+
+
+def route(flags):
+    """Route per-token flags (0 INT2, 1 INT4, 2 FP16); returns (cls, n2_groups, n4, n16)."""
+    flags = _c_array(flags, np.uint8)
+    cls = np.zeros(flags.shape[0], np.uint8)
+    n2, n4, n16 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().orc_route(_ptr(flags), flags.shape[0], _ptr(cls), ctypes.byref(n2),
+                           ctypes.byref(n4), ctypes.byref(n16)), "route")
+    return cls, n2.value, n4.value, n16.value
+
+
+def merge(part_out, part_lse, offsets, batch, hq, hkv):
+    part_out = _c_array(part_out, np.float64)
+    part_lse = _c_array(part_lse, np.float64)
+    offsets = _c_array(offsets, np.int32)
+    out = np.zeros((batch, hq, HEAD_DIM), np.float64)
+    lse = np.zeros((batch, hq), np.float64)
+    _check(lib().orc_merge(_ptr(part_out), _ptr(part_lse), _ptr(offsets), batch, hq, hkv,
+                           _ptr(out), _ptr(lse)), "merge")
+    return out, lse
+
+
+class Cache:
+    """Host-side pools laid out exactly as the GPU pools (one per class)."""
+
+    def __init__(self, heads_per_page, n_int2, n_int4, n_fp16, sentinel_slot=-1):
+        self.heads_per_page = int(heads_per_page)
+        self.n_pages = (int(n_int2), int(n_int4), int(n_fp16))
+        self.pools = [np.zeros(max(1, n * self.heads_per_page * BLOCK_BYTES[c]), np.uint8)
+                      for c, n in zip((INT2, INT4, FP16), self.n_pages)]
+        self.sentinel_slot = int(sentinel_slot)
+
+    def _struct(self):
+        c = _Cache()
+        c.heads_per_page = self.heads_per_page
+        for i in range(3):
+            c.n_pages[i] = self.n_pages[i]
+            c.pool[i] = self.pools[i].ctypes.data
+        c.sentinel_slot = self.sentinel_slot
+        return c
+
+    def pool_bytes(self, cls):
+        n = self.n_pages[cls] * self.heads_per_page * BLOCK_BYTES[cls]
+        return self.pools[cls][:n]
+
+    def append(self, k, v, dtype, row_stride, head_stride, rows4=(), slots4=(),
+               rows2=(), pages2=(), rows16=(), slots16=()):
+        """k, v: numpy arrays (float32, or uint16 bit patterns for bf16/f16)."""
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        r4, s4 = _c_array(rows4, np.int32), _c_array(slots4, np.int32)
+        r2, p2 = _c_array(rows2, np.int32), _c_array(pages2, np.int32)
+        r16, s16 = _c_array(rows16, np.int32), _c_array(slots16, np.int32)
+        assert r4.shape == s4.shape and r16.shape == s16.shape and r2.shape[0] == 32 * p2.shape[0]
+        c = self._struct()
+        _check(lib().orc_append(ctypes.byref(c), _ptr(k), _ptr(v), dtype, row_stride, head_stride,
+                                r4.shape[0], _ptr(r4), _ptr(s4), p2.shape[0], _ptr(r2), _ptr(p2),
+                                r16.shape[0], _ptr(r16), _ptr(s16)), "append")
+
+    def reorder(self, tables, n_entries):
+        """In-place stable partition of int32 tables [n_tables, max_entries]; returns counts."""
+        assert tables.dtype == np.int32 and tables.flags.c_contiguous
+        n_entries = _c_array(n_entries, np.int32)
+        counts = np.zeros((tables.shape[0], 3), np.int32)
+        c = self._struct()
+        _check(lib().orc_reorder(ctypes.byref(c), _ptr(tables), tables.shape[0], tables.shape[1],
+                                 _ptr(n_entries), _ptr(counts)), "reorder")
+        return counts
+
+    def token(self, page, off, head):
+        k = np.zeros(HEAD_DIM, np.float64)
+        v = np.zeros(HEAD_DIM, np.float64)
+        c = self._struct()
+        _check(lib().orc_token(ctypes.byref(c), page, off, head, _ptr(k), _ptr(v)), "token")
+        return k, v
+
+    def attend(self, q, batch, hq, hkv, tables, kind, ranges, n_threads=1):
+        q = _c_array(q, np.float32)
+        tables = _c_array(tables, np.int32)
+        ranges = np.ascontiguousarray(ranges, dtype=RANGE_DTYPE)
+        out = np.zeros((batch, hq, HEAD_DIM), np.float64)
+        lse = np.zeros((batch, hq), np.float64)
+        c = self._struct()
+        _check(lib().orc_attend(ctypes.byref(c), _ptr(q), batch, hq, hkv, _ptr(tables),
+                                tables.shape[0], tables.shape[1], kind, _ptr(ranges),
+                                ranges.shape[0], _ptr(out), _ptr(lse), n_threads), "attend")
+        return out, lse
+
+    def attend_ranges(self, q, batch, hq, hkv, tables, kind, ranges, n_threads=1):
+        q = _c_array(q, np.float32)
+        tables = _c_array(tables, np.int32)
+        ranges = np.ascontiguousarray(ranges, dtype=RANGE_DTYPE)
+        g = hq // hkv
+        out = np.zeros((ranges.shape[0], g, HEAD_DIM), np.float64)
+        lse = np.zeros((ranges.shape[0], g), np.float64)
+        c = self._struct()
+        _check(lib().orc_attend_ranges(ctypes.byref(c), _ptr(q), batch, hq, hkv, _ptr(tables),
+                                       tables.shape[0], tables.shape[1], kind, _ptr(ranges),
+                                       ranges.shape[0], _ptr(out), _ptr(lse), n_threads),
+               "attend_ranges")
+        return out, lse

@@ -1,0 +1,410 @@
+"""Seeded synthetic workloads for decode attention over a mixed-precision KV cache.
+
+Shared by the tests, the benchmark and the smoke check, for both the GPU path and
+the CPU oracle.  This module holds none of the method's arithmetic: no
+quantization, no routing, no reorder, no attention and no merge.  It draws random
+numbers, fixes shapes, and does the caller-side page bookkeeping a serving system
+does around the cache (handing out physical pages and slots, recording which table
+entry holds which tokens).
+
+Workload shapes follow the pages' settings: TriAxialKV (mixed INT2/INT4 with G = 32
+groups; Qwen3-8B and Qwen3-VL shapes), HyQuant (INT4 prefix plus FP16 anchors:
+vertical-line tokens, a staging buffer and a W = 128 window) and Tangram/IntentKV
+(ragged per-head budgets, head-group page tables, sentinel dead slots).  Values are
+synthetic: no dataset, suite or model weight is involved.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+INT2, INT4, FP16 = 0, 1, 2          # precision classes (flags use the same numbers)
+PAGE = 16
+GROUP = 32
+HEAD_DIM = 128
+PAGES, SLOTS = 0, 1
+
+RANGE_DTYPE = np.dtype([("table", "<i4"), ("head", "<i4"), ("cls", "<i4"),
+                        ("tok_begin", "<i4"), ("tok_end", "<i4")])
+
+
+# ----------------------------------------------------------------------------
+# random streams
+# ----------------------------------------------------------------------------
+
+def np_rng(seed: int, *stream: int) -> np.random.Generator:
+    """Independent numpy stream for (seed, stream ids)."""
+    return np.random.default_rng([int(seed) & 0xFFFFFFFF, *[int(s) & 0xFFFFFFFF for s in stream]])
+
+
+def torch_gen(seed: int, *stream: int, device="cpu") -> torch.Generator:
+    """Independent torch stream for (seed, stream ids) on a device."""
+    s = int(np_rng(seed, 0x7A11, *stream).integers(0, 2**62))
+    g = torch.Generator(device=device)
+    g.manual_seed(s)
+    return g
+
+
+def randn(shape, seed, *stream, device="cpu", std=1.0) -> torch.Tensor:
+    t = torch.randn(shape, generator=torch_gen(seed, *stream, device=device),
+                    device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t
+
+
+# ----------------------------------------------------------------------------
+# caller-side page bookkeeping
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class AppendLists:
+    """Destination lists of one append call (rows index the k / v row space)."""
+    rows4: List[int] = dataclasses.field(default_factory=list)
+    slots4: List[int] = dataclasses.field(default_factory=list)
+    rows2: List[int] = dataclasses.field(default_factory=list)
+    pages2: List[int] = dataclasses.field(default_factory=list)
+    rows16: List[int] = dataclasses.field(default_factory=list)
+    slots16: List[int] = dataclasses.field(default_factory=list)
+
+    def arrays(self):
+        a = lambda x: np.asarray(x, dtype=np.int32)  # noqa: E731
+        return dict(rows4=a(self.rows4), slots4=a(self.slots4), rows2=a(self.rows2),
+                    pages2=a(self.pages2), rows16=a(self.rows16), slots16=a(self.slots16))
+
+
+class PageAllocator:
+    """Hands out physical pages from shuffled free lists and records every table.
+
+    Page ids use one id space: INT2 [0, n2), INT4 [n2, n2+n4), FP16 after.  INT2
+    pages are handed out as aligned pairs (even, even+1): one 32-token group."""
+
+    def __init__(self, n_pages, heads_per_page, n_tables, max_entries, seed, reserve_int4=0):
+        self.n_pages = tuple(int(n) for n in n_pages)
+        self.heads_per_page = heads_per_page
+        r = np_rng(seed, 0xA110C)
+        n2, n4, n16 = self.n_pages
+        assert n2 % 2 == 0
+        self.free2 = list((r.permutation(n2 // 2) * 2).astype(np.int64))
+        ids4 = np.arange(n2 + reserve_int4, n2 + n4)
+        self.free4 = list(r.permutation(ids4))
+        self.free16 = list(r.permutation(np.arange(n2 + n4, n2 + n4 + n16)))
+        self.reserved4 = list(range(n2, n2 + reserve_int4))
+        self.max_entries = max_entries
+        self.tables = np.full((n_tables, max_entries), -1, dtype=np.int32)
+        self.n_entries = np.zeros(n_tables, dtype=np.int32)
+        self.fill = [[] for _ in range(n_tables)]          # tokens per entry
+        self.entry_cls = [[] for _ in range(n_tables)]
+        self.open = [dict() for _ in range(n_tables)]      # cls -> entry index of open page
+        self.tokens = np.zeros((n_tables, 3), dtype=np.int64)
+
+    def _push(self, t, page, cls, fill):
+        e = int(self.n_entries[t])
+        assert e < self.max_entries, "table capacity exceeded"
+        self.tables[t, e] = page
+        self.n_entries[t] += 1
+        self.fill[t].append(fill)
+        self.entry_cls[t].append(cls)
+        return e
+
+    def place(self, t, classes, rows, lists: AppendLists, new_page=False):
+        """Give every token of one append call (classes already routed) a place.
+
+        classes / rows: per token, in position order.  new_page: start a fresh
+        page for the first INT4 / FP16 token (a new buffer segment)."""
+        classes = np.asarray(classes)
+        rows = np.asarray(rows)
+        if new_page:
+            self.open[t].pop(INT4, None)
+            self.open[t].pop(FP16, None)
+        in_group = 0
+        for c, row in zip(classes.tolist(), rows.tolist()):
+            if c == INT2:
+                if in_group == 0:
+                    p = int(self.free2.pop())
+                    self._push(t, p, INT2, 16)
+                    self._push(t, p + 1, INT2, 16)
+                    lists.pages2.append(p)
+                lists.rows2.append(row)
+                in_group = (in_group + 1) % GROUP
+                self.tokens[t, INT2] += 1
+            else:
+                e = self.open[t].get(c)
+                if e is None or self.fill[t][e] == PAGE:
+                    p = int((self.free4 if c == INT4 else self.free16).pop())
+                    e = self._push(t, p, c, 0)
+                    self.open[t][c] = e
+                slot = int(self.tables[t, e]) * PAGE + self.fill[t][e]
+                self.fill[t][e] += 1
+                self.tokens[t, c] += 1
+                if c == INT4:
+                    lists.rows4.append(row)
+                    lists.slots4.append(slot)
+                else:
+                    lists.rows16.append(row)
+                    lists.slots16.append(slot)
+        assert in_group == 0, "INT2 tokens of an append call must fill whole groups"
+
+    def ranges(self, t, heads):
+        """Token ranges of table t in its current entry order (one class per range)."""
+        out = []
+        start = None
+        cls_run = None
+        for e, (c, f) in enumerate(zip(self.entry_cls[t], self.fill[t])):
+            if start is not None and c == cls_run and prev_full:
+                end = e * PAGE + f
+            else:
+                if start is not None:
+                    out.append((cls_run, start, end))
+                start, cls_run, end = e * PAGE, c, e * PAGE + f
+            prev_full = f == PAGE
+        if start is not None:
+            out.append((cls_run, start, end))
+        return [(t, h, c, b, e) for h in heads for (c, b, e) in out if e > b]
+
+
+def ranges_array(items) -> np.ndarray:
+    return np.array(list(items), dtype=RANGE_DTYPE).reshape(-1)
+
+
+def class_ordered_ranges(t, heads, tokens_per_class):
+    """Ranges of a table whose entries are grouped INT2, INT4, FP16 (in that order)
+    and whose only partially filled page per class is the last one of the class."""
+    out, page0 = [], 0
+    for c in (INT2, INT4, FP16):
+        n = int(tokens_per_class[c])
+        if n:
+            out.append((c, page0 * PAGE, page0 * PAGE + n))
+        page0 += -(-n // PAGE)
+    return [(t, h, c, b, e) for h in heads for (c, b, e) in out]
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    seed: int
+    batch: int
+    hq: int
+    hkv: int
+    heads_per_page: int
+    kind: int                       # PAGES or SLOTS
+    src_dtype: torch.dtype          # dtype of K / V source rows
+    q_dtype: torch.dtype
+    k: torch.Tensor                 # [R, heads_per_page, 128]
+    v: torch.Tensor
+    q: torch.Tensor                 # [batch, hq, 128]
+    n_pages: tuple                  # pages per class
+    alloc: PageAllocator
+    calls: list                     # per append call: (table, flags np.uint8, rows np.int32, new_page)
+    sentinel_slot: int = -1
+    dead_entries: Optional[list] = None  # per table: entry indices redirected to the sentinel
+    head_tokens: Optional[np.ndarray] = None  # [n_tables, heads_per_page] tokens read per head
+    head_budget: Optional[np.ndarray] = None  # [hkv] retained fraction per KV head (ragged tables)
+    note: str = ""
+
+    @property
+    def n_tables(self):
+        return self.alloc.tables.shape[0]
+
+    @property
+    def g(self):
+        return self.hq // self.hkv
+
+
+def _bf16(t):
+    return t.to(torch.bfloat16)
+
+
+def _unit_flags(n_tokens, frac_int2, rng):
+    """Per-token flags from 32-token units, INT2 units a fraction of all, shuffled."""
+    units = n_tokens // GROUP
+    n2 = int(round(frac_int2 * units))
+    u = np.array([INT2] * n2 + [INT4] * (units - n2), dtype=np.uint8)
+    rng.shuffle(u)
+    return np.repeat(u, GROUP)
+
+
+def tiny(seed=0, device="cpu"):
+    """Tiny decode step: batch 1, Hq 4 / Hkv 1, 256 tokens = 6 INT2 groups + 64 INT4
+    tokens in shuffled 32-token units; fp32 K, V, q ~ N(0,1); four K outlier
+    channels x10."""
+    B, hq, hkv, T = 1, 4, 1, 256
+    rng = np_rng(seed, 1)
+    k = randn((T, 1, HEAD_DIM), seed, 2, device=device)
+    v = randn((T, 1, HEAD_DIM), seed, 3, device=device)
+    out_ch = torch.as_tensor(np.sort(rng.choice(HEAD_DIM, 4, replace=False)), device=device)
+    k[:, :, out_ch] *= 10.0
+    q = randn((B, hq, HEAD_DIM), seed, 4, device=device)
+    flags = np.repeat(rng.permutation(np.array([INT2] * 6 + [INT4] * 2, np.uint8)), GROUP)
+    n_pages = (12, 4, 0)
+    alloc = PageAllocator(n_pages, 1, 1, 16, seed)
+    return Workload("tiny", seed, B, hq, hkv, 1, PAGES, torch.float32, torch.float32, k, v, q,
+                    n_pages, alloc, [(0, flags, np.arange(T, dtype=np.int32), False)])
+
+
+def qwen3_8b(seed=2, batch=16, n_tokens=32768, device="cpu", frac_int2=0.7, layer=0):
+    """Qwen3-8B-shaped decode: Hq 32 / Hkv 8 (g = 4), d 128, one page table per request
+    holding all 8 KV heads, 16-token pages.  Per request 70 % INT2 / 30 % INT4 tokens in
+    shuffled runs of 32; bf16 K, V ~ N(0,1) with 1 % of K channels (10 of 1024 head
+    channels) x8; bf16 q."""
+    hq, hkv, H = 32, 8, 8
+    assert n_tokens % GROUP == 0
+    rng = np_rng(seed, 11, layer)
+    flags = [_unit_flags(n_tokens, frac_int2, np_rng(seed, 12, t)) for t in range(batch)]
+    n2 = sum(int((f == INT2).sum()) for f in flags) // PAGE
+    n4 = sum(-(-int((f == INT4).sum()) // PAGE) for f in flags)
+    k = randn((batch * n_tokens, H, HEAD_DIM), seed, 13, layer, device=device)
+    v = randn((batch * n_tokens, H, HEAD_DIM), seed, 14, layer, device=device)
+    n_out = max(1, round(0.01 * H * HEAD_DIM))
+    hc = rng.choice(H * HEAD_DIM, n_out, replace=False)
+    kf = k.view(batch * n_tokens, H * HEAD_DIM)
+    kf[:, torch.as_tensor(np.sort(hc), device=device)] *= 8.0
+    k, v = _bf16(k), _bf16(v)
+    q = _bf16(randn((batch, hq, HEAD_DIM), seed, 15, layer, device=device))
+    max_entries = n_tokens // PAGE
+    alloc = PageAllocator((n2, n4, 0), H, batch, max_entries, seed)
+    calls = [(t, flags[t], np.arange(t * n_tokens, (t + 1) * n_tokens, dtype=np.int32), False)
+             for t in range(batch)]
+    return Workload("qwen3_8b", seed, batch, hq, hkv, H, PAGES, torch.bfloat16, torch.bfloat16,
+                    k, v, q, (n2, n4, 0), alloc, calls,
+                    note=f"{batch}x{n_tokens} tokens, {frac_int2:.0%} INT2 units")
+
+
+def hybrid_anchor(seed=4, batch=32, n_tokens=65536, device="cpu", window=128, staging=64,
+                  vl_ratio=0.05, layer=0):
+    """Hybrid FP16-anchor decode (Llama-3.1-8B shape): Hq 32 / Hkv 8, one table per
+    (request, KV head).  Per head: an INT4 prefix, FP16 vertical-line tokens (top 5 %
+    of the non-window prefix by a Zipf(1.1) column mass over randomly permuted ranks),
+    a 64-token FP16 staging buffer and a W = 128 FP16 window; each anchor segment starts
+    on its own page.  bf16 K, V ~ N(0,1)."""
+    hq, hkv, H = 32, 8, 1
+    n_tables = batch * hkv
+    frozen = n_tokens - staging               # tokens present at the freeze point
+    nonwin = frozen - window
+    n_vl = int(round(vl_ratio * nonwin))
+    n_q = nonwin - n_vl
+    k = _bf16(randn((n_tables * n_tokens, 1, HEAD_DIM), seed, 41, layer, device=device))
+    v = _bf16(randn((n_tables * n_tokens, 1, HEAD_DIM), seed, 42, layer, device=device))
+    q = _bf16(randn((batch, hq, HEAD_DIM), seed, 43, layer, device=device))
+    pg = lambda n: -(-n // PAGE)  # noqa: E731
+    n4 = n_tables * pg(n_q)
+    n16 = n_tables * (pg(n_vl) + pg(staging) + pg(window))
+    max_entries = pg(n_q) + pg(n_vl) + pg(staging) + pg(window)
+    alloc = PageAllocator((0, n4, n16), H, n_tables, max_entries, seed)
+    calls = []
+    ranks_mass = np.arange(1, nonwin + 1, dtype=np.float64) ** -1.1   # Zipf(1.1) by rank
+    for t in range(n_tables):
+        r = np_rng(seed, 44, t)
+        rank_of_pos = r.permutation(nonwin)                # random rank per position
+        mass = ranks_mass[rank_of_pos]
+        vl = np.sort(np.argsort(-mass, kind="stable")[:n_vl])
+        is_vl = np.zeros(nonwin, bool)
+        is_vl[vl] = True
+        base = t * n_tokens
+        pos = np.arange(nonwin)
+        rows_q = (base + pos[~is_vl]).astype(np.int32)
+        rows_vl = (base + pos[is_vl]).astype(np.int32)
+        rows_win = (base + nonwin + np.arange(window)).astype(np.int32)
+        rows_stage = (base + frozen + np.arange(staging)).astype(np.int32)
+        calls.append((t, np.full(n_q, INT4, np.uint8), rows_q, False))
+        calls.append((t, np.full(n_vl, FP16, np.uint8), rows_vl, True))
+        calls.append((t, np.full(staging, FP16, np.uint8), rows_stage, True))
+        calls.append((t, np.full(window, FP16, np.uint8), rows_win, True))
+    return Workload("hybrid_anchor", seed, batch, hq, hkv, H, PAGES, torch.bfloat16,
+                    torch.bfloat16, k, v, q, (0, n4, n16), alloc, calls,
+                    note=f"per head {n_q} INT4 + {n_vl} VL + {staging} staging + {window} window")
+
+
+def ragged_dead(seed=5, batch=64, lo=4096, hi=131072, device="cpu", dead_frac=0.2, layer=0):
+    """Ragged per-head budgets with sentinel dead slots: Hq 32 / Hkv 8, context lengths
+    log-uniform in [lo, hi]; per-KV-head retained fraction r_h = 0.1 + 0.9 h / 7; heads
+    in 4 groups of 2 with one slot-map table per (request, group) of length
+    ceil(max r_h * len); each head reads its first ceil(r_h * len) entries; slots are
+    handed out in shuffled 16-slot pages; 20 % of each table's entries point at the
+    sentinel dead slot.  INT4 per-token."""
+    hq, hkv, H = 32, 8, 2
+    groups = hkv // H
+    rng = np_rng(seed, 51, layer)
+    lens = np.round(np.exp(rng.uniform(math.log(lo), math.log(hi), batch))).astype(np.int64)
+    r_h = 0.1 + 0.9 * np.arange(hkv) / (hkv - 1)
+    n_tables = batch * groups
+    head_tokens = np.zeros((n_tables, H), np.int32)
+    tlen = np.zeros(n_tables, np.int64)
+    for b in range(batch):
+        for gr in range(groups):
+            t = b * groups + gr
+            for h in range(H):
+                head_tokens[t, h] = int(math.ceil(r_h[gr * H + h] * lens[b]))
+            tlen[t] = head_tokens[t].max()
+    pg = lambda n: -(-int(n) // PAGE)  # noqa: E731
+    n4 = 1 + sum(pg(n) for n in tlen)       # page 0 of the INT4 pool holds the sentinel
+    max_entries = int(tlen.max())
+    rows_total = int(tlen.sum()) + 1
+    k = randn((rows_total, H, HEAD_DIM), seed, 52, layer, device=device)
+    v = randn((rows_total, H, HEAD_DIM), seed, 53, layer, device=device)
+    k[0] = -1.0e4                            # sentinel row: K = -1e4, V = 0
+    v[0] = 0.0
+    k, v = _bf16(k), _bf16(v)
+    q = _bf16(randn((batch, hq, HEAD_DIM), seed, 54, layer, device=device))
+    alloc = PageAllocator((0, n4, 0), H, n_tables, max_entries, seed, reserve_int4=1)
+    calls, dead, row = [], [], 1
+    for t in range(n_tables):
+        n = int(tlen[t])
+        calls.append((t, np.full(n, INT4, np.uint8), np.arange(row, row + n, dtype=np.int32), True))
+        row += n
+        dead.append(np.sort(np_rng(seed, 55, t).choice(n, int(round(dead_frac * n)), replace=False)))
+    sentinel = alloc.reserved4[0] * PAGE
+    return Workload("ragged_dead", seed, batch, hq, hkv, H, SLOTS, torch.bfloat16, torch.bfloat16,
+                    k, v, q, (0, n4, 0), alloc, calls, sentinel_slot=sentinel, dead_entries=dead,
+                    head_tokens=head_tokens, head_budget=r_h.astype(np.float32),
+                    note=f"lengths {int(lens.min())}..{int(lens.max())}, {dead_frac:.0%} dead")
+
+
+# ----------------------------------------------------------------------------
+# turning a routed workload into append lists, tables and ranges
+# ----------------------------------------------------------------------------
+
+def place_all(w: Workload, route_fn):
+    """Route every append call with route_fn(flags) -> classes and give each token a
+    place.  Returns the append lists of the whole workload (one list set)."""
+    lists = AppendLists()
+    for (t, flags, rows, new_page) in w.calls:
+        classes = route_fn(flags)
+        w.alloc.place(t, classes, rows, lists, new_page=new_page)
+    return lists
+
+
+def slot_tables(w: Workload):
+    """Slot-map tables of a slot-mode workload after placement: entry e of table t
+    holds its token's slot, or the sentinel slot if the entry is dead."""
+    assert w.kind == SLOTS
+    nt, me = w.alloc.tables.shape
+    out = np.full((nt, me), -1, np.int32)
+    for t in range(nt):
+        pages = w.alloc.tables[t, : w.alloc.n_entries[t]]
+        n = int(sum(w.alloc.fill[t]))
+        e = np.arange(n)
+        out[t, :n] = pages[e // PAGE] * PAGE + e % PAGE
+        out[t, w.dead_entries[t]] = w.sentinel_slot
+    return out
+
+
+def slot_ranges(w: Workload):
+    items = []
+    for t in range(w.n_tables):
+        for h in range(w.heads_per_page):
+            items.append((t, h, INT4, 0, int(w.head_tokens[t, h])))
+    return ranges_array(items)
+
+
+def sentinel_lists(w: Workload):
+    """Append lists that write the sentinel row (row 0) into the sentinel slot."""
+    return AppendLists(rows4=[0], slots4=[w.sentinel_slot])
