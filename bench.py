@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+Workload: Qwen3-8B-shaped decode step over a mixed INT2 / INT4 paged KV cache: batch
+16, Hq 32 / Hkv 8 (g = 4), d 128, 32768 tokens per request (70 % INT2 / 30 % INT4 in
+shuffled 32-token units, INT2-first reorder), 16-token pages, bf16 q and output,
+36 layers each with its own pools (17.4 GB in total, so no layer is served from the
+256 MB Infinity Cache).  A step = split-K decode + log-sum-exp merge for all 36
+layers.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line: effective KV GB/s of the whole step (algorithmic bytes: packed
+codes + fp16 scale/zero of every live token-head, 4 B per page-table entry, q and the
+output), us per step, the roofline of the decode kernel and the CPU oracle's rate on a
+bounded sample of the same workload."""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn effective KV GB/s (% HBM peak) + µs/step, Qwen3-8B shape @32K"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_qwen3_8b.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def effective_bytes(w, q_bytes_per_elem=2, out_bytes_per_elem=2):
+    """Algorithmic bytes of one layer: live token-heads x (96 / 160 / 512 B), 4 B per
+    page-table entry, q and output."""
+    H = w.heads_per_page
+    kv = int((w.alloc.tokens[:, 0] * 96 + w.alloc.tokens[:, 1] * 160 + w.alloc.tokens[:, 2] * 512).sum()) * H
+    tables = int(w.alloc.n_entries.sum()) * 4
+    qo = w.batch * w.hq * 128 * (q_bytes_per_elem + out_bytes_per_elem)
+    return kv + tables + qo, kv
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("kvq_decode.hip", "kvq_internal.h"):
+        with open(os.path.join(ROOT, "mixed_precision_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(decode_launches_per_step):
+    """HBM bytes per decode launch from committed rocprofv3 PMC summaries, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--target-bytes", type=int, default=1 << 18, help="effective bytes per split")
+    ap.add_argument("--cpu-requests", type=int, default=4, help="requests in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(requests and KV heads shard with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from mixed_precision_quantized_amd import kvq
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    w0 = synth.qwen3_8b(device=dev, layer=0)
+    lists = synth.place_all(w0, lambda f: kvq.route_tokens(f)[0])
+    dl = {n: torch.as_tensor(a, device=dev) for n, a in lists.arrays().items()}
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    tables = torch.as_tensor(w0.alloc.tables, device=dev).contiguous()
+    n_entries = torch.as_tensor(w0.alloc.n_entries, device=dev)
+    counts = torch.zeros((w0.n_tables, 3), dtype=torch.int32, device=dev)
+    eff_layer, kv_layer = effective_bytes(w0)
+    log(f"workload: {w0.note}; effective bytes per layer {eff_layer}")
+
+    cpu_sample = None
+    if not args.no_cpu_baseline:
+        cpu_sample = synth.subset(w0, list(range(args.cpu_requests)), device="cpu")
+
+    caches, qs = [], []
+    for L in range(args.layers):
+        w = w0 if L == 0 else synth.qwen3_8b(device=dev, layer=L)
+        cache = kvq.Cache(w0.heads_per_page, w0.n_pages, dev)
+        kvq.quantize_append(cache, w.k, w.v, rows4=dl["rows4"], slots4=dl["slots4"], rows2=dl["rows2"],
+                            pages2=dl["pages2"], dev_err=err)
+        caches.append(cache)
+        qs.append(w.q.contiguous())
+        w.k = w.v = None
+        del w
+    torch.cuda.synchronize()
+    w0.k = w0.v = None
+    torch.cuda.empty_cache()
+    kvq.reorder_pages(caches[0], tables, n_entries, counts, dev_err=err)
+    items = []
+    for t in range(w0.n_tables):
+        items += w0.alloc.ranges_after_partition(t, list(range(w0.heads_per_page)))
+    ranges = synth.ranges_array(items)
+    splits, offsets = kvq.plan_splits(ranges, w0.batch, w0.hkv, w0.heads_per_page,
+                                      target_bytes=args.target_bytes)
+    n_splits = splits.shape[0]
+    sp = torch.as_tensor(splits, device=dev).contiguous()
+    off = torch.as_tensor(offsets, device=dev)
+    g = w0.g
+    part_o = torch.empty((n_splits, g, 128), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((n_splits, g), dtype=torch.float32, device=dev)
+    outs = [torch.empty((w0.batch, w0.hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(args.layers)]
+    dec = [kvq.bind_decode_attn(caches[L], qs[L], w0.hkv, tables, kvq.TABLE_PAGES, sp, part_o, part_lse)
+           for L in range(args.layers)]
+    mrg = [kvq.bind_lse_merge(part_o, part_lse, n_splits, off, w0.batch, w0.hq, w0.hkv, outs[L])
+           for L in range(args.layers)]
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, f"device error bits {int(err.item())}"
+    log(f"setup {time.time() - t0:.1f}s: {args.layers} layers, {n_splits} splits per layer, "
+        f"pools {sum(sum(p.numel() for p in c.pools) for c in caches) / 2**30:.1f} GiB")
+
+    def step():
+        for L in range(args.layers):
+            dec[L]()
+            mrg[L]()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"step {ms_step * 1000:.1f} us ({ms_step * 1000 / args.layers:.1f} us per layer)")
+
+    # The dominant kernel alone: back-to-back decode launches on the same stream.
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, args.steps // 2)
+    d0.record(stream)
+    for _ in range(reps):
+        for L in range(args.layers):
+            dec[L]()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    us_decode = d0.elapsed_time(d1) * 1000 / (reps * args.layers)
+    decode_bytes = kv_layer + int(w0.alloc.n_entries.sum()) * 4 + w0.batch * w0.hq * 128 * 2
+    achieved = decode_bytes / (us_decode * 1e-6) / 1e9
+    log(f"decode kernel {us_decode:.1f} us per launch, {achieved:.0f} GB/s algorithmic")
+    assert int(err.item()) == 0
+
+    gbs = eff_layer * args.layers / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "us_per_step": round(ms_step * 1000, 1),
+        "us_per_layer": round(ms_step * 1000 / args.layers, 2),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u2/u4 codes, fp16 scale/zero, fp32 math",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-8B-shaped decode: batch 16, Hq 32 / Hkv 8, d 128, 32768 tokens per "
+                        "request, 70% INT2 / 30% INT4, 16-token pages, 36 layers",
+            "batch": w0.batch, "context": 32768, "layers": args.layers, "splits_per_layer": n_splits,
+            "effective_bytes_per_layer": eff_layer,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(args.layers),
+            "bytes_per_launch": decode_bytes,
+            "us_per_launch": round(us_decode, 2),
+        },
+        "cpu_baseline": None,
+    }
+
+    if cpu_sample is not None:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from harness import OracleRun
+        try:
+            n_threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            n_threads = min(16, os.cpu_count() or 1)
+        orc = OracleRun(cpu_sample)
+        t = time.perf_counter()
+        orc.attend(n_threads=n_threads)
+        dt = time.perf_counter() - t
+        sample_bytes, _ = effective_bytes(cpu_sample)
+        result["cpu_baseline"] = {
+            "value": round(sample_bytes / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": n_threads,
+            "kind": "oracle",
+            "sample": f"{args.cpu_requests} of 16 requests of one layer (all 8 KV heads, g = 4, "
+                      f"32768 tokens each), fp64 two-pass softmax; {dt:.2f} s",
+        }
+        log(f"cpu oracle {result['cpu_baseline']['value']} GB/s on {n_threads} threads ({dt:.1f} s)")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+/*
+ * kvq.h -- C ABI of libkvq: GQA decode attention read directly from a
+ * mixed-precision (INT2 / INT4 / FP16) paged KV cache on AMD MI355X (gfx950).
+ *
+ * Pages this interface follows (title, part of the page):
+ *   TriAxialKV ("TriAxialKV: Toward Extreme Low-Precision KV-Cache Quantization
+ *     for Agentic Inference Tasks"), key design 3: asymmetric group quantization
+ *     with G = 32 (INT4 K and V per-token; INT2 K per-channel across the 32 tokens
+ *     of a group; INT2 V per-token); a residual tail of fewer than 32 tokens goes
+ *     to INT4 per-token.  Key design 4: INT2 and INT4 pools in one address range
+ *     with the precision decided by the base offset; before decoding, each
+ *     request's page pointers are sorted so INT2 comes first (phase 1); the
+ *     decode kernel splits the sequence Flash-Decoding style into splits of one
+ *     precision each and merges them with a global log-sum-exp reduction
+ *     (phase 2); newly generated tokens are written as INT4 at the tail.
+ *   HyQuant ("HyQuant: Hybrid-Precision Quantization for LLM Attention"),
+ *     background (softmax(q k^T / sqrt(d)), online softmax state m, l, acc; GQA
+ *     stacks g = Hq/Hkv query heads on one KV head), method (keys partitioned into
+ *     quantized, vertical-line and window sets; anchors kept FP16) and
+ *     Algorithm 3 (split-K over the quantized prefix with dequantization inside
+ *     attention, reduce, then the FP16 segments with the same softmax state).
+ *   IntentKV (technical summary), layout-preserving eviction: evicted slot-map
+ *     entries point at one sentinel dead slot (K = -1e4, V = 0) whose attention
+ *     contribution is zero.
+ *   Tangram, method steps 5-7: one page table per head group whose heads read
+ *     only the entries their budget needs; split counts fixed ahead of time in
+ *     proportion to each group's budget.
+ *
+ * Conventions for every call:
+ *   - Pointers marked [dev] are device memory, [host] host memory.  The caller
+ *     owns every buffer.  The library never allocates, frees or synchronizes.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  They return after enqueueing.
+ *   - Argument errors the host can see are reported before anything is
+ *     enqueued, as a negative kvq_status; kvq_last_error() then describes it.
+ *   - Bad values inside device arrays (ids out of range, class mismatches,
+ *     broken INT2 pairs) never make a kernel read or write out of bounds: the
+ *     offending item is skipped (its outputs are zero / -inf) and, when
+ *     dev_err is not NULL, a KVQ_DEVERR_* bit is OR-ed into *dev_err.
+ *   - head_dim must be 128 and page_size 16.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = -1,  /* a host-visible argument is wrong            */
+    KVQ_ERR_UNSUPPORTED = -2,  /* valid but not supported (e.g. head_dim 64) */
+    KVQ_ERR_CAPACITY = -3,     /* an output buffer is too small               */
+    KVQ_ERR_HIP = -4,          /* a HIP runtime call failed                   */
+    KVQ_ERR_NO_DEVICE = -5     /* no usable gfx950 device                     */
+} kvq_status;
+
+typedef enum { KVQ_INT2 = 0, KVQ_INT4 = 1, KVQ_FP16 = 2 } kvq_class;
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1, KVQ_F16 = 2 } kvq_dtype;
+typedef enum { KVQ_TABLE_PAGES = 0, KVQ_TABLE_SLOTS = 1 } kvq_table_kind;
+
+/* Bits OR-ed into *dev_err by kernels that meet bad device data. */
+enum {
+    KVQ_DEVERR_ID = 1,      /* page / slot id outside the pools or of the wrong class */
+    KVQ_DEVERR_RANGE = 2,   /* token range, table or head index out of bounds         */
+    KVQ_DEVERR_PAIR = 4,    /* INT2 entries that are not aligned (even, even+1) pairs */
+    KVQ_DEVERR_SPLIT = 8    /* malformed split descriptor                             */
+};
+
+/*
+ * Pools.  Page ids form one id space: INT2 [0, n2), INT4 [n2, n2+n4), FP16
+ * [n2+n4, n2+n4+n16); the class of a page is found by comparing its id with the
+ * bases.  pool[c] holds n_pages[c] pages of heads_per_page head blocks each;
+ * page p's head h block starts at
+ *   pool[c] + ((p - base_c) * heads_per_page + h) * kvq_block_bytes(c).
+ * The three pools may be carved out of one allocation.  A slot id is
+ * page * 16 + offset.  Head block layouts (little-endian, fp16 (scale, zero)):
+ *   INT4 (2560 B): K codes [16 tok][64 B] @0 (channel c in byte c/2, even c in
+ *     the low nibble); K meta [4 groups][16 tok][scale, zero] @1024; V codes
+ *     @1280; V meta @2304.
+ *   INT2 (1536 B): K codes [16 tok][32 B] @0 (channel c in byte c/4 at bit
+ *     2*(c%4)); K per-channel meta of the page pair [64 ch][scale, zero] @512
+ *     (even page: channels 0-63, odd page: 64-127); V codes [16 tok][32 B] @768;
+ *     V meta [4 groups][16 tok][scale, zero] @1280.  INT2 pages are used in
+ *     aligned pairs (even, even+1) holding one 32-token group; n_pages[KVQ_INT2]
+ *     must be even.
+ *   FP16 (8192 B): K [16 tok][128] fp16 @0; V @4096.
+ */
+typedef struct {
+    int32_t head_dim;         /* must be 128                                  */
+    int32_t page_size;        /* must be 16                                   */
+    int32_t heads_per_page;   /* H_t: KV heads per page = per table, >= 1     */
+    int32_t n_pages[3];       /* pages per class (INT2, INT4, FP16)           */
+    void *pool[3];            /* [dev] one pool per class (NULL if 0 pages)   */
+    int32_t sentinel_slot;    /* slot id of the dead slot, or -1              */
+} kvq_cache;
+
+/* A token range of one (table, head-in-table) in one precision class:
+ * tokens t in [tok_begin, tok_end); in a page table token t is entry t/16,
+ * offset t%16; in a slot map token t is entry t. */
+typedef struct {
+    int32_t table, head, cls, tok_begin, tok_end;
+} kvq_split;
+
+/* Bytes of one head block of a page of class cls (0 for an unknown class). */
+size_t kvq_block_bytes(int32_t cls);
+
+/*
+ * Routing [host] (TriAxialKV key design 3).  flags[i]: 0 = the token wants
+ * INT2, 1 = INT4, 2 = FP16 anchor.  INT2-flagged tokens, in order, are grouped
+ * into groups of 32; the final fewer-than-32 of them are routed to INT4.
+ * Writes cls_out[i] (a kvq_class) and the counts (each pointer may be NULL).
+ * Errors: INVALID_ARG for n < 0, NULL arrays with n > 0, or a flag > 2.
+ */
+kvq_status kvq_route_tokens(const uint8_t *flags, int32_t n, uint8_t *cls_out,
+                            int32_t *n_int2_groups, int32_t *n_int4, int32_t *n_fp16);
+
+/*
+ * Quantize and pack tokens into the pools (TriAxialKV key design 3; new decode
+ * tokens are INT4 per key design 4; FP16 anchors per HyQuant's method).
+ *   k, v [dev]: n_rows source rows; element (row r, head h, channel c) is at
+ *     r*row_stride + h*head_stride + c, of type src_dtype (KVQ_F32, KVQ_BF16 or
+ *     KVQ_F16).  Every one of the heads_per_page heads of a row is written; a
+ *     row index outside [0, n_rows) is skipped (KVQ_DEVERR_ID).
+ *   INT4:  int4_rows[i] [dev] -> slot int4_slots[i] [dev]  (i < n_int4)
+ *   INT2:  the 32 rows int2_rows[32g .. 32g+31] [dev] -> the pair starting at
+ *          the even INT2 page int2_pages[g] [dev] (tokens 0-15 in the even page,
+ *          16-31 in the odd page)                          (g < n_int2_groups)
+ *   FP16:  fp16_rows[i] [dev] -> slot fp16_slots[i] [dev]   (i < n_fp16)
+ * Quantizer (bit-exact, IEEE fp32): z = largest fp16 <= min, s = smallest fp16
+ * >= (max - z) / L, code = clamp(rint((x - z) / s), 0, L), L = 2^b - 1; s = 0
+ * gives all-zero codes.  FP16 anchors are rounded to nearest even.  Destinations
+ * of one call must be distinct.
+ * Errors: INVALID_ARG (bad cache, NULL arrays with nonzero counts, bad dtype,
+ * negative counts or strides), UNSUPPORTED (head_dim != 128, page_size != 16),
+ * HIP.  Device-side: KVQ_DEVERR_ID / PAIR for bad slots or pages.
+ */
+kvq_status kvq_quantize_append(const kvq_cache *c, const void *k, const void *v,
+                               int32_t src_dtype, int64_t n_rows, int64_t row_stride,
+                               int64_t head_stride,
+                               int32_t n_int4, const int32_t *int4_rows, const int32_t *int4_slots,
+                               int32_t n_int2_groups, const int32_t *int2_rows,
+                               const int32_t *int2_pages,
+                               int32_t n_fp16, const int32_t *fp16_rows, const int32_t *fp16_slots,
+                               int32_t *dev_err, void *stream);
+
+/*
+ * Phase-1 page-table reorder (TriAxialKV key design 4).  tables [dev] int32
+ * [n_tables][max_entries] of page ids; for every table t, entries
+ * [0, n_entries[t]) ([dev]) are stably partitioned in place into INT2, then
+ * INT4, then FP16 pages.  class_counts [dev] int32 [n_tables][3] receives the
+ * number of pages per class (may be NULL).  The INT2 entries must form aligned
+ * pairs after the partition (KVQ_DEVERR_PAIR otherwise; the table is still
+ * partitioned).  Errors: INVALID_ARG, UNSUPPORTED (max_entries > 8192), HIP.
+ */
+kvq_status kvq_reorder_pages(const kvq_cache *c, int32_t *tables, int32_t n_tables,
+                             int32_t max_entries, const int32_t *n_entries,
+                             int32_t *class_counts, int32_t *dev_err, void *stream);
+
+/*
+ * Split-K decode attention (TriAxialKV key design 4, phase 2; HyQuant
+ * Algorithm 3).  One work item per split.  Split s = splits[s] [dev] covers
+ * tokens [tok_begin, tok_end) of (table, head) in class cls; table t serves
+ * request b = t / (hkv / heads_per_page) and KV head
+ * kvh = (t % (hkv / heads_per_page)) * heads_per_page + head, whose query heads
+ * are kvh*g .. kvh*g + g - 1 (g = hq / hkv; 1 <= g <= 16).
+ *   q [dev]: [batch][hq][128] of q_dtype (KVQ_F32 / KVQ_BF16 / KVQ_F16).
+ *   tables [dev]: int32 [n_tables][max_entries]: page ids (KVQ_TABLE_PAGES) or
+ *     slot ids (KVQ_TABLE_SLOTS); a slot equal to c->sentinel_slot is dead and
+ *     excluded from the softmax.  n_tables must equal batch * hkv / heads_per_page.
+ *   Every page a split touches must be of the split's class; INT2 splits must
+ *   start and end on multiples of 32 tokens and use page tables.
+ *   part_o [dev]: float [n_splits][g][128] = sum_t p_t v_t / sum_t p_t;
+ *   part_lse [dev]: float [n_splits][g] = natural-log log-sum-exp of the
+ *   logits q.k / sqrt(128) over the split's live tokens.  A split with no
+ *   live token gives part_o = 0 and part_lse = -inf.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP; device-side KVQ_DEVERR_*.
+ */
+kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype,
+                           int32_t batch, int32_t hq, int32_t hkv,
+                           const int32_t *tables, int32_t n_tables, int32_t max_entries,
+                           int32_t table_kind, const kvq_split *splits, int32_t n_splits,
+                           float *part_o, float *part_lse, int32_t *dev_err, void *stream);
+
+/*
+ * Log-sum-exp merge of split partials (TriAxialKV key design 4: global online
+ * log-sum-exp reduction; HyQuant Algorithm 3: ReduceSoftmax).  The partials of
+ * (request b, KV head kvh) are rows split_offsets[b*hkv + kvh] ..
+ * split_offsets[b*hkv + kvh + 1] - 1 of part_o / part_lse ([dev], n_splits rows;
+ * offsets are clamped to [0, n_splits]).  For each
+ * query head: LSE = log sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) O_s;
+ * partials with lse = -inf drop out; no partial gives O = 0, LSE = -inf.
+ *   split_offsets [dev]: int32 [batch*hkv + 1], non-decreasing.
+ *   out [dev]: [batch][hq][128] of out_dtype; out_lse [dev]: float [batch][hq]
+ *   (may be NULL).
+ * Errors: INVALID_ARG, HIP.
+ */
+kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, int32_t n_splits,
+                         const int32_t *split_offsets, int32_t batch, int32_t hq,
+                         int32_t hkv, void *out, int32_t out_dtype, float *out_lse,
+                         void *stream);
+
+/*
+ * Split plan [host] (TriAxialKV key design 4: splits of one precision each;
+ * Tangram steps 6-7: counts fixed ahead of time).  ranges [host]: the live token
+ * ranges of every (table, head), one class each, sorted by (table, head); INT2
+ * ranges on 32-token boundaries.  Each range is cut into near-equal pieces
+ * (INT2 pieces on 32-token boundaries); the number of pieces is, in order of
+ * precedence:
+ *   splits_per_head [host, may be NULL]: int32 [n_tables*heads_per_page]
+ *     pieces per (table, head), shared among its ranges in proportion to their
+ *     bytes (at least one each);
+ *   tokens_per_split[cls] > 0 [host, may be NULL]: ceil(tokens / that);
+ *   otherwise max(1, round(range bytes / target_bytes)) with 96 / 160 / 512
+ *     bytes per INT2 / INT4 / FP16 token-head.
+ * Writes out[0 .. *n_out) [host] sorted by (table, head) and split_offsets
+ * [host] int32 [batch*hkv + 1] for kvq_lse_merge.
+ * Errors: INVALID_ARG (unsorted or malformed ranges), CAPACITY (max_out).
+ */
+kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t batch,
+                           int32_t hkv, int32_t heads_per_page,
+                           const int32_t *splits_per_head, const int32_t *tokens_per_split,
+                           int64_t target_bytes, kvq_split *out, int32_t max_out,
+                           int32_t *n_out, int32_t *split_offsets);
+
+/*
+ * Ahead-of-time split counts [host] (Tangram steps 6-7: a partition factor per
+ * head group in proportion to its aggregate budget; invariant to context
+ * length).  budgets [host] float [hkv]: retained fraction per KV head (> 0).
+ * out [host] int32 [batch * hkv]: per (table, head-in-table) in table order,
+ * max(1, round(C * budget)) with C = total_work / (batch * sum(budgets)).
+ * Errors: INVALID_ARG.
+ */
+kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch,
+                                int32_t total_work, int32_t *out);
+
+/*
+ * Work groups of the decode kernel that fit on the current device at once:
+ * *per_cu from the HIP occupancy API, *n_cu the compute-unit count.  g selects
+ * the kernel variant (query heads per KV head).  Errors: NO_DEVICE, HIP.
+ */
+kvq_status kvq_decode_occupancy(int32_t g, int32_t *per_cu, int32_t *n_cu);
+
+/* Text of a status code, and a description of this thread's last error. */
+const char *kvq_status_string(int32_t status);
+const char *kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

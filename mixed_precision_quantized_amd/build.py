@@ -1,0 +1,55 @@
+"""Build libkvq.so in-tree for gfx950 with hipcc (cross-compiles without a GPU).
+
+The write path (quantize / pack / reorder) is compiled with -ffp-contract=off and
+fp32 denormals kept, so its fp32 arithmetic rounds exactly as IEEE specifies.
+Every HIP translation unit is compiled without packed fp32 instructions."""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libkvq.so")
+ARCH = "gfx950"
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
+HIP = ["--offload-arch=" + ARCH, "-fno-gpu-flush-denormals-to-zero",
+       "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+SOURCES = [
+    ("kvq_host.cpp", ["-ffp-contract=off"]),
+    ("kvq_write.hip", HIP + ["-ffp-contract=off"]),
+    ("kvq_decode.hip", HIP),
+]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src, flags in SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        cmd = ["hipcc", *COMMON, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        noise = "packed-fp32-ops"  # host pass does not know the feature: harmless
+        err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+        if err.strip() and verbose:
+            print(err, flush=True)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = ["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

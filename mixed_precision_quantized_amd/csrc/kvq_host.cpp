@@ -1,0 +1,176 @@
+// Host-only parts of libkvq: status text, argument checks, token routing and
+// split planning.  No device code and no HIP calls here.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+static thread_local char g_last_error[512] = "";
+
+kvq_status fail(kvq_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvq_status check_cache(const kvq_cache *c) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache descriptor is NULL");
+  if (c->head_dim != kHeadDim)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", c->head_dim);
+  if (c->page_size != kPage)
+    return fail(KVQ_ERR_UNSUPPORTED, "page_size %d is not supported (only 16)", c->page_size);
+  if (c->heads_per_page < 1) return fail(KVQ_ERR_INVALID_ARG, "heads_per_page must be >= 1");
+  int64_t total = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (c->n_pages[i] < 0) return fail(KVQ_ERR_INVALID_ARG, "n_pages[%d] is negative", i);
+    if (c->n_pages[i] > 0 && !c->pool[i])
+      return fail(KVQ_ERR_INVALID_ARG, "pool[%d] is NULL but holds %d pages", i, c->n_pages[i]);
+    total += c->n_pages[i];
+  }
+  if (c->n_pages[KVQ_INT2] % 2)
+    return fail(KVQ_ERR_INVALID_ARG, "the INT2 pool must hold whole page pairs");
+  if (total * kPage > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many pages for int32 slot ids");
+  if (c->sentinel_slot < -1 || c->sentinel_slot >= total * kPage)
+    return fail(KVQ_ERR_INVALID_ARG, "sentinel_slot %d is outside the pools", c->sentinel_slot);
+  return KVQ_OK;
+}
+
+static int64_t token_bytes(int cls) { return cls == KVQ_INT2 ? 96 : cls == KVQ_INT4 ? 160 : 512; }
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+size_t kvq_block_bytes(int32_t cls) {
+  return cls == KVQ_INT2 ? kI2Bytes : cls == KVQ_INT4 ? kI4Bytes : cls == KVQ_FP16 ? kF16Bytes : 0;
+}
+
+const char *kvq_status_string(int32_t st) {
+  switch (st) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported";
+    case KVQ_ERR_CAPACITY: return "output capacity too small";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+    case KVQ_ERR_NO_DEVICE: return "no usable device";
+    default: return "unknown status";
+  }
+}
+
+const char *kvq_last_error(void) { return g_last_error; }
+
+kvq_status kvq_route_tokens(const uint8_t *flags, int32_t n, uint8_t *cls_out, int32_t *n_int2_groups,
+                            int32_t *n_int4, int32_t *n_fp16) {
+  if (n < 0) return fail(KVQ_ERR_INVALID_ARG, "negative token count");
+  if (n > 0 && (!flags || !cls_out)) return fail(KVQ_ERR_INVALID_ARG, "NULL flags or output");
+  // First pass: how many INT2-flagged tokens fill whole groups of 32.
+  int32_t wants_int2 = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (flags[i] > 2) return fail(KVQ_ERR_INVALID_ARG, "flag %u at %d is not 0, 1 or 2", flags[i], i);
+    wants_int2 += flags[i] == 0;
+  }
+  const int32_t grouped = wants_int2 - wants_int2 % kGroup;
+  int32_t seen = 0, c4 = 0, c16 = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    uint8_t cls;
+    if (flags[i] == 0) cls = seen++ < grouped ? KVQ_INT2 : KVQ_INT4;  // residual tail -> INT4
+    else cls = flags[i] == 1 ? KVQ_INT4 : KVQ_FP16;
+    c4 += cls == KVQ_INT4;
+    c16 += cls == KVQ_FP16;
+    cls_out[i] = cls;
+  }
+  if (n_int2_groups) *n_int2_groups = grouped / kGroup;
+  if (n_int4) *n_int4 = c4;
+  if (n_fp16) *n_fp16 = c16;
+  return KVQ_OK;
+}
+
+kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t batch, int32_t hkv,
+                           int32_t heads_per_page, const int32_t *splits_per_head,
+                           const int32_t *tokens_per_split, int64_t target_bytes, kvq_split *out,
+                           int32_t max_out, int32_t *n_out, int32_t *split_offsets) {
+  if (n_ranges < 0 || batch < 0 || hkv <= 0 || heads_per_page <= 0 || hkv % heads_per_page)
+    return fail(KVQ_ERR_INVALID_ARG, "bad plan shape");
+  if ((n_ranges > 0 && !ranges) || !n_out || !split_offsets || (max_out > 0 && !out))
+    return fail(KVQ_ERR_INVALID_ARG, "NULL plan array");
+  const int32_t tpr = hkv / heads_per_page;
+  const int32_t n_tables = batch * tpr;
+  // Bytes per (table, head) to share splits_per_head among its ranges.
+  std::vector<int64_t> head_bytes;
+  if (splits_per_head) head_bytes.assign((size_t)n_tables * heads_per_page, 0);
+  for (int32_t i = 0; i < n_ranges; ++i) {
+    const kvq_split &r = ranges[i];
+    if (r.table < 0 || r.table >= n_tables || r.head < 0 || r.head >= heads_per_page || r.cls < 0 ||
+        r.cls > 2 || r.tok_begin < 0 || r.tok_end < r.tok_begin)
+      return fail(KVQ_ERR_INVALID_ARG, "malformed range %d", i);
+    if (r.cls == KVQ_INT2 && (r.tok_begin % kGroup || r.tok_end % kGroup))
+      return fail(KVQ_ERR_INVALID_ARG, "INT2 range %d is not on 32-token boundaries", i);
+    if (i > 0) {
+      const kvq_split &p = ranges[i - 1];
+      if (p.table > r.table || (p.table == r.table && p.head > r.head))
+        return fail(KVQ_ERR_INVALID_ARG, "ranges are not sorted by (table, head) at %d", i);
+    }
+    if (splits_per_head) head_bytes[(size_t)r.table * heads_per_page + r.head] +=
+        (int64_t)(r.tok_end - r.tok_begin) * token_bytes(r.cls);
+  }
+  int32_t w = 0;
+  int32_t next_pair = 0;  // next (b*hkv + kvh) whose offset is still unset
+  for (int32_t i = 0; i < n_ranges; ++i) {
+    const kvq_split &r = ranges[i];
+    const int32_t pair = (r.table / tpr) * hkv + (r.table % tpr) * heads_per_page + r.head;
+    while (next_pair <= pair) split_offsets[next_pair++] = w;
+    const int32_t unit = r.cls == KVQ_INT2 ? kGroup : 1;
+    const int64_t units = (r.tok_end - r.tok_begin) / unit;
+    if (units == 0) continue;
+    const int64_t bytes = (int64_t)(r.tok_end - r.tok_begin) * token_bytes(r.cls);
+    int64_t pieces;
+    if (splits_per_head) {
+      const size_t hk = (size_t)r.table * heads_per_page + r.head;
+      const double share = (double)splits_per_head[hk] * (double)bytes / (double)head_bytes[hk];
+      pieces = std::max<int64_t>(1, std::llround(share));
+    } else if (tokens_per_split && tokens_per_split[r.cls] > 0) {
+      pieces = ((int64_t)(r.tok_end - r.tok_begin) + tokens_per_split[r.cls] - 1) / tokens_per_split[r.cls];
+    } else if (target_bytes > 0) {
+      pieces = std::max<int64_t>(1, std::llround((double)bytes / (double)target_bytes));
+    } else {
+      pieces = 1;
+    }
+    pieces = std::min(pieces, units);
+    for (int64_t p = 0; p < pieces; ++p) {
+      if (w >= max_out) return fail(KVQ_ERR_CAPACITY, "more than %d splits", max_out);
+      const int64_t a = units * p / pieces, b = units * (p + 1) / pieces;
+      out[w++] = kvq_split{r.table, r.head, r.cls, (int32_t)(r.tok_begin + a * unit),
+                           p + 1 == pieces ? r.tok_end : (int32_t)(r.tok_begin + b * unit)};
+    }
+  }
+  while (next_pair <= batch * hkv) split_offsets[next_pair++] = w;
+  *n_out = w;
+  return KVQ_OK;
+}
+
+kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch, int32_t total_work,
+                                int32_t *out) {
+  if (!budgets || !out || hkv <= 0 || batch <= 0 || total_work <= 0)
+    return fail(KVQ_ERR_INVALID_ARG, "bad AOT split-count arguments");
+  double sum = 0.0;
+  for (int32_t h = 0; h < hkv; ++h) {
+    if (!(budgets[h] > 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "budget of head %d is not positive", h);
+    sum += budgets[h];
+  }
+  const double per_unit = (double)total_work / ((double)batch * sum);
+  for (int32_t b = 0; b < batch; ++b)
+    for (int32_t h = 0; h < hkv; ++h)
+      out[(size_t)b * hkv + h] = (int32_t)std::max<long long>(1, std::llround(per_unit * budgets[h]));
+  return KVQ_OK;
+}
+
+}  // extern "C"

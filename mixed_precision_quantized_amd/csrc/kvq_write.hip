@@ -1,0 +1,401 @@
+// Write path of libkvq for gfx950: quantize + pack into the INT2 / INT4 / FP16
+// pools, and the phase-1 page-table reorder.
+//
+// Quantizer (TriAxialKV key design 3): asymmetric groups of G = 32, scale and
+// zero stored as fp16: z = largest fp16 <= min, s = smallest fp16 >=
+// fl32(fl32(max - z) / L), code = clamp(rint(fl32(fl32(x - z) / s)), 0, L).
+// This translation unit is compiled with -ffp-contract=off and keeps fp32
+// denormals, so every operation rounds exactly as IEEE fp32 does.
+//
+// Work mapping: one 64-lane wavefront per (token, head) for per-token groups;
+// lane l owns channels 2l and 2l+1, so a 32-channel group is 16 adjacent lanes
+// and its min / max is a 4-step butterfly within those lanes.  One wavefront per
+// (INT2 group, head) for the per-channel INT2 K groups (each lane keeps its two
+// channels of all 32 tokens in registers).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ void report(int32_t *err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// ---------------------------------------------------------------- fp16 --------
+
+// fp16 bits -> fp32, exact (including fp16 subnormals), by integer arithmetic.
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  const uint32_t sign = (h & 0x8000u) << 16;
+  const uint32_t ex = (h >> 10) & 31u, man = h & 1023u;
+  float mag;
+  if (ex == 0) {
+    mag = (float)man * 5.9604644775390625e-08f;  // man * 2^-24, exact
+  } else {
+    mag = __uint_as_float(((ex + 112u) << 23) | (man << 13));
+  }
+  return __uint_as_float(__float_as_uint(mag) | sign);
+}
+
+// Directed rounding of a finite fp32 value to fp16 bits: up = false gives the
+// largest fp16 <= x, up = true the smallest fp16 >= x.  -0 is returned as +0.
+__device__ __forceinline__ uint32_t float_to_half_directed(float x, bool up) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t sign = b >> 31;
+  const uint32_t a = b & 0x7fffffffu;
+  if (a == 0) return 0;
+  const int e = (int)(a >> 23) - 127;
+  uint32_t mant = a & 0x7fffffu;
+  int e_eff = e;
+  if (e == -127) e_eff = -126;  // fp32 subnormal
+  else mant |= 0x800000u;       // implicit bit
+  uint32_t mag, lost;
+  if (e_eff > 15) {
+    mag = 0x7c00u;  // beyond fp16 range: only reachable when the caller's precondition fails
+    lost = 0;
+  } else if (e_eff >= -14) {  // fp16 normal: keep 10 fraction bits
+    mag = ((uint32_t)(e_eff + 15) << 10) | ((mant >> 13) & 0x3ffu);
+    lost = mant & 0x1fffu;
+  } else {  // fp16 subnormal: value / 2^-24 = mant * 2^(e_eff + 1)
+    const int sh = -(e_eff + 1);
+    if (sh >= 32) {
+      mag = 0;
+      lost = mant;
+    } else {
+      mag = mant >> sh;
+      lost = mant & ((1u << sh) - 1u);
+    }
+  }
+  // Truncation rounded the magnitude toward zero; step away from zero when
+  // the direction asks for it (a carry into the exponent field is correct).
+  const bool away = lost != 0 && (up ? sign == 0 : sign == 1);
+  mag += away ? 1u : 0u;
+  return mag == 0 ? 0u : (mag | (sign << 15));
+}
+
+// Round-to-nearest-even fp32 -> fp16 bits (FP16 anchors).
+__device__ __forceinline__ uint32_t float_to_half_rne(float x) {
+  const uint32_t h = (uint32_t)__half_as_ushort(__float2half_rn(x));
+  return h == 0x8000u ? 0u : h;
+}
+
+__device__ __forceinline__ float load_src(const void *base, int32_t dtype, int64_t idx) {
+  if (dtype == KVQ_F32) return static_cast<const float *>(base)[idx];
+  const uint32_t h = static_cast<const uint16_t *>(base)[idx];
+  if (dtype == KVQ_BF16) return __uint_as_float(h << 16);
+  return half_bits_to_float(h);
+}
+
+// Min and max over the 16 lanes of a group (lanes differing in bits 0..3).
+__device__ __forceinline__ void group16_minmax(float &mn, float &mx) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m));
+    mx = fmaxf(mx, __shfl_xor(mx, m));
+  }
+}
+
+struct Quant {
+  float s, z;
+  uint32_t sb, zb;
+};
+
+__device__ __forceinline__ Quant quant_params(float mn, float mx, float levels) {
+  Quant q;
+  q.zb = float_to_half_directed(mn, false);
+  q.z = half_bits_to_float(q.zb);
+  const float range = __fsub_rn(mx, q.z);
+  const float step = __fdiv_rn(range, levels);
+  q.sb = float_to_half_directed(step, true);
+  q.s = half_bits_to_float(q.sb);
+  return q;
+}
+
+__device__ __forceinline__ uint32_t quant_code(float x, const Quant &q, float levels) {
+  if (q.s == 0.0f) return 0;
+  const float t = __fdiv_rn(__fsub_rn(x, q.z), q.s);
+  const float r = fminf(fmaxf(rintf(t), 0.0f), levels);
+  return (uint32_t)r;
+}
+
+__device__ __forceinline__ float canon(float x) { return x == 0.0f ? 0.0f : x; }  // -0 -> +0
+
+struct CacheView {
+  int32_t heads;
+  int32_t n2, n4, n16;
+  uint8_t *pool2, *pool4, *pool16;
+};
+
+__device__ __forceinline__ int page_class(const CacheView &c, int64_t p) {
+  if (p < 0) return -1;
+  if (p < c.n2) return KVQ_INT2;
+  if (p < (int64_t)c.n2 + c.n4) return KVQ_INT4;
+  if (p < (int64_t)c.n2 + c.n4 + c.n16) return KVQ_FP16;
+  return -1;
+}
+
+// ---------------------------------------------------------- per-token path ----
+
+// Quantizes one 128-channel row (this lane: channels 2l, 2l+1) in per-token
+// groups of 32 and writes codes + (scale, zero) of token `off` into a block.
+template <int BITS>
+__device__ __forceinline__ void put_token_row(uint8_t *blk, int codes_at, int meta_at, int off,
+                                              float x0, float x1, int lane) {
+  constexpr float kLevels = (float)((1 << BITS) - 1);
+  float mn = fminf(canon(x0), canon(x1)), mx = fmaxf(canon(x0), canon(x1));
+  group16_minmax(mn, mx);
+  const Quant q = quant_params(mn, mx, kLevels);
+  const uint32_t c0 = quant_code(x0, q, kLevels), c1 = quant_code(x1, q, kLevels);
+  if (BITS == 4) {
+    blk[codes_at + off * 64 + lane] = (uint8_t)(c0 | (c1 << 4));
+  } else {
+    // Channels 4j..4j+3 share byte j = lane / 2: even lane low nibble, odd lane high.
+    const uint32_t nib = c0 | (c1 << 2);
+    const uint32_t other = (uint32_t)__shfl_xor((int)nib, 1);
+    if ((lane & 1) == 0) blk[codes_at + off * 32 + (lane >> 1)] = (uint8_t)(nib | (other << 4));
+  }
+  if ((lane & 15) == 0) {
+    const int g = lane >> 4;
+    *reinterpret_cast<uint32_t *>(blk + meta_at + (g * kPage + off) * 4) = q.sb | (q.zb << 16);
+  }
+}
+
+// One wavefront per (item, head): items [0, n4) are INT4 tokens, then FP16 tokens.
+__global__ void __launch_bounds__(256) append_tokens_kernel(
+    CacheView c, const void *k, const void *v, int32_t dtype, int64_t n_rows, int64_t row_stride,
+    int64_t head_stride,
+    int32_t n4, const int32_t *rows4, const int32_t *slots4, int32_t n16, const int32_t *rows16,
+    const int32_t *slots16, int32_t *err) {
+  const int lane = threadIdx.x & 63;
+  const int64_t work = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t total = (int64_t)(n4 + n16) * c.heads;
+  if (work >= total) return;
+  const int64_t item = work / c.heads;
+  const int head = (int)(work % c.heads);
+  const bool is4 = item < n4;
+  const int32_t row = is4 ? rows4[item] : rows16[item - n4];
+  const int32_t slot = is4 ? slots4[item] : slots16[item - n4];
+  const int64_t page = slot >> 4;
+  const int off = slot & 15;
+  if (slot < 0 || row < 0 || row >= n_rows || page_class(c, page) != (is4 ? KVQ_INT4 : KVQ_FP16)) {
+    if (lane == 0) report(err, KVQ_DEVERR_ID);
+    return;
+  }
+  const int64_t src = (int64_t)row * row_stride + (int64_t)head * head_stride + 2 * lane;
+  const float k0 = load_src(k, dtype, src), k1 = load_src(k, dtype, src + 1);
+  const float v0 = load_src(v, dtype, src), v1 = load_src(v, dtype, src + 1);
+  if (is4) {
+    uint8_t *blk = c.pool4 + ((page - c.n2) * c.heads + head) * (int64_t)kI4Bytes;
+    put_token_row<4>(blk, kI4KC, kI4KM, off, k0, k1, lane);
+    put_token_row<4>(blk, kI4VC, kI4VM, off, v0, v1, lane);
+  } else {
+    uint8_t *blk = c.pool16 + ((page - c.n2 - c.n4) * c.heads + head) * (int64_t)kF16Bytes;
+    *reinterpret_cast<uint32_t *>(blk + kF16K + off * 256 + lane * 4) =
+        float_to_half_rne(k0) | (float_to_half_rne(k1) << 16);
+    *reinterpret_cast<uint32_t *>(blk + kF16V + off * 256 + lane * 4) =
+        float_to_half_rne(v0) | (float_to_half_rne(v1) << 16);
+  }
+}
+
+// ------------------------------------------------------------- INT2 groups ----
+
+// One wavefront per (INT2 group, head).  K: per-channel groups across the 32
+// tokens; V: per-token groups of 32 channels.
+__global__ void __launch_bounds__(64) append_int2_kernel(
+    CacheView c, const void *k, const void *v, int32_t dtype, int64_t n_rows, int64_t row_stride,
+    int64_t head_stride,
+    int32_t n_groups, const int32_t *rows2, const int32_t *pages2, int32_t *err) {
+  const int lane = threadIdx.x;
+  const int32_t grp = blockIdx.x / c.heads;
+  const int head = blockIdx.x % c.heads;
+  if (grp >= n_groups) return;
+  const int64_t even = pages2[grp];
+  if (page_class(c, even) != KVQ_INT2 || (even & 1) || even + 1 >= c.n2) {
+    if (lane == 0) report(err, KVQ_DEVERR_PAIR);
+    return;
+  }
+  uint8_t *blk[2];
+  blk[0] = c.pool2 + (even * c.heads + head) * (int64_t)kI2Bytes;
+  blk[1] = c.pool2 + ((even + 1) * c.heads + head) * (int64_t)kI2Bytes;
+  const int32_t *rows = rows2 + (int64_t)grp * kGroup;
+
+  // K, per channel: lane holds channels 2l, 2l+1 of all 32 tokens.
+  float kx[kGroup][2];
+  bool bad = false;
+  float mn0 = 0.f, mx0 = 0.f, mn1 = 0.f, mx1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t) {
+    const int32_t r = rows[t];
+    bad |= r < 0 || r >= n_rows;
+    const int64_t src = (int64_t)(r < 0 || r >= n_rows ? 0 : r) * row_stride + (int64_t)head * head_stride + 2 * lane;
+    kx[t][0] = load_src(k, dtype, src);
+    kx[t][1] = load_src(k, dtype, src + 1);
+    const float a = canon(kx[t][0]), b = canon(kx[t][1]);
+    mn0 = t ? fminf(mn0, a) : a;
+    mx0 = t ? fmaxf(mx0, a) : a;
+    mn1 = t ? fminf(mn1, b) : b;
+    mx1 = t ? fmaxf(mx1, b) : b;
+  }
+  if (bad) {
+    if (lane == 0) report(err, KVQ_DEVERR_ID);
+    return;
+  }
+  const Quant q0 = quant_params(mn0, mx0, 3.0f), q1 = quant_params(mn1, mx1, 3.0f);
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t) {
+    const uint32_t nib = quant_code(kx[t][0], q0, 3.0f) | (quant_code(kx[t][1], q1, 3.0f) << 2);
+    const uint32_t other = (uint32_t)__shfl_xor((int)nib, 1);
+    if ((lane & 1) == 0) blk[t >> 4][kI2KC + (t & 15) * 32 + (lane >> 1)] = (uint8_t)(nib | (other << 4));
+  }
+  {
+    // Channel c's (scale, zero): even page for c < 64, odd page for c >= 64.
+    const int ch = 2 * lane;
+    uint8_t *m = blk[ch >> 6] + kI2KM + (ch & 63) * 4;
+    *reinterpret_cast<uint2 *>(m) = make_uint2(q0.sb | (q0.zb << 16), q1.sb | (q1.zb << 16));
+  }
+
+  // V, per token.
+#pragma unroll 4
+  for (int t = 0; t < kGroup; ++t) {
+    const int64_t src = (int64_t)rows[t] * row_stride + (int64_t)head * head_stride + 2 * lane;
+    put_token_row<2>(blk[t >> 4], kI2VC, kI2VM, t & 15, load_src(v, dtype, src),
+                     load_src(v, dtype, src + 1), lane);
+  }
+}
+
+// --------------------------------------------------------------- reorder ------
+
+// One wavefront per table: stable partition of the entries by class with
+// ballot + popcount prefix sums.  The entries are staged in LDS (input and
+// output halves), so the write-back is in place and the pair check reads LDS.
+__global__ void __launch_bounds__(64) reorder_kernel(CacheView c, int32_t *tables, int32_t max_entries,
+                                                     const int32_t *n_entries, int32_t *class_counts,
+                                                     int32_t *err) {
+  extern __shared__ int32_t lds[];
+  int32_t *ent = lds;                 // [max_entries] input order
+  int32_t *part = lds + max_entries;  // [max_entries] partitioned order
+  const int lane = threadIdx.x;
+  const int32_t t = blockIdx.x;
+  int32_t *row = tables + (int64_t)t * max_entries;
+  const int32_t n = n_entries[t];
+  if (n < 0 || n > max_entries) {
+    if (lane == 0) report(err, KVQ_DEVERR_RANGE);
+    return;
+  }
+  bool bad = false;
+  for (int32_t e = lane; e < n; e += 64) {
+    ent[e] = row[e];
+    bad |= page_class(c, ent[e]) < 0;
+  }
+  if (__any(bad)) {  // leave the table as it was
+    if (lane == 0) report(err, KVQ_DEVERR_ID);
+    return;
+  }
+  int32_t w = 0, counts[3];
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int cls = 0; cls < 3; ++cls) {
+    const int32_t start = w;
+    for (int32_t base = 0; base < n; base += 64) {
+      const int32_t e = base + lane;  // written by this same lane above
+      const bool mine = e < n && page_class(c, ent[e]) == cls;
+      const uint64_t mask = __ballot(mine);
+      if (mine) part[w + __popcll(mask & below)] = ent[e];
+      w += __popcll(mask);
+    }
+    counts[cls] = w - start;
+  }
+  __syncthreads();  // part[] is read across lanes below
+  for (int32_t e = lane; e < n; e += 64) row[e] = part[e];
+  if (class_counts && lane == 0)
+    for (int cls = 0; cls < 3; ++cls) class_counts[(int64_t)t * 3 + cls] = counts[cls];
+  // INT2 entries must now be aligned pairs (even, even + 1).
+  bool pair_bad = counts[0] & 1;
+  for (int32_t e = 2 * lane; e + 1 < counts[0]; e += 128) {
+    const int32_t p = part[e];
+    pair_bad |= (p & 1) || part[e + 1] != p + 1;
+  }
+  if (__any(pair_bad) && lane == 0) report(err, KVQ_DEVERR_PAIR);
+}
+
+CacheView view_of(const kvq_cache *c) {
+  CacheView v;
+  v.heads = c->heads_per_page;
+  v.n2 = c->n_pages[0];
+  v.n4 = c->n_pages[1];
+  v.n16 = c->n_pages[2];
+  v.pool2 = static_cast<uint8_t *>(c->pool[0]);
+  v.pool4 = static_cast<uint8_t *>(c->pool[1]);
+  v.pool16 = static_cast<uint8_t *>(c->pool[2]);
+  return v;
+}
+
+kvq_status launched(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" kvq_status kvq_quantize_append(const kvq_cache *c, const void *k, const void *v,
+                                          int32_t src_dtype, int64_t n_rows, int64_t row_stride,
+                                          int64_t head_stride,
+                                          int32_t n_int4, const int32_t *int4_rows,
+                                          const int32_t *int4_slots, int32_t n_int2_groups,
+                                          const int32_t *int2_rows, const int32_t *int2_pages,
+                                          int32_t n_fp16, const int32_t *fp16_rows,
+                                          const int32_t *fp16_slots, int32_t *dev_err, void *stream) {
+  kvq_status st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  if (src_dtype < KVQ_F32 || src_dtype > KVQ_F16) return fail(KVQ_ERR_INVALID_ARG, "bad source dtype %d", src_dtype);
+  if (n_int4 < 0 || n_int2_groups < 0 || n_fp16 < 0) return fail(KVQ_ERR_INVALID_ARG, "negative token count");
+  if (row_stride < 0 || head_stride < 0 || n_rows < 0) return fail(KVQ_ERR_INVALID_ARG, "negative stride or row count");
+  if ((n_int4 && (!int4_rows || !int4_slots)) || (n_int2_groups && (!int2_rows || !int2_pages)) ||
+      (n_fp16 && (!fp16_rows || !fp16_slots)))
+    return fail(KVQ_ERR_INVALID_ARG, "NULL destination list with a nonzero count");
+  if ((n_int4 || n_int2_groups || n_fp16) && (!k || !v)) return fail(KVQ_ERR_INVALID_ARG, "NULL k or v");
+  if (c->heads_per_page > 1 && head_stride < kHeadDim)
+    return fail(KVQ_ERR_INVALID_ARG, "head_stride %lld overlaps heads", (long long)head_stride);
+  const CacheView view = view_of(c);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t token_waves = (int64_t)(n_int4 + n_fp16) * c->heads_per_page;
+  if (token_waves > 0) {
+    const int64_t blocks = (token_waves + 3) / 4;
+    if (blocks > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many tokens in one call");
+    hipLaunchKernelGGL(append_tokens_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, view, k, v, src_dtype,
+                       n_rows, row_stride, head_stride, n_int4, int4_rows, int4_slots, n_fp16, fp16_rows,
+                       fp16_slots, dev_err);
+    if ((st = launched("append_tokens_kernel")) != KVQ_OK) return st;
+  }
+  if (n_int2_groups > 0) {
+    const int64_t blocks = (int64_t)n_int2_groups * c->heads_per_page;
+    if (blocks > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many INT2 groups in one call");
+    hipLaunchKernelGGL(append_int2_kernel, dim3((uint32_t)blocks), dim3(64), 0, s, view, k, v, src_dtype,
+                       n_rows, row_stride, head_stride, n_int2_groups, int2_rows, int2_pages, dev_err);
+    if ((st = launched("append_int2_kernel")) != KVQ_OK) return st;
+  }
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_reorder_pages(const kvq_cache *c, int32_t *tables, int32_t n_tables,
+                                        int32_t max_entries, const int32_t *n_entries,
+                                        int32_t *class_counts, int32_t *dev_err, void *stream) {
+  kvq_status st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  if (n_tables < 0 || max_entries < 0) return fail(KVQ_ERR_INVALID_ARG, "negative table shape");
+  if (n_tables == 0) return KVQ_OK;
+  if (!tables || !n_entries) return fail(KVQ_ERR_INVALID_ARG, "NULL tables or n_entries");
+  if (max_entries > kMaxReorderEntries)
+    return fail(KVQ_ERR_UNSUPPORTED, "max_entries %d exceeds %d", max_entries, kMaxReorderEntries);
+  hipLaunchKernelGGL(reorder_kernel, dim3(n_tables), dim3(64), (size_t)(max_entries > 0 ? max_entries : 1) * 8,
+                     static_cast<hipStream_t>(stream), view_of(c), tables, max_entries, n_entries,
+                     class_counts, dev_err);
+  return launched("reorder_kernel");
+}

@@ -1,0 +1,275 @@
+"""Thin Python binding of libkvq (ctypes).  Argument marshalling only: every step of
+the decode path runs in the library's HIP kernels or its host C++ code.
+
+Device arrays are torch tensors on a ROCm device; host arrays are numpy arrays.
+Calls enqueue on torch's current stream unless a stream is given.  The binding
+raises ImportError when libkvq.so is missing: there is no fallback path.
+
+The operations and their sources are documented in include/kvq.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+INT2, INT4, FP16 = 0, 1, 2
+F32, BF16, F16 = 0, 1, 2
+TABLE_PAGES, TABLE_SLOTS = 0, 1
+DEVERR_ID, DEVERR_RANGE, DEVERR_PAIR, DEVERR_SPLIT = 1, 2, 4, 8
+HEAD_DIM = 128
+PAGE = 16
+
+SPLIT_DTYPE = np.dtype([("table", "<i4"), ("head", "<i4"), ("cls", "<i4"),
+                        ("tok_begin", "<i4"), ("tok_end", "<i4")])
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                      "(the decode path has no fallback)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.kvq_status_string(status).decode()
+        detail = _lib.kvq_last_error().decode()
+        super().__init__(f"{where}: {msg} ({status}): {detail}")
+
+
+class _CacheC(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("heads_per_page", ctypes.c_int32), ("n_pages", ctypes.c_int32 * 3),
+                ("pool", ctypes.c_void_p * 3), ("sentinel_slot", ctypes.c_int32)]
+
+
+class _SplitC(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_int32), ("head", ctypes.c_int32), ("cls", ctypes.c_int32),
+                ("tok_begin", ctypes.c_int32), ("tok_end", ctypes.c_int32)]
+
+
+_P, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+_SIGS = {
+    "kvq_block_bytes": ([_i32], ctypes.c_size_t),
+    "kvq_route_tokens": ([_P, _i32, _P, _P, _P, _P], ctypes.c_int),
+    "kvq_quantize_append": ([_P, _P, _P, _i32, _i64, _i64, _i64, _i32, _P, _P, _i32, _P, _P, _i32, _P, _P,
+                             _P, _P], ctypes.c_int),
+    "kvq_reorder_pages": ([_P, _P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
+    "kvq_decode_attn": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P, _P,
+                         _P], ctypes.c_int),
+    "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
+    "kvq_plan_splits": ([_P, _i32, _i32, _i32, _i32, _P, _P, _i64, _P, _i32, _P, _P], ctypes.c_int),
+    "kvq_aot_split_counts": ([_P, _i32, _i32, _i32, _P], ctypes.c_int),
+    "kvq_decode_occupancy": ([_i32, _P, _P], ctypes.c_int),
+    "kvq_status_string": ([_i32], ctypes.c_char_p),
+    "kvq_last_error": ([], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KvqError(status, where)
+
+
+def _dptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_cuda, "device array expected"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _hptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+def block_bytes(cls: int) -> int:
+    return int(_lib.kvq_block_bytes(cls))
+
+
+class Cache:
+    """Device pools of a mixed-precision paged KV cache (allocated by torch)."""
+
+    def __init__(self, heads_per_page: int, n_pages, device="cuda", sentinel_slot: int = -1,
+                 pools=None):
+        self.heads_per_page = int(heads_per_page)
+        self.n_pages = tuple(int(n) for n in n_pages)
+        self.sentinel_slot = int(sentinel_slot)
+        if pools is None:
+            pools = [torch.zeros(max(1, n * self.heads_per_page * block_bytes(c)), dtype=torch.uint8,
+                                 device=device) for c, n in enumerate(self.n_pages)]
+        self.pools = pools
+        self._c = _CacheC()
+        self._c.head_dim = HEAD_DIM
+        self._c.page_size = PAGE
+        self._c.heads_per_page = self.heads_per_page
+        for i in range(3):
+            self._c.n_pages[i] = self.n_pages[i]
+            self._c.pool[i] = self.pools[i].data_ptr()
+        self._c.sentinel_slot = self.sentinel_slot
+
+    @property
+    def struct(self):
+        return ctypes.byref(self._c)
+
+    def pool_bytes(self, cls: int) -> torch.Tensor:
+        return self.pools[cls][: self.n_pages[cls] * self.heads_per_page * block_bytes(cls)]
+
+
+def route_tokens(flags: np.ndarray):
+    """flags uint8 [n] (0 INT2, 1 INT4, 2 FP16) -> (classes, n_int2_groups, n_int4, n_fp16)."""
+    flags = np.ascontiguousarray(flags, dtype=np.uint8)
+    cls = np.zeros(flags.shape[0], np.uint8)
+    n2, n4, n16 = _i32(), _i32(), _i32()
+    _check(_lib.kvq_route_tokens(_hptr(flags), flags.shape[0], _hptr(cls), ctypes.byref(n2),
+                                 ctypes.byref(n4), ctypes.byref(n16)), "kvq_route_tokens")
+    return cls, n2.value, n4.value, n16.value
+
+
+def quantize_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, rows4=None, slots4=None,
+                    rows2=None, pages2=None, rows16=None, slots16=None, dev_err=None, stream=None):
+    """k, v [R, heads_per_page, 128] (any strides with unit channel stride); lists are
+    int32 device tensors (or None)."""
+    assert k.shape == v.shape and k.stride() == v.stride() and k.dtype == v.dtype
+    assert k.shape[-1] == HEAD_DIM and k.stride(-1) == 1
+    n = lambda t: 0 if t is None else int(t.numel())  # noqa: E731
+    head_stride = k.stride(1) if k.dim() == 3 else HEAD_DIM
+    _check(_lib.kvq_quantize_append(
+        cache.struct, _dptr(k), _dptr(v), _DTYPES[k.dtype], k.shape[0], k.stride(0), head_stride,
+        n(rows4), _dptr(rows4), _dptr(slots4), n(pages2), _dptr(rows2), _dptr(pages2),
+        n(rows16), _dptr(rows16), _dptr(slots16), _dptr(dev_err), _stream(stream)),
+        "kvq_quantize_append")
+
+
+def reorder_pages(cache: Cache, tables: torch.Tensor, n_entries: torch.Tensor,
+                  class_counts: Optional[torch.Tensor] = None, dev_err=None, stream=None):
+    assert tables.dtype == torch.int32 and tables.is_contiguous() and tables.dim() == 2
+    _check(_lib.kvq_reorder_pages(cache.struct, _dptr(tables), tables.shape[0], tables.shape[1],
+                                  _dptr(n_entries), _dptr(class_counts), _dptr(dev_err),
+                                  _stream(stream)), "kvq_reorder_pages")
+
+
+def decode_attn(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, table_kind: int,
+                splits: torch.Tensor, part_o: torch.Tensor, part_lse: torch.Tensor, dev_err=None,
+                stream=None):
+    """q [batch, hq, 128]; splits int32 device [n, 5]; part_o float [n, g, 128]; part_lse [n, g]."""
+    assert q.is_contiguous() and tables.is_contiguous() and splits.is_contiguous()
+    assert splits.dtype == torch.int32 and splits.shape[-1] == 5
+    batch, hq = q.shape[0], q.shape[1]
+    n_splits = splits.shape[0]
+    g = hq // hkv
+    assert part_o.numel() >= n_splits * g * HEAD_DIM and part_lse.numel() >= n_splits * g
+    assert part_o.dtype == torch.float32 and part_lse.dtype == torch.float32
+    _check(_lib.kvq_decode_attn(cache.struct, _dptr(q), _DTYPES[q.dtype], batch, hq, hkv,
+                                _dptr(tables), tables.shape[0], tables.shape[1], table_kind,
+                                _dptr(splits), n_splits, _dptr(part_o), _dptr(part_lse),
+                                _dptr(dev_err), _stream(stream)), "kvq_decode_attn")
+
+
+def lse_merge(part_o: torch.Tensor, part_lse: torch.Tensor, n_splits: int, split_offsets: torch.Tensor,
+              batch: int, hq: int, hkv: int, out: torch.Tensor, out_lse=None, stream=None):
+    assert out.is_contiguous() and out.numel() >= batch * hq * HEAD_DIM
+    _check(_lib.kvq_lse_merge(_dptr(part_o), _dptr(part_lse), n_splits, _dptr(split_offsets), batch,
+                              hq, hkv, _dptr(out), _DTYPES[out.dtype], _dptr(out_lse),
+                              _stream(stream)), "kvq_lse_merge")
+
+
+def plan_splits(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int,
+                splits_per_head: Optional[np.ndarray] = None, tokens_per_split=None,
+                target_bytes: int = 0, max_out: Optional[int] = None):
+    """ranges: structured (SPLIT_DTYPE) or int32 [n, 5], sorted by (table, head).
+    Returns (splits int32 [n_out, 5], split_offsets int32 [batch*hkv + 1])."""
+    r = np.ascontiguousarray(np.asarray(ranges).view(np.int32).reshape(-1, 5))
+    if max_out is None:
+        n_units = int(np.maximum(0, (r[:, 4] - r[:, 3])).sum()) if len(r) else 0
+        max_out = max(1, n_units + len(r))
+        if splits_per_head is not None:
+            max_out = max(max_out, int(np.asarray(splits_per_head).sum()) + len(r))
+    out = np.zeros((max_out, 5), np.int32)
+    offsets = np.zeros(batch * hkv + 1, np.int32)
+    n_out = _i32()
+    sph = None if splits_per_head is None else np.ascontiguousarray(splits_per_head, np.int32)
+    tps = None if tokens_per_split is None else np.ascontiguousarray(tokens_per_split, np.int32)
+    _check(_lib.kvq_plan_splits(_hptr(r), r.shape[0], batch, hkv, heads_per_page, _hptr(sph),
+                                _hptr(tps), int(target_bytes), _hptr(out), max_out,
+                                ctypes.byref(n_out), _hptr(offsets)), "kvq_plan_splits")
+    return out[: n_out.value].copy(), offsets
+
+
+def aot_split_counts(budgets: np.ndarray, batch: int, total_work: int) -> np.ndarray:
+    b = np.ascontiguousarray(budgets, np.float32)
+    out = np.zeros(batch * b.shape[0], np.int32)
+    _check(_lib.kvq_aot_split_counts(_hptr(b), b.shape[0], batch, total_work, _hptr(out)),
+           "kvq_aot_split_counts")
+    return out
+
+
+def decode_occupancy(g: int):
+    per_cu, n_cu = _i32(), _i32()
+    _check(_lib.kvq_decode_occupancy(g, ctypes.byref(per_cu), ctypes.byref(n_cu)),
+           "kvq_decode_occupancy")
+    return per_cu.value, n_cu.value
+
+
+def status_string(status: int) -> str:
+    return _lib.kvq_status_string(status).decode()
+
+
+def raw_library():
+    """The loaded ctypes library (for tests of the ABI itself)."""
+    return _lib
+
+
+class BoundCall:
+    """A library call with its ctypes arguments marshalled once (for tight launch loops:
+    replaying a decode step costs one ctypes call per kernel).  The tensors passed at
+    construction must stay alive and in place."""
+
+    def __init__(self, name: str, args, keep=()):
+        self._fn = getattr(_lib, name)
+        self._args = tuple(args)
+        self._keep = keep
+        self._name = name
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise KvqError(st, self._name)
+
+
+def bind_decode_attn(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, table_kind: int,
+                     splits: torch.Tensor, part_o: torch.Tensor, part_lse: torch.Tensor,
+                     dev_err=None, stream=None) -> BoundCall:
+    assert q.is_contiguous() and tables.is_contiguous() and splits.is_contiguous()
+    batch, hq = q.shape[0], q.shape[1]
+    args = (cache.struct, _dptr(q), _DTYPES[q.dtype], batch, hq, hkv, _dptr(tables), tables.shape[0],
+            tables.shape[1], table_kind, _dptr(splits), splits.shape[0], _dptr(part_o),
+            _dptr(part_lse), _dptr(dev_err), _stream(stream))
+    return BoundCall("kvq_decode_attn", args, keep=(cache, q, tables, splits, part_o, part_lse, dev_err))
+
+
+def bind_lse_merge(part_o, part_lse, n_splits, split_offsets, batch, hq, hkv, out, out_lse=None,
+                   stream=None) -> BoundCall:
+    args = (_dptr(part_o), _dptr(part_lse), n_splits, _dptr(split_offsets), batch, hq, hkv, _dptr(out),
+            _DTYPES[out.dtype], _dptr(out_lse), _stream(stream))
+    return BoundCall("kvq_lse_merge", args, keep=(part_o, part_lse, split_offsets, out, out_lse))

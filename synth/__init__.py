@@ -167,6 +167,20 @@ class PageAllocator:
         return [(t, h, c, b, e) for h in heads for (c, b, e) in out if e > b]
 
 
+    def ranges_after_partition(self, t, heads):
+        """Token ranges of table t once its entries are stably grouped INT2, INT4,
+        FP16 (the order the phase-1 reorder produces): the caller's record of where
+        its tokens now sit."""
+        order = sorted(range(int(self.n_entries[t])), key=lambda e: self.entry_cls[t][e])
+        saved = (self.entry_cls[t], self.fill[t])
+        self.entry_cls[t] = [saved[0][e] for e in order]
+        self.fill[t] = [saved[1][e] for e in order]
+        try:
+            return self.ranges(t, heads)
+        finally:
+            self.entry_cls[t], self.fill[t] = saved
+
+
 def ranges_array(items) -> np.ndarray:
     return np.array(list(items), dtype=RANGE_DTYPE).reshape(-1)
 
@@ -366,6 +380,39 @@ def ragged_dead(seed=5, batch=64, lo=4096, hi=131072, device="cpu", dead_frac=0.
                     k, v, q, (0, n4, 0), alloc, calls, sentinel_slot=sentinel, dead_entries=dead,
                     head_tokens=head_tokens, head_budget=r_h.astype(np.float32),
                     note=f"lengths {int(lens.min())}..{int(lens.max())}, {dead_frac:.0%} dead")
+
+
+def subset(w: Workload, requests, device="cpu") -> Workload:
+    """The same page-table workload restricted to some requests (tables of those
+    requests, their source rows and queries), with a fresh allocator sized for them.
+    Entry structure per table is unchanged; physical page ids differ."""
+    assert w.kind == PAGES
+    tpr = w.hkv // w.heads_per_page
+    tabs = [b * tpr + i for b in requests for i in range(tpr)]
+    rows, calls, new_calls = [], [], []
+    for (t, flags, r, new_page) in w.calls:
+        if t in tabs:
+            calls.append((tabs.index(t), flags, r, new_page))
+    all_rows = np.unique(np.concatenate([c[2] for c in calls]))
+    remap = {int(r): i for i, r in enumerate(all_rows.tolist())}
+    for (t, flags, r, new_page) in calls:
+        new_calls.append((t, flags, np.array([remap[int(x)] for x in r.tolist()], np.int32), new_page))
+    idx = torch.as_tensor(all_rows, device=w.k.device, dtype=torch.long)
+    k = w.k.index_select(0, idx).to(device)
+    v = w.v.index_select(0, idx).to(device)
+    q = w.q[torch.as_tensor(list(requests), device=w.q.device)].to(device)
+    pages = [0, 0, 0]
+    for t in tabs:
+        for c in range(3):
+            n = int(w.alloc.tokens[t, c])
+            pages[c] += (n // PAGE if c == INT2 else -(-n // PAGE)) if n else 0
+    extra_fp16 = 0
+    if w.name == "hybrid_anchor":                      # anchor segments start on fresh pages
+        extra_fp16 = 3 * len(tabs)
+    n_pages = (pages[0], pages[1], pages[2] + extra_fp16)
+    alloc = PageAllocator(n_pages, w.heads_per_page, len(tabs), w.alloc.max_entries, w.seed + 1000)
+    return dataclasses.replace(w, batch=len(requests), k=k, v=v, q=q, n_pages=n_pages, alloc=alloc,
+                               calls=new_calls, note=w.note + f" (requests {list(requests)})")
 
 
 # ----------------------------------------------------------------------------

@@ -1,0 +1,147 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and its
+host-side logic (routing, split planning, ahead-of-time split counts, argument
+validation) behaves as include/kvq.h states.  No device work is enqueued here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    from mixed_precision_quantized_amd import kvq
+    return kvq
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kvq_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(kvq):
+    names = _declared()
+    assert len(names) >= 11, names
+    lib = kvq.raw_library()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in kvq.h but not exported"
+    assert set(names) == set(kvq.EXPORTED)
+
+
+def test_block_bytes(kvq):
+    assert [kvq.block_bytes(c) for c in (0, 1, 2, 3)] == [1536, 2560, 8192, 0]
+
+
+def test_route_matches_oracle_and_closed_form(kvq, orc):
+    r = np.random.default_rng(5)
+    for n in (0, 1, 31, 32, 33, 100, 5000):
+        flags = r.choice([0, 0, 1, 2], n).astype(np.uint8)
+        got = kvq.route_tokens(flags)
+        ref = orc.route(flags)
+        assert np.array_equal(got[0], ref[0]) and got[1:] == ref[1:]
+        assert got[1] == int((flags == 0).sum()) // 32
+
+
+def test_route_rejects_bad_flags(kvq):
+    with pytest.raises(kvq.KvqError):
+        kvq.route_tokens(np.array([0, 3], np.uint8))
+
+
+def _ranges(items, kvq):
+    return np.array(items, dtype=kvq.SPLIT_DTYPE)
+
+
+def test_plan_splits_cover_ranges_exactly(kvq):
+    r = np.random.default_rng(6)
+    for trial in range(20):
+        batch, hkv, H = 3, 4, 2
+        items = []
+        for t in range(batch * hkv // H):
+            for h in range(H):
+                n2 = int(r.integers(0, 8)) * 32
+                n4 = int(r.integers(0, 300))
+                if n2:
+                    items.append((t, h, 0, 0, n2))
+                if n4:
+                    items.append((t, h, 1, n2, n2 + n4))
+        rng = _ranges(items, kvq)
+        kw = [dict(target_bytes=int(r.integers(1000, 50000))), dict(tokens_per_split=[64, 17, 5])][trial % 2]
+        splits, off = kvq.plan_splits(rng, batch, hkv, H, **kw)
+        # every range covered exactly once, pieces in order, INT2 pieces on 32-token edges
+        for (t, h, c, b, e) in items:
+            mine = splits[(splits[:, 0] == t) & (splits[:, 1] == h) & (splits[:, 2] == c)]
+            assert mine[0, 3] == b and mine[-1, 4] == e
+            assert np.all(mine[1:, 3] == mine[:-1, 4]) and np.all(mine[:, 4] > mine[:, 3])
+            if c == 0:
+                assert np.all(mine[:, 3] % 32 == 0) and np.all(mine[:, 4] % 32 == 0)
+        # offsets: non-decreasing, partials of (b, kvh) contiguous
+        assert off[0] == 0 and off[-1] == len(splits) and np.all(np.diff(off) >= 0)
+        tpr = hkv // H
+        for pair in range(batch * hkv):
+            b, kvh = divmod(pair, hkv)
+            rows = splits[off[pair]:off[pair + 1]]
+            assert np.all(rows[:, 0] == b * tpr + kvh // H) and np.all(rows[:, 1] == kvh % H)
+
+
+def test_plan_splits_tokens_per_split_and_aot(kvq):
+    rng = _ranges([(0, 0, 0, 0, 192), (0, 0, 1, 192, 256)], kvq)
+    s, off = kvq.plan_splits(rng, 1, 1, 1, tokens_per_split=[64, 64, 64])
+    assert s.tolist() == [[0, 0, 0, 0, 64], [0, 0, 0, 64, 128], [0, 0, 0, 128, 192], [0, 0, 1, 192, 256]]
+    assert off.tolist() == [0, 4]
+    s, _ = kvq.plan_splits(rng, 1, 1, 1, splits_per_head=np.array([8], np.int32))
+    assert len(s) == 8 or len(s) == 7
+    budgets = (0.1 + 0.9 * np.arange(8) / 7).astype(np.float32)
+    c = kvq.aot_split_counts(budgets, 64, 2048).reshape(64, 8)
+    assert np.all(c == c[0]) and np.all(np.diff(c[0]) >= 0) and c[0, 0] >= 1
+    assert abs(int(c[0].sum()) - 32) <= 4                         # 2048 work groups / 64 requests
+    assert np.array_equal(kvq.aot_split_counts(budgets, 64, 2048),
+                          kvq.aot_split_counts(budgets, 64, 2048))  # independent of lengths
+
+
+def test_plan_splits_rejects_unsorted_and_misaligned(kvq):
+    with pytest.raises(kvq.KvqError):
+        kvq.plan_splits(_ranges([(1, 0, 1, 0, 5), (0, 0, 1, 0, 5)], kvq), 2, 1, 1)
+    with pytest.raises(kvq.KvqError):
+        kvq.plan_splits(_ranges([(0, 0, 0, 0, 40)], kvq), 1, 1, 1)
+
+
+def _cache_struct(kvq, head_dim=128, page=16, heads=1, n=(2, 2, 0)):
+    c = kvq._CacheC()
+    c.head_dim, c.page_size, c.heads_per_page = head_dim, page, heads
+    for i in range(3):
+        c.n_pages[i] = n[i]
+        c.pool[i] = 0x1000 if n[i] else 0          # never dereferenced: calls fail validation
+    c.sentinel_slot = -1
+    return c
+
+
+def test_validation_fails_before_any_launch(kvq):
+    lib = kvq.raw_library()
+    fake = ctypes.c_void_p(0x1000)
+    cases = [
+        (_cache_struct(kvq, head_dim=64), 1, 8, 8, 1, -2),     # head_dim 64: unsupported
+        (_cache_struct(kvq, page=32), 1, 8, 8, 1, -2),         # page size 32: unsupported
+        (_cache_struct(kvq), 1, 8, 3, 1, -1),                  # hq % hkv != 0
+        (_cache_struct(kvq), 1, 8, 8, 3, -1),                  # n_tables != batch*hkv/H
+        (_cache_struct(kvq), 1, 8 * 17, 8, 8, -2),             # g = 17 > 16
+        (_cache_struct(kvq, n=(3, 2, 0)), 1, 8, 8, 8, -1),     # odd INT2 pool
+    ]
+    for c, batch, hq, hkv, n_tables, want in cases:
+        st = lib.kvq_decode_attn(ctypes.byref(c), fake, 0, batch, hq, hkv, fake, n_tables, 4, 0, fake, 1,
+                                 fake, fake, None, None)
+        assert st == want, (st, want, kvq.raw_library().kvq_last_error())
+    c = _cache_struct(kvq)
+    assert lib.kvq_quantize_append(ctypes.byref(c), fake, fake, 7, 1, 128, 128, 0, None, None, 0, None,
+                                   None, 0, None, None, None, None) == -1       # bad dtype
+    assert lib.kvq_quantize_append(ctypes.byref(c), fake, fake, 0, 1, 128, 128, 3, None, None, 0, None,
+                                   None, 0, None, None, None, None) == -1       # NULL list
+    assert lib.kvq_reorder_pages(ctypes.byref(c), fake, 1, 9000, fake, None, None, None) == -2
+    assert lib.kvq_lse_merge(fake, fake, 1, fake, 1, 8, 3, fake, 0, None, None) == -1
+    assert lib.kvq_lse_merge(fake, fake, 1, fake, 1, 8, 8, fake, 9, None, None) == -1
+    assert b"dtype" in lib.kvq_last_error()
+    for st in (0, -1, -2, -3, -4, -5, 7):
+        assert kvq.status_string(st)
