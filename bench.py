@@ -69,7 +69,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--target-bytes", type=int, default=1 << 18, help="effective bytes per split")
-    ap.add_argument("--cpu-requests", type=int, default=4, help="requests in the CPU-oracle sample")
+    ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the CPU-oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -140,6 +142,14 @@ def main():
         for L in range(args.layers):
             dec[L]()
             mrg[L]()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: one 1 GiB device-to-device copy")
 
     for _ in range(args.warmup):
         step()

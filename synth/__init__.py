@@ -401,15 +401,14 @@ def subset(w: Workload, requests, device="cpu") -> Workload:
     k = w.k.index_select(0, idx).to(device)
     v = w.v.index_select(0, idx).to(device)
     q = w.q[torch.as_tensor(list(requests), device=w.q.device)].to(device)
-    pages = [0, 0, 0]
-    for t in tabs:
-        for c in range(3):
-            n = int(w.alloc.tokens[t, c])
-            pages[c] += (n // PAGE if c == INT2 else -(-n // PAGE)) if n else 0
-    extra_fp16 = 0
-    if w.name == "hybrid_anchor":                      # anchor segments start on fresh pages
-        extra_fp16 = 3 * len(tabs)
-    n_pages = (pages[0], pages[1], pages[2] + extra_fp16)
+    # Pool sizes: upper bounds from the flags alone (whatever the routing decides).
+    n2 = n4 = n16 = 0
+    for (_, flags, _, _) in new_calls:
+        c0, c1, c2 = (int((flags == c).sum()) for c in (INT2, INT4, FP16))
+        n2 += 2 * (c0 // GROUP)
+        n4 += -(-(c0 + c1) // PAGE) + 1
+        n16 += -(-c2 // PAGE) + 1
+    n_pages = (n2, n4, n16)
     alloc = PageAllocator(n_pages, w.heads_per_page, len(tabs), w.alloc.max_entries, w.seed + 1000)
     return dataclasses.replace(w, batch=len(requests), k=k, v=v, q=q, n_pages=n_pages, alloc=alloc,
                                calls=new_calls, note=w.note + f" (requests {list(requests)})")
