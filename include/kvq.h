@@ -77,16 +77,18 @@ enum {
  * page p's head h block starts at
  *   pool[c] + ((p - base_c) * heads_per_page + h) * kvq_block_bytes(c).
  * The three pools may be carved out of one allocation.  A slot id is
- * page * 16 + offset.  Head block layouts (little-endian, fp16 (scale, zero)):
- *   INT4 (2560 B): K codes [16 tok][64 B] @0 (channel c in byte c/2, even c in
- *     the low nibble); K meta [4 groups][16 tok][scale, zero] @1024; V codes
- *     @1280; V meta @2304.
- *   INT2 (1536 B): K codes [16 tok][32 B] @0 (channel c in byte c/4 at bit
- *     2*(c%4)); K per-channel meta of the page pair [64 ch][scale, zero] @512
- *     (even page: channels 0-63, odd page: 64-127); V codes [16 tok][32 B] @768;
- *     V meta [4 groups][16 tok][scale, zero] @1280.  INT2 pages are used in
- *     aligned pairs (even, even+1) holding one 32-token group; n_pages[KVQ_INT2]
- *     must be even.
+ * page * 16 + offset.  Head block layouts (little-endian, fp16 (scale, zero)).
+ * A code row is a sequence of 32-bit words; with b bits per code, word w holds
+ * channels w*32/b .. (w+1)*32/b - 1, the even-indexed of them in the low 16 bits
+ * and the odd-indexed in the high 16 bits, ascending, b bits each.
+ *   INT4 (2560 B): K codes [16 tok][64 B] @0; K meta [16 tok][4 groups][scale,
+ *     zero] @1024; V codes [16 tok][64 B] @1280; V meta [4 groups][16 tok]
+ *     [scale, zero] @2304.
+ *   INT2 (1536 B): K codes [16 tok][32 B] @0; K per-channel meta of the page
+ *     pair @512: 64 fp16 scales then 64 fp16 zeros @640 (even page: channels
+ *     0-63, odd page: 64-127); V codes [16 tok][32 B] @768; V meta [4 groups]
+ *     [16 tok][scale, zero] @1280.  INT2 pages are used in aligned pairs (even,
+ *     even+1) holding one 32-token group; n_pages[KVQ_INT2] must be even.
  *   FP16 (8192 B): K [16 tok][128] fp16 @0; V @4096.
  */
 typedef struct {

@@ -86,6 +86,12 @@ __device__ __forceinline__ const uint8_t *block_of(const DecodeArgs &a, int cls,
   return a.pool16 + ((page - a.n2 - a.n4) * a.heads + head) * (int64_t)kF16Bytes;
 }
 
+// Bit of the code of channel index k (0 .. 32/b - 1) inside its 32-bit word.
+template <int BITS>
+__device__ __forceinline__ int word_bit(int k) {
+  return (k & 1) * 16 + (k >> 1) * BITS;
+}
+
 // Logits of the GP (padded) query rows against one dequantized K row.
 template <int GP, int CLS>
 __device__ __forceinline__ void k_logits(const DecodeArgs &a, const uint8_t *blk, int off, int64_t page,
@@ -94,10 +100,11 @@ __device__ __forceinline__ void k_logits(const DecodeArgs &a, const uint8_t *blk
   for (int j = 0; j < GP; ++j) x[j] = 0.0f;
   if (CLS == KVQ_INT4) {
     const uint4 *row = reinterpret_cast<const uint4 *>(blk + kI4KC + off * 64);
+    const uint4 meta = *reinterpret_cast<const uint4 *>(blk + kI4KM + off * 16);
+    const uint32_t metas[4] = {meta.x, meta.y, meta.z, meta.w};
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
-      const uint32_t meta = *reinterpret_cast<const uint32_t *>(blk + kI4KM + (grp * kPage + off) * 4);
-      const float s = h2f(meta), z = h2f(meta >> 16);
+      const float s = h2f(metas[grp]), z = h2f(metas[grp] >> 16);
       const uint4 w = row[grp];
       const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -105,7 +112,7 @@ __device__ __forceinline__ void k_logits(const DecodeArgs &a, const uint8_t *blk
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
           const int ch = grp * 32 + wi * 8 + n;
-          const float kv = fmaf((float)((words[wi] >> (4 * n)) & 15u), s, z);
+          const float kv = fmaf((float)((words[wi] >> word_bit<4>(n)) & 15u), s, z);
 #pragma unroll
           for (int j = 0; j < GP; ++j) x[j] = fmaf(qs[j][ch], kv, x[j]);
         }
@@ -113,8 +120,8 @@ __device__ __forceinline__ void k_logits(const DecodeArgs &a, const uint8_t *blk
   } else if (CLS == KVQ_INT2) {
     const uint4 *row = reinterpret_cast<const uint4 *>(blk + kI2KC + off * 32);
     const int64_t even = page & ~1ll;
-    const uint8_t *m_even = block_of(a, KVQ_INT2, even, head) + kI2KM;
-    const uint8_t *m_odd = block_of(a, KVQ_INT2, even + 1, head) + kI2KM;
+    const uint8_t *m_even = block_of(a, KVQ_INT2, even, head);
+    const uint8_t *m_odd = block_of(a, KVQ_INT2, even + 1, head);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const uint4 w = row[half];
@@ -125,8 +132,9 @@ __device__ __forceinline__ void k_logits(const DecodeArgs &a, const uint8_t *blk
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
           const int ch = half * 64 + wi * 16 + n;
-          const uint32_t meta = *reinterpret_cast<const uint32_t *>(mb + (ch & 63) * 4);
-          const float kv = fmaf((float)((words[wi] >> (2 * n)) & 3u), h2f(meta), h2f(meta >> 16));
+          const float s = h2f(*reinterpret_cast<const uint16_t *>(mb + kI2KS + (ch & 63) * 2));
+          const float z = h2f(*reinterpret_cast<const uint16_t *>(mb + kI2KZ + (ch & 63) * 2));
+          const float kv = fmaf((float)((words[wi] >> word_bit<2>(n)) & 3u), s, z);
 #pragma unroll
           for (int j = 0; j < GP; ++j) x[j] = fmaf(qs[j][ch], kv, x[j]);
         }
@@ -148,21 +156,24 @@ __device__ __forceinline__ void k_logits(const DecodeArgs &a, const uint8_t *blk
   }
 }
 
-// This lane's two V channels (2l, 2l+1) of one token.
+// This lane's two V channels (2l, 2l+1) of one token: the even and odd members of
+// pair (l % (16/b)) of word l / (16/b).
 template <int CLS>
 __device__ __forceinline__ void v_pair(const uint8_t *blk, int off, int lane, float &v0, float &v1) {
   if (CLS == KVQ_INT4) {
-    const uint32_t byte = blk[kI4VC + off * 64 + lane];
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(blk + kI4VC + off * 64 + (lane >> 2) * 4);
     const uint32_t meta = *reinterpret_cast<const uint32_t *>(blk + kI4VM + ((lane >> 4) * kPage + off) * 4);
     const float s = h2f(meta), z = h2f(meta >> 16);
-    v0 = fmaf((float)(byte & 15u), s, z);
-    v1 = fmaf((float)(byte >> 4), s, z);
+    const int sh = (lane & 3) * 4;
+    v0 = fmaf((float)((w >> sh) & 15u), s, z);
+    v1 = fmaf((float)((w >> (16 + sh)) & 15u), s, z);
   } else if (CLS == KVQ_INT2) {
-    const uint32_t byte = blk[kI2VC + off * 32 + (lane >> 1)] >> (4 * (lane & 1));
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(blk + kI2VC + off * 32 + (lane >> 3) * 4);
     const uint32_t meta = *reinterpret_cast<const uint32_t *>(blk + kI2VM + ((lane >> 4) * kPage + off) * 4);
     const float s = h2f(meta), z = h2f(meta >> 16);
-    v0 = fmaf((float)(byte & 3u), s, z);
-    v1 = fmaf((float)((byte >> 2) & 3u), s, z);
+    const int sh = (lane & 7) * 2;
+    v0 = fmaf((float)((w >> sh) & 3u), s, z);
+    v1 = fmaf((float)((w >> (16 + sh)) & 3u), s, z);
   } else {
     const uint32_t w = *reinterpret_cast<const uint32_t *>(blk + kF16V + off * 256 + lane * 4);
     v0 = h2f(w);

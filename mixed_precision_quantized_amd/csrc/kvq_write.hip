@@ -140,27 +140,36 @@ __device__ __forceinline__ int page_class(const CacheView &c, int64_t p) {
 
 // ---------------------------------------------------------- per-token path ----
 
-// Quantizes one 128-channel row (this lane: channels 2l, 2l+1) in per-token
-// groups of 32 and writes codes + (scale, zero) of token `off` into a block.
+// Packs this lane's two codes (channels 2l and 2l+1 of a row) into the row's 32-bit
+// word: the word holds 32/BITS channels, so 16/BITS lanes share it; channel 2l is the
+// even member of its pair (low half), 2l+1 the odd one (high half).  The first lane of
+// each word stores it.
 template <int BITS>
+__device__ __forceinline__ void put_code_pair(uint8_t *row, uint32_t c0, uint32_t c1, int lane) {
+  constexpr int kLanesPerWord = 16 / BITS;
+  const int k = lane % kLanesPerWord;
+  uint32_t w = (c0 << (k * BITS)) | (c1 << (16 + k * BITS));
+#pragma unroll
+  for (int m = 1; m < kLanesPerWord; m <<= 1) w |= (uint32_t)__shfl_xor((int)w, m);
+  if (k == 0) *reinterpret_cast<uint32_t *>(row + (lane / kLanesPerWord) * 4) = w;
+}
+
+// Quantizes one 128-channel row (this lane: channels 2l, 2l+1) in per-token groups
+// of 32 and writes codes + (scale, zero) of token `off` into a block; the metadata of
+// (group g, token off) is entry off*4 + g (TOKEN_MAJOR) or g*16 + off.
+template <int BITS, bool TOKEN_MAJOR>
 __device__ __forceinline__ void put_token_row(uint8_t *blk, int codes_at, int meta_at, int off,
                                               float x0, float x1, int lane) {
   constexpr float kLevels = (float)((1 << BITS) - 1);
   float mn = fminf(canon(x0), canon(x1)), mx = fmaxf(canon(x0), canon(x1));
   group16_minmax(mn, mx);
   const Quant q = quant_params(mn, mx, kLevels);
-  const uint32_t c0 = quant_code(x0, q, kLevels), c1 = quant_code(x1, q, kLevels);
-  if (BITS == 4) {
-    blk[codes_at + off * 64 + lane] = (uint8_t)(c0 | (c1 << 4));
-  } else {
-    // Channels 4j..4j+3 share byte j = lane / 2: even lane low nibble, odd lane high.
-    const uint32_t nib = c0 | (c1 << 2);
-    const uint32_t other = (uint32_t)__shfl_xor((int)nib, 1);
-    if ((lane & 1) == 0) blk[codes_at + off * 32 + (lane >> 1)] = (uint8_t)(nib | (other << 4));
-  }
+  put_code_pair<BITS>(blk + codes_at + off * (kHeadDim * BITS / 8), quant_code(x0, q, kLevels),
+                      quant_code(x1, q, kLevels), lane);
   if ((lane & 15) == 0) {
     const int g = lane >> 4;
-    *reinterpret_cast<uint32_t *>(blk + meta_at + (g * kPage + off) * 4) = q.sb | (q.zb << 16);
+    const int entry = TOKEN_MAJOR ? off * 4 + g : g * kPage + off;
+    *reinterpret_cast<uint32_t *>(blk + meta_at + entry * 4) = q.sb | (q.zb << 16);
   }
 }
 
@@ -190,8 +199,8 @@ __global__ void __launch_bounds__(256) append_tokens_kernel(
   const float v0 = load_src(v, dtype, src), v1 = load_src(v, dtype, src + 1);
   if (is4) {
     uint8_t *blk = c.pool4 + ((page - c.n2) * c.heads + head) * (int64_t)kI4Bytes;
-    put_token_row<4>(blk, kI4KC, kI4KM, off, k0, k1, lane);
-    put_token_row<4>(blk, kI4VC, kI4VM, off, v0, v1, lane);
+    put_token_row<4, true>(blk, kI4KC, kI4KM, off, k0, k1, lane);
+    put_token_row<4, false>(blk, kI4VC, kI4VM, off, v0, v1, lane);
   } else {
     uint8_t *blk = c.pool16 + ((page - c.n2 - c.n4) * c.heads + head) * (int64_t)kF16Bytes;
     *reinterpret_cast<uint32_t *>(blk + kF16K + off * 256 + lane * 4) =
@@ -246,24 +255,23 @@ __global__ void __launch_bounds__(64) append_int2_kernel(
   }
   const Quant q0 = quant_params(mn0, mx0, 3.0f), q1 = quant_params(mn1, mx1, 3.0f);
 #pragma unroll
-  for (int t = 0; t < kGroup; ++t) {
-    const uint32_t nib = quant_code(kx[t][0], q0, 3.0f) | (quant_code(kx[t][1], q1, 3.0f) << 2);
-    const uint32_t other = (uint32_t)__shfl_xor((int)nib, 1);
-    if ((lane & 1) == 0) blk[t >> 4][kI2KC + (t & 15) * 32 + (lane >> 1)] = (uint8_t)(nib | (other << 4));
-  }
+  for (int t = 0; t < kGroup; ++t)
+    put_code_pair<2>(blk[t >> 4] + kI2KC + (t & 15) * 32, quant_code(kx[t][0], q0, 3.0f),
+                     quant_code(kx[t][1], q1, 3.0f), lane);
   {
-    // Channel c's (scale, zero): even page for c < 64, odd page for c >= 64.
-    const int ch = 2 * lane;
-    uint8_t *m = blk[ch >> 6] + kI2KM + (ch & 63) * 4;
-    *reinterpret_cast<uint2 *>(m) = make_uint2(q0.sb | (q0.zb << 16), q1.sb | (q1.zb << 16));
+    // Channels 2l, 2l+1: scales and zeros of the even page (c < 64) or odd page.
+    uint8_t *m = blk[lane >> 5];
+    const int at = (lane & 31) * 4;
+    *reinterpret_cast<uint32_t *>(m + kI2KS + at) = q0.sb | (q1.sb << 16);
+    *reinterpret_cast<uint32_t *>(m + kI2KZ + at) = q0.zb | (q1.zb << 16);
   }
 
   // V, per token.
 #pragma unroll 4
   for (int t = 0; t < kGroup; ++t) {
     const int64_t src = (int64_t)rows[t] * row_stride + (int64_t)head * head_stride + 2 * lane;
-    put_token_row<2>(blk[t >> 4], kI2VC, kI2VM, t & 15, load_src(v, dtype, src),
-                     load_src(v, dtype, src + 1), lane);
+    put_token_row<2, false>(blk[t >> 4], kI2VC, kI2VM, t & 15, load_src(v, dtype, src),
+                            load_src(v, dtype, src + 1), lane);
   }
 }
 

@@ -120,19 +120,43 @@ void orc_quantize(const float *x, int32_t n, int64_t stride, int32_t bits,
 /* ------------------------------------------------------------------------ */
 /* Byte layout of one head block of a page (written specification)          */
 /* ------------------------------------------------------------------------ */
-/* INT4 (2560 B): K codes [16 tok][64 B] at 0 (channel c in byte c/2, even c in
- *   the low nibble); K meta [4 groups][16 tok][scale, zero fp16] at 1024;
- *   V codes at 1280; V meta at 2304.
- * INT2 (1536 B): K codes [16 tok][32 B] at 0 (channel c in byte c/4, bits
- *   2*(c%4)); K per-channel meta of the page pair at 512: the even page of the
- *   pair holds channels 0-63, the odd page 64-127, [64][scale, zero];
- *   V codes [16 tok][32 B] at 768; V meta [4][16][scale, zero] at 1280.
+/* Code rows are sequences of little-endian 32-bit words.  With b bits per code,
+ * word w holds the 32/b channels w*32/b ... (w+1)*32/b - 1; among them the
+ * even-indexed ones fill the low 16 bits and the odd-indexed ones the high 16
+ * bits, each half in ascending channel order, b bits per channel.
+ * INT4 (2560 B): K codes [16 tok][64 B] at 0; K meta [16 tok][4 groups][scale,
+ *   zero fp16] at 1024; V codes [16][64 B] at 1280; V meta [4 groups][16 tok]
+ *   [scale, zero] at 2304.
+ * INT2 (1536 B): K codes [16 tok][32 B] at 0; K per-channel meta of the page
+ *   pair at 512: 64 fp16 scales then 64 fp16 zeros (the even page of the pair
+ *   holds channels 0-63, the odd page 64-127); V codes [16 tok][32 B] at 768;
+ *   V meta [4 groups][16 tok][scale, zero] at 1280.
  * FP16 (8192 B): K [16 tok][128] fp16 at 0; V at 4096. */
 enum {
     I4_KC = 0, I4_KM = 1024, I4_VC = 1280, I4_VM = 2304, I4_BYTES = 2560,
-    I2_KC = 0, I2_KM = 512, I2_VC = 768, I2_VM = 1280, I2_BYTES = 1536,
+    I2_KC = 0, I2_KS = 512, I2_KZ = 640, I2_VC = 768, I2_VM = 1280, I2_BYTES = 1536,
     F16_K = 0, F16_V = 4096, F16_BYTES = 8192
 };
+
+/* Bit position of channel ch inside its code row (b bits per code). */
+static int code_bit(int ch, int bits)
+{
+    int per_word = 32 / bits, k = ch % per_word;
+    return (ch / per_word) * 32 + (k % 2) * 16 + (k / 2) * bits;
+}
+
+static int get_code(const uint8_t *row, int ch, int bits)
+{
+    int bit = code_bit(ch, bits);
+    return (row[bit / 8] >> (bit % 8)) & ((1 << bits) - 1);
+}
+
+static void put_code(uint8_t *row, int ch, int bits, int code)
+{
+    int bit = code_bit(ch, bits);
+    uint8_t mask = (uint8_t)(((1 << bits) - 1) << (bit % 8));
+    row[bit / 8] = (uint8_t)((row[bit / 8] & ~mask) | (code << (bit % 8)));
+}
 
 int64_t orc_block_bytes(int32_t cls)
 {
@@ -225,23 +249,19 @@ int orc_route(const uint8_t *flags, int32_t n, uint8_t *cls_out,
 /* Write path                                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Per-token groups of 32 channels (INT4 K and V, INT2 V). */
-static void put_token_groups(uint8_t *blk, int codes_at, int meta_at, int bits,
+/* Per-token groups of 32 channels (INT4 K and V, INT2 V); the metadata of
+ * (group g, token off) sits at meta_at + 4 * (token_major ? off*4 + g : g*16 + off). */
+static void put_token_groups(uint8_t *blk, int codes_at, int meta_at, int token_major, int bits,
                              int off, const float *row)
 {
-    const int per_byte = 8 / bits, row_bytes = D * bits / 8;
+    const int row_bytes = D * bits / 8;
     for (int g = 0; g < D / GRP; ++g) {
         uint8_t codes[GRP];
         uint16_t s, z;
         orc_quantize(row + g * GRP, GRP, 1, bits, codes, &s, &z);
-        for (int i = 0; i < GRP; ++i) {
-            int ch = g * GRP + i;
-            uint8_t *b = blk + codes_at + off * row_bytes + ch / per_byte;
-            int shift = (ch % per_byte) * bits;
-            uint8_t mask = (uint8_t)(((1 << bits) - 1) << shift);
-            *b = (uint8_t)((*b & ~mask) | (codes[i] << shift));
-        }
-        uint8_t *m = blk + meta_at + (g * PAGE + off) * 4;
+        for (int i = 0; i < GRP; ++i)
+            put_code(blk + codes_at + off * row_bytes, g * GRP + i, bits, codes[i]);
+        uint8_t *m = blk + meta_at + 4 * (token_major ? off * 4 + g : g * PAGE + off);
         put_u16(m, s);
         put_u16(m + 2, z);
     }
@@ -266,8 +286,8 @@ int orc_append(orc_cache *c, const void *k, const void *v, int32_t dtype,
             uint8_t *blk = block_ptr(c, page, h);
             load_row(kr, k, dtype, rows4[i], row_stride, head_stride, h);
             load_row(vr, v, dtype, rows4[i], row_stride, head_stride, h);
-            put_token_groups(blk, I4_KC, I4_KM, 4, off, kr);
-            put_token_groups(blk, I4_VC, I4_VM, 4, off, vr);
+            put_token_groups(blk, I4_KC, I4_KM, 1, 4, off, kr);
+            put_token_groups(blk, I4_VC, I4_VM, 0, 4, off, vr);
         }
     }
 
@@ -286,19 +306,15 @@ int orc_append(orc_cache *c, const void *k, const void *v, int32_t dtype,
                 uint8_t codes[GRP];
                 uint16_t s, z;
                 orc_quantize(col, GRP, 1, 2, codes, &s, &z);
-                for (int t = 0; t < GRP; ++t) {
-                    uint8_t *b = blk[t / PAGE] + I2_KC + (t % PAGE) * 32 + ch / 4;
-                    int shift = (ch % 4) * 2;
-                    *b = (uint8_t)((*b & ~(3 << shift)) | (codes[t] << shift));
-                }
-                uint8_t *m = blk[ch / 64] + I2_KM + (ch % 64) * 4;
-                put_u16(m, s);
-                put_u16(m + 2, z);
+                for (int t = 0; t < GRP; ++t)
+                    put_code(blk[t / PAGE] + I2_KC + (t % PAGE) * 32, ch, 2, codes[t]);
+                put_u16(blk[ch / 64] + I2_KS + (ch % 64) * 2, s);
+                put_u16(blk[ch / 64] + I2_KZ + (ch % 64) * 2, z);
             }
             /* V: per-token groups. */
             for (int t = 0; t < GRP; ++t) {
                 load_row(vr, v, dtype, rows[t], row_stride, head_stride, h);
-                put_token_groups(blk[t / PAGE], I2_VC, I2_VM, 2, t % PAGE, vr);
+                put_token_groups(blk[t / PAGE], I2_VC, I2_VM, 0, 2, t % PAGE, vr);
             }
         }
     }
@@ -357,10 +373,9 @@ int orc_reorder(const orc_cache *c, int32_t *tables, int32_t n_tables,
 /* Dequantization of one token (fp64, exact)                                 */
 /* ------------------------------------------------------------------------ */
 
-static double meta_deq(const uint8_t *m, int code)
+static double deq(uint16_t s, uint16_t z, int code)
 {
-    double s = orc_f16_value(get_u16(m)), z = orc_f16_value(get_u16(m + 2));
-    return z + code * s;
+    return orc_f16_value(z) + code * orc_f16_value(s);
 }
 
 int orc_token(const orc_cache *c, int32_t page, int32_t off, int32_t head,
@@ -373,17 +388,17 @@ int orc_token(const orc_cache *c, int32_t page, int32_t off, int32_t head,
     for (int ch = 0; ch < D; ++ch) {
         int g = ch / GRP;
         if (cls == ORC_INT4) {
-            int kc = (blk[I4_KC + off * 64 + ch / 2] >> ((ch & 1) * 4)) & 15;
-            int vc = (blk[I4_VC + off * 64 + ch / 2] >> ((ch & 1) * 4)) & 15;
-            k[ch] = meta_deq(blk + I4_KM + (g * PAGE + off) * 4, kc);
-            v[ch] = meta_deq(blk + I4_VM + (g * PAGE + off) * 4, vc);
+            const uint8_t *km = blk + I4_KM + (off * 4 + g) * 4;
+            const uint8_t *vm = blk + I4_VM + (g * PAGE + off) * 4;
+            k[ch] = deq(get_u16(km), get_u16(km + 2), get_code(blk + I4_KC + off * 64, ch, 4));
+            v[ch] = deq(get_u16(vm), get_u16(vm + 2), get_code(blk + I4_VC + off * 64, ch, 4));
         } else if (cls == ORC_INT2) {
             int32_t even = page & ~1;               /* INT2 ids start at 0 */
             const uint8_t *mblk = block_ptr(c, even + ch / 64, head);
-            int kc = (blk[I2_KC + off * 32 + ch / 4] >> ((ch % 4) * 2)) & 3;
-            int vc = (blk[I2_VC + off * 32 + ch / 4] >> ((ch % 4) * 2)) & 3;
-            k[ch] = meta_deq(mblk + I2_KM + (ch % 64) * 4, kc);
-            v[ch] = meta_deq(blk + I2_VM + (g * PAGE + off) * 4, vc);
+            const uint8_t *vm = blk + I2_VM + (g * PAGE + off) * 4;
+            k[ch] = deq(get_u16(mblk + I2_KS + (ch % 64) * 2), get_u16(mblk + I2_KZ + (ch % 64) * 2),
+                        get_code(blk + I2_KC + off * 32, ch, 2));
+            v[ch] = deq(get_u16(vm), get_u16(vm + 2), get_code(blk + I2_VC + off * 32, ch, 2));
         } else {
             k[ch] = orc_f16_value(get_u16(blk + F16_K + off * 256 + ch * 2));
             v[ch] = orc_f16_value(get_u16(blk + F16_V + off * 256 + ch * 2));

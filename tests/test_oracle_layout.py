@@ -52,13 +52,12 @@ def test_int4_layout_golden(orc):
     assert not c.pool_bytes(orc.INT4)[:2560].any()
     assert bytes(blk[192:256]) == g["int4 token_off=3 kcodes@192"]
     assert bytes(blk[1472:1536]) == g["int4 token_off=3 vcodes@1472"]
-    for off in (1036, 1100, 1164, 1228):
-        assert bytes(blk[off:off + 4]) == g["int4 token_off=3 kmeta@1036,1100,1164,1228"]
+    assert bytes(blk[1072:1088]) == g["int4 token_off=3 kmeta@1072"]
     for off in (2316, 2380, 2444, 2508):
         assert bytes(blk[off:off + 4]) == g["int4 token_off=3 vmeta@2316,2380,2444,2508"]
     written = np.zeros(2560, bool)
-    written[192:256] = written[1472:1536] = True
-    for off in (1036, 1100, 1164, 1228, 2316, 2380, 2444, 2508):
+    written[192:256] = written[1472:1536] = written[1072:1088] = True
+    for off in (2316, 2380, 2444, 2508):
         written[off:off + 4] = True
     assert not blk[~written].any(), "bytes of other tokens must stay untouched"
 
@@ -82,7 +81,8 @@ def test_int2_layout_golden(orc):
         for gi in range(4):
             m = 1280 + (gi * 16 + off) * 4
             assert bytes(blk[m:m + 4]) == g["int2 vmeta"]
-    assert bytes(even[512:768]) == g["int2 kmeta"] and bytes(odd[512:768]) == g["int2 kmeta"]
+    for page in (even, odd):
+        assert bytes(page[512:640]) == g["int2 kscales"] and bytes(page[640:768]) == g["int2 kzeros"]
 
 
 def test_fp16_layout_golden(orc):
