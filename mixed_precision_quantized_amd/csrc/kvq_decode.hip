@@ -1,23 +1,39 @@
-// Decode path of libkvq for gfx950: split-K decode attention read directly from
-// the INT2 / INT4 / FP16 pools (dequantization inside the attention loop), and
-// the log-sum-exp merge of the split partials.
+// Decode path of libkvq for gfx950: split-K GQA decode attention read directly from
+// the INT2 / INT4 / FP16 pools (dequantization inside the attention loop), and the
+// log-sum-exp merge of the split partials.
 //
-// TriAxialKV key design 4 (phase 2): every split covers tokens of one precision,
-// so the loop over a split has no precision branch; splits are merged by a
-// global log-sum-exp reduction.  HyQuant background / Algorithm 3: online
-// softmax state (m, l, acc) with O = acc / l; the g query heads that share a KV
-// head are processed together (GQA packing); the FP16 anchor segments are more
-// splits of the same launch.  IntentKV layout-preserving eviction: a slot-map
-// entry equal to the sentinel slot contributes nothing.
+// Method (pages): TriAxialKV key design 4, phase 2 -- every split covers tokens of one
+// precision, so a split's loop has no precision branch, and splits are merged by a
+// global log-sum-exp reduction.  HyQuant background / Algorithm 3 -- online softmax
+// state (m, l, acc) with O = acc / l; the g query heads sharing a KV head are packed
+// together (GQA); the FP16 anchor segments are more splits of the same launch.
+// IntentKV layout-preserving eviction -- a slot-map entry equal to the sentinel slot
+// contributes nothing.
 //
-// Reference kernel (one 64-lane wavefront per split):
-//   - tokens are taken 64 at a time, lane = token: each lane dequantizes its own
-//     K row and forms the g logits in fp32 (q pre-scaled by log2(e)/sqrt(128) so
-//     the softmax runs on exp2);
-//   - chunk maximum and sum by wavefront butterflies; the running (m, l, acc)
-//     is rescaled only when the maximum moves;
-//   - P V with lane = channel pair: each lane dequantizes its two channels of
-//     every V row of the chunk and accumulates g outputs.
+// Kernel (one 64-lane wavefront per split; lane l = 16*lb + lr):
+//   QK^T on MFMA (v_mfma_f32_16x16x32_f16).  Rows of the 16x16 tile are (query j',
+//   channel group i) = 4j' + i; the query operand is block-diagonal (row (j', i) only
+//   sees channels of group i), so the result keeps the four per-group partial dot
+//   products of every (query, token) apart and the per-token INT4 group scales are
+//   applied after the product: lane (lr, lb) ends with query lb's four group partials
+//   of token lr.  q enters unscaled (bf16 / fp16 queries are exact in fp16) and the
+//   softmax scale is applied to the fp32 result.  K codes enter as exact centered
+//   fp16 values (c - 8 for INT4, c - 2 for INT2; see below), and the zero term
+//   (z + 8 s) * sum(q) is added per group.  INT2 K has per-channel scales: the code
+//   operand becomes s * (c - 2), exact in fp16 because c - 2 is in {-2, -1, 0, 1},
+//   and the zero term sum q (z + 2 s) of the 32-token pair enters through the
+//   accumulator start.
+//   Online softmax in base 2 per query with 16-lane DPP row reductions; the running
+//   state is rescaled only when a row maximum grows.
+//   P V on MFMA.  Rows (query j', group i); the weight operand is p * s (fp16) for
+//   group i, the value operand is the centered code (c - 8 for INT4, c - 2 for INT2,
+//   exact in fp16), and the zero term p * (z + 8 s) (resp. z + 2 s) is accumulated
+//   with v_dot2_f32_f16.  Centering keeps the fp32 accumulator of the same magnitude
+//   as the result (an uncentered 0..15 code would leave a large positive sum that the
+//   zero term must cancel).  Lane (lr, lb) ends with query lb's outputs for channels
+//   8 lr .. 8 lr + 7.
+//   Tokens come 32 at a time (two 16-token pages, or one INT2 page pair); the loads of
+//   the next 32 tokens are issued before the current ones are computed.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -29,6 +45,11 @@
 namespace kvq {
 namespace {
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -36,27 +57,75 @@ __device__ __forceinline__ void report(int32_t *err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }
 
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ h8 h8_of(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u4v v = {a, b, c, d};
+  return __builtin_bit_cast(h8, v);
+}
+__device__ __forceinline__ h8 h8_of(uint4 v) { return h8_of(v.x, v.y, v.z, v.w); }
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float dot2(h2 a, h2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
 __device__ __forceinline__ float h2f(uint32_t bits) {
   return __half2float(__ushort_as_half((unsigned short)(bits & 0xffffu)));
 }
 
-__device__ __forceinline__ float load_q(const void *q, int32_t dtype, int64_t idx) {
-  if (dtype == KVQ_F32) return static_cast<const float *>(q)[idx];
-  const uint32_t h = static_cast<const uint16_t *>(q)[idx];
-  return dtype == KVQ_BF16 ? __uint_as_float(h << 16) : h2f(h);
+// Row (16-lane) reductions by DPP row rotations; every lane of the row gets the result.
+template <int N>
+__device__ __forceinline__ float dpp_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_ror<8>(x));
+  x = fmaxf(x, dpp_ror<4>(x));
+  x = fmaxf(x, dpp_ror<2>(x));
+  return fmaxf(x, dpp_ror<1>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_ror<8>(x);
+  x += dpp_ror<4>(x);
+  x += dpp_ror<2>(x);
+  return x + dpp_ror<1>(x);
+}
+// Sum over the 4 lanes of a quad (quad_perm xor 1, then xor 2).
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+// ------------------------------------------------------------ code -> fp16 ----
+
+// Exact centered fp16 codes.  A code OR-ed into the low mantissa bits of a power of
+// two gives 2^e + c exactly (1024 + c for bits 0-3 / 0-1, 256 + c for bits 2-3,
+// 64 + c for bits 4-7 / 4-5, 16 + c for bits 6-7); one packed fp16 subtraction of
+// 2^e + center then leaves c - center, exact in fp16.
+
+// One INT4 word (channels 8w..8w+7, even ones in the low half) -> c - 8 of the 8
+// channels in channel order.
+__device__ __forceinline__ h8 k4_word(uint32_t x) {
+  const uint32_t y = x >> 8;
+  const h2 lo = {(_Float16)1032.0f, (_Float16)1032.0f}, hi = {(_Float16)72.0f, (_Float16)72.0f};
+  return h8_of(as_u32(as_h2((x & 0x000F000Fu) | 0x64006400u) - lo), as_u32(as_h2((x & 0x00F000F0u) | 0x54005400u) - hi),
+               as_u32(as_h2((y & 0x000F000Fu) | 0x64006400u) - lo), as_u32(as_h2((y & 0x00F000F0u) | 0x54005400u) - hi));
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+// Eight channels of an INT2 word: `x` holds them in bits 0-7 (even channels) and
+// 16-23 (odd channels) -> c - 2 in channel order.
+__device__ __forceinline__ h8 k2_byte(uint32_t x) {
+  return h8_of(as_u32(as_h2((x & 0x00030003u) | 0x64006400u) - h2{(_Float16)1026.0f, (_Float16)1026.0f}),
+               as_u32(as_h2((x & 0x000C000Cu) | 0x5C005C00u) - h2{(_Float16)258.0f, (_Float16)258.0f}),
+               as_u32(as_h2((x & 0x00300030u) | 0x54005400u) - h2{(_Float16)66.0f, (_Float16)66.0f}),
+               as_u32(as_h2((x & 0x00C000C0u) | 0x4C004C00u) - h2{(_Float16)18.0f, (_Float16)18.0f}));
 }
+
+// Byte b of token word wa in bits 0-7 and of token word wb in bits 16-23.
+__device__ __forceinline__ uint32_t pair_bytes(uint32_t wa, uint32_t wb, int b) {
+  return ((wa >> (8 * b)) & 0xffu) | (((wb >> (8 * b)) & 0xffu) << 16);
+}
+
+// ------------------------------------------------------------------ args ------
 
 struct DecodeArgs {
   int32_t heads, n2, n4, n16;
@@ -65,7 +134,7 @@ struct DecodeArgs {
   const void *q;
   int32_t q_dtype, batch, hq, hkv, g, tpr;
   const int32_t *tables;
-  int32_t n_tables, max_entries, kind;
+  int32_t n_tables, max_entries;
   const kvq_split *splits;
   int32_t n_splits;
   float *part_o, *part_lse;
@@ -80,206 +149,435 @@ __device__ __forceinline__ int page_class(const DecodeArgs &a, int64_t p) {
   return -1;
 }
 
-__device__ __forceinline__ const uint8_t *block_of(const DecodeArgs &a, int cls, int64_t page, int head) {
-  if (cls == KVQ_INT2) return a.pool2 + (page * a.heads + head) * (int64_t)kI2Bytes;
-  if (cls == KVQ_INT4) return a.pool4 + ((page - a.n2) * a.heads + head) * (int64_t)kI4Bytes;
+template <int CLS>
+__device__ __forceinline__ const uint8_t *block_of(const DecodeArgs &a, int64_t page, int head) {
+  if (CLS == KVQ_INT2) return a.pool2 + (page * a.heads + head) * (int64_t)kI2Bytes;
+  if (CLS == KVQ_INT4) return a.pool4 + ((page - a.n2) * a.heads + head) * (int64_t)kI4Bytes;
   return a.pool16 + ((page - a.n2 - a.n4) * a.heads + head) * (int64_t)kF16Bytes;
 }
 
-// Bit of the code of channel index k (0 .. 32/b - 1) inside its 32-bit word.
-template <int BITS>
-__device__ __forceinline__ int word_bit(int k) {
-  return (k & 1) * 16 + (k >> 1) * BITS;
-}
-
-// Logits of the GP (padded) query rows against one dequantized K row.
-template <int GP, int CLS>
-__device__ __forceinline__ void k_logits(const DecodeArgs &a, const uint8_t *blk, int off, int64_t page,
-                                         int head, const float (*qs)[kHeadDim], float *x) {
-#pragma unroll
-  for (int j = 0; j < GP; ++j) x[j] = 0.0f;
-  if (CLS == KVQ_INT4) {
-    const uint4 *row = reinterpret_cast<const uint4 *>(blk + kI4KC + off * 64);
-    const uint4 meta = *reinterpret_cast<const uint4 *>(blk + kI4KM + off * 16);
-    const uint32_t metas[4] = {meta.x, meta.y, meta.z, meta.w};
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const float s = h2f(metas[grp]), z = h2f(metas[grp] >> 16);
-      const uint4 w = row[grp];
-      const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi)
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const int ch = grp * 32 + wi * 8 + n;
-          const float kv = fmaf((float)((words[wi] >> word_bit<4>(n)) & 15u), s, z);
-#pragma unroll
-          for (int j = 0; j < GP; ++j) x[j] = fmaf(qs[j][ch], kv, x[j]);
-        }
-    }
-  } else if (CLS == KVQ_INT2) {
-    const uint4 *row = reinterpret_cast<const uint4 *>(blk + kI2KC + off * 32);
-    const int64_t even = page & ~1ll;
-    const uint8_t *m_even = block_of(a, KVQ_INT2, even, head);
-    const uint8_t *m_odd = block_of(a, KVQ_INT2, even + 1, head);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint4 w = row[half];
-      const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-      const uint8_t *mb = half ? m_odd : m_even;  // channels 64*half .. 64*half+63
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi)
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-          const int ch = half * 64 + wi * 16 + n;
-          const float s = h2f(*reinterpret_cast<const uint16_t *>(mb + kI2KS + (ch & 63) * 2));
-          const float z = h2f(*reinterpret_cast<const uint16_t *>(mb + kI2KZ + (ch & 63) * 2));
-          const float kv = fmaf((float)((words[wi] >> word_bit<2>(n)) & 3u), s, z);
-#pragma unroll
-          for (int j = 0; j < GP; ++j) x[j] = fmaf(qs[j][ch], kv, x[j]);
-        }
-    }
-  } else {
-    const uint4 *row = reinterpret_cast<const uint4 *>(blk + kF16K + off * 256);
-#pragma unroll 4
-    for (int wi = 0; wi < 16; ++wi) {
-      const uint4 w = row[wi];
-      const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int ch = wi * 8 + n;
-        const float kv = h2f(words[n >> 1] >> (16 * (n & 1)));
-#pragma unroll
-        for (int j = 0; j < GP; ++j) x[j] = fmaf(qs[j][ch], kv, x[j]);
-      }
-    }
-  }
-}
-
-// This lane's two V channels (2l, 2l+1) of one token: the even and odd members of
-// pair (l % (16/b)) of word l / (16/b).
 template <int CLS>
-__device__ __forceinline__ void v_pair(const uint8_t *blk, int off, int lane, float &v0, float &v1) {
-  if (CLS == KVQ_INT4) {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(blk + kI4VC + off * 64 + (lane >> 2) * 4);
-    const uint32_t meta = *reinterpret_cast<const uint32_t *>(blk + kI4VM + ((lane >> 4) * kPage + off) * 4);
-    const float s = h2f(meta), z = h2f(meta >> 16);
-    const int sh = (lane & 3) * 4;
-    v0 = fmaf((float)((w >> sh) & 15u), s, z);
-    v1 = fmaf((float)((w >> (16 + sh)) & 15u), s, z);
-  } else if (CLS == KVQ_INT2) {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(blk + kI2VC + off * 32 + (lane >> 3) * 4);
-    const uint32_t meta = *reinterpret_cast<const uint32_t *>(blk + kI2VM + ((lane >> 4) * kPage + off) * 4);
-    const float s = h2f(meta), z = h2f(meta >> 16);
-    const int sh = (lane & 7) * 2;
-    v0 = fmaf((float)((w >> sh) & 3u), s, z);
-    v1 = fmaf((float)((w >> (16 + sh)) & 3u), s, z);
-  } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(blk + kF16V + off * 256 + lane * 4);
-    v0 = h2f(w);
-    v1 = h2f(w >> 16);
-  }
+__device__ __forceinline__ int64_t class_first_page(const DecodeArgs &a) {
+  return CLS == KVQ_INT2 ? 0 : CLS == KVQ_INT4 ? a.n2 : (int64_t)a.n2 + a.n4;
 }
 
-template <int GP, int CLS>
-__device__ void decode_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, float (*qs)[kHeadDim],
-                             float (*ps)[64], const uint8_t **tok_blk, int *tok_off) {
-  const int lane = threadIdx.x;
-  const int32_t *trow = a.tables + (int64_t)sp.table * a.max_entries;
-  float m[GP], l[GP], acc0[GP], acc1[GP];
-#pragma unroll
-  for (int j = 0; j < GP; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.0f;
-    acc0[j] = acc1[j] = 0.0f;
+template <int QT>
+struct Lds {
+  float q[4 * QT][kHeadDim];         // queries (rows beyond g are zero)
+  _Float16 p[QT][4][32];             // softmax weights of the current 32 tokens
+};
+
+// ------------------------------------------------------------- per window -----
+
+// What one lane loads for 32 tokens (the next window is loaded while the current one
+// is computed).
+struct Win {
+  uint4 k[2][4];     // K codes: [page half][up to 64 B]
+  uint4 km[2];       // INT4 K meta of token lr (per page half)
+  uint4 ks, kz;      // INT2 per-channel scales / zeros of channels 8 lr .. 8 lr + 7
+  uint4 kg[4];       // INT2 per-channel scales of channels 32 lb .. 32 lb + 31
+  uint4 v[8];        // V words / FP16 rows of this lane's 8 tokens
+  uint4 vm[2];       // V meta (scale, zero) of this lane's 8 tokens, group lr & 3
+  uint32_t ok;       // bit h: page half h exists and has the right class
+  uint32_t live;     // bit h: the QK token T + 16 h + lr is live
+  uint32_t vlive;    // bit q: this lane's P V token q (0..7) is live
+};
+
+template <int CLS, bool SLOTS>
+struct Loader {
+  const DecodeArgs &a;
+  const kvq_split sp;
+  const int lr, lb;
+  const int32_t *trow;
+  int64_t first_page;
+
+  __device__ Loader(const DecodeArgs &a_, const kvq_split &s_, int lane)
+      : a(a_), sp(s_), lr(lane & 15), lb(lane >> 4),
+        trow(a_.tables + (int64_t)s_.table * a_.max_entries), first_page(class_first_page<CLS>(a_)) {}
+
+  // Page-table mode: the page of a 16-token page half, clamped to the split's entries.
+  __device__ __forceinline__ int64_t half_page(int32_t T, int h, bool &ok) const {
+    const int32_t e_first = sp.tok_begin >> 4, e_last = (sp.tok_end - 1) >> 4;
+    int32_t e = (T >> 4) + h;
+    e = e < e_first ? e_first : (e > e_last ? e_last : e);
+    const int64_t p = __builtin_amdgcn_readfirstlane(trow[e]);
+    ok = page_class(a, p) == CLS;
+    return ok ? p : first_page;
   }
-  for (int32_t base = sp.tok_begin; base < sp.tok_end; base += 64) {
-    const int32_t t = base + lane;
-    bool live = t < sp.tok_end;
-    int64_t page = 0;
-    int off = 0;
-    if (live) {
-      if (a.kind == KVQ_TABLE_PAGES) {
-        page = trow[t >> 4];
-        off = t & 15;
-      } else {
-        const int32_t slot = trow[t];
-        live = !(a.sentinel >= 0 && slot == a.sentinel);
-        page = slot >> 4;
-        off = slot & 15;
-        if (slot < 0) live = false;
+
+  // Slot-map mode: the block and offset of token t (clamped into the split); live is
+  // false for dead, absent or bad entries.
+  __device__ __forceinline__ const uint8_t *token_block(int32_t t, int &off, bool &live) const {
+    const int32_t tc = t < sp.tok_begin ? sp.tok_begin : (t >= sp.tok_end ? sp.tok_end - 1 : t);
+    const int32_t slot = trow[tc];
+    const bool dead = a.sentinel >= 0 && slot == a.sentinel;
+    const int64_t page = slot >> 4;
+    const bool ok = slot >= 0 && page_class(a, page) == CLS;
+    live = ok && !dead && t >= sp.tok_begin && t < sp.tok_end;
+    if (!ok && !dead) report(a.err, KVQ_DEVERR_ID);
+    off = ok ? (slot & 15) : 0;
+    return block_of<CLS>(a, ok ? page : first_page, sp.head);
+  }
+
+  __device__ void load(int32_t T, Win &w) const {
+    const int ti = lb * 8;  // first of this lane's 8 P V tokens
+    w.ok = 0;
+    w.live = 0;
+    w.vlive = 0;
+    if (!SLOTS) {
+      bool ok0, ok1;
+      const int64_t p0 = half_page(T, 0, ok0), p1 = half_page(T, 1, ok1);
+      if (!ok0 || !ok1) report(a.err, KVQ_DEVERR_ID);
+      w.ok = (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u);
+      const uint8_t *blk[2] = {block_of<CLS>(a, p0, sp.head), block_of<CLS>(a, p1, sp.head)};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int32_t t = T + 16 * h + lr;
+        if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> h & 1)) w.live |= 1u << h;
+        if (CLS == KVQ_INT4) {
+          w.k[h][0] = *reinterpret_cast<const uint4 *>(blk[h] + kI4KC + lr * 64 + lb * 16);
+          w.km[h] = *reinterpret_cast<const uint4 *>(blk[h] + kI4KM + lr * 16);
+        } else if (CLS == KVQ_INT2) {
+          const uint2 x = *reinterpret_cast<const uint2 *>(blk[h] + kI2KC + lr * 32 + lb * 8);
+          w.k[h][0] = make_uint4(x.x, x.y, 0, 0);
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            w.k[h][m] = *reinterpret_cast<const uint4 *>(blk[h] + kF16K + lr * 256 + lb * 64 + m * 16);
+        }
       }
-      if (live && page_class(a, page) != CLS) {
-        report(a.err, KVQ_DEVERR_ID);
-        live = false;
+      if (CLS == KVQ_INT2) {  // per-channel meta of the pair: even page ch 0-63, odd 64-127
+        const uint8_t *mb = blk[lr >> 3];
+        w.ks = *reinterpret_cast<const uint4 *>(mb + kI2KS + (lr & 7) * 16);
+        w.kz = *reinterpret_cast<const uint4 *>(mb + kI2KZ + (lr & 7) * 16);
+        const uint4 *g = reinterpret_cast<const uint4 *>(blk[lb >> 1] + kI2KS + (lb & 1) * 64);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w.kg[m] = g[m];
       }
-    }
-    const uint8_t *blk = live ? block_of(a, CLS, page, sp.head) : nullptr;
-    float x[GP];
-    if (live) {
-      k_logits<GP, CLS>(a, blk, off, page, sp.head, qs, x);
+      // P V lanes: 8 tokens of page half lb / 2, offsets 8 (lb & 1) .. + 7.
+      const uint8_t *vb = blk[lb >> 1];
+      const int o0 = 8 * (lb & 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int32_t t = T + ti + q;
+        if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> (lb >> 1) & 1)) w.vlive |= 1u << q;
+        if (CLS == KVQ_INT4) w.v[q].x = *reinterpret_cast<const uint32_t *>(vb + kI4VC + (o0 + q) * 64 + lr * 4);
+        else if (CLS == KVQ_INT2) w.v[q].x = *reinterpret_cast<const uint32_t *>(vb + kI2VC + (o0 + q) * 32 + (lr >> 1) * 4);
+        else w.v[q] = *reinterpret_cast<const uint4 *>(vb + kF16V + (o0 + q) * 256 + lr * 16);
+      }
+      if (CLS != KVQ_FP16) {
+        const int vm_at = CLS == KVQ_INT4 ? kI4VM : kI2VM;
+        const uint4 *m = reinterpret_cast<const uint4 *>(vb + vm_at + ((lr & 3) * kPage + o0) * 4);
+        w.vm[0] = m[0];
+        w.vm[1] = m[1];
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < GP; ++j) x[j] = -INFINITY;
-    }
-    tok_blk[lane] = blk;
-    tok_off[lane] = off;
+      for (int h = 0; h < 2; ++h) {
+        int off;
+        bool live;
+        const uint8_t *b = token_block(T + 16 * h + lr, off, live);
+        if (live) w.live |= 1u << h;
+        if (CLS == KVQ_INT4) {
+          w.k[h][0] = *reinterpret_cast<const uint4 *>(b + kI4KC + off * 64 + lb * 16);
+          w.km[h] = *reinterpret_cast<const uint4 *>(b + kI4KM + off * 16);
+        } else {
 #pragma unroll
-    for (int j = 0; j < GP; ++j) {
-      const float mc = wave_max(x[j]);
-      const float mn = fmaxf(m[j], mc);
-      float p = 0.0f, alpha = 1.0f;
-      if (mn != -INFINITY) {
-        alpha = exp2f(m[j] - mn);  // 0 while nothing was live before
-        p = live ? exp2f(x[j] - mn) : 0.0f;
+          for (int m = 0; m < 4; ++m)
+            w.k[h][m] = *reinterpret_cast<const uint4 *>(b + kF16K + off * 256 + lb * 64 + m * 16);
+        }
       }
-      ps[j][lane] = p;
-      l[j] = l[j] * alpha + wave_sum(p);
-      acc0[j] *= alpha;
-      acc1[j] *= alpha;
-      m[j] = mn;
-    }
-    __syncthreads();
-    const int n_here = min(64, sp.tok_end - base);
-    for (int tt = 0; tt < n_here; ++tt) {
-      const uint8_t *b = tok_blk[tt];
-      if (!b) continue;  // dead or invalid token: weight 0
-      float v0, v1;
-      v_pair<CLS>(b, tok_off[tt], lane, v0, v1);
+      uint32_t vm[8];
 #pragma unroll
-      for (int j = 0; j < GP; ++j) {
-        acc0[j] = fmaf(ps[j][tt], v0, acc0[j]);
-        acc1[j] = fmaf(ps[j][tt], v1, acc1[j]);
+      for (int q = 0; q < 8; ++q) {
+        int off;
+        bool live;
+        const uint8_t *b = token_block(T + ti + q, off, live);
+        if (live) w.vlive |= 1u << q;
+        if (CLS == KVQ_INT4) {
+          w.v[q].x = *reinterpret_cast<const uint32_t *>(b + kI4VC + off * 64 + lr * 4);
+          vm[q] = *reinterpret_cast<const uint32_t *>(b + kI4VM + ((lr & 3) * kPage + off) * 4);
+        } else {
+          w.v[q] = *reinterpret_cast<const uint4 *>(b + kF16V + off * 256 + lr * 16);
+        }
+      }
+      if (CLS == KVQ_INT4) {
+        w.vm[0] = make_uint4(vm[0], vm[1], vm[2], vm[3]);
+        w.vm[1] = make_uint4(vm[4], vm[5], vm[6], vm[7]);
       }
     }
-    __syncthreads();
   }
-  for (int j = 0; j < a.g; ++j) {
-    const bool any = l[j] > 0.0f;
-    const float inv = any ? 1.0f / l[j] : 0.0f;
-    float *o = a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim;
-    *reinterpret_cast<float2 *>(o + 2 * lane) = make_float2(acc0[j] * inv, acc1[j] * inv);
-    if (lane == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (m[j] + log2f(l[j])) * kLn2 : -INFINITY;
+};
+
+// One split: writes part_o / part_lse of split s_idx.
+template <int QT, int CLS, bool SLOTS>
+__device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L) {
+  const int lane = threadIdx.x, lr = lane & 15, lb = lane >> 4;
+  const Loader<CLS, SLOTS> ld(a, sp, lane);
+
+  // ---- constants of the split (query side) ----
+  h8 Aq[QT][4];        // block-diagonal query operand
+  h2 qn[QT][4];        // natural-order q pairs: query 4 qt + lb, channels 8 lr .. 8 lr + 7
+  float qsum[QT][4];   // per-group sum of q of query 4 qt + lb (INT4 zero term)
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int jr = 4 * qt + (lr >> 2), gi = lr & 3;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const h2 hv = {(_Float16)L.q[jr][32 * lb + 8 * m + 2 * u], (_Float16)L.q[jr][32 * lb + 8 * m + 2 * u + 1]};
+        w[u] = lb == gi ? as_u32(hv) : 0u;
+      }
+      Aq[qt][m] = h8_of(w[0], w[1], w[2], w[3]);
+    }
+    float ps = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      qn[qt][u] = h2{(_Float16)L.q[4 * qt + lb][8 * lr + 2 * u], (_Float16)L.q[4 * qt + lb][8 * lr + 2 * u + 1]};
+      ps += (float)qn[qt][u][0] + (float)qn[qt][u][1];
+    }
+    ps = quad_sum(ps);  // lanes (lb, lr): query 4 qt + lb, group lr / 4
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qsum[qt][r] = __shfl(ps, 16 * lb + 4 * r);
+  }
+  const float scale = kLog2e / sqrtf((float)kHeadDim);  // logits in base-2 units
+
+  // ---- running state ----
+  f4 acc[QT][8];
+  float m_run[QT], l_run[QT], zacc[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.0f;
+    zacc[qt] = 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  const int32_t T0 = SLOTS ? sp.tok_begin : (sp.tok_begin & ~15);
+  Win cur;
+  ld.load(T0, cur);
+  for (int32_t T = T0; T < sp.tok_end; T += 32) {
+    Win nxt;
+    if (T + 32 < sp.tok_end) ld.load(T + 32, nxt);
+    const bool partial = (T < sp.tok_begin) || (T + 32 > sp.tok_end) || cur.ok != 3u;
+
+    // ---- INT2: zero term of the pair, sum over the group of q (z + 2 s) ----
+    f4 c2[QT];
+    if (CLS == KVQ_INT2) {
+      const uint32_t ks[4] = {cur.ks.x, cur.ks.y, cur.ks.z, cur.ks.w};
+      const uint32_t kz[4] = {cur.kz.x, cur.kz.y, cur.kz.z, cur.kz.w};
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float bz = 0.0f, bs = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          bz = dot2(qn[qt][u], as_h2(kz[u]), bz);
+          bs = dot2(qn[qt][u], as_h2(ks[u]), bs);
+        }
+        const float bias = quad_sum(fmaf(2.0f, bs, bz));  // query 4 qt + lb, group lr / 4
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c2[qt][r] = __shfl(bias, 16 * lb + 4 * r);
+      }
+    }
+
+    // ---- QK^T: logit (base 2) of query 4 qt + lb and token T + 16 h + lr ----
+    float x[QT][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      h8 kb[4];
+      if (CLS == KVQ_INT4) {
+        const uint4 w = cur.k[h][0];
+        kb[0] = k4_word(w.x);
+        kb[1] = k4_word(w.y);
+        kb[2] = k4_word(w.z);
+        kb[3] = k4_word(w.w);
+      } else if (CLS == KVQ_INT2) {
+        const uint4 w = cur.k[h][0];
+        const h8 c[4] = {k2_byte(w.x), k2_byte(w.x >> 8), k2_byte(w.y), k2_byte(w.y >> 8)};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) kb[m] = c[m] * h8_of(cur.kg[m]);  // s (c - 2): exact
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) kb[m] = h8_of(cur.k[h][m]);
+      }
+      const bool live = cur.live >> h & 1;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        f4 d = CLS == KVQ_INT2 ? c2[qt] : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) d = mfma(Aq[qt][m], kb[m], d);
+        float s;
+        if (CLS == KVQ_INT4) {
+          const uint32_t mm[4] = {cur.km[h].x, cur.km[h].y, cur.km[h].z, cur.km[h].w};
+          s = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sc = h2f(mm[r]), zc = fmaf(8.0f, sc, h2f(mm[r] >> 16));  // z + 8 s
+            s = fmaf(sc, d[r], fmaf(zc, qsum[qt][r], s));
+          }
+        } else {
+          s = (d[0] + d[1]) + (d[2] + d[3]);
+        }
+        x[qt][h] = live ? s * scale : -INFINITY;
+      }
+    }
+
+    // ---- online softmax (per query: the 16 lanes of row lb) ----
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float bm = row_max16(fmaxf(x[qt][0], x[qt][1]));
+      const float mn = fmaxf(m_run[qt], bm);
+      if (__any(mn > m_run[qt])) {
+        const float alpha = mn == -INFINITY ? 1.0f : exp2f(m_run[qt] - mn);
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
+        zacc[qt] *= __shfl(alpha, 16 * (lr >> 2));  // zero-term rows belong to query lr / 4
+        m_run[qt] = mn;
+      }
+      const float p0 = x[qt][0] == -INFINITY ? 0.0f : exp2f(x[qt][0] - m_run[qt]);
+      const float p1 = x[qt][1] == -INFINITY ? 0.0f : exp2f(x[qt][1] - m_run[qt]);
+      l_run[qt] += p0 + p1;
+      L.p[qt][lb][lr] = (_Float16)p0;
+      L.p[qt][lb][16 + lr] = (_Float16)p1;
+    }
+
+    // ---- V operand: this lane's channels 8 lr + nt, its 8 tokens as 4 pairs ----
+    h8 vb[8];
+    {
+      uint32_t t[8][4];  // [nt][token pair]
+      if (CLS == KVQ_INT4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t wa = cur.v[2 * u].x, wb = cur.v[2 * u + 1].x;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t y = pair_bytes(wa, wb, b);
+            const int lo = b == 0 ? 0 : b == 1 ? 4 : b == 2 ? 1 : 5;  // channel in the low nibble
+            t[lo][u] = as_u32(as_h2((y & 0x000F000Fu) | 0x64006400u) - h2{(_Float16)1032.0f, (_Float16)1032.0f});
+            t[lo + 2][u] = as_u32(as_h2((y & 0x00F000F0u) | 0x54005400u) - h2{(_Float16)72.0f, (_Float16)72.0f});
+          }
+        }
+      } else if (CLS == KVQ_INT2) {
+        const int be = lr & 1;  // byte of this lane's even channels (odd ones: be + 2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t wa = cur.v[2 * u].x, wb = cur.v[2 * u + 1].x;
+#pragma unroll
+          for (int par = 0; par < 2; ++par) {
+            const uint32_t y = pair_bytes(wa, wb, be + 2 * par);
+            t[par + 0][u] = as_u32(as_h2((y & 0x00030003u) | 0x64006400u) - h2{(_Float16)1026.0f, (_Float16)1026.0f});
+            t[par + 2][u] = as_u32(as_h2((y & 0x000C000Cu) | 0x5C005C00u) - h2{(_Float16)258.0f, (_Float16)258.0f});
+            t[par + 4][u] = as_u32(as_h2((y & 0x00300030u) | 0x54005400u) - h2{(_Float16)66.0f, (_Float16)66.0f});
+            t[par + 6][u] = as_u32(as_h2((y & 0x00C000C0u) | 0x4C004C00u) - h2{(_Float16)18.0f, (_Float16)18.0f});
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 ra = cur.v[2 * u], rb = cur.v[2 * u + 1];
+          const uint32_t da[4] = {ra.x, ra.y, ra.z, ra.w}, db[4] = {rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            const uint32_t xa = da[nt >> 1], xb = db[nt >> 1];
+            t[nt][u] = (nt & 1) ? ((xa >> 16) | (xb & 0xffff0000u)) : ((xa & 0xffffu) | (xb << 16));
+          }
+        }
+        if (partial) {  // absent or dead tokens: keep the operand finite
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t mk = ((cur.vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
+                                ((cur.vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) t[nt][u] &= mk;
+          }
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) vb[nt] = h8_of(t[nt][0], t[nt][1], t[nt][2], t[nt][3]);
+    }
+    __syncthreads();  // the weights of this window are in LDS
+
+    // ---- P V ----
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const uint4 pw = *reinterpret_cast<const uint4 *>(&L.p[qt][lr >> 2][8 * lb]);
+      h8 ap;
+      if (CLS == KVQ_FP16) {
+        ap = h8_of(pw);
+      } else {
+        const uint32_t p2[4] = {pw.x, pw.y, pw.z, pw.w};
+        const uint32_t mv[8] = {cur.vm[0].x, cur.vm[0].y, cur.vm[0].z, cur.vm[0].w,
+                                cur.vm[1].x, cur.vm[1].y, cur.vm[1].z, cur.vm[1].w};
+        const _Float16 center = CLS == KVQ_INT4 ? (_Float16)8.0f : (_Float16)2.0f;
+        uint32_t aw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          uint32_t s2 = (mv[2 * u] & 0xffffu) | (mv[2 * u + 1] << 16);      // scales
+          uint32_t z2 = (mv[2 * u] >> 16) | (mv[2 * u + 1] & 0xffff0000u);  // zeros
+          if (partial) {
+            const uint32_t mk = ((cur.vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
+                                ((cur.vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
+            s2 &= mk;
+            z2 &= mk;
+          }
+          const h2 sv = as_h2(s2), pp = as_h2(p2[u]);
+          const h2 zc = sv * h2{center, center} + as_h2(z2);
+          aw[u] = as_u32(pp * sv);
+          zacc[qt] = dot2(pp, zc, zacc[qt]);
+        }
+        ap = h8_of(aw[0], aw[1], aw[2], aw[3]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = mfma(ap, vb[nt], acc[qt][nt]);
+    }
+    cur = nxt;
+  }
+
+  // ---- epilogue: lane (lr, lb) owns query 4 qt + lb, channels 8 lr .. 8 lr + 7 ----
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l_tot = row_sum16(l_run[qt]);
+    float z = zacc[qt];
+    z += __shfl_xor(z, 16);
+    z += __shfl_xor(z, 32);
+    const float zrow = __shfl(z, 4 * lb + (lr >> 2));  // row (query lb, group lr / 4)
+    const int j = 4 * qt + lb;
+    const bool any = l_tot > 0.0f;
+    const float inv = any ? 1.0f / l_tot : 0.0f;
+    const int r = lr >> 2;
+    float o[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const f4 d = acc[qt][nt];
+      const float v = r == 0 ? d[0] : r == 1 ? d[1] : r == 2 ? d[2] : d[3];
+      o[nt] = any ? (v + (CLS == KVQ_FP16 ? 0.0f : zrow)) * inv : 0.0f;
+    }
+    if (j < a.g) {
+      float4 *dst = reinterpret_cast<float4 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 8 * lr);
+      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+      if (lr == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (m_run[qt] + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 
-template <int GP>
-__global__ void __launch_bounds__(64) decode_ref_kernel(DecodeArgs a) {
-  __shared__ float qs[GP][kHeadDim];
-  __shared__ float ps[GP][64];
-  __shared__ const uint8_t *tok_blk[64];
-  __shared__ int tok_off[64];
+template <int QT, bool SLOTS>
+__global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
+  __shared__ Lds<QT> L;
   const int lane = threadIdx.x;
   const int s_idx = blockIdx.x;
   const kvq_split sp = a.splits[s_idx];
-  const int64_t cap = a.kind == KVQ_TABLE_PAGES ? (int64_t)a.max_entries * kPage : a.max_entries;
+  const int64_t cap = SLOTS ? (int64_t)a.max_entries : (int64_t)a.max_entries * kPage;
   const bool ok = sp.table >= 0 && sp.table < a.n_tables && sp.head >= 0 && sp.head < a.heads &&
                   sp.cls >= 0 && sp.cls <= 2 && sp.tok_begin >= 0 && sp.tok_end >= sp.tok_begin &&
                   sp.tok_end <= cap &&
-                  (sp.cls != KVQ_INT2 ||
-                   (a.kind == KVQ_TABLE_PAGES && sp.tok_begin % kGroup == 0 && sp.tok_end % kGroup == 0));
-  if (!ok) {
-    if (lane == 0) report(a.err, KVQ_DEVERR_SPLIT);
+                  (sp.cls != KVQ_INT2 || (!SLOTS && sp.tok_begin % kGroup == 0 && sp.tok_end % kGroup == 0));
+  if (!ok || sp.tok_end == sp.tok_begin) {
+    if (!ok && lane == 0) report(a.err, KVQ_DEVERR_SPLIT);
     for (int j = 0; j < a.g; ++j) {
       float *o = a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim;
       *reinterpret_cast<float2 *>(o + 2 * lane) = make_float2(0.0f, 0.0f);
@@ -289,16 +587,24 @@ __global__ void __launch_bounds__(64) decode_ref_kernel(DecodeArgs a) {
   }
   const int b = sp.table / a.tpr;
   const int kvh = (sp.table % a.tpr) * a.heads + sp.head;
-  const float scale = kLog2e / sqrtf((float)kHeadDim);
-#pragma unroll
-  for (int j = 0; j < GP; ++j)
-    for (int c = lane; c < kHeadDim; c += 64)
-      qs[j][c] = j < a.g ? load_q(a.q, a.q_dtype, ((int64_t)b * a.hq + kvh * a.g + j) * kHeadDim + c) * scale
-                         : 0.0f;
+  for (int j = 0; j < 4 * QT; ++j)
+    for (int c = lane; c < kHeadDim; c += 64) {
+      float v = 0.0f;
+      if (j < a.g) {
+        const int64_t idx = ((int64_t)b * a.hq + kvh * a.g + j) * kHeadDim + c;
+        if (a.q_dtype == KVQ_F32) {
+          v = static_cast<const float *>(a.q)[idx];
+        } else {
+          const uint32_t h = static_cast<const uint16_t *>(a.q)[idx];
+          v = a.q_dtype == KVQ_BF16 ? __uint_as_float(h << 16) : h2f(h);
+        }
+      }
+      L.q[j][c] = v;
+    }
   __syncthreads();
-  if (sp.cls == KVQ_INT2) decode_split<GP, KVQ_INT2>(a, sp, s_idx, qs, ps, tok_blk, tok_off);
-  else if (sp.cls == KVQ_INT4) decode_split<GP, KVQ_INT4>(a, sp, s_idx, qs, ps, tok_blk, tok_off);
-  else decode_split<GP, KVQ_FP16>(a, sp, s_idx, qs, ps, tok_blk, tok_off);
+  if (sp.cls == KVQ_INT4) run_split<QT, KVQ_INT4, SLOTS>(a, sp, s_idx, L);
+  else if (sp.cls == KVQ_FP16) run_split<QT, KVQ_FP16, SLOTS>(a, sp, s_idx, L);
+  else if (!SLOTS) run_split<QT, KVQ_INT2, false>(a, sp, s_idx, L);
 }
 
 // ------------------------------------------------------------------ merge -----
@@ -400,17 +706,25 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
   a.tables = tables;
   a.n_tables = n_tables;
   a.max_entries = max_entries;
-  a.kind = table_kind;
   a.splits = splits;
   a.n_splits = n_splits;
   a.part_o = part_o;
   a.part_lse = part_lse;
   a.err = dev_err;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (g <= 4) hipLaunchKernelGGL(decode_ref_kernel<4>, dim3(n_splits), dim3(64), 0, s, a);
-  else if (g <= 8) hipLaunchKernelGGL(decode_ref_kernel<8>, dim3(n_splits), dim3(64), 0, s, a);
-  else hipLaunchKernelGGL(decode_ref_kernel<16>, dim3(n_splits), dim3(64), 0, s, a);
-  return launched("decode_ref_kernel");
+  const bool slots = table_kind == KVQ_TABLE_SLOTS;
+  const dim3 grid(n_splits), block(64);
+  if (g <= 4) {
+    if (slots) hipLaunchKernelGGL((decode_kernel<1, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, s, a);
+  } else if (g <= 8) {
+    if (slots) hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, s, a);
+  } else {
+    if (slots) hipLaunchKernelGGL((decode_kernel<4, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, s, a);
+  }
+  return launched("decode_kernel");
 }
 
 extern "C" kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, int32_t n_splits,
@@ -437,9 +751,9 @@ extern "C" kvq_status kvq_decode_occupancy(int32_t g, int32_t *per_cu, int32_t *
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_NO_DEVICE, "hipGetDevice failed");
   int blocks = 0, cus = 0;
   hipError_t e;
-  if (g <= 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ref_kernel<4>, 64, 0);
-  else if (g <= 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ref_kernel<8>, 64, 0);
-  else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ref_kernel<16>, 64, 0);
+  if (g <= 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<1, false>, 64, 0);
+  else if (g <= 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<2, false>, 64, 0);
+  else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, false>, 64, 0);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(KVQ_ERR_HIP, "CU count query failed");

@@ -102,7 +102,8 @@ def test_g8_and_g1_heads():
 
 
 def test_split_count_invariance_on_gpu():
-    """Different split plans of the same cache agree (the result does not depend on S)."""
+    """Different split plans of the same cache agree to the parity tolerance (fp16 operand
+    roundings depend on each split's running maximum, so agreement is not bitwise)."""
     wg = synth.qwen3_8b(batch=1, n_tokens=2048)
     gpu = GpuRun(wg)
     outs = []
@@ -111,7 +112,7 @@ def test_split_count_invariance_on_gpu():
         outs.append(gpu.decode(s, o)[0].cpu().numpy())
         _say("split plan", kw, s.shape[0])
     for o in outs[1:]:
-        assert row_metric(outs[0], o) < 1e-5
+        assert row_metric(outs[0], o) < TOL
 
 
 def test_edge_cases_empty_dead_single():
