@@ -49,6 +49,24 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+// Pool bytes through the global address space (vector memory counters only), and
+// page-table entries through the constant address space: wave-uniform entries become
+// scalar loads that never wait on the vector loads in flight.
+typedef const __attribute__((address_space(1))) uint8_t *gbytes;
+typedef const __attribute__((address_space(4))) int32_t *cints;
+
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld4(gbytes p) {
+  const u4v v = *reinterpret_cast<const __attribute__((address_space(1))) u4v *>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 ld2(gbytes p) {
+  const u2v v = *reinterpret_cast<const __attribute__((address_space(1))) u2v *>(p);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint32_t ld1(gbytes p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t *>(p);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -129,7 +147,7 @@ __device__ __forceinline__ uint32_t pair_bytes(uint32_t wa, uint32_t wb, int b) 
 
 struct DecodeArgs {
   int32_t heads, n2, n4, n16;
-  const uint8_t *pool2, *pool4, *pool16;
+  gbytes pool2, pool4, pool16;
   int32_t sentinel;
   const void *q;
   int32_t q_dtype, batch, hq, hkv, g, tpr;
@@ -141,25 +159,25 @@ struct DecodeArgs {
   int32_t *err;
 };
 
-__device__ __forceinline__ int page_class(const DecodeArgs &a, int64_t p) {
-  if (p < 0) return -1;
-  if (p < a.n2) return KVQ_INT2;
-  if (p < (int64_t)a.n2 + a.n4) return KVQ_INT4;
-  if (p < (int64_t)a.n2 + a.n4 + a.n16) return KVQ_FP16;
-  return -1;
-}
-
+// The pages of one class: ids first .. first + count - 1 of the unified numbering,
+// blocks of head `head` at base + (id - first) * stride.  The host keeps every unified
+// slot id (16 x page id) inside int32, so ids relative to `first` fit 32 bits.
 template <int CLS>
-__device__ __forceinline__ const uint8_t *block_of(const DecodeArgs &a, int64_t page, int head) {
-  if (CLS == KVQ_INT2) return a.pool2 + (page * a.heads + head) * (int64_t)kI2Bytes;
-  if (CLS == KVQ_INT4) return a.pool4 + ((page - a.n2) * a.heads + head) * (int64_t)kI4Bytes;
-  return a.pool16 + ((page - a.n2 - a.n4) * a.heads + head) * (int64_t)kF16Bytes;
-}
-
-template <int CLS>
-__device__ __forceinline__ int64_t class_first_page(const DecodeArgs &a) {
-  return CLS == KVQ_INT2 ? 0 : CLS == KVQ_INT4 ? a.n2 : (int64_t)a.n2 + a.n4;
-}
+struct ClassPages {
+  gbytes base;
+  uint32_t first, count, stride;
+  __device__ ClassPages(const DecodeArgs &a, int head) {
+    const uint32_t bytes = CLS == KVQ_INT2 ? kI2Bytes : CLS == KVQ_INT4 ? kI4Bytes : kF16Bytes;
+    first = CLS == KVQ_INT2 ? 0u : CLS == KVQ_INT4 ? (uint32_t)a.n2 : (uint32_t)(a.n2 + a.n4);
+    count = (uint32_t)(CLS == KVQ_INT2 ? a.n2 : CLS == KVQ_INT4 ? a.n4 : a.n16);
+    stride = (uint32_t)a.heads * bytes;
+    base = (CLS == KVQ_INT2 ? a.pool2 : CLS == KVQ_INT4 ? a.pool4 : a.pool16) + (uint32_t)head * bytes;
+  }
+  // Page id -> class-relative index; ids outside the class (negative included) are
+  // not `< count` after the unsigned wrap.
+  __device__ __forceinline__ uint32_t rel(int32_t id) const { return (uint32_t)id - first; }
+  __device__ __forceinline__ gbytes block(uint32_t r) const { return base + (uint64_t)r * stride; }
+};
 
 template <int QT>
 struct Lds {
@@ -189,34 +207,37 @@ struct Loader {
   const kvq_split sp;
   const int lr, lb;
   const int32_t *trow;
-  int64_t first_page;
+  cints crow;
+  const ClassPages<CLS> pages;
+  int32_t e_first, e_last;    // page-table entries of the split
+  mutable uint32_t errs = 0;  // KVQ_DEVERR_* met so far (reported once, after the loop)
 
   __device__ Loader(const DecodeArgs &a_, const kvq_split &s_, int lane)
       : a(a_), sp(s_), lr(lane & 15), lb(lane >> 4),
-        trow(a_.tables + (int64_t)s_.table * a_.max_entries), first_page(class_first_page<CLS>(a_)) {}
+        trow(a_.tables + (int64_t)s_.table * a_.max_entries), crow((cints)trow), pages(a_, s_.head),
+        e_first(s_.tok_begin >> 4), e_last((s_.tok_end - 1) >> 4) {}
 
-  // Page-table mode: the page of a 16-token page half, clamped to the split's entries.
-  __device__ __forceinline__ int64_t half_page(int32_t T, int h, bool &ok) const {
-    const int32_t e_first = sp.tok_begin >> 4, e_last = (sp.tok_end - 1) >> 4;
-    int32_t e = (T >> 4) + h;
-    e = e < e_first ? e_first : (e > e_last ? e_last : e);
-    const int64_t p = __builtin_amdgcn_readfirstlane(trow[e]);
-    ok = page_class(a, p) == CLS;
-    return ok ? p : first_page;
+  // Page-table mode: the block of a 16-token page half, clamped to the split's entries
+  // (a bad id reads the class's first block and is flagged).
+  __device__ __forceinline__ gbytes half_page(int32_t T, int h, bool &ok) const {
+    const int32_t e = min(max((T >> 4) + h, e_first), e_last);
+    const uint32_t r = pages.rel(crow[__builtin_amdgcn_readfirstlane(e)]);
+    ok = r < pages.count;
+    return pages.block(ok ? r : 0u);
   }
 
   // Slot-map mode: the block and offset of token t (clamped into the split); live is
   // false for dead, absent or bad entries.
-  __device__ __forceinline__ const uint8_t *token_block(int32_t t, int &off, bool &live) const {
-    const int32_t tc = t < sp.tok_begin ? sp.tok_begin : (t >= sp.tok_end ? sp.tok_end - 1 : t);
-    const int32_t slot = trow[tc];
+  __device__ __forceinline__ gbytes token_block(int32_t t, int &off, bool &live) const {
+    const int32_t tc = min(max(t, sp.tok_begin), sp.tok_end - 1);
+    const int32_t slot = (int32_t)ld1((gbytes)(trow + tc));
     const bool dead = a.sentinel >= 0 && slot == a.sentinel;
-    const int64_t page = slot >> 4;
-    const bool ok = slot >= 0 && page_class(a, page) == CLS;
+    const uint32_t r = pages.rel(slot >> 4);
+    const bool ok = slot >= 0 && r < pages.count;
     live = ok && !dead && t >= sp.tok_begin && t < sp.tok_end;
-    if (!ok && !dead) report(a.err, KVQ_DEVERR_ID);
+    errs |= (!ok && !dead) ? (uint32_t)KVQ_DEVERR_ID : 0u;
     off = ok ? (slot & 15) : 0;
-    return block_of<CLS>(a, ok ? page : first_page, sp.head);
+    return pages.block(ok ? r : 0u);
   }
 
   __device__ void load(int32_t T, Win &w) const {
@@ -226,65 +247,63 @@ struct Loader {
     w.vlive = 0;
     if (!SLOTS) {
       bool ok0, ok1;
-      const int64_t p0 = half_page(T, 0, ok0), p1 = half_page(T, 1, ok1);
-      if (!ok0 || !ok1) report(a.err, KVQ_DEVERR_ID);
+      const gbytes blk0 = half_page(T, 0, ok0), blk1 = half_page(T, 1, ok1);
+      errs |= (ok0 && ok1) ? 0u : (uint32_t)KVQ_DEVERR_ID;
       w.ok = (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u);
-      const uint8_t *blk[2] = {block_of<CLS>(a, p0, sp.head), block_of<CLS>(a, p1, sp.head)};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int32_t t = T + 16 * h + lr;
         if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> h & 1)) w.live |= 1u << h;
+        const gbytes bh = h ? blk1 : blk0;
         if (CLS == KVQ_INT4) {
-          w.k[h][0] = *reinterpret_cast<const uint4 *>(blk[h] + kI4KC + lr * 64 + lb * 16);
-          w.km[h] = *reinterpret_cast<const uint4 *>(blk[h] + kI4KM + lr * 16);
+          w.k[h][0] = ld4(bh + kI4KC + lr * 64 + lb * 16);
+          w.km[h] = ld4(bh + kI4KM + lr * 16);
         } else if (CLS == KVQ_INT2) {
-          const uint2 x = *reinterpret_cast<const uint2 *>(blk[h] + kI2KC + lr * 32 + lb * 8);
+          const uint2 x = ld2(bh + kI2KC + lr * 32 + lb * 8);
           w.k[h][0] = make_uint4(x.x, x.y, 0, 0);
         } else {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            w.k[h][m] = *reinterpret_cast<const uint4 *>(blk[h] + kF16K + lr * 256 + lb * 64 + m * 16);
+          for (int m = 0; m < 4; ++m) w.k[h][m] = ld4(bh + kF16K + lr * 256 + lb * 64 + m * 16);
         }
       }
       if (CLS == KVQ_INT2) {  // per-channel meta of the pair: even page ch 0-63, odd 64-127
-        const uint8_t *mb = blk[lr >> 3];
-        w.ks = *reinterpret_cast<const uint4 *>(mb + kI2KS + (lr & 7) * 16);
-        w.kz = *reinterpret_cast<const uint4 *>(mb + kI2KZ + (lr & 7) * 16);
-        const uint4 *g = reinterpret_cast<const uint4 *>(blk[lb >> 1] + kI2KS + (lb & 1) * 64);
+        const gbytes mb = (lr >> 3) ? blk1 : blk0;
+        w.ks = ld4(mb + kI2KS + (lr & 7) * 16);
+        w.kz = ld4(mb + kI2KZ + (lr & 7) * 16);
+        const gbytes g = ((lb >> 1) ? blk1 : blk0) + kI2KS + (lb & 1) * 64;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) w.kg[m] = g[m];
+        for (int m = 0; m < 4; ++m) w.kg[m] = ld4(g + 16 * m);
       }
       // P V lanes: 8 tokens of page half lb / 2, offsets 8 (lb & 1) .. + 7.
-      const uint8_t *vb = blk[lb >> 1];
+      const gbytes vb = (lb >> 1) ? blk1 : blk0;
       const int o0 = 8 * (lb & 1);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int32_t t = T + ti + q;
         if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> (lb >> 1) & 1)) w.vlive |= 1u << q;
-        if (CLS == KVQ_INT4) w.v[q].x = *reinterpret_cast<const uint32_t *>(vb + kI4VC + (o0 + q) * 64 + lr * 4);
-        else if (CLS == KVQ_INT2) w.v[q].x = *reinterpret_cast<const uint32_t *>(vb + kI2VC + (o0 + q) * 32 + (lr >> 1) * 4);
-        else w.v[q] = *reinterpret_cast<const uint4 *>(vb + kF16V + (o0 + q) * 256 + lr * 16);
+        if (CLS == KVQ_INT4) w.v[q].x = ld1(vb + kI4VC + (o0 + q) * 64 + lr * 4);
+        else if (CLS == KVQ_INT2) w.v[q].x = ld1(vb + kI2VC + (o0 + q) * 32 + (lr >> 1) * 4);
+        else w.v[q] = ld4(vb + kF16V + (o0 + q) * 256 + lr * 16);
       }
       if (CLS != KVQ_FP16) {
         const int vm_at = CLS == KVQ_INT4 ? kI4VM : kI2VM;
-        const uint4 *m = reinterpret_cast<const uint4 *>(vb + vm_at + ((lr & 3) * kPage + o0) * 4);
-        w.vm[0] = m[0];
-        w.vm[1] = m[1];
+        const gbytes m = vb + vm_at + ((lr & 3) * kPage + o0) * 4;
+        w.vm[0] = ld4(m);
+        w.vm[1] = ld4(m + 16);
       }
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         int off;
         bool live;
-        const uint8_t *b = token_block(T + 16 * h + lr, off, live);
+        const gbytes b = token_block(T + 16 * h + lr, off, live);
         if (live) w.live |= 1u << h;
         if (CLS == KVQ_INT4) {
-          w.k[h][0] = *reinterpret_cast<const uint4 *>(b + kI4KC + off * 64 + lb * 16);
-          w.km[h] = *reinterpret_cast<const uint4 *>(b + kI4KM + off * 16);
+          w.k[h][0] = ld4(b + kI4KC + off * 64 + lb * 16);
+          w.km[h] = ld4(b + kI4KM + off * 16);
         } else {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            w.k[h][m] = *reinterpret_cast<const uint4 *>(b + kF16K + off * 256 + lb * 64 + m * 16);
+          for (int m = 0; m < 4; ++m) w.k[h][m] = ld4(b + kF16K + off * 256 + lb * 64 + m * 16);
         }
       }
       uint32_t vm[8];
@@ -292,13 +311,13 @@ struct Loader {
       for (int q = 0; q < 8; ++q) {
         int off;
         bool live;
-        const uint8_t *b = token_block(T + ti + q, off, live);
+        const gbytes b = token_block(T + ti + q, off, live);
         if (live) w.vlive |= 1u << q;
         if (CLS == KVQ_INT4) {
-          w.v[q].x = *reinterpret_cast<const uint32_t *>(b + kI4VC + off * 64 + lr * 4);
-          vm[q] = *reinterpret_cast<const uint32_t *>(b + kI4VM + ((lr & 3) * kPage + off) * 4);
+          w.v[q].x = ld1(b + kI4VC + off * 64 + lr * 4);
+          vm[q] = ld1(b + kI4VM + ((lr & 3) * kPage + off) * 4);
         } else {
-          w.v[q] = *reinterpret_cast<const uint4 *>(b + kF16V + off * 256 + lr * 16);
+          w.v[q] = ld4(b + kF16V + off * 256 + lr * 16);
         }
       }
       if (CLS == KVQ_INT4) {
@@ -309,66 +328,94 @@ struct Loader {
   }
 };
 
+// Keeps a 32-bit constant in a VGPR, so that (x & mask) | magic can be one
+// v_and_or_b32 (a VOP3 instruction may read only one scalar / literal operand).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+  asm volatile("" : "+v"(c));
+  return c;
+}
+
+struct Consts {
+  uint32_t m000F, m00F0, m0003, m000C, m0030, m00C0;
+  __device__ Consts()
+      : m000F(in_vgpr(0x000F000Fu)), m00F0(in_vgpr(0x00F000F0u)), m0003(in_vgpr(0x00030003u)),
+        m000C(in_vgpr(0x000C000Cu)), m0030(in_vgpr(0x00300030u)), m00C0(in_vgpr(0x00C000C0u)) {}
+};
+
+// Exact centered codes of 8 channels: INT4 word (c - 8), INT2 bytes (c - 2).
+__device__ __forceinline__ h8 cvt_k4(uint32_t x, const Consts &k) {
+  const uint32_t y = x >> 8;
+  const h2 lo = {(_Float16)1032.0f, (_Float16)1032.0f}, hi = {(_Float16)72.0f, (_Float16)72.0f};
+  return h8_of(as_u32(as_h2((x & k.m000F) | 0x64006400u) - lo), as_u32(as_h2((x & k.m00F0) | 0x54005400u) - hi),
+               as_u32(as_h2((y & k.m000F) | 0x64006400u) - lo), as_u32(as_h2((y & k.m00F0) | 0x54005400u) - hi));
+}
+__device__ __forceinline__ h8 cvt_k2(uint32_t x, const Consts &k) {
+  return h8_of(as_u32(as_h2((x & k.m0003) | 0x64006400u) - h2{(_Float16)1026.0f, (_Float16)1026.0f}),
+               as_u32(as_h2((x & k.m000C) | 0x5C005C00u) - h2{(_Float16)258.0f, (_Float16)258.0f}),
+               as_u32(as_h2((x & k.m0030) | 0x54005400u) - h2{(_Float16)66.0f, (_Float16)66.0f}),
+               as_u32(as_h2((x & k.m00C0) | 0x4C004C00u) - h2{(_Float16)18.0f, (_Float16)18.0f}));
+}
+
+constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so no exp2 ever sees -inf - -inf
+
 // One split: writes part_o / part_lse of split s_idx.
 template <int QT, int CLS, bool SLOTS>
-__device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L) {
-  const int lane = threadIdx.x, lr = lane & 15, lb = lane >> 4;
-  const Loader<CLS, SLOTS> ld(a, sp, lane);
-
-  // ---- constants of the split (query side) ----
+struct SplitRun {
+  const DecodeArgs &a;
+  const kvq_split &sp;
+  Lds<QT> &L;
+  const Loader<CLS, SLOTS> &ld;
+  const int lane, lr, lb;
+  const Consts k;
+  float scale;
   h8 Aq[QT][4];        // block-diagonal query operand
   h2 qn[QT][4];        // natural-order q pairs: query 4 qt + lb, channels 8 lr .. 8 lr + 7
   float qsum[QT][4];   // per-group sum of q of query 4 qt + lb (INT4 zero term)
+  f4 acc[QT][8];       // P V accumulators
+  float m_run[QT], l_run[QT], zacc[QT];
+
+  __device__ SplitRun(const DecodeArgs &a_, const kvq_split &sp_, Lds<QT> &L_, const Loader<CLS, SLOTS> &ld_)
+      : a(a_), sp(sp_), L(L_), ld(ld_), lane(threadIdx.x), lr(threadIdx.x & 15), lb(threadIdx.x >> 4) {
+    scale = kLog2e / sqrtf((float)kHeadDim);
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int jr = 4 * qt + (lr >> 2), gi = lr & 3;
+    for (int qt = 0; qt < QT; ++qt) {
+      const int jr = 4 * qt + (lr >> 2), gi = lr & 3;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t w[4];
+      for (int m = 0; m < 4; ++m) {
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const h2 hv = {(_Float16)L.q[jr][32 * lb + 8 * m + 2 * u], (_Float16)L.q[jr][32 * lb + 8 * m + 2 * u + 1]};
+          w[u] = lb == gi ? as_u32(hv) : 0u;
+        }
+        Aq[qt][m] = h8_of(w[0], w[1], w[2], w[3]);
+      }
+      float ps = 0.0f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const h2 hv = {(_Float16)L.q[jr][32 * lb + 8 * m + 2 * u], (_Float16)L.q[jr][32 * lb + 8 * m + 2 * u + 1]};
-        w[u] = lb == gi ? as_u32(hv) : 0u;
+        qn[qt][u] = h2{(_Float16)L.q[4 * qt + lb][8 * lr + 2 * u], (_Float16)L.q[4 * qt + lb][8 * lr + 2 * u + 1]};
+        ps += (float)qn[qt][u][0] + (float)qn[qt][u][1];
       }
-      Aq[qt][m] = h8_of(w[0], w[1], w[2], w[3]);
+      ps = quad_sum(ps);  // lanes (lb, lr): query 4 qt + lb, group lr / 4
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qsum[qt][r] = __shfl(ps, 16 * lb + 4 * r);
+      m_run[qt] = kNegBig;
+      l_run[qt] = 0.0f;
+      zacc[qt] = 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    float ps = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      qn[qt][u] = h2{(_Float16)L.q[4 * qt + lb][8 * lr + 2 * u], (_Float16)L.q[4 * qt + lb][8 * lr + 2 * u + 1]};
-      ps += (float)qn[qt][u][0] + (float)qn[qt][u][1];
-    }
-    ps = quad_sum(ps);  // lanes (lb, lr): query 4 qt + lb, group lr / 4
-#pragma unroll
-    for (int r = 0; r < 4; ++r) qsum[qt][r] = __shfl(ps, 16 * lb + 4 * r);
-  }
-  const float scale = kLog2e / sqrtf((float)kHeadDim);  // logits in base-2 units
-
-  // ---- running state ----
-  f4 acc[QT][8];
-  float m_run[QT], l_run[QT], zacc[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.0f;
-    zacc[qt] = 0.0f;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  const int32_t T0 = SLOTS ? sp.tok_begin : (sp.tok_begin & ~15);
-  Win cur;
-  ld.load(T0, cur);
-  for (int32_t T = T0; T < sp.tok_end; T += 32) {
-    Win nxt;
-    if (T + 32 < sp.tok_end) ld.load(T + 32, nxt);
-    const bool partial = (T < sp.tok_begin) || (T + 32 > sp.tok_end) || cur.ok != 3u;
+  // 32 tokens starting at T, from the loaded window `w`.
+  __device__ __forceinline__ void window(const Win &w, int32_t T) {
+    const bool partial = (T < sp.tok_begin) || (T + 32 > sp.tok_end) || w.ok != 3u;
 
-    // ---- INT2: zero term of the pair, sum over the group of q (z + 2 s) ----
+    // INT2: zero term of the pair, sum over the group of q (z + 2 s).
     f4 c2[QT];
     if (CLS == KVQ_INT2) {
-      const uint32_t ks[4] = {cur.ks.x, cur.ks.y, cur.ks.z, cur.ks.w};
-      const uint32_t kz[4] = {cur.kz.x, cur.kz.y, cur.kz.z, cur.kz.w};
+      const uint32_t ks[4] = {w.ks.x, w.ks.y, w.ks.z, w.ks.w};
+      const uint32_t kz[4] = {w.kz.x, w.kz.y, w.kz.z, w.kz.w};
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         float bz = 0.0f, bs = 0.0f;
@@ -383,27 +430,28 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
       }
     }
 
-    // ---- QK^T: logit (base 2) of query 4 qt + lb and token T + 16 h + lr ----
+    // QK^T: logit (base 2) of query 4 qt + lb and token T + 16 h + lr.
     float x[QT][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       h8 kb[4];
       if (CLS == KVQ_INT4) {
-        const uint4 w = cur.k[h][0];
-        kb[0] = k4_word(w.x);
-        kb[1] = k4_word(w.y);
-        kb[2] = k4_word(w.z);
-        kb[3] = k4_word(w.w);
+        const uint4 v = w.k[h][0];
+        kb[0] = cvt_k4(v.x, k);
+        kb[1] = cvt_k4(v.y, k);
+        kb[2] = cvt_k4(v.z, k);
+        kb[3] = cvt_k4(v.w, k);
       } else if (CLS == KVQ_INT2) {
-        const uint4 w = cur.k[h][0];
-        const h8 c[4] = {k2_byte(w.x), k2_byte(w.x >> 8), k2_byte(w.y), k2_byte(w.y >> 8)};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) kb[m] = c[m] * h8_of(cur.kg[m]);  // s (c - 2): exact
+        const uint4 v = w.k[h][0];
+        kb[0] = cvt_k2(v.x, k) * h8_of(w.kg[0]);  // s (c - 2): exact in fp16
+        kb[1] = cvt_k2(v.x >> 8, k) * h8_of(w.kg[1]);
+        kb[2] = cvt_k2(v.y, k) * h8_of(w.kg[2]);
+        kb[3] = cvt_k2(v.y >> 8, k) * h8_of(w.kg[3]);
       } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) kb[m] = h8_of(cur.k[h][m]);
+        for (int m = 0; m < 4; ++m) kb[m] = h8_of(w.k[h][m]);
       }
-      const bool live = cur.live >> h & 1;
+      const bool live = w.live >> h & 1;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         f4 d = CLS == KVQ_INT2 ? c2[qt] : f4{0.f, 0.f, 0.f, 0.f};
@@ -411,7 +459,7 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
         for (int m = 0; m < 4; ++m) d = mfma(Aq[qt][m], kb[m], d);
         float s;
         if (CLS == KVQ_INT4) {
-          const uint32_t mm[4] = {cur.km[h].x, cur.km[h].y, cur.km[h].z, cur.km[h].w};
+          const uint32_t mm[4] = {w.km[h].x, w.km[h].y, w.km[h].z, w.km[h].w};
           s = 0.0f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -425,60 +473,61 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
       }
     }
 
-    // ---- online softmax (per query: the 16 lanes of row lb) ----
+    // Online softmax per query (the 16 lanes of row lb).
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float bm = row_max16(fmaxf(x[qt][0], x[qt][1]));
       const float mn = fmaxf(m_run[qt], bm);
-      if (__any(mn > m_run[qt])) {
-        const float alpha = mn == -INFINITY ? 1.0f : exp2f(m_run[qt] - mn);
+      if (__any(mn > m_run[qt])) {  // rare after the first windows
+        const float alpha = exp2f(m_run[qt] - mn);
         l_run[qt] *= alpha;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
         zacc[qt] *= __shfl(alpha, 16 * (lr >> 2));  // zero-term rows belong to query lr / 4
         m_run[qt] = mn;
       }
-      const float p0 = x[qt][0] == -INFINITY ? 0.0f : exp2f(x[qt][0] - m_run[qt]);
-      const float p1 = x[qt][1] == -INFINITY ? 0.0f : exp2f(x[qt][1] - m_run[qt]);
+      const float p0 = exp2f(x[qt][0] - m_run[qt]), p1 = exp2f(x[qt][1] - m_run[qt]);
       l_run[qt] += p0 + p1;
       L.p[qt][lb][lr] = (_Float16)p0;
       L.p[qt][lb][16 + lr] = (_Float16)p1;
     }
 
-    // ---- V operand: this lane's channels 8 lr + nt, its 8 tokens as 4 pairs ----
+    // V operand: this lane's channels 8 lr + nt, its 8 tokens as 4 pairs.
     h8 vb[8];
     {
       uint32_t t[8][4];  // [nt][token pair]
       if (CLS == KVQ_INT4) {
+        const h2 lo = {(_Float16)1032.0f, (_Float16)1032.0f}, hi = {(_Float16)72.0f, (_Float16)72.0f};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t wa = cur.v[2 * u].x, wb = cur.v[2 * u + 1].x;
+          const uint32_t wa = w.v[2 * u].x, wb = w.v[2 * u + 1].x;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const uint32_t y = pair_bytes(wa, wb, b);
-            const int lo = b == 0 ? 0 : b == 1 ? 4 : b == 2 ? 1 : 5;  // channel in the low nibble
-            t[lo][u] = as_u32(as_h2((y & 0x000F000Fu) | 0x64006400u) - h2{(_Float16)1032.0f, (_Float16)1032.0f});
-            t[lo + 2][u] = as_u32(as_h2((y & 0x00F000F0u) | 0x54005400u) - h2{(_Float16)72.0f, (_Float16)72.0f});
+            const int c = b == 0 ? 0 : b == 1 ? 4 : b == 2 ? 1 : 5;  // channel in the low nibble
+            t[c][u] = as_u32(as_h2((y & k.m000F) | 0x64006400u) - lo);
+            t[c + 2][u] = as_u32(as_h2((y & k.m00F0) | 0x54005400u) - hi);
           }
         }
       } else if (CLS == KVQ_INT2) {
         const int be = lr & 1;  // byte of this lane's even channels (odd ones: be + 2)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t wa = cur.v[2 * u].x, wb = cur.v[2 * u + 1].x;
+          const uint32_t wa = w.v[2 * u].x, wb = w.v[2 * u + 1].x;
 #pragma unroll
           for (int par = 0; par < 2; ++par) {
-            const uint32_t y = pair_bytes(wa, wb, be + 2 * par);
-            t[par + 0][u] = as_u32(as_h2((y & 0x00030003u) | 0x64006400u) - h2{(_Float16)1026.0f, (_Float16)1026.0f});
-            t[par + 2][u] = as_u32(as_h2((y & 0x000C000Cu) | 0x5C005C00u) - h2{(_Float16)258.0f, (_Float16)258.0f});
-            t[par + 4][u] = as_u32(as_h2((y & 0x00300030u) | 0x54005400u) - h2{(_Float16)66.0f, (_Float16)66.0f});
-            t[par + 6][u] = as_u32(as_h2((y & 0x00C000C0u) | 0x4C004C00u) - h2{(_Float16)18.0f, (_Float16)18.0f});
+            const h8 c = cvt_k2(pair_bytes(wa, wb, be + 2 * par), k);
+            const u4v cv = __builtin_bit_cast(u4v, c);
+            t[par + 0][u] = cv[0];
+            t[par + 2][u] = cv[1];
+            t[par + 4][u] = cv[2];
+            t[par + 6][u] = cv[3];
           }
         }
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint4 ra = cur.v[2 * u], rb = cur.v[2 * u + 1];
+          const uint4 ra = w.v[2 * u], rb = w.v[2 * u + 1];
           const uint32_t da[4] = {ra.x, ra.y, ra.z, ra.w}, db[4] = {rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
           for (int nt = 0; nt < 8; ++nt) {
@@ -489,8 +538,8 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
         if (partial) {  // absent or dead tokens: keep the operand finite
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const uint32_t mk = ((cur.vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
-                                ((cur.vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
+            const uint32_t mk = ((w.vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
+                                ((w.vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) t[nt][u] &= mk;
           }
@@ -501,7 +550,7 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
     }
     __syncthreads();  // the weights of this window are in LDS
 
-    // ---- P V ----
+    // P V.
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const uint4 pw = *reinterpret_cast<const uint4 *>(&L.p[qt][lr >> 2][8 * lb]);
@@ -510,17 +559,17 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
         ap = h8_of(pw);
       } else {
         const uint32_t p2[4] = {pw.x, pw.y, pw.z, pw.w};
-        const uint32_t mv[8] = {cur.vm[0].x, cur.vm[0].y, cur.vm[0].z, cur.vm[0].w,
-                                cur.vm[1].x, cur.vm[1].y, cur.vm[1].z, cur.vm[1].w};
+        const uint32_t mv[8] = {w.vm[0].x, w.vm[0].y, w.vm[0].z, w.vm[0].w,
+                                w.vm[1].x, w.vm[1].y, w.vm[1].z, w.vm[1].w};
         const _Float16 center = CLS == KVQ_INT4 ? (_Float16)8.0f : (_Float16)2.0f;
         uint32_t aw[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          uint32_t s2 = (mv[2 * u] & 0xffffu) | (mv[2 * u + 1] << 16);      // scales
-          uint32_t z2 = (mv[2 * u] >> 16) | (mv[2 * u + 1] & 0xffff0000u);  // zeros
+          uint32_t s2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x05040100u);  // scales
+          uint32_t z2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x07060302u);  // zeros
           if (partial) {
-            const uint32_t mk = ((cur.vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
-                                ((cur.vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
+            const uint32_t mk = ((w.vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
+                                ((w.vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
             s2 &= mk;
             z2 &= mk;
           }
@@ -534,35 +583,62 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = mfma(ap, vb[nt], acc[qt][nt]);
     }
-    cur = nxt;
   }
 
-  // ---- epilogue: lane (lr, lb) owns query 4 qt + lb, channels 8 lr .. 8 lr + 7 ----
+  // Normalize and store: lane (lr, lb) owns query 4 qt + lb, channels 8 lr .. 8 lr + 7.
+  __device__ void finish(int s_idx) {
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float l_tot = row_sum16(l_run[qt]);
-    float z = zacc[qt];
-    z += __shfl_xor(z, 16);
-    z += __shfl_xor(z, 32);
-    const float zrow = __shfl(z, 4 * lb + (lr >> 2));  // row (query lb, group lr / 4)
-    const int j = 4 * qt + lb;
-    const bool any = l_tot > 0.0f;
-    const float inv = any ? 1.0f / l_tot : 0.0f;
-    const int r = lr >> 2;
-    float o[8];
+    for (int qt = 0; qt < QT; ++qt) {
+      const float l_tot = row_sum16(l_run[qt]);
+      float z = zacc[qt];
+      z += __shfl_xor(z, 16);
+      z += __shfl_xor(z, 32);
+      const float zrow = __shfl(z, 4 * lb + (lr >> 2));  // row (query lb, group lr / 4)
+      const int j = 4 * qt + lb;
+      const bool any = l_tot > 0.0f;
+      const float inv = any ? 1.0f / l_tot : 0.0f;
+      const int r = lr >> 2;
+      float o[8];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const f4 d = acc[qt][nt];
-      const float v = r == 0 ? d[0] : r == 1 ? d[1] : r == 2 ? d[2] : d[3];
-      o[nt] = any ? (v + (CLS == KVQ_FP16 ? 0.0f : zrow)) * inv : 0.0f;
-    }
-    if (j < a.g) {
-      float4 *dst = reinterpret_cast<float4 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 8 * lr);
-      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-      if (lr == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (m_run[qt] + log2f(l_tot)) * kLn2 : -INFINITY;
+      for (int nt = 0; nt < 8; ++nt) {
+        const f4 d = acc[qt][nt];
+        const float v = r == 0 ? d[0] : r == 1 ? d[1] : r == 2 ? d[2] : d[3];
+        o[nt] = any ? (v + (CLS == KVQ_FP16 ? 0.0f : zrow)) * inv : 0.0f;
+      }
+      if (j < a.g) {
+        float4 *dst = reinterpret_cast<float4 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 8 * lr);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        if (lr == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (m_run[qt] + log2f(l_tot)) * kLn2 : -INFINITY;
+      }
     }
   }
+};
+
+template <int QT, int CLS, bool SLOTS>
+__device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L) {
+  const Loader<CLS, SLOTS> ld(a, sp, threadIdx.x);
+  SplitRun<QT, CLS, SLOTS> R(a, sp, L, ld);
+  // Two window buffers used alternately: the loads of the next 32 tokens are issued
+  // before the current 32 are computed, unconditionally (the last step reloads the
+  // current window), so no wait ever has to drain them early.
+  const int32_t end = sp.tok_end;
+  int32_t T = SLOTS ? sp.tok_begin : (sp.tok_begin & ~15);
+  Win wa, wb;
+  ld.load(T, wa);
+  for (;;) {
+    const int32_t T1 = T + 32;
+    ld.load(T1 < end ? T1 : T, wb);
+    R.window(wa, T);
+    if (T1 >= end) break;
+    const int32_t T2 = T1 + 32;
+    ld.load(T2 < end ? T2 : T1, wa);
+    R.window(wb, T1);
+    if (T2 >= end) break;
+    T = T2;
+  }
+  if (ld.errs) report(a.err, (int32_t)ld.errs);  // bad ids met by this lane (rare)
+  R.finish(s_idx);
 }
 
 template <int QT, bool SLOTS>
@@ -692,9 +768,9 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
   a.n2 = c->n_pages[0];
   a.n4 = c->n_pages[1];
   a.n16 = c->n_pages[2];
-  a.pool2 = static_cast<const uint8_t *>(c->pool[0]);
-  a.pool4 = static_cast<const uint8_t *>(c->pool[1]);
-  a.pool16 = static_cast<const uint8_t *>(c->pool[2]);
+  a.pool2 = (gbytes)c->pool[0];
+  a.pool4 = (gbytes)c->pool[1];
+  a.pool16 = (gbytes)c->pool[2];
   a.sentinel = c->sentinel_slot;
   a.q = q;
   a.q_dtype = q_dtype;
