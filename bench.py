@@ -68,7 +68,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=36)
-    ap.add_argument("--target-bytes", type=int, default=1 << 18, help="effective bytes per split")
+    ap.add_argument("--splits-per-head", type=int, default=0,
+                    help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
@@ -120,8 +121,12 @@ def main():
     for t in range(w0.n_tables):
         items += w0.alloc.ranges_after_partition(t, list(range(w0.heads_per_page)))
     ranges = synth.ranges_array(items)
+    # One wave per split; fill every resident slot of the chip once (a second, partial
+    # round of waves would leave most of the chip idle at the end).
+    per_cu, n_cu = kvq.decode_occupancy(w0.g)
+    sph = args.splits_per_head or max(1, (per_cu * n_cu) // (w0.batch * w0.hkv))
     splits, offsets = kvq.plan_splits(ranges, w0.batch, w0.hkv, w0.heads_per_page,
-                                      target_bytes=args.target_bytes)
+                                      splits_per_head=np.full(w0.batch * w0.hkv, sph, np.int32))
     n_splits = splits.shape[0]
     sp = torch.as_tensor(splits, device=dev).contiguous()
     off = torch.as_tensor(offsets, device=dev)
@@ -135,7 +140,8 @@ def main():
            for L in range(args.layers)]
     torch.cuda.synchronize()
     assert int(err.item()) == 0, f"device error bits {int(err.item())}"
-    log(f"setup {time.time() - t0:.1f}s: {args.layers} layers, {n_splits} splits per layer, "
+    log(f"setup {time.time() - t0:.1f}s: {args.layers} layers, {n_splits} splits per layer "
+        f"({sph} per head; {per_cu} resident per CU x {n_cu} CUs), "
         f"pools {sum(sum(p.numel() for p in c.pools) for c in caches) / 2**30:.1f} GiB")
 
     def step():
@@ -144,12 +150,16 @@ def main():
             mrg[L]()
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log("copy calibration: one 1 GiB device-to-device copy")
+        # Known-size references for the HBM byte counters: 1 GiB read + 1 GiB written,
+        # once as bytes and once as float32 (torch picks a different copy kernel for each).
+        for dt in (torch.uint8, torch.float32):
+            src = torch.ones((1 << 30) // torch.empty((), dtype=dt).element_size(), dtype=dt, device=dev)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        log("copy calibration: two 1 GiB device-to-device copies (uint8, float32)")
 
     for _ in range(args.warmup):
         step()

@@ -213,8 +213,11 @@ kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, int32_t n_s
  * (INT2 pieces on 32-token boundaries); the number of pieces is, in order of
  * precedence:
  *   splits_per_head [host, may be NULL]: int32 [n_tables*heads_per_page]
- *     pieces per (table, head), shared among its ranges in proportion to their
- *     bytes (at least one each);
+ *     pieces per (table, head), shared among its non-empty ranges in proportion
+ *     to their decode cost (tokens x 1.0 / 1.3 / 4.0 for INT2 / INT4 / FP16:
+ *     the kernel's relative time per token-head on MI355X), at least one each,
+ *     largest remainders first, so a head gets exactly its count whenever that
+ *     is at least its number of non-empty ranges;
  *   tokens_per_split[cls] > 0 [host, may be NULL]: ceil(tokens / that);
  *   otherwise max(1, round(range bytes / target_bytes)) with 96 / 160 / 512
  *     bytes per INT2 / INT4 / FP16 token-head.

@@ -115,32 +115,18 @@ __device__ __forceinline__ float quad_sum(float x) {
 
 // ------------------------------------------------------------ code -> fp16 ----
 
-// Exact centered fp16 codes.  A code OR-ed into the low mantissa bits of a power of
-// two gives 2^e + c exactly (1024 + c for bits 0-3 / 0-1, 256 + c for bits 2-3,
-// 64 + c for bits 4-7 / 4-5, 16 + c for bits 6-7); one packed fp16 subtraction of
-// 2^e + center then leaves c - center, exact in fp16.
+// A code OR-ed into the low mantissa bits of a power of two gives 2^e + c exactly
+// in fp16 (1024 + c for bits 0-3 / 0-1, 256 + c for bits 2-3, 64 + c for bits 4-7 /
+// 4-5, 16 + c for bits 6-7).  The K operand of INT2 subtracts 2^e + 2 to get the
+// exact centered code; the INT4 K and all V operands keep the offset 2^e and
+// remove its contribution after the product: the query is exact in fp16, and the
+// V side subtracts 2^e times the sum of the very fp16 weights that entered the
+// product, so only fp32 rounding of the larger sums remains.
 
-// One INT4 word (channels 8w..8w+7, even ones in the low half) -> c - 8 of the 8
-// channels in channel order.
-__device__ __forceinline__ h8 k4_word(uint32_t x) {
-  const uint32_t y = x >> 8;
-  const h2 lo = {(_Float16)1032.0f, (_Float16)1032.0f}, hi = {(_Float16)72.0f, (_Float16)72.0f};
-  return h8_of(as_u32(as_h2((x & 0x000F000Fu) | 0x64006400u) - lo), as_u32(as_h2((x & 0x00F000F0u) | 0x54005400u) - hi),
-               as_u32(as_h2((y & 0x000F000Fu) | 0x64006400u) - lo), as_u32(as_h2((y & 0x00F000F0u) | 0x54005400u) - hi));
-}
-
-// Eight channels of an INT2 word: `x` holds them in bits 0-7 (even channels) and
-// 16-23 (odd channels) -> c - 2 in channel order.
-__device__ __forceinline__ h8 k2_byte(uint32_t x) {
-  return h8_of(as_u32(as_h2((x & 0x00030003u) | 0x64006400u) - h2{(_Float16)1026.0f, (_Float16)1026.0f}),
-               as_u32(as_h2((x & 0x000C000Cu) | 0x5C005C00u) - h2{(_Float16)258.0f, (_Float16)258.0f}),
-               as_u32(as_h2((x & 0x00300030u) | 0x54005400u) - h2{(_Float16)66.0f, (_Float16)66.0f}),
-               as_u32(as_h2((x & 0x00C000C0u) | 0x4C004C00u) - h2{(_Float16)18.0f, (_Float16)18.0f}));
-}
-
-// Byte b of token word wa in bits 0-7 and of token word wb in bits 16-23.
-__device__ __forceinline__ uint32_t pair_bytes(uint32_t wa, uint32_t wb, int b) {
-  return ((wa >> (8 * b)) & 0xffu) | (((wb >> (8 * b)) & 0xffu) << 16);
+// v_perm selector giving byte b of the first word in bits 0-7 and byte b of the
+// second in bits 16-23 (bytes 1 and 3 zero).
+__host__ __device__ constexpr uint32_t pair_sel(uint32_t b) {
+  return b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
 }
 
 // ------------------------------------------------------------------ args ------
@@ -342,13 +328,14 @@ struct Consts {
         m000C(in_vgpr(0x000C000Cu)), m0030(in_vgpr(0x00300030u)), m00C0(in_vgpr(0x00C000C0u)) {}
 };
 
-// Exact centered codes of 8 channels: INT4 word (c - 8), INT2 bytes (c - 2).
+// INT4 word (channels 8w .. 8w + 7, even ones in the low half) -> 8 fp16 values in
+// channel order: 1024 + c for channels with (ch & 2) == 0, 64 + c for the others.
 __device__ __forceinline__ h8 cvt_k4(uint32_t x, const Consts &k) {
   const uint32_t y = x >> 8;
-  const h2 lo = {(_Float16)1032.0f, (_Float16)1032.0f}, hi = {(_Float16)72.0f, (_Float16)72.0f};
-  return h8_of(as_u32(as_h2((x & k.m000F) | 0x64006400u) - lo), as_u32(as_h2((x & k.m00F0) | 0x54005400u) - hi),
-               as_u32(as_h2((y & k.m000F) | 0x64006400u) - lo), as_u32(as_h2((y & k.m00F0) | 0x54005400u) - hi));
+  return h8_of((x & k.m000F) | 0x64006400u, (x & k.m00F0) | 0x54005400u, (y & k.m000F) | 0x64006400u,
+               (y & k.m00F0) | 0x54005400u);
 }
+// INT2 byte pair (bits 0-7 and 16-23) -> c - 2 of its 8 codes, exact.
 __device__ __forceinline__ h8 cvt_k2(uint32_t x, const Consts &k) {
   return h8_of(as_u32(as_h2((x & k.m0003) | 0x64006400u) - h2{(_Float16)1026.0f, (_Float16)1026.0f}),
                as_u32(as_h2((x & k.m000C) | 0x5C005C00u) - h2{(_Float16)258.0f, (_Float16)258.0f}),
@@ -367,16 +354,22 @@ struct SplitRun {
   const Loader<CLS, SLOTS> &ld;
   const int lane, lr, lb;
   const Consts k;
+  uint32_t sel2[2];    // INT2 V: byte pairs of this lane's even / odd channels
   float scale;
   h8 Aq[QT][4];        // block-diagonal query operand
   h2 qn[QT][4];        // natural-order q pairs: query 4 qt + lb, channels 8 lr .. 8 lr + 7
   float qsum[QT][4];   // per-group sum of q of query 4 qt + lb (INT4 zero term)
+  float qoff[QT][4];   // per-group sum of q x code offset (1024 / 64) of query 4 qt + lb
   f4 acc[QT][8];       // P V accumulators
-  float m_run[QT], l_run[QT], zacc[QT];
+  float m_run[QT], l_run[QT];
+  float zacc[QT];      // row lr: sum of p z over this lane's tokens (V zero term)
+  float asum[QT];      // row lr: sum of the fp16 operand weights p s (V code offset)
 
   __device__ SplitRun(const DecodeArgs &a_, const kvq_split &sp_, Lds<QT> &L_, const Loader<CLS, SLOTS> &ld_)
       : a(a_), sp(sp_), L(L_), ld(ld_), lane(threadIdx.x), lr(threadIdx.x & 15), lb(threadIdx.x >> 4) {
     scale = kLog2e / sqrtf((float)kHeadDim);
+    sel2[0] = pair_sel(lr & 1);  // byte lr & 1: even channels of the lane's half word
+    sel2[1] = pair_sel((lr & 1) + 2);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const int jr = 4 * qt + (lr >> 2), gi = lr & 3;
@@ -390,18 +383,25 @@ struct SplitRun {
         }
         Aq[qt][m] = h8_of(w[0], w[1], w[2], w[3]);
       }
-      float ps = 0.0f;
+      float ps = 0.0f, po = 0.0f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         qn[qt][u] = h2{(_Float16)L.q[4 * qt + lb][8 * lr + 2 * u], (_Float16)L.q[4 * qt + lb][8 * lr + 2 * u + 1]};
-        ps += (float)qn[qt][u][0] + (float)qn[qt][u][1];
+        const float pair = (float)qn[qt][u][0] + (float)qn[qt][u][1];
+        ps += pair;
+        po += (u & 1 ? 64.0f : 1024.0f) * pair;  // channels 8 lr + 2 u, + 1: (ch & 2) == 2 u & 2
       }
       ps = quad_sum(ps);  // lanes (lb, lr): query 4 qt + lb, group lr / 4
+      po = quad_sum(po);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) qsum[qt][r] = __shfl(ps, 16 * lb + 4 * r);
+      for (int r = 0; r < 4; ++r) {
+        qsum[qt][r] = __shfl(ps, 16 * lb + 4 * r);
+        qoff[qt][r] = __shfl(po, 16 * lb + 4 * r);
+      }
       m_run[qt] = kNegBig;
       l_run[qt] = 0.0f;
       zacc[qt] = 0.0f;
+      asum[qt] = 0.0f;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -462,10 +462,8 @@ struct SplitRun {
           const uint32_t mm[4] = {w.km[h].x, w.km[h].y, w.km[h].z, w.km[h].w};
           s = 0.0f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float sc = h2f(mm[r]), zc = fmaf(8.0f, sc, h2f(mm[r] >> 16));  // z + 8 s
-            s = fmaf(sc, d[r], fmaf(zc, qsum[qt][r], s));
-          }
+          for (int r = 0; r < 4; ++r)  // s (q . (offset + c) - q . offset) + z sum(q)
+            s = fmaf(h2f(mm[r]), d[r] - qoff[qt][r], fmaf(h2f(mm[r] >> 16), qsum[qt][r], s));
         } else {
           s = (d[0] + d[1]) + (d[2] + d[3]);
         }
@@ -483,7 +481,9 @@ struct SplitRun {
         l_run[qt] *= alpha;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
-        zacc[qt] *= __shfl(alpha, 16 * (lr >> 2));  // zero-term rows belong to query lr / 4
+        const float alpha_row = __shfl(alpha, 16 * (lr >> 2));  // rows lr belong to query lr / 4
+        zacc[qt] *= alpha_row;
+        asum[qt] *= alpha_row;
         m_run[qt] = mn;
       }
       const float p0 = exp2f(x[qt][0] - m_run[qt]), p1 = exp2f(x[qt][1] - m_run[qt]);
@@ -496,32 +496,31 @@ struct SplitRun {
     h8 vb[8];
     {
       uint32_t t[8][4];  // [nt][token pair]
-      if (CLS == KVQ_INT4) {
-        const h2 lo = {(_Float16)1032.0f, (_Float16)1032.0f}, hi = {(_Float16)72.0f, (_Float16)72.0f};
+      // Codes go to bits 4-7 / 4-5 / 6-7 only (offset 64 / 64 / 16): the offsets'
+      // share of the fp32 accumulators, and so its rounding, stays small.
+      if (CLS == KVQ_INT4) {  // 64 + c for every channel
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const uint32_t wa = w.v[2 * u].x, wb = w.v[2 * u + 1].x;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const uint32_t y = pair_bytes(wa, wb, b);
+            const uint32_t y = __builtin_amdgcn_perm(wb, wa, pair_sel(b));
             const int c = b == 0 ? 0 : b == 1 ? 4 : b == 2 ? 1 : 5;  // channel in the low nibble
-            t[c][u] = as_u32(as_h2((y & k.m000F) | 0x64006400u) - lo);
-            t[c + 2][u] = as_u32(as_h2((y & k.m00F0) | 0x54005400u) - hi);
+            t[c][u] = ((y << 4) & k.m00F0) | 0x54005400u;
+            t[c + 2][u] = (y & k.m00F0) | 0x54005400u;
           }
         }
-      } else if (CLS == KVQ_INT2) {
-        const int be = lr & 1;  // byte of this lane's even channels (odd ones: be + 2)
+      } else if (CLS == KVQ_INT2) {  // 64 + c for channels with (nt >> 1) even, 16 + c for odd
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const uint32_t wa = w.v[2 * u].x, wb = w.v[2 * u + 1].x;
 #pragma unroll
           for (int par = 0; par < 2; ++par) {
-            const h8 c = cvt_k2(pair_bytes(wa, wb, be + 2 * par), k);
-            const u4v cv = __builtin_bit_cast(u4v, c);
-            t[par + 0][u] = cv[0];
-            t[par + 2][u] = cv[1];
-            t[par + 4][u] = cv[2];
-            t[par + 6][u] = cv[3];
+            const uint32_t y = __builtin_amdgcn_perm(wb, wa, sel2[par]), y4 = y << 4;
+            t[par + 0][u] = (y4 & k.m0030) | 0x54005400u;
+            t[par + 2][u] = (y4 & k.m00C0) | 0x4C004C00u;
+            t[par + 4][u] = (y & k.m0030) | 0x54005400u;
+            t[par + 6][u] = (y & k.m00C0) | 0x4C004C00u;
           }
         }
       } else {
@@ -561,7 +560,6 @@ struct SplitRun {
         const uint32_t p2[4] = {pw.x, pw.y, pw.z, pw.w};
         const uint32_t mv[8] = {w.vm[0].x, w.vm[0].y, w.vm[0].z, w.vm[0].w,
                                 w.vm[1].x, w.vm[1].y, w.vm[1].z, w.vm[1].w};
-        const _Float16 center = CLS == KVQ_INT4 ? (_Float16)8.0f : (_Float16)2.0f;
         uint32_t aw[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -573,10 +571,10 @@ struct SplitRun {
             s2 &= mk;
             z2 &= mk;
           }
-          const h2 sv = as_h2(s2), pp = as_h2(p2[u]);
-          const h2 zc = sv * h2{center, center} + as_h2(z2);
-          aw[u] = as_u32(pp * sv);
-          zacc[qt] = dot2(pp, zc, zacc[qt]);
+          const h2 pp = as_h2(p2[u]), ap2 = pp * as_h2(s2);
+          aw[u] = as_u32(ap2);
+          zacc[qt] = dot2(pp, as_h2(z2), zacc[qt]);
+          asum[qt] = dot2(ap2, h2{(_Float16)1.0f, (_Float16)1.0f}, asum[qt]);
         }
         ap = h8_of(aw[0], aw[1], aw[2], aw[3]);
       }
@@ -590,10 +588,13 @@ struct SplitRun {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float l_tot = row_sum16(l_run[qt]);
-      float z = zacc[qt];
+      float z = zacc[qt], as = asum[qt];
       z += __shfl_xor(z, 16);
       z += __shfl_xor(z, 32);
+      as += __shfl_xor(as, 16);
+      as += __shfl_xor(as, 32);
       const float zrow = __shfl(z, 4 * lb + (lr >> 2));  // row (query lb, group lr / 4)
+      const float arow = __shfl(as, 4 * lb + (lr >> 2));
       const int j = 4 * qt + lb;
       const bool any = l_tot > 0.0f;
       const float inv = any ? 1.0f / l_tot : 0.0f;
@@ -603,7 +604,10 @@ struct SplitRun {
       for (int nt = 0; nt < 8; ++nt) {
         const f4 d = acc[qt][nt];
         const float v = r == 0 ? d[0] : r == 1 ? d[1] : r == 2 ? d[2] : d[3];
-        o[nt] = any ? (v + (CLS == KVQ_FP16 ? 0.0f : zrow)) * inv : 0.0f;
+        float off = 0.0f;  // code offset of channel 8 lr + nt in the V operand
+        if (CLS == KVQ_INT4) off = 64.0f;
+        if (CLS == KVQ_INT2) off = (nt >> 1) & 1 ? 16.0f : 64.0f;
+        o[nt] = any ? (CLS == KVQ_FP16 ? v : fmaf(-off, arow, v) + zrow) * inv : 0.0f;
       }
       if (j < a.g) {
         float4 *dst = reinterpret_cast<float4 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 8 * lr);

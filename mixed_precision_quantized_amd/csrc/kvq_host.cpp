@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "kvq_internal.h"
@@ -43,6 +44,11 @@ kvq_status check_cache(const kvq_cache *c) {
 }
 
 static int64_t token_bytes(int cls) { return cls == KVQ_INT2 ? 96 : cls == KVQ_INT4 ? 160 : 512; }
+
+// Relative decode time of one token-head per class on MI355X, used to share a head's
+// split count among its ranges: INT2 windows are bound by dequantization work, INT4
+// and FP16 ones by their bytes (160 / 512 B against 96 B).
+static double token_cost(int cls) { return cls == KVQ_INT2 ? 1.0 : cls == KVQ_INT4 ? 1.3 : 4.0; }
 
 }  // namespace kvq
 
@@ -104,9 +110,6 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
     return fail(KVQ_ERR_INVALID_ARG, "NULL plan array");
   const int32_t tpr = hkv / heads_per_page;
   const int32_t n_tables = batch * tpr;
-  // Bytes per (table, head) to share splits_per_head among its ranges.
-  std::vector<int64_t> head_bytes;
-  if (splits_per_head) head_bytes.assign((size_t)n_tables * heads_per_page, 0);
   for (int32_t i = 0; i < n_ranges; ++i) {
     const kvq_split &r = ranges[i];
     if (r.table < 0 || r.table >= n_tables || r.head < 0 || r.head >= heads_per_page || r.cls < 0 ||
@@ -119,8 +122,54 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
       if (p.table > r.table || (p.table == r.table && p.head > r.head))
         return fail(KVQ_ERR_INVALID_ARG, "ranges are not sorted by (table, head) at %d", i);
     }
-    if (splits_per_head) head_bytes[(size_t)r.table * heads_per_page + r.head] +=
-        (int64_t)(r.tok_end - r.tok_begin) * token_bytes(r.cls);
+  }
+  // Pieces per range.
+  std::vector<int64_t> pieces((size_t)n_ranges, 0);
+  for (int32_t i0 = 0, i1; i0 < n_ranges; i0 = i1) {
+    i1 = i0 + 1;
+    while (i1 < n_ranges && ranges[i1].table == ranges[i0].table && ranges[i1].head == ranges[i0].head) ++i1;
+    if (splits_per_head) {
+      // Share the head's count in proportion to decode cost (largest remainders, so
+      // the shares add up to the count when it is at least the number of ranges).
+      const int64_t total = splits_per_head[(size_t)ranges[i0].table * heads_per_page + ranges[i0].head];
+      double cost_sum = 0.0;
+      int32_t n_live = 0;
+      for (int32_t i = i0; i < i1; ++i) {
+        const int64_t toks = ranges[i].tok_end - ranges[i].tok_begin;
+        if (toks > 0) ++n_live;
+        cost_sum += (double)toks * token_cost(ranges[i].cls);
+      }
+      if (n_live == 0) continue;
+      const int64_t spare = std::max<int64_t>(0, total - n_live);  // beyond one piece each
+      std::vector<std::pair<double, int32_t>> frac;
+      int64_t given = 0;
+      for (int32_t i = i0; i < i1; ++i) {
+        const int64_t toks = ranges[i].tok_end - ranges[i].tok_begin;
+        if (toks == 0) continue;
+        const double share = (double)spare * (double)toks * token_cost(ranges[i].cls) / cost_sum;
+        const int64_t whole = (int64_t)std::floor(share);
+        pieces[i] = 1 + whole;
+        given += whole;
+        frac.push_back({share - (double)whole, i});
+      }
+      std::stable_sort(frac.begin(), frac.end(),
+                       [](const std::pair<double, int32_t> &x, const std::pair<double, int32_t> &y) {
+                         return x.first > y.first;
+                       });
+      for (size_t k = 0; given < spare && k < frac.size(); ++k, ++given) ++pieces[frac[k].second];
+    } else {
+      for (int32_t i = i0; i < i1; ++i) {
+        const kvq_split &r = ranges[i];
+        const int64_t toks = r.tok_end - r.tok_begin;
+        if (toks == 0) continue;
+        if (tokens_per_split && tokens_per_split[r.cls] > 0)
+          pieces[i] = (toks + tokens_per_split[r.cls] - 1) / tokens_per_split[r.cls];
+        else if (target_bytes > 0)
+          pieces[i] = std::max<int64_t>(1, std::llround((double)(toks * token_bytes(r.cls)) / (double)target_bytes));
+        else
+          pieces[i] = 1;
+      }
+    }
   }
   int32_t w = 0;
   int32_t next_pair = 0;  // next (b*hkv + kvh) whose offset is still unset
@@ -131,25 +180,12 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
     const int32_t unit = r.cls == KVQ_INT2 ? kGroup : 1;
     const int64_t units = (r.tok_end - r.tok_begin) / unit;
     if (units == 0) continue;
-    const int64_t bytes = (int64_t)(r.tok_end - r.tok_begin) * token_bytes(r.cls);
-    int64_t pieces;
-    if (splits_per_head) {
-      const size_t hk = (size_t)r.table * heads_per_page + r.head;
-      const double share = (double)splits_per_head[hk] * (double)bytes / (double)head_bytes[hk];
-      pieces = std::max<int64_t>(1, std::llround(share));
-    } else if (tokens_per_split && tokens_per_split[r.cls] > 0) {
-      pieces = ((int64_t)(r.tok_end - r.tok_begin) + tokens_per_split[r.cls] - 1) / tokens_per_split[r.cls];
-    } else if (target_bytes > 0) {
-      pieces = std::max<int64_t>(1, std::llround((double)bytes / (double)target_bytes));
-    } else {
-      pieces = 1;
-    }
-    pieces = std::min(pieces, units);
-    for (int64_t p = 0; p < pieces; ++p) {
+    const int64_t n = std::min(pieces[i], units);
+    for (int64_t p = 0; p < n; ++p) {
       if (w >= max_out) return fail(KVQ_ERR_CAPACITY, "more than %d splits", max_out);
-      const int64_t a = units * p / pieces, b = units * (p + 1) / pieces;
+      const int64_t a = units * p / n, b = units * (p + 1) / n;
       out[w++] = kvq_split{r.table, r.head, r.cls, (int32_t)(r.tok_begin + a * unit),
-                           p + 1 == pieces ? r.tok_end : (int32_t)(r.tok_begin + b * unit)};
+                           p + 1 == n ? r.tok_end : (int32_t)(r.tok_begin + b * unit)};
     }
   }
   while (next_pair <= batch * hkv) split_offsets[next_pair++] = w;
