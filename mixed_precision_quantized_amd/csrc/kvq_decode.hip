@@ -143,6 +143,7 @@ struct DecodeArgs {
   int32_t n_splits;
   float *part_o, *part_lse;
   int32_t *err;
+  int32_t only_fp16;  // page mode with the LDS-staged kernel present: this kernel takes FP16 splits only
 };
 
 // The pages of one class: ids first .. first + count - 1 of the unified numbering,
@@ -351,7 +352,6 @@ struct SplitRun {
   const DecodeArgs &a;
   const kvq_split &sp;
   Lds<QT> &L;
-  const Loader<CLS, SLOTS> &ld;
   const int lane, lr, lb;
   const Consts k;
   uint32_t sel2[2];    // INT2 V: byte pairs of this lane's even / odd channels
@@ -365,8 +365,8 @@ struct SplitRun {
   float zacc[QT];      // row lr: sum of p z over this lane's tokens (V zero term)
   float asum[QT];      // row lr: sum of the fp16 operand weights p s (V code offset)
 
-  __device__ SplitRun(const DecodeArgs &a_, const kvq_split &sp_, Lds<QT> &L_, const Loader<CLS, SLOTS> &ld_)
-      : a(a_), sp(sp_), L(L_), ld(ld_), lane(threadIdx.x), lr(threadIdx.x & 15), lb(threadIdx.x >> 4) {
+  __device__ SplitRun(const DecodeArgs &a_, const kvq_split &sp_, Lds<QT> &L_)
+      : a(a_), sp(sp_), L(L_), lane(threadIdx.x), lr(threadIdx.x & 15), lb(threadIdx.x >> 4) {
     scale = kLog2e / sqrtf((float)kHeadDim);
     sel2[0] = pair_sel(lr & 1);  // byte lr & 1: even channels of the lane's half word
     sel2[1] = pair_sel((lr & 1) + 2);
@@ -622,7 +622,7 @@ struct SplitRun {
 template <int QT, int CLS, bool SLOTS>
 __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L) {
   const Loader<CLS, SLOTS> ld(a, sp, threadIdx.x);
-  SplitRun<QT, CLS, SLOTS> R(a, sp, L, ld);
+  SplitRun<QT, CLS, SLOTS> R(a, sp, L);
   // Two window buffers used alternately: the loads of the next 32 tokens are issued
   // before the current 32 are computed, unconditionally (the last step reloads the
   // current window), so no wait ever has to drain them early.
@@ -645,25 +645,217 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
   R.finish(s_idx);
 }
 
-template <int QT, bool SLOTS>
-__global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
-  __shared__ Lds<QT> L;
+// ------------------------------------------------------- LDS-staged path -----
+//
+// Page-table mode, INT2 / INT4 splits.  Every 32-token window is copied HBM -> LDS
+// by global_load_lds_dwordx4 (each lane moves 16 B, one instruction fills a 1 KB
+// chunk at M0) into a per-wave ring of window slots, several windows ahead of the
+// one being computed; no registers hold bytes in flight, so the prefetch depth is
+// set by LDS, not by the register file.  The copies are issued from inline assembly
+// and waited for with explicit vmcnt counts (the compiler would otherwise wait for
+// every copy in flight before each LDS read); the compute is the register path's.
+
+constexpr int kRingBytes = 10240;  // per wave: 12 waves fit a CU's LDS
+
+template <int CLS>
+struct RingGeom;
+template <>
+struct RingGeom<KVQ_INT4> {  // K codes x2, V codes x2, meta: 5 KB per window
+  static constexpr int kChunks = 5, kSlots = 2;
+};
+template <>
+struct RingGeom<KVQ_INT2> {  // K codes, V codes, meta: 3 KB per window
+  static constexpr int kChunks = 3, kSlots = 3;
+};
+
+// One 1 KB chunk: lane L copies 16 B from src to LDS byte lds + 16 L.
+__device__ __forceinline__ void dma_chunk(uint32_t lds, gbytes src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"((uint64_t)src)
+               : "memory", "m0");
+}
+
+// Waits until at most N copies issued by this wave are still in flight (they complete
+// in issue order).
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int CLS>
+struct RingLoader {
+  using G = RingGeom<CLS>;
+  static constexpr int kAhead = G::kSlots - 1;  // windows in flight
+  const kvq_split sp;
+  cints crow;
+  const ClassPages<CLS> pages;
+  const int32_t e_first, e_last;
+  const int lane, lr, lb;
+  const uint32_t ring;  // LDS byte address of the ring
+  const uint8_t *lds;   // the same, as a pointer
+  uint32_t errs = 0;
+
+  __device__ RingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_)
+      : sp(s_), crow((cints)(a.tables + (int64_t)s_.table * a.max_entries)), pages(a, s_.head),
+        e_first(s_.tok_begin >> 4), e_last((s_.tok_end - 1) >> 4), lane(threadIdx.x), lr(threadIdx.x & 15),
+        lb(threadIdx.x >> 4), ring((uint32_t)(uintptr_t)ring_), lds(ring_) {}
+
+  __device__ __forceinline__ int32_t entry(int32_t T, int h) const {
+    return crow[__builtin_amdgcn_readfirstlane(min(max((T >> 4) + h, e_first), e_last))];
+  }
+
+  // Copies window T (page ids id0, id1 of its two halves) into slot `slot`; returns
+  // the window's page-half validity bits.  A window past the split's end (`real`
+  // false) copies one 16-byte line to every lane, so the copy count per window stays
+  // fixed at kChunks.
+  __device__ __forceinline__ uint32_t issue(int32_t id0, int32_t id1, bool real, int slot) {
+    const uint32_t r0 = pages.rel(id0), r1 = pages.rel(id1);
+    const bool ok0 = r0 < pages.count, ok1 = r1 < pages.count;
+    if (real && !(ok0 && ok1)) errs |= KVQ_DEVERR_ID;
+    const gbytes b0 = pages.block(ok0 ? r0 : 0u), b1 = pages.block(ok1 ? r1 : 0u);
+    const uint32_t base = ring + (uint32_t)slot * (G::kChunks * 1024);
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // earlier reads of this slot are done
+    if (!real) {
+      for (int c = 0; c < G::kChunks; ++c) dma_chunk(base + 1024 * c, pages.base);
+      return 0u;
+    }
+    const gbytes mb = (lane >> 4) & 1 ? b1 : b0;  // meta chunk: 4 x 256 B pieces
+    if (CLS == KVQ_INT4) {
+      // K codes in reader-lane order (lane L reads 16 B at 16 L), V codes natural.
+      dma_chunk(base, b0 + kI4KC + lr * 64 + lb * 16);
+      dma_chunk(base + 1024, b1 + kI4KC + lr * 64 + lb * 16);
+      dma_chunk(base + 2048, b0 + kI4VC + lane * 16);
+      dma_chunk(base + 3072, b1 + kI4VC + lane * 16);
+      dma_chunk(base + 4096, mb + (lane < 32 ? kI4KM : kI4VM) + (lane & 15) * 16);
+    } else {
+      const gbytes hb = lane < 32 ? b0 : b1;  // K / V codes: 512 B per page, natural
+      dma_chunk(base, hb + kI2KC + (lane & 31) * 16);
+      dma_chunk(base + 1024, hb + kI2VC + (lane & 31) * 16);
+      dma_chunk(base + 2048, mb + (lane < 32 ? kI2KS : kI2VM) + (lane & 15) * 16);
+    }
+    return (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u);
+  }
+
+  // Reads window T from slot `slot` into the register window of the compute.
+  __device__ __forceinline__ void read(int32_t T, int slot, uint32_t ok, Win &w) const {
+    const uint8_t *S = lds + slot * (G::kChunks * 1024);
+    w.ok = ok;
+    w.live = 0;
+    w.vlive = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int32_t t = T + 16 * h + lr;
+      if (t >= sp.tok_begin && t < sp.tok_end && (ok >> h & 1)) w.live |= 1u << h;
+    }
+    const int o0 = 8 * (lb & 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int32_t t = T + 8 * lb + q;
+      if (t >= sp.tok_begin && t < sp.tok_end && (ok >> (lb >> 1) & 1)) w.vlive |= 1u << q;
+    }
+    if (CLS == KVQ_INT4) {
+      const uint8_t *M = S + 4096;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        w.k[h][0] = *reinterpret_cast<const uint4 *>(S + 1024 * h + 16 * lane);
+        w.km[h] = *reinterpret_cast<const uint4 *>(M + 256 * h + 16 * lr);
+      }
+      const uint8_t *V = S + 2048 + 1024 * (lb >> 1) + 64 * o0 + 4 * lr;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 64 * q);
+      const uint8_t *VM = M + 512 + 256 * (lb >> 1) + ((lr & 3) * kPage + o0) * 4;
+      w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
+      w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
+    } else {
+      const uint8_t *M = S + 2048;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(S + 512 * h + 32 * lr + 8 * lb);
+        w.k[h][0] = make_uint4(x.x, x.y, 0, 0);
+      }
+      const uint8_t *KS = M + 256 * (lr >> 3) + 16 * (lr & 7);  // scales; zeros 128 B on
+      w.ks = *reinterpret_cast<const uint4 *>(KS);
+      w.kz = *reinterpret_cast<const uint4 *>(KS + (kI2KZ - kI2KS));
+      const uint8_t *KG = M + 256 * (lb >> 1) + 64 * (lb & 1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) w.kg[m] = *reinterpret_cast<const uint4 *>(KG + 16 * m);
+      const uint8_t *V = S + 1024 + 512 * (lb >> 1) + 32 * o0 + 4 * (lr >> 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 32 * q);
+      const uint8_t *VM = M + 512 + 256 * (lb >> 1) + ((lr & 3) * kPage + o0) * 4;
+      w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
+      w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
+    }
+  }
+};
+
+template <int QT, int CLS>
+__device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L, uint8_t *ring) {
+  using G = RingGeom<CLS>;
+  constexpr int A = RingLoader<CLS>::kAhead;
+  RingLoader<CLS> ld(a, sp, ring);
+  SplitRun<QT, CLS, false> R(a, sp, L);
+  const int32_t T0 = sp.tok_begin & ~15;  // INT2 splits start on 32-token pairs
+  const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
+  // Window i is copied into slot i mod kSlots, A windows ahead of its compute.
+  uint32_t okq = 0;  // validity bits of the windows in flight, 2 per window, newest lowest
+  int32_t id0 = ld.entry(T0, 0), id1 = ld.entry(T0, 1);
+#pragma unroll
+  for (int i = 0; i < A; ++i) {
+    const int32_t Ti = T0 + 32 * i;
+    const int32_t n0 = ld.entry(Ti + 32, 0), n1 = ld.entry(Ti + 32, 1);
+    okq = (okq << 2) | ld.issue(id0, id1, i < nw, i);
+    id0 = n0;
+    id1 = n1;
+  }
+  int slot_c = 0, slot_i = A;  // slots of the window computed and of the window copied
+  for (int32_t n = 0; n < nw; ++n) {
+    const int32_t Ti = T0 + 32 * (n + A);
+    const int32_t n0 = ld.entry(Ti + 32, 0), n1 = ld.entry(Ti + 32, 1);  // ids one window early
+    okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
+    id0 = n0;
+    id1 = n1;
+    wait_copies<A * G::kChunks>();
+    Win w;
+    const int32_t T = T0 + 32 * n;
+    ld.read(T, slot_c, (okq >> (2 * A)) & 3u, w);
+    R.window(w, T);
+    slot_c = slot_c + 1 == G::kSlots ? 0 : slot_c + 1;
+    slot_i = slot_i + 1 == G::kSlots ? 0 : slot_i + 1;
+  }
+  wait_copies<0>();  // no copy outlives the wave
+  if (ld.errs) report(a.err, (int32_t)ld.errs);
+  R.finish(s_idx);
+}
+
+// Checks split s_idx.  A split this launch does not own returns false at once; an
+// owned split that is malformed or empty (or of a class with no pages) gets O = 0,
+// lse = -inf (and an error bit when malformed) and returns false.  Otherwise stages
+// the split's queries, unscaled, in LDS rows 0 .. g - 1 (rows up to 4 QT - 1 zero).
+template <int QT, bool SLOTS, bool RING>
+__device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Lds<QT> &L) {
   const int lane = threadIdx.x;
-  const int s_idx = blockIdx.x;
-  const kvq_split sp = a.splits[s_idx];
+  sp = a.splits[s_idx];
   const int64_t cap = SLOTS ? (int64_t)a.max_entries : (int64_t)a.max_entries * kPage;
   const bool ok = sp.table >= 0 && sp.table < a.n_tables && sp.head >= 0 && sp.head < a.heads &&
                   sp.cls >= 0 && sp.cls <= 2 && sp.tok_begin >= 0 && sp.tok_end >= sp.tok_begin &&
                   sp.tok_end <= cap &&
                   (sp.cls != KVQ_INT2 || (!SLOTS && sp.tok_begin % kGroup == 0 && sp.tok_end % kGroup == 0));
-  if (!ok || sp.tok_end == sp.tok_begin) {
-    if (!ok && lane == 0) report(a.err, KVQ_DEVERR_SPLIT);
+  // Page mode runs two launches: the LDS-staged one owns every split except the FP16
+  // ones of a cache that has FP16 pages, which the register-staged one takes.
+  const bool fp16_elsewhere = ok && sp.cls == KVQ_FP16 && a.n16 > 0;
+  if (!SLOTS && (RING ? fp16_elsewhere : (a.only_fp16 && !fp16_elsewhere))) return false;
+  const int32_t n_cls = !ok ? 0 : sp.cls == KVQ_INT2 ? a.n2 : sp.cls == KVQ_INT4 ? a.n4 : a.n16;
+  if (!ok || sp.tok_end == sp.tok_begin || n_cls == 0) {
+    if (lane == 0 && (!ok || sp.tok_end > sp.tok_begin))  // (a class with no pages: its ids are bad)
+      report(a.err, ok ? KVQ_DEVERR_ID : KVQ_DEVERR_SPLIT);
     for (int j = 0; j < a.g; ++j) {
       float *o = a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim;
       *reinterpret_cast<float2 *>(o + 2 * lane) = make_float2(0.0f, 0.0f);
       if (lane == 0) a.part_lse[(int64_t)s_idx * a.g + j] = -INFINITY;
     }
-    return;
+    return false;
   }
   const int b = sp.table / a.tpr;
   const int kvh = (sp.table % a.tpr) * a.heads + sp.head;
@@ -682,9 +874,33 @@ __global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
       L.q[j][c] = v;
     }
   __syncthreads();
+  return true;
+}
+
+// Register-staged kernel: slot-map mode (all classes), and FP16 splits in page mode.
+template <int QT, bool SLOTS>
+__global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
+  __shared__ Lds<QT> L;
+  const int s_idx = blockIdx.x;
+  kvq_split sp;
+  if (!split_prologue<QT, SLOTS, false>(a, s_idx, sp, L)) return;
   if (sp.cls == KVQ_INT4) run_split<QT, KVQ_INT4, SLOTS>(a, sp, s_idx, L);
   else if (sp.cls == KVQ_FP16) run_split<QT, KVQ_FP16, SLOTS>(a, sp, s_idx, L);
   else if (!SLOTS) run_split<QT, KVQ_INT2, false>(a, sp, s_idx, L);
+}
+
+// LDS-staged kernel: page-table mode, INT2 and INT4 splits.
+// g <= 4: three waves per SIMD (at most 168 registers a lane).
+template <int QT>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 1)))
+decode_ring_kernel(DecodeArgs a) {
+  __shared__ Lds<QT> L;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+  const int s_idx = blockIdx.x;
+  kvq_split sp;
+  if (!split_prologue<QT, false, true>(a, s_idx, sp, L)) return;
+  if (sp.cls == KVQ_INT4) run_split_ring<QT, KVQ_INT4>(a, sp, s_idx, L, ring);
+  else if (sp.cls == KVQ_INT2) run_split_ring<QT, KVQ_INT2>(a, sp, s_idx, L, ring);
 }
 
 // ------------------------------------------------------------------ merge -----
@@ -791,19 +1007,26 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
   a.part_o = part_o;
   a.part_lse = part_lse;
   a.err = dev_err;
+  a.only_fp16 = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool slots = table_kind == KVQ_TABLE_SLOTS;
   const dim3 grid(n_splits), block(64);
-  if (g <= 4) {
-    if (slots) hipLaunchKernelGGL((decode_kernel<1, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, s, a);
-  } else if (g <= 8) {
-    if (slots) hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, s, a);
-  } else {
-    if (slots) hipLaunchKernelGGL((decode_kernel<4, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, s, a);
+  if (table_kind == KVQ_TABLE_SLOTS) {
+    if (g <= 4) hipLaunchKernelGGL((decode_kernel<1, true>), grid, block, 0, s, a);
+    else if (g <= 8) hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<4, true>), grid, block, 0, s, a);
+    return launched("decode_kernel");
   }
+  // Page mode: INT2 / INT4 splits (and every malformed one) in the LDS-staged kernel,
+  // FP16 splits in the register-staged one when the cache has FP16 pages.
+  if (g <= 4) hipLaunchKernelGGL((decode_ring_kernel<1>), grid, block, 0, s, a);
+  else if (g <= 8) hipLaunchKernelGGL((decode_ring_kernel<2>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_ring_kernel<4>), grid, block, 0, s, a);
+  st = launched("decode_ring_kernel");
+  if (st != KVQ_OK || a.n16 == 0) return st;
+  a.only_fp16 = 1;
+  if (g <= 4) hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, s, a);
+  else if (g <= 8) hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, s, a);
   return launched("decode_kernel");
 }
 
@@ -831,9 +1054,9 @@ extern "C" kvq_status kvq_decode_occupancy(int32_t g, int32_t *per_cu, int32_t *
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_NO_DEVICE, "hipGetDevice failed");
   int blocks = 0, cus = 0;
   hipError_t e;
-  if (g <= 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<1, false>, 64, 0);
-  else if (g <= 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<2, false>, 64, 0);
-  else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, false>, 64, 0);
+  if (g <= 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1>, 64, 0);
+  else if (g <= 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<2>, 64, 0);
+  else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<4>, 64, 0);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(KVQ_ERR_HIP, "CU count query failed");
