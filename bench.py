@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn effective KV GB/s (% HBM peak) + µs/step, Qwen3-8B shape @32K"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_qwen3_8b.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_8b_traffic.md")
+CPU_SECONDS = 10.0  # lower bound on the timed oracle work
 
 
 def log(*a):
@@ -49,12 +50,17 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(decode_launches_per_step):
-    """HBM bytes per decode launch from committed rocprofv3 PMC summaries, if they were
-    taken on the current kernel source; else None."""
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 PMC summary (its line
+    starting 'bench-traffic:'), if it was taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+            for line in f:
+                if line.startswith("bench-traffic:"):
+                    t = json.loads(line.split(":", 1)[1])
+                    break
+            else:
+                return None
     except (OSError, ValueError):
         return None
     if t.get("kernel_sha") != kernel_source_sha():
@@ -164,27 +170,28 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Every launch goes to torch's current stream (the bound calls pass it), so events
+    # recorded there bracket exactly the kernels.  Inside the timed steps each decode
+    # launch is bracketed too, for the roofline of the dominant kernel.
     stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * args.layers)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
+    i = 0
     for _ in range(args.steps):
-        step()
+        for L in range(args.layers):
+            ev[i][0].record(stream)
+            dec[L]()
+            ev[i][1].record(stream)
+            mrg[L]()
+            i += 1
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+    us_decode = sum(a.elapsed_time(b) for a, b in ev) * 1000 / len(ev)
     log(f"step {ms_step * 1000:.1f} us ({ms_step * 1000 / args.layers:.1f} us per layer)")
-
-    # The dominant kernel alone: back-to-back decode launches on the same stream.
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = max(1, args.steps // 2)
-    d0.record(stream)
-    for _ in range(reps):
-        for L in range(args.layers):
-            dec[L]()
-    d1.record(stream)
-    torch.cuda.synchronize()
-    us_decode = d0.elapsed_time(d1) * 1000 / (reps * args.layers)
     decode_bytes = kv_layer + int(w0.alloc.n_entries.sum()) * 4 + w0.batch * w0.hq * 128 * 2
     achieved = decode_bytes / (us_decode * 1e-6) / 1e9
     log(f"decode kernel {us_decode:.1f} us per launch, {achieved:.0f} GB/s algorithmic")
@@ -220,7 +227,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.layers),
+            "traffic": measured_traffic(),
             "bytes_per_launch": decode_bytes,
             "us_per_launch": round(us_decode, 2),
         },
@@ -235,17 +242,21 @@ def main():
         except AttributeError:
             n_threads = min(16, os.cpu_count() or 1)
         orc = OracleRun(cpu_sample)
-        t = time.perf_counter()
-        orc.attend(n_threads=n_threads)
-        dt = time.perf_counter() - t
+        reps, t = 0, time.perf_counter()
+        while True:  # whole passes over the sample until CPU_SECONDS have gone by
+            orc.attend(n_threads=n_threads)
+            reps += 1
+            dt = time.perf_counter() - t
+            if dt >= CPU_SECONDS:
+                break
         sample_bytes, _ = effective_bytes(cpu_sample)
         result["cpu_baseline"] = {
-            "value": round(sample_bytes / dt / 1e9, 3),
+            "value": round(sample_bytes * reps / dt / 1e9, 3),
             "unit": "GB/s",
             "cores": n_threads,
             "kind": "oracle",
             "sample": f"{args.cpu_requests} of 16 requests of one layer (all 8 KV heads, g = 4, "
-                      f"32768 tokens each), fp64 two-pass softmax; {dt:.2f} s",
+                      f"32768 tokens each), fp64 two-pass softmax, {reps} passes in {dt:.1f} s",
         }
         log(f"cpu oracle {result['cpu_baseline']['value']} GB/s on {n_threads} threads ({dt:.1f} s)")
     print(json.dumps(result), flush=True)

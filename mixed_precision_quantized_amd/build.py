@@ -21,7 +21,10 @@ HIP = ["--offload-arch=" + ARCH, "-fno-gpu-flush-denormals-to-zero",
 SOURCES = [
     ("kvq_host.cpp", ["-ffp-contract=off"]),
     ("kvq_write.hip", HIP + ["-ffp-contract=off"]),
-    ("kvq_decode.hip", HIP),
+    # The decode kernels never rely on NaN semantics (the softmax runs from a finite
+    # start, masked logits are -inf); without NaNs to honour, max needs no quieting and
+    # DPP row reductions fold into v_max_f32_dpp.
+    ("kvq_decode.hip", HIP + ["-fno-honor-nans"]),
 ]
 
 

@@ -93,7 +93,7 @@ __device__ __forceinline__ float h2f(uint32_t bits) {
 // Row (16-lane) reductions by DPP row rotations; every lane of the row gets the result.
 template <int N>
 __device__ __forceinline__ float dpp_ror(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp_ror<8>(x));
@@ -109,8 +109,8 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 // Sum over the 4 lanes of a quad (quad_perm xor 1, then xor 2).
 __device__ __forceinline__ float quad_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, true));
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, true));
 }
 
 // ------------------------------------------------------------ code -> fp16 ----
@@ -239,8 +239,6 @@ struct Loader {
       w.ok = (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int32_t t = T + 16 * h + lr;
-        if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> h & 1)) w.live |= 1u << h;
         const gbytes bh = h ? blk1 : blk0;
         if (CLS == KVQ_INT4) {
           w.k[h][0] = ld4(bh + kI4KC + lr * 64 + lb * 16);
@@ -266,8 +264,6 @@ struct Loader {
       const int o0 = 8 * (lb & 1);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int32_t t = T + ti + q;
-        if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> (lb >> 1) & 1)) w.vlive |= 1u << q;
         if (CLS == KVQ_INT4) w.v[q].x = ld1(vb + kI4VC + (o0 + q) * 64 + lr * 4);
         else if (CLS == KVQ_INT2) w.v[q].x = ld1(vb + kI2VC + (o0 + q) * 32 + (lr >> 1) * 4);
         else w.v[q] = ld4(vb + kF16V + (o0 + q) * 256 + lr * 16);
@@ -409,7 +405,23 @@ struct SplitRun {
 
   // 32 tokens starting at T, from the loaded window `w`.
   __device__ __forceinline__ void window(const Win &w, int32_t T) {
-    const bool partial = (T < sp.tok_begin) || (T + 32 > sp.tok_end) || w.ok != 3u;
+    const bool partial = (T < sp.tok_begin) || (T + 32 > sp.tok_end) || w.ok != 3u;  // (slot maps: ok = 0)
+    // live bit h: QK token T + 16 h + lr counts; vlive bit q: P V token T + 8 lb + q counts.
+    uint32_t live = 3u, vlive = 0xFFu;
+    if (SLOTS) {
+      live = w.live;
+      vlive = w.vlive;
+    } else if (partial) {
+      live = 0u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int32_t t = T + 16 * h + lr;
+        if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> h & 1)) live |= 1u << h;
+      }
+      const int32_t t0 = T + 8 * lb;
+      const int32_t lo = min(max(sp.tok_begin - t0, 0), 8), hi = min(max(sp.tok_end - t0, 0), 8);
+      vlive = (w.ok >> (lb >> 1) & 1) ? (0xFFu >> (8 - hi)) & (0xFFu << lo) & 0xFFu : 0u;
+    }
 
     // INT2: zero term of the pair, sum over the group of q (z + 2 s).
     f4 c2[QT];
@@ -451,7 +463,7 @@ struct SplitRun {
 #pragma unroll
         for (int m = 0; m < 4; ++m) kb[m] = h8_of(w.k[h][m]);
       }
-      const bool live = w.live >> h & 1;
+      const bool tok_live = live >> h & 1;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         f4 d = CLS == KVQ_INT2 ? c2[qt] : f4{0.f, 0.f, 0.f, 0.f};
@@ -467,7 +479,7 @@ struct SplitRun {
         } else {
           s = (d[0] + d[1]) + (d[2] + d[3]);
         }
-        x[qt][h] = live ? s * scale : -INFINITY;
+        x[qt][h] = tok_live ? s * scale : -INFINITY;
       }
     }
 
@@ -477,7 +489,7 @@ struct SplitRun {
       const float bm = row_max16(fmaxf(x[qt][0], x[qt][1]));
       const float mn = fmaxf(m_run[qt], bm);
       if (__any(mn > m_run[qt])) {  // rare after the first windows
-        const float alpha = exp2f(m_run[qt] - mn);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mn);
         l_run[qt] *= alpha;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
@@ -486,7 +498,9 @@ struct SplitRun {
         asum[qt] *= alpha_row;
         m_run[qt] = mn;
       }
-      const float p0 = exp2f(x[qt][0] - m_run[qt]), p1 = exp2f(x[qt][1] - m_run[qt]);
+      // v_exp_f32: exp2(-inf) = 0; results below 2^-126 may flush to zero, which no
+      // softmax weight of consequence is.
+      const float p0 = __builtin_amdgcn_exp2f(x[qt][0] - m_run[qt]), p1 = __builtin_amdgcn_exp2f(x[qt][1] - m_run[qt]);
       l_run[qt] += p0 + p1;
       L.p[qt][lb][lr] = (_Float16)p0;
       L.p[qt][lb][16 + lr] = (_Float16)p1;
@@ -537,8 +551,8 @@ struct SplitRun {
         if (partial) {  // absent or dead tokens: keep the operand finite
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const uint32_t mk = ((w.vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
-                                ((w.vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
+            const uint32_t mk = ((vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
+                                ((vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) t[nt][u] &= mk;
           }
@@ -566,8 +580,8 @@ struct SplitRun {
           uint32_t s2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x05040100u);  // scales
           uint32_t z2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x07060302u);  // zeros
           if (partial) {
-            const uint32_t mk = ((w.vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
-                                ((w.vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
+            const uint32_t mk = ((vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
+                                ((vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
             s2 &= mk;
             z2 &= mk;
           }
@@ -668,12 +682,14 @@ struct RingGeom<KVQ_INT2> {  // K codes, V codes, meta: 3 KB per window
   static constexpr int kChunks = 3, kSlots = 3;
 };
 
-// One 1 KB chunk: lane L copies 16 B from src to LDS byte lds + 16 L.
+// One 1 KB chunk: lane L copies 16 B from src to LDS byte lds + 16 L.  M0 carries the
+// LDS base; it is a register the compiler reserves, so its value is put back.
 __device__ __forceinline__ void dma_chunk(uint32_t lds, gbytes src) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "s"(lds), "v"((uint64_t)src)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Waits until at most N copies issued by this wave are still in flight (they complete
@@ -701,8 +717,10 @@ struct RingLoader {
         e_first(s_.tok_begin >> 4), e_last((s_.tok_end - 1) >> 4), lane(threadIdx.x), lr(threadIdx.x & 15),
         lb(threadIdx.x >> 4), ring((uint32_t)(uintptr_t)ring_), lds(ring_) {}
 
+  // Page-table entry of page half h of window T (T is never before the split's first
+  // page; past its last page the last entry is repeated).
   __device__ __forceinline__ int32_t entry(int32_t T, int h) const {
-    return crow[__builtin_amdgcn_readfirstlane(min(max((T >> 4) + h, e_first), e_last))];
+    return crow[(uint32_t)__builtin_amdgcn_readfirstlane(min((T >> 4) + h, e_last))];
   }
 
   // Copies window T (page ids id0, id1 of its two halves) into slot `slot`; returns
@@ -741,19 +759,7 @@ struct RingLoader {
   __device__ __forceinline__ void read(int32_t T, int slot, uint32_t ok, Win &w) const {
     const uint8_t *S = lds + slot * (G::kChunks * 1024);
     w.ok = ok;
-    w.live = 0;
-    w.vlive = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int32_t t = T + 16 * h + lr;
-      if (t >= sp.tok_begin && t < sp.tok_end && (ok >> h & 1)) w.live |= 1u << h;
-    }
     const int o0 = 8 * (lb & 1);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int32_t t = T + 8 * lb + q;
-      if (t >= sp.tok_begin && t < sp.tok_end && (ok >> (lb >> 1) & 1)) w.vlive |= 1u << q;
-    }
     if (CLS == KVQ_INT4) {
       const uint8_t *M = S + 4096;
 #pragma unroll
