@@ -243,9 +243,11 @@ kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch
                                 int32_t total_work, int32_t *out);
 
 /*
- * Work groups of the decode kernel that fit on the current device at once:
- * *per_cu from the HIP occupancy API, *n_cu the compute-unit count.  g selects
- * the kernel variant (query heads per KV head).  Errors: NO_DEVICE, HIP.
+ * Work groups (one wavefront each) of the page-table decode kernel for INT2 /
+ * INT4 splits that fit on the current device at once: *per_cu from the HIP
+ * occupancy API, *n_cu the compute-unit count.  g (query heads per KV head)
+ * selects the kernel variant.  A plan with per_cu * n_cu splits runs as one
+ * round of waves.  Errors: INVALID_ARG, NO_DEVICE, HIP.
  */
 kvq_status kvq_decode_occupancy(int32_t g, int32_t *per_cu, int32_t *n_cu);
 

@@ -17,23 +17,23 @@
 //   products of every (query, token) apart and the per-token INT4 group scales are
 //   applied after the product: lane (lr, lb) ends with query lb's four group partials
 //   of token lr.  q enters unscaled (bf16 / fp16 queries are exact in fp16) and the
-//   softmax scale is applied to the fp32 result.  K codes enter as exact centered
-//   fp16 values (c - 8 for INT4, c - 2 for INT2; see below), and the zero term
-//   (z + 8 s) * sum(q) is added per group.  INT2 K has per-channel scales: the code
-//   operand becomes s * (c - 2), exact in fp16 because c - 2 is in {-2, -1, 0, 1},
-//   and the zero term sum q (z + 2 s) of the 32-token pair enters through the
-//   accumulator start.
+//   softmax scale is applied to the fp32 result.  INT4 K codes enter as exact
+//   offset-coded fp16 values (2^e + c, see below) and the offset's share of the dot
+//   product is removed per group together with the zero term z * sum(q).  INT2 K has
+//   per-channel scales: the code operand becomes s * (c - 2), exact in fp16 because
+//   c - 2 is in {-2, -1, 0, 1}, and the zero term sum q (z + 2 s) of the 32-token pair
+//   enters through the accumulator start.
 //   Online softmax in base 2 per query with 16-lane DPP row reductions; the running
 //   state is rescaled only when a row maximum grows.
 //   P V on MFMA.  Rows (query j', group i); the weight operand is p * s (fp16) for
-//   group i, the value operand is the centered code (c - 8 for INT4, c - 2 for INT2,
-//   exact in fp16), and the zero term p * (z + 8 s) (resp. z + 2 s) is accumulated
-//   with v_dot2_f32_f16.  Centering keeps the fp32 accumulator of the same magnitude
-//   as the result (an uncentered 0..15 code would leave a large positive sum that the
-//   zero term must cancel).  Lane (lr, lb) ends with query lb's outputs for channels
-//   8 lr .. 8 lr + 7.
-//   Tokens come 32 at a time (two 16-token pages, or one INT2 page pair); the loads of
-//   the next 32 tokens are issued before the current ones are computed.
+//   group i, the value operand the offset-coded codes with small offsets (64 / 16), and
+//   the zero term p * z is accumulated with v_dot2_f32_f16; the offsets' share, 2^e
+//   times the sum of the fp16 weights that entered the product, is removed at the end.
+//   Lane (lr, lb) ends with query lb's outputs for channels 8 lr .. 8 lr + 7.
+//   Tokens come 32 at a time (two 16-token pages, or one INT2 page pair).  Page-table
+//   INT2 / INT4 splits stage their bytes through an LDS ring filled by direct
+//   HBM -> LDS copies (decode_ring_kernel); FP16 splits and slot maps load into two
+//   alternating register windows (decode_kernel).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
