@@ -16,6 +16,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,10 +44,13 @@ def effective_bytes(w, q_bytes_per_elem=2, out_bytes_per_elem=2):
 
 
 def kernel_source_sha():
+    """Hash of the decode kernel's source code (comments and layout ignored)."""
     h = hashlib.sha256()
     for f in ("kvq_decode.hip", "kvq_internal.h"):
-        with open(os.path.join(ROOT, "mixed_precision_quantized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mixed_precision_quantized_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
