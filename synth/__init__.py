@@ -292,6 +292,111 @@ def qwen3_8b(seed=2, batch=16, n_tokens=32768, device="cpu", frac_int2=0.7, laye
                     note=f"{batch}x{n_tokens} tokens, {frac_int2:.0%} INT2 units")
 
 
+# Tag axes of the agentic workload: temporal (by turn from the end), modal, semantic.
+N_TEMPORAL, N_MODAL, N_SEMANTIC = 4, 2, 7
+# Synthetic 2-bit distortion weights per axis value (semantic axis dominant, its first
+# value highest); 4-bit distortion is 1/25 of it (a 5x finer step).
+_D_SEM = np.array([8.0, 4.0, 2.0, 1.5, 1.0, 0.7, 0.5])
+_D_MOD = np.array([1.0, 0.6])
+_D_TMP = np.array([4.0, 2.0, 1.3, 1.0])
+
+
+def _temporal_bucket(turns_from_end):
+    return np.select([turns_from_end == 0, turns_from_end <= 2, turns_from_end <= 7], [0, 1, 2], 3)
+
+
+def agentic_spans(length, rng):
+    """Per-token tag ids (temporal, modal, semantic) of one synthetic multi-turn
+    context: 12-40 turns of near-equal share, each a run of spans with geometric
+    lengths (mean 300); a span is an image span with probability 0.15."""
+    n_turns = int(rng.integers(12, 41))
+    cuts = np.sort(rng.choice(np.arange(1, length), n_turns - 1, replace=False))
+    bounds = np.concatenate([[0], cuts, [length]])
+    tmp = np.empty(length, np.int8)
+    mod = np.empty(length, np.int8)
+    sem = np.empty(length, np.int8)
+    sem_p = np.array([0.05, 0.2, 0.25, 0.15, 0.15, 0.1, 0.1])
+    for i in range(n_turns):
+        a, b = int(bounds[i]), int(bounds[i + 1])
+        tmp[a:b] = _temporal_bucket(np.array(n_turns - 1 - i))
+        pos = a
+        while pos < b:
+            n = min(b - pos, int(rng.geometric(1.0 / 300.0)))
+            mod[pos:pos + n] = 1 if rng.random() < 0.15 else 0
+            sem[pos:pos + n] = rng.choice(N_SEMANTIC, p=sem_p)
+            pos += n
+    return tmp, mod, sem
+
+
+def greedy_bits(counts, budget):
+    """2 / 4 bits per tag: start every tag at 2 bits, walk tags by decreasing
+    rho_k = (D_k(2) - D_k(4)) / (2 N_k) (ties by tag index), upgrade a tag while the
+    average width stays within `budget`, stop at the first that would exceed it.
+    counts: tokens per tag [N_TEMPORAL, N_MODAL, N_SEMANTIC]."""
+    d2 = _D_TMP[:, None, None] * _D_MOD[None, :, None] * _D_SEM[None, None, :]
+    d4 = d2 / 25.0
+    n = counts.astype(np.float64).reshape(-1)
+    bits = np.full(n.shape, 2, np.int8)
+    live = np.nonzero(n > 0)[0]
+    rho = (d2.reshape(-1) - d4.reshape(-1))[live] / (2.0 * n[live])
+    order = live[np.lexsort((live, -rho))]
+    total, used = n.sum(), 2.0 * n.sum()
+    for k in order:
+        if used + 2.0 * n[k] > budget * total:
+            break
+        bits[k] = 4
+        used += 2.0 * n[k]
+    return bits.reshape(counts.shape)
+
+
+def qwen3_vl_agentic(seed=3, batch=8, lo=65536, hi=131072, device="cpu", chunk=8192,
+                     budget_bits=2.6, layer=0):
+    """Qwen3-VL-32B-shaped agentic decode: Hq 64 / Hkv 8 (g = 8), d 128, one page table
+    per request holding all 8 KV heads, contexts uniform in [lo, hi].  Tokens carry
+    tri-axis tags (agentic_spans); one tag -> bits map for the batch comes from
+    greedy_bits on the aggregate tag counts at `budget_bits`; tokens are appended in
+    `chunk`-token calls, so every call leaves its own INT4 residual.  bf16 K, V ~ N(0,1),
+    N(0, 2) (variance) on image spans; bf16 q."""
+    hq, hkv, H = 64, 8, 8
+    rng = np_rng(seed, 31)
+    lens = rng.integers(lo, hi + 1, batch)
+    tags = [agentic_spans(int(n), np_rng(seed, 32, b)) for b, n in enumerate(lens)]
+    counts = np.zeros((N_TEMPORAL, N_MODAL, N_SEMANTIC), np.int64)
+    for tmp, mod, sem in tags:
+        np.add.at(counts, (tmp, mod, sem), 1)
+    bits = greedy_bits(counts, budget_bits)
+    rows_total = int(lens.sum())
+    k = randn((rows_total, H, HEAD_DIM), seed, 33, layer, device=device)
+    v = randn((rows_total, H, HEAD_DIM), seed, 34, layer, device=device)
+    calls, n2, n4, row = [], 0, 0, 0
+    image_rows = []
+    for b, (tmp, mod, sem) in enumerate(tags):
+        n = int(lens[b])
+        flags = np.where(bits[tmp, mod, sem] == 4, INT4, INT2).astype(np.uint8)
+        image_rows.append(row + np.nonzero(mod == 1)[0])
+        n4_tab = 0
+        for c0 in range(0, n, chunk):
+            f = flags[c0:c0 + chunk]
+            calls.append((b, f, np.arange(row + c0, row + c0 + len(f), dtype=np.int32), False))
+            n_int2 = int((f == INT2).sum())
+            n2 += 2 * (n_int2 // GROUP)
+            n4_tab += len(f) - GROUP * (n_int2 // GROUP)
+        n4 += -(-n4_tab // PAGE)
+        row += n
+    img = torch.as_tensor(np.concatenate(image_rows), device=device, dtype=torch.long)
+    k[img] *= math.sqrt(2.0)
+    v[img] *= math.sqrt(2.0)
+    k, v = _bf16(k), _bf16(v)
+    q = _bf16(randn((batch, hq, HEAD_DIM), seed, 35, layer, device=device))
+    max_entries = -(-int(hi) // PAGE)  # INT2 groups fill whole page pairs, so ceil(n / 16) entries
+    alloc = PageAllocator((n2, n4, 0), H, batch, max_entries, seed)
+    int4_frac = float((counts * (bits == 4)).sum()) / float(counts.sum())
+    return Workload("qwen3_vl_agentic", seed, batch, hq, hkv, H, PAGES, torch.bfloat16, torch.bfloat16,
+                    k, v, q, (n2, n4, 0), alloc, calls,
+                    note=f"{batch} requests of {int(lens.min())}..{int(lens.max())} tokens, "
+                         f"{int4_frac:.0%} INT4 tags at {budget_bits} bits, {chunk}-token appends")
+
+
 def hybrid_anchor(seed=4, batch=32, n_tokens=65536, device="cpu", window=128, staging=64,
                   vl_ratio=0.05, layer=0):
     """Hybrid FP16-anchor decode (Llama-3.1-8B shape): Hq 32 / Hkv 8, one table per

@@ -168,13 +168,47 @@ def test_bad_device_data_is_reported_not_faulted():
     gpu.tables.copy_(tab)
 
 
+def _resident_plan(gpu):
+    """The benchmark's plan: one split per resident wave slot of the decode kernel."""
+    w = gpu.w
+    per_cu, n_cu = gpu.kvq.decode_occupancy(w.g)
+    sph = max(1, (per_cu * n_cu) // (w.batch * w.hkv))
+    return gpu.plan(splits_per_head=np.full(w.batch * w.hkv, sph, np.int32))
+
+
+def test_qwen3_vl_agentic_small():
+    """g = 8 (Qwen3-VL-32B GQA ratio) over tagged multi-turn contexts appended in
+    4096-token calls (an INT4 residual per call), full oracle comparison."""
+    make = lambda: synth.qwen3_vl_agentic(batch=2, lo=9000, hi=12000, chunk=4096)  # noqa: E731
+    _check_case("qwen3_vl_agentic 2 x ~10K", make, dict(splits_per_head=np.full(16, 5, np.int32)))
+
+
+def test_full_size_qwen3_vl_agentic_sampled():
+    """The agentic workload at full size (8 requests of 64K-128K tokens, g = 8) with the
+    resident-wave plan, checked on one sampled request against the oracle."""
+    _say("full-size qwen3_vl_agentic: generating on the GPU")
+    w = synth.qwen3_vl_agentic(device="cuda")
+    gpu = GpuRun(w)
+    splits, offsets = _resident_plan(gpu)
+    out, lse, _, _ = gpu.decode(splits, offsets)
+    assert int(gpu.err.item()) == 0
+    _say(f"  {w.note}; {splits.shape[0]} splits decoded; oracle on request 5")
+    del gpu
+    sub_w = synth.subset(synth.qwen3_vl_agentic(device="cuda"), [5])
+    ref, ref_lse = OracleRun(sub_w).attend()
+    err = row_metric(ref, out.cpu().numpy()[[5]])
+    _say(f"  sampled row error {err:.2e}")
+    assert err <= TOL
+    assert np.allclose(lse.cpu().numpy()[[5]], ref_lse, rtol=0, atol=1e-3)
+
+
 def test_full_size_qwen3_8b_sampled():
     """The benchmark's workload (16 x 32768 tokens, 8 KV heads, g = 4) and split plan,
     checked on two sampled requests against the oracle."""
     _say("full-size qwen3_8b: generating on the GPU")
     w = synth.qwen3_8b(device="cuda")
     gpu = GpuRun(w)
-    splits, offsets = gpu.plan(target_bytes=1 << 18)
+    splits, offsets = _resident_plan(gpu)
     out, lse, _, _ = gpu.decode(splits, offsets)
     assert int(gpu.err.item()) == 0
     _say(f"  {splits.shape[0]} splits decoded; oracle on requests 3 and 11")
