@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark on one MI355X.
 
-Workload: Qwen3-8B-shaped decode step over a mixed INT2 / INT4 paged KV cache: batch
-16, Hq 32 / Hkv 8 (g = 4), d 128, 32768 tokens per request (70 % INT2 / 30 % INT4 in
-shuffled 32-token units, INT2-first reorder), 16-token pages, bf16 q and output,
-36 layers each with its own pools (17.4 GB in total, so no layer is served from the
-256 MB Infinity Cache).  A step = split-K decode + log-sum-exp merge for all 36
-layers.  Inputs are resident in HBM before timing starts.
+Default workload (the metric's): Qwen3-8B-shaped decode step over a mixed INT2 / INT4
+paged KV cache: batch 16, Hq 32 / Hkv 8 (g = 4), d 128, 32768 tokens per request (70 %
+INT2 / 30 % INT4 in shuffled 32-token units, INT2-first reorder), 16-token pages, bf16
+q and output, 36 layers each with its own pools (17.4 GB in total, so no layer is
+served from the 256 MB Infinity Cache).  A step = split-K decode + log-sum-exp merge
+for every layer.  Inputs are resident in HBM before timing starts.
+
+--workload also times the other synthetic workloads (agentic g = 8, FP16 anchors,
+ragged slot maps with dead slots) with the same columns, on fewer layers by default.
 
 Prints ONE JSON line: effective KV GB/s of the whole step (algorithmic bytes: packed
-codes + fp16 scale/zero of every live token-head, 4 B per page-table entry, q and the
+codes + fp16 scale/zero of every live token-head, 4 B per table entry, q and the
 output), us per step, the roofline of the decode kernel and the CPU oracle's rate on a
 bounded sample of the same workload."""
 import argparse
@@ -22,11 +25,27 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+sys.path.insert(1, os.path.join(ROOT, "tests"))
 
-METRIC = "decode-attn effective KV GB/s (% HBM peak) + µs/step, Qwen3-8B shape @32K"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_8b_traffic.md")
 CPU_SECONDS = 10.0  # lower bound on the timed oracle work
+
+# name: (metric suffix, default layers, description)
+WORKLOADS = {
+    "qwen3_8b": ("Qwen3-8B shape @32K", 36,
+                 "Qwen3-8B-shaped decode: batch 16, Hq 32 / Hkv 8, d 128, 32768 tokens per request, "
+                 "70% INT2 / 30% INT4, 16-token pages"),
+    "qwen3_vl_agentic": ("Qwen3-VL-32B agentic shape @64K-128K", 8,
+                         "Qwen3-VL-32B-shaped agentic decode: batch 8, Hq 64 / Hkv 8, d 128, "
+                         "65536-131072 tokens per request, tri-axis tags at 2.6 bits, 8192-token appends"),
+    "hybrid_anchor": ("Llama-3.1-8B hybrid FP16-anchor shape @64K", 4,
+                      "Llama-3.1-8B-shaped hybrid decode: batch 32, Hq 32 / Hkv 8, one table per "
+                      "(request, head), 65536 tokens: INT4 prefix + FP16 vertical lines, staging, window"),
+    "ragged_dead": ("ragged head-group slot maps with dead slots", 8,
+                    "ragged decode: batch 64, Hq 32 / Hkv 8, lengths 4K-128K, per-head budgets "
+                    "0.1-1.0, 2-head slot-map tables, 20% dead slots, INT4"),
+}
 
 
 def log(*a):
@@ -35,12 +54,24 @@ def log(*a):
 
 def effective_bytes(w, q_bytes_per_elem=2, out_bytes_per_elem=2):
     """Algorithmic bytes of one layer: live token-heads x (96 / 160 / 512 B), 4 B per
-    page-table entry, q and output."""
-    H = w.heads_per_page
-    kv = int((w.alloc.tokens[:, 0] * 96 + w.alloc.tokens[:, 1] * 160 + w.alloc.tokens[:, 2] * 512).sum()) * H
-    tables = int(w.alloc.n_entries.sum()) * 4
-    qo = w.batch * w.hq * 128 * (q_bytes_per_elem + out_bytes_per_elem)
-    return kv + tables + qo, kv
+    table entry, q and output; and the decode kernel's share (without the output)."""
+    import numpy as np
+    import synth
+    per_tok = np.array([96, 160, 512], np.int64)
+    if w.kind == synth.PAGES:
+        kv = int((w.alloc.tokens * per_tok).sum()) * w.heads_per_page
+        tables = int(w.alloc.n_entries.sum()) * 4
+    else:  # slot maps: each head reads its first head_tokens entries; dead ones move nothing
+        live = 0
+        for t in range(w.n_tables):
+            dead = np.asarray(w.dead_entries[t])
+            for h in range(w.heads_per_page):
+                n = int(w.head_tokens[t, h])
+                live += n - int((dead < n).sum())
+        kv = live * int(per_tok[synth.INT4])
+        tables = int(w.head_tokens.sum()) * 4
+    q = w.batch * w.hq * 128 * q_bytes_per_elem
+    return kv + tables + q + w.batch * w.hq * 128 * out_bytes_per_elem, kv + tables + q
 
 
 def kernel_source_sha():
@@ -72,17 +103,36 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+def resident_plan(gpu, kvq, synth, splits_per_head=0):
+    """One wave per split, as many splits as the decode kernel keeps resident at once
+    (a second, partial round of waves would leave most of the chip idle).  Ragged slot
+    maps share the count among heads in proportion to their budgets (Tangram AOT)."""
+    import numpy as np
+    w = gpu.w
+    kind = kvq.TABLE_SLOTS if w.kind == synth.SLOTS else kvq.TABLE_PAGES
+    per_cu, n_cu = kvq.decode_occupancy(w.g, kind)
+    if splits_per_head:
+        sph = np.full(w.batch * w.hkv, splits_per_head, np.int32)
+    elif w.head_budget is not None:
+        sph = kvq.aot_split_counts(w.head_budget, w.batch, per_cu * n_cu)
+    else:
+        sph = np.full(w.batch * w.hkv, max(1, (per_cu * n_cu) // (w.batch * w.hkv)), np.int32)
+    splits, offsets = gpu.plan(splits_per_head=sph)
+    return splits, offsets, per_cu, n_cu
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="qwen3_8b")
+    ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--splits-per-head", type=int, default=0,
                     help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+                    help="also run plain 1 GiB device copies (reference for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -94,68 +144,65 @@ def main():
     import torch
 
     import synth
+    from harness import GpuRun
     from mixed_precision_quantized_amd import kvq
 
+    suffix, default_layers, description = WORKLOADS[args.workload]
+    make = getattr(synth, args.workload)
+    layers = args.layers or default_layers
     dev = "cuda"
     torch.cuda.set_device(0)
     t0 = time.time()
-    w0 = synth.qwen3_8b(device=dev, layer=0)
-    lists = synth.place_all(w0, lambda f: kvq.route_tokens(f)[0])
-    dl = {n: torch.as_tensor(a, device=dev) for n, a in lists.arrays().items()}
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    tables = torch.as_tensor(w0.alloc.tables, device=dev).contiguous()
-    n_entries = torch.as_tensor(w0.alloc.n_entries, device=dev)
-    counts = torch.zeros((w0.n_tables, 3), dtype=torch.int32, device=dev)
-    eff_layer, kv_layer = effective_bytes(w0)
+
+    # Layer 0 is built, placed, quantized and reordered through the library; every other
+    # layer gets its own pools holding its own K / V with the same placement, so the
+    # reordered tables, ranges and plan serve all layers.
+    gpu = GpuRun(make(device=dev, layer=0))
+    w0 = gpu.w
+    eff_layer, decode_bytes = effective_bytes(w0)
     log(f"workload: {w0.note}; effective bytes per layer {eff_layer}")
-
     cpu_sample = None
-    if not args.no_cpu_baseline:
-        cpu_sample = synth.subset(w0, list(range(args.cpu_requests)), device="cpu")
-
-    caches, qs = [], []
-    for L in range(args.layers):
-        w = w0 if L == 0 else synth.qwen3_8b(device=dev, layer=L)
-        cache = kvq.Cache(w0.heads_per_page, w0.n_pages, dev)
-        kvq.quantize_append(cache, w.k, w.v, rows4=dl["rows4"], slots4=dl["slots4"], rows2=dl["rows2"],
-                            pages2=dl["pages2"], dev_err=err)
+    if not args.no_cpu_baseline and w0.kind == synth.PAGES:
+        req = list(range(min(args.cpu_requests, w0.batch)))
+        cpu_sample = synth.subset(make(device=dev, layer=0), req, device="cpu")
+    lists = {n: torch.as_tensor(a, device=dev) for n, a in gpu.lists.arrays().items()}
+    lists = {n: (a if len(a) else None) for n, a in lists.items()}
+    sent = synth.sentinel_lists(w0).arrays() if w0.kind == synth.SLOTS and w0.sentinel_slot >= 0 else None
+    caches, qs = [gpu.cache], [gpu.q]
+    w0.k = w0.v = gpu.k = gpu.v = None
+    for L in range(1, layers):
+        w = make(device=dev, layer=L)
+        cache = kvq.Cache(w0.heads_per_page, w0.n_pages, dev, sentinel_slot=w0.sentinel_slot)
+        if sent is not None:
+            kvq.quantize_append(cache, w.k, w.v, rows4=torch.as_tensor(sent["rows4"], device=dev),
+                                slots4=torch.as_tensor(sent["slots4"], device=dev), dev_err=gpu.err)
+        kvq.quantize_append(cache, w.k, w.v, dev_err=gpu.err, **lists)
         caches.append(cache)
         qs.append(w.q.contiguous())
-        w.k = w.v = None
         del w
     torch.cuda.synchronize()
-    w0.k = w0.v = None
     torch.cuda.empty_cache()
-    kvq.reorder_pages(caches[0], tables, n_entries, counts, dev_err=err)
-    items = []
-    for t in range(w0.n_tables):
-        items += w0.alloc.ranges_after_partition(t, list(range(w0.heads_per_page)))
-    ranges = synth.ranges_array(items)
-    # One wave per split; fill every resident slot of the chip once (a second, partial
-    # round of waves would leave most of the chip idle at the end).
-    per_cu, n_cu = kvq.decode_occupancy(w0.g)
-    sph = args.splits_per_head or max(1, (per_cu * n_cu) // (w0.batch * w0.hkv))
-    splits, offsets = kvq.plan_splits(ranges, w0.batch, w0.hkv, w0.heads_per_page,
-                                      splits_per_head=np.full(w0.batch * w0.hkv, sph, np.int32))
+    splits, offsets, per_cu, n_cu = resident_plan(gpu, kvq, synth, args.splits_per_head)
     n_splits = splits.shape[0]
     sp = torch.as_tensor(splits, device=dev).contiguous()
     off = torch.as_tensor(offsets, device=dev)
     g = w0.g
+    kind = kvq.TABLE_SLOTS if w0.kind == synth.SLOTS else kvq.TABLE_PAGES
     part_o = torch.empty((n_splits, g, 128), dtype=torch.float32, device=dev)
     part_lse = torch.empty((n_splits, g), dtype=torch.float32, device=dev)
-    outs = [torch.empty((w0.batch, w0.hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(args.layers)]
-    dec = [kvq.bind_decode_attn(caches[L], qs[L], w0.hkv, tables, kvq.TABLE_PAGES, sp, part_o, part_lse)
-           for L in range(args.layers)]
+    outs = [torch.empty((w0.batch, w0.hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+    dec = [kvq.bind_decode_attn(caches[L], qs[L], w0.hkv, gpu.tables, kind, sp, part_o, part_lse)
+           for L in range(layers)]
     mrg = [kvq.bind_lse_merge(part_o, part_lse, n_splits, off, w0.batch, w0.hq, w0.hkv, outs[L])
-           for L in range(args.layers)]
+           for L in range(layers)]
     torch.cuda.synchronize()
-    assert int(err.item()) == 0, f"device error bits {int(err.item())}"
-    log(f"setup {time.time() - t0:.1f}s: {args.layers} layers, {n_splits} splits per layer "
-        f"({sph} per head; {per_cu} resident per CU x {n_cu} CUs), "
+    assert int(gpu.err.item()) == 0, f"device error bits {int(gpu.err.item())}"
+    log(f"setup {time.time() - t0:.1f}s: {layers} layers, {n_splits} splits per layer "
+        f"({per_cu} resident per CU x {n_cu} CUs), "
         f"pools {sum(sum(p.numel() for p in c.pools) for c in caches) / 2**30:.1f} GiB")
 
     def step():
-        for L in range(args.layers):
+        for L in range(layers):
             dec[L]()
             mrg[L]()
 
@@ -179,13 +226,13 @@ def main():
     # launch is bracketed too, for the roofline of the dominant kernel.
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps * args.layers)]
+          for _ in range(args.steps * layers)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     i = 0
     for _ in range(args.steps):
-        for L in range(args.layers):
+        for L in range(layers):
             ev[i][0].record(stream)
             dec[L]()
             ev[i][1].record(stream)
@@ -195,15 +242,15 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
     us_decode = sum(a.elapsed_time(b) for a, b in ev) * 1000 / len(ev)
-    log(f"step {ms_step * 1000:.1f} us ({ms_step * 1000 / args.layers:.1f} us per layer)")
-    decode_bytes = kv_layer + int(w0.alloc.n_entries.sum()) * 4 + w0.batch * w0.hq * 128 * 2
     achieved = decode_bytes / (us_decode * 1e-6) / 1e9
+    log(f"step {ms_step * 1000:.1f} us ({ms_step * 1000 / layers:.1f} us per layer)")
     log(f"decode kernel {us_decode:.1f} us per launch, {achieved:.0f} GB/s algorithmic")
-    assert int(err.item()) == 0
+    assert int(gpu.err.item()) == 0
 
-    gbs = eff_layer * args.layers / (ms_step * 1e-3) / 1e9
+    gbs = eff_layer * layers / (ms_step * 1e-3) / 1e9
+    default = args.workload == "qwen3_8b"
     result = {
-        "metric": METRIC,
+        "metric": "decode-attn effective KV GB/s (% HBM peak) + µs/step, " + suffix,
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -211,17 +258,16 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "us_per_step": round(ms_step * 1000, 1),
-        "us_per_layer": round(ms_step * 1000 / args.layers, 2),
+        "us_per_layer": round(ms_step * 1000 / layers, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u2/u4 codes, fp16 scale/zero, fp32 math",
+        "dtype": "u2/u4 codes, fp16 scale/zero" + (", fp16 anchors" if w0.n_pages[2] else "") + ", fp32 math",
         "data": "synthetic",
         "config": {
-            "workload": "Qwen3-8B-shaped decode: batch 16, Hq 32 / Hkv 8, d 128, 32768 tokens per "
-                        "request, 70% INT2 / 30% INT4, 16-token pages, 36 layers",
-            "batch": w0.batch, "context": 32768, "layers": args.layers, "splits_per_layer": n_splits,
+            "workload": description + f", {layers} layers",
+            "batch": w0.batch, "hq": w0.hq, "hkv": w0.hkv, "layers": layers, "splits_per_layer": n_splits,
             "effective_bytes_per_layer": eff_layer,
         },
         "roofline": {
@@ -231,7 +277,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if default else None,
             "bytes_per_launch": decode_bytes,
             "us_per_launch": round(us_decode, 2),
         },
@@ -239,7 +285,6 @@ def main():
     }
 
     if cpu_sample is not None:
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
         from harness import OracleRun
         try:
             n_threads = min(16, len(os.sched_getaffinity(0)))
@@ -259,8 +304,8 @@ def main():
             "unit": "GB/s",
             "cores": n_threads,
             "kind": "oracle",
-            "sample": f"{args.cpu_requests} of 16 requests of one layer (all 8 KV heads, g = 4, "
-                      f"32768 tokens each), fp64 two-pass softmax, {reps} passes in {dt:.1f} s",
+            "sample": f"{cpu_sample.batch} of {w0.batch} requests of one layer (all {w0.hkv} KV heads, "
+                      f"g = {w0.g}), fp64 two-pass softmax, {reps} passes in {dt:.1f} s",
         }
         log(f"cpu oracle {result['cpu_baseline']['value']} GB/s on {n_threads} threads ({dt:.1f} s)")
     print(json.dumps(result), flush=True)

@@ -243,13 +243,15 @@ kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch
                                 int32_t total_work, int32_t *out);
 
 /*
- * Work groups (one wavefront each) of the page-table decode kernel for INT2 /
- * INT4 splits that fit on the current device at once: *per_cu from the HIP
- * occupancy API, *n_cu the compute-unit count.  g (query heads per KV head)
- * selects the kernel variant.  A plan with per_cu * n_cu splits runs as one
- * round of waves.  Errors: INVALID_ARG, NO_DEVICE, HIP.
+ * Work groups (one wavefront each) of the decode kernel that fit on the current
+ * device at once: *per_cu from the HIP occupancy API, *n_cu the compute-unit
+ * count.  g (query heads per KV head) and table_kind select the kernel: page
+ * tables -> the kernel of INT2 / INT4 splits, slot maps -> the slot-map kernel.
+ * A plan with per_cu * n_cu splits runs as one round of waves (Tangram step 6:
+ * the total work-group count from the occupancy API).
+ * Errors: INVALID_ARG, NO_DEVICE, HIP.
  */
-kvq_status kvq_decode_occupancy(int32_t g, int32_t *per_cu, int32_t *n_cu);
+kvq_status kvq_decode_occupancy(int32_t g, int32_t table_kind, int32_t *per_cu, int32_t *n_cu);
 
 /* Text of a status code, and a description of this thread's last error. */
 const char *kvq_status_string(int32_t status);

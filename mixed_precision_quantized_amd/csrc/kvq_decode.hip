@@ -113,6 +113,9 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, true));
 }
 
+// Lane within the wavefront (a work group may hold several waves).
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+
 // ------------------------------------------------------------ code -> fp16 ----
 
 // A code OR-ed into the low mantissa bits of a power of two gives 2^e + c exactly
@@ -358,11 +361,12 @@ struct SplitRun {
   float qoff[QT][4];   // per-group sum of q x code offset (1024 / 64) of query 4 qt + lb
   f4 acc[QT][8];       // P V accumulators
   float m_run[QT], l_run[QT];
+  int qbase = 0;       // first query head (of the g) this wave computes
   float zacc[QT];      // row lr: sum of p z over this lane's tokens (V zero term)
   float asum[QT];      // row lr: sum of the fp16 operand weights p s (V code offset)
 
   __device__ SplitRun(const DecodeArgs &a_, const kvq_split &sp_, Lds<QT> &L_)
-      : a(a_), sp(sp_), L(L_), lane(threadIdx.x), lr(threadIdx.x & 15), lb(threadIdx.x >> 4) {
+      : a(a_), sp(sp_), L(L_), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4) {
     scale = kLog2e / sqrtf((float)kHeadDim);
     sel2[0] = pair_sel(lr & 1);  // byte lr & 1: even channels of the lane's half word
     sel2[1] = pair_sel((lr & 1) + 2);
@@ -609,7 +613,7 @@ struct SplitRun {
       as += __shfl_xor(as, 32);
       const float zrow = __shfl(z, 4 * lb + (lr >> 2));  // row (query lb, group lr / 4)
       const float arow = __shfl(as, 4 * lb + (lr >> 2));
-      const int j = 4 * qt + lb;
+      const int j = qbase + 4 * qt + lb;
       const bool any = l_tot > 0.0f;
       const float inv = any ? 1.0f / l_tot : 0.0f;
       const int r = lr >> 2;
@@ -635,7 +639,7 @@ struct SplitRun {
 
 template <int QT, int CLS, bool SLOTS>
 __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L) {
-  const Loader<CLS, SLOTS> ld(a, sp, threadIdx.x);
+  const Loader<CLS, SLOTS> ld(a, sp, lane_id());
   SplitRun<QT, CLS, SLOTS> R(a, sp, L);
   // Two window buffers used alternately: the loads of the next 32 tokens are issued
   // before the current 32 are computed, unconditionally (the last step reloads the
@@ -669,17 +673,25 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
 // and waited for with explicit vmcnt counts (the compiler would otherwise wait for
 // every copy in flight before each LDS read); the compute is the register path's.
 
-constexpr int kRingBytes = 10240;  // per wave: 12 waves fit a CU's LDS
+// A split's g query heads are spread over W waves of one work group, 4 QT each (one
+// wave up to g = 8, two for g = 16); the waves share the ring, each wave issues the
+// copies of every W-th chunk, and a barrier per window publishes the chunks.  With
+// one wave no barrier is needed.
 
-template <int CLS>
-struct RingGeom;
-template <>
-struct RingGeom<KVQ_INT4> {  // K codes x2, V codes x2, meta: 5 KB per window
-  static constexpr int kChunks = 5, kSlots = 2;
-};
-template <>
-struct RingGeom<KVQ_INT2> {  // K codes, V codes, meta: 3 KB per window
-  static constexpr int kChunks = 3, kSlots = 3;
+template <int W>
+constexpr int ring_bytes() { return W == 1 ? 10240 : 15360; }
+
+template <int CLS, int W>
+struct RingGeom {
+  static constexpr int kChunks = CLS == KVQ_INT4 ? 5 : 3;  // INT4: K x2, V x2, meta; INT2: K, V, meta
+  static constexpr int kSlotBytes = kChunks * 1024;
+  static constexpr int kSlots = ring_bytes<W>() / kSlotBytes;
+  // Windows in flight.  With several waves one more slot stays untouched while
+  // being refilled, so a wave still reading its previous window never races a copy.
+  static constexpr int kAhead = kSlots - (W == 1 ? 1 : 2);
+  static_assert(kAhead >= 1, "ring too small");
+  // Copies wave w issues per window: chunks c with c % W == w.
+  static constexpr int chunks_of(int w) { return (kChunks - w + W - 1) / W; }
 };
 
 // One 1 KB chunk: lane L copies 16 B from src to LDS byte lds + 16 L.  M0 carries the
@@ -699,23 +711,23 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <int CLS>
+template <int CLS, int W>
 struct RingLoader {
-  using G = RingGeom<CLS>;
-  static constexpr int kAhead = G::kSlots - 1;  // windows in flight
+  using G = RingGeom<CLS, W>;
+  static constexpr int kAhead = G::kAhead;
   const kvq_split sp;
   cints crow;
   const ClassPages<CLS> pages;
-  const int32_t e_first, e_last;
-  const int lane, lr, lb;
+  const int32_t e_last;
+  const int lane, lr, lb, wave;
   const uint32_t ring;  // LDS byte address of the ring
   const uint8_t *lds;   // the same, as a pointer
   uint32_t errs = 0;
 
-  __device__ RingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_)
+  __device__ RingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_, int wave_)
       : sp(s_), crow((cints)(a.tables + (int64_t)s_.table * a.max_entries)), pages(a, s_.head),
-        e_first(s_.tok_begin >> 4), e_last((s_.tok_end - 1) >> 4), lane(threadIdx.x), lr(threadIdx.x & 15),
-        lb(threadIdx.x >> 4), ring((uint32_t)(uintptr_t)ring_), lds(ring_) {}
+        e_last((s_.tok_end - 1) >> 4), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4), wave(wave_),
+        ring((uint32_t)(uintptr_t)ring_), lds(ring_) {}
 
   // Page-table entry of page half h of window T (T is never before the split's first
   // page; past its last page the last entry is repeated).
@@ -723,41 +735,56 @@ struct RingLoader {
     return crow[(uint32_t)__builtin_amdgcn_readfirstlane(min((T >> 4) + h, e_last))];
   }
 
-  // Copies window T (page ids id0, id1 of its two halves) into slot `slot`; returns
-  // the window's page-half validity bits.  A window past the split's end (`real`
-  // false) copies one 16-byte line to every lane, so the copy count per window stays
-  // fixed at kChunks.
+  // Source of chunk c of a window whose page halves live in blocks b0, b1.
+  __device__ __forceinline__ gbytes chunk_src(int c, gbytes b0, gbytes b1) const {
+    const gbytes mb = (lane >> 4) & 1 ? b1 : b0;  // meta chunk: 4 x 256 B pieces
+    if (CLS == KVQ_INT4) {
+      // K codes in reader-lane order (lane L reads 16 B at 16 L), V codes natural.
+      switch (c) {
+        case 0: return b0 + kI4KC + lr * 64 + lb * 16;
+        case 1: return b1 + kI4KC + lr * 64 + lb * 16;
+        case 2: return b0 + kI4VC + lane * 16;
+        case 3: return b1 + kI4VC + lane * 16;
+        default: return mb + (lane < 32 ? kI4KM : kI4VM) + (lane & 15) * 16;
+      }
+    } else {
+      const gbytes hb = lane < 32 ? b0 : b1;  // K / V codes: 512 B per page, natural
+      switch (c) {
+        case 0: return hb + kI2KC + (lane & 31) * 16;
+        case 1: return hb + kI2VC + (lane & 31) * 16;
+        default: return mb + (lane < 32 ? kI2KS : kI2VM) + (lane & 15) * 16;
+      }
+    }
+  }
+
+  // Copies this wave's chunks of window T (page ids id0, id1 of its two halves) into
+  // slot `slot`; returns the window's page-half validity bits.  A window past the
+  // split's end (`real` false) copies one 16-byte line to every lane, so the copy
+  // count per window stays fixed.
   __device__ __forceinline__ uint32_t issue(int32_t id0, int32_t id1, bool real, int slot) {
     const uint32_t r0 = pages.rel(id0), r1 = pages.rel(id1);
     const bool ok0 = r0 < pages.count, ok1 = r1 < pages.count;
     if (real && !(ok0 && ok1)) errs |= KVQ_DEVERR_ID;
     const gbytes b0 = pages.block(ok0 ? r0 : 0u), b1 = pages.block(ok1 ? r1 : 0u);
-    const uint32_t base = ring + (uint32_t)slot * (G::kChunks * 1024);
-    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // earlier reads of this slot are done
-    if (!real) {
-      for (int c = 0; c < G::kChunks; ++c) dma_chunk(base + 1024 * c, pages.base);
-      return 0u;
-    }
-    const gbytes mb = (lane >> 4) & 1 ? b1 : b0;  // meta chunk: 4 x 256 B pieces
-    if (CLS == KVQ_INT4) {
-      // K codes in reader-lane order (lane L reads 16 B at 16 L), V codes natural.
-      dma_chunk(base, b0 + kI4KC + lr * 64 + lb * 16);
-      dma_chunk(base + 1024, b1 + kI4KC + lr * 64 + lb * 16);
-      dma_chunk(base + 2048, b0 + kI4VC + lane * 16);
-      dma_chunk(base + 3072, b1 + kI4VC + lane * 16);
-      dma_chunk(base + 4096, mb + (lane < 32 ? kI4KM : kI4VM) + (lane & 15) * 16);
-    } else {
-      const gbytes hb = lane < 32 ? b0 : b1;  // K / V codes: 512 B per page, natural
-      dma_chunk(base, hb + kI2KC + (lane & 31) * 16);
-      dma_chunk(base + 1024, hb + kI2VC + (lane & 31) * 16);
-      dma_chunk(base + 2048, mb + (lane < 32 ? kI2KS : kI2VM) + (lane & 15) * 16);
-    }
-    return (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u);
+    const uint32_t base = ring + (uint32_t)slot * G::kSlotBytes;
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // this wave's reads of the slot are done
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c)
+      if (c % W == wave) dma_chunk(base + 1024 * c, real ? chunk_src(c, b0, b1) : pages.base);
+    return real ? (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u) : 0u;
+  }
+
+  // Waits for this wave's copies of the window kAhead windows back.
+  __device__ __forceinline__ void wait() const {
+    if (W == 1 || wave == 0) wait_copies<kAhead * G::chunks_of(0)>();
+    else if (wave == 1) wait_copies<kAhead * G::chunks_of(1)>();
+    else if (wave == 2) wait_copies<kAhead * G::chunks_of(2)>();
+    else wait_copies<kAhead * G::chunks_of(3)>();
   }
 
   // Reads window T from slot `slot` into the register window of the compute.
   __device__ __forceinline__ void read(int32_t T, int slot, uint32_t ok, Win &w) const {
-    const uint8_t *S = lds + slot * (G::kChunks * 1024);
+    const uint8_t *S = lds + slot * G::kSlotBytes;
     w.ok = ok;
     const int o0 = 8 * (lb & 1);
     if (CLS == KVQ_INT4) {
@@ -796,12 +823,14 @@ struct RingLoader {
   }
 };
 
-template <int QT, int CLS>
-__device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L, uint8_t *ring) {
-  using G = RingGeom<CLS>;
-  constexpr int A = RingLoader<CLS>::kAhead;
-  RingLoader<CLS> ld(a, sp, ring);
+template <int CLS, int W, int QT>
+__device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L, uint8_t *ring,
+                               int wave) {
+  using G = RingGeom<CLS, W>;
+  constexpr int A = G::kAhead;
+  RingLoader<CLS, W> ld(a, sp, ring, wave);
   SplitRun<QT, CLS, false> R(a, sp, L);
+  R.qbase = 4 * QT * wave;
   const int32_t T0 = sp.tok_begin & ~15;  // INT2 splits start on 32-token pairs
   const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
   // Window i is copied into slot i mod kSlots, A windows ahead of its compute.
@@ -822,7 +851,8 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
     okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
     id0 = n0;
     id1 = n1;
-    wait_copies<A * G::kChunks>();
+    ld.wait();
+    if (W > 1) __syncthreads();  // every wave's chunks of window n have landed
     Win w;
     const int32_t T = T0 + 32 * n;
     ld.read(T, slot_c, (okq >> (2 * A)) & 3u, w);
@@ -838,10 +868,11 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
 // Checks split s_idx.  A split this launch does not own returns false at once; an
 // owned split that is malformed or empty (or of a class with no pages) gets O = 0,
 // lse = -inf (and an error bit when malformed) and returns false.  Otherwise stages
-// the split's queries, unscaled, in LDS rows 0 .. g - 1 (rows up to 4 QT - 1 zero).
+// the split's query heads q_first .. q_first + 4 QT - 1, unscaled, in LDS rows
+// 0 .. 4 QT - 1 (rows past g zero).  Every wave of the work group calls it alike.
 template <int QT, bool SLOTS, bool RING>
-__device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Lds<QT> &L) {
-  const int lane = threadIdx.x;
+__device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Lds<QT> &L, int q_first = 0) {
+  const int lane = lane_id();
   sp = a.splits[s_idx];
   const int64_t cap = SLOTS ? (int64_t)a.max_entries : (int64_t)a.max_entries * kPage;
   const bool ok = sp.table >= 0 && sp.table < a.n_tables && sp.head >= 0 && sp.head < a.heads &&
@@ -856,7 +887,7 @@ __device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Ld
   if (!ok || sp.tok_end == sp.tok_begin || n_cls == 0) {
     if (lane == 0 && (!ok || sp.tok_end > sp.tok_begin))  // (a class with no pages: its ids are bad)
       report(a.err, ok ? KVQ_DEVERR_ID : KVQ_DEVERR_SPLIT);
-    for (int j = 0; j < a.g; ++j) {
+    for (int j = q_first; j < min(q_first + 4 * QT, a.g); ++j) {
       float *o = a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim;
       *reinterpret_cast<float2 *>(o + 2 * lane) = make_float2(0.0f, 0.0f);
       if (lane == 0) a.part_lse[(int64_t)s_idx * a.g + j] = -INFINITY;
@@ -868,8 +899,8 @@ __device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Ld
   for (int j = 0; j < 4 * QT; ++j)
     for (int c = lane; c < kHeadDim; c += 64) {
       float v = 0.0f;
-      if (j < a.g) {
-        const int64_t idx = ((int64_t)b * a.hq + kvh * a.g + j) * kHeadDim + c;
+      if (q_first + j < a.g) {
+        const int64_t idx = ((int64_t)b * a.hq + kvh * a.g + q_first + j) * kHeadDim + c;
         if (a.q_dtype == KVQ_F32) {
           v = static_cast<const float *>(a.q)[idx];
         } else {
@@ -895,18 +926,20 @@ __global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
   else if (!SLOTS) run_split<QT, KVQ_INT2, false>(a, sp, s_idx, L);
 }
 
-// LDS-staged kernel: page-table mode, INT2 and INT4 splits.
-// g <= 4: three waves per SIMD (at most 168 registers a lane).
-template <int QT>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 1)))
+// LDS-staged kernel: page-table mode, INT2 and INT4 splits; W waves per split with 4 QT
+// query heads each; three waves per SIMD at QT = 1 (at most 168 registers a lane), two
+// at QT = 2.
+template <int W, int QT>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 2)))
 decode_ring_kernel(DecodeArgs a) {
-  __shared__ Lds<QT> L;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+  __shared__ Lds<QT> L[W];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes<W>()];
   const int s_idx = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   kvq_split sp;
-  if (!split_prologue<QT, false, true>(a, s_idx, sp, L)) return;
-  if (sp.cls == KVQ_INT4) run_split_ring<QT, KVQ_INT4>(a, sp, s_idx, L, ring);
-  else if (sp.cls == KVQ_INT2) run_split_ring<QT, KVQ_INT2>(a, sp, s_idx, L, ring);
+  if (!split_prologue<QT, false, true>(a, s_idx, sp, L[wave], 4 * QT * wave)) return;
+  if (sp.cls == KVQ_INT4) run_split_ring<KVQ_INT4, W, QT>(a, sp, s_idx, L[wave], ring, wave);
+  else if (sp.cls == KVQ_INT2) run_split_ring<KVQ_INT2, W, QT>(a, sp, s_idx, L[wave], ring, wave);
 }
 
 // ------------------------------------------------------------------ merge -----
@@ -1024,9 +1057,9 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
   }
   // Page mode: INT2 / INT4 splits (and every malformed one) in the LDS-staged kernel,
   // FP16 splits in the register-staged one when the cache has FP16 pages.
-  if (g <= 4) hipLaunchKernelGGL((decode_ring_kernel<1>), grid, block, 0, s, a);
-  else if (g <= 8) hipLaunchKernelGGL((decode_ring_kernel<2>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((decode_ring_kernel<4>), grid, block, 0, s, a);
+  if (g <= 4) hipLaunchKernelGGL((decode_ring_kernel<1, 1>), grid, dim3(64), 0, s, a);
+  else if (g <= 8) hipLaunchKernelGGL((decode_ring_kernel<1, 2>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_ring_kernel<2, 2>), grid, dim3(128), 0, s, a);
   st = launched("decode_ring_kernel");
   if (st != KVQ_OK || a.n16 == 0) return st;
   a.only_fp16 = 1;
@@ -1053,16 +1086,24 @@ extern "C" kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, 
   return launched("lse_merge_kernel");
 }
 
-extern "C" kvq_status kvq_decode_occupancy(int32_t g, int32_t *per_cu, int32_t *n_cu) {
-  if (!per_cu || !n_cu || g < 1 || g > kMaxG) return fail(KVQ_ERR_INVALID_ARG, "bad occupancy query");
+extern "C" kvq_status kvq_decode_occupancy(int32_t g, int32_t table_kind, int32_t *per_cu, int32_t *n_cu) {
+  if (!per_cu || !n_cu || g < 1 || g > kMaxG || (table_kind != KVQ_TABLE_PAGES && table_kind != KVQ_TABLE_SLOTS))
+    return fail(KVQ_ERR_INVALID_ARG, "bad occupancy query");
   int dev = 0, count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count == 0) return fail(KVQ_ERR_NO_DEVICE, "no HIP device");
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_NO_DEVICE, "hipGetDevice failed");
   int blocks = 0, cus = 0;
   hipError_t e;
-  if (g <= 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1>, 64, 0);
-  else if (g <= 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<2>, 64, 0);
-  else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<4>, 64, 0);
+  const bool slots = table_kind == KVQ_TABLE_SLOTS;
+  if (g <= 4)
+    e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<1, true>, 64, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1, 1>, 64, 0);
+  else if (g <= 8)
+    e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<2, true>, 64, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1, 2>, 64, 0);
+  else
+    e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, true>, 64, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<2, 2>, 128, 0);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(KVQ_ERR_HIP, "CU count query failed");

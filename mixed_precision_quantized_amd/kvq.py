@@ -66,7 +66,7 @@ _SIGS = {
     "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
     "kvq_plan_splits": ([_P, _i32, _i32, _i32, _i32, _P, _P, _i64, _P, _i32, _P, _P], ctypes.c_int),
     "kvq_aot_split_counts": ([_P, _i32, _i32, _i32, _P], ctypes.c_int),
-    "kvq_decode_occupancy": ([_i32, _P, _P], ctypes.c_int),
+    "kvq_decode_occupancy": ([_i32, _i32, _P, _P], ctypes.c_int),
     "kvq_status_string": ([_i32], ctypes.c_char_p),
     "kvq_last_error": ([], ctypes.c_char_p),
 }
@@ -224,9 +224,9 @@ def aot_split_counts(budgets: np.ndarray, batch: int, total_work: int) -> np.nda
     return out
 
 
-def decode_occupancy(g: int):
+def decode_occupancy(g: int, table_kind: int = 0):
     per_cu, n_cu = _i32(), _i32()
-    _check(_lib.kvq_decode_occupancy(g, ctypes.byref(per_cu), ctypes.byref(n_cu)),
+    _check(_lib.kvq_decode_occupancy(g, table_kind, ctypes.byref(per_cu), ctypes.byref(n_cu)),
            "kvq_decode_occupancy")
     return per_cu.value, n_cu.value
 

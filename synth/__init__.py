@@ -451,7 +451,7 @@ def ragged_dead(seed=5, batch=64, lo=4096, hi=131072, device="cpu", dead_frac=0.
     sentinel dead slot.  INT4 per-token."""
     hq, hkv, H = 32, 8, 2
     groups = hkv // H
-    rng = np_rng(seed, 51, layer)
+    rng = np_rng(seed, 51)  # structure (lengths, dead entries) is the same in every layer
     lens = np.round(np.exp(rng.uniform(math.log(lo), math.log(hi), batch))).astype(np.int64)
     r_h = 0.1 + 0.9 * np.arange(hkv) / (hkv - 1)
     n_tables = batch * groups

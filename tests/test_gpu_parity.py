@@ -171,7 +171,7 @@ def test_bad_device_data_is_reported_not_faulted():
 def _resident_plan(gpu):
     """The benchmark's plan: one split per resident wave slot of the decode kernel."""
     w = gpu.w
-    per_cu, n_cu = gpu.kvq.decode_occupancy(w.g)
+    per_cu, n_cu = gpu.kvq.decode_occupancy(w.g, gpu.kvq.TABLE_SLOTS if w.kind == synth.SLOTS else 0)
     sph = max(1, (per_cu * n_cu) // (w.batch * w.hkv))
     return gpu.plan(splits_per_head=np.full(w.batch * w.hkv, sph, np.int32))
 
