@@ -704,6 +704,15 @@ __device__ __forceinline__ void dma_chunk(uint32_t lds, gbytes src) {
                : "memory");
 }
 
+// One 256 B chunk: lane L copies 4 B from src to LDS byte lds + 4 L.
+__device__ __forceinline__ void dma_dword(uint32_t lds, gbytes src) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"((uint64_t)src)
+               : "memory");
+}
+
 // Waits until at most N copies issued by this wave are still in flight (they complete
 // in issue order).
 template <int N>
@@ -865,6 +874,135 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
   R.finish(s_idx);
 }
 
+
+// Slot maps, INT4 splits, one wave.  Every token of a window may live in a different
+// page, so the window's 32 slot ids are copied into LDS one window ahead of its data
+// (lanes 0-31, 4 B each), and the data copies gather per token into the INT4 window
+// layout of the page-table path: K codes (2 x 1 KB, reader-lane order), V codes
+// (2 x 1 KB), K metadata (lanes 0-31, 16 B per token), V metadata (2 x 256 B of 4-byte
+// (token, group) pieces).  Eight copies per window, slot ids first.
+struct SlotRingLoader {
+  using G = RingGeom<KVQ_INT4, 1>;
+  static constexpr int kCopies = 8;
+  static constexpr int kIdBlocks = 4;  // slot-id blocks of 128 B, window i in block i mod 4
+  const kvq_split sp;
+  gbytes trow;
+  const ClassPages<KVQ_INT4> pages;
+  const int32_t sentinel;
+  const int lane, lr, lb;
+  const uint32_t ring, ids;  // LDS byte addresses of the data ring and of the slot-id blocks
+  const uint8_t *lds_ring;
+  const int32_t *lds_ids;
+  uint32_t errs = 0;
+
+  __device__ SlotRingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_, int32_t *ids_)
+      : sp(s_), trow((gbytes)(a.tables + (int64_t)s_.table * a.max_entries)), pages(a, s_.head),
+        sentinel(a.sentinel), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4),
+        ring((uint32_t)(uintptr_t)ring_), ids((uint32_t)(uintptr_t)ids_), lds_ring(ring_), lds_ids(ids_) {}
+
+  // Slot ids of window T (entries clamped into the split) into id block `blk`.
+  __device__ __forceinline__ void issue_ids(int32_t T, int blk) {
+    const int32_t e = min(T + (lane & 31), sp.tok_end - 1);
+    if (lane < 32) dma_dword(ids + 128u * (uint32_t)blk, trow + 4 * (int64_t)e);
+  }
+
+  // Block of a slot id (the class's first block for ids outside the class).
+  __device__ __forceinline__ gbytes block_of(int32_t id, int &off) const {
+    const uint32_t r = pages.rel(id >> 4);
+    const bool ok = id >= 0 && r < pages.count;
+    off = ok ? (id & 15) : 0;
+    return pages.block(ok ? r : 0u);
+  }
+
+  // Copies the data of window T, whose slot ids sit in block `blk`, into data slot
+  // `slot`; returns the window's live mask (bit i: token T + i counts).  A window past
+  // the split's end (`real` false) copies one 16-byte line to every lane.
+  __device__ __forceinline__ uint32_t issue_data(int32_t T, int blk, bool real, int slot) {
+    const int32_t *I = lds_ids + 32 * blk;
+    const uint32_t base = ring + (uint32_t)slot * G::kSlotBytes;
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // reads of the slot are done
+    if (!real) {
+      for (int c = 0; c < 5; ++c) dma_chunk(base + 1024 * c, pages.base);
+      dma_dword(base + 4608, pages.base);
+      dma_dword(base + 4864, pages.base);
+      return 0u;
+    }
+    const int32_t idk0 = I[lr], idk1 = I[16 + lr], idv0 = I[lane >> 2], idv1 = I[16 + (lane >> 2)];
+    const int32_t idm = I[lane & 31];
+    int ok0, ok1, ov0, ov1, om;
+    const gbytes bk0 = block_of(idk0, ok0), bk1 = block_of(idk1, ok1);
+    const gbytes bv0 = block_of(idv0, ov0), bv1 = block_of(idv1, ov1), bm = block_of(idm, om);
+    dma_chunk(base, bk0 + kI4KC + ok0 * 64 + lb * 16);
+    dma_chunk(base + 1024, bk1 + kI4KC + ok1 * 64 + lb * 16);
+    dma_chunk(base + 2048, bv0 + kI4VC + ov0 * 64 + (lane & 3) * 16);
+    dma_chunk(base + 3072, bv1 + kI4VC + ov1 * 64 + (lane & 3) * 16);
+    if (lane < 32) dma_chunk(base + 4096, bm + kI4KM + om * 16);
+    dma_dword(base + 4608, bk0 + kI4VM + ((lane >> 4) * kPage + ok0) * 4);
+    dma_dword(base + 4864, bk1 + kI4VM + ((lane >> 4) * kPage + ok1) * 4);
+    // live mask from lanes 0-31 (token T + lane)
+    const int32_t t = T + (lane & 31);
+    const bool dead = sentinel >= 0 && idm == sentinel;
+    const uint32_t r = pages.rel(idm >> 4);
+    const bool ok = idm >= 0 && r < pages.count;
+    const bool in = lane < 32 && t >= sp.tok_begin && t < sp.tok_end;
+    if (in && !dead && !ok) errs |= KVQ_DEVERR_ID;
+    return (uint32_t)__ballot(in && !dead && ok);
+  }
+
+  // Reads window T from data slot `slot`; live mask `mask`.
+  __device__ __forceinline__ void read(int slot, uint32_t mask, Win &w) const {
+    const uint8_t *S = lds_ring + slot * G::kSlotBytes;
+    const uint8_t *M = S + 4096;
+    w.ok = mask == 0xFFFFFFFFu ? 3u : 0u;  // a window with every token live needs no masks
+    w.live = ((mask >> lr) & 1u) | (((mask >> (16 + lr)) & 1u) << 1);
+    w.vlive = (mask >> (8 * lb)) & 0xFFu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      w.k[h][0] = *reinterpret_cast<const uint4 *>(S + 1024 * h + 16 * lane);
+      w.km[h] = *reinterpret_cast<const uint4 *>(M + 256 * h + 16 * lr);
+    }
+    const int o0 = 8 * (lb & 1);
+    const uint8_t *V = S + 2048 + 1024 * (lb >> 1) + 64 * o0 + 4 * lr;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 64 * q);
+    const uint8_t *VM = M + 512 + 256 * (lb >> 1) + ((lr & 3) * kPage + o0) * 4;
+    w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
+    w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
+  }
+};
+
+template <int QT>
+__device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L,
+                                     uint8_t *ring, int32_t *id_blocks) {
+  using G = RingGeom<KVQ_INT4, 1>;
+  static_assert(G::kSlots == 2, "one window in flight");
+  constexpr int C = SlotRingLoader::kCopies;
+  SlotRingLoader ld(a, sp, ring, id_blocks);
+  SplitRun<QT, KVQ_INT4, true> R(a, sp, L);
+  const int32_t T0 = sp.tok_begin;
+  const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
+  // Window i: slot ids copied at iteration i - 2 into id block i mod 4, data at
+  // iteration i - 1 into data slot i mod 2, computed at iteration i.  Per iteration:
+  // ids of i + 2, (wait: ids of i + 1), data of i + 1, (wait: data of i), compute i.
+  ld.issue_ids(T0, 0);
+  ld.issue_ids(T0 + 32, 1);
+  wait_copies<1>();
+  uint32_t mask_next = ld.issue_data(T0, 0, true, 0);
+  for (int32_t n = 0; n < nw; ++n) {
+    ld.issue_ids(T0 + 32 * (n + 2), (n + 2) & 3);
+    wait_copies<C>();  // the ids of window n + 1
+    const uint32_t mask = mask_next;
+    mask_next = ld.issue_data(T0 + 32 * (n + 1), (n + 1) & 3, n + 1 < nw, (n + 1) & 1);
+    wait_copies<C>();  // the data of window n
+    Win w;
+    ld.read(n & 1, mask, w);
+    R.window(w, T0 + 32 * n);
+  }
+  wait_copies<0>();  // no copy outlives the wave
+  if (ld.errs) report(a.err, (int32_t)ld.errs);
+  R.finish(s_idx);
+}
+
 // Checks split s_idx.  A split this launch does not own returns false at once; an
 // owned split that is malformed or empty (or of a class with no pages) gets O = 0,
 // lse = -inf (and an error bit when malformed) and returns false.  Otherwise stages
@@ -879,10 +1017,10 @@ __device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Ld
                   sp.cls >= 0 && sp.cls <= 2 && sp.tok_begin >= 0 && sp.tok_end >= sp.tok_begin &&
                   sp.tok_end <= cap &&
                   (sp.cls != KVQ_INT2 || (!SLOTS && sp.tok_begin % kGroup == 0 && sp.tok_end % kGroup == 0));
-  // Page mode runs two launches: the LDS-staged one owns every split except the FP16
-  // ones of a cache that has FP16 pages, which the register-staged one takes.
+  // With the LDS-staged kernel in the launch, it owns every split except the FP16 ones
+  // of a cache that has FP16 pages, which the register-staged one takes.
   const bool fp16_elsewhere = ok && sp.cls == KVQ_FP16 && a.n16 > 0;
-  if (!SLOTS && (RING ? fp16_elsewhere : (a.only_fp16 && !fp16_elsewhere))) return false;
+  if (RING ? fp16_elsewhere : (a.only_fp16 && !fp16_elsewhere)) return false;
   const int32_t n_cls = !ok ? 0 : sp.cls == KVQ_INT2 ? a.n2 : sp.cls == KVQ_INT4 ? a.n4 : a.n16;
   if (!ok || sp.tok_end == sp.tok_begin || n_cls == 0) {
     if (lane == 0 && (!ok || sp.tok_end > sp.tok_begin))  // (a class with no pages: its ids are bad)
@@ -940,6 +1078,19 @@ decode_ring_kernel(DecodeArgs a) {
   if (!split_prologue<QT, false, true>(a, s_idx, sp, L[wave], 4 * QT * wave)) return;
   if (sp.cls == KVQ_INT4) run_split_ring<KVQ_INT4, W, QT>(a, sp, s_idx, L[wave], ring, wave);
   else if (sp.cls == KVQ_INT2) run_split_ring<KVQ_INT2, W, QT>(a, sp, s_idx, L[wave], ring, wave);
+}
+
+// LDS-staged kernel for slot maps (INT4 splits, g <= 8).
+template <int QT>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 2)))
+decode_slots_ring_kernel(DecodeArgs a) {
+  __shared__ Lds<QT> L;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes<1>()];
+  __shared__ __attribute__((aligned(16))) int32_t id_blocks[SlotRingLoader::kIdBlocks * 32];
+  const int s_idx = blockIdx.x;
+  kvq_split sp;
+  if (!split_prologue<QT, true, true>(a, s_idx, sp, L)) return;
+  if (sp.cls == KVQ_INT4) run_split_slots_ring<QT>(a, sp, s_idx, L, ring, id_blocks);
 }
 
 // ------------------------------------------------------------------ merge -----
@@ -1050,9 +1201,19 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(n_splits), block(64);
   if (table_kind == KVQ_TABLE_SLOTS) {
+    if (g > 8) {  // register-staged kernel for every split
+      hipLaunchKernelGGL((decode_kernel<4, true>), grid, block, 0, s, a);
+      return launched("decode_kernel");
+    }
+    // INT4 splits (and every malformed one) in the LDS-staged kernel, FP16 splits in
+    // the register-staged one when the cache has FP16 pages.
+    if (g <= 4) hipLaunchKernelGGL((decode_slots_ring_kernel<1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_slots_ring_kernel<2>), grid, block, 0, s, a);
+    st = launched("decode_slots_ring_kernel");
+    if (st != KVQ_OK || a.n16 == 0) return st;
+    a.only_fp16 = 1;
     if (g <= 4) hipLaunchKernelGGL((decode_kernel<1, true>), grid, block, 0, s, a);
-    else if (g <= 8) hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<4, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, s, a);
     return launched("decode_kernel");
   }
   // Page mode: INT2 / INT4 splits (and every malformed one) in the LDS-staged kernel,
@@ -1096,10 +1257,10 @@ extern "C" kvq_status kvq_decode_occupancy(int32_t g, int32_t table_kind, int32_
   hipError_t e;
   const bool slots = table_kind == KVQ_TABLE_SLOTS;
   if (g <= 4)
-    e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<1, true>, 64, 0)
+    e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_slots_ring_kernel<1>, 64, 0)
               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1, 1>, 64, 0);
   else if (g <= 8)
-    e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<2, true>, 64, 0)
+    e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_slots_ring_kernel<2>, 64, 0)
               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1, 2>, 64, 0);
   else
     e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, true>, 64, 0)
