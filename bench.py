@@ -103,7 +103,7 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def resident_plan(gpu, kvq, synth, splits_per_head=0):
+def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None):
     """One wave per split, as many splits as the decode kernel keeps resident at once
     (a second, partial round of waves would leave most of the chip idle).  Ragged slot
     maps share the count among heads in proportion to their budgets (Tangram AOT)."""
@@ -117,7 +117,7 @@ def resident_plan(gpu, kvq, synth, splits_per_head=0):
         sph = kvq.aot_split_counts(w.head_budget, w.batch, per_cu * n_cu)
     else:
         sph = np.full(w.batch * w.hkv, max(1, (per_cu * n_cu) // (w.batch * w.hkv)), np.int32)
-    splits, offsets = gpu.plan(splits_per_head=sph)
+    splits, offsets = gpu.plan(splits_per_head=sph, class_cost=class_cost)
     return splits, offsets, per_cu, n_cu
 
 
@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--splits-per-head", type=int, default=0,
                     help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
+    ap.add_argument("--class-cost", default=None,
+                    help="per-token decode cost INT2,INT4,FP16 for sharing splits (default: the library's)")
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (reference for HBM byte counters)")
@@ -182,7 +184,8 @@ def main():
         del w
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    splits, offsets, per_cu, n_cu = resident_plan(gpu, kvq, synth, args.splits_per_head)
+    cost = None if args.class_cost is None else [float(x) for x in args.class_cost.split(",")]
+    splits, offsets, per_cu, n_cu = resident_plan(gpu, kvq, synth, args.splits_per_head, cost)
     n_splits = splits.shape[0]
     sp = torch.as_tensor(splits, device=dev).contiguous()
     off = torch.as_tensor(offsets, device=dev)

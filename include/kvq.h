@@ -214,22 +214,25 @@ kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, int32_t n_s
  * precedence:
  *   splits_per_head [host, may be NULL]: int32 [n_tables*heads_per_page]
  *     pieces per (table, head), shared among its non-empty ranges in proportion
- *     to their decode cost (tokens x 1.0 / 1.3 / 4.0 for INT2 / INT4 / FP16:
- *     the kernel's relative time per token-head on MI355X), at least one each,
- *     largest remainders first, so a head gets exactly its count whenever that
- *     is at least its number of non-empty ranges;
+ *     to their decode cost, tokens x class_cost[cls] (class_cost [host, may be
+ *     NULL]: float [3] per INT2 / INT4 / FP16 token-head, all > 0; NULL =
+ *     1.0 / 1.0 / 4.0, the kernel's relative time per token-head on MI355X), at
+ *     least one each, largest remainders first, so a head gets exactly its count
+ *     whenever that is at least its number of non-empty ranges;
  *   tokens_per_split[cls] > 0 [host, may be NULL]: ceil(tokens / that);
  *   otherwise max(1, round(range bytes / target_bytes)) with 96 / 160 / 512
  *     bytes per INT2 / INT4 / FP16 token-head.
  * Writes out[0 .. *n_out) [host] sorted by (table, head) and split_offsets
  * [host] int32 [batch*hkv + 1] for kvq_lse_merge.
- * Errors: INVALID_ARG (unsorted or malformed ranges), CAPACITY (max_out).
+ * Errors: INVALID_ARG (unsorted or malformed ranges, non-positive costs),
+ * CAPACITY (max_out).
  */
 kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t batch,
                            int32_t hkv, int32_t heads_per_page,
-                           const int32_t *splits_per_head, const int32_t *tokens_per_split,
-                           int64_t target_bytes, kvq_split *out, int32_t max_out,
-                           int32_t *n_out, int32_t *split_offsets);
+                           const int32_t *splits_per_head, const float *class_cost,
+                           const int32_t *tokens_per_split, int64_t target_bytes,
+                           kvq_split *out, int32_t max_out, int32_t *n_out,
+                           int32_t *split_offsets);
 
 /*
  * Ahead-of-time split counts [host] (Tangram steps 6-7: a partition factor per

@@ -1095,7 +1095,10 @@ decode_slots_ring_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ merge -----
 
-// One wavefront per (request, query head); lane = channel pair.
+// One wavefront per (request, query head); lane = channel pair.  The row's split lse
+// values are read 64 at a time (lane = split), their maximum and weights
+// exp(lse - max) computed across the wave, and the partial rows are loaded 16 at a
+// time before any is used, so a row costs about one memory latency per 16 splits.
 __global__ void __launch_bounds__(64) lse_merge_kernel(const float *part_o, const float *part_lse,
                                                        int32_t n_splits, const int32_t *offsets, int32_t hq,
                                                        int32_t hkv, void *out, int32_t out_dtype,
@@ -1107,17 +1110,36 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(const float *part_o, cons
   const int32_t s0 = min(max(offsets[(int64_t)b * hkv + kvh], 0), n_splits);
   const int32_t s1 = min(max(offsets[(int64_t)b * hkv + kvh + 1], s0), n_splits);
   float mx = -INFINITY;
-  for (int32_t s = s0; s < s1; ++s) mx = fmaxf(mx, part_lse[(int64_t)s * g + j]);
+  for (int32_t base = s0; base < s1; base += 64) {
+    const int32_t s = base + lane;
+    if (s < s1) mx = fmaxf(mx, part_lse[(int64_t)s * g + j]);
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float o0 = 0.0f, o1 = 0.0f, lse = -INFINITY;
   if (mx != -INFINITY) {
     float tot = 0.0f;
-    for (int32_t s = s0; s < s1; ++s) {
-      const float w = expf(part_lse[(int64_t)s * g + j] - mx);
-      const float2 po = *reinterpret_cast<const float2 *>(part_o + ((int64_t)s * g + j) * kHeadDim + 2 * lane);
+    for (int32_t base = s0; base < s1; base += 64) {
+      const int32_t s = base + lane;
+      const float w = s < s1 ? expf(part_lse[(int64_t)s * g + j] - mx) : 0.0f;  // lane k: split base + k
       tot += w;
-      o0 = fmaf(w, po.x, o0);
-      o1 = fmaf(w, po.y, o1);
+      const int32_t n = min(s1 - base, 64);
+      for (int32_t k0 = 0; k0 < n; k0 += 16) {
+        float2 po[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int32_t kk = min(k0 + k, n - 1);  // past the end: a repeated row, weight 0
+          po[k] = *reinterpret_cast<const float2 *>(part_o + ((int64_t)(base + kk) * g + j) * kHeadDim + 2 * lane);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float wk = __shfl(w, k0 + k < n ? k0 + k : 63);  // lane 63's w is 0 unless n = 64
+          const float wk_valid = k0 + k < n ? wk : 0.0f;
+          o0 = fmaf(wk_valid, po[k].x, o0);
+          o1 = fmaf(wk_valid, po[k].y, o1);
+        }
+      }
     }
+    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
     o0 /= tot;
     o1 /= tot;
     lse = mx + logf(tot);

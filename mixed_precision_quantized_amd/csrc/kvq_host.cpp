@@ -45,10 +45,11 @@ kvq_status check_cache(const kvq_cache *c) {
 
 static int64_t token_bytes(int cls) { return cls == KVQ_INT2 ? 96 : cls == KVQ_INT4 ? 160 : 512; }
 
-// Relative decode time of one token-head per class on MI355X, used to share a head's
-// split count among its ranges: INT2 windows are bound by dequantization work, INT4
-// and FP16 ones by their bytes (160 / 512 B against 96 B).
-static double token_cost(int cls) { return cls == KVQ_INT2 ? 1.0 : cls == KVQ_INT4 ? 1.3 : 4.0; }
+// Default relative decode time of one token-head per class on MI355X, used to share a
+// head's split count among its ranges.  INT2 windows are bound by dequantization work
+// and INT4 ones by their bytes, which takes about as long per token (measured: a
+// weight of 1.0 for INT4 beat 0.8 and 1.15-1.8); FP16 windows move 512 B per token.
+static const float kDefaultTokenCost[3] = {1.0f, 1.0f, 4.0f};
 
 }  // namespace kvq
 
@@ -102,8 +103,12 @@ kvq_status kvq_route_tokens(const uint8_t *flags, int32_t n, uint8_t *cls_out, i
 
 kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t batch, int32_t hkv,
                            int32_t heads_per_page, const int32_t *splits_per_head,
-                           const int32_t *tokens_per_split, int64_t target_bytes, kvq_split *out,
-                           int32_t max_out, int32_t *n_out, int32_t *split_offsets) {
+                           const float *class_cost, const int32_t *tokens_per_split, int64_t target_bytes,
+                           kvq_split *out, int32_t max_out, int32_t *n_out, int32_t *split_offsets) {
+  const float *cost = class_cost ? class_cost : kDefaultTokenCost;
+  for (int c = 0; c < 3; ++c)
+    if (!(cost[c] > 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "class cost %d is not positive", c);
+  auto token_cost = [cost](int cls) { return (double)cost[cls]; };
   if (n_ranges < 0 || batch < 0 || hkv <= 0 || heads_per_page <= 0 || hkv % heads_per_page)
     return fail(KVQ_ERR_INVALID_ARG, "bad plan shape");
   if ((n_ranges > 0 && !ranges) || !n_out || !split_offsets || (max_out > 0 && !out))

@@ -64,7 +64,7 @@ _SIGS = {
     "kvq_decode_attn": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P, _P,
                          _P], ctypes.c_int),
     "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
-    "kvq_plan_splits": ([_P, _i32, _i32, _i32, _i32, _P, _P, _i64, _P, _i32, _P, _P], ctypes.c_int),
+    "kvq_plan_splits": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _i64, _P, _i32, _P, _P], ctypes.c_int),
     "kvq_aot_split_counts": ([_P, _i32, _i32, _i32, _P], ctypes.c_int),
     "kvq_decode_occupancy": ([_i32, _i32, _P, _P], ctypes.c_int),
     "kvq_status_string": ([_i32], ctypes.c_char_p),
@@ -196,7 +196,7 @@ def lse_merge(part_o: torch.Tensor, part_lse: torch.Tensor, n_splits: int, split
 
 def plan_splits(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int,
                 splits_per_head: Optional[np.ndarray] = None, tokens_per_split=None,
-                target_bytes: int = 0, max_out: Optional[int] = None):
+                target_bytes: int = 0, max_out: Optional[int] = None, class_cost=None):
     """ranges: structured (SPLIT_DTYPE) or int32 [n, 5], sorted by (table, head).
     Returns (splits int32 [n_out, 5], split_offsets int32 [batch*hkv + 1])."""
     r = np.ascontiguousarray(np.asarray(ranges).view(np.int32).reshape(-1, 5))
@@ -210,7 +210,8 @@ def plan_splits(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int,
     n_out = _i32()
     sph = None if splits_per_head is None else np.ascontiguousarray(splits_per_head, np.int32)
     tps = None if tokens_per_split is None else np.ascontiguousarray(tokens_per_split, np.int32)
-    _check(_lib.kvq_plan_splits(_hptr(r), r.shape[0], batch, hkv, heads_per_page, _hptr(sph),
+    cc = None if class_cost is None else np.ascontiguousarray(class_cost, np.float32)
+    _check(_lib.kvq_plan_splits(_hptr(r), r.shape[0], batch, hkv, heads_per_page, _hptr(sph), _hptr(cc),
                                 _hptr(tps), int(target_bytes), _hptr(out), max_out,
                                 ctypes.byref(n_out), _hptr(offsets)), "kvq_plan_splits")
     return out[: n_out.value].copy(), offsets

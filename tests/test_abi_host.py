@@ -145,3 +145,15 @@ def test_validation_fails_before_any_launch(kvq):
     assert b"dtype" in lib.kvq_last_error()
     for st in (0, -1, -2, -3, -4, -5, 7):
         assert kvq.status_string(st)
+
+
+def test_plan_splits_class_cost_shares_a_head_count(kvq):
+    """A head's count is shared by tokens x class cost, largest remainders first."""
+    rng = _ranges([(0, 0, 0, 0, 640), (0, 0, 1, 640, 960)], kvq)   # 640 INT2 + 320 INT4 tokens
+    sph = np.array([9], np.int32)
+    s, _ = kvq.plan_splits(rng, 1, 1, 1, splits_per_head=sph, class_cost=[1.0, 1.0, 1.0])
+    assert [int((s[:, 2] == c).sum()) for c in (0, 1)] == [6, 3]     # 1 + 7*2/3, 1 + 7/3 -> 5.67, 3.33
+    s, _ = kvq.plan_splits(rng, 1, 1, 1, splits_per_head=sph, class_cost=[1.0, 2.0, 1.0])
+    assert [int((s[:, 2] == c).sum()) for c in (0, 1)] == [5, 4]     # 1 + 3.5, 1 + 3.5 -> 4.5, 4.5
+    with pytest.raises(kvq.KvqError):
+        kvq.plan_splits(rng, 1, 1, 1, splits_per_head=sph, class_cost=[1.0, 0.0, 1.0])
