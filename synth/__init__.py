@@ -442,6 +442,12 @@ def hybrid_anchor(seed=4, batch=32, n_tokens=65536, device="cpu", window=128, st
                     note=f"per head {n_q} INT4 + {n_vl} VL + {staging} staging + {window} window")
 
 
+def ragged_lengths(seed=5, batch=64, lo=4096, hi=131072):
+    """Context lengths of the ragged workload: log-uniform in [lo, hi]."""
+    rng = np_rng(seed, 51)
+    return np.round(np.exp(rng.uniform(math.log(lo), math.log(hi), batch))).astype(np.int64)
+
+
 def ragged_dead(seed=5, batch=64, lo=4096, hi=131072, device="cpu", dead_frac=0.2, layer=0):
     """Ragged per-head budgets with sentinel dead slots: Hq 32 / Hkv 8, context lengths
     log-uniform in [lo, hi]; per-KV-head retained fraction r_h = 0.1 + 0.9 h / 7; heads
@@ -451,8 +457,7 @@ def ragged_dead(seed=5, batch=64, lo=4096, hi=131072, device="cpu", dead_frac=0.
     sentinel dead slot.  INT4 per-token."""
     hq, hkv, H = 32, 8, 2
     groups = hkv // H
-    rng = np_rng(seed, 51)  # structure (lengths, dead entries) is the same in every layer
-    lens = np.round(np.exp(rng.uniform(math.log(lo), math.log(hi), batch))).astype(np.int64)
+    lens = ragged_lengths(seed, batch, lo, hi)  # structure is the same in every layer
     r_h = 0.1 + 0.9 * np.arange(hkv) / (hkv - 1)
     n_tables = batch * groups
     head_tokens = np.zeros((n_tables, H), np.int32)
@@ -488,10 +493,11 @@ def ragged_dead(seed=5, batch=64, lo=4096, hi=131072, device="cpu", dead_frac=0.
 
 
 def subset(w: Workload, requests, device="cpu") -> Workload:
-    """The same page-table workload restricted to some requests (tables of those
-    requests, their source rows and queries), with a fresh allocator sized for them.
-    Entry structure per table is unchanged; physical page ids differ."""
-    assert w.kind == PAGES
+    """The same workload restricted to some requests (tables of those requests, their
+    source rows and queries), with a fresh allocator sized for them.  Entry structure
+    per table is unchanged; physical page ids differ."""
+    if w.kind == SLOTS:
+        return _subset_slots(w, requests, device)
     tpr = w.hkv // w.heads_per_page
     tabs = [b * tpr + i for b in requests for i in range(tpr)]
     rows, calls, new_calls = [], [], []
@@ -517,6 +523,29 @@ def subset(w: Workload, requests, device="cpu") -> Workload:
     alloc = PageAllocator(n_pages, w.heads_per_page, len(tabs), w.alloc.max_entries, w.seed + 1000)
     return dataclasses.replace(w, batch=len(requests), k=k, v=v, q=q, n_pages=n_pages, alloc=alloc,
                                calls=new_calls, note=w.note + f" (requests {list(requests)})")
+
+
+def _subset_slots(w: Workload, requests, device="cpu") -> Workload:
+    """subset() for slot-map workloads: row 0 (the sentinel row) is kept as row 0."""
+    tpr = w.hkv // w.heads_per_page
+    tabs = [b * tpr + i for b in requests for i in range(tpr)]
+    calls = [(tabs.index(t), f, r, n) for (t, f, r, n) in w.calls if t in tabs]
+    all_rows = np.unique(np.concatenate([np.array([0], np.int32)] + [c[2] for c in calls]))
+    remap = np.zeros(int(all_rows.max()) + 1, np.int64)
+    remap[all_rows] = np.arange(len(all_rows))
+    new_calls = [(t, f, remap[r].astype(np.int32), n) for (t, f, r, n) in calls]
+    idx = torch.as_tensor(all_rows, device=w.k.device, dtype=torch.long)
+    k = w.k.index_select(0, idx).to(device)
+    v = w.v.index_select(0, idx).to(device)
+    q = w.q[torch.as_tensor(list(requests), device=w.q.device)].to(device)
+    n4 = 1 + sum(-(-len(c[1]) // PAGE) for c in new_calls)
+    alloc = PageAllocator((0, n4, 0), w.heads_per_page, len(tabs), w.alloc.max_entries, w.seed + 1000,
+                          reserve_int4=1)
+    return dataclasses.replace(w, batch=len(requests), k=k, v=v, q=q, n_pages=(0, n4, 0), alloc=alloc,
+                               calls=new_calls, sentinel_slot=alloc.reserved4[0] * PAGE,
+                               dead_entries=[w.dead_entries[t] for t in tabs],
+                               head_tokens=w.head_tokens[tabs].copy(),
+                               note=w.note + f" (requests {list(requests)})")
 
 
 # ----------------------------------------------------------------------------

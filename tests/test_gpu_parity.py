@@ -169,11 +169,47 @@ def test_bad_device_data_is_reported_not_faulted():
 
 
 def _resident_plan(gpu):
-    """The benchmark's plan: one split per resident wave slot of the decode kernel."""
+    """The benchmark's plan: one split per resident work group of the decode kernel,
+    shared among heads by budget (Tangram AOT) for ragged workloads."""
     w = gpu.w
     per_cu, n_cu = gpu.kvq.decode_occupancy(w.g, gpu.kvq.TABLE_SLOTS if w.kind == synth.SLOTS else 0)
+    if w.head_budget is not None:
+        return gpu.plan(splits_per_head=gpu.kvq.aot_split_counts(w.head_budget, w.batch, per_cu * n_cu))
     sph = max(1, (per_cu * n_cu) // (w.batch * w.hkv))
     return gpu.plan(splits_per_head=np.full(w.batch * w.hkv, sph, np.int32))
+
+
+def _full_size_sampled(name, make, requests):
+    """Full-size workload with the benchmark's plan on the GPU; the oracle recomputes
+    the sampled requests from the same seeded sources."""
+    _say(f"full-size {name}: generating on the GPU")
+    w = make()
+    gpu = GpuRun(w)
+    splits, offsets = _resident_plan(gpu)
+    out, lse, _, _ = gpu.decode(splits, offsets)
+    assert int(gpu.err.item()) == 0
+    _say(f"  {w.note}; {splits.shape[0]} splits decoded; oracle on requests {requests}")
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    del gpu, w
+    ref, ref_lse = OracleRun(synth.subset(make(), requests)).attend()
+    err = row_metric(ref, out[requests])
+    _say(f"  sampled row error {err:.2e}")
+    assert err <= TOL
+    assert np.allclose(lse[requests], ref_lse, rtol=0, atol=1e-3)
+
+
+def test_full_size_hybrid_anchor_sampled():
+    """FP16 anchors at full size (32 requests x 8 heads x 65536 tokens, INT4 prefix and
+    FP16 vertical-line / staging / window segments): two launches (INT4, FP16)."""
+    _full_size_sampled("hybrid_anchor", lambda: synth.hybrid_anchor(device="cuda"), [7])
+
+
+def test_full_size_ragged_dead_sampled():
+    """Ragged slot maps with 20 % dead slots at full size (64 requests, 4K-128K tokens),
+    budget-proportional split counts; a short and a long request sampled."""
+    lens = synth.ragged_lengths()
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens))})
+    _full_size_sampled("ragged_dead", lambda: synth.ragged_dead(device="cuda"), pick)
 
 
 def test_qwen3_vl_agentic_small():

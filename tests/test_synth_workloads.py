@@ -40,3 +40,29 @@ def test_agentic_recipe():
     lists = synth.place_all(w, lambda f: oracle.route(f)[0])
     assert len(lists.rows2) == 32 * len(lists.pages2)
     assert int(w.alloc.n_entries.max()) <= w.alloc.max_entries
+
+
+def _oracle_rows(w, requests=None):
+    import sys, os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from harness import OracleRun
+    out, lse = OracleRun(w).attend()
+    return (out, lse) if requests is None else (out[requests], lse[requests])
+
+
+def test_subset_reproduces_the_sampled_requests():
+    """Full-size parity samples requests through subset(): the oracle on the subset must
+    equal the oracle on the whole workload for those requests (page and slot maps)."""
+    for make, req in ((lambda: synth.qwen3_8b(batch=3, n_tokens=1024), [0, 2]),
+                      (lambda: synth.ragged_dead(batch=4, lo=512, hi=4096), [1, 3]),
+                      (lambda: synth.hybrid_anchor(batch=2, n_tokens=2048), [1])):
+        full_o, full_l = _oracle_rows(make(), req)
+        sub_o, sub_l = _oracle_rows(synth.subset(make(), req))
+        assert np.array_equal(full_o, sub_o) and np.array_equal(full_l, sub_l)
+
+
+def test_ragged_lengths_match_the_workload():
+    w = synth.ragged_dead(batch=6, lo=512, hi=4096)
+    lens = synth.ragged_lengths(batch=6, lo=512, hi=4096)
+    tl = w.head_tokens.reshape(6, -1).max(axis=1)
+    assert np.array_equal(tl, np.ceil(lens * 1.0).astype(np.int64))
