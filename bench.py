@@ -103,16 +103,20 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None):
-    """One wave per split, as many splits as the decode kernel keeps resident at once
-    (a second, partial round of waves would leave most of the chip idle).  Ragged slot
-    maps share the count among heads in proportion to their budgets (Tangram AOT)."""
+def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_plan="aot"):
+    """One work group per split, as many splits as the decode kernel keeps resident at
+    once (a second, partial round would leave most of the chip idle).  Ragged slot maps
+    share the count among heads in proportion to their budgets (Tangram AOT), or, with
+    ragged_plan="tokens", to the tokens each head reads."""
     import numpy as np
     w = gpu.w
     kind = kvq.TABLE_SLOTS if w.kind == synth.SLOTS else kvq.TABLE_PAGES
     per_cu, n_cu = kvq.decode_occupancy(w.g, kind)
     if splits_per_head:
         sph = np.full(w.batch * w.hkv, splits_per_head, np.int32)
+    elif w.head_tokens is not None and ragged_plan == "tokens":
+        toks = w.head_tokens.reshape(-1).astype(np.float64)
+        sph = np.maximum(1, np.floor(per_cu * n_cu * toks / toks.sum())).astype(np.int32)
     elif w.head_budget is not None:
         sph = kvq.aot_split_counts(w.head_budget, w.batch, per_cu * n_cu)
     else:
@@ -132,6 +136,8 @@ def main():
                     help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
     ap.add_argument("--class-cost", default=None,
                     help="per-token decode cost INT2,INT4,FP16 for sharing splits (default: the library's)")
+    ap.add_argument("--ragged-plan", choices=("aot", "tokens"), default="aot",
+                    help="split counts of ragged slot maps: by budget (Tangram AOT) or by tokens read")
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (reference for HBM byte counters)")
@@ -185,7 +191,7 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     cost = None if args.class_cost is None else [float(x) for x in args.class_cost.split(",")]
-    splits, offsets, per_cu, n_cu = resident_plan(gpu, kvq, synth, args.splits_per_head, cost)
+    splits, offsets, per_cu, n_cu = resident_plan(gpu, kvq, synth, args.splits_per_head, cost, args.ragged_plan)
     n_splits = splits.shape[0]
     sp = torch.as_tensor(splits, device=dev).contiguous()
     off = torch.as_tensor(offsets, device=dev)
