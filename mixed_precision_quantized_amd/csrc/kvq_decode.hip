@@ -426,9 +426,18 @@ struct SplitRun {
       const int32_t lo = min(max(sp.tok_begin - t0, 0), 8), hi = min(max(sp.tok_end - t0, 0), 8);
       vlive = (w.ok >> (lb >> 1) & 1) ? (0xFFu >> (8 - hi)) & (0xFFu << lo) & 0xFFu : 0u;
     }
+    // V metadata (scale, zero) of this lane's 8 P V tokens; a token that does not count
+    // may sit in an unwritten slot, so its pair is cleared (its weight is 0, and 0 times
+    // a non-finite scale would not be).
+    uint32_t mv[8] = {w.vm[0].x, w.vm[0].y, w.vm[0].z, w.vm[0].w, w.vm[1].x, w.vm[1].y, w.vm[1].z, w.vm[1].w};
+    if (CLS != KVQ_FP16 && partial) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) mv[q] = (vlive >> q & 1) ? mv[q] : 0u;
+    }
 
-    // INT2: zero term of the pair, sum over the group of q (z + 2 s).
-    f4 c2[QT];
+    // INT2: zero term of the pair, q . (z + 2 s) summed over the 128 channels (the 16
+    // lanes of row lb hold 8 channels each); added to the logits of query 4 qt + lb.
+    float c2[QT];
     if (CLS == KVQ_INT2) {
       const uint32_t ks[4] = {w.ks.x, w.ks.y, w.ks.z, w.ks.w};
       const uint32_t kz[4] = {w.kz.x, w.kz.y, w.kz.z, w.kz.w};
@@ -440,9 +449,7 @@ struct SplitRun {
           bz = dot2(qn[qt][u], as_h2(kz[u]), bz);
           bs = dot2(qn[qt][u], as_h2(ks[u]), bs);
         }
-        const float bias = quad_sum(fmaf(2.0f, bs, bz));  // query 4 qt + lb, group lr / 4
-#pragma unroll
-        for (int r = 0; r < 4; ++r) c2[qt][r] = __shfl(bias, 16 * lb + 4 * r);
+        c2[qt] = row_sum16(fmaf(2.0f, bs, bz));
       }
     }
 
@@ -470,7 +477,7 @@ struct SplitRun {
       const bool tok_live = live >> h & 1;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        f4 d = CLS == KVQ_INT2 ? c2[qt] : f4{0.f, 0.f, 0.f, 0.f};
+        f4 d = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) d = mfma(Aq[qt][m], kb[m], d);
         float s;
@@ -480,34 +487,13 @@ struct SplitRun {
 #pragma unroll
           for (int r = 0; r < 4; ++r)  // s (q . (offset + c) - q . offset) + z sum(q)
             s = fmaf(h2f(mm[r]), d[r] - qoff[qt][r], fmaf(h2f(mm[r] >> 16), qsum[qt][r], s));
+        } else if (CLS == KVQ_INT2) {
+          s = ((d[0] + d[1]) + (d[2] + d[3])) + c2[qt];
         } else {
           s = (d[0] + d[1]) + (d[2] + d[3]);
         }
         x[qt][h] = tok_live ? s * scale : -INFINITY;
       }
-    }
-
-    // Online softmax per query (the 16 lanes of row lb).
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float bm = row_max16(fmaxf(x[qt][0], x[qt][1]));
-      const float mn = fmaxf(m_run[qt], bm);
-      if (__any(mn > m_run[qt])) {  // rare after the first windows
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mn);
-        l_run[qt] *= alpha;
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
-        const float alpha_row = __shfl(alpha, 16 * (lr >> 2));  // rows lr belong to query lr / 4
-        zacc[qt] *= alpha_row;
-        asum[qt] *= alpha_row;
-        m_run[qt] = mn;
-      }
-      // v_exp_f32: exp2(-inf) = 0; results below 2^-126 may flush to zero, which no
-      // softmax weight of consequence is.
-      const float p0 = __builtin_amdgcn_exp2f(x[qt][0] - m_run[qt]), p1 = __builtin_amdgcn_exp2f(x[qt][1] - m_run[qt]);
-      l_run[qt] += p0 + p1;
-      L.p[qt][lb][lr] = (_Float16)p0;
-      L.p[qt][lb][16 + lr] = (_Float16)p1;
     }
 
     // V operand: this lane's channels 8 lr + nt, its 8 tokens as 4 pairs.
@@ -565,6 +551,29 @@ struct SplitRun {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) vb[nt] = h8_of(t[nt][0], t[nt][1], t[nt][2], t[nt][3]);
     }
+    // Online softmax per query (the 16 lanes of row lb).
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float bm = row_max16(fmaxf(x[qt][0], x[qt][1]));
+      const float mn = fmaxf(m_run[qt], bm);
+      if (__any(mn > m_run[qt])) {  // rare after the first windows
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mn);
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
+        const float alpha_row = __shfl(alpha, 16 * (lr >> 2));  // rows lr belong to query lr / 4
+        zacc[qt] *= alpha_row;
+        asum[qt] *= alpha_row;
+        m_run[qt] = mn;
+      }
+      // v_exp_f32: exp2(-inf) = 0; results below 2^-126 may flush to zero, which no
+      // softmax weight of consequence is.
+      const float p0 = __builtin_amdgcn_exp2f(x[qt][0] - m_run[qt]), p1 = __builtin_amdgcn_exp2f(x[qt][1] - m_run[qt]);
+      l_run[qt] += p0 + p1;
+      L.p[qt][lb][lr] = (_Float16)p0;
+      L.p[qt][lb][16 + lr] = (_Float16)p1;
+    }
+
     __syncthreads();  // the weights of this window are in LDS
 
     // P V.
@@ -576,19 +585,11 @@ struct SplitRun {
         ap = h8_of(pw);
       } else {
         const uint32_t p2[4] = {pw.x, pw.y, pw.z, pw.w};
-        const uint32_t mv[8] = {w.vm[0].x, w.vm[0].y, w.vm[0].z, w.vm[0].w,
-                                w.vm[1].x, w.vm[1].y, w.vm[1].z, w.vm[1].w};
         uint32_t aw[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          uint32_t s2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x05040100u);  // scales
-          uint32_t z2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x07060302u);  // zeros
-          if (partial) {
-            const uint32_t mk = ((vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
-                                ((vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
-            s2 &= mk;
-            z2 &= mk;
-          }
+          const uint32_t s2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x05040100u);  // scales
+          const uint32_t z2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x07060302u);  // zeros
           const h2 pp = as_h2(p2[u]), ap2 = pp * as_h2(s2);
           aw[u] = as_u32(ap2);
           zacc[qt] = dot2(pp, as_h2(z2), zacc[qt]);
@@ -683,12 +684,17 @@ constexpr int ring_bytes() { return W == 1 ? 10240 : 15360; }
 
 template <int CLS, int W>
 struct RingGeom {
-  static constexpr int kChunks = CLS == KVQ_INT4 ? 5 : 3;  // INT4: K x2, V x2, meta; INT2: K, V, meta
-  static constexpr int kSlotBytes = kChunks * 1024;
+  // Copies per window, each from one page block (see RingLoader::issue):
+  // INT4: K codes x2, V codes x2, metadata x2 (half-wave each); INT2: the first KB of
+  // each page, then the last 512 B of each page (half-wave each).
+  static constexpr int kChunks = CLS == KVQ_INT4 ? 6 : 4;
+  static constexpr int kSlotBytes = CLS == KVQ_INT4 ? 5120 : 3072;
   static constexpr int kSlots = ring_bytes<W>() / kSlotBytes;
-  // Windows in flight.  With several waves one more slot stays untouched while
-  // being refilled, so a wave still reading its previous window never races a copy.
-  static constexpr int kAhead = kSlots - (W == 1 ? 1 : 2);
+  // Windows copied ahead of the one computed.  One wave refills a slot as soon as its
+  // window sits in registers, so every slot is in flight during a compute; with
+  // several waves the slot refilled is the previous window's, which the block barrier
+  // of the current window shows every wave to have read.
+  static constexpr int kAhead = kSlots - (W == 1 ? 0 : 1);
   static_assert(kAhead >= 1, "ring too small");
   // Copies wave w issues per window: chunks c with c % W == w.
   static constexpr int chunks_of(int w) { return (kChunks - w + W - 1) / W; }
@@ -704,6 +710,16 @@ __device__ __forceinline__ void dma_chunk(uint32_t lds, gbytes src) {
                : "memory");
 }
 
+// One 1 KB chunk from one page block: lane L copies 16 B from base + voff (base
+// wave-uniform in SGPRs, voff per lane) to LDS byte lds + 16 L.
+__device__ __forceinline__ void dma_block(uint32_t lds, gbytes base, uint32_t voff) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds), "v"(voff), "s"((uint64_t)base)
+               : "memory");
+}
+
 // One 256 B chunk: lane L copies 4 B from src to LDS byte lds + 4 L.
 __device__ __forceinline__ void dma_dword(uint32_t lds, gbytes src) {
   uint32_t saved;
@@ -713,12 +729,46 @@ __device__ __forceinline__ void dma_dword(uint32_t lds, gbytes src) {
                : "memory");
 }
 
+// Lanes 0 and 1 copy the dwords at base + voff to LDS bytes lds, lds + 4 (the other
+// lanes copy nothing).
+__device__ __forceinline__ void dma_pair(uint32_t lds, gbytes base, uint32_t voff, int lane) {
+  if (lane < 2) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(lds), "v"(voff), "s"((uint64_t)base)
+                 : "memory");
+  }
+}
+
 // Waits until at most N copies issued by this wave are still in flight (they complete
 // in issue order).
 template <int N>
 __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
+
+// Issue priority by progress.  A SIMD's waves issue oldest first among equal
+// priorities, so waves given equal work would finish one after another and leave the
+// SIMD to a single wave at the end.  A wave lowers its priority when half, three
+// quarters and seven eighths of its split are done: waves ahead yield to waves behind
+// at each of these points, and only the last eighth runs oldest first.
+struct ProgressPriority {
+  int32_t next, level = 3;
+  const int32_t nw;
+  __device__ explicit ProgressPriority(int32_t nw_) : next(nw_ >> 1), nw(nw_) {
+    __builtin_amdgcn_s_setprio(3);
+  }
+  __device__ __forceinline__ void step(int32_t n) {  // before window n
+    if (n == next && level > 0) {
+      --level;
+      if (level == 2) __builtin_amdgcn_s_setprio(2);
+      else if (level == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+      next = nw - (nw >> (4 - level));  // 3/4, then 7/8 of the windows
+    }
+  }
+};
 
 template <int CLS, int W>
 struct RingLoader {
@@ -731,12 +781,25 @@ struct RingLoader {
   const int lane, lr, lb, wave;
   const uint32_t ring;  // LDS byte address of the ring
   const uint8_t *lds;   // the same, as a pointer
+  const uint32_t idr;   // LDS byte address of this wave's page-id ring (kIdSlots x 2 ids)
+  const int32_t *lds_idr;
+  uint32_t voff[3];     // per-lane source offsets of this class's copies (within a block)
   uint32_t errs = 0;
 
-  __device__ RingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_, int wave_)
+  __device__ RingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_, int32_t *idr_, int wave_)
       : sp(s_), crow((cints)(a.tables + (int64_t)s_.table * a.max_entries)), pages(a, s_.head),
         e_last((s_.tok_end - 1) >> 4), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4), wave(wave_),
-        ring((uint32_t)(uintptr_t)ring_), lds(ring_) {}
+        ring((uint32_t)(uintptr_t)ring_), lds(ring_), idr((uint32_t)(uintptr_t)idr_), lds_idr(idr_) {
+    if (CLS == KVQ_INT4) {
+      voff[0] = kI4KC + lr * 64 + lb * 16;                                 // K codes, reader-lane order
+      voff[1] = kI4VC + lane * 16;                                         // V codes, natural
+      voff[2] = (lane & 15) * 16 + ((lane >> 4) & 1 ? kI4VM : kI4KM);     // K meta | V meta
+    } else {
+      voff[0] = lane * 16;                                                 // bytes 0 .. 1023
+      voff[1] = 1024 + (lane & 31) * 16;                                   // bytes 1024 .. 1535
+      voff[2] = 0;
+    }
+  }
 
   // Page-table entry of page half h of window T (T is never before the split's first
   // page; past its last page the last entry is repeated).
@@ -744,32 +807,45 @@ struct RingLoader {
     return crow[(uint32_t)__builtin_amdgcn_readfirstlane(min((T >> 4) + h, e_last))];
   }
 
-  // Source of chunk c of a window whose page halves live in blocks b0, b1.
-  __device__ __forceinline__ gbytes chunk_src(int c, gbytes b0, gbytes b1) const {
-    const gbytes mb = (lane >> 4) & 1 ? b1 : b0;  // meta chunk: 4 x 256 B pieces
+  // Copies the two entries of window T into id slot `slot` (lanes 0, 1), clamped the
+  // same way as entry().
+  __device__ __forceinline__ void issue_ids(int32_t T, int slot) const {
+    const int32_t e = min((T >> 4) + (lane & 1), e_last);
+    dma_pair(idr + 8u * (uint32_t)slot, (gbytes)crow, 4u * (uint32_t)e, lane);
+  }
+  // The two entries of id slot `slot` (its copy has landed).
+  __device__ __forceinline__ void ids(int slot, int32_t &id0, int32_t &id1) const {
+    const int2 v = *reinterpret_cast<const int2 *>(lds_idr + 2 * slot);
+    id0 = __builtin_amdgcn_readfirstlane(v.x);
+    id1 = __builtin_amdgcn_readfirstlane(v.y);
+  }
+
+  // Copy c of a window whose page halves live in blocks b0, b1 (LDS slot layout in
+  // read()); a window past the split's end copies one 16-byte line to every lane.
+  __device__ __forceinline__ void copy(int c, uint32_t base, gbytes b0, gbytes b1, bool real) const {
+    const uint32_t zero = 0u;
     if (CLS == KVQ_INT4) {
-      // K codes in reader-lane order (lane L reads 16 B at 16 L), V codes natural.
       switch (c) {
-        case 0: return b0 + kI4KC + lr * 64 + lb * 16;
-        case 1: return b1 + kI4KC + lr * 64 + lb * 16;
-        case 2: return b0 + kI4VC + lane * 16;
-        case 3: return b1 + kI4VC + lane * 16;
-        default: return mb + (lane < 32 ? kI4KM : kI4VM) + (lane & 15) * 16;
+        case 0: dma_block(base, real ? b0 : pages.base, real ? voff[0] : zero); break;
+        case 1: dma_block(base + 1024, real ? b1 : pages.base, real ? voff[0] : zero); break;
+        case 2: dma_block(base + 2048, real ? b0 : pages.base, real ? voff[1] : zero); break;
+        case 3: dma_block(base + 3072, real ? b1 : pages.base, real ? voff[1] : zero); break;
+        case 4: if (lane < 32) dma_block(base + 4096, real ? b0 : pages.base, real ? voff[2] : zero); break;
+        default: if (lane >= 32) dma_block(base + 4096, real ? b1 : pages.base, real ? voff[2] : zero); break;
       }
     } else {
-      const gbytes hb = lane < 32 ? b0 : b1;  // K / V codes: 512 B per page, natural
       switch (c) {
-        case 0: return hb + kI2KC + (lane & 31) * 16;
-        case 1: return hb + kI2VC + (lane & 31) * 16;
-        default: return mb + (lane < 32 ? kI2KS : kI2VM) + (lane & 15) * 16;
+        case 0: dma_block(base, real ? b0 : pages.base, real ? voff[0] : zero); break;
+        case 1: dma_block(base + 1024, real ? b1 : pages.base, real ? voff[0] : zero); break;
+        case 2: if (lane < 32) dma_block(base + 2048, real ? b0 : pages.base, real ? voff[1] : zero); break;
+        default: if (lane >= 32) dma_block(base + 2048, real ? b1 : pages.base, real ? voff[1] : zero); break;
       }
     }
   }
 
-  // Copies this wave's chunks of window T (page ids id0, id1 of its two halves) into
-  // slot `slot`; returns the window's page-half validity bits.  A window past the
-  // split's end (`real` false) copies one 16-byte line to every lane, so the copy
-  // count per window stays fixed.
+  // Copies this wave's share of window T (page ids id0, id1 of its two halves) into
+  // slot `slot`; returns the window's page-half validity bits.  The copy count per
+  // window is fixed.
   __device__ __forceinline__ uint32_t issue(int32_t id0, int32_t id1, bool real, int slot) {
     const uint32_t r0 = pages.rel(id0), r1 = pages.rel(id1);
     const bool ok0 = r0 < pages.count, ok1 = r1 < pages.count;
@@ -779,16 +855,17 @@ struct RingLoader {
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // this wave's reads of the slot are done
 #pragma unroll
     for (int c = 0; c < G::kChunks; ++c)
-      if (c % W == wave) dma_chunk(base + 1024 * c, real ? chunk_src(c, b0, b1) : pages.base);
+      if (c % W == wave) copy(c, base, b0, b1, real);
     return real ? (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u) : 0u;
   }
 
-  // Waits for this wave's copies of the window kAhead windows back.
+  // Waits for this wave's copies of the oldest window in flight (kAhead windows are,
+  // each followed by one id copy).
   __device__ __forceinline__ void wait() const {
-    if (W == 1 || wave == 0) wait_copies<kAhead * G::chunks_of(0)>();
-    else if (wave == 1) wait_copies<kAhead * G::chunks_of(1)>();
-    else if (wave == 2) wait_copies<kAhead * G::chunks_of(2)>();
-    else wait_copies<kAhead * G::chunks_of(3)>();
+    if (W == 1 || wave == 0) wait_copies<(kAhead - 1) * (G::chunks_of(0) + 1)>();
+    else if (wave == 1) wait_copies<(kAhead - 1) * (G::chunks_of(1) + 1)>();
+    else if (wave == 2) wait_copies<(kAhead - 1) * (G::chunks_of(2) + 1)>();
+    else wait_copies<(kAhead - 1) * (G::chunks_of(3) + 1)>();
   }
 
   // Reads window T from slot `slot` into the register window of the compute.
@@ -797,35 +874,38 @@ struct RingLoader {
     w.ok = ok;
     const int o0 = 8 * (lb & 1);
     if (CLS == KVQ_INT4) {
+      // [K codes A][K codes B][V codes A][V codes B][K meta A, V meta A][K meta B, V meta B]
       const uint8_t *M = S + 4096;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         w.k[h][0] = *reinterpret_cast<const uint4 *>(S + 1024 * h + 16 * lane);
-        w.km[h] = *reinterpret_cast<const uint4 *>(M + 256 * h + 16 * lr);
+        w.km[h] = *reinterpret_cast<const uint4 *>(M + 512 * h + 16 * lr);
       }
       const uint8_t *V = S + 2048 + 1024 * (lb >> 1) + 64 * o0 + 4 * lr;
 #pragma unroll
       for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 64 * q);
-      const uint8_t *VM = M + 512 + 256 * (lb >> 1) + ((lr & 3) * kPage + o0) * 4;
+      const uint8_t *VM = M + 512 * (lb >> 1) + 256 + ((lr & 3) * kPage + o0) * 4;
       w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
       w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
     } else {
-      const uint8_t *M = S + 2048;
+      // Page P's bytes 0 .. 1023 at 1024 P, its bytes 1024 .. 1535 at 2048 + 512 P.
+      auto at = [S](int P, int byte) { return byte < 1024 ? S + 1024 * P + byte : S + 2048 + 512 * P + (byte - 1024); };
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(S + 512 * h + 32 * lr + 8 * lb);
+        const uint2 x = *reinterpret_cast<const uint2 *>(S + 1024 * h + kI2KC + 32 * lr + 8 * lb);
         w.k[h][0] = make_uint4(x.x, x.y, 0, 0);
       }
-      const uint8_t *KS = M + 256 * (lr >> 3) + 16 * (lr & 7);  // scales; zeros 128 B on
+      const uint8_t *KS = S + 1024 * (lr >> 3) + kI2KS + 16 * (lr & 7);  // scales; zeros 128 B on
       w.ks = *reinterpret_cast<const uint4 *>(KS);
       w.kz = *reinterpret_cast<const uint4 *>(KS + (kI2KZ - kI2KS));
-      const uint8_t *KG = M + 256 * (lb >> 1) + 64 * (lb & 1);
+      const uint8_t *KG = S + 1024 * (lb >> 1) + kI2KS + 64 * (lb & 1);
 #pragma unroll
       for (int m = 0; m < 4; ++m) w.kg[m] = *reinterpret_cast<const uint4 *>(KG + 16 * m);
-      const uint8_t *V = S + 1024 + 512 * (lb >> 1) + 32 * o0 + 4 * (lr >> 1);
+      // V codes of tokens o0 .. o0 + 7: tokens 0-7 sit in the first KB, 8-15 after it
+      const uint8_t *V = at(lb >> 1, kI2VC + 32 * o0) + 4 * (lr >> 1);
 #pragma unroll
       for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 32 * q);
-      const uint8_t *VM = M + 512 + 256 * (lb >> 1) + ((lr & 3) * kPage + o0) * 4;
+      const uint8_t *VM = at(lb >> 1, kI2VM) + ((lr & 3) * kPage + o0) * 4;
       w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
       w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
     }
@@ -834,40 +914,48 @@ struct RingLoader {
 
 template <int CLS, int W, int QT>
 __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L, uint8_t *ring,
-                               int wave) {
+                               int32_t *idr, int wave) {
   using G = RingGeom<CLS, W>;
   constexpr int A = G::kAhead;
-  RingLoader<CLS, W> ld(a, sp, ring, wave);
+  RingLoader<CLS, W> ld(a, sp, ring, idr, wave);
   SplitRun<QT, CLS, false> R(a, sp, L);
   R.qbase = 4 * QT * wave;
   const int32_t T0 = sp.tok_begin & ~15;  // INT2 splits start on 32-token pairs
   const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
-  // Window i is copied into slot i mod kSlots, A windows ahead of its compute.
+  // Window i is copied into slot i mod kSlots, A windows ahead of its compute; the page
+  // ids of window i are copied into id slot i mod kIdSlots another A windows earlier
+  // (before the copies of window i - A, so they have landed when those have).
+  constexpr int kIdSlots = 8;
+  static_assert(A < kIdSlots, "id ring too small");
   uint32_t okq = 0;  // validity bits of the windows in flight, 2 per window, newest lowest
-  int32_t id0 = ld.entry(T0, 0), id1 = ld.entry(T0, 1);
 #pragma unroll
   for (int i = 0; i < A; ++i) {
     const int32_t Ti = T0 + 32 * i;
-    const int32_t n0 = ld.entry(Ti + 32, 0), n1 = ld.entry(Ti + 32, 1);
-    okq = (okq << 2) | ld.issue(id0, id1, i < nw, i);
-    id0 = n0;
-    id1 = n1;
+    ld.issue_ids(Ti + 32 * A, i + A);
+    okq = (okq << 2) | ld.issue(ld.entry(Ti, 0), ld.entry(Ti, 1), i < nw, i);
   }
-  int slot_c = 0, slot_i = A;  // slots of the window computed and of the window copied
+  int slot_c = 0, slot_i = A == G::kSlots ? 0 : A;  // slots of the window computed and of the next copy
+  int id_slot = A;                                   // id slot of window n + A
+  ProgressPriority prio(nw);
   for (int32_t n = 0; n < nw; ++n) {
-    const int32_t Ti = T0 + 32 * (n + A);
-    const int32_t n0 = ld.entry(Ti + 32, 0), n1 = ld.entry(Ti + 32, 1);  // ids one window early
-    okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
-    id0 = n0;
-    id1 = n1;
+    if (W == 1) prio.step(n);  // (the waves of one block move in step anyway)
     ld.wait();
-    if (W > 1) __syncthreads();  // every wave's chunks of window n have landed
+    if (W > 1) __syncthreads();  // every wave's chunks of window n have landed, window n - 1 is read
+    const uint32_t ok = (okq >> (2 * (A - 1))) & 3u;
+    const int32_t Tn = T0 + 32 * (n + A);
+    int32_t id0, id1;
+    ld.ids(id_slot, id0, id1);  // window n + A
     Win w;
     const int32_t T = T0 + 32 * n;
-    ld.read(T, slot_c, (okq >> (2 * A)) & 3u, w);
+    if (W == 1) ld.read(T, slot_c, ok, w);  // the slot is refilled below
+    // issue() waits for this wave's LDS reads before its copies
+    ld.issue_ids(Tn + 32 * A, (id_slot + A) & (kIdSlots - 1));
+    okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
+    if (W > 1) ld.read(T, slot_c, ok, w);
     R.window(w, T);
     slot_c = slot_c + 1 == G::kSlots ? 0 : slot_c + 1;
     slot_i = slot_i + 1 == G::kSlots ? 0 : slot_i + 1;
+    id_slot = (id_slot + 1) & (kIdSlots - 1);
   }
   wait_copies<0>();  // no copy outlives the wave
   if (ld.errs) report(a.err, (int32_t)ld.errs);
@@ -988,7 +1076,9 @@ __device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, i
   ld.issue_ids(T0 + 32, 1);
   wait_copies<1>();
   uint32_t mask_next = ld.issue_data(T0, 0, true, 0);
+  ProgressPriority prio(nw);
   for (int32_t n = 0; n < nw; ++n) {
+    prio.step(n);
     ld.issue_ids(T0 + 32 * (n + 2), (n + 2) & 3);
     wait_copies<C>();  // the ids of window n + 1
     const uint32_t mask = mask_next;
@@ -1072,12 +1162,13 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(QT 
 decode_ring_kernel(DecodeArgs a) {
   __shared__ Lds<QT> L[W];
   __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes<W>()];
+  __shared__ __attribute__((aligned(16))) int32_t idr[W][16];
   const int s_idx = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   kvq_split sp;
   if (!split_prologue<QT, false, true>(a, s_idx, sp, L[wave], 4 * QT * wave)) return;
-  if (sp.cls == KVQ_INT4) run_split_ring<KVQ_INT4, W, QT>(a, sp, s_idx, L[wave], ring, wave);
-  else if (sp.cls == KVQ_INT2) run_split_ring<KVQ_INT2, W, QT>(a, sp, s_idx, L[wave], ring, wave);
+  if (sp.cls == KVQ_INT4) run_split_ring<KVQ_INT4, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
+  else if (sp.cls == KVQ_INT2) run_split_ring<KVQ_INT2, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
 }
 
 // LDS-staged kernel for slot maps (INT4 splits, g <= 8).
