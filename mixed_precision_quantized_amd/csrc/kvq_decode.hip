@@ -358,7 +358,7 @@ struct SplitRun {
   h8 Aq[QT][4];        // block-diagonal query operand
   h2 qn[QT][4];        // natural-order q pairs: query 4 qt + lb, channels 8 lr .. 8 lr + 7
   float qsum[QT][4];   // per-group sum of q of query 4 qt + lb (INT4 zero term)
-  float qoff[QT][4];   // per-group sum of q x code offset (1024 / 64) of query 4 qt + lb
+  f4 qoff[QT];         // minus the per-group sum of q x code offset (1024 / 64) of query 4 qt + lb
   f4 acc[QT][8];       // P V accumulators
   float m_run[QT], l_run[QT];
   int qbase = 0;       // first query head (of the g) this wave computes
@@ -396,7 +396,7 @@ struct SplitRun {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         qsum[qt][r] = __shfl(ps, 16 * lb + 4 * r);
-        qoff[qt][r] = __shfl(po, 16 * lb + 4 * r);
+        qoff[qt][r] = -__shfl(po, 16 * lb + 4 * r);
       }
       m_run[qt] = kNegBig;
       l_run[qt] = 0.0f;
@@ -477,7 +477,8 @@ struct SplitRun {
       const bool tok_live = live >> h & 1;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        f4 d = f4{0.f, 0.f, 0.f, 0.f};
+        // INT4: the accumulators start at minus the offsets' share of the dot products
+        f4 d = CLS == KVQ_INT4 ? qoff[qt] : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) d = mfma(Aq[qt][m], kb[m], d);
         float s;
@@ -486,7 +487,7 @@ struct SplitRun {
           s = 0.0f;
 #pragma unroll
           for (int r = 0; r < 4; ++r)  // s (q . (offset + c) - q . offset) + z sum(q)
-            s = fmaf(h2f(mm[r]), d[r] - qoff[qt][r], fmaf(h2f(mm[r] >> 16), qsum[qt][r], s));
+            s = fmaf(h2f(mm[r]), d[r], fmaf(h2f(mm[r] >> 16), qsum[qt][r], s));
         } else if (CLS == KVQ_INT2) {
           s = ((d[0] + d[1]) + (d[2] + d[3])) + c2[qt];
         } else {
@@ -748,6 +749,9 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+template <int QT>
+__device__ void stage_q(const DecodeArgs &a, const kvq_split &sp, Lds<QT> &L, int q_first);
+
 // Issue priority by progress.  A SIMD's waves issue oldest first among equal
 // priorities, so waves given equal work would finish one after another and leave the
 // SIMD to a single wave at the end.  A wave lowers its priority when half, three
@@ -918,8 +922,6 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
   using G = RingGeom<CLS, W>;
   constexpr int A = G::kAhead;
   RingLoader<CLS, W> ld(a, sp, ring, idr, wave);
-  SplitRun<QT, CLS, false> R(a, sp, L);
-  R.qbase = 4 * QT * wave;
   const int32_t T0 = sp.tok_begin & ~15;  // INT2 splits start on 32-token pairs
   const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
   // Window i is copied into slot i mod kSlots, A windows ahead of its compute; the page
@@ -934,6 +936,10 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
     ld.issue_ids(Ti + 32 * A, i + A);
     okq = (okq << 2) | ld.issue(ld.entry(Ti, 0), ld.entry(Ti, 1), i < nw, i);
   }
+  // The queries are fetched while the first windows are on their way.
+  stage_q<QT>(a, sp, L, 4 * QT * wave);
+  SplitRun<QT, CLS, false> R(a, sp, L);
+  R.qbase = 4 * QT * wave;
   int slot_c = 0, slot_i = A == G::kSlots ? 0 : A;  // slots of the window computed and of the next copy
   int id_slot = A;                                   // id slot of window n + A
   ProgressPriority prio(nw);
@@ -1095,11 +1101,9 @@ __device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, i
 
 // Checks split s_idx.  A split this launch does not own returns false at once; an
 // owned split that is malformed or empty (or of a class with no pages) gets O = 0,
-// lse = -inf (and an error bit when malformed) and returns false.  Otherwise stages
-// the split's query heads q_first .. q_first + 4 QT - 1, unscaled, in LDS rows
-// 0 .. 4 QT - 1 (rows past g zero).  Every wave of the work group calls it alike.
+// lse = -inf (and an error bit when malformed) and returns false.
 template <int QT, bool SLOTS, bool RING>
-__device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Lds<QT> &L, int q_first = 0) {
+__device__ bool split_check(const DecodeArgs &a, int s_idx, kvq_split &sp, int q_first = 0) {
   const int lane = lane_id();
   sp = a.splits[s_idx];
   const int64_t cap = SLOTS ? (int64_t)a.max_entries : (int64_t)a.max_entries * kPage;
@@ -1122,6 +1126,14 @@ __device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Ld
     }
     return false;
   }
+  return true;
+}
+
+// Stages the split's query heads q_first .. q_first + 4 QT - 1, unscaled, in LDS rows
+// 0 .. 4 QT - 1 (rows past g zero).  Every wave of the work group calls it alike.
+template <int QT>
+__device__ void stage_q(const DecodeArgs &a, const kvq_split &sp, Lds<QT> &L, int q_first) {
+  const int lane = lane_id();
   const int b = sp.table / a.tpr;
   const int kvh = (sp.table % a.tpr) * a.heads + sp.head;
   for (int j = 0; j < 4 * QT; ++j)
@@ -1139,6 +1151,12 @@ __device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Ld
       L.q[j][c] = v;
     }
   __syncthreads();
+}
+
+template <int QT, bool SLOTS, bool RING>
+__device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Lds<QT> &L, int q_first = 0) {
+  if (!split_check<QT, SLOTS, RING>(a, s_idx, sp, q_first)) return false;
+  stage_q<QT>(a, sp, L, q_first);
   return true;
 }
 
@@ -1166,7 +1184,7 @@ decode_ring_kernel(DecodeArgs a) {
   const int s_idx = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   kvq_split sp;
-  if (!split_prologue<QT, false, true>(a, s_idx, sp, L[wave], 4 * QT * wave)) return;
+  if (!split_check<QT, false, true>(a, s_idx, sp, 4 * QT * wave)) return;
   if (sp.cls == KVQ_INT4) run_split_ring<KVQ_INT4, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
   else if (sp.cls == KVQ_INT2) run_split_ring<KVQ_INT2, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
 }
