@@ -407,8 +407,14 @@ struct SplitRun {
     }
   }
 
-  // 32 tokens starting at T, from the loaded window `w`.
   __device__ __forceinline__ void window(const Win &w, int32_t T) {
+    window(w, T, [] {});
+  }
+
+  // 32 tokens starting at T, from the loaded window `w`; `mid()` runs once the
+  // window's words have all been used (before the softmax).
+  template <typename F>
+  __device__ __forceinline__ void window(const Win &w, int32_t T, F &&mid) {
     const bool partial = (T < sp.tok_begin) || (T + 32 > sp.tok_end) || w.ok != 3u;  // (slot maps: ok = 0)
     // live bit h: QK token T + 16 h + lr counts; vlive bit q: P V token T + 8 lb + q counts.
     uint32_t live = 3u, vlive = 0xFFu;
@@ -552,6 +558,8 @@ struct SplitRun {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) vb[nt] = h8_of(t[nt][0], t[nt][1], t[nt][2], t[nt][3]);
     }
+    mid();
+
     // Online softmax per query (the 16 lanes of row lb).
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -953,12 +961,19 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
     ld.ids(id_slot, id0, id1);  // window n + A
     Win w;
     const int32_t T = T0 + 32 * n;
-    if (W == 1) ld.read(T, slot_c, ok, w);  // the slot is refilled below
-    // issue() waits for this wave's LDS reads before its copies
-    ld.issue_ids(Tn + 32 * A, (id_slot + A) & (kIdSlots - 1));
-    okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
-    if (W > 1) ld.read(T, slot_c, ok, w);
-    R.window(w, T);
+    const int id_next = (id_slot + A) & (kIdSlots - 1);
+    if (W > 1) {  // into window n - 1's slot
+      ld.issue_ids(Tn + 32 * A, id_next);
+      okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
+      ld.read(T, slot_c, ok, w);
+      R.window(w, T);
+    } else {  // into this window's slot, once its words are used (issue() waits for the LDS reads)
+      ld.read(T, slot_c, ok, w);
+      R.window(w, T, [&] {
+        ld.issue_ids(Tn + 32 * A, id_next);
+        okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
+      });
+    }
     slot_c = slot_c + 1 == G::kSlots ? 0 : slot_c + 1;
     slot_i = slot_i + 1 == G::kSlots ? 0 : slot_i + 1;
     id_slot = (id_slot + 1) & (kIdSlots - 1);
