@@ -832,43 +832,50 @@ struct RingLoader {
     id1 = __builtin_amdgcn_readfirstlane(v.y);
   }
 
-  // Copy c of a window whose page halves live in blocks b0, b1 (LDS slot layout in
-  // read()); a window past the split's end copies one 16-byte line to every lane.
-  __device__ __forceinline__ void copy(int c, uint32_t base, gbytes b0, gbytes b1, bool real) const {
-    const uint32_t zero = 0u;
+  // Copy c of a window whose page halves live in blocks b0, b1, with per-lane source
+  // offsets voff (LDS slot layout in read()).
+  __device__ __forceinline__ void copy(int c, uint32_t base, gbytes b0, gbytes b1, const uint32_t (&vo)[3]) const {
     if (CLS == KVQ_INT4) {
       switch (c) {
-        case 0: dma_block(base, real ? b0 : pages.base, real ? voff[0] : zero); break;
-        case 1: dma_block(base + 1024, real ? b1 : pages.base, real ? voff[0] : zero); break;
-        case 2: dma_block(base + 2048, real ? b0 : pages.base, real ? voff[1] : zero); break;
-        case 3: dma_block(base + 3072, real ? b1 : pages.base, real ? voff[1] : zero); break;
-        case 4: if (lane < 32) dma_block(base + 4096, real ? b0 : pages.base, real ? voff[2] : zero); break;
-        default: if (lane >= 32) dma_block(base + 4096, real ? b1 : pages.base, real ? voff[2] : zero); break;
+        case 0: dma_block(base, b0, vo[0]); break;
+        case 1: dma_block(base + 1024, b1, vo[0]); break;
+        case 2: dma_block(base + 2048, b0, vo[1]); break;
+        case 3: dma_block(base + 3072, b1, vo[1]); break;
+        case 4: if (lane < 32) dma_block(base + 4096, b0, vo[2]); break;
+        default: if (lane >= 32) dma_block(base + 4096, b1, vo[2]); break;
       }
     } else {
       switch (c) {
-        case 0: dma_block(base, real ? b0 : pages.base, real ? voff[0] : zero); break;
-        case 1: dma_block(base + 1024, real ? b1 : pages.base, real ? voff[0] : zero); break;
-        case 2: if (lane < 32) dma_block(base + 2048, real ? b0 : pages.base, real ? voff[1] : zero); break;
-        default: if (lane >= 32) dma_block(base + 2048, real ? b1 : pages.base, real ? voff[1] : zero); break;
+        case 0: dma_block(base, b0, vo[0]); break;
+        case 1: dma_block(base + 1024, b1, vo[0]); break;
+        case 2: if (lane < 32) dma_block(base + 2048, b0, vo[1]); break;
+        default: if (lane >= 32) dma_block(base + 2048, b1, vo[1]); break;
       }
     }
   }
 
   // Copies this wave's share of window T (page ids id0, id1 of its two halves) into
   // slot `slot`; returns the window's page-half validity bits.  The copy count per
-  // window is fixed.
+  // window is fixed: a window past the split's end copies the class's first 16-byte
+  // line to every lane.
   __device__ __forceinline__ uint32_t issue(int32_t id0, int32_t id1, bool real, int slot) {
-    const uint32_t r0 = pages.rel(id0), r1 = pages.rel(id1);
-    const bool ok0 = r0 < pages.count, ok1 = r1 < pages.count;
-    if (real && !(ok0 && ok1)) errs |= KVQ_DEVERR_ID;
-    const gbytes b0 = pages.block(ok0 ? r0 : 0u), b1 = pages.block(ok1 ? r1 : 0u);
     const uint32_t base = ring + (uint32_t)slot * G::kSlotBytes;
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // this wave's reads of the slot are done
+    if (real) {
+      const uint32_t r0 = pages.rel(id0), r1 = pages.rel(id1);
+      const bool ok0 = r0 < pages.count, ok1 = r1 < pages.count;
+      const gbytes b0 = pages.block(ok0 ? r0 : 0u), b1 = pages.block(ok1 ? r1 : 0u);
+#pragma unroll
+      for (int c = 0; c < G::kChunks; ++c)
+        if (c % W == wave) copy(c, base, b0, b1, voff);
+      if (!(ok0 && ok1)) errs |= KVQ_DEVERR_ID;
+      return (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u);
+    }
+    const uint32_t zero[3] = {0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < G::kChunks; ++c)
-      if (c % W == wave) copy(c, base, b0, b1, real);
-    return real ? (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u) : 0u;
+      if (c % W == wave) copy(c, base, pages.base, pages.base, zero);
+    return 0u;
   }
 
   // Waits for this wave's copies of the oldest window in flight (kAhead windows are,
