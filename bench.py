@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (reference for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from Python instead of replaying a captured HIP graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -200,20 +202,33 @@ def main():
     part_o = torch.empty((n_splits, g, 128), dtype=torch.float32, device=dev)
     part_lse = torch.empty((n_splits, g), dtype=torch.float32, device=dev)
     outs = [torch.empty((w0.batch, w0.hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
-    dec = [kvq.bind_decode_attn(caches[L], qs[L], w0.hkv, gpu.tables, kind, sp, part_o, part_lse)
-           for L in range(layers)]
-    mrg = [kvq.bind_lse_merge(part_o, part_lse, n_splits, off, w0.batch, w0.hq, w0.hkv, outs[L])
-           for L in range(layers)]
     torch.cuda.synchronize()
     assert int(gpu.err.item()) == 0, f"device error bits {int(gpu.err.item())}"
     log(f"setup {time.time() - t0:.1f}s: {layers} layers, {n_splits} splits per layer "
         f"({per_cu} resident per CU x {n_cu} CUs), "
         f"pools {sum(sum(p.numel() for p in c.pools) for c in caches) / 2**30:.1f} GiB")
 
+    # Every launch goes to `stream`: torch's current stream when eager, a side stream
+    # (default priority) for graph capture; events recorded on it bracket the kernels.
+    stream = torch.cuda.current_stream() if args.eager else torch.cuda.Stream()
+
+    def bound(st):
+        d = [kvq.bind_decode_attn(caches[L], qs[L], w0.hkv, gpu.tables, kind, sp, part_o, part_lse, stream=st)
+             for L in range(layers)]
+        m = [kvq.bind_lse_merge(part_o, part_lse, n_splits, off, w0.batch, w0.hq, w0.hkv, outs[L], stream=st)
+             for L in range(layers)]
+        return d, m
+
+    dec, mrg = bound(stream)
+
     def step():
         for L in range(layers):
             dec[L]()
             mrg[L]()
+
+    def decodes():
+        for L in range(layers):
+            dec[L]()
 
     if args.copy_calibration:
         # Known-size references for the HBM byte counters: 1 GiB read + 1 GiB written,
@@ -227,33 +242,59 @@ def main():
             del src, dst
         log("copy calibration: two 1 GiB device-to-device copies (uint8, float32)")
 
-    for _ in range(args.warmup):
-        step()
+    with torch.cuda.stream(stream):
+        step()  # first launches (code objects load) outside any capture
     torch.cuda.synchronize()
-    # Every launch goes to torch's current stream (the bound calls pass it), so events
-    # recorded there bracket exactly the kernels.  Inside the timed steps each decode
-    # launch is bracketed too, for the roofline of the dominant kernel.
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps * layers)]
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    run_step, run_decodes = step, decodes
+    if not args.eager:
+        # The step as one HIP graph (the 2 x layers launches, no allocation, no memset),
+        # and the decode launches alone for the kernel's own duration.  Each replay of
+        # the step is checked against the eager outputs, with eager work in between.
+        ref = torch.stack([o.float() for o in outs])
+        g_step, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step, stream=stream):
+            step()
+        with torch.cuda.graph(g_dec, stream=stream):
+            decodes()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for o in outs:
+                o.zero_()
+            g_step.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(torch.stack([o.float() for o in outs]), ref), "graph replay differs from eager"
+            with torch.cuda.stream(stream):
+                step()
+            torch.cuda.synchronize()
+        assert int(gpu.err.item()) == 0
+        run_step, run_decodes = g_step.replay, g_dec.replay
+        log("step captured as a HIP graph of the decode + merge launches; 3 replays equal to eager")
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            run_step()
     torch.cuda.synchronize()
-    e0.record(stream)
-    i = 0
-    for _ in range(args.steps):
-        for L in range(layers):
-            ev[i][0].record(stream)
-            dec[L]()
-            ev[i][1].record(stream)
-            mrg[L]()
-            i += 1
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    us_decode = sum(a.elapsed_time(b) for a, b in ev) * 1000 / len(ev)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps  # seconds per rep
+
+    # The timed steps: K steps back to back between two events, nothing in between.
+    ms_step = timed(run_step, args.steps) * 1e3
+    # The dominant kernel alone: the layers' decode launches back to back, K times;
+    # the average launch duration is the span over the number of launches.
+    us_decode = timed(run_decodes, args.steps) * 1e6 / layers
     achieved = decode_bytes / (us_decode * 1e-6) / 1e9
     log(f"step {ms_step * 1000:.1f} us ({ms_step * 1000 / layers:.1f} us per layer)")
-    log(f"decode kernel {us_decode:.1f} us per launch, {achieved:.0f} GB/s algorithmic")
+    log(f"decode kernel {us_decode:.1f} us per launch ({layers} x {args.steps} back-to-back launches), "
+        f"{achieved:.0f} GB/s algorithmic")
     assert int(gpu.err.item()) == 0
 
     gbs = eff_layer * layers / (ms_step * 1e-3) / 1e9

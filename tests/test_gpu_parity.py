@@ -271,3 +271,48 @@ def test_full_size_qwen3_8b_sampled():
                 gb = gpu.cache.pool_bytes(cls)[base_g: base_g + bb].cpu().numpy()
                 ob = orc.cache.pool_bytes(cls)[base_o: base_o + bb]
                 assert np.array_equal(gb, ob), (b, e)
+
+
+def test_graph_replay_matches_eager():
+    """Decode + merge captured as one HIP graph (as the benchmark replays it): three
+    replays, each after eager launches and a synchronization, equal the eager result
+    bit for bit and the oracle within the tolerance."""
+    w = synth.qwen3_8b(batch=2, n_tokens=2048)
+    gpu = GpuRun(w, reorder=True)
+    orc = OracleRun(synth.qwen3_8b(batch=2, n_tokens=2048), reorder=True)
+    ref, _ = orc.attend()
+    kvq = gpu.kvq
+    splits, offsets = gpu.plan(target_bytes=1 << 16)
+    n = splits.shape[0]
+    sp = torch.as_tensor(splits, device="cuda").contiguous()
+    off = torch.as_tensor(offsets, device="cuda")
+    part_o = torch.empty((n, w.g, 128), dtype=torch.float32, device="cuda")
+    part_lse = torch.empty((n, w.g), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.batch, w.hq, 128), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def bind():
+        d = kvq.bind_decode_attn(gpu.cache, gpu.q, w.hkv, gpu.tables, kvq.TABLE_PAGES, sp, part_o, part_lse,
+                                 dev_err=gpu.err, stream=stream)
+        m = kvq.bind_lse_merge(part_o, part_lse, n, off, w.batch, w.hq, w.hkv, out, stream=stream)
+        return lambda: (d(), m())
+
+    run = bind()
+    with torch.cuda.stream(stream):
+        run()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert row_metric(ref, eager.cpu().numpy()) <= TOL
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager result"
+        with torch.cuda.stream(stream):
+            run()
+        torch.cuda.synchronize()
+    assert int(gpu.err.item()) == 0
