@@ -480,7 +480,6 @@ struct SplitRun {
 #pragma unroll
         for (int m = 0; m < 4; ++m) kb[m] = h8_of(w.k[h][m]);
       }
-      const bool tok_live = live >> h & 1;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         // INT4: the accumulators start at minus the offsets' share of the dot products
@@ -499,8 +498,14 @@ struct SplitRun {
         } else {
           s = (d[0] + d[1]) + (d[2] + d[3]);
         }
-        x[qt][h] = tok_live ? s * scale : -INFINITY;
+        x[qt][h] = s * scale;
       }
+    }
+    if (partial) {  // tokens that do not count get logit -inf (weight 0)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) x[qt][h] = (live >> h & 1) ? x[qt][h] : -INFINITY;
     }
 
     // V operand: this lane's channels 8 lr + nt, its 8 tokens as 4 pairs.
@@ -955,10 +960,12 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
   stage_q<QT>(a, sp, L, 4 * QT * wave);
   SplitRun<QT, CLS, false> R(a, sp, L);
   R.qbase = 4 * QT * wave;
-  int slot_c = 0, slot_i = A == G::kSlots ? 0 : A;  // slots of the window computed and of the next copy
-  int id_slot = A;                                   // id slot of window n + A
+  int id_slot = A;  // id slot of window n + A
   ProgressPriority prio(nw);
-  for (int32_t n = 0; n < nw; ++n) {
+  // Window n: wait for its copies, read it, compute it; the copies of window n + A go
+  // into window n - 1's slot (several waves) or into window n's own slot once its
+  // words are used (one wave).
+  auto step = [&](int32_t n, int slot_c, int slot_i) {
     if (W == 1) prio.step(n);  // (the waves of one block move in step anyway)
     ld.wait();
     if (W > 1) __syncthreads();  // every wave's chunks of window n have landed, window n - 1 is read
@@ -969,21 +976,34 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
     Win w;
     const int32_t T = T0 + 32 * n;
     const int id_next = (id_slot + A) & (kIdSlots - 1);
-    if (W > 1) {  // into window n - 1's slot
+    if (W > 1) {
       ld.issue_ids(Tn + 32 * A, id_next);
       okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
       ld.read(T, slot_c, ok, w);
       R.window(w, T);
-    } else {  // into this window's slot, once its words are used (issue() waits for the LDS reads)
+    } else {  // (issue() waits for the LDS reads)
       ld.read(T, slot_c, ok, w);
       R.window(w, T, [&] {
         ld.issue_ids(Tn + 32 * A, id_next);
         okq = (okq << 2) | ld.issue(id0, id1, n + A < nw, slot_i);
       });
     }
-    slot_c = slot_c + 1 == G::kSlots ? 0 : slot_c + 1;
-    slot_i = slot_i + 1 == G::kSlots ? 0 : slot_i + 1;
     id_slot = (id_slot + 1) & (kIdSlots - 1);
+  };
+  if (W == 1) {
+    // Unrolled over the ring so that every slot address is a compile-time offset.
+    for (int32_t n0 = 0; n0 < nw; n0 += G::kSlots) {
+#pragma unroll
+      for (int k = 0; k < G::kSlots; ++k)
+        if (n0 + k < nw) step(n0 + k, k, k);
+    }
+  } else {
+    int slot_c = 0, slot_i = A;  // slots of the window computed and of the next copy
+    for (int32_t n = 0; n < nw; ++n) {
+      step(n, slot_c, slot_i);
+      slot_c = slot_c + 1 == G::kSlots ? 0 : slot_c + 1;
+      slot_i = slot_i + 1 == G::kSlots ? 0 : slot_i + 1;
+    }
   }
   wait_copies<0>();  // no copy outlives the wave
   if (ld.errs) report(a.err, (int32_t)ld.errs);
