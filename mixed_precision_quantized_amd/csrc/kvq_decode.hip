@@ -1246,10 +1246,11 @@ decode_slots_ring_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ merge -----
 
-// One wavefront per (request, query head); lane = channel pair.  The row's split lse
-// values are read 64 at a time (lane = split), their maximum and weights
-// exp(lse - max) computed across the wave, and the partial rows are loaded 16 at a
-// time before any is used, so a row costs about one memory latency per 16 splits.
+// One wavefront per (request, query head); lane = channel pair.  Splits come 32 at a
+// time: their lse values (lane = split) and partial rows are loaded together before any
+// is used, so a row costs about one memory latency per 32 splits after the offsets;
+// the maximum and the weights exp(lse - max) are formed across the wave and broadcast
+// with v_readlane.
 __global__ void __launch_bounds__(64) lse_merge_kernel(const float *part_o, const float *part_lse,
                                                        int32_t n_splits, const int32_t *offsets, int32_t hq,
                                                        int32_t hkv, void *out, int32_t out_dtype,
@@ -1260,40 +1261,42 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(const float *part_o, cons
   const int g = hq / hkv, kvh = qh / g, j = qh % g;
   const int32_t s0 = min(max(offsets[(int64_t)b * hkv + kvh], 0), n_splits);
   const int32_t s1 = min(max(offsets[(int64_t)b * hkv + kvh + 1], s0), n_splits);
-  float mx = -INFINITY;
-  for (int32_t base = s0; base < s1; base += 64) {
-    const int32_t s = base + lane;
-    if (s < s1) mx = fmaxf(mx, part_lse[(int64_t)s * g + j]);
-  }
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float o0 = 0.0f, o1 = 0.0f, lse = -INFINITY;
-  if (mx != -INFINITY) {
-    float tot = 0.0f;
-    for (int32_t base = s0; base < s1; base += 64) {
-      const int32_t s = base + lane;
-      const float w = s < s1 ? expf(part_lse[(int64_t)s * g + j] - mx) : 0.0f;  // lane k: split base + k
-      tot += w;
-      const int32_t n = min(s1 - base, 64);
-      for (int32_t k0 = 0; k0 < n; k0 += 16) {
-        float2 po[16];
+  // Up to 32 splits at a time: their lse values (lane = split) and partial rows are
+  // loaded together, then folded into a running (max, sum, row).
+  float m = -INFINITY, tot = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int32_t base = s0; base < s1; base += 32) {
+    const int32_t n = min(s1 - base, 32);
+    const float l = lane < n ? part_lse[(int64_t)(base + lane) * g + j] : -INFINITY;
+    float2 po[32];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int32_t kk = min(k0 + k, n - 1);  // past the end: a repeated row, weight 0
-          po[k] = *reinterpret_cast<const float2 *>(part_o + ((int64_t)(base + kk) * g + j) * kHeadDim + 2 * lane);
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const float wk = __shfl(w, k0 + k < n ? k0 + k : 63);  // lane 63's w is 0 unless n = 64
-          const float wk_valid = k0 + k < n ? wk : 0.0f;
-          o0 = fmaf(wk_valid, po[k].x, o0);
-          o1 = fmaf(wk_valid, po[k].y, o1);
-        }
-      }
+    for (int k = 0; k < 32; ++k) {
+      const int32_t kk = min(k, n - 1);  // past the end: a repeated row, weight 0
+      po[k] = *reinterpret_cast<const float2 *>(part_o + ((int64_t)(base + kk) * g + j) * kHeadDim + 2 * lane);
     }
-    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+    float mc = l;
+    for (int off = 32; off > 0; off >>= 1) mc = fmaxf(mc, __shfl_xor(mc, off));
+    const float mn = fmaxf(m, mc);
+    if (mn == -INFINITY) continue;  // every split so far is empty
+    const float r = expf(m - mn);   // 0 while m is -inf
+    const float w = expf(l - mn);   // lane k: split base + k (0 past the end)
+    float ws = w;
+    for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off);
+    tot = fmaf(tot, r, ws);
+    o0 *= r;
+    o1 *= r;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+      o0 = fmaf(wk, po[k].x, o0);
+      o1 = fmaf(wk, po[k].y, o1);
+    }
+    m = mn;
+  }
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
     o0 /= tot;
     o1 /= tot;
-    lse = mx + logf(tot);
+    lse = m + logf(tot);
   }
   const int64_t at = row * kHeadDim + 2 * lane;
   if (out_dtype == KVQ_F32) {
