@@ -8,8 +8,9 @@
 // denormals, so every operation rounds exactly as IEEE fp32 does.
 //
 // Work mapping: one 64-lane wavefront per (token, head) for per-token groups;
-// lane l owns channels 2l and 2l+1, so a 32-channel group is 16 adjacent lanes
-// and its min / max is a 4-step butterfly within those lanes.  One wavefront per
+// lane l owns channels 2l and 2l+1 (one load), so a 32-channel group is one 16-lane
+// DPP row and its min / max four row rotations; codes are packed into words across
+// 4 (INT4) or 8 (INT2) lanes by DPP as well.  One wavefront per
 // (INT2 group, head) for the per-channel INT2 K groups (each lane keeps its two
 // channels of all 32 tokens in registers).
 #include <hip/hip_fp16.h>
@@ -83,20 +84,40 @@ __device__ __forceinline__ uint32_t float_to_half_rne(float x) {
   return h == 0x8000u ? 0u : h;
 }
 
-__device__ __forceinline__ float load_src(const void *base, int32_t dtype, int64_t idx) {
-  if (dtype == KVQ_F32) return static_cast<const float *>(base)[idx];
-  const uint32_t h = static_cast<const uint16_t *>(base)[idx];
-  if (dtype == KVQ_BF16) return __uint_as_float(h << 16);
-  return half_bits_to_float(h);
+// Source values idx and idx + 1 (one lane's channel pair) in one load.
+__device__ __forceinline__ float2 load_pair(const void *base, int32_t dtype, int64_t idx) {
+  if (dtype == KVQ_F32) return *reinterpret_cast<const float2 *>(static_cast<const float *>(base) + idx);
+  const uint32_t h = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(base) + idx);
+  if (dtype == KVQ_BF16) return make_float2(__uint_as_float(h << 16), __uint_as_float(h & 0xffff0000u));
+  return make_float2(half_bits_to_float(h & 0xffffu), half_bits_to_float(h >> 16));
 }
 
-// Min and max over the 16 lanes of a group (lanes differing in bits 0..3).
+// DPP moves within a 16-lane row: rotation by N (every lane of the row gets the
+// rotated value), shift towards lower lanes by N (lanes past the row's end read 0),
+// and quad permutations.
+template <int N>
+__device__ __forceinline__ uint32_t row_ror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x120 + N, 0xf, 0xf, true);
+}
+template <int N>
+__device__ __forceinline__ uint32_t row_shl(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x100 + N, 0xf, 0xf, true);
+}
+template <int P>
+__device__ __forceinline__ uint32_t quad_perm(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, P, 0xf, 0xf, true);
+}
+
+// Min and max over the 16 lanes of a group (one DPP row); every lane gets both.
 __device__ __forceinline__ void group16_minmax(float &mn, float &mx) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, m));
-    mx = fmaxf(mx, __shfl_xor(mx, m));
-  }
+#define KVQ_STEP(N)                                                   \
+  mn = fminf(mn, __uint_as_float(row_ror<N>(__float_as_uint(mn)))); \
+  mx = fmaxf(mx, __uint_as_float(row_ror<N>(__float_as_uint(mx))));
+  KVQ_STEP(8)
+  KVQ_STEP(4)
+  KVQ_STEP(2)
+  KVQ_STEP(1)
+#undef KVQ_STEP
 }
 
 struct Quant {
@@ -149,8 +170,9 @@ __device__ __forceinline__ void put_code_pair(uint8_t *row, uint32_t c0, uint32_
   constexpr int kLanesPerWord = 16 / BITS;
   const int k = lane % kLanesPerWord;
   uint32_t w = (c0 << (k * BITS)) | (c1 << (16 + k * BITS));
-#pragma unroll
-  for (int m = 1; m < kLanesPerWord; m <<= 1) w |= (uint32_t)__shfl_xor((int)w, m);
+  w |= quad_perm<0xB1>(w);  // lane ^ 1
+  w |= quad_perm<0x4E>(w);  // lane ^ 2: each quad holds its 4 lanes' bits
+  if (kLanesPerWord == 8) w |= row_shl<4>(w);  // the first lane of 8 adds the next quad's
   if (k == 0) *reinterpret_cast<uint32_t *>(row + (lane / kLanesPerWord) * 4) = w;
 }
 
@@ -195,8 +217,8 @@ __global__ void __launch_bounds__(256) append_tokens_kernel(
     return;
   }
   const int64_t src = (int64_t)row * row_stride + (int64_t)head * head_stride + 2 * lane;
-  const float k0 = load_src(k, dtype, src), k1 = load_src(k, dtype, src + 1);
-  const float v0 = load_src(v, dtype, src), v1 = load_src(v, dtype, src + 1);
+  const float2 kp = load_pair(k, dtype, src), vp = load_pair(v, dtype, src);
+  const float k0 = kp.x, k1 = kp.y, v0 = vp.x, v1 = vp.y;
   if (is4) {
     uint8_t *blk = c.pool4 + ((page - c.n2) * c.heads + head) * (int64_t)kI4Bytes;
     put_token_row<4, true>(blk, kI4KC, kI4KM, off, k0, k1, lane);
@@ -241,8 +263,9 @@ __global__ void __launch_bounds__(64) append_int2_kernel(
     const int32_t r = rows[t];
     bad |= r < 0 || r >= n_rows;
     const int64_t src = (int64_t)(r < 0 || r >= n_rows ? 0 : r) * row_stride + (int64_t)head * head_stride + 2 * lane;
-    kx[t][0] = load_src(k, dtype, src);
-    kx[t][1] = load_src(k, dtype, src + 1);
+    const float2 kp = load_pair(k, dtype, src);
+    kx[t][0] = kp.x;
+    kx[t][1] = kp.y;
     const float a = canon(kx[t][0]), b = canon(kx[t][1]);
     mn0 = t ? fminf(mn0, a) : a;
     mx0 = t ? fmaxf(mx0, a) : a;
@@ -266,13 +289,14 @@ __global__ void __launch_bounds__(64) append_int2_kernel(
     *reinterpret_cast<uint32_t *>(m + kI2KZ + at) = q0.zb | (q1.zb << 16);
   }
 
-  // V, per token.
-#pragma unroll 4
-  for (int t = 0; t < kGroup; ++t) {
-    const int64_t src = (int64_t)rows[t] * row_stride + (int64_t)head * head_stride + 2 * lane;
-    put_token_row<2, false>(blk[t >> 4], kI2VC, kI2VM, t & 15, load_src(v, dtype, src),
-                            load_src(v, dtype, src + 1), lane);
-  }
+  // V, per token: all 32 rows loaded first, then quantized independently.
+  float2 vx[kGroup];
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t)
+    vx[t] = load_pair(v, dtype, (int64_t)rows[t] * row_stride + (int64_t)head * head_stride + 2 * lane);
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t)
+    put_token_row<2, false>(blk[t >> 4], kI2VC, kI2VM, t & 15, vx[t].x, vx[t].y, lane);
 }
 
 // --------------------------------------------------------------- reorder ------
