@@ -714,45 +714,29 @@ struct RingGeom {
   static constexpr int chunks_of(int w) { return (kChunks - w + W - 1) / W; }
 };
 
-// One 1 KB chunk: lane L copies 16 B from src to LDS byte lds + 16 L.  M0 carries the
-// LDS base; it is a register the compiler reserves, so its value is put back.
+// One 1 KB chunk: lane L copies 16 B from src to LDS byte lds + 16 L.  The LDS base
+// goes in M0 (an input the compiler sets, so it may reuse the value across copies); an
+// LDS-bound global load needs one wait state after a write of M0, hence the s_nop.
 __device__ __forceinline__ void dma_chunk(uint32_t lds, gbytes src) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "s"(lds), "v"((uint64_t)src)
-               : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"((uint64_t)src), "{m0}"(lds) : "memory");
 }
 
 // One 1 KB chunk from one page block: lane L copies 16 B from base + voff (base
 // wave-uniform in SGPRs, voff per lane) to LDS byte lds + 16 L.
 __device__ __forceinline__ void dma_block(uint32_t lds, gbytes base, uint32_t voff) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "s"(lds), "v"(voff), "s"((uint64_t)base)
-               : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
 }
 
 // One 256 B chunk: lane L copies 4 B from src to LDS byte lds + 4 L.
 __device__ __forceinline__ void dma_dword(uint32_t lds, gbytes src) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "s"(lds), "v"((uint64_t)src)
-               : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"((uint64_t)src), "{m0}"(lds) : "memory");
 }
 
 // Lanes 0 and 1 copy the dwords at base + voff to LDS bytes lds, lds + 4 (the other
 // lanes copy nothing).
 __device__ __forceinline__ void dma_pair(uint32_t lds, gbytes base, uint32_t voff, int lane) {
-  if (lane < 2) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "s"(lds), "v"(voff), "s"((uint64_t)base)
-                 : "memory");
-  }
+  if (lane < 2)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
 }
 
 // Waits until at most N copies issued by this wave are still in flight (they complete
