@@ -154,7 +154,7 @@ def main():
     import torch
 
     import synth
-    from harness import GpuRun
+    from harness import DeviceRun
     from mixed_precision_quantized_amd import kvq
 
     suffix, default_layers, description = WORKLOADS[args.workload]
@@ -167,7 +167,7 @@ def main():
     # Layer 0 is built, placed, quantized and reordered through the library; every other
     # layer gets its own pools holding its own K / V with the same placement, so the
     # reordered tables, ranges and plan serve all layers.
-    gpu = GpuRun(make(device=dev, layer=0))
+    gpu = DeviceRun(make(device=dev, layer=0))
     w0 = gpu.w
     eff_layer, decode_bytes = effective_bytes(w0)
     log(f"workload: {w0.note}; effective bytes per layer {eff_layer}")

@@ -1,6 +1,6 @@
 """Builders that run one synthetic workload through the GPU library or through the CPU
 oracle.  The two builders never share anything but the seeded workload itself
-(synth): GpuRun routes with the library's router and only calls the binding;
+(synth): DeviceRun routes with the library's router and only calls the binding;
 OracleRun routes with the oracle's router and only calls the oracle.  Build each side
 from its own Workload object (same constructor, same seed) because placement is
 stateful."""
@@ -35,7 +35,7 @@ def _ranges(w, after_reorder: bool):
     return synth.ranges_array(items)
 
 
-class GpuRun:
+class DeviceRun:
     """Route (library), place, quantize + append, reorder and decode on the GPU."""
 
     def __init__(self, w: synth.Workload, device="cuda", reorder=True):

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from harness import GpuRun, OracleRun, row_metric
+from harness import DeviceRun, OracleRun, row_metric
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -32,7 +32,7 @@ def _pools_equal(gpu, orc):
 def _check_case(name, make, plan_kw, reorder=True, out_dtype=torch.float32):
     _say(name, plan_kw)
     wg, wo = make(), make()
-    gpu = GpuRun(wg, reorder=reorder)
+    gpu = DeviceRun(wg, reorder=reorder)
     orc = OracleRun(wo, reorder=reorder)
     torch.cuda.synchronize()
     assert int(gpu.err.item()) == 0, f"device error bits {int(gpu.err.item())}"
@@ -105,7 +105,7 @@ def test_split_count_invariance_on_gpu():
     """Different split plans of the same cache agree to the parity tolerance (fp16 operand
     roundings depend on each split's running maximum, so agreement is not bitwise)."""
     wg = synth.qwen3_8b(batch=1, n_tokens=2048)
-    gpu = GpuRun(wg)
+    gpu = DeviceRun(wg)
     outs = []
     for kw in (dict(target_bytes=1 << 30), dict(target_bytes=1 << 16), dict(tokens_per_split=[32, 1, 1])):
         s, o = gpu.plan(**kw)
@@ -118,7 +118,7 @@ def test_split_count_invariance_on_gpu():
 def test_edge_cases_empty_dead_single():
     """Empty split, all-dead split, single-token split, and a (b, head) with no split."""
     wg = synth.ragged_dead(batch=2, lo=64, hi=128)
-    gpu = GpuRun(wg)
+    gpu = DeviceRun(wg)
     w = gpu.w
     sentinel = w.sentinel_slot
     tab = gpu.tables.cpu().numpy()
@@ -152,7 +152,7 @@ def test_edge_cases_empty_dead_single():
 def test_bad_device_data_is_reported_not_faulted():
     """Out-of-range split / page ids set dev_err bits; the kernels stay in bounds."""
     wg = synth.tiny()
-    gpu = GpuRun(wg)
+    gpu = DeviceRun(wg)
     splits = np.array([[5, 0, 1, 0, 16],        # table out of range
                        [0, 0, 0, 0, 10],        # INT2 range not on 32-token pairs
                        [0, 0, 1, 0, 1 << 20]], np.int32)   # past the table
@@ -184,7 +184,7 @@ def _full_size_sampled(name, make, requests):
     the sampled requests from the same seeded sources."""
     _say(f"full-size {name}: generating on the GPU")
     w = make()
-    gpu = GpuRun(w)
+    gpu = DeviceRun(w)
     splits, offsets = _resident_plan(gpu)
     out, lse, _, _ = gpu.decode(splits, offsets)
     assert int(gpu.err.item()) == 0
@@ -224,7 +224,7 @@ def test_full_size_qwen3_vl_agentic_sampled():
     resident-wave plan, checked on one sampled request against the oracle."""
     _say("full-size qwen3_vl_agentic: generating on the GPU")
     w = synth.qwen3_vl_agentic(device="cuda")
-    gpu = GpuRun(w)
+    gpu = DeviceRun(w)
     splits, offsets = _resident_plan(gpu)
     out, lse, _, _ = gpu.decode(splits, offsets)
     assert int(gpu.err.item()) == 0
@@ -243,7 +243,7 @@ def test_full_size_qwen3_8b_sampled():
     checked on two sampled requests against the oracle."""
     _say("full-size qwen3_8b: generating on the GPU")
     w = synth.qwen3_8b(device="cuda")
-    gpu = GpuRun(w)
+    gpu = DeviceRun(w)
     splits, offsets = _resident_plan(gpu)
     out, lse, _, _ = gpu.decode(splits, offsets)
     assert int(gpu.err.item()) == 0
@@ -278,7 +278,7 @@ def test_graph_replay_matches_eager():
     replays, each after eager launches and a synchronization, equal the eager result
     bit for bit and the oracle within the tolerance."""
     w = synth.qwen3_8b(batch=2, n_tokens=2048)
-    gpu = GpuRun(w, reorder=True)
+    gpu = DeviceRun(w, reorder=True)
     orc = OracleRun(synth.qwen3_8b(batch=2, n_tokens=2048), reorder=True)
     ref, _ = orc.attend()
     kvq = gpu.kvq
