@@ -370,6 +370,38 @@ int orc_reorder(const orc_cache *c, int32_t *tables, int32_t n_tables,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Slot-map compaction                                                       */
+/* ------------------------------------------------------------------------ */
+
+int orc_compact_slots(const orc_cache *c, int32_t *tables, int32_t n_tables,
+                      int32_t max_entries, const int32_t *n_entries,
+                      const int32_t *head_tokens, int32_t heads,
+                      int32_t *live_tokens)
+{
+    if (!c || !tables || !n_entries || !head_tokens || !live_tokens || n_tables < 0 ||
+        max_entries < 0 || heads <= 0)
+        return ORC_EARG;
+    const int32_t dead = c->sentinel_slot;
+    for (int32_t t = 0; t < n_tables; ++t) {
+        int32_t n = n_entries[t];
+        int32_t *row = tables + (int64_t)t * max_entries;
+        if (n < 0 || n > max_entries) return ORC_EARG;
+        for (int32_t h = 0; h < heads; ++h) {     /* live entries among the head's prefix */
+            int32_t m = head_tokens[t * heads + h], live = 0;
+            if (m < 0 || m > n) return ORC_ERANGE;
+            for (int32_t e = 0; e < m; ++e)
+                if (row[e] != dead) ++live;
+            live_tokens[t * heads + h] = live;
+        }
+        int32_t w = 0;                             /* stable: live entries in their order */
+        for (int32_t e = 0; e < n; ++e)
+            if (row[e] != dead) row[w++] = row[e];
+        for (int32_t e = w; e < n; ++e) row[e] = dead;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantization of one token (fp64, exact)                                 */
 /* ------------------------------------------------------------------------ */
 

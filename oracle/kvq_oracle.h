@@ -103,6 +103,18 @@ int orc_reorder(const orc_cache *c, int32_t *tables, int32_t n_tables,
                 int32_t max_entries, const int32_t *n_entries,
                 int32_t *class_counts);
 
+/* --- slot-map compaction (Tangram dead slots carry no attention mass) -----
+ * For every table t, entries [0, n_entries[t]) are stably partitioned: the
+ * live entries (not the sentinel slot) keep their order at the front, the
+ * dead ones follow, written as the sentinel.  Head h of table t read the first
+ * head_tokens[t*heads + h] entries before; live_tokens[t*heads + h] receives
+ * how many of them were live, which is the number of leading entries it reads
+ * afterwards (the live entries of that prefix, in the same order). */
+int orc_compact_slots(const orc_cache *c, int32_t *tables, int32_t n_tables,
+                      int32_t max_entries, const int32_t *n_entries,
+                      const int32_t *head_tokens, int32_t heads,
+                      int32_t *live_tokens);
+
 /* Dequantize one token of one head to fp64 (K and V, 128 channels each). */
 int orc_token(const orc_cache *c, int32_t page, int32_t off, int32_t head,
               double *k, double *v);

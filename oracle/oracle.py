@@ -70,11 +70,12 @@ def _declare(L):
     L.orc_route.argtypes = [P, i32, P, P, P, P]
     L.orc_append.argtypes = [P, P, P, i32, i64, i64, i32, P, P, i32, P, P, i32, P, P]
     L.orc_reorder.argtypes = [P, P, i32, i32, P, P]
+    L.orc_compact_slots.argtypes = [P, P, i32, i32, P, P, i32, P]
     L.orc_token.argtypes = [P, i32, i32, i32, P, P]
     L.orc_attend.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, P, i32, P, P, i32]
     L.orc_attend_ranges.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, P, i32, P, P, i32]
     L.orc_merge.argtypes = [P, P, P, i32, i32, i32, P, P]
-    for name in ("orc_route", "orc_append", "orc_reorder", "orc_token", "orc_attend",
+    for name in ("orc_route", "orc_append", "orc_reorder", "orc_compact_slots", "orc_token", "orc_attend",
                  "orc_attend_ranges", "orc_merge"):
         getattr(L, name).restype = ctypes.c_int
 
@@ -187,6 +188,19 @@ class Cache:
         _check(lib().orc_reorder(ctypes.byref(c), _ptr(tables), tables.shape[0], tables.shape[1],
                                  _ptr(n_entries), _ptr(counts)), "reorder")
         return counts
+
+    def compact_slots(self, tables, n_entries, head_tokens):
+        """In-place stable compaction of int32 slot tables [n_tables, max_entries]
+        (live entries first); returns the live counts [n_tables, heads]."""
+        assert tables.dtype == np.int32 and tables.flags.c_contiguous
+        n_entries = _c_array(n_entries, np.int32)
+        head_tokens = _c_array(head_tokens, np.int32)
+        live = np.zeros(head_tokens.shape, np.int32)
+        c = self._struct()
+        _check(lib().orc_compact_slots(ctypes.byref(c), _ptr(tables), tables.shape[0], tables.shape[1],
+                                       _ptr(n_entries), _ptr(head_tokens), head_tokens.shape[1],
+                                       _ptr(live)), "compact_slots")
+        return live
 
     def token(self, page, off, head):
         k = np.zeros(HEAD_DIM, np.float64)

@@ -195,6 +195,46 @@ def test_dead_slots_equal_dropped_tokens(orc):
     assert not out.any() and np.all(np.isneginf(lse))
 
 
+def test_slot_compaction_keeps_attention_and_order(orc):
+    """Compacting a two-head slot table (live entries first, in order) and reading each
+    head's live count leaves every head's attention as it was: the dead entries carry
+    no weight.  Counts, order and the all-dead / empty-prefix cases checked directly."""
+    r = np.random.default_rng(16)
+    T, g, H = 300, 4, 2
+    k = r.standard_normal((T + 1, H, 128)).astype(np.float32)
+    v = r.standard_normal((T + 1, H, 128)).astype(np.float32)
+    k[0], v[0] = -1e4, 0.0
+    c = orc.Cache(H, 0, -(-T // 16) + 1, 0, sentinel_slot=0)
+    slots = 16 + r.permutation(T)                      # scattered slots
+    c.append(k, v, orc.F32, H * 128, 128, rows4=np.concatenate([[0], 1 + np.arange(T)]),
+             slots4=np.concatenate([[0], slots]))
+    q = r.standard_normal((1, g * H, 128)).astype(np.float32)
+    tabs = np.full((3, T), 7, np.int32)                # table 1: all dead; table 2: empty prefixes
+    tabs[0] = slots
+    tabs[0, np.sort(r.choice(T, 61, replace=False))] = 0
+    tabs[1] = 0
+    n_entries = np.array([T, 40, 0], np.int32)
+    head_tokens = np.array([[T, 173], [40, 9], [0, 0]], np.int32)
+    orig = tabs.copy()
+    live = c.compact_slots(tabs, n_entries, head_tokens)
+    for t in range(3):
+        n = n_entries[t]
+        keep = orig[t, :n][orig[t, :n] != 0]
+        assert np.array_equal(tabs[t, :len(keep)], keep) and np.all(tabs[t, len(keep):n] == 0)
+        assert np.array_equal(tabs[t, n:], orig[t, n:])  # past n_entries: untouched
+        for h in range(H):
+            assert live[t, h] == int((orig[t, :head_tokens[t, h]] != 0).sum())
+    # attention of table 0 (both heads: one request, hkv = 2)
+    before = synth.ranges_array([(0, h, 1, 0, int(head_tokens[0, h])) for h in range(H)])
+    after = synth.ranges_array([(0, h, 1, 0, int(live[0, h])) for h in range(H)])
+    o0, l0 = c.attend(q, 1, g * H, H, np.ascontiguousarray(orig[:1]), orc.SLOTS, before)
+    o1, l1 = c.attend(q, 1, g * H, H, np.ascontiguousarray(tabs[:1]), orc.SLOTS, after)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1) and np.isfinite(l0).all()
+    assert live[1].tolist() == [0, 0] and live[2].tolist() == [0, 0]
+    with pytest.raises(RuntimeError):                   # a prefix longer than the table
+        c.compact_slots(orig.copy(), n_entries, np.array([[T + 1, 0], [0, 0], [0, 0]], np.int32))
+
+
 def test_merge_closed_form(orc):
     r = np.random.default_rng(15)
     g, S = 3, 5
