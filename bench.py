@@ -115,7 +115,8 @@ def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_pl
     if splits_per_head:
         sph = np.full(w.batch * w.hkv, splits_per_head, np.int32)
     elif w.head_tokens is not None and ragged_plan == "tokens":
-        toks = w.head_tokens.reshape(-1).astype(np.float64)
+        read = w.head_tokens if getattr(gpu, "live_tokens", None) is None else gpu.live_tokens.cpu().numpy()
+        toks = read.reshape(-1).astype(np.float64)
         sph = np.maximum(1, np.floor(per_cu * n_cu * toks / toks.sum())).astype(np.int32)
     elif w.head_budget is not None:
         sph = kvq.aot_split_counts(w.head_budget, w.batch, per_cu * n_cu)
@@ -142,6 +143,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (reference for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compact", action="store_true",
+                    help="slot maps: decode the tables as they are instead of dropping dead entries ahead of time")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured HIP graph")
     args = ap.parse_args()
@@ -167,7 +170,7 @@ def main():
     # Layer 0 is built, placed, quantized and reordered through the library; every other
     # layer gets its own pools holding its own K / V with the same placement, so the
     # reordered tables, ranges and plan serve all layers.
-    gpu = DeviceRun(make(device=dev, layer=0))
+    gpu = DeviceRun(make(device=dev, layer=0), compact=not args.no_compact)
     w0 = gpu.w
     eff_layer, decode_bytes = effective_bytes(w0)
     log(f"workload: {w0.note}; effective bytes per layer {eff_layer}")
@@ -299,6 +302,10 @@ def main():
 
     gbs = eff_layer * layers / (ms_step * 1e-3) / 1e9
     default = args.workload == "qwen3_8b"
+    if w0.kind == synth.SLOTS:
+        description += (", slot maps as given (dead entries decoded and masked)" if args.no_compact
+                        else ", slot maps compacted ahead of time (dead entries dropped)")
+        description += f", {args.ragged_plan} split counts"
     result = {
         "metric": "decode-attn effective KV GB/s (% HBM peak) + µs/step, " + suffix,
         "value": round(gbs, 1),

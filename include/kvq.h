@@ -163,6 +163,27 @@ kvq_status kvq_reorder_pages(const kvq_cache *c, int32_t *tables, int32_t n_tabl
                              int32_t *class_counts, int32_t *dev_err, void *stream);
 
 /*
+ * Slot-map compaction (optional, before decoding slot maps; Tangram's sentinel
+ * dead slots carry no attention mass, so the decode may skip them ahead of
+ * time instead of per token).  tables [dev] int32 [n_tables][max_entries] of
+ * slot ids: for every table t, entries [0, n_entries[t]) ([dev]) are stably
+ * partitioned in place, live entries (not c->sentinel_slot) first in their
+ * order, then the dead ones, rewritten as the sentinel.  head_tokens [dev]
+ * int32 [n_tables][heads_per_page]: head h of table t reads the first
+ * head_tokens[t][h] <= n_entries[t] entries; live_tokens [dev] int32
+ * [n_tables][heads_per_page] receives the live entries among them, the number
+ * of leading entries head h reads after the compaction (its attention is
+ * unchanged).  With no sentinel slot (-1) nothing moves.  A table whose
+ * n_entries or head_tokens are out of range is left as it was
+ * (KVQ_DEVERR_RANGE).  Errors: INVALID_ARG, UNSUPPORTED (heads_per_page > 64),
+ * HIP.
+ */
+kvq_status kvq_compact_slots(const kvq_cache *c, int32_t *tables, int32_t n_tables,
+                             int32_t max_entries, const int32_t *n_entries,
+                             const int32_t *head_tokens, int32_t *live_tokens,
+                             int32_t *dev_err, void *stream);
+
+/*
  * Split-K decode attention (TriAxialKV key design 4, phase 2; HyQuant
  * Algorithm 3).  One work item per split.  Split s = splits[s] [dev] covers
  * tokens [tok_begin, tok_end) of (table, head) in class cls; table t serves

@@ -353,6 +353,51 @@ __global__ void __launch_bounds__(64) reorder_kernel(CacheView c, int32_t *table
   if (__any(pair_bad) && lane == 0) report(err, KVQ_DEVERR_PAIR);
 }
 
+// Slot-map compaction: one wave per table streams its entries in 64-entry chunks, four
+// chunks loaded at a time; a ballot over the live lanes gives each live entry its place
+// (live entries so far + live lanes below).  In place: an entry only moves towards the
+// front, to a position already read.  Lane h < heads keeps head h's live count, taken
+// in the chunk where the head's prefix ends.
+__global__ void __launch_bounds__(64) compact_slots_kernel(int32_t sentinel, int32_t heads, int32_t *tables,
+                                                           int32_t max_entries, const int32_t *n_entries,
+                                                           const int32_t *head_tokens, int32_t *live_tokens,
+                                                           int32_t *err) {
+  const int lane = threadIdx.x;
+  const int32_t t = blockIdx.x;
+  int32_t *row = tables + (int64_t)t * max_entries;
+  const int32_t n = n_entries[t];
+  const int32_t m = lane < heads ? head_tokens[(int64_t)t * heads + lane] : 0;
+  if (__any(n < 0 || n > max_entries || m < 0 || m > n)) {  // leave the table as it was
+    if (lane == 0) report(err, KVQ_DEVERR_RANGE);
+    return;
+  }
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  constexpr int kBatch = 4;
+  int32_t w = 0, live_m = 0;
+  for (int32_t base = 0; base < n; base += 64 * kBatch) {
+    int32_t v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int32_t e = base + 64 * i + lane;
+      v[i] = e < n ? row[e] : sentinel;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int32_t cb = base + 64 * i;
+      const bool live = cb + lane < n && v[i] != sentinel;
+      const uint64_t mask = __ballot(live);
+      if (m > cb && m <= cb + 64) {  // head lane's prefix ends in this chunk
+        const int32_t k = m - cb;
+        live_m = w + __popcll(mask & (k == 64 ? ~0ull : (1ull << k) - 1ull));
+      }
+      if (live) row[w + __popcll(mask & below)] = v[i];
+      w += __popcll(mask);
+    }
+  }
+  for (int32_t e = w + lane; e < n; e += 64) row[e] = sentinel;
+  if (lane < heads) live_tokens[(int64_t)t * heads + lane] = live_m;
+}
+
 CacheView view_of(const kvq_cache *c) {
   CacheView v;
   v.heads = c->heads_per_page;
@@ -430,4 +475,21 @@ extern "C" kvq_status kvq_reorder_pages(const kvq_cache *c, int32_t *tables, int
                      static_cast<hipStream_t>(stream), view_of(c), tables, max_entries, n_entries,
                      class_counts, dev_err);
   return launched("reorder_kernel");
+}
+
+extern "C" kvq_status kvq_compact_slots(const kvq_cache *c, int32_t *tables, int32_t n_tables,
+                                        int32_t max_entries, const int32_t *n_entries,
+                                        const int32_t *head_tokens, int32_t *live_tokens, int32_t *dev_err,
+                                        void *stream) {
+  kvq_status st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  if (n_tables < 0 || max_entries < 0) return fail(KVQ_ERR_INVALID_ARG, "negative table shape");
+  if (n_tables == 0) return KVQ_OK;
+  if (!tables || !n_entries || !head_tokens || !live_tokens)
+    return fail(KVQ_ERR_INVALID_ARG, "NULL tables, n_entries, head_tokens or live_tokens");
+  if (c->heads_per_page > 64) return fail(KVQ_ERR_UNSUPPORTED, "more than 64 heads per table");
+  hipLaunchKernelGGL(compact_slots_kernel, dim3(n_tables), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     c->sentinel_slot, c->heads_per_page, tables, max_entries, n_entries, head_tokens,
+                     live_tokens, dev_err);
+  return launched("compact_slots_kernel");
 }

@@ -61,6 +61,7 @@ _SIGS = {
     "kvq_quantize_append": ([_P, _P, _P, _i32, _i64, _i64, _i64, _i32, _P, _P, _i32, _P, _P, _i32, _P, _P,
                              _P, _P], ctypes.c_int),
     "kvq_reorder_pages": ([_P, _P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
+    "kvq_compact_slots": ([_P, _P, _i32, _i32, _P, _P, _P, _P, _P], ctypes.c_int),
     "kvq_decode_attn": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P, _P,
                          _P], ctypes.c_int),
     "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
@@ -167,6 +168,23 @@ def reorder_pages(cache: Cache, tables: torch.Tensor, n_entries: torch.Tensor,
     _check(_lib.kvq_reorder_pages(cache.struct, _dptr(tables), tables.shape[0], tables.shape[1],
                                   _dptr(n_entries), _dptr(class_counts), _dptr(dev_err),
                                   _stream(stream)), "kvq_reorder_pages")
+
+
+def compact_slots(cache: Cache, tables: torch.Tensor, n_entries: torch.Tensor, head_tokens: torch.Tensor,
+                  live_tokens: Optional[torch.Tensor] = None, dev_err=None, stream=None) -> torch.Tensor:
+    """Slot tables int32 [n_tables, max_entries], compacted in place; returns the live
+    counts int32 [n_tables, heads_per_page] (device)."""
+    assert tables.dtype == torch.int32 and tables.is_contiguous() and tables.dim() == 2
+    assert head_tokens.dtype == torch.int32 and head_tokens.is_contiguous()
+    assert n_entries.dtype == torch.int32 and n_entries.numel() >= tables.shape[0]
+    assert head_tokens.numel() >= tables.shape[0] * cache.heads_per_page
+    if live_tokens is None:
+        live_tokens = torch.empty_like(head_tokens)
+    assert live_tokens.dtype == torch.int32 and live_tokens.numel() >= head_tokens.numel()
+    _check(_lib.kvq_compact_slots(cache.struct, _dptr(tables), tables.shape[0], tables.shape[1],
+                                  _dptr(n_entries), _dptr(head_tokens), _dptr(live_tokens), _dptr(dev_err),
+                                  _stream(stream)), "kvq_compact_slots")
+    return live_tokens
 
 
 def decode_attn(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, table_kind: int,

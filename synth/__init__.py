@@ -577,11 +577,20 @@ def slot_tables(w: Workload):
     return out
 
 
-def slot_ranges(w: Workload):
+def slot_entry_counts(w: Workload):
+    """Entries per slot-map table (the longest head prefix of the table)."""
+    assert w.kind == SLOTS
+    return np.array([int(sum(w.alloc.fill[t])) for t in range(w.n_tables)], np.int32)
+
+
+def slot_ranges(w: Workload, head_tokens=None):
+    """One INT4 range [0, n) per (table, head); n = the workload's head_tokens, or the
+    given per-(table, head) counts (the live counts of compacted tables)."""
+    ht = w.head_tokens if head_tokens is None else np.asarray(head_tokens)
     items = []
     for t in range(w.n_tables):
         for h in range(w.heads_per_page):
-            items.append((t, h, INT4, 0, int(w.head_tokens[t, h])))
+            items.append((t, h, INT4, 0, int(ht[t, h])))
     return ranges_array(items)
 
 

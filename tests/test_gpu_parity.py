@@ -29,14 +29,17 @@ def _pools_equal(gpu, orc):
             raise AssertionError(f"class {cls}: {bad.size} bytes differ, first at {bad[:8]}")
 
 
-def _check_case(name, make, plan_kw, reorder=True, out_dtype=torch.float32):
-    _say(name, plan_kw)
+def _check_case(name, make, plan_kw, reorder=True, out_dtype=torch.float32, compact=False):
+    _say(name, plan_kw, "compacted" if compact else "")
     wg, wo = make(), make()
-    gpu = DeviceRun(wg, reorder=reorder)
-    orc = OracleRun(wo, reorder=reorder)
+    gpu = DeviceRun(wg, reorder=reorder, compact=compact)
+    orc = OracleRun(wo, reorder=reorder, compact=compact)
     torch.cuda.synchronize()
     assert int(gpu.err.item()) == 0, f"device error bits {int(gpu.err.item())}"
     _pools_equal(gpu, orc)
+    if compact:
+        assert np.array_equal(gpu.tables.cpu().numpy(), orc.tables)
+        assert np.array_equal(gpu.live_tokens.cpu().numpy(), orc.live_tokens)
     if wg.kind == synth.PAGES:
         assert np.array_equal(gpu.tables.cpu().numpy(), orc.tables)
         if reorder:
@@ -88,6 +91,60 @@ def test_ragged_dead_small():
         return dict(splits_per_head=kvq.aot_split_counts(w.head_budget, w.batch, 64))
     make = lambda: synth.ragged_dead(batch=4, lo=512, hi=4096)  # noqa: E731
     _check_case("ragged 4", make, plan_for(make()))
+
+
+@pytest.mark.parametrize("plan", ["aot", "tokens"])
+def test_ragged_dead_small_compacted(plan):
+    """The same ragged slot maps compacted ahead of time (dead entries dropped, each
+    head reading its live count): tables and counts bit-exact, attention within TOL."""
+    from mixed_precision_quantized_amd import kvq
+    make = lambda: synth.ragged_dead(batch=4, lo=512, hi=4096)  # noqa: E731
+    w = make()
+    if plan == "aot":
+        kw = dict(splits_per_head=kvq.aot_split_counts(w.head_budget, w.batch, 64))
+    else:
+        kw = dict(tokens_per_split=[512, 512, 512])
+    _check_case("ragged 4", make, kw, compact=True)
+
+
+def test_slot_compaction_edges():
+    """Compaction alone on crafted tables: several 256-entry batches and a ragged tail,
+    an all-dead table, empty prefixes, no dead entry; a prefix longer than its table is
+    reported and leaves that table untouched."""
+    from mixed_precision_quantized_amd import kvq
+    from oracle import oracle
+    r = np.random.default_rng(3)
+    H, sentinel, me = 2, 16, 1000
+    n = np.array([1000, 37, 64, 0, 300, 5], np.int32)
+    tabs = (32 + r.integers(0, 5000, (len(n), me))).astype(np.int32)
+    for t, frac in enumerate([0.2, 1.0, 0.5, 0.0, 0.0, 0.6]):
+        dead = r.random(me) < frac
+        tabs[t, dead] = sentinel
+    ht = np.array([[1000, 517], [37, 0], [64, 63], [0, 0], [300, 300], [1, 5]], np.int32)
+    cache = kvq.Cache(H, (0, 400, 0), "cuda", sentinel_slot=sentinel)
+    ocache = oracle.Cache(H, 0, 400, 0, sentinel_slot=sentinel)
+    for bad in (False, True):
+        h2 = ht.copy()
+        if bad:
+            h2[4, 1] = 301  # beyond n_entries of table 4
+        dt = torch.as_tensor(tabs, device="cuda").contiguous()
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        live = kvq.compact_slots(cache, dt, torch.as_tensor(n, device="cuda"),
+                                 torch.as_tensor(h2, device="cuda").contiguous(), dev_err=err)
+        torch.cuda.synchronize()
+        got, got_live = dt.cpu().numpy(), live.cpu().numpy()
+        if not bad:
+            ot = tabs.copy()
+            ol = ocache.compact_slots(ot, n, h2)
+            assert int(err.item()) == 0
+            assert np.array_equal(got, ot) and np.array_equal(got_live, ol)
+        else:
+            assert int(err.item()) == kvq.DEVERR_RANGE
+            assert np.array_equal(got[4], tabs[4])   # the bad table is left as it was
+            good = [0, 1, 2, 3, 5]
+            ot = np.ascontiguousarray(tabs[good])
+            ol = ocache.compact_slots(ot, n[good], np.ascontiguousarray(ht[good]))
+            assert np.array_equal(got[good], ot) and np.array_equal(got_live[good], ol)
 
 
 def test_g8_and_g1_heads():
@@ -179,12 +236,12 @@ def _resident_plan(gpu):
     return gpu.plan(splits_per_head=np.full(w.batch * w.hkv, sph, np.int32))
 
 
-def _full_size_sampled(name, make, requests):
+def _full_size_sampled(name, make, requests, compact=False):
     """Full-size workload with the benchmark's plan on the GPU; the oracle recomputes
-    the sampled requests from the same seeded sources."""
-    _say(f"full-size {name}: generating on the GPU")
+    the sampled requests from the same seeded sources (slot maps: uncompacted)."""
+    _say(f"full-size {name}: generating on the GPU" + (" (compacted slot maps)" if compact else ""))
     w = make()
-    gpu = DeviceRun(w)
+    gpu = DeviceRun(w, compact=compact)
     splits, offsets = _resident_plan(gpu)
     out, lse, _, _ = gpu.decode(splits, offsets)
     assert int(gpu.err.item()) == 0
@@ -210,6 +267,14 @@ def test_full_size_ragged_dead_sampled():
     lens = synth.ragged_lengths()
     pick = sorted({int(np.argmin(lens)), int(np.argmax(lens))})
     _full_size_sampled("ragged_dead", lambda: synth.ragged_dead(device="cuda"), pick)
+
+
+def test_full_size_ragged_dead_compacted_sampled():
+    """The same full-size ragged workload with its slot maps compacted (the benchmark's
+    default for slot maps), sampled requests against the uncompacted oracle."""
+    lens = synth.ragged_lengths()
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens))})
+    _full_size_sampled("ragged_dead", lambda: synth.ragged_dead(device="cuda"), pick, compact=True)
 
 
 def test_qwen3_vl_agentic_small():
