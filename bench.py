@@ -107,7 +107,8 @@ def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_pl
     """One work group per split, as many splits as the decode kernel keeps resident at
     once (a second, partial round would leave most of the chip idle).  Ragged slot maps
     share the count among heads in proportion to their budgets (Tangram AOT), or, with
-    ragged_plan="tokens", to the tokens each head reads."""
+    ragged_plan="tokens", so that no piece holds more tokens than it must for the count
+    to fit (balanced split counts over the tokens each head reads)."""
     import numpy as np
     w = gpu.w
     kind = kvq.TABLE_SLOTS if w.kind == synth.SLOTS else kvq.TABLE_PAGES
@@ -116,8 +117,7 @@ def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_pl
         sph = np.full(w.batch * w.hkv, splits_per_head, np.int32)
     elif w.head_tokens is not None and ragged_plan == "tokens":
         read = w.head_tokens if getattr(gpu, "live_tokens", None) is None else gpu.live_tokens.cpu().numpy()
-        toks = read.reshape(-1).astype(np.float64)
-        sph = np.maximum(1, np.floor(per_cu * n_cu * toks / toks.sum())).astype(np.int32)
+        sph = kvq.balanced_split_counts(read, per_cu * n_cu)  # no piece longer than needed to fit
     elif w.head_budget is not None:
         sph = kvq.aot_split_counts(w.head_budget, w.batch, per_cu * n_cu)
     else:
@@ -138,7 +138,7 @@ def main():
     ap.add_argument("--class-cost", default=None,
                     help="per-token decode cost INT2,INT4,FP16 for sharing splits (default: the library's)")
     ap.add_argument("--ragged-plan", choices=("aot", "tokens"), default="aot",
-                    help="split counts of ragged slot maps: by budget (Tangram AOT) or by tokens read")
+                    help="split counts of ragged slot maps: by budget (Tangram AOT) or balanced by tokens read")
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (reference for HBM byte counters)")

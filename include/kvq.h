@@ -267,6 +267,19 @@ kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch
                                 int32_t total_work, int32_t *out);
 
 /*
+ * Balanced split counts [host]: the smallest cap c >= 1 on the work of one piece
+ * such that sum_i ceil(work[i] / c) over the non-empty entries fits total_work
+ * work groups, and out[i] = ceil(work[i] / c) (0 for work[i] == 0).  Every piece
+ * of a range cut into out[i] near-equal pieces then holds at most c, so one
+ * round of resident work groups ends with no piece much longer than the
+ * average (the AOT rule above fixes counts from budgets alone and lets long
+ * requests straggle).  work [host] int64 [n] >= 0: e.g. live tokens per (table,
+ * head), or tokens x class cost; out [host] int32 [n].  With more non-empty
+ * entries than total_work, every non-empty entry gets 1.  Errors: INVALID_ARG.
+ */
+kvq_status kvq_balanced_split_counts(const int64_t *work, int32_t n, int32_t total_work, int32_t *out);
+
+/*
  * Work groups (one wavefront each) of the decode kernel that fit on the current
  * device at once: *per_cu from the HIP occupancy API, *n_cu the compute-unit
  * count.  g (query heads per KV head) and table_kind select the kernel: page

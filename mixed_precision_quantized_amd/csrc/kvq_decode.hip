@@ -1095,30 +1095,36 @@ template <int QT>
 __device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L,
                                      uint8_t *ring, int32_t *id_blocks) {
   using G = RingGeom<KVQ_INT4, 1>;
-  static_assert(G::kSlots == 2, "one window in flight");
-  constexpr int C = SlotRingLoader::kCopies;
+  static_assert(G::kSlots == 2, "two data slots");
+  constexpr int C = SlotRingLoader::kCopies - 1;  // data copies per window (the eighth: its ids)
   SlotRingLoader ld(a, sp, ring, id_blocks);
   SplitRun<QT, KVQ_INT4, true> R(a, sp, L);
   const int32_t T0 = sp.tok_begin;
   const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
-  // Window i: slot ids copied at iteration i - 2 into id block i mod 4, data at
-  // iteration i - 1 into data slot i mod 2, computed at iteration i.  Per iteration:
-  // ids of i + 2, (wait: ids of i + 1), data of i + 1, (wait: data of i), compute i.
+  // Window i: slot ids copied at iteration i - 3 into id block i mod 4, data at
+  // iteration i - 2 into data slot i mod 2 (as soon as window i - 2 sits in registers),
+  // computed at iteration i, so two windows are in flight during every compute.  Per
+  // iteration: (wait: data of i), read i, ids of i + 3, (wait: ids of i + 2), data of
+  // i + 2, compute i.  Copies complete in issue order; the waits count what follows.
   ld.issue_ids(T0, 0);
   ld.issue_ids(T0 + 32, 1);
-  wait_copies<1>();
-  uint32_t mask_next = ld.issue_data(T0, 0, true, 0);
+  wait_copies<1>();  // ids of window 0
+  uint32_t mask0 = ld.issue_data(T0, 0, true, 0);
+  ld.issue_ids(T0 + 64, 2);
+  wait_copies<C + 1>();  // ids of window 1
+  uint32_t mask1 = ld.issue_data(T0 + 32, 1, 1 < nw, 1);
   ProgressPriority prio(nw);
   for (int32_t n = 0; n < nw; ++n) {
     prio.step(n);
-    ld.issue_ids(T0 + 32 * (n + 2), (n + 2) & 3);
-    wait_copies<C>();  // the ids of window n + 1
-    const uint32_t mask = mask_next;
-    mask_next = ld.issue_data(T0 + 32 * (n + 1), (n + 1) & 3, n + 1 < nw, (n + 1) & 1);
-    wait_copies<C>();  // the data of window n
+    wait_copies<C + 1>();  // the data of window n (then: ids of n + 2, data of n + 1)
     Win w;
-    ld.read(n & 1, mask, w);
+    ld.read(n & 1, mask0, w);
+    ld.issue_ids(T0 + 32 * (n + 3), (n + 3) & 3);
+    wait_copies<C + 1>();  // the ids of window n + 2 (then: data of n + 1, ids of n + 3)
+    const uint32_t mask2 = ld.issue_data(T0 + 32 * (n + 2), (n + 2) & 3, n + 2 < nw, n & 1);
     R.window(w, T0 + 32 * n);
+    mask0 = mask1;
+    mask1 = mask2;
   }
   wait_copies<0>();  // no copy outlives the wave
   if (ld.errs) report(a.err, (int32_t)ld.errs);

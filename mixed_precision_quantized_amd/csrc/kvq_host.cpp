@@ -198,6 +198,28 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
   return KVQ_OK;
 }
 
+kvq_status kvq_balanced_split_counts(const int64_t *work, int32_t n, int32_t total_work, int32_t *out) {
+  if (!work || !out || n <= 0 || total_work <= 0) return fail(KVQ_ERR_INVALID_ARG, "bad balanced-count arguments");
+  int64_t hi = 1;
+  for (int32_t i = 0; i < n; ++i) {
+    if (work[i] < 0) return fail(KVQ_ERR_INVALID_ARG, "work[%d] is negative", i);
+    hi = std::max(hi, work[i]);
+  }
+  auto pieces = [&](int64_t cap) {  // non-increasing in cap; at cap = max work, one per entry
+    int64_t sum = 0;
+    for (int32_t i = 0; i < n; ++i) sum += (work[i] + cap - 1) / cap;
+    return sum;
+  };
+  int64_t lo = 1;  // smallest cap whose pieces fit (or the largest work, when nothing fits)
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (pieces(mid) <= total_work) hi = mid;
+    else lo = mid + 1;
+  }
+  for (int32_t i = 0; i < n; ++i) out[i] = (int32_t)((work[i] + lo - 1) / lo);
+  return KVQ_OK;
+}
+
 kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch, int32_t total_work,
                                 int32_t *out) {
   if (!budgets || !out || hkv <= 0 || batch <= 0 || total_work <= 0)

@@ -67,6 +67,7 @@ _SIGS = {
     "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
     "kvq_plan_splits": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _i64, _P, _i32, _P, _P], ctypes.c_int),
     "kvq_aot_split_counts": ([_P, _i32, _i32, _i32, _P], ctypes.c_int),
+    "kvq_balanced_split_counts": ([_P, _i32, _i32, _P], ctypes.c_int),
     "kvq_decode_occupancy": ([_i32, _i32, _P, _P], ctypes.c_int),
     "kvq_status_string": ([_i32], ctypes.c_char_p),
     "kvq_last_error": ([], ctypes.c_char_p),
@@ -240,6 +241,16 @@ def aot_split_counts(budgets: np.ndarray, batch: int, total_work: int) -> np.nda
     out = np.zeros(batch * b.shape[0], np.int32)
     _check(_lib.kvq_aot_split_counts(_hptr(b), b.shape[0], batch, total_work, _hptr(out)),
            "kvq_aot_split_counts")
+    return out
+
+
+def balanced_split_counts(work, total_work: int) -> np.ndarray:
+    """Split counts such that no piece holds more than the smallest cap that fits
+    total_work work groups (work: per-entry cost, e.g. live tokens per (table, head))."""
+    w = np.ascontiguousarray(np.asarray(work).reshape(-1), np.int64)
+    out = np.zeros(w.shape[0], np.int32)
+    _check(_lib.kvq_balanced_split_counts(_hptr(w), w.shape[0], total_work, _hptr(out)),
+           "kvq_balanced_split_counts")
     return out
 
 

@@ -157,3 +157,22 @@ def test_plan_splits_class_cost_shares_a_head_count(kvq):
     assert [int((s[:, 2] == c).sum()) for c in (0, 1)] == [5, 4]     # 1 + 3.5, 1 + 3.5 -> 4.5, 4.5
     with pytest.raises(kvq.KvqError):
         kvq.plan_splits(rng, 1, 1, 1, splits_per_head=sph, class_cost=[1.0, 0.0, 1.0])
+
+
+def test_balanced_split_counts_minimal_cap(kvq):
+    """Counts fit the work groups, and no smaller cap on one piece's work would."""
+    r = np.random.default_rng(8)
+    work = r.integers(300, 120000, 512).astype(np.int64)
+    work[::37] = 0
+    total = 3072
+    out = kvq.balanced_split_counts(work, total)
+    assert out.sum() <= total and np.array_equal(out == 0, work == 0)
+    live = work > 0
+    cap = int(np.max(-(-work[live] // out[live])))          # the longest piece
+    assert int(np.sum(-(-work[live] // (cap - 1)))) > total  # one less does not fit
+    same = kvq.balanced_split_counts(np.full(128, 4096, np.int64), 3072)
+    assert np.all(same == 24)
+    few = kvq.balanced_split_counts(np.array([5, 0, 7, 9], np.int64), 2)   # more entries than groups
+    assert few.tolist() == [1, 0, 1, 1]
+    with pytest.raises(kvq.KvqError):
+        kvq.balanced_split_counts(np.array([3, -1], np.int64), 4)
