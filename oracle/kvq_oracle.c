@@ -402,6 +402,66 @@ int orc_compact_slots(const orc_cache *c, int32_t *tables, int32_t n_tables,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Vertical-line selection (HyQuant Algorithm 1) and FREEZE routing (Alg. 4) */
+/* ------------------------------------------------------------------------ */
+
+static const double *g_sort_scores;  /* qsort has no context argument */
+
+static int by_score_then_index(const void *a, const void *b)
+{
+    int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+    double si = g_sort_scores[i], sj = g_sort_scores[j];
+    if (si > sj) return -1;
+    if (si < sj) return 1;
+    return (i > j) - (i < j);
+}
+
+int orc_select_vl(const float *k, const float *q_tail, int32_t batch,
+                  int32_t max_tokens, int32_t hkv, int32_t hq, int32_t max_tail,
+                  const int32_t *n_tokens, const int32_t *n_tail, int32_t window,
+                  double rho, double *scores, uint8_t *cls, int32_t *n_vl)
+{
+    if (!k || !q_tail || !n_tokens || !n_tail || !scores || !cls || !n_vl || batch < 0 ||
+        max_tokens < 0 || hkv <= 0 || hq <= 0 || hq % hkv || max_tail <= 0 || window < 0 ||
+        !(rho >= 0.0 && rho <= 1.0))
+        return ORC_EARG;
+    const int32_t g = hq / hkv;
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)(max_tokens > 0 ? max_tokens : 1));
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t n = n_tokens[b], nt = n_tail[b];
+        if (n < 0 || n > max_tokens || nt < 0 || nt > max_tail) { free(order); return ORC_ERANGE; }
+        for (int32_t h = 0; h < hkv; ++h) {
+            double u[D];                              /* tail-query proxy of the group */
+            for (int c = 0; c < D; ++c) {
+                double sum = 0.0;
+                for (int32_t j = 0; j < g; ++j)
+                    for (int32_t i = 0; i < nt; ++i)
+                        sum += q_tail[(((int64_t)b * max_tail + i) * hq + h * g + j) * D + c];
+                u[c] = nt > 0 ? sum / nt : 0.0;
+            }
+            const int64_t row = ((int64_t)b * hkv + h) * max_tokens;
+            for (int32_t t = 0; t < max_tokens; ++t) {
+                double s = 0.0;
+                if (t < n)
+                    for (int c = 0; c < D; ++c)
+                        s += u[c] * k[(((int64_t)b * max_tokens + t) * hkv + h) * D + c];
+                scores[row + t] = s;
+                cls[row + t] = (t < n && t >= n - window) ? 2 : 0;
+            }
+            const int32_t n_pre = n - window > 0 ? n - window : 0;
+            const int32_t m = (int32_t)floor(rho * n_pre + 0.5);
+            for (int32_t t = 0; t < n_pre; ++t) order[t] = t;
+            g_sort_scores = scores + row;
+            qsort(order, (size_t)n_pre, sizeof(int32_t), by_score_then_index);
+            for (int32_t r = 0; r < m; ++r) cls[row + order[r]] = 1;
+            n_vl[b * hkv + h] = m;
+        }
+    }
+    free(order);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantization of one token (fp64, exact)                                 */
 /* ------------------------------------------------------------------------ */
 

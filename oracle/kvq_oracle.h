@@ -17,7 +17,10 @@
  *   [HyQuant] "HyQuant: Hybrid-Precision Quantization for LLM Attention",
  *       background (softmax(QK^T/sqrt(d)), online softmax m / l / acc, GQA
  *       stacking of g = Hq/Hkv query heads), method (key partition into
- *       quantized / vertical-line / window sets; FP16 anchors), Algorithm 3.
+ *       quantized / vertical-line / window sets; FP16 anchors), Algorithm 3;
+ *       Algorithm 1 (vertical lines: window W excluded, tail-query proxy,
+ *       GQA column scores, top rho of the prefix) and Algorithm 4 (FREEZE:
+ *       vertical lines and window stay full precision, the rest is quantized).
  *   [IntentKV] technical summary, "layout-preserving eviction": evicted
  *       positions are redirected to one sentinel dead slot (K = -1e4, V = 0)
  *       whose attention contribution is zero.
@@ -114,6 +117,22 @@ int orc_compact_slots(const orc_cache *c, int32_t *tables, int32_t n_tables,
                       int32_t max_entries, const int32_t *n_entries,
                       const int32_t *head_tokens, int32_t heads,
                       int32_t *live_tokens);
+
+/* --- vertical-line selection and FREEZE routing (HyQuant Algorithms 1, 4) --
+ * Per request b and KV head h, in fp64: the tail-query proxy is the mean over
+ * the n_tail[b] tail queries of the sum of the g = hq/hkv query heads of h,
+ * u = sum_j (1/n_tail) sum_i q[b][i][h*g + j]; the score of token k is u . K[b][k][h].
+ * Tokens k >= n - window (n = n_tokens[b]) form the window; of the prefix
+ * k < n - window, the n_vl = floor(rho * n_pre + 1/2) tokens of highest score
+ * (ties: lower k) are the vertical lines.  cls[(b*hkv + h)*max_tokens + k] =
+ * 1 (vertical line), 2 (window), 0 (quantized prefix, and k >= n); scores
+ * [same index] for k < n (0 past n); n_vl[b*hkv + h].  K [batch][max_tokens]
+ * [hkv][128] and q_tail [batch][max_tail][hq][128] are fp32 (bf16 sources
+ * widen exactly). */
+int orc_select_vl(const float *k, const float *q_tail, int32_t batch,
+                  int32_t max_tokens, int32_t hkv, int32_t hq, int32_t max_tail,
+                  const int32_t *n_tokens, const int32_t *n_tail, int32_t window,
+                  double rho, double *scores, uint8_t *cls, int32_t *n_vl);
 
 /* Dequantize one token of one head to fp64 (K and V, 128 channels each). */
 int orc_token(const orc_cache *c, int32_t page, int32_t off, int32_t head,

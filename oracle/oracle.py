@@ -72,10 +72,12 @@ def _declare(L):
     L.orc_reorder.argtypes = [P, P, i32, i32, P, P]
     L.orc_compact_slots.argtypes = [P, P, i32, i32, P, P, i32, P]
     L.orc_token.argtypes = [P, i32, i32, i32, P, P]
+    L.orc_select_vl.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, i32, ctypes.c_double, P, P, P]
     L.orc_attend.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, P, i32, P, P, i32]
     L.orc_attend_ranges.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, P, i32, P, P, i32]
     L.orc_merge.argtypes = [P, P, P, i32, i32, i32, P, P]
-    for name in ("orc_route", "orc_append", "orc_reorder", "orc_compact_slots", "orc_token", "orc_attend",
+    for name in ("orc_route", "orc_append", "orc_reorder", "orc_compact_slots", "orc_token", "orc_select_vl",
+                 "orc_attend",
                  "orc_attend_ranges", "orc_merge"):
         getattr(L, name).restype = ctypes.c_int
 
@@ -140,6 +142,23 @@ def merge(part_out, part_lse, offsets, batch, hq, hkv):
     _check(lib().orc_merge(_ptr(part_out), _ptr(part_lse), _ptr(offsets), batch, hq, hkv,
                            _ptr(out), _ptr(lse)), "merge")
     return out, lse
+
+
+def select_vl(k, q_tail, n_tokens, n_tail, window=128, rho=0.05):
+    """Vertical-line selection + FREEZE routing.  k float32 [batch, max_tokens, hkv, 128],
+    q_tail float32 [batch, max_tail, hq, 128]; returns (scores fp64 [batch, hkv, max_tokens],
+    classes uint8 (0 quantized, 1 vertical line, 2 window) same shape, n_vl [batch, hkv])."""
+    k = _c_array(k, np.float32)
+    q_tail = _c_array(q_tail, np.float32)
+    batch, max_tokens, hkv = k.shape[:3]
+    max_tail, hq = q_tail.shape[1:3]
+    scores = np.zeros((batch, hkv, max_tokens), np.float64)
+    cls = np.zeros((batch, hkv, max_tokens), np.uint8)
+    n_vl = np.zeros((batch, hkv), np.int32)
+    _check(lib().orc_select_vl(_ptr(k), _ptr(q_tail), batch, max_tokens, hkv, hq, max_tail,
+                               _ptr(_c_array(n_tokens, np.int32)), _ptr(_c_array(n_tail, np.int32)),
+                               window, float(rho), _ptr(scores), _ptr(cls), _ptr(n_vl)), "select_vl")
+    return scores, cls, n_vl
 
 
 class Cache:
