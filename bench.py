@@ -131,7 +131,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="qwen3_8b")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["vl_select"], default="qwen3_8b",
+                    help="a decode workload, or vl_select: vertical-line selection + FREEZE routing at the "
+                         "hybrid-anchor prefill shape")
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--splits-per-head", type=int, default=0,
                     help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
@@ -160,6 +162,8 @@ def main():
     from harness import DeviceRun
     from mixed_precision_quantized_amd import kvq
 
+    if args.workload == "vl_select":
+        return bench_vl(args)
     suffix, default_layers, description = WORKLOADS[args.workload]
     make = getattr(synth, args.workload)
     layers = args.layers or default_layers
@@ -365,6 +369,82 @@ def main():
                       f"g = {w0.g}), fp64 two-pass softmax, {reps} passes in {dt:.1f} s",
         }
         log(f"cpu oracle {result['cpu_baseline']['value']} GB/s on {n_threads} threads ({dt:.1f} s)")
+    print(json.dumps(result), flush=True)
+
+
+def bench_vl(args):
+    """Vertical-line selection + FREEZE routing (one kvq_select_vertical_lines call: proxy,
+    scores, selection) on the hybrid-anchor prefill shape: 32 requests x 65536 tokens,
+    Hq 32 / Hkv 8, 64 bf16 tail queries, bf16 keys resident in HBM.  Algorithmic bytes per
+    call: the keys and tail queries read once, per token-head a 4-byte score written and
+    read back and a 1-byte class written."""
+    import numpy as np
+    import torch
+
+    import synth
+    from mixed_precision_quantized_amd import kvq
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    w = synth.vl_prefill(device=dev)
+    batch, mt, hkv = w.k.shape[:3]
+    hq = w.q_tail.shape[2]
+    nt = torch.as_tensor(w.n_tokens, device=dev)
+    ntl = torch.as_tensor(w.n_tail, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+    out = kvq.select_vertical_lines(w.k, w.q_tail, nt, ntl, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    log(f"vl_select: {w.note}; {int(out[3].sum())} vertical lines")
+    call = lambda: kvq.select_vertical_lines(w.k, w.q_tail, nt, ntl, out=out, dev_err=err,  # noqa: E731
+                                             stream=stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.steps):
+            call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    sec = e0.elapsed_time(e1) * 1e-3 / args.steps
+    token_heads = int(w.n_tokens.astype(np.int64).sum()) * hkv
+    nbytes = w.k.numel() * w.k.element_size() + w.q_tail.numel() * w.q_tail.element_size() + 9 * token_heads
+    gbs = nbytes / sec / 1e9
+    log(f"vl_select: {sec * 1e6:.1f} us per call, {gbs:.0f} GB/s algorithmic")
+    result = {
+        "metric": "vertical-line selection + FREEZE routing GB/s (HyQuant Alg. 1, 4), hybrid-anchor prefill shape",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 keys and queries, fp32 scores", "data": "synthetic",
+        "config": {"workload": f"vertical-line selection: {w.note}, window 128, rho 0.05",
+                   "batch": batch, "max_tokens": mt, "hkv": hkv, "hq": hq, "bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "vl_select (proxy, scores, selection)", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        req = [0, 1]
+        k = w.k[req].float().cpu().numpy()
+        q = w.q_tail[req].float().cpu().numpy()
+        reps, t = 0, time.perf_counter()
+        while True:
+            oracle.select_vl(k, q, w.n_tokens[req], w.n_tail[req])
+            reps += 1
+            dt = time.perf_counter() - t
+            if dt >= CPU_SECONDS:
+                break
+        sample = k.nbytes // 2 + q.nbytes // 2 + 9 * int(w.n_tokens[req].astype(np.int64).sum()) * hkv
+        result["cpu_baseline"] = {"value": round(sample * reps / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"2 of {batch} requests (bf16-sized bytes), fp64 scores and a "
+                                            f"sort per head, one thread, {reps} passes in {dt:.1f} s"}
+        log(f"cpu oracle {result['cpu_baseline']['value']} GB/s on 1 thread ({dt:.1f} s)")
     print(json.dumps(result), flush=True)
 
 

@@ -184,6 +184,34 @@ kvq_status kvq_compact_slots(const kvq_cache *c, int32_t *tables, int32_t n_tabl
                              int32_t *dev_err, void *stream);
 
 /*
+ * Vertical-line selection and FREEZE routing (HyQuant Algorithm 1 and Algorithm
+ * 4), run once at the end of a prefill.  For request b < batch and KV head h:
+ *   proxy[b][h][c] = (1/n_tail[b]) sum_{i < n_tail[b]} sum_{j < g} q_tail[b][i][h*g + j][c]
+ *     (the tail-query proxy of the GQA group, g = hq / hkv; 0 when n_tail is 0);
+ *   scores[b][h][t] = proxy[b][h] . k[b][t][h] for t < n_tokens[b] (0 beyond);
+ *   token_class[b][h][t]: 2 for the window t in [n - window, n), 1 for the
+ *     n_vl[b][h] = floor(rho * n_pre + 1/2) prefix tokens (t < n_pre = max(n -
+ *     window, 0)) of highest score, ties to the lower t (the vertical lines),
+ *     0 for the rest of the prefix and for t >= n.  FREEZE keeps classes 1 and
+ *     2 in FP16 and quantizes class 0.
+ *   k [dev]: [batch][max_tokens][hkv][128] of k_dtype; q_tail [dev]:
+ *   [batch][max_tail][hq][128] of q_dtype (KVQ_F32 / BF16 / F16); n_tokens,
+ *   n_tail [dev] int32 [batch] (n_tail <= max_tail <= 64); proxy [dev] float
+ *   [batch][hkv][128]; scores [dev] float and token_class [dev] uint8
+ *   [batch][hkv][max_tokens]; n_vl [dev] int32 [batch][hkv].
+ * Scores are fp32 dot products; the selection is exact on them.  A request whose
+ * n_tokens or n_tail is out of range is treated as empty (KVQ_DEVERR_RANGE).
+ * Errors: INVALID_ARG, UNSUPPORTED (hkv other than 1, 2, 4, 8, 16), HIP.
+ */
+kvq_status kvq_select_vertical_lines(const void *k, int32_t k_dtype, const void *q_tail,
+                                     int32_t q_dtype, int32_t batch, int32_t max_tokens,
+                                     int32_t hkv, int32_t hq, int32_t max_tail,
+                                     const int32_t *n_tokens, const int32_t *n_tail,
+                                     int32_t window, float rho, float *proxy, float *scores,
+                                     uint8_t *token_class, int32_t *n_vl, int32_t *dev_err,
+                                     void *stream);
+
+/*
  * Split-K decode attention (TriAxialKV key design 4, phase 2; HyQuant
  * Algorithm 3).  One work item per split.  Split s = splits[s] [dev] covers
  * tokens [tok_begin, tok_end) of (table, head) in class cls; table t serves

@@ -25,6 +25,7 @@ SOURCES = [
     # start, masked logits are -inf); without NaNs to honour, max needs no quieting and
     # DPP row reductions fold into v_max_f32_dpp.
     ("kvq_decode.hip", HIP + ["-fno-honor-nans"]),
+    ("kvq_select.hip", HIP),
 ]
 
 

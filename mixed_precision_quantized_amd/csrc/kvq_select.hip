@@ -1,0 +1,296 @@
+// Vertical-line selection and FREEZE routing (HyQuant Algorithm 1 and Algorithm 4).
+//
+// Per request b and KV head h: the tail-query proxy u (the mean over the request's
+// tail queries of the sum of the g query heads of h), the score u . K of every token,
+// and, over the non-window prefix (the last `window` tokens excluded), the
+// round(rho * prefix) tokens of highest score (ties: lower index) as vertical lines.
+// The class written per token is the FREEZE routing: vertical lines and window stay
+// FP16, the rest of the prefix is quantized.
+//
+// Three launches: the proxy (one wave per (b, h)); the scores (HBM-bound: every K row
+// read once, a token's hkv x 128 values across the 64 lanes of a wave, a dot product
+// per lane and a reduction over the lanes of one head); the selection (one work group
+// per (b, h): a four-pass 8-bit radix select of the threshold key over the prefix
+// scores in LDS histograms, then one ordered pass that ranks the keys equal to the
+// threshold by index).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kMaxTail = 64;  // tail queries kept by the proxy
+constexpr int kScoreWaves = 4;
+constexpr int kTokensPerWave = 64;
+constexpr int kSelectThreads = 256;
+
+__device__ __forceinline__ void report(int32_t *err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+template <int DT>
+__device__ __forceinline__ float elem(const void *p, int64_t i) {
+  if (DT == KVQ_F32) return static_cast<const float *>(p)[i];
+  const uint16_t h = static_cast<const uint16_t *>(p)[i];
+  if (DT == KVQ_BF16) return __uint_as_float((uint32_t)h << 16);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// u[b][h][c] = (1 / n_tail) sum_i sum_j q[b][i][h g + j][c]; lane = channel pair.
+template <int QD>
+__global__ void __launch_bounds__(64) vl_proxy_kernel(const void *q, int32_t hkv, int32_t hq, int32_t max_tail,
+                                                      const int32_t *n_tail, float *u, int32_t *err) {
+  const int b = blockIdx.x / hkv, h = blockIdx.x % hkv, lane = threadIdx.x;
+  const int g = hq / hkv;
+  int32_t nt = n_tail[b];
+  if (nt < 0 || nt > max_tail) {
+    if (lane == 0) report(err, KVQ_DEVERR_RANGE);
+    nt = 0;
+  }
+  float s0 = 0.0f, s1 = 0.0f;
+  for (int i = 0; i < nt; ++i)
+    for (int j = 0; j < g; ++j) {
+      const int64_t at = (((int64_t)b * max_tail + i) * hq + h * g + j) * kHeadDim + 2 * lane;
+      s0 += elem<QD>(q, at);
+      s1 += elem<QD>(q, at + 1);
+    }
+  const float inv = nt > 0 ? 1.0f / (float)nt : 0.0f;
+  float *dst = u + ((int64_t)b * hkv + h) * kHeadDim + 2 * lane;
+  dst[0] = s0 * inv;
+  dst[1] = s1 * inv;
+}
+
+// NW consecutive 32-bit words at p (16-byte aligned when NW >= 4), in the widest loads.
+template <int NW>
+__device__ __forceinline__ void load_words(const uint32_t *p, uint32_t (&w)[NW]) {
+  if constexpr (NW >= 4) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+      w[4 * i] = v.x, w[4 * i + 1] = v.y, w[4 * i + 2] = v.z, w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    w[0] = v.x, w[1] = v.y;
+  } else {
+    w[0] = *p;
+  }
+}
+
+// The E values of one lane (words of E elements of type KD) as fp32.
+template <int KD, int E>
+__device__ __forceinline__ void lane_values(const void *k, int64_t first, float (&v)[E]) {
+  if constexpr (KD == KVQ_F32) {
+    uint32_t w[E];
+    load_words<E>(static_cast<const uint32_t *>(k) + first, w);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = __uint_as_float(w[e]);
+  } else {
+    uint32_t w[E / 2];
+    load_words<E / 2>(static_cast<const uint32_t *>(k) + first / 2, w);
+#pragma unroll
+    for (int e = 0; e < E / 2; ++e) {
+      if (KD == KVQ_BF16) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      } else {
+        v[2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xFFFFu));
+        v[2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+      }
+    }
+  }
+}
+
+// Scores of 64 consecutive tokens per wave.  A token row holds HKV x 128 values; lane
+// l takes E = 2 HKV consecutive ones (all of one head: 64 / HKV lanes per head), so a
+// wave reads each row as one contiguous block.
+template <int KD, int HKV>
+__global__ void __launch_bounds__(64 * kScoreWaves) vl_score_kernel(const void *k, int32_t max_tokens,
+                                                                    const int32_t *n_tokens, const float *u,
+                                                                    float *scores) {
+  constexpr int E = 2 * HKV, LPH = 64 / HKV;  // values per lane, lanes per head
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.y, h = lane / LPH;
+  const int32_t n = min(max(n_tokens[b], 0), max_tokens);
+  const int32_t t0 = (blockIdx.x * kScoreWaves + wave) * kTokensPerWave;
+  if (t0 >= max_tokens) return;
+  float uu[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) uu[e] = u[((int64_t)b * HKV + h) * kHeadDim + (lane % LPH) * E + e];
+  const int64_t row0 = (int64_t)b * max_tokens;
+  const int32_t t_end = min(t0 + kTokensPerWave, max_tokens);
+  constexpr int U = 4;  // tokens in flight per lane
+  for (int32_t t = t0; t < t_end; t += U) {
+    float v[U][E];
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      const int32_t tt = min(t + r, n - 1);  // rows past n are not read (their score is 0)
+      if (n > 0) {
+        lane_values<KD, E>(k, (row0 + tt) * (HKV * kHeadDim) + (int64_t)lane * E, v[r]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[r][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) s = fmaf(uu[e], v[r][e], s);
+#pragma unroll
+      for (int off = LPH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      const int32_t tt = t + r;
+      if (lane % LPH == 0 && tt < t_end) scores[((int64_t)b * HKV + h) * max_tokens + tt] = tt < n ? s : 0.0f;
+    }
+  }
+}
+
+// Order-preserving key of a score (+0 and -0 alike).
+__device__ __forceinline__ uint32_t key_of(float s) {
+  const uint32_t x = __float_as_uint(s == 0.0f ? 0.0f : s);
+  return (x & 0x80000000u) ? ~x : (x | 0x80000000u);
+}
+
+__global__ void __launch_bounds__(kSelectThreads) vl_select_kernel(const float *scores, int32_t hkv,
+                                                                   int32_t max_tokens, const int32_t *n_tokens,
+                                                                   int32_t window, float rho, uint8_t *cls,
+                                                                   int32_t *n_vl, int32_t *err) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wave_eq[kSelectThreads / 64];
+  __shared__ uint32_t sel[2];  // threshold prefix, keys still needed at it
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x / hkv;
+  const int64_t row = (int64_t)blockIdx.x * max_tokens;
+  int32_t n = n_tokens[b];
+  if (n < 0 || n > max_tokens) {
+    if (tid == 0) report(err, KVQ_DEVERR_RANGE);
+    n = 0;
+  }
+  const int32_t n_pre = max(n - window, 0);
+  const int32_t m = (int32_t)floor((double)rho * (double)n_pre + 0.5);
+  const float *S = scores + row;
+
+  // Radix select of the m-th largest key, 8 bits a pass from the top.
+  uint32_t prefix = 0, need = (uint32_t)m;
+  if (m > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      const uint32_t hi_mask = shift == 24 ? 0u : (~0u << (shift + 8));
+      hist[tid] = 0;
+      __syncthreads();
+      for (int32_t t = tid; t < n_pre; t += kSelectThreads) {
+        const uint32_t key = key_of(S[t]);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t above = 0;
+        int bin = 255;
+        for (; bin > 0; --bin) {
+          if (above + hist[bin] >= need) break;
+          above += hist[bin];
+        }
+        sel[0] = prefix | ((uint32_t)bin << shift);
+        sel[1] = need - above;
+      }
+      __syncthreads();
+      prefix = sel[0];
+      need = sel[1];
+      __syncthreads();  // hist is cleared again next pass
+    }
+  }
+  // Classes in token order: above the threshold, or at it among the first `need`.
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  uint32_t eq_before = 0;
+  for (int32_t base = 0; base < max_tokens; base += kSelectThreads) {
+    const int32_t t = base + tid;
+    const bool in_pre = t < n_pre;
+    const uint32_t key = in_pre && m > 0 ? key_of(S[t]) : 0u;
+    const bool gt = in_pre && m > 0 && key > prefix, eq = in_pre && m > 0 && key == prefix;
+    const uint64_t eq_mask = __ballot(eq);
+    if (lane == 0) wave_eq[wave] = (uint32_t)__popcll(eq_mask);
+    __syncthreads();
+    uint32_t off = eq_before, total = 0;
+    for (int w = 0; w < kSelectThreads / 64; ++w) {
+      if (w < wave) off += wave_eq[w];
+      total += wave_eq[w];
+    }
+    const uint32_t rank = off + (uint32_t)__popcll(eq_mask & below);
+    if (t < max_tokens) {
+      uint8_t c = 0;
+      if (t < n && t >= n_pre) c = 2;
+      else if (gt || (eq && rank < need)) c = 1;
+      cls[row + t] = c;
+    }
+    eq_before += total;
+    __syncthreads();  // wave_eq is rewritten by the next chunk
+  }
+  if (tid == 0) n_vl[blockIdx.x] = m;
+}
+
+kvq_status launched(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+template <int KD>
+void launch_scores(int hkv, dim3 grid, hipStream_t s, const void *k, int32_t max_tokens, const int32_t *n_tokens,
+                   const float *u, float *scores) {
+  const dim3 block(64 * kScoreWaves);
+  switch (hkv) {
+    case 1: hipLaunchKernelGGL((vl_score_kernel<KD, 1>), grid, block, 0, s, k, max_tokens, n_tokens, u, scores); break;
+    case 2: hipLaunchKernelGGL((vl_score_kernel<KD, 2>), grid, block, 0, s, k, max_tokens, n_tokens, u, scores); break;
+    case 4: hipLaunchKernelGGL((vl_score_kernel<KD, 4>), grid, block, 0, s, k, max_tokens, n_tokens, u, scores); break;
+    case 8: hipLaunchKernelGGL((vl_score_kernel<KD, 8>), grid, block, 0, s, k, max_tokens, n_tokens, u, scores); break;
+    default: hipLaunchKernelGGL((vl_score_kernel<KD, 16>), grid, block, 0, s, k, max_tokens, n_tokens, u, scores);
+  }
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" kvq_status kvq_select_vertical_lines(const void *k, int32_t k_dtype, const void *q_tail, int32_t q_dtype,
+                                                int32_t batch, int32_t max_tokens, int32_t hkv, int32_t hq,
+                                                int32_t max_tail, const int32_t *n_tokens, const int32_t *n_tail,
+                                                int32_t window, float rho, float *proxy, float *scores,
+                                                uint8_t *token_class, int32_t *n_vl, int32_t *dev_err,
+                                                void *stream) {
+  auto dtype_ok = [](int32_t d) { return d == KVQ_F32 || d == KVQ_BF16 || d == KVQ_F16; };
+  if (!dtype_ok(k_dtype) || !dtype_ok(q_dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown K or query dtype");
+  if (batch < 0 || max_tokens < 0) return fail(KVQ_ERR_INVALID_ARG, "negative batch or max_tokens");
+  if (hkv <= 0 || hq <= 0 || hq % hkv) return fail(KVQ_ERR_INVALID_ARG, "hq %d is not a multiple of hkv %d", hq, hkv);
+  if (hkv != 1 && hkv != 2 && hkv != 4 && hkv != 8 && hkv != 16)
+    return fail(KVQ_ERR_UNSUPPORTED, "hkv %d: 1, 2, 4, 8 or 16 KV heads", hkv);
+  if (max_tail < 1 || max_tail > kMaxTail) return fail(KVQ_ERR_INVALID_ARG, "max_tail %d outside [1, 64]", max_tail);
+  if (window < 0 || !(rho >= 0.0f && rho <= 1.0f)) return fail(KVQ_ERR_INVALID_ARG, "window < 0 or rho outside [0, 1]");
+  if (batch == 0 || max_tokens == 0) return KVQ_OK;
+  if (!k || !q_tail || !n_tokens || !n_tail || !proxy || !scores || !token_class || !n_vl)
+    return fail(KVQ_ERR_INVALID_ARG, "NULL buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 pgrid(batch * hkv), pblock(64);
+  if (q_dtype == KVQ_F32)
+    hipLaunchKernelGGL(vl_proxy_kernel<KVQ_F32>, pgrid, pblock, 0, s, q_tail, hkv, hq, max_tail, n_tail, proxy, dev_err);
+  else if (q_dtype == KVQ_BF16)
+    hipLaunchKernelGGL(vl_proxy_kernel<KVQ_BF16>, pgrid, pblock, 0, s, q_tail, hkv, hq, max_tail, n_tail, proxy, dev_err);
+  else
+    hipLaunchKernelGGL(vl_proxy_kernel<KVQ_F16>, pgrid, pblock, 0, s, q_tail, hkv, hq, max_tail, n_tail, proxy, dev_err);
+  kvq_status st = launched("vl_proxy_kernel");
+  if (st != KVQ_OK) return st;
+  const int per_block = kScoreWaves * kTokensPerWave;
+  const dim3 sgrid((max_tokens + per_block - 1) / per_block, batch);
+  if (k_dtype == KVQ_F32) launch_scores<KVQ_F32>(hkv, sgrid, s, k, max_tokens, n_tokens, proxy, scores);
+  else if (k_dtype == KVQ_BF16) launch_scores<KVQ_BF16>(hkv, sgrid, s, k, max_tokens, n_tokens, proxy, scores);
+  else launch_scores<KVQ_F16>(hkv, sgrid, s, k, max_tokens, n_tokens, proxy, scores);
+  st = launched("vl_score_kernel");
+  if (st != KVQ_OK) return st;
+  hipLaunchKernelGGL(vl_select_kernel, dim3(batch * hkv), dim3(kSelectThreads), 0, s, scores, hkv, max_tokens,
+                     n_tokens, window, rho, token_class, n_vl, dev_err);
+  return launched("vl_select_kernel");
+}

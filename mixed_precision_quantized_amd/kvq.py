@@ -62,6 +62,8 @@ _SIGS = {
                              _P, _P], ctypes.c_int),
     "kvq_reorder_pages": ([_P, _P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
     "kvq_compact_slots": ([_P, _P, _i32, _i32, _P, _P, _P, _P, _P], ctypes.c_int),
+    "kvq_select_vertical_lines": ([_P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32,
+                                   ctypes.c_float, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "kvq_decode_attn": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P, _P,
                          _P], ctypes.c_int),
     "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
@@ -186,6 +188,32 @@ def compact_slots(cache: Cache, tables: torch.Tensor, n_entries: torch.Tensor, h
                                   _dptr(n_entries), _dptr(head_tokens), _dptr(live_tokens), _dptr(dev_err),
                                   _stream(stream)), "kvq_compact_slots")
     return live_tokens
+
+
+CLASS_QUANTIZED, CLASS_VERTICAL_LINE, CLASS_WINDOW = 0, 1, 2
+
+
+def select_vertical_lines(k: torch.Tensor, q_tail: torch.Tensor, n_tokens: torch.Tensor, n_tail: torch.Tensor,
+                          window: int = 128, rho: float = 0.05, out=None, dev_err=None, stream=None):
+    """k [batch, max_tokens, hkv, 128], q_tail [batch, max_tail, hq, 128] (device);
+    returns (proxy [batch, hkv, 128], scores [batch, hkv, max_tokens], token_class uint8
+    [batch, hkv, max_tokens], n_vl [batch, hkv]), or fills `out` (the same four)."""
+    assert k.is_contiguous() and q_tail.is_contiguous() and k.dim() == 4 and q_tail.dim() == 4
+    batch, max_tokens, hkv = k.shape[:3]
+    max_tail, hq = q_tail.shape[1:3]
+    assert n_tokens.dtype == torch.int32 and n_tail.dtype == torch.int32
+    if out is None:
+        dev = k.device
+        out = (torch.empty((batch, hkv, HEAD_DIM), dtype=torch.float32, device=dev),
+               torch.empty((batch, hkv, max_tokens), dtype=torch.float32, device=dev),
+               torch.empty((batch, hkv, max_tokens), dtype=torch.uint8, device=dev),
+               torch.empty((batch, hkv), dtype=torch.int32, device=dev))
+    proxy, scores, cls, n_vl = out
+    _check(_lib.kvq_select_vertical_lines(_dptr(k), _DTYPES[k.dtype], _dptr(q_tail), _DTYPES[q_tail.dtype], batch,
+                                          max_tokens, hkv, hq, max_tail, _dptr(n_tokens), _dptr(n_tail), window,
+                                          float(rho), _dptr(proxy), _dptr(scores), _dptr(cls), _dptr(n_vl),
+                                          _dptr(dev_err), _stream(stream)), "kvq_select_vertical_lines")
+    return out
 
 
 def decode_attn(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, table_kind: int,

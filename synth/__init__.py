@@ -597,3 +597,40 @@ def slot_ranges(w: Workload, head_tokens=None):
 def sentinel_lists(w: Workload):
     """Append lists that write the sentinel row (row 0) into the sentinel slot."""
     return AppendLists(rows4=[0], slots4=[w.sentinel_slot])
+
+
+@dataclasses.dataclass
+class PrefillKQ:
+    """Keys of a finished prefill and its tail queries, padded to a batch."""
+    k: torch.Tensor          # [batch, max_tokens, hkv, 128]
+    q_tail: torch.Tensor     # [batch, max_tail, hq, 128]
+    n_tokens: np.ndarray     # int32 [batch]
+    n_tail: np.ndarray       # int32 [batch]
+    note: str
+
+
+def vl_prefill(seed=6, batch=32, n_tokens=65536, hkv=8, hq=32, max_tail=64, lengths=None, n_tail=None,
+               planted=0.03, dtype=torch.bfloat16, device="cpu") -> PrefillKQ:
+    """Keys and tail queries shaped like the hybrid-anchor prefill (Llama-3.1-8B:
+    Hq 32 / Hkv 8, 65536 tokens, 64 tail queries).  K, q ~ N(0, 1); the tail queries of
+    each (request, KV-head group) share a random direction c (q = c + noise), and a
+    seeded `planted` fraction of each head's tokens carries 4 c / |c| on top of its key,
+    the columns many queries attend to.  `lengths` / `n_tail` (per request) may be
+    ragged; rows past a request's length are zero."""
+    g = hq // hkv
+    lens = np.full(batch, n_tokens, np.int64) if lengths is None else np.asarray(lengths, np.int64)
+    tails = np.full(batch, max_tail, np.int64) if n_tail is None else np.asarray(n_tail, np.int64)
+    mt = int(lens.max()) if batch else 0
+    c = randn((batch, 1, hkv, 1, 128), seed, 61, device=device)
+    q = randn((batch, max_tail, hkv, g, 128), seed, 62, device=device) + c
+    k = randn((batch, mt, hkv, 128), seed, 63, device=device)
+    unit = (c / c.norm(dim=-1, keepdim=True)).reshape(batch, 1, hkv, 128)
+    mark = torch.rand((batch, mt, hkv, 1), generator=torch_gen(seed, 64, device=device), device=device) < planted
+    k.add_(mark.float() * 4.0 * unit)
+    for b in range(batch):
+        k[b, int(lens[b]):] = 0.0
+        q[b, int(tails[b]):] = 0.0
+    q = q.reshape(batch, max_tail, hq, 128)
+    return PrefillKQ(k.to(dtype).contiguous(), q.to(dtype).contiguous(), lens.astype(np.int32),
+                     tails.astype(np.int32), f"{batch} requests, {mt} tokens max, Hq {hq} / Hkv {hkv}, "
+                     f"{max_tail} tail queries, {planted:.0%} planted lines")

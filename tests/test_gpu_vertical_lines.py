@@ -1,0 +1,97 @@
+"""GPU vertical-line selection and FREEZE routing (HyQuant Algorithms 1 and 4) through
+the C ABI against the oracle.
+
+Bars: per-(request, head) counts and window classes exact; fp32 scores within 1e-5 of
+the row's largest fp64 score; the vertical-line sets equal, except that a token may
+swap across the threshold only when its fp64 score lies within that same tolerance of
+the threshold (several sets are then correct: the decision is taken on fp32 scores)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _say(*a):
+    print("[gpu-vl]", *a, flush=True)
+
+
+def _run(w, window=128, rho=0.05, n_tokens=None):
+    from mixed_precision_quantized_amd import kvq
+    dev = "cuda"
+    nt = torch.as_tensor(w.n_tokens if n_tokens is None else n_tokens, device=dev, dtype=torch.int32)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = kvq.select_vertical_lines(w.k.to(dev), w.q_tail.to(dev), nt,
+                                    torch.as_tensor(w.n_tail, device=dev, dtype=torch.int32),
+                                    window=window, rho=rho, dev_err=err)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in out], int(err.item())
+
+
+def _check(w, window=128, rho=0.05, requests=None):
+    from oracle import oracle
+    (proxy, scores, cls, n_vl), err = _run(w, window, rho)
+    assert err == 0
+    req = list(range(w.k.shape[0])) if requests is None else list(requests)
+    ref_s, ref_c, ref_n = oracle.select_vl(w.k[req].float().cpu().numpy(), w.q_tail[req].float().cpu().numpy(),
+                                           w.n_tokens[req], w.n_tail[req], window, float(np.float32(rho)))
+    scores, cls, n_vl = scores[req], cls[req], n_vl[req]
+    assert np.array_equal(n_vl, ref_n)
+    assert np.array_equal(cls == 2, ref_c == 2)
+    swaps = 0
+    for b in range(len(req)):
+        for h in range(scores.shape[1]):
+            s_ref = ref_s[b, h]
+            tol = TOL * max(float(np.abs(s_ref).max()), 1e-30)
+            assert np.abs(scores[b, h] - s_ref).max() <= tol, (b, h)
+            diff = (cls[b, h] == 1) != (ref_c[b, h] == 1)
+            if diff.any():
+                thr = s_ref[ref_c[b, h] == 1].min()
+                assert np.all(np.abs(s_ref[diff] - thr) <= tol), (b, h, np.flatnonzero(diff))
+                swaps += int(diff.sum())
+    _say(f"  counts {ref_n.sum()} vertical lines, {swaps} tokens swapped at a threshold tie")
+    return cls, n_vl
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_small_ragged_batch(dtype):
+    _say("small ragged", dtype)
+    w = synth.vl_prefill(batch=3, n_tokens=1000, hkv=2, hq=8, lengths=[1000, 300, 129], n_tail=[64, 5, 1],
+                         dtype=dtype)
+    cls, n_vl = _check(w)
+    assert n_vl.tolist() == [[44, 44], [9, 9], [0, 0]]
+
+
+@pytest.mark.parametrize("hkv,hq", [(1, 8), (4, 16), (8, 64), (16, 16)])
+def test_head_layouts_fp16(hkv, hq):
+    _say("heads", hkv, hq)
+    w = synth.vl_prefill(batch=2, n_tokens=700, hkv=hkv, hq=hq, lengths=[700, 450], n_tail=[64, 33],
+                         dtype=torch.float16)
+    _check(w)
+
+
+def test_edges():
+    """Shorter than the window, empty, no tail query (all scores 0: the lowest indices
+    win the ties), rho 0 and 1; a length beyond max_tokens is reported and treated as
+    empty."""
+    from mixed_precision_quantized_amd import kvq
+    w = synth.vl_prefill(batch=4, n_tokens=600, hkv=2, hq=4, lengths=[600, 100, 0, 400], n_tail=[8, 8, 8, 0])
+    for rho in (0.0, 0.05, 1.0):
+        _say("edges rho", rho)
+        cls, n_vl = _check(w, rho=rho)
+        assert np.all(cls[1, :, :100] == 2) and np.all(cls[2] == 0)
+        m = int(n_vl[3, 0])
+        assert np.array_equal(np.flatnonzero(cls[3, 0] == 1), np.arange(m))
+    (_, _, cls, n_vl), err = _run(w, n_tokens=np.array([600, 100, 601, 400], np.int32))
+    assert err == kvq.DEVERR_RANGE and np.all(cls[2] == 0) and n_vl[2].tolist() == [0, 0]
+
+
+def test_full_size_sampled():
+    """The hybrid-anchor prefill shape (32 requests x 65536 tokens, Hq 32 / Hkv 8, 64 tail
+    queries, bf16) on the GPU; two requests recomputed by the oracle."""
+    _say("full size: generating on the GPU")
+    w = synth.vl_prefill(device="cuda")
+    _check(w, requests=[3, 30])
