@@ -27,7 +27,7 @@ namespace {
 constexpr int kMaxTail = 64;  // tail queries kept by the proxy
 constexpr int kScoreWaves = 4;
 constexpr int kTokensPerWave = 64;
-constexpr int kSelectThreads = 256;
+constexpr int kSelectThreads = 1024;
 
 __device__ __forceinline__ void report(int32_t *err, int32_t bit) {
   if (err) atomicOr(err, bit);
@@ -41,28 +41,39 @@ __device__ __forceinline__ float elem(const void *p, int64_t i) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// u[b][h][c] = (1 / n_tail) sum_i sum_j q[b][i][h g + j][c]; lane = channel pair.
+// u[b][h][c] = (1 / n_tail) sum_i sum_j q[b][i][h g + j][c].  Lane = channel pair; the
+// four waves take every fourth (i, j) term and add their sums through LDS.
 template <int QD>
-__global__ void __launch_bounds__(64) vl_proxy_kernel(const void *q, int32_t hkv, int32_t hq, int32_t max_tail,
-                                                      const int32_t *n_tail, float *u, int32_t *err) {
-  const int b = blockIdx.x / hkv, h = blockIdx.x % hkv, lane = threadIdx.x;
+__global__ void __launch_bounds__(256) vl_proxy_kernel(const void *q, int32_t hkv, int32_t hq, int32_t max_tail,
+                                                       const int32_t *n_tail, float *u, int32_t *err) {
+  __shared__ float part[4][kHeadDim];
+  const int b = blockIdx.x / hkv, h = blockIdx.x % hkv, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = hq / hkv;
   int32_t nt = n_tail[b];
   if (nt < 0 || nt > max_tail) {
-    if (lane == 0) report(err, KVQ_DEVERR_RANGE);
+    if (threadIdx.x == 0) report(err, KVQ_DEVERR_RANGE);
     nt = 0;
   }
   float s0 = 0.0f, s1 = 0.0f;
-  for (int i = 0; i < nt; ++i)
-    for (int j = 0; j < g; ++j) {
-      const int64_t at = (((int64_t)b * max_tail + i) * hq + h * g + j) * kHeadDim + 2 * lane;
-      s0 += elem<QD>(q, at);
-      s1 += elem<QD>(q, at + 1);
-    }
-  const float inv = nt > 0 ? 1.0f / (float)nt : 0.0f;
-  float *dst = u + ((int64_t)b * hkv + h) * kHeadDim + 2 * lane;
-  dst[0] = s0 * inv;
-  dst[1] = s1 * inv;
+  const int terms = nt * g;
+#pragma unroll 8
+  for (int x = wave; x < terms; x += 4) {
+    const int i = x / g, j = x % g;
+    const int64_t at = (((int64_t)b * max_tail + i) * hq + h * g + j) * kHeadDim + 2 * lane;
+    s0 += elem<QD>(q, at);
+    s1 += elem<QD>(q, at + 1);
+  }
+  part[wave][2 * lane] = s0;
+  part[wave][2 * lane + 1] = s1;
+  __syncthreads();
+  if (wave == 0) {
+    const float inv = nt > 0 ? 1.0f / (float)nt : 0.0f;
+    float *dst = u + ((int64_t)b * hkv + h) * kHeadDim + 2 * lane;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      dst[c] = (((part[0][2 * lane + c] + part[1][2 * lane + c]) + part[2][2 * lane + c]) + part[3][2 * lane + c]) *
+               inv;
+  }
 }
 
 // NW consecutive 32-bit words at p (16-byte aligned when NW >= 4), in the widest loads.
@@ -82,17 +93,17 @@ __device__ __forceinline__ void load_words(const uint32_t *p, uint32_t (&w)[NW])
   }
 }
 
-// The E values of one lane (words of E elements of type KD) as fp32.
+// Words one lane loads per token row: E values of type KD.
 template <int KD, int E>
-__device__ __forceinline__ void lane_values(const void *k, int64_t first, float (&v)[E]) {
+constexpr int words_of() { return KD == KVQ_F32 ? E : E / 2; }
+
+// The E values of one lane, from its words, as fp32.
+template <int KD, int E>
+__device__ __forceinline__ void values_of(const uint32_t (&w)[words_of<KD, E>()], float (&v)[E]) {
   if constexpr (KD == KVQ_F32) {
-    uint32_t w[E];
-    load_words<E>(static_cast<const uint32_t *>(k) + first, w);
 #pragma unroll
     for (int e = 0; e < E; ++e) v[e] = __uint_as_float(w[e]);
   } else {
-    uint32_t w[E / 2];
-    load_words<E / 2>(static_cast<const uint32_t *>(k) + first / 2, w);
 #pragma unroll
     for (int e = 0; e < E / 2; ++e) {
       if (KD == KVQ_BF16) {
@@ -106,47 +117,81 @@ __device__ __forceinline__ void lane_values(const void *k, int64_t first, float 
   }
 }
 
+// Sum over the LPH consecutive lanes of a head; lane 0 of each group gets the total.
+// Within 16-lane rows by DPP (quad swaps, then row rotations that bring lane i + 4 and
+// lane i + 8 to lane i), across rows by a lane shuffle.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPH>
+__device__ __forceinline__ float head_sum(float s) {
+  if constexpr (LPH >= 2) s += dpp_mov<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+  if constexpr (LPH >= 4) s += dpp_mov<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+  if constexpr (LPH >= 8) s += dpp_mov<0x12C>(s);  // row_ror:12 (lane i reads lane i + 4 of its row)
+  if constexpr (LPH >= 16) s += dpp_mov<0x128>(s); // row_ror:8
+  if constexpr (LPH >= 32) s += __shfl_xor(s, 16);
+  if constexpr (LPH >= 64) s += __shfl_xor(s, 32);
+  return s;
+}
+
 // Scores of 64 consecutive tokens per wave.  A token row holds HKV x 128 values; lane
 // l takes E = 2 HKV consecutive ones (all of one head: 64 / HKV lanes per head), so a
-// wave reads each row as one contiguous block.
+// wave reads each row as one contiguous block.  U rows are loaded per step, the next
+// step's rows before the current ones are reduced; rows past the request's length
+// are clamped to its last row (read, never scored), so no load sits under a branch.
 template <int KD, int HKV>
 __global__ void __launch_bounds__(64 * kScoreWaves) vl_score_kernel(const void *k, int32_t max_tokens,
                                                                     const int32_t *n_tokens, const float *u,
                                                                     float *scores) {
-  constexpr int E = 2 * HKV, LPH = 64 / HKV;  // values per lane, lanes per head
+  constexpr int E = 2 * HKV, LPH = 64 / HKV, NW = words_of<KD, E>(), U = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y, h = lane / LPH;
   const int32_t n = min(max(n_tokens[b], 0), max_tokens);
   const int32_t t0 = (blockIdx.x * kScoreWaves + wave) * kTokensPerWave;
   if (t0 >= max_tokens) return;
+  const int32_t t_end = min(t0 + kTokensPerWave, max_tokens);
+  float *out = scores + ((int64_t)b * HKV + h) * max_tokens;
+  const bool writer = lane % LPH == 0;
+  if (n <= t0) {  // nothing of this request here
+    for (int32_t t = t0; t < t_end; ++t)
+      if (writer) out[t] = 0.0f;
+    return;
+  }
   float uu[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) uu[e] = u[((int64_t)b * HKV + h) * kHeadDim + (lane % LPH) * E + e];
+  const uint32_t *kw = static_cast<const uint32_t *>(k);
   const int64_t row0 = (int64_t)b * max_tokens;
-  const int32_t t_end = min(t0 + kTokensPerWave, max_tokens);
-  constexpr int U = 4;  // tokens in flight per lane
-  for (int32_t t = t0; t < t_end; t += U) {
-    float v[U][E];
+  auto load = [&](int32_t t, uint32_t (&w)[U][NW]) {
 #pragma unroll
     for (int r = 0; r < U; ++r) {
-      const int32_t tt = min(t + r, n - 1);  // rows past n are not read (their score is 0)
-      if (n > 0) {
-        lane_values<KD, E>(k, (row0 + tt) * (HKV * kHeadDim) + (int64_t)lane * E, v[r]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[r][e] = 0.0f;
-      }
+      const int64_t row = row0 + min(t + r, n - 1);
+      load_words<NW>(kw + row * (HKV * kHeadDim * NW / E) + (int64_t)lane * NW, w[r]);
     }
+  };
+  auto score = [&](int32_t t, const uint32_t (&w)[U][NW]) {
 #pragma unroll
     for (int r = 0; r < U; ++r) {
+      float v[E];
+      values_of<KD, E>(w[r], v);
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) s = fmaf(uu[e], v[r][e], s);
-#pragma unroll
-      for (int off = LPH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      for (int e = 0; e < E; ++e) s = fmaf(uu[e], v[e], s);
+      s = head_sum<LPH>(s);
       const int32_t tt = t + r;
-      if (lane % LPH == 0 && tt < t_end) scores[((int64_t)b * HKV + h) * max_tokens + tt] = tt < n ? s : 0.0f;
+      if (writer && tt < t_end) out[tt] = tt < n ? s : 0.0f;
     }
+  };
+  uint32_t wa[U][NW], wb[U][NW];
+  load(t0, wa);
+  for (int32_t t = t0; t < t_end; t += 2 * U) {
+    load(t + U < t_end ? t + U : t, wb);
+    score(t, wa);
+    if (t + U >= t_end) break;
+    load(t + 2 * U < t_end ? t + 2 * U : t + U, wa);
+    score(t + U, wb);
   }
 }
 
@@ -180,7 +225,7 @@ __global__ void __launch_bounds__(kSelectThreads) vl_select_kernel(const float *
   if (m > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       const uint32_t hi_mask = shift == 24 ? 0u : (~0u << (shift + 8));
-      hist[tid] = 0;
+      if (tid < 256) hist[tid] = 0;
       __syncthreads();
       for (int32_t t = tid; t < n_pre; t += kSelectThreads) {
         const uint32_t key = key_of(S[t]);
@@ -274,7 +319,7 @@ extern "C" kvq_status kvq_select_vertical_lines(const void *k, int32_t k_dtype, 
   if (!k || !q_tail || !n_tokens || !n_tail || !proxy || !scores || !token_class || !n_vl)
     return fail(KVQ_ERR_INVALID_ARG, "NULL buffer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 pgrid(batch * hkv), pblock(64);
+  const dim3 pgrid(batch * hkv), pblock(256);
   if (q_dtype == KVQ_F32)
     hipLaunchKernelGGL(vl_proxy_kernel<KVQ_F32>, pgrid, pblock, 0, s, q_tail, hkv, hq, max_tail, n_tail, proxy, dev_err);
   else if (q_dtype == KVQ_BF16)
