@@ -205,8 +205,11 @@ __global__ void __launch_bounds__(kSelectThreads) vl_select_kernel(const float *
                                                                    int32_t max_tokens, const int32_t *n_tokens,
                                                                    int32_t window, float rho, uint8_t *cls,
                                                                    int32_t *n_vl, int32_t *err) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_eq[kSelectThreads / 64];
+  constexpr int kWaves = kSelectThreads / 64;
+  __shared__ uint32_t hist[kWaves][256];  // one histogram per wave (the top bits of the keys
+                                          // of nearby scores collide: few distinct bins)
+  __shared__ uint32_t suffix[256];
+  __shared__ uint32_t wave_eq[kWaves];
   __shared__ uint32_t sel[2];  // threshold prefix, keys still needed at it
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / hkv;
@@ -220,32 +223,44 @@ __global__ void __launch_bounds__(kSelectThreads) vl_select_kernel(const float *
   const int32_t m = (int32_t)floor((double)rho * (double)n_pre + 0.5);
   const float *S = scores + row;
 
-  // Radix select of the m-th largest key, 8 bits a pass from the top.
+  // Radix select of the m-th largest key, 8 bits a pass from the top: per-wave
+  // histograms of the next digit among the keys that match the prefix so far, their
+  // per-bin totals, suffix sums over the bins (a log-step scan), and the one bin where
+  // the suffix sum first reaches the count still needed.
   uint32_t prefix = 0, need = (uint32_t)m;
   if (m > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       const uint32_t hi_mask = shift == 24 ? 0u : (~0u << (shift + 8));
-      if (tid < 256) hist[tid] = 0;
+      for (int i = tid; i < kWaves * 256; i += kSelectThreads) (&hist[0][0])[i] = 0;
       __syncthreads();
       for (int32_t t = tid; t < n_pre; t += kSelectThreads) {
         const uint32_t key = key_of(S[t]);
-        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t above = 0;
-        int bin = 255;
-        for (; bin > 0; --bin) {
-          if (above + hist[bin] >= need) break;
-          above += hist[bin];
+      if (tid < 256) {
+        uint32_t c = 0;
+        for (int w = 0; w < kWaves; ++w) c += hist[w][tid];
+        suffix[tid] = c;
+      }
+      __syncthreads();
+      for (int d = 1; d < 256; d <<= 1) {  // suffix[t] = sum of bins t .. 255
+        const uint32_t add = (tid < 256 && tid + d < 256) ? suffix[tid + d] : 0u;
+        __syncthreads();
+        if (tid < 256) suffix[tid] += add;
+        __syncthreads();
+      }
+      if (tid < 256) {
+        const uint32_t here = suffix[tid], next = tid < 255 ? suffix[tid + 1] : 0u;
+        if (here >= need && next < need) {
+          sel[0] = prefix | ((uint32_t)tid << shift);
+          sel[1] = need - next;
         }
-        sel[0] = prefix | ((uint32_t)bin << shift);
-        sel[1] = need - above;
       }
       __syncthreads();
       prefix = sel[0];
       need = sel[1];
-      __syncthreads();  // hist is cleared again next pass
+      __syncthreads();  // the histograms are cleared again next pass
     }
   }
   // Classes in token order: above the threshold, or at it among the first `need`.
