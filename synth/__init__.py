@@ -398,12 +398,13 @@ def qwen3_vl_agentic(seed=3, batch=8, lo=65536, hi=131072, device="cpu", chunk=8
 
 
 def hybrid_anchor(seed=4, batch=32, n_tokens=65536, device="cpu", window=128, staging=64,
-                  vl_ratio=0.05, layer=0):
+                  vl_ratio=0.05, layer=0, vl_positions=None):
     """Hybrid FP16-anchor decode (Llama-3.1-8B shape): Hq 32 / Hkv 8, one table per
     (request, KV head).  Per head: an INT4 prefix, FP16 vertical-line tokens (top 5 %
-    of the non-window prefix by a Zipf(1.1) column mass over randomly permuted ranks),
-    a 64-token FP16 staging buffer and a W = 128 FP16 window; each anchor segment starts
-    on its own page.  bf16 K, V ~ N(0,1)."""
+    of the non-window prefix by a Zipf(1.1) column mass over randomly permuted ranks,
+    or the given vl_positions[table]: sorted positions in the non-window prefix), a
+    64-token FP16 staging buffer and a W = 128 FP16 window; each anchor segment starts
+    on its own page.  bf16 K, V ~ N(0,1); table t holds rows t * n_tokens + position."""
     hq, hkv, H = 32, 8, 1
     n_tables = batch * hkv
     frozen = n_tokens - staging               # tokens present at the freeze point
@@ -421,10 +422,14 @@ def hybrid_anchor(seed=4, batch=32, n_tokens=65536, device="cpu", window=128, st
     calls = []
     ranks_mass = np.arange(1, nonwin + 1, dtype=np.float64) ** -1.1   # Zipf(1.1) by rank
     for t in range(n_tables):
-        r = np_rng(seed, 44, t)
-        rank_of_pos = r.permutation(nonwin)                # random rank per position
-        mass = ranks_mass[rank_of_pos]
-        vl = np.sort(np.argsort(-mass, kind="stable")[:n_vl])
+        if vl_positions is None:
+            r = np_rng(seed, 44, t)
+            rank_of_pos = r.permutation(nonwin)            # random rank per position
+            mass = ranks_mass[rank_of_pos]
+            vl = np.sort(np.argsort(-mass, kind="stable")[:n_vl])
+        else:
+            vl = np.asarray(vl_positions[t], np.int64)
+            assert vl.shape == (n_vl,) and np.all(np.diff(vl) > 0) and vl[0] >= 0 and vl[-1] < nonwin
         is_vl = np.zeros(nonwin, bool)
         is_vl[vl] = True
         base = t * n_tokens

@@ -95,3 +95,41 @@ def test_full_size_sampled():
     _say("full size: generating on the GPU")
     w = synth.vl_prefill(device="cuda")
     _check(w, requests=[3, 30])
+
+
+def test_selection_feeds_a_hybrid_cache():
+    """Select, freeze, append, decode: the GPU's vertical lines (from the keys of a
+    hybrid-anchor cache at its freeze point and 64 tail queries) become the FP16
+    anchors of the GPU cache, the oracle's own selection those of the oracle cache; the
+    two selections agree, and the decoded attention matches the oracle within TOL."""
+    from mixed_precision_quantized_amd import kvq
+    from oracle import oracle
+    from harness import DeviceRun, OracleRun, row_metric
+    batch, n_tokens, staging, window, hkv, hq = 2, 4096, 64, 128, 8, 32
+    frozen = n_tokens - staging
+    w0 = synth.hybrid_anchor(batch=batch, n_tokens=n_tokens)
+    k4 = w0.k.view(batch, hkv, n_tokens, 128)[:, :, :frozen].transpose(1, 2).contiguous()
+    q_tail = synth.randn((batch, 64, hq, 128), 4, 45).to(torch.bfloat16)
+    n_tok, n_tail = np.full(batch, frozen, np.int32), np.full(batch, 64, np.int32)
+    dev = "cuda"
+    _, _, cls, _ = kvq.select_vertical_lines(k4.to(dev), q_tail.to(dev), torch.as_tensor(n_tok, device=dev),
+                                             torch.as_tensor(n_tail, device=dev), window=window)
+    cls = cls.cpu().numpy()
+    _, ocls, _ = oracle.select_vl(k4.float().numpy(), q_tail.float().numpy(), n_tok, n_tail, window,
+                                  float(np.float32(0.05)))
+    assert np.array_equal(cls, ocls), "selections differ (a threshold tie)"
+    nonwin = frozen - window
+    assert np.all(cls[:, :, nonwin:frozen] == 2)
+    sets = lambda c: {b * hkv + h: np.flatnonzero(c[b, h, :nonwin] == 1) for b in range(batch)  # noqa: E731
+                      for h in range(hkv)}
+    wg = synth.hybrid_anchor(batch=batch, n_tokens=n_tokens, vl_positions=sets(cls))
+    wo = synth.hybrid_anchor(batch=batch, n_tokens=n_tokens, vl_positions=sets(ocls))
+    gpu, orc = DeviceRun(wg), OracleRun(wo)
+    torch.cuda.synchronize()
+    assert int(gpu.err.item()) == 0
+    ref, _ = orc.attend()
+    splits, offsets = gpu.plan(target_bytes=1 << 16)
+    out, _, _, _ = gpu.decode(splits, offsets)
+    err = row_metric(ref, out.cpu().numpy())
+    _say(f"  select -> freeze -> decode: {int((cls == 1).sum())} anchors, row error {err:.2e}")
+    assert err <= 2e-3
