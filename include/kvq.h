@@ -121,6 +121,61 @@ kvq_status kvq_route_tokens(const uint8_t *flags, int32_t n, uint8_t *cls_out,
                             int32_t *n_int2_groups, int32_t *n_int4, int32_t *n_fp16);
 
 /*
+ * Tri-axis token tags (TriAxialKV key design 1) [host].  Every token gets a tag
+ * s(t) = (temporal * KVQ_N_MODAL + modal) * KVQ_N_SEMANTIC + semantic, read in one
+ * pass over the token ids from the chat template's boundary tokens, named by the
+ * caller in `markers` (token id -> event; each id at most once):
+ *   semantic: 0 inst (system prompt, tool specs; also before any marker), 1 user,
+ *     2 assistant, 3 reasoning (between THINK_BEGIN / _END), 4 tool_call (between
+ *     TOOL_CALL_BEGIN / _END), 5 obs (tool or environment output), 6 delim (every
+ *     marker token itself).  A role event (SYSTEM, USER, ASSISTANT, OBSERVATION)
+ *     or END closes any open reasoning, tool-call or image span.
+ *   modal: 1 image between IMAGE_BEGIN and IMAGE_END (markers excluded), else 0.
+ *   temporal: each USER event starts a turn (tokens before the first are turn 0);
+ *     with T turns in all, a token of turn u gets min(T - u, 3): 0 current,
+ *     1 the turn before, 2 two before, 3 older.
+ * tokens [host] int32 [n]; tags [host] uint8 [n]; *n_turns (may be NULL) = T.
+ * Errors: INVALID_ARG (negative counts, NULL arrays, unknown event, an id named twice).
+ */
+enum { KVQ_N_TEMPORAL = 4, KVQ_N_MODAL = 2, KVQ_N_SEMANTIC = 7, KVQ_N_TAGS = 56 };
+enum {
+    KVQ_EV_SYSTEM = 0, KVQ_EV_USER = 1, KVQ_EV_ASSISTANT = 2, KVQ_EV_OBSERVATION = 3,
+    KVQ_EV_END = 4, KVQ_EV_THINK_BEGIN = 5, KVQ_EV_THINK_END = 6,
+    KVQ_EV_TOOL_CALL_BEGIN = 7, KVQ_EV_TOOL_CALL_END = 8,
+    KVQ_EV_IMAGE_BEGIN = 9, KVQ_EV_IMAGE_END = 10
+};
+typedef struct {
+    int32_t token_id;
+    int32_t event;  /* KVQ_EV_* */
+} kvq_tag_marker;
+
+kvq_status kvq_tag_tokens(const int32_t *tokens, int32_t n, const kvq_tag_marker *markers,
+                          int32_t n_markers, uint8_t *tags, int32_t *n_turns);
+
+/*
+ * Greedy width allocation (TriAxialKV key design 2) [host]: minimise sum_k D_k(b_k)
+ * over b_k in {2, 4} subject to sum_k N_k b_k <= budget_bits * sum_k N_k.  Every tag
+ * starts at 2 bits; tags with N_k > 0 are visited by decreasing
+ * rho_k = (D_k(2) - D_k(4)) / (2 N_k) (ties: lower k) and upgraded to 4 bits while
+ * the constraint holds; the walk stops at the first tag that would break it.
+ * d2, d4 [host] double [n_tags] (the distortion table), counts [host] int64
+ * [n_tags]; bits [host] uint8 [n_tags] = 2 or 4; *avg_bits (may be NULL) = the
+ * resulting average width.  Errors: INVALID_ARG (budget outside [2, 4], negative
+ * counts, NULL arrays).
+ */
+kvq_status kvq_allocate_bits(const double *d2, const double *d4, const int64_t *counts,
+                             int32_t n_tags, double budget_bits, uint8_t *bits,
+                             double *avg_bits);
+
+/*
+ * Per-token routing flags from tags and widths [host]: flags[i] = 0 (INT2) when
+ * bits[tags[i]] is 2, 1 (INT4) when it is 4 -- the input of kvq_route_tokens.
+ * Errors: INVALID_ARG (a tag >= n_tags or a width other than 2 / 4).
+ */
+kvq_status kvq_tag_flags(const uint8_t *tags, int32_t n, const uint8_t *bits, int32_t n_tags,
+                         uint8_t *flags);
+
+/*
  * Quantize and pack tokens into the pools (TriAxialKV key design 3; new decode
  * tokens are INT4 per key design 4; FP16 anchors per HyQuant's method).
  *   k, v [dev]: n_rows source rows; element (row r, head h, channel c) is at

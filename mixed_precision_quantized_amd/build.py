@@ -20,6 +20,7 @@ HIP = ["--offload-arch=" + ARCH, "-fno-gpu-flush-denormals-to-zero",
 
 SOURCES = [
     ("kvq_host.cpp", ["-ffp-contract=off"]),
+    ("kvq_tags.cpp", ["-ffp-contract=off"]),
     ("kvq_write.hip", HIP + ["-ffp-contract=off"]),
     # The decode kernels never rely on NaN semantics (the softmax runs from a finite
     # start, masked logits are -inf); without NaNs to honour, max needs no quieting and

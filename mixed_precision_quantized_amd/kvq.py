@@ -58,6 +58,9 @@ _P, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 _SIGS = {
     "kvq_block_bytes": ([_i32], ctypes.c_size_t),
     "kvq_route_tokens": ([_P, _i32, _P, _P, _P, _P], ctypes.c_int),
+    "kvq_tag_tokens": ([_P, _i32, _P, _i32, _P, _P], ctypes.c_int),
+    "kvq_allocate_bits": ([_P, _P, _P, _i32, ctypes.c_double, _P, _P], ctypes.c_int),
+    "kvq_tag_flags": ([_P, _i32, _P, _i32, _P], ctypes.c_int),
     "kvq_quantize_append": ([_P, _P, _P, _i32, _i64, _i64, _i64, _i32, _P, _P, _i32, _P, _P, _i32, _P, _P,
                              _P, _P], ctypes.c_int),
     "kvq_reorder_pages": ([_P, _P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
@@ -148,6 +151,48 @@ def route_tokens(flags: np.ndarray):
     _check(_lib.kvq_route_tokens(_hptr(flags), flags.shape[0], _hptr(cls), ctypes.byref(n2),
                                  ctypes.byref(n4), ctypes.byref(n16)), "kvq_route_tokens")
     return cls, n2.value, n4.value, n16.value
+
+
+N_TEMPORAL, N_MODAL, N_SEMANTIC, N_TAGS = 4, 2, 7, 56
+(EV_SYSTEM, EV_USER, EV_ASSISTANT, EV_OBSERVATION, EV_END, EV_THINK_BEGIN, EV_THINK_END,
+ EV_TOOL_CALL_BEGIN, EV_TOOL_CALL_END, EV_IMAGE_BEGIN, EV_IMAGE_END) = range(11)
+
+
+class _MarkerC(ctypes.Structure):
+    _fields_ = [("token_id", ctypes.c_int32), ("event", ctypes.c_int32)]
+
+
+def tag_tokens(tokens: np.ndarray, markers):
+    """tokens int32 [n]; markers: {token id: EV_*}.  Returns (tags uint8 [n], turns)."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    arr = (_MarkerC * max(1, len(markers)))(*[_MarkerC(int(t), int(e)) for t, e in markers.items()])
+    tags = np.zeros(tokens.shape[0], np.uint8)
+    turns = _i32()
+    _check(_lib.kvq_tag_tokens(_hptr(tokens), tokens.shape[0], ctypes.cast(arr, _P), len(markers), _hptr(tags),
+                               ctypes.byref(turns)), "kvq_tag_tokens")
+    return tags, turns.value
+
+
+def allocate_bits(d2, d4, counts, budget_bits: float):
+    """Greedy 2 / 4-bit widths per tag; returns (bits uint8 [n_tags], average width)."""
+    d2 = np.ascontiguousarray(d2, np.float64).reshape(-1)
+    d4 = np.ascontiguousarray(d4, np.float64).reshape(-1)
+    counts = np.ascontiguousarray(counts, np.int64).reshape(-1)
+    bits = np.zeros(counts.shape[0], np.uint8)
+    avg = ctypes.c_double()
+    _check(_lib.kvq_allocate_bits(_hptr(d2), _hptr(d4), _hptr(counts), counts.shape[0], float(budget_bits),
+                                  _hptr(bits), ctypes.byref(avg)), "kvq_allocate_bits")
+    return bits, avg.value
+
+
+def tag_flags(tags: np.ndarray, bits: np.ndarray) -> np.ndarray:
+    """Routing flags (0 INT2, 1 INT4) of tagged tokens under per-tag widths."""
+    tags = np.ascontiguousarray(tags, np.uint8)
+    bits = np.ascontiguousarray(bits, np.uint8)
+    flags = np.zeros(tags.shape[0], np.uint8)
+    _check(_lib.kvq_tag_flags(_hptr(tags), tags.shape[0], _hptr(bits), bits.shape[0], _hptr(flags)),
+           "kvq_tag_flags")
+    return flags
 
 
 def quantize_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, rows4=None, slots4=None,

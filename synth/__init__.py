@@ -639,3 +639,57 @@ def vl_prefill(seed=6, batch=32, n_tokens=65536, hkv=8, hq=32, max_tail=64, leng
     return PrefillKQ(k.to(dtype).contiguous(), q.to(dtype).contiguous(), lens.astype(np.int32),
                      tails.astype(np.int32), f"{batch} requests, {mt} tokens max, Hq {hq} / Hkv {hkv}, "
                      f"{max_tail} tail queries, {planted:.0%} planted lines")
+
+
+@dataclasses.dataclass
+class TokenStream:
+    """Token ids of a synthetic agentic conversation and the template's boundary ids."""
+    tokens: np.ndarray       # int32 [n]
+    markers: dict            # token id -> event name (system, user, assistant, ...)
+
+
+_STREAM_EVENTS = ("system", "user", "assistant", "observation", "end", "think_begin", "think_end",
+                  "tool_call_begin", "tool_call_end", "image_begin", "image_end")
+
+
+def agentic_token_stream(seed=0, n_turns=8, tokens_per_turn=400, vocab=900) -> TokenStream:
+    """A seeded multi-turn agent conversation as token ids: a system prompt, then per turn
+    a user message (sometimes with an image span), an assistant reply with think and
+    tool-call spans, and tool observations (sometimes with images).  Boundary tokens are
+    ids vocab .. vocab + 10; about 5 % of spans are left open or closed twice, as
+    truncated or malformed template output would."""
+    rng = np_rng(seed, 71)
+    markers = {vocab + i: e for i, e in enumerate(_STREAM_EVENTS)}
+    mid = {e: vocab + i for i, e in enumerate(_STREAM_EVENTS)}
+    out = []
+    text = lambda n: out.extend(rng.integers(0, vocab, max(1, int(n))).tolist())  # noqa: E731
+
+    def span(name, n):
+        out.append(mid[name + "_begin"])
+        text(n)
+        if rng.random() > 0.05:
+            out.append(mid[name + "_end"])
+        if rng.random() < 0.05:
+            out.append(mid[name + "_end"])
+
+    out.append(mid["system"]); text(tokens_per_turn); out.append(mid["end"])
+    for _ in range(n_turns):
+        m = tokens_per_turn
+        out.append(mid["user"]); text(rng.exponential(m / 4))
+        if rng.random() < 0.3:
+            span("image", rng.exponential(m / 3))
+        out.append(mid["end"])
+        out.append(mid["assistant"])
+        if rng.random() < 0.7:
+            span("think", rng.exponential(m / 4))
+        text(rng.exponential(m / 8))
+        for _ in range(int(rng.integers(0, 3))):
+            span("tool_call", rng.exponential(m / 16))
+            out.append(mid["end"])
+            out.append(mid["observation"]); text(rng.exponential(m / 4))
+            if rng.random() < 0.2:
+                span("image", rng.exponential(m / 4))
+            out.append(mid["end"])
+            out.append(mid["assistant"]); text(rng.exponential(m / 16))
+        out.append(mid["end"])
+    return TokenStream(np.array(out, np.int32), markers)
