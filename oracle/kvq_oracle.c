@@ -462,6 +462,113 @@ int orc_select_vl(const float *k, const float *q_tail, int32_t batch,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Prefill attention with an INT8 prefix (HyQuant Algorithm 2)               */
+/* ------------------------------------------------------------------------ */
+
+#define QTILE 64
+
+/* Symmetric INT8 scale of a tile: fp32 max |x| / 127 (no contraction: -ffp-contract=off). */
+static float int8_scale(float amax)
+{
+    volatile float q = amax / 127.0f;
+    return q;
+}
+
+static int8_t int8_code(float x, float s)
+{
+    if (s == 0.0f) return 0;
+    volatile float r = x / s;
+    float c = rintf(r);
+    if (c > 127.0f) c = 127.0f;
+    if (c < -127.0f) c = -127.0f;
+    return (int8_t)c;
+}
+
+int orc_prefill_attend(const float *q, const float *k, const float *v,
+                       int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
+                       const int32_t *n_tokens, const uint8_t *cls, int32_t window,
+                       double *out, int8_t *q_codes, float *q_scales,
+                       int8_t *k_codes, float *k_scales)
+{
+    if (!q || !k || !v || !n_tokens || !out || !q_codes || !q_scales || !k_codes || !k_scales ||
+        batch < 0 || n_max < 0 || hq <= 0 || hkv <= 0 || hq % hkv || window < 0)
+        return ORC_EARG;
+    const int32_t g = hq / hkv, tiles = (n_max + QTILE - 1) / QTILE;
+    for (int32_t b = 0; b < batch; ++b)
+        if (n_tokens[b] < 0 || n_tokens[b] > n_max) return ORC_ERANGE;
+#define QI(b, t, j, c) ((((int64_t)(b) * n_max + (t)) * hq + (j)) * D + (c))
+#define KI(b, t, h, c) ((((int64_t)(b) * n_max + (t)) * hkv + (h)) * D + (c))
+    /* the INT8 tiles: queries per query head, keys per KV head (vertical lines out) */
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t n = n_tokens[b];
+        for (int32_t tile = 0; tile < tiles; ++tile) {
+            const int32_t t0 = tile * QTILE, t1 = t0 + QTILE < n ? t0 + QTILE : n;
+            for (int32_t j = 0; j < hq; ++j) {
+                float amax = 0.0f;
+                for (int32_t t = t0; t < t1; ++t)
+                    for (int c = 0; c < D; ++c) amax = fmaxf(amax, fabsf(q[QI(b, t, j, c)]));
+                const float s = int8_scale(amax);
+                q_scales[((int64_t)b * hq + j) * tiles + tile] = s;
+                for (int32_t t = t0; t < t0 + QTILE && t < n_max; ++t)
+                    for (int c = 0; c < D; ++c)
+                        q_codes[QI(b, t, j, c)] = t < n ? int8_code(q[QI(b, t, j, c)], s) : 0;
+            }
+            for (int32_t h = 0; h < hkv; ++h) {
+                const uint8_t *vl = cls ? cls + ((int64_t)b * hkv + h) * n_max : NULL;
+                float amax = 0.0f;
+                for (int32_t t = t0; t < t1; ++t)
+                    if (!(vl && vl[t] == 1))
+                        for (int c = 0; c < D; ++c) amax = fmaxf(amax, fabsf(k[KI(b, t, h, c)]));
+                const float s = int8_scale(amax);
+                k_scales[((int64_t)b * hkv + h) * tiles + tile] = s;
+                for (int32_t t = t0; t < t0 + QTILE && t < n_max; ++t)
+                    for (int c = 0; c < D; ++c)
+                        k_codes[KI(b, t, h, c)] = t < n ? int8_code(k[KI(b, t, h, c)], s) : 0;
+            }
+        }
+    }
+    /* attention: one softmax per (b, t, j) over the keys k <= t */
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    double *x = (double *)malloc(sizeof(double) * (size_t)(n_max > 0 ? n_max : 1));
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t n = n_tokens[b];
+        for (int32_t j = 0; j < hq; ++j) {
+            const int32_t h = j / g;
+            const uint8_t *vl = cls ? cls + ((int64_t)b * hkv + h) * n_max : NULL;
+            for (int32_t t = 0; t < n_max; ++t) {
+                double *o = out + QI(b, t, j, 0);
+                for (int c = 0; c < D; ++c) o[c] = 0.0;
+                if (t >= n) continue;
+                const double sq = q_scales[((int64_t)b * hq + j) * tiles + t / QTILE];
+                double mx = -INFINITY;
+                for (int32_t kk = 0; kk <= t; ++kk) {
+                    double dot = 0.0;
+                    if ((vl && vl[kk] == 1) || kk > t - window) {
+                        for (int c = 0; c < D; ++c) dot += (double)q[QI(b, t, j, c)] * (double)k[KI(b, kk, h, c)];
+                    } else {
+                        int64_t idot = 0;
+                        for (int c = 0; c < D; ++c) idot += (int64_t)q_codes[QI(b, t, j, c)] * k_codes[KI(b, kk, h, c)];
+                        dot = sq * (double)k_scales[((int64_t)b * hkv + h) * tiles + kk / QTILE] * (double)idot;
+                    }
+                    x[kk] = dot * inv_sqrt_d;
+                    if (x[kk] > mx) mx = x[kk];
+                }
+                double den = 0.0;
+                for (int32_t kk = 0; kk <= t; ++kk) den += exp(x[kk] - mx);
+                for (int32_t kk = 0; kk <= t; ++kk) {
+                    const double p = exp(x[kk] - mx) / den;
+                    for (int c = 0; c < D; ++c) o[c] += p * (double)v[KI(b, kk, h, c)];
+                }
+            }
+        }
+    }
+    free(x);
+#undef QI
+#undef KI
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantization of one token (fp64, exact)                                 */
 /* ------------------------------------------------------------------------ */
 
