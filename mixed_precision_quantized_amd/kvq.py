@@ -65,6 +65,8 @@ _SIGS = {
                              _P, _P], ctypes.c_int),
     "kvq_reorder_pages": ([_P, _P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
     "kvq_compact_slots": ([_P, _P, _i32, _i32, _P, _P, _P, _P, _P], ctypes.c_int),
+    "kvq_prefill_attn": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P],
+                         ctypes.c_int),
     "kvq_select_vertical_lines": ([_P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32,
                                    ctypes.c_float, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "kvq_decode_attn": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P, _P,
@@ -259,6 +261,37 @@ def select_vertical_lines(k: torch.Tensor, q_tail: torch.Tensor, n_tokens: torch
                                           float(rho), _dptr(proxy), _dptr(scores), _dptr(cls), _dptr(n_vl),
                                           _dptr(dev_err), _stream(stream)), "kvq_select_vertical_lines")
     return out
+
+
+def prefill_workspace(batch: int, n_max: int, hq: int, hkv: int, device="cuda"):
+    """Workspace and output of prefill_attn: (q_codes, q_scales, k_codes, k_scales, v_t, out)."""
+    tiles = n_max // 64
+    return (torch.empty((batch, n_max, hq, HEAD_DIM), dtype=torch.int8, device=device),
+            torch.empty((batch, hq, tiles), dtype=torch.float32, device=device),
+            torch.empty((batch, n_max, hkv, HEAD_DIM), dtype=torch.int8, device=device),
+            torch.empty((batch, hkv, tiles), dtype=torch.float32, device=device),
+            torch.empty((batch, hkv, HEAD_DIM, n_max), dtype=torch.float16, device=device),
+            torch.empty((batch, n_max, hq, HEAD_DIM), dtype=torch.float32, device=device))
+
+
+def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens: torch.Tensor,
+                 token_class: Optional[torch.Tensor] = None, window: int = 128, ws=None, dev_err=None,
+                 stream=None):
+    """q [batch, n_max, hq, 128], k, v [batch, n_max, hkv, 128] bf16 (device); token_class
+    uint8 [batch, hkv, n_max] or None.  Returns prefill_workspace's tuple, filled."""
+    assert q.dtype == k.dtype == v.dtype == torch.bfloat16
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    batch, n_max, hq = q.shape[:3]
+    hkv = k.shape[2]
+    if ws is None:
+        ws = prefill_workspace(batch, n_max, hq, hkv, q.device)
+    qc, qs, kc, ks, vt, out = ws
+    if token_class is not None:
+        assert token_class.dtype == torch.uint8 and token_class.is_contiguous()
+    _check(_lib.kvq_prefill_attn(_dptr(q), _dptr(k), _dptr(v), BF16, batch, n_max, hq, hkv, _dptr(n_tokens),
+                                 _dptr(token_class), window, _dptr(qc), _dptr(qs), _dptr(kc), _dptr(ks),
+                                 _dptr(vt), _dptr(out), _dptr(dev_err), _stream(stream)), "kvq_prefill_attn")
+    return ws
 
 
 def decode_attn(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, table_kind: int,

@@ -693,3 +693,18 @@ def agentic_token_stream(seed=0, n_turns=8, tokens_per_turn=400, vocab=900) -> T
             out.append(mid["assistant"]); text(rng.exponential(m / 16))
         out.append(mid["end"])
     return TokenStream(np.array(out, np.int32), markers)
+
+
+def prefill_qkv(seed=7, batch=2, n_max=256, hq=8, hkv=2, lengths=None, vl_frac=0.05, device="cpu"):
+    """Prompt queries, keys and values (bf16, ~N(0,1); keys of a few seeded channels
+    x4, an outlier pattern INT8 tiles must carry), per-request lengths (default n_max),
+    and seeded vertical-line flags (uint8 [batch, hkv, n_max], 1 for vl_frac of the
+    positions) for the prefill operator."""
+    lens = np.full(batch, n_max, np.int32) if lengths is None else np.asarray(lengths, np.int32)
+    q = randn((batch, n_max, hq, HEAD_DIM), seed, 81, device=device)
+    k = randn((batch, n_max, hkv, HEAD_DIM), seed, 82, device=device)
+    v = randn((batch, n_max, hkv, HEAD_DIM), seed, 83, device=device)
+    ch = np_rng(seed, 84).choice(HEAD_DIM, 4, replace=False)
+    k[..., torch.as_tensor(ch, device=device)] *= 4.0
+    cls = (np_rng(seed, 85).random((batch, hkv, n_max)) < vl_frac).astype(np.uint8)
+    return _bf16(q).contiguous(), _bf16(k).contiguous(), _bf16(v).contiguous(), lens, cls

@@ -1,0 +1,72 @@
+"""GPU prefill attention with an INT8 prefix (HyQuant Algorithm 2) through the C ABI
+against the oracle: INT8 codes and tile scales bit-exact (both sides divide in IEEE
+fp32), outputs within 2e-3 by the per-row metric (rows = (request, position, query
+head) below the request's length)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _say(*a):
+    print("[gpu-prefill]", *a, flush=True)
+
+
+def _case(name, batch, n_max, hq, hkv, lengths, window, vl_frac=0.05, with_cls=True, seed=7):
+    from mixed_precision_quantized_amd import kvq
+    from oracle import oracle
+    from harness import row_metric
+    _say(name)
+    q, k, v, lens, cls = synth.prefill_qkv(seed, batch, n_max, hq, hkv, lengths, vl_frac)
+    dev = "cuda"
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    c_dev = torch.as_tensor(cls, device=dev).contiguous() if with_cls else None
+    qc, qs, kc, ks, vt, out = kvq.prefill_attn(q.to(dev), k.to(dev), v.to(dev), torch.as_tensor(lens, device=dev),
+                                               c_dev, window=window, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref, rqc, rqs, rkc, rks = oracle.prefill_attend(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens,
+                                                    cls if with_cls else None, window)
+    assert np.array_equal(qs.cpu().numpy(), rqs) and np.array_equal(ks.cpu().numpy(), rks)
+    assert np.array_equal(qc.cpu().numpy(), rqc) and np.array_equal(kc.cpu().numpy(), rkc)
+    got = out.cpu().numpy()
+    rows_ref, rows_got = [], []
+    for b in range(batch):
+        rows_ref.append(ref[b, : lens[b]].reshape(-1, 128))
+        rows_got.append(got[b, : lens[b]].reshape(-1, 128))
+        assert not got[b, lens[b]:].any()
+    e = row_metric(np.concatenate(rows_ref), np.concatenate(rows_got))
+    _say(f"  {name}: row error {e:.2e}")
+    assert e <= TOL
+    return e
+
+
+def test_small_mixed_segments():
+    _case("b2 n256 g4 W64", 2, 256, 8, 2, [256, 150], window=64)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 2)])
+def test_gqa_ratios(hq, hkv):
+    _case(f"g={hq // hkv}", 1, 192, hq, hkv, [181], window=32)
+
+
+def test_limits():
+    """Window covering the whole prompt (all full precision); no window and no vertical
+    line (all INT8); every position a vertical line."""
+    _case("all full precision", 1, 128, 4, 2, [128], window=128)
+    _case("all INT8", 1, 128, 4, 2, [120], window=0, with_cls=False)
+    _case("all vertical lines", 1, 128, 4, 2, [128], window=0, vl_frac=1.0)
+
+
+def test_bad_length_is_reported():
+    from mixed_precision_quantized_amd import kvq
+    q, k, v, lens, cls = synth.prefill_qkv(1, 2, 64, 4, 2)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    *_, out = kvq.prefill_attn(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(np.array([64, 65], np.int32),
+                               device="cuda"), None, window=16, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == kvq.DEVERR_RANGE and not out[1].any()
