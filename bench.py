@@ -131,9 +131,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["vl_select"], default="qwen3_8b",
-                    help="a decode workload, or vl_select: vertical-line selection + FREEZE routing at the "
-                         "hybrid-anchor prefill shape")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["vl_select", "prefill"], default="qwen3_8b",
+                    help="a decode workload; vl_select: vertical-line selection + FREEZE routing at the "
+                         "hybrid-anchor prefill shape; prefill: INT8-prefix prefill attention")
+    ap.add_argument("--prefill-tokens", type=int, default=16384, help="prompt length of the prefill workload")
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--splits-per-head", type=int, default=0,
                     help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
@@ -164,6 +165,8 @@ def main():
 
     if args.workload == "vl_select":
         return bench_vl(args)
+    if args.workload == "prefill":
+        return bench_prefill(args)
     suffix, default_layers, description = WORKLOADS[args.workload]
     make = getattr(synth, args.workload)
     layers = args.layers or default_layers
@@ -445,6 +448,77 @@ def bench_vl(args):
                                   "sample": f"2 of {batch} requests (bf16-sized bytes), fp64 scores and a "
                                             f"sort per head, one thread, {reps} passes in {dt:.1f} s"}
         log(f"cpu oracle {result['cpu_baseline']['value']} GB/s on 1 thread ({dt:.1f} s)")
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args):
+    """INT8-prefix prefill attention (HyQuant Algorithm 2) at the Llama-3.1-8B shape: one
+    request of --prefill-tokens positions, Hq 32 / Hkv 8, bf16, 5 % vertical lines, a
+    128-token window.  Algorithmic work per call: the causal Q K^T and P V products,
+    2 x 2 x 128 x n (n + 1) / 2 x Hq operations (INT8 ones for the quantized pairs,
+    bf16 / fp16 ones for the rest), against the bf16 dense MFMA peak."""
+    import numpy as np
+    import torch
+
+    import synth
+    from mixed_precision_quantized_amd import kvq
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    n, hq, hkv = args.prefill_tokens, 32, 8
+    q, k, v, lens, cls = synth.prefill_qkv(seed=8, batch=1, n_max=n, hq=hq, hkv=hkv, device=dev)
+    nt = torch.as_tensor(lens, device=dev)
+    cd = torch.as_tensor(cls, device=dev).contiguous()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = kvq.prefill_workspace(1, n, hq, hkv, dev)
+    stream = torch.cuda.Stream()
+    call = lambda: kvq.prefill_attn(q, k, v, nt, cd, window=128, ws=ws, dev_err=err, stream=stream)  # noqa: E731
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            call()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    steps = max(1, args.steps // 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / steps
+    flops = 2 * 2 * 128 * n * (n + 1) / 2 * hq
+    tflops = flops / sec / 1e12
+    log(f"prefill: {n} tokens, Hq {hq} / Hkv {hkv}: {sec * 1e3:.2f} ms per call, {tflops:.1f} TFLOP/s")
+    result = {
+        "metric": "INT8-prefix prefill attention TFLOP/s (HyQuant Alg. 2), Llama-3.1-8B shape",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 / bf16 Q K^T, fp16 P V, fp32 softmax", "data": "synthetic",
+        "config": {"workload": f"prefill attention: 1 request x {n} tokens, Hq {hq} / Hkv {hkv}, 5% vertical lines, "
+                               "window 128", "tokens": n, "hq": hq, "hkv": hkv, "flops_per_call": flops},
+        "roofline": {"bound": "mfma", "kernel": "pf_attn_kernel (+ quantize, V transpose)",
+                     "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        m = 1024  # a prompt prefix the fp64 oracle finishes in seconds
+        qq, kk, vv = (x[:, :m].float().cpu().numpy() for x in (q, k, v))
+        cc = np.ascontiguousarray(cls[:, :, :m])
+        reps, t = 0, time.perf_counter()
+        while True:
+            oracle.prefill_attend(qq, kk, vv, [m], cc, 128)
+            reps += 1
+            dt = time.perf_counter() - t
+            if dt >= CPU_SECONDS:
+                break
+        f = 2 * 2 * 128 * m * (m + 1) / 2 * hq
+        result["cpu_baseline"] = {"value": round(f * reps / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                                  "kind": "oracle", "sample": f"the first {m} positions, fp64, one thread, "
+                                                              f"{reps} passes in {dt:.1f} s"}
+        log(f"cpu oracle {result['cpu_baseline']['value']} TFLOP/s on 1 thread ({dt:.1f} s)")
     print(json.dumps(result), flush=True)
 
 
