@@ -267,6 +267,12 @@ kvq_status kvq_select_vertical_lines(const void *k, int32_t k_dtype, const void 
                                      void *stream);
 
 /*
+ * Bytes of scratch kvq_prefill_attn needs for these sizes (0 for sizes it rejects).
+ * Host only.
+ */
+size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_max, int32_t hkv);
+
+/*
  * Prefill attention with an INT8 prefix (HyQuant Algorithm 2).  For request b
  * (n = n_tokens[b] <= n_max prompt positions), query head j (KV head h = j / g)
  * and query position t < n, over the keys k <= t: a key is read in full
@@ -278,18 +284,23 @@ kvq_status kvq_select_vertical_lines(const void *k, int32_t k_dtype, const void 
  * maximum); scale s = fl32(max |x| / 127), code = clamp(rint(fl32(x / s)), -127,
  * 127) (0 when s = 0); the logit of an INT8 pair is s_Q s_K (q_code . k_code).
  *   q [dev] bf16 [batch][n_max][hq][128]; k, v [dev] bf16 [batch][n_max][hkv][128]
- *   (|v| < 65504); n_max a multiple of 64.  Workspace and outputs [dev]: q_codes
- *   int8 like q, q_scales float [batch][hq][n_max/64], k_codes int8 like k,
- *   k_scales float [batch][hkv][n_max/64], v_t 2-byte [batch][hkv][128][n_max]
- *   (V transposed, fp16), out float [batch][n_max][hq][128] (0 for t >= n).
- * Errors: INVALID_ARG, UNSUPPORTED (dtype other than KVQ_BF16), HIP; a request
- * whose n_tokens is out of range is treated as empty (KVQ_DEVERR_RANGE).
+ *   (|v| < 65504); n_max a multiple of 64; g = hq / hkv in {1, 2, 4, 8, 16}.
+ *   Outputs [dev]: q_codes int8 like q, q_scales float [batch][hq][n_max/64],
+ *   k_codes int8 like k, k_scales float [batch][hkv][n_max/64], out float
+ *   [batch][n_max][hq][128] (0 for t >= n).  workspace [dev]: at least
+ *   kvq_prefill_workspace_bytes(batch, n_max, hkv) bytes of scratch (V transposed
+ *   to fp16, the vertical-line lists and their gathered K and V), 256-byte aligned,
+ *   owned by the caller; its contents between calls mean nothing.
+ * Errors: INVALID_ARG, UNSUPPORTED (dtype other than KVQ_BF16, another g, sizes
+ * past 32-bit offsets), CAPACITY (workspace too small), HIP; a request whose
+ * n_tokens is out of range is treated as empty (KVQ_DEVERR_RANGE).
  */
 kvq_status kvq_prefill_attn(const void *q, const void *k, const void *v, int32_t dtype,
                             int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
                             const int32_t *n_tokens, const uint8_t *token_class,
                             int32_t window, int8_t *q_codes, float *q_scales,
-                            int8_t *k_codes, float *k_scales, void *v_t, float *out,
+                            int8_t *k_codes, float *k_scales, void *workspace,
+                            size_t workspace_bytes, float *out,
                             int32_t *dev_err, void *stream);
 
 /*

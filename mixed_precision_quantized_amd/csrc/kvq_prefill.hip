@@ -8,14 +8,27 @@
 // quantized: it enters P.V as fp16 (exact for bf16 values in fp16's normal range), with
 // fp16 weights (bf16 weights would lose too much for the 2e-3 bar).
 //
-// Three launches: the INT8 codes and scales (one work group per 64-position tile and
-// head); V transposed to fp16 [b][h][channel][position] so the P.V operand reads whole
-// channels; the attention: one wave per (request, query head, 16 query positions), 32
-// keys a step, S^T = K Q^T on MFMA (i32 16x16x64 for the INT8 pairs, f32 16x16x32 bf16
-// for the full-precision pairs, each only when the step has such a pair), so a lane holds
-// its query's scores in the layout the P operand of O^T = V^T P^T wants.
+// The three segments of the scan are three key lists:
+//   INT8    keys k <= t - W that are not vertical lines: K codes, and V^T with the
+//           vertical-line columns zeroed, so their weights drop out of P.V; their
+//           softmax weights enter the row sum through a 0 / 1 keep mask;
+//   VL      the vertical lines k <= t, gathered per KV head into a compact list (bf16
+//           K rows, fp16 V^T columns, positions);
+//   window  keys t - W < k <= t that are not vertical lines, bf16 K.
+// Their union is every key k <= t, each in the precision the method gives it.
+//
+// Launches: INT8 codes and scales (one work group per 64-position tile and head); V^T
+// with the keep mask; the vertical-line list (one work group per request and KV head);
+// its gather; the attention.  An attention work group (256 threads) takes one request,
+// one KV head and 256 / g positions of all g of its query heads: 16 column blocks of 16
+// (position, head) rows, four per wave.  K and V^T stages of 64 keys go to LDS by
+// LDS-bound global loads, double-buffered across all three segments; S^T = K Q^T on
+// MFMA (i32 16x16x64 for INT8, f32 16x16x32 bf16 otherwise) puts a lane's scores where
+// the P operand of O^T = V^T P^T wants them (f32 16x16x32 f16).  The softmax rescales
+// lazily: the running maximum moves only when a score exceeds it by 2^8.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -25,14 +38,16 @@
 namespace kvq {
 namespace {
 
-constexpr int kTile = 64;       // INT8 tile (positions)
-constexpr int kQBlock = 16;     // query positions per wave
-constexpr int kKStep = 32;      // keys per step
+constexpr int kTile = 64;       // INT8 tile = LDS stage (positions)
+constexpr int kGroupRows = 256; // (position, query head) rows per attention work group
+constexpr float kLazy = 8.0f;   // log2 headroom of the running maximum
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) uint8_t *gbytes;
 
 __device__ __forceinline__ void report(int32_t *err, int32_t bit) {
   if (err) atomicOr(err, bit);
@@ -44,10 +59,15 @@ struct PfArgs {
   const uint16_t *q, *k, *v;     // bf16 [batch][n_max][heads][128]
   const uint8_t *cls;            // [batch][hkv][n_max] (1 = vertical line) or null
   const int32_t *n_tokens;
-  int32_t batch, n_max, hq, hkv, window, tiles;
+  int32_t batch, n_max, hq, hkv, g, window, tiles;
   int8_t *q_codes, *k_codes;     // like q, k
   float *q_scales, *k_scales;    // [batch][hq][tiles], [batch][hkv][tiles]
-  uint16_t *vt;                  // fp16 [batch][hkv][128][n_max]
+  uint16_t *vt;                  // fp16 [batch][hkv][128][n_max]; vertical lines, t >= n: 0
+  float *keep;                   // [batch][hkv][n_max]: 1 for live keys that are not lines
+  int32_t *vl_pos;               // [batch][hkv][n_max]: line positions in order, then INT32_MAX
+  int32_t *vl_cnt;               // [batch][hkv][tiles]: lines at positions < 64 (tile + 1)
+  uint16_t *vl_k;                // bf16 [batch][hkv][n_max][128]: line K rows, then 0
+  uint16_t *vl_vt;               // fp16 [batch][hkv][128][n_max]: line V columns, then 0
   float *out;                    // [batch][n_max][hq][128]
   int32_t *err;
 };
@@ -112,18 +132,28 @@ __global__ void __launch_bounds__(256) pf_quant_kernel(PfArgs a) {
 }
 
 // V [b][t][h][c] (bf16) -> vt [b][h][c][t] (fp16, exact in fp16's normal range) through
-// LDS, 64 positions x 128 channels a group; positions at or past the request's length
-// are written as 0.
+// LDS, 64 positions x 128 channels a group; vertical lines and positions at or past the
+// request's length are written as 0.  Also the keep mask of the INT8 and window
+// segments: 1 for live positions that are not vertical lines.
 __global__ void __launch_bounds__(256) pf_vt_kernel(PfArgs a) {
   __shared__ uint16_t tileb[kTile][kHeadDim + 2];
+  __shared__ uint8_t kept[kTile];
   const int tid = threadIdx.x, tile = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
   int32_t n = checked_n(a, b);
   if (n < 0) n = 0;
+  const int64_t bh = (int64_t)b * a.hkv + h;
+  if (tid < kTile) {
+    const int t = tile * kTile + tid;
+    const bool k = t < n && !(a.cls && a.cls[bh * a.n_max + t] == 1);
+    kept[tid] = k ? 1 : 0;
+    a.keep[bh * a.n_max + t] = k ? 1.0f : 0.0f;
+  }
+  __syncthreads();
   for (int i = tid; i < kTile * kHeadDim / 2; i += 256) {  // 2 channels per step
     const int r = i / (kHeadDim / 2), c = 2 * (i % (kHeadDim / 2));
     const int t = tile * kTile + r;
     uint32_t w = 0;
-    if (t < n) w = *reinterpret_cast<const uint32_t *>(a.v + (((int64_t)b * a.n_max + t) * a.hkv + h) * kHeadDim + c);
+    if (kept[r]) w = *reinterpret_cast<const uint32_t *>(a.v + (((int64_t)b * a.n_max + t) * a.hkv + h) * kHeadDim + c);
     tileb[r][c] = __builtin_bit_cast(uint16_t, (_Float16)bf16_value((uint16_t)(w & 0xFFFFu)));
     tileb[r][c + 1] = __builtin_bit_cast(uint16_t, (_Float16)bf16_value((uint16_t)(w >> 16)));
   }
@@ -131,140 +161,432 @@ __global__ void __launch_bounds__(256) pf_vt_kernel(PfArgs a) {
   for (int i = tid; i < kHeadDim * kTile / 2; i += 256) {  // 2 positions per step
     const int c = i / (kTile / 2), r = 2 * (i % (kTile / 2));
     const uint32_t w = (uint32_t)tileb[r][c] | ((uint32_t)tileb[r + 1][c] << 16);
-    *reinterpret_cast<uint32_t *>(a.vt + (((int64_t)b * a.hkv + h) * kHeadDim + c) * a.n_max + tile * kTile + r) = w;
+    *reinterpret_cast<uint32_t *>(a.vt + (bh * kHeadDim + c) * a.n_max + tile * kTile + r) = w;
   }
+}
+
+// The vertical-line list of one (request, KV head): positions t < n with class 1, in
+// order, then INT32_MAX up to n_max; vl_cnt[tile] = lines at positions < 64 (tile + 1).
+constexpr int kScanThreads = 1024;
+__global__ void __launch_bounds__(kScanThreads) pf_vl_scan_kernel(PfArgs a) {
+  __shared__ int32_t wsum[kScanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x / a.hkv;
+  const int64_t bh = blockIdx.x;
+  int32_t n = checked_n(a, b);
+  if (n < 0) n = 0;
+  int32_t *pos = a.vl_pos + bh * a.n_max;
+  int32_t running = 0;
+  for (int base = 0; base < a.n_max; base += kScanThreads) {
+    const int t = base + tid;
+    const bool f = t < n && a.cls && a.cls[bh * a.n_max + t] == 1;
+    const uint64_t m = __ballot(f);
+    const int below = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wv] = __popcll(m);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kScanThreads / 64; ++i) {
+      before += i < wv ? wsum[i] : 0;
+      total += wsum[i];
+    }
+    if (f) pos[running + before + below] = t;
+    if (t < a.n_max && (t & (kTile - 1)) == kTile - 1)
+      a.vl_cnt[bh * a.tiles + t / kTile] = running + before + below + (f ? 1 : 0);
+    running += total;
+    __syncthreads();
+  }
+  for (int i = running + tid; i < a.n_max; i += kScanThreads) pos[i] = INT32_MAX;
+}
+
+// Gathers 64 entries of one vertical-line list: K rows (bf16, as they are) and V
+// columns (fp16, transposed); entries past the list's length up to the next multiple of
+// 64 are zeros.
+__global__ void __launch_bounds__(256) pf_vl_gather_kernel(PfArgs a) {
+  __shared__ uint16_t tileb[kTile][kHeadDim + 2];
+  const int tid = threadIdx.x, it = blockIdx.x;
+  const int b = blockIdx.y / a.hkv, h = blockIdx.y % a.hkv;
+  const int64_t bh = blockIdx.y;
+  const int32_t total = a.vl_cnt[bh * a.tiles + a.tiles - 1];
+  if (it * kTile >= ((total + kTile - 1) & ~(kTile - 1))) return;
+  const int32_t *pos = a.vl_pos + bh * a.n_max;
+  for (int i = tid; i < kTile * kHeadDim / 8; i += 256) {  // 8 channels per step
+    const int r = i / (kHeadDim / 8), c = 8 * (i % (kHeadDim / 8));
+    const int32_t e = it * kTile + r;
+    uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
+    if (e < total) {
+      const int64_t src = (((int64_t)b * a.n_max + pos[e]) * a.hkv + h) * kHeadDim + c;
+      kw = *reinterpret_cast<const uint4 *>(a.k + src);
+      vw = *reinterpret_cast<const uint4 *>(a.v + src);
+    }
+    *reinterpret_cast<uint4 *>(a.vl_k + (bh * a.n_max + e) * kHeadDim + c) = kw;
+    const uint32_t ww[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tileb[r][c + 2 * q] = __builtin_bit_cast(uint16_t, (_Float16)bf16_value((uint16_t)(ww[q] & 0xFFFFu)));
+      tileb[r][c + 2 * q + 1] = __builtin_bit_cast(uint16_t, (_Float16)bf16_value((uint16_t)(ww[q] >> 16)));
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kHeadDim * kTile / 2; i += 256) {
+    const int c = i / (kTile / 2), r = 2 * (i % (kTile / 2));
+    const uint32_t w = (uint32_t)tileb[r][c] | ((uint32_t)tileb[r + 1][c] << 16);
+    *reinterpret_cast<uint32_t *>(a.vl_vt + (bh * kHeadDim + c) * a.n_max + it * kTile + r) = w;
+  }
+}
+
+// ---- attention ----------------------------------------------------------------------
+
+// One stage in LDS: 64 keys of K (INT8 rows of 128 B, or bf16 rows of 256 B), V^T (128
+// channel rows of 64 fp16 keys) and 64 words of side data (keep weights, or line
+// positions).  16-byte chunks are XOR-swizzled within a row so that the 8 lanes an LDS
+// read serves at once hit 8 different chunk positions: a key row's chunk c sits at
+// c ^ swz_k(key), a channel row's at c ^ (channel & 7).
+struct __align__(16) PfStage {
+  uint8_t k[kTile * 256];
+  uint8_t v[kHeadDim * kTile * 2];
+  float aux[kTile];
+};
+
+__device__ __forceinline__ int swz_k(int key) { return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | ((key & 1) << 2); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
+
+// 1 KB to LDS: lane L copies 16 B from base + voff to LDS byte lds + 16 L.  The LDS base
+// goes in M0; an LDS-bound global load needs one wait state after a write of M0.
+__device__ __forceinline__ void dma_block(uint32_t lds, gbytes base, uint32_t voff) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ gbytes uniform(const void *p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (gbytes)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The work group's stage list: INT8 stages 0 .. n8 - 1 (key tiles 0 ..), line stages
+// (64 list entries each), window stages (key tiles w_first ..).
+struct PfPlan {
+  int32_t n8, n8_clean, nvl, nwin, w_first;
+};
+
+__device__ __forceinline__ void issue_stage(const PfArgs &a, const PfPlan &pl, int sigma, PfStage &S, int b, int h,
+                                            int w, int lane) {
+  const int64_t bh = (int64_t)b * a.hkv + h;
+  const void *kp, *vp, *xp;
+  uint32_t krow;
+  int32_t k0;
+  bool wide;
+  if (sigma < pl.n8) {
+    k0 = sigma * kTile;
+    wide = false;
+    kp = a.k_codes + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim;
+    krow = (uint32_t)a.hkv * kHeadDim;
+    vp = a.vt + bh * kHeadDim * a.n_max;
+    xp = a.keep + bh * a.n_max;
+  } else if (sigma < pl.n8 + pl.nvl) {
+    k0 = (sigma - pl.n8) * kTile;
+    wide = true;
+    kp = a.vl_k + bh * a.n_max * kHeadDim;
+    krow = kHeadDim * 2;
+    vp = a.vl_vt + bh * kHeadDim * a.n_max;
+    xp = a.vl_pos + bh * a.n_max;
+  } else {
+    k0 = (pl.w_first + sigma - pl.n8 - pl.nvl) * kTile;
+    wide = true;
+    kp = a.k + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim;
+    krow = (uint32_t)a.hkv * kHeadDim * 2;
+    vp = a.vt + bh * kHeadDim * a.n_max;
+    xp = a.keep + bh * a.n_max;
+  }
+  const gbytes kb = uniform(kp), vb = uniform(vp), xb = uniform(xp);
+  const uint32_t kl = lds_addr(S.k), vl = lds_addr(S.v);
+  if (!wide) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // 1 KB = 8 keys of 128 B
+      const int blk = w + 4 * i, key = 8 * blk + (lane >> 3), c = (lane & 7) ^ swz_k(key);
+      dma_block(kl + 1024u * blk, kb, (uint32_t)(k0 + key) * krow + 16u * c);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // 1 KB = 4 keys of 256 B
+      const int blk = w + 4 * i, key = 4 * blk + (lane >> 4), c = (lane & 15) ^ swz_k(key);
+      dma_block(kl + 1024u * blk, kb, (uint32_t)(k0 + key) * krow + 16u * c);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // 1 KB = 8 channels x 64 keys
+    const int blk = w + 4 * i, ch = 8 * blk + (lane >> 3), c = (lane & 7) ^ (ch & 7);
+    dma_block(vl + 1024u * blk, vb, ((uint32_t)ch * (uint32_t)a.n_max + (uint32_t)k0 + 8u * c) * 2u);
+  }
+  if (w == 0 && lane < 16) dma_block(lds_addr(S.aux), xb, (uint32_t)(k0 + 4 * lane) * 4u);
+}
+
+// Per-lane softmax state and output accumulators of the wave's four column blocks.
+struct PfState {
+  v4f acc[8][4];  // O^T tiles: [channel tile][column block]
+  float m[4], l[4];
+};
+
+enum PfKind { kInt8 = 0, kInt8Edge = 1, kLines = 2, kWindow = 3 };
+
+__device__ __forceinline__ float col_max(float x) {  // over the 4 lanes of a column
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float col_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+  return __builtin_bit_cast(uint32_t, h2{(_Float16)lo, (_Float16)hi});
 }
 
-__global__ void __launch_bounds__(64) pf_attn_kernel(PfArgs a) {
-  const int lane = threadIdx.x, col = lane & 15, rg = lane >> 4;
-  const int b = blockIdx.y / a.hq, j = blockIdx.y % a.hq, h = j / (a.hq / a.hkv);
-  const int t0 = blockIdx.x * kQBlock, t = t0 + col;  // this lane's query (column)
-  int32_t n = checked_n(a, b);
-  if (n < 0) n = 0;
-  float *outq = a.out + (((int64_t)b * a.n_max + t) * a.hq + j) * kHeadDim;
-  if (t0 >= n) {
+// One stage (64 keys, two halves of 32) of one segment.  Lane (col, rg) of column block
+// cb holds the scores of keys 32 half + 8 rg + e (e = 0 .. 7) for its query: the A
+// operand row r of block u (u = 0, 1) is key 8 (r / 4) + 4 u + r % 4.
+template <int kKind>
+__device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, const v4i (&qi)[4][2],
+                                             const bf8 (&qf)[4][4], const float (&coef)[4], const int32_t (&tq)[4],
+                                             int32_t k0, int32_t window, int lane) {
+  constexpr bool kI8 = kKind == kInt8 || kKind == kInt8Edge;
+  constexpr bool kMasked = kKind != kInt8;
+  const int r = lane & 15, rg = lane >> 4;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-      *reinterpret_cast<float4 *>(outq + 16 * ct + 4 * rg) = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
-  }
-  // Query operands (B of S^T = K Q^T): lane (query col, k group rg).
-  const int tq = min(t, n - 1);
-  const uint16_t *qrow = a.q + (((int64_t)b * a.n_max + tq) * a.hq + j) * kHeadDim;
-  const int8_t *qcrow = a.q_codes + (((int64_t)b * a.n_max + tq) * a.hq + j) * kHeadDim;
-  bf8 qf[4];
-  v4i qi[2];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) qf[m] = *reinterpret_cast<const bf8 *>(qrow + 32 * m + 8 * rg);
-#pragma unroll
-  for (int m = 0; m < 2; ++m) qi[m] = *reinterpret_cast<const v4i *>(qcrow + 64 * m + 16 * rg);
-  const float sq = a.q_scales[((int64_t)b * a.hq + j) * a.tiles + t0 / kTile];
-  const float scale = 1.4426950408889634f / sqrtf((float)kHeadDim);  // log2(e) / sqrt(d)
-  const uint8_t *vl = a.cls ? a.cls + ((int64_t)b * a.hkv + h) * a.n_max : nullptr;
-  const uint16_t *vt = a.vt + (int64_t)(b * a.hkv + h) * kHeadDim * a.n_max;
-
-  float m_run = -1.0e30f, l_run = 0.0f;
-  v4f acc[8];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) acc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int32_t k_last = min(t0 + kQBlock - 1, n - 1);
-  for (int32_t k0 = 0; k0 <= k_last; k0 += kKStep) {
-    // Lane (query col, rg) holds keys k0 + 16 u + 4 rg + i (u = 0, 1; i = 0 .. 3).
-    uint32_t vlw[2] = {0u, 0u};
-    if (vl) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) vlw[u] = *reinterpret_cast<const uint32_t *>(vl + k0 + 16 * u + 4 * rg);
-    }
-    bool vis[2][4], fp[2][4];
-    bool any_q = false, any_f = false;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t kk = k0 + 16 * u + 4 * rg + i;
-        vis[u][i] = kk <= t && kk < n;
-        fp[u][i] = ((vlw[u] >> (8 * i)) & 0xFFu) == 1u || kk > t - a.window;
-        any_q |= vis[u][i] && !fp[u][i];
-        any_f |= vis[u][i] && fp[u][i];
-      }
-    const bool need_q = __any(any_q), need_f = __any(any_f);
-    v4f sf[2], sqv[2];
+  for (int half = 0; half < 2; ++half) {
+    float x[4][8];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int32_t kr = k0 + 16 * u + col;  // A-operand row: key
-      const int64_t krow = (((int64_t)b * a.n_max + kr) * a.hkv + h) * kHeadDim;
-      sf[u] = v4f{0.f, 0.f, 0.f, 0.f};
-      sqv[u] = v4f{0.f, 0.f, 0.f, 0.f};
-      if (need_f) {
+      const int key = 32 * half + 8 * (r >> 2) + 4 * u + (r & 3);
+      if constexpr (kI8) {
+        v4i ka[2];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const bf8 kf = *reinterpret_cast<const bf8 *>(a.k + krow + 32 * m + 8 * rg);
-          sf[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[m], sf[u], 0, 0, 0);
+        for (int m = 0; m < 2; ++m)
+          ka[m] = *reinterpret_cast<const v4i *>(S.k + key * 128 + 16 * ((4 * m + rg) ^ swz_k(key)));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          v4i s32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[0], qi[cb][0], v4i{0, 0, 0, 0}, 0, 0, 0);
+          s32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[1], qi[cb][1], s32, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[cb][4 * u + i] = (float)s32[i];
+        }
+      } else {
+        bf8 ka[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          ka[m] = *reinterpret_cast<const bf8 *>(S.k + key * 256 + 16 * ((4 * m + rg) ^ swz_k(key)));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          v4f sf = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) sf = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], qf[cb][m], sf, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[cb][4 * u + i] = sf[i];
         }
       }
-      if (need_q) {
-        v4i s32 = v4i{0, 0, 0, 0};
+    }
+    // Side data of this lane's 8 keys.
+    const int e0 = 32 * half + 8 * rg;
+    const v4f w0 = *reinterpret_cast<const v4f *>(S.aux + e0), w1 = *reinterpret_cast<const v4f *>(S.aux + e0 + 4);
+    const float side[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    if constexpr (kMasked) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const v4i kc = *reinterpret_cast<const v4i *>(a.k_codes + krow + 64 * m + 16 * rg);
-          s32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, qi[m], s32, 0, 0, 0);
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int32_t key = k0 + e0 + e;
+          bool ok;
+          if constexpr (kKind == kInt8Edge) ok = key <= tq[cb] - window;
+          else if constexpr (kKind == kLines) ok = __float_as_int(side[e]) <= tq[cb];
+          else ok = key <= tq[cb] && key > tq[cb] - window && side[e] > 0.0f;
+          x[cb][e] = ok ? x[cb][e] : -INFINITY;
         }
-        const float sk = a.k_scales[((int64_t)b * a.hkv + h) * a.tiles + k0 / kTile];
+    }
+    // Step maximum per column (coef >= FLT_MIN, so -inf stays -inf); the running
+    // maximum moves only by more than kLazy.
+    float bmax[4];
+    bool grow = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sqv[u][i] = (float)s32[i] * (sq * sk);
+    for (int cb = 0; cb < 4; ++cb) {
+      float mx = fmaxf(fmaxf(fmaxf(x[cb][0], x[cb][1]), fmaxf(x[cb][2], x[cb][3])),
+                       fmaxf(fmaxf(x[cb][4], x[cb][5]), fmaxf(x[cb][6], x[cb][7])));
+      bmax[cb] = col_max(mx) * coef[cb];
+      grow |= bmax[cb] > st.m[cb] + kLazy;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const float mn = fmaxf(st.m[cb], bmax[cb]);
+        const float al = __builtin_amdgcn_exp2f(st.m[cb] - mn);
+        st.m[cb] = mn;
+        st.l[cb] *= al;
+        // One tile at a time: the accumulators stay in the matrix registers, with a
+        // few temporaries, instead of all moving out at once.
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          st.acc[ct][cb] *= al;
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    // Logits (base 2), masked; the step's maximum per query over its 4 lanes.
-    float x[2][4], bmax = -INFINITY;
+    // Weights: p = 2^(x coef - m), fp16 for P.V; INT8 keys enter the row sum through
+    // the keep mask (their lines' and dead keys' V columns are 0 already).
+    h8 pw[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int cb = 0; cb < 4; ++cb) {
+      float p[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float s = fp[u][i] ? sf[u][i] : sqv[u][i];
-        x[u][i] = vis[u][i] ? s * scale : -INFINITY;
-        bmax = fmaxf(bmax, x[u][i]);
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(x[cb][e], coef[cb], -st.m[cb]));
+        st.l[cb] = kI8 ? fmaf(p[e], side[e], st.l[cb]) : st.l[cb] + p[e];
       }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(m_run, bmax);
-    if (m_new > m_run) {
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) acc[ct] *= alpha;
-      m_run = m_new;
+      pw[cb] = __builtin_bit_cast(h8, make_uint4(pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]),
+                                                 pack_f16(p[6], p[7])));
     }
-    float p[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[u][i] = exp2f(x[u][i] - m_run);
-        l_run += p[u][i];
-      }
-    // P^T operand (fp16 weights): k slot 8 rg + i <-> key 4 rg + i (i < 4), 16 + 4 rg +
-    // (i - 4) (i >= 4): the lane's own eight weights, in order.
-    const h8 pw = __builtin_bit_cast(h8, make_uint4(pack_f16(p[0][0], p[0][1]), pack_f16(p[0][2], p[0][3]),
-                                                    pack_f16(p[1][0], p[1][1]), pack_f16(p[1][2], p[1][3])));
+    // O^T += V^T P^T: lane (channel row r, key group rg) reads keys 32 half + 8 rg ...+7.
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      const uint16_t *vrow = vt + (int64_t)(16 * ct + col) * a.n_max + k0 + 4 * rg;
-      const uint2 lo = *reinterpret_cast<const uint2 *>(vrow), hi = *reinterpret_cast<const uint2 *>(vrow + 16);
-      const h8 vw = __builtin_bit_cast(h8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vw, pw, acc[ct], 0, 0, 0);
+      const int ch = 16 * ct + r;
+      const h8 va = *reinterpret_cast<const h8 *>(S.v + ch * 128 + 16 * ((4 * half + rg) ^ (ch & 7)));
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) st.acc[ct][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pw[cb], st.acc[ct][cb], 0, 0, 0);
     }
   }
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const float inv = (t < n && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+}
+
+__global__ void __launch_bounds__(256) pf_attn_kernel(PfArgs a) {
+  __shared__ PfStage stage[2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, rg = lane >> 4;
+  const int n_bh = a.batch * a.hkv;
+  const int qp = kGroupRows / a.g;                     // positions per work group
+  const int n_blk = (a.n_max + qp - 1) / qp;
+  const int blk = n_blk - 1 - (int)(blockIdx.x / n_bh);  // longest rows first
+  const int bh = (int)(blockIdx.x % n_bh), b = bh / a.hkv, h = bh % a.hkv;
+  const int32_t p0 = blk * qp;
+  int32_t n = checked_n(a, b);
+  if (n < 0) n = 0;
+  // Column blocks 4 w + c: query head h g + hg, positions pos0 .. pos0 + 15.
+  const int per_head = 16 / a.g;
+  int32_t tq[4], jq[4], pos0[4];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
-    *reinterpret_cast<float4 *>(outq + 16 * ct + 4 * rg) =
-        make_float4(acc[ct][0] * inv, acc[ct][1] * inv, acc[ct][2] * inv, acc[ct][3] * inv);
+  for (int c = 0; c < 4; ++c) {
+    const int cbg = 4 * w + c;
+    jq[c] = h * a.g + cbg / per_head;
+    pos0[c] = p0 + 16 * (cbg % per_head);
+    tq[c] = pos0[c] + col;
+  }
+  auto store = [&](int c, const float *vals) {
+    const int32_t t = tq[c];
+    if (t >= a.n_max) return;
+    float *o = a.out + (((int64_t)b * a.n_max + t) * a.hq + jq[c]) * kHeadDim + 4 * rg;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      *reinterpret_cast<float4 *>(o + 16 * ct) = make_float4(vals[4 * ct], vals[4 * ct + 1], vals[4 * ct + 2], vals[4 * ct + 3]);
+  };
+  if (p0 >= n) {
+    float zero[32] = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) store(c, zero);
+    return;
+  }
+  const int32_t kmax = min(p0 + qp, n) - 1;  // the last key any live row reads
+  PfPlan pl;
+  const int32_t q_hi = kmax - a.window;       // the last INT8 key
+  pl.n8 = q_hi >= 0 ? q_hi / kTile + 1 : 0;
+  pl.n8_clean = min(pl.n8, max(p0 - a.window + 1, 0) / kTile);
+  pl.nvl = a.cls ? (a.vl_cnt[(int64_t)bh * a.tiles + kmax / kTile] + kTile - 1) / kTile : 0;
+  pl.w_first = max(p0 - a.window + 1, 0) / kTile;
+  pl.nwin = a.window > 0 ? kmax / kTile - pl.w_first + 1 : 0;
+  const int total = pl.n8 + pl.nvl + pl.nwin;
+
+  PfState st;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    st.m[c] = -1.0e30f;
+    st.l[c] = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) st.acc[ct][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  constexpr float kScale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  v4i qi[4][2];
+  bf8 qf[4][4];
+  float cq[4], coef[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int32_t t = min(tq[c], a.n_max - 1);
+    const int8_t *row = a.q_codes + (((int64_t)b * a.n_max + t) * a.hq + jq[c]) * kHeadDim;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) qi[c][m] = *reinterpret_cast<const v4i *>(row + 64 * m + 16 * rg);
+    cq[c] = kScale * a.q_scales[((int64_t)b * a.hq + jq[c]) * a.tiles + min(pos0[c], a.n_max - 1) / kTile];
+  }
+  const float *ks = a.k_scales + (int64_t)bh * a.tiles;
+
+  if (total > 0) issue_stage(a, pl, 0, stage[0], b, h, w, lane);
+  int sigma = 0;
+  // INT8 stages: first those whose keys every row reads in INT8, then the ones that
+  // reach the window.
+  for (; sigma < pl.n8_clean; ++sigma) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
+    const float sk = ks[sigma];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
+    attend_stage<kInt8>(stage[sigma & 1], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
+  }
+  for (; sigma < pl.n8; ++sigma) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
+    const float sk = ks[sigma];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
+    attend_stage<kInt8Edge>(stage[sigma & 1], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
+  }
+  // Full-precision segments: bf16 queries (0 for rows past the request's length).
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bool live = tq[c] < n;
+    const int32_t t = min(tq[c], a.n_max - 1);
+    const uint16_t *row = a.q + (((int64_t)b * a.n_max + t) * a.hq + jq[c]) * kHeadDim;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint4 v = live ? *reinterpret_cast<const uint4 *>(row + 32 * m + 8 * rg) : make_uint4(0u, 0u, 0u, 0u);
+      qf[c][m] = __builtin_bit_cast(bf8, v);
+    }
+    coef[c] = kScale;
+  }
+  for (; sigma < pl.n8 + pl.nvl; ++sigma) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
+    attend_stage<kLines>(stage[sigma & 1], st, qi, qf, coef, tq, 0, a.window, lane);
+  }
+  for (; sigma < total; ++sigma) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
+    attend_stage<kWindow>(stage[sigma & 1], st, qi, qf, coef, tq, (pl.w_first + sigma - pl.n8 - pl.nvl) * kTile,
+                          a.window, lane);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float l = col_sum(st.l[c]);
+    const bool live = tq[c] < n && l > 0.0f;
+    const float inv = live ? 1.0f / l : 0.0f;
+    float vals[32];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vals[4 * ct + i] = live ? st.acc[ct][c][i] * inv : 0.0f;
+    store(c, vals);
+  }
 }
 
 kvq_status launched(const char *what) {
@@ -273,24 +595,67 @@ kvq_status launched(const char *what) {
   return KVQ_OK;
 }
 
+// Workspace regions (each 256-byte aligned), in this order: vt, keep, vl_pos, vl_cnt,
+// vl_k, vl_vt.
+struct PfLayout {
+  size_t vt, keep, vl_pos, vl_cnt, vl_k, vl_vt, total;
+};
+
+PfLayout pf_layout(int64_t batch, int64_t n_max, int64_t hkv) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t bh = (size_t)(batch * hkv), n = (size_t)n_max;
+  PfLayout L;
+  size_t o = 0;
+  L.vt = o;
+  o = up(o + bh * kHeadDim * n * 2);
+  L.keep = o;
+  o = up(o + bh * n * 4);
+  L.vl_pos = o;
+  o = up(o + bh * n * 4);
+  L.vl_cnt = o;
+  o = up(o + bh * (n / kTile) * 4);
+  L.vl_k = o;
+  o = up(o + bh * n * kHeadDim * 2);
+  L.vl_vt = o;
+  o = up(o + bh * kHeadDim * n * 2);
+  L.total = o;
+  return L;
+}
+
 }  // namespace
 }  // namespace kvq
 
 using namespace kvq;
 
+extern "C" size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_max, int32_t hkv) {
+  if (batch <= 0 || n_max <= 0 || hkv <= 0 || n_max % kTile) return 0;
+  return pf_layout(batch, n_max, hkv).total;
+}
+
 extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, const void *v, int32_t dtype, int32_t batch,
                                        int32_t n_max, int32_t hq, int32_t hkv, const int32_t *n_tokens,
                                        const uint8_t *token_class, int32_t window, int8_t *q_codes,
-                                       float *q_scales, int8_t *k_codes, float *k_scales, void *v_t, float *out,
-                                       int32_t *dev_err, void *stream) {
+                                       float *q_scales, int8_t *k_codes, float *k_scales, void *workspace,
+                                       size_t workspace_bytes, float *out, int32_t *dev_err, void *stream) {
   if (dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "prefill attention takes bf16 q, k, v");
   if (batch < 0 || n_max < 0 || n_max % kTile) return fail(KVQ_ERR_INVALID_ARG, "n_max %d: a multiple of 64", n_max);
   if (hkv <= 0 || hq <= 0 || hq % hkv) return fail(KVQ_ERR_INVALID_ARG, "hq %d is not a multiple of hkv %d", hq, hkv);
+  const int32_t g = hq / hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+    return fail(KVQ_ERR_UNSUPPORTED, "hq / hkv = %d: 1, 2, 4, 8 or 16 query heads per KV head", g);
   if (window < 0) return fail(KVQ_ERR_INVALID_ARG, "negative window");
   if (batch == 0 || n_max == 0) return KVQ_OK;
-  if (!q || !k || !v || !n_tokens || !q_codes || !q_scales || !k_codes || !k_scales || !v_t || !out)
+  if (!q || !k || !v || !n_tokens || !q_codes || !q_scales || !k_codes || !k_scales || !workspace || !out)
     return fail(KVQ_ERR_INVALID_ARG, "NULL buffer");
-  if ((int64_t)batch * hq > 65535 || (int64_t)hq + hkv > 65535) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  // LDS-bound loads address one (request, head)'s K rows, V^T rows and lists with 32-bit
+  // byte offsets.
+  if ((int64_t)n_max * hkv * kHeadDim * 2 > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "n_max * hkv too large");
+  if ((int64_t)batch * hq > 65535 || (int64_t)hq + hkv > 65535 || (int64_t)batch * hkv > 65535)
+    return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  const PfLayout L = pf_layout(batch, n_max, hkv);
+  if (workspace_bytes < L.total)
+    return fail(KVQ_ERR_CAPACITY, "prefill workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
   PfArgs a;
   a.q = static_cast<const uint16_t *>(q);
   a.k = static_cast<const uint16_t *>(k);
@@ -301,13 +666,19 @@ extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, const void 
   a.n_max = n_max;
   a.hq = hq;
   a.hkv = hkv;
+  a.g = g;
   a.window = window;
   a.tiles = n_max / kTile;
   a.q_codes = q_codes;
   a.k_codes = k_codes;
   a.q_scales = q_scales;
   a.k_scales = k_scales;
-  a.vt = static_cast<uint16_t *>(v_t);
+  a.vt = reinterpret_cast<uint16_t *>(ws + L.vt);
+  a.keep = reinterpret_cast<float *>(ws + L.keep);
+  a.vl_pos = reinterpret_cast<int32_t *>(ws + L.vl_pos);
+  a.vl_cnt = reinterpret_cast<int32_t *>(ws + L.vl_cnt);
+  a.vl_k = reinterpret_cast<uint16_t *>(ws + L.vl_k);
+  a.vl_vt = reinterpret_cast<uint16_t *>(ws + L.vl_vt);
   a.out = out;
   a.err = dev_err;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -315,8 +686,15 @@ extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, const void 
   kvq_status st = launched("pf_quant_kernel");
   if (st != KVQ_OK) return st;
   hipLaunchKernelGGL(pf_vt_kernel, dim3(a.tiles, batch, hkv), dim3(256), 0, s, a);
-  st = launched("pf_vt_kernel");
-  if (st != KVQ_OK) return st;
-  hipLaunchKernelGGL(pf_attn_kernel, dim3(n_max / kQBlock, batch * hq), dim3(64), 0, s, a);
+  if ((st = launched("pf_vt_kernel")) != KVQ_OK) return st;
+  if (token_class) {
+    hipLaunchKernelGGL(pf_vl_scan_kernel, dim3(batch * hkv), dim3(kScanThreads), 0, s, a);
+    if ((st = launched("pf_vl_scan_kernel")) != KVQ_OK) return st;
+    hipLaunchKernelGGL(pf_vl_gather_kernel, dim3(a.tiles, batch * hkv), dim3(256), 0, s, a);
+    if ((st = launched("pf_vl_gather_kernel")) != KVQ_OK) return st;
+  }
+  const int64_t n_blk = (n_max + kGroupRows / g - 1) / (kGroupRows / g);
+  if (n_blk * batch * hkv > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  hipLaunchKernelGGL(pf_attn_kernel, dim3((uint32_t)(n_blk * batch * hkv)), dim3(256), 0, s, a);
   return launched("pf_attn_kernel");
 }

@@ -65,8 +65,9 @@ _SIGS = {
                              _P, _P], ctypes.c_int),
     "kvq_reorder_pages": ([_P, _P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
     "kvq_compact_slots": ([_P, _P, _i32, _i32, _P, _P, _P, _P, _P], ctypes.c_int),
-    "kvq_prefill_attn": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P],
-                         ctypes.c_int),
+    "kvq_prefill_attn": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P, _P, _P, _P,
+                          ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
+    "kvq_prefill_workspace_bytes": ([_i32, _i32, _i32], ctypes.c_size_t),
     "kvq_select_vertical_lines": ([_P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32,
                                    ctypes.c_float, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "kvq_decode_attn": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P, _P,
@@ -264,13 +265,17 @@ def select_vertical_lines(k: torch.Tensor, q_tail: torch.Tensor, n_tokens: torch
 
 
 def prefill_workspace(batch: int, n_max: int, hq: int, hkv: int, device="cuda"):
-    """Workspace and output of prefill_attn: (q_codes, q_scales, k_codes, k_scales, v_t, out)."""
+    """Outputs and scratch of prefill_attn: (q_codes, q_scales, k_codes, k_scales,
+    scratch, out); scratch is kvq_prefill_workspace_bytes bytes."""
     tiles = n_max // 64
+    nbytes = _lib.kvq_prefill_workspace_bytes(batch, n_max, hkv)
+    if nbytes == 0:
+        raise KvqError(-1, f"kvq_prefill_workspace_bytes({batch}, {n_max}, {hkv})")
     return (torch.empty((batch, n_max, hq, HEAD_DIM), dtype=torch.int8, device=device),
             torch.empty((batch, hq, tiles), dtype=torch.float32, device=device),
             torch.empty((batch, n_max, hkv, HEAD_DIM), dtype=torch.int8, device=device),
             torch.empty((batch, hkv, tiles), dtype=torch.float32, device=device),
-            torch.empty((batch, hkv, HEAD_DIM, n_max), dtype=torch.float16, device=device),
+            torch.empty(nbytes, dtype=torch.uint8, device=device),
             torch.empty((batch, n_max, hq, HEAD_DIM), dtype=torch.float32, device=device))
 
 
@@ -285,12 +290,13 @@ def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens: to
     hkv = k.shape[2]
     if ws is None:
         ws = prefill_workspace(batch, n_max, hq, hkv, q.device)
-    qc, qs, kc, ks, vt, out = ws
+    qc, qs, kc, ks, scratch, out = ws
     if token_class is not None:
         assert token_class.dtype == torch.uint8 and token_class.is_contiguous()
     _check(_lib.kvq_prefill_attn(_dptr(q), _dptr(k), _dptr(v), BF16, batch, n_max, hq, hkv, _dptr(n_tokens),
                                  _dptr(token_class), window, _dptr(qc), _dptr(qs), _dptr(kc), _dptr(ks),
-                                 _dptr(vt), _dptr(out), _dptr(dev_err), _stream(stream)), "kvq_prefill_attn")
+                                 _dptr(scratch), scratch.numel(), _dptr(out), _dptr(dev_err), _stream(stream)),
+           "kvq_prefill_attn")
     return ws
 
 

@@ -176,3 +176,34 @@ def test_balanced_split_counts_minimal_cap(kvq):
     assert few.tolist() == [1, 0, 1, 1]
     with pytest.raises(kvq.KvqError):
         kvq.balanced_split_counts(np.array([3, -1], np.int64), 4)
+
+
+def test_prefill_workspace_and_validation(kvq):
+    """The prefill scratch size follows its region list (V^T fp16, keep mask, line
+    positions, per-tile line counts, gathered K and V^T, each 256-byte aligned); the
+    entry point rejects g outside {1, 2, 4, 8, 16}, n_max off 64 and a short scratch
+    before touching any pointer."""
+    lib = kvq.raw_library()
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for batch, n_max, hkv in ((1, 64, 1), (2, 1024, 8), (3, 192, 2)):
+        bh = batch * hkv
+        want = 0
+        for size in (bh * 128 * n_max * 2, bh * n_max * 4, bh * n_max * 4, bh * (n_max // 64) * 4,
+                     bh * n_max * 128 * 2, bh * 128 * n_max * 2):
+            want = up(want + size)
+        assert lib.kvq_prefill_workspace_bytes(batch, n_max, hkv) == want
+    assert lib.kvq_prefill_workspace_bytes(1, 100, 1) == 0
+    assert lib.kvq_prefill_workspace_bytes(0, 64, 1) == 0
+    fake = ctypes.c_void_p(0x1000)
+    need = lib.kvq_prefill_workspace_bytes(1, 128, 2)
+
+    def call(hq=4, hkv=2, n_max=128, nbytes=need, dtype=1):
+        return lib.kvq_prefill_attn(fake, fake, fake, dtype, 1, n_max, hq, hkv, fake, None, 16, fake, fake, fake,
+                                    fake, fake, nbytes, fake, None, None)
+    assert call(hq=6, hkv=2) == -2          # g = 3
+    assert call(hq=64, hkv=2) == -2         # g = 32
+    assert call(hq=6, hkv=4) == -1          # hq % hkv != 0
+    assert call(n_max=100) == -1            # not a multiple of 64
+    assert call(dtype=0) == -2              # fp32 inputs
+    assert call(nbytes=need - 1) == -3      # scratch too small
+    assert b"workspace" in lib.kvq_last_error()

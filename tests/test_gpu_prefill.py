@@ -49,9 +49,16 @@ def test_small_mixed_segments():
     _case("b2 n256 g4 W64", 2, 256, 8, 2, [256, 150], window=64)
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (16, 2), (16, 1)])
 def test_gqa_ratios(hq, hkv):
+    """Every supported g: a work group holds 256 / g positions of all g heads."""
     _case(f"g={hq // hkv}", 1, 192, hq, hkv, [181], window=32)
+
+
+def test_many_stages():
+    """Several work groups per head, INT8 stages before and across the window edge,
+    more than one 64-entry stage of vertical lines, a ragged second request."""
+    _case("b2 n1024 g4 W128", 2, 1024, 8, 2, [1024, 701], window=128, vl_frac=0.1, seed=11)
 
 
 def test_limits():
