@@ -283,24 +283,36 @@ size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_max, int32_t hkv);
  * per query head for Q and per KV head for K (vertical lines left out of the
  * maximum); scale s = fl32(max |x| / 127), code = clamp(rint(fl32(x / s)), -127,
  * 127) (0 when s = 0); the logit of an INT8 pair is s_Q s_K (q_code . k_code).
+ *
+ * Two calls, in stream order on one workspace:
+ *   kvq_prefill_prepare: the INT8 codes and tile scales of q and k, and the
+ *     scratch the attention reads (V transposed to fp16, the keep mask, the
+ *     vertical-line lists and their gathered K and V);
+ *   kvq_prefill_attn: the attention, from what prepare left with the same q, k,
+ *     n_tokens and token_class.
  *   q [dev] bf16 [batch][n_max][hq][128]; k, v [dev] bf16 [batch][n_max][hkv][128]
  *   (|v| < 65504); n_max a multiple of 64; g = hq / hkv in {1, 2, 4, 8, 16}.
- *   Outputs [dev]: q_codes int8 like q, q_scales float [batch][hq][n_max/64],
- *   k_codes int8 like k, k_scales float [batch][hkv][n_max/64], out float
- *   [batch][n_max][hq][128] (0 for t >= n).  workspace [dev]: at least
- *   kvq_prefill_workspace_bytes(batch, n_max, hkv) bytes of scratch (V transposed
- *   to fp16, the vertical-line lists and their gathered K and V), 256-byte aligned,
- *   owned by the caller; its contents between calls mean nothing.
+ *   q_codes [dev] int8 like q, q_scales float [batch][hq][n_max/64], k_codes int8
+ *   like k, k_scales float [batch][hkv][n_max/64]: written by prepare, read by
+ *   attn.  workspace [dev]: at least kvq_prefill_workspace_bytes(batch, n_max,
+ *   hkv) bytes, 256-byte aligned, owned by the caller.  out [dev] float
+ *   [batch][n_max][hq][128] (0 for t >= n).
  * Errors: INVALID_ARG, UNSUPPORTED (dtype other than KVQ_BF16, another g, sizes
  * past 32-bit offsets), CAPACITY (workspace too small), HIP; a request whose
  * n_tokens is out of range is treated as empty (KVQ_DEVERR_RANGE).
  */
-kvq_status kvq_prefill_attn(const void *q, const void *k, const void *v, int32_t dtype,
-                            int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
-                            const int32_t *n_tokens, const uint8_t *token_class,
-                            int32_t window, int8_t *q_codes, float *q_scales,
-                            int8_t *k_codes, float *k_scales, void *workspace,
-                            size_t workspace_bytes, float *out,
+kvq_status kvq_prefill_prepare(const void *q, const void *k, const void *v, int32_t dtype,
+                               int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
+                               const int32_t *n_tokens, const uint8_t *token_class,
+                               int8_t *q_codes, float *q_scales, int8_t *k_codes,
+                               float *k_scales, void *workspace, size_t workspace_bytes,
+                               int32_t *dev_err, void *stream);
+kvq_status kvq_prefill_attn(const void *q, const void *k, int32_t dtype, int32_t batch,
+                            int32_t n_max, int32_t hq, int32_t hkv, const int32_t *n_tokens,
+                            const uint8_t *token_class, int32_t window,
+                            const int8_t *q_codes, const float *q_scales,
+                            const int8_t *k_codes, const float *k_scales,
+                            const void *workspace, size_t workspace_bytes, float *out,
                             int32_t *dev_err, void *stream);
 
 /*

@@ -27,7 +27,7 @@ SOURCES = [
     # DPP row reductions fold into v_max_f32_dpp.
     ("kvq_decode.hip", HIP + ["-fno-honor-nans"]),
     ("kvq_select.hip", HIP),
-    ("kvq_prefill.hip", HIP),
+    ("kvq_prefill.hip", HIP + ["-fno-honor-nans"]),
 ]
 
 

@@ -19,9 +19,9 @@
 //
 // Launches: INT8 codes and scales (one work group per 64-position tile and head); V^T
 // with the keep mask; the vertical-line list (one work group per request and KV head);
-// its gather; the attention.  An attention work group (256 threads) takes one request,
-// one KV head and 256 / g positions of all g of its query heads: 16 column blocks of 16
-// (position, head) rows, four per wave.  K and V^T stages of 64 keys go to LDS by
+// its gather; the attention.  An attention work group (8 waves) takes one request, one
+// KV head and 256 / g positions of all g of its query heads: 16 column blocks of 16
+// (position, head) rows, two per wave.  K and V^T stages of 64 keys go to LDS by
 // LDS-bound global loads, double-buffered across all three segments; S^T = K Q^T on
 // MFMA (i32 16x16x64 for INT8, f32 16x16x32 bf16 otherwise) puts a lane's scores where
 // the P operand of O^T = V^T P^T wants them (f32 16x16x32 f16).  The softmax rescales
@@ -40,6 +40,9 @@ namespace {
 
 constexpr int kTile = 64;       // INT8 tile = LDS stage (positions)
 constexpr int kGroupRows = 256; // (position, query head) rows per attention work group
+constexpr int kAttnWaves = 8;   // attention waves per work group
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kCB = kGroupRows / 16 / kAttnWaves;  // 16-row column blocks per wave
 constexpr float kLazy = 8.0f;   // log2 headroom of the running maximum
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -303,20 +306,20 @@ __device__ __forceinline__ void issue_stage(const PfArgs &a, const PfPlan &pl, i
   const uint32_t kl = lds_addr(S.k), vl = lds_addr(S.v);
   if (!wide) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // 1 KB = 8 keys of 128 B
-      const int blk = w + 4 * i, key = 8 * blk + (lane >> 3), c = (lane & 7) ^ swz_k(key);
+    for (int i = 0; i < 8 / kAttnWaves; ++i) {  // 1 KB = 8 keys of 128 B
+      const int blk = w + kAttnWaves * i, key = 8 * blk + (lane >> 3), c = (lane & 7) ^ swz_k(key);
       dma_block(kl + 1024u * blk, kb, (uint32_t)(k0 + key) * krow + 16u * c);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // 1 KB = 4 keys of 256 B
-      const int blk = w + 4 * i, key = 4 * blk + (lane >> 4), c = (lane & 15) ^ swz_k(key);
+    for (int i = 0; i < 16 / kAttnWaves; ++i) {  // 1 KB = 4 keys of 256 B
+      const int blk = w + kAttnWaves * i, key = 4 * blk + (lane >> 4), c = (lane & 15) ^ swz_k(key);
       dma_block(kl + 1024u * blk, kb, (uint32_t)(k0 + key) * krow + 16u * c);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {  // 1 KB = 8 channels x 64 keys
-    const int blk = w + 4 * i, ch = 8 * blk + (lane >> 3), c = (lane & 7) ^ (ch & 7);
+  for (int i = 0; i < 16 / kAttnWaves; ++i) {  // 1 KB = 8 channels x 64 keys
+    const int blk = w + kAttnWaves * i, ch = 8 * blk + (lane >> 3), c = (lane & 7) ^ (ch & 7);
     dma_block(vl + 1024u * blk, vb, ((uint32_t)ch * (uint32_t)a.n_max + (uint32_t)k0 + 8u * c) * 2u);
   }
   if (w == 0 && lane < 16) dma_block(lds_addr(S.aux), xb, (uint32_t)(k0 + 4 * lane) * 4u);
@@ -324,8 +327,8 @@ __device__ __forceinline__ void issue_stage(const PfArgs &a, const PfPlan &pl, i
 
 // Per-lane softmax state and output accumulators of the wave's four column blocks.
 struct PfState {
-  v4f acc[8][4];  // O^T tiles: [channel tile][column block]
-  float m[4], l[4];
+  v4f acc[8][kCB];  // O^T tiles: [channel tile][column block]
+  float m[kCB], l[kCB];
 };
 
 enum PfKind { kInt8 = 0, kInt8Edge = 1, kLines = 2, kWindow = 3 };
@@ -352,15 +355,15 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {  // round to 
 // cb holds the scores of keys 32 half + 8 rg + e (e = 0 .. 7) for its query: the A
 // operand row r of block u (u = 0, 1) is key 8 (r / 4) + 4 u + r % 4.
 template <int kKind>
-__device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, const v4i (&qi)[4][2],
-                                             const bf8 (&qf)[4][4], const float (&coef)[4], const int32_t (&tq)[4],
+__device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, const v4i (&qi)[kCB][2],
+                                             const bf8 (&qf)[kCB][4], const float (&coef)[kCB], const int32_t (&tq)[kCB],
                                              int32_t k0, int32_t window, int lane) {
   constexpr bool kI8 = kKind == kInt8 || kKind == kInt8Edge;
   constexpr bool kMasked = kKind != kInt8;
   const int r = lane & 15, rg = lane >> 4;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    float x[4][8];
+    float x[kCB][8];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int key = 32 * half + 8 * (r >> 2) + 4 * u + (r & 3);
@@ -370,7 +373,7 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
         for (int m = 0; m < 2; ++m)
           ka[m] = *reinterpret_cast<const v4i *>(S.k + key * 128 + 16 * ((4 * m + rg) ^ swz_k(key)));
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < kCB; ++cb) {
           v4i s32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[0], qi[cb][0], v4i{0, 0, 0, 0}, 0, 0, 0);
           s32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[1], qi[cb][1], s32, 0, 0, 0);
 #pragma unroll
@@ -382,7 +385,7 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
         for (int m = 0; m < 4; ++m)
           ka[m] = *reinterpret_cast<const bf8 *>(S.k + key * 256 + 16 * ((4 * m + rg) ^ swz_k(key)));
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < kCB; ++cb) {
           v4f sf = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 4; ++m) sf = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], qf[cb][m], sf, 0, 0, 0);
@@ -397,7 +400,7 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
     const float side[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
     if constexpr (kMasked) {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int32_t key = k0 + e0 + e;
@@ -410,10 +413,10 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
     }
     // Step maximum per column (coef >= FLT_MIN, so -inf stays -inf); the running
     // maximum moves only by more than kLazy.
-    float bmax[4];
+    float bmax[kCB];
     bool grow = false;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       float mx = fmaxf(fmaxf(fmaxf(x[cb][0], x[cb][1]), fmaxf(x[cb][2], x[cb][3])),
                        fmaxf(fmaxf(x[cb][4], x[cb][5]), fmaxf(x[cb][6], x[cb][7])));
       bmax[cb] = col_max(mx) * coef[cb];
@@ -421,7 +424,7 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
     }
     if (__any(grow)) {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < kCB; ++cb) {
         const float mn = fmaxf(st.m[cb], bmax[cb]);
         const float al = __builtin_amdgcn_exp2f(st.m[cb] - mn);
         st.m[cb] = mn;
@@ -437,9 +440,9 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
     }
     // Weights: p = 2^(x coef - m), fp16 for P.V; INT8 keys enter the row sum through
     // the keep mask (their lines' and dead keys' V columns are 0 already).
-    h8 pw[4];
+    h8 pw[kCB];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -455,12 +458,12 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
       const int ch = 16 * ct + r;
       const h8 va = *reinterpret_cast<const h8 *>(S.v + ch * 128 + 16 * ((4 * half + rg) ^ (ch & 7)));
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) st.acc[ct][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pw[cb], st.acc[ct][cb], 0, 0, 0);
+      for (int cb = 0; cb < kCB; ++cb) st.acc[ct][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pw[cb], st.acc[ct][cb], 0, 0, 0);
     }
   }
 }
 
-__global__ void __launch_bounds__(256) pf_attn_kernel(PfArgs a) {
+__global__ void __launch_bounds__(kAttnThreads) pf_attn_kernel(PfArgs a) {
   __shared__ PfStage stage[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, rg = lane >> 4;
   const int n_bh = a.batch * a.hkv;
@@ -471,12 +474,12 @@ __global__ void __launch_bounds__(256) pf_attn_kernel(PfArgs a) {
   const int32_t p0 = blk * qp;
   int32_t n = checked_n(a, b);
   if (n < 0) n = 0;
-  // Column blocks 4 w + c: query head h g + hg, positions pos0 .. pos0 + 15.
+  // Column blocks kCB w + c: query head h g + hg, positions pos0 .. pos0 + 15.
   const int per_head = 16 / a.g;
-  int32_t tq[4], jq[4], pos0[4];
+  int32_t tq[kCB], jq[kCB], pos0[kCB];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int cbg = 4 * w + c;
+  for (int c = 0; c < kCB; ++c) {
+    const int cbg = kCB * w + c;
     jq[c] = h * a.g + cbg / per_head;
     pos0[c] = p0 + 16 * (cbg % per_head);
     tq[c] = pos0[c] + col;
@@ -492,7 +495,7 @@ __global__ void __launch_bounds__(256) pf_attn_kernel(PfArgs a) {
   if (p0 >= n) {
     float zero[32] = {};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) store(c, zero);
+    for (int c = 0; c < kCB; ++c) store(c, zero);
     return;
   }
   const int32_t kmax = min(p0 + qp, n) - 1;  // the last key any live row reads
@@ -507,18 +510,18 @@ __global__ void __launch_bounds__(256) pf_attn_kernel(PfArgs a) {
 
   PfState st;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < kCB; ++c) {
     st.m[c] = -1.0e30f;
     st.l[c] = 0.0f;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) st.acc[ct][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   constexpr float kScale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  v4i qi[4][2];
-  bf8 qf[4][4];
-  float cq[4], coef[4];
+  v4i qi[kCB][2];
+  bf8 qf[kCB][4];
+  float cq[kCB], coef[kCB];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < kCB; ++c) {
     const int32_t t = min(tq[c], a.n_max - 1);
     const int8_t *row = a.q_codes + (((int64_t)b * a.n_max + t) * a.hq + jq[c]) * kHeadDim;
 #pragma unroll
@@ -537,7 +540,7 @@ __global__ void __launch_bounds__(256) pf_attn_kernel(PfArgs a) {
     if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
     const float sk = ks[sigma];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
+    for (int c = 0; c < kCB; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
     attend_stage<kInt8>(stage[sigma & 1], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
   }
   for (; sigma < pl.n8; ++sigma) {
@@ -546,12 +549,12 @@ __global__ void __launch_bounds__(256) pf_attn_kernel(PfArgs a) {
     if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
     const float sk = ks[sigma];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
+    for (int c = 0; c < kCB; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
     attend_stage<kInt8Edge>(stage[sigma & 1], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
   }
   // Full-precision segments: bf16 queries (0 for rows past the request's length).
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < kCB; ++c) {
     const bool live = tq[c] < n;
     const int32_t t = min(tq[c], a.n_max - 1);
     const uint16_t *row = a.q + (((int64_t)b * a.n_max + t) * a.hq + jq[c]) * kHeadDim;
@@ -576,7 +579,7 @@ __global__ void __launch_bounds__(256) pf_attn_kernel(PfArgs a) {
                           a.window, lane);
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < kCB; ++c) {
     const float l = col_sum(st.l[c]);
     const bool live = tq[c] < n && l > 0.0f;
     const float inv = live ? 1.0f / l : 0.0f;
@@ -632,11 +635,14 @@ extern "C" size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_max, int3
   return pf_layout(batch, n_max, hkv).total;
 }
 
-extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, const void *v, int32_t dtype, int32_t batch,
-                                       int32_t n_max, int32_t hq, int32_t hkv, const int32_t *n_tokens,
-                                       const uint8_t *token_class, int32_t window, int8_t *q_codes,
-                                       float *q_scales, int8_t *k_codes, float *k_scales, void *workspace,
-                                       size_t workspace_bytes, float *out, int32_t *dev_err, void *stream) {
+namespace {
+
+// Validation shared by both entry points, then the argument block.
+kvq_status pf_setup(PfArgs &a, const void *q, const void *k, const void *v, int32_t dtype, int32_t batch,
+                    int32_t n_max, int32_t hq, int32_t hkv, const int32_t *n_tokens, const uint8_t *token_class,
+                    int32_t window, int8_t *q_codes, float *q_scales, int8_t *k_codes, float *k_scales,
+                    void *workspace, size_t workspace_bytes, float *out, int32_t *dev_err, bool &empty) {
+  empty = false;
   if (dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "prefill attention takes bf16 q, k, v");
   if (batch < 0 || n_max < 0 || n_max % kTile) return fail(KVQ_ERR_INVALID_ARG, "n_max %d: a multiple of 64", n_max);
   if (hkv <= 0 || hq <= 0 || hq % hkv) return fail(KVQ_ERR_INVALID_ARG, "hq %d is not a multiple of hkv %d", hq, hkv);
@@ -644,8 +650,11 @@ extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, const void 
   if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
     return fail(KVQ_ERR_UNSUPPORTED, "hq / hkv = %d: 1, 2, 4, 8 or 16 query heads per KV head", g);
   if (window < 0) return fail(KVQ_ERR_INVALID_ARG, "negative window");
-  if (batch == 0 || n_max == 0) return KVQ_OK;
-  if (!q || !k || !v || !n_tokens || !q_codes || !q_scales || !k_codes || !k_scales || !workspace || !out)
+  if (batch == 0 || n_max == 0) {
+    empty = true;
+    return KVQ_OK;
+  }
+  if (!q || !k || !n_tokens || !q_codes || !q_scales || !k_codes || !k_scales || !workspace)
     return fail(KVQ_ERR_INVALID_ARG, "NULL buffer");
   // LDS-bound loads address one (request, head)'s K rows, V^T rows and lists with 32-bit
   // byte offsets.
@@ -656,7 +665,6 @@ extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, const void 
   if (workspace_bytes < L.total)
     return fail(KVQ_ERR_CAPACITY, "prefill workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
-  PfArgs a;
   a.q = static_cast<const uint16_t *>(q);
   a.k = static_cast<const uint16_t *>(k);
   a.v = static_cast<const uint16_t *>(v);
@@ -681,10 +689,25 @@ extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, const void 
   a.vl_vt = reinterpret_cast<uint16_t *>(ws + L.vl_vt);
   a.out = out;
   a.err = dev_err;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" kvq_status kvq_prefill_prepare(const void *q, const void *k, const void *v, int32_t dtype, int32_t batch,
+                                          int32_t n_max, int32_t hq, int32_t hkv, const int32_t *n_tokens,
+                                          const uint8_t *token_class, int8_t *q_codes, float *q_scales,
+                                          int8_t *k_codes, float *k_scales, void *workspace, size_t workspace_bytes,
+                                          int32_t *dev_err, void *stream) {
+  PfArgs a;
+  bool empty;
+  kvq_status st = pf_setup(a, q, k, v, dtype, batch, n_max, hq, hkv, n_tokens, token_class, 0, q_codes, q_scales,
+                           k_codes, k_scales, workspace, workspace_bytes, nullptr, dev_err, empty);
+  if (st != KVQ_OK || empty) return st;
+  if (!v) return fail(KVQ_ERR_INVALID_ARG, "NULL v");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(pf_quant_kernel, dim3(a.tiles, batch, hq + hkv), dim3(256), 0, s, a);
-  kvq_status st = launched("pf_quant_kernel");
-  if (st != KVQ_OK) return st;
+  if ((st = launched("pf_quant_kernel")) != KVQ_OK) return st;
   hipLaunchKernelGGL(pf_vt_kernel, dim3(a.tiles, batch, hkv), dim3(256), 0, s, a);
   if ((st = launched("pf_vt_kernel")) != KVQ_OK) return st;
   if (token_class) {
@@ -693,8 +716,24 @@ extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, const void 
     hipLaunchKernelGGL(pf_vl_gather_kernel, dim3(a.tiles, batch * hkv), dim3(256), 0, s, a);
     if ((st = launched("pf_vl_gather_kernel")) != KVQ_OK) return st;
   }
-  const int64_t n_blk = (n_max + kGroupRows / g - 1) / (kGroupRows / g);
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, int32_t dtype, int32_t batch, int32_t n_max,
+                                       int32_t hq, int32_t hkv, const int32_t *n_tokens, const uint8_t *token_class,
+                                       int32_t window, const int8_t *q_codes, const float *q_scales,
+                                       const int8_t *k_codes, const float *k_scales, const void *workspace,
+                                       size_t workspace_bytes, float *out, int32_t *dev_err, void *stream) {
+  PfArgs a;
+  bool empty;
+  kvq_status st = pf_setup(a, q, k, nullptr, dtype, batch, n_max, hq, hkv, n_tokens, token_class, window,
+                           const_cast<int8_t *>(q_codes), const_cast<float *>(q_scales), const_cast<int8_t *>(k_codes),
+                           const_cast<float *>(k_scales), const_cast<void *>(workspace), workspace_bytes, out, dev_err,
+                           empty);
+  if (st != KVQ_OK || empty) return st;
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "NULL out");
+  const int64_t n_blk = (n_max + kGroupRows / a.g - 1) / (kGroupRows / a.g);
   if (n_blk * batch * hkv > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
-  hipLaunchKernelGGL(pf_attn_kernel, dim3((uint32_t)(n_blk * batch * hkv)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(pf_attn_kernel, dim3((uint32_t)(n_blk * batch * hkv)), dim3(kAttnThreads), 0, static_cast<hipStream_t>(stream), a);
   return launched("pf_attn_kernel");
 }

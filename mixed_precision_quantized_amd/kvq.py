@@ -65,7 +65,9 @@ _SIGS = {
                              _P, _P], ctypes.c_int),
     "kvq_reorder_pages": ([_P, _P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
     "kvq_compact_slots": ([_P, _P, _i32, _i32, _P, _P, _P, _P, _P], ctypes.c_int),
-    "kvq_prefill_attn": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P, _P, _P, _P,
+    "kvq_prefill_prepare": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P,
+                             ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "kvq_prefill_attn": ([_P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P, _P, _P, _P,
                           ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
     "kvq_prefill_workspace_bytes": ([_i32, _i32, _i32], ctypes.c_size_t),
     "kvq_select_vertical_lines": ([_P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32,
@@ -279,24 +281,46 @@ def prefill_workspace(batch: int, n_max: int, hq: int, hkv: int, device="cuda"):
             torch.empty((batch, n_max, hq, HEAD_DIM), dtype=torch.float32, device=device))
 
 
-def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens: torch.Tensor,
-                 token_class: Optional[torch.Tensor] = None, window: int = 128, ws=None, dev_err=None,
-                 stream=None):
-    """q [batch, n_max, hq, 128], k, v [batch, n_max, hkv, 128] bf16 (device); token_class
-    uint8 [batch, hkv, n_max] or None.  Returns prefill_workspace's tuple, filled."""
+def prefill_prepare(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens: torch.Tensor,
+                    token_class: Optional[torch.Tensor], ws, dev_err=None, stream=None):
+    """The INT8 codes and scales of q, k and the attention's scratch, into ws
+    (prefill_workspace's tuple)."""
     assert q.dtype == k.dtype == v.dtype == torch.bfloat16
     assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
     batch, n_max, hq = q.shape[:3]
     hkv = k.shape[2]
-    if ws is None:
-        ws = prefill_workspace(batch, n_max, hq, hkv, q.device)
-    qc, qs, kc, ks, scratch, out = ws
+    qc, qs, kc, ks, scratch, _ = ws
     if token_class is not None:
         assert token_class.dtype == torch.uint8 and token_class.is_contiguous()
-    _check(_lib.kvq_prefill_attn(_dptr(q), _dptr(k), _dptr(v), BF16, batch, n_max, hq, hkv, _dptr(n_tokens),
+    _check(_lib.kvq_prefill_prepare(_dptr(q), _dptr(k), _dptr(v), BF16, batch, n_max, hq, hkv, _dptr(n_tokens),
+                                    _dptr(token_class), _dptr(qc), _dptr(qs), _dptr(kc), _dptr(ks),
+                                    _dptr(scratch), scratch.numel(), _dptr(dev_err), _stream(stream)),
+           "kvq_prefill_prepare")
+
+
+def prefill_attend(q: torch.Tensor, k: torch.Tensor, n_tokens: torch.Tensor, token_class: Optional[torch.Tensor],
+                   window: int, ws, dev_err=None, stream=None):
+    """The attention over what prefill_prepare left in ws; fills ws[5]."""
+    batch, n_max, hq = q.shape[:3]
+    hkv = k.shape[2]
+    qc, qs, kc, ks, scratch, out = ws
+    _check(_lib.kvq_prefill_attn(_dptr(q), _dptr(k), BF16, batch, n_max, hq, hkv, _dptr(n_tokens),
                                  _dptr(token_class), window, _dptr(qc), _dptr(qs), _dptr(kc), _dptr(ks),
                                  _dptr(scratch), scratch.numel(), _dptr(out), _dptr(dev_err), _stream(stream)),
            "kvq_prefill_attn")
+
+
+def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens: torch.Tensor,
+                 token_class: Optional[torch.Tensor] = None, window: int = 128, ws=None, dev_err=None,
+                 stream=None):
+    """q [batch, n_max, hq, 128], k, v [batch, n_max, hkv, 128] bf16 (device); token_class
+    uint8 [batch, hkv, n_max] or None.  prepare then attend; returns prefill_workspace's
+    tuple, filled."""
+    batch, n_max, hq = q.shape[:3]
+    if ws is None:
+        ws = prefill_workspace(batch, n_max, hq, k.shape[2], q.device)
+    prefill_prepare(q, k, v, n_tokens, token_class, ws, dev_err, stream)
+    prefill_attend(q, k, n_tokens, token_class, window, ws, dev_err, stream)
     return ws
 
 

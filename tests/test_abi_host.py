@@ -197,13 +197,19 @@ def test_prefill_workspace_and_validation(kvq):
     fake = ctypes.c_void_p(0x1000)
     need = lib.kvq_prefill_workspace_bytes(1, 128, 2)
 
-    def call(hq=4, hkv=2, n_max=128, nbytes=need, dtype=1):
-        return lib.kvq_prefill_attn(fake, fake, fake, dtype, 1, n_max, hq, hkv, fake, None, 16, fake, fake, fake,
-                                    fake, fake, nbytes, fake, None, None)
-    assert call(hq=6, hkv=2) == -2          # g = 3
-    assert call(hq=64, hkv=2) == -2         # g = 32
-    assert call(hq=6, hkv=4) == -1          # hq % hkv != 0
-    assert call(n_max=100) == -1            # not a multiple of 64
-    assert call(dtype=0) == -2              # fp32 inputs
-    assert call(nbytes=need - 1) == -3      # scratch too small
-    assert b"workspace" in lib.kvq_last_error()
+    def attn(hq=4, hkv=2, n_max=128, nbytes=need, dtype=1, out=fake):
+        return lib.kvq_prefill_attn(fake, fake, dtype, 1, n_max, hq, hkv, fake, None, 16, fake, fake, fake,
+                                    fake, fake, nbytes, out, None, None)
+
+    def prepare(hq=4, hkv=2, n_max=128, nbytes=need, dtype=1, v=fake):
+        return lib.kvq_prefill_prepare(fake, fake, v, dtype, 1, n_max, hq, hkv, fake, None, fake, fake, fake,
+                                       fake, fake, nbytes, None, None)
+    for call in (attn, prepare):
+        assert call(hq=6, hkv=2) == -2          # g = 3
+        assert call(hq=64, hkv=2) == -2         # g = 32
+        assert call(hq=6, hkv=4) == -1          # hq % hkv != 0
+        assert call(n_max=100) == -1            # not a multiple of 64
+        assert call(dtype=0) == -2              # fp32 inputs
+        assert call(nbytes=need - 1) == -3      # scratch too small
+        assert b"workspace" in lib.kvq_last_error()
+    assert attn(out=None) == -1 and prepare(v=None) == -1
