@@ -19,9 +19,9 @@
 //
 // Launches: INT8 codes and scales (one work group per 64-position tile and head); V^T
 // with the keep mask; the vertical-line list (one work group per request and KV head);
-// its gather; the attention.  An attention work group (8 waves) takes one request, one
-// KV head and 256 / g positions of all g of its query heads: 16 column blocks of 16
-// (position, head) rows, two per wave.  K and V^T stages of 64 keys go to LDS by
+// its gather; the attention.  An attention work group (4 waves, two groups per CU) takes
+// one request, one KV head and 128 / g positions of all g of its query heads (of half of
+// them, for g = 16): 8 column blocks of 16 (position, head) rows, two per wave.  K and V^T stages of 64 keys go to LDS by
 // LDS-bound global loads, double-buffered across all three segments; S^T = K Q^T on
 // MFMA (i32 16x16x64 for INT8, f32 16x16x32 bf16 otherwise) puts a lane's scores where
 // the P operand of O^T = V^T P^T wants them (f32 16x16x32 f16).  The softmax rescales
@@ -31,6 +31,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "kvq.h"
 #include "kvq_internal.h"
@@ -39,11 +40,13 @@ namespace kvq {
 namespace {
 
 constexpr int kTile = 64;       // INT8 tile = LDS stage (positions)
-constexpr int kGroupRows = 256; // (position, query head) rows per attention work group
-constexpr int kAttnWaves = 8;   // attention waves per work group
+constexpr int kGroupRows = 128; // (position, query head) rows per attention work group
+constexpr int kAttnWaves = 4;   // attention waves per work group
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kCB = kGroupRows / 16 / kAttnWaves;  // 16-row column blocks per wave
 constexpr float kLazy = 8.0f;   // log2 headroom of the running maximum
+constexpr int kRing = 2;        // LDS stages: the copy of stage s + kRing - 1 overlaps stage s
+constexpr int kColBlocks = kGroupRows / 16;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -63,10 +66,11 @@ struct PfArgs {
   const uint8_t *cls;            // [batch][hkv][n_max] (1 = vertical line) or null
   const int32_t *n_tokens;
   int32_t batch, n_max, hq, hkv, g, window, tiles;
+  int32_t hsplit;                // attention work groups per (position block, KV head)
   int8_t *q_codes, *k_codes;     // like q, k
   float *q_scales, *k_scales;    // [batch][hq][tiles], [batch][hkv][tiles]
   uint16_t *vt;                  // fp16 [batch][hkv][128][n_max]; vertical lines, t >= n: 0
-  float *keep;                   // [batch][hkv][n_max]: 1 for live keys that are not lines
+  uint16_t *keep;                // fp16 [batch][hkv][n_max]: 1 for live keys that are not lines
   int32_t *vl_pos;               // [batch][hkv][n_max]: line positions in order, then INT32_MAX
   int32_t *vl_cnt;               // [batch][hkv][tiles]: lines at positions < 64 (tile + 1)
   uint16_t *vl_k;                // bf16 [batch][hkv][n_max][128]: line K rows, then 0
@@ -149,7 +153,7 @@ __global__ void __launch_bounds__(256) pf_vt_kernel(PfArgs a) {
     const int t = tile * kTile + tid;
     const bool k = t < n && !(a.cls && a.cls[bh * a.n_max + t] == 1);
     kept[tid] = k ? 1 : 0;
-    a.keep[bh * a.n_max + t] = k ? 1.0f : 0.0f;
+    a.keep[bh * a.n_max + t] = k ? 0x3C00u : 0u;  // fp16 1.0, 0.0
   }
   __syncthreads();
   for (int i = tid; i < kTile * kHeadDim / 2; i += 256) {  // 2 channels per step
@@ -241,17 +245,26 @@ __global__ void __launch_bounds__(256) pf_vl_gather_kernel(PfArgs a) {
 // ---- attention ----------------------------------------------------------------------
 
 // One stage in LDS: 64 keys of K (INT8 rows of 128 B, or bf16 rows of 256 B), V^T (128
-// channel rows of 64 fp16 keys) and 64 words of side data (keep weights, or line
-// positions).  16-byte chunks are XOR-swizzled within a row so that the 8 lanes an LDS
-// read serves at once hit 8 different chunk positions: a key row's chunk c sits at
-// c ^ swz_k(key), a channel row's at c ^ (channel & 7).
+// channel rows of 64 fp16 keys) and 256 B of side data (fp16 keep weights, or line
+// positions).  16-byte chunks are XOR-swizzled within a row so that the 16 lanes a
+// 16-byte LDS read serves at once hit 16 different banks quads: a key row's chunk c sits
+// at c ^ swz_k(key) (INT8) or c ^ swz_w(key) (bf16), a channel row's at c ^ swz_v(ch).
 struct __align__(16) PfStage {
   uint8_t k[kTile * 256];
   uint8_t v[kHeadDim * kTile * 2];
-  float aux[kTile];
+  uint32_t aux[kTile];
 };
 
-__device__ __forceinline__ int swz_k(int key) { return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | ((key & 1) << 2); }
+// The A-operand rows a 16-lane group reads are keys {0..3, 8..11, 16..19, 24..27} (+4,
+// +32): even and odd keys land in different bank halves of a 128-byte row pair, and the
+// swizzle gives the 8 keys of each parity 8 different chunks.
+__device__ __forceinline__ int swz_k(int key) {
+  return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | (((key >> 4) & 1) << 2);
+}
+// 256-byte rows span every bank: the parity picks the other half of the 16 chunks.
+__device__ __forceinline__ int swz_w(int key) { return swz_k(key) | ((key & 1) << 3); }
+// Channel rows 16 ct .. 16 ct + 15: parity picks the bank half, ch / 2 the chunk.
+__device__ __forceinline__ int swz_v(int ch) { return (ch >> 1) & 7; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 
@@ -279,7 +292,7 @@ __device__ __forceinline__ void issue_stage(const PfArgs &a, const PfPlan &pl, i
   const void *kp, *vp, *xp;
   uint32_t krow;
   int32_t k0;
-  bool wide;
+  bool wide, lines = false;
   if (sigma < pl.n8) {
     k0 = sigma * kTile;
     wide = false;
@@ -289,7 +302,7 @@ __device__ __forceinline__ void issue_stage(const PfArgs &a, const PfPlan &pl, i
     xp = a.keep + bh * a.n_max;
   } else if (sigma < pl.n8 + pl.nvl) {
     k0 = (sigma - pl.n8) * kTile;
-    wide = true;
+    wide = lines = true;
     kp = a.vl_k + bh * a.n_max * kHeadDim;
     krow = kHeadDim * 2;
     vp = a.vl_vt + bh * kHeadDim * a.n_max;
@@ -313,22 +326,26 @@ __device__ __forceinline__ void issue_stage(const PfArgs &a, const PfPlan &pl, i
   } else {
 #pragma unroll
     for (int i = 0; i < 16 / kAttnWaves; ++i) {  // 1 KB = 4 keys of 256 B
-      const int blk = w + kAttnWaves * i, key = 4 * blk + (lane >> 4), c = (lane & 15) ^ swz_k(key);
+      const int blk = w + kAttnWaves * i, key = 4 * blk + (lane >> 4), c = (lane & 15) ^ swz_w(key);
       dma_block(kl + 1024u * blk, kb, (uint32_t)(k0 + key) * krow + 16u * c);
     }
   }
 #pragma unroll
   for (int i = 0; i < 16 / kAttnWaves; ++i) {  // 1 KB = 8 channels x 64 keys
-    const int blk = w + kAttnWaves * i, ch = 8 * blk + (lane >> 3), c = (lane & 7) ^ (ch & 7);
+    const int blk = w + kAttnWaves * i, ch = 8 * blk + (lane >> 3), c = (lane & 7) ^ swz_v(ch);
     dma_block(vl + 1024u * blk, vb, ((uint32_t)ch * (uint32_t)a.n_max + (uint32_t)k0 + 8u * c) * 2u);
   }
-  if (w == 0 && lane < 16) dma_block(lds_addr(S.aux), xb, (uint32_t)(k0 + 4 * lane) * 4u);
+  // Side data: 64 fp16 keep weights (128 B), or 64 line positions (256 B).
+  if (w == 0 && lane < (lines ? 16 : 8)) dma_block(lds_addr(S.aux), xb, (uint32_t)k0 * (lines ? 4u : 2u) + 16u * lane);
 }
 
 // Per-lane softmax state and output accumulators of the wave's four column blocks.
+// The row sums ride along as a ninth P.V tile whose A operand is the keep weight of each
+// key in every row: row 0 of it (lane (col, 0), element 0) is column col's sum.
 struct PfState {
   v4f acc[8][kCB];  // O^T tiles: [channel tile][column block]
-  float m[kCB], l[kCB];
+  v4f sum[kCB];     // row sums
+  float m[kCB];
 };
 
 enum PfKind { kInt8 = 0, kInt8Edge = 1, kLines = 2, kWindow = 3 };
@@ -338,13 +355,6 @@ __device__ __forceinline__ float col_max(float x) {  // over the 4 lanes of a co
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float col_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {  // round to nearest even
@@ -361,9 +371,12 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
   constexpr bool kI8 = kKind == kInt8 || kKind == kInt8Edge;
   constexpr bool kMasked = kKind != kInt8;
   const int r = lane & 15, rg = lane >> 4;
+  // Scores of both halves first: the second half's products run on the matrix cores
+  // while the first half's softmax runs on the vector ALUs.
+  using Raw = typename std::conditional<kI8, v4i, v4f>::type;
+  Raw raw[2][2][kCB];  // [half][u][column block]
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    float x[kCB][8];
+  for (int half = 0; half < 2; ++half)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int key = 32 * half + 8 * (r >> 2) + 4 * u + (r & 3);
@@ -375,29 +388,47 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) {
           v4i s32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[0], qi[cb][0], v4i{0, 0, 0, 0}, 0, 0, 0);
-          s32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[1], qi[cb][1], s32, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[cb][4 * u + i] = (float)s32[i];
+          raw[half][u][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[1], qi[cb][1], s32, 0, 0, 0);
         }
       } else {
         bf8 ka[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          ka[m] = *reinterpret_cast<const bf8 *>(S.k + key * 256 + 16 * ((4 * m + rg) ^ swz_k(key)));
+          ka[m] = *reinterpret_cast<const bf8 *>(S.k + key * 256 + 16 * ((4 * m + rg) ^ swz_w(key)));
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) {
           v4f sf = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 4; ++m) sf = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], qf[cb][m], sf, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[cb][4 * u + i] = sf[i];
+          raw[half][u][cb] = sf;
         }
       }
     }
-    // Side data of this lane's 8 keys.
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    float x[kCB][8];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[cb][4 * u + i] = (float)raw[half][u][cb][i];
+    // Side data of this lane's 8 keys: keep weights (INT8 and window stages; the A
+    // operand of the row-sum tile), or positions (line stages).
     const int e0 = 32 * half + 8 * rg;
-    const v4f w0 = *reinterpret_cast<const v4f *>(S.aux + e0), w1 = *reinterpret_cast<const v4f *>(S.aux + e0 + 4);
-    const float side[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    h8 keep8;
+    int32_t pos8[8];
+    if constexpr (kKind == kLines) {
+      const v4i p0 = *reinterpret_cast<const v4i *>(S.aux + e0), p1 = *reinterpret_cast<const v4i *>(S.aux + e0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pos8[e] = p0[e];
+        pos8[4 + e] = p1[e];
+      }
+      keep8 = h8{1, 1, 1, 1, 1, 1, 1, 1};  // masked entries weigh 0 already
+    } else {
+      keep8 = *reinterpret_cast<const h8 *>(reinterpret_cast<const uint8_t *>(S.aux) + 2 * e0);
+    }
     if constexpr (kMasked) {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb)
@@ -406,8 +437,8 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
           const int32_t key = k0 + e0 + e;
           bool ok;
           if constexpr (kKind == kInt8Edge) ok = key <= tq[cb] - window;
-          else if constexpr (kKind == kLines) ok = __float_as_int(side[e]) <= tq[cb];
-          else ok = key <= tq[cb] && key > tq[cb] - window && side[e] > 0.0f;
+          else if constexpr (kKind == kLines) ok = pos8[e] <= tq[cb];
+          else ok = key <= tq[cb] && key > tq[cb] - window && keep8[e] > (_Float16)0;
           x[cb][e] = ok ? x[cb][e] : -INFINITY;
         }
     }
@@ -417,8 +448,10 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
     bool grow = false;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
-      float mx = fmaxf(fmaxf(fmaxf(x[cb][0], x[cb][1]), fmaxf(x[cb][2], x[cb][3])),
-                       fmaxf(fmaxf(x[cb][4], x[cb][5]), fmaxf(x[cb][6], x[cb][7])));
+      float mx = __builtin_fmaxf(__builtin_fmaxf(x[cb][0], x[cb][1]), x[cb][2]);
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, x[cb][3]), x[cb][4]);
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, x[cb][5]), x[cb][6]);
+      mx = __builtin_fmaxf(mx, x[cb][7]);
       bmax[cb] = col_max(mx) * coef[cb];
       grow |= bmax[cb] > st.m[cb] + kLazy;
     }
@@ -428,7 +461,7 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
         const float mn = fmaxf(st.m[cb], bmax[cb]);
         const float al = __builtin_amdgcn_exp2f(st.m[cb] - mn);
         st.m[cb] = mn;
-        st.l[cb] *= al;
+        st.sum[cb] *= al;
         // One tile at a time: the accumulators stay in the matrix registers, with a
         // few temporaries, instead of all moving out at once.
 #pragma unroll
@@ -438,17 +471,14 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
         }
       }
     }
-    // Weights: p = 2^(x coef - m), fp16 for P.V; INT8 keys enter the row sum through
-    // the keep mask (their lines' and dead keys' V columns are 0 already).
+    // Weights: p = 2^(x coef - m), fp16 for P.V and the row sums; INT8 keys enter the
+    // row sum through the keep weights (their lines' and dead keys' V columns are 0).
     h8 pw[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(x[cb][e], coef[cb], -st.m[cb]));
-        st.l[cb] = kI8 ? fmaf(p[e], side[e], st.l[cb]) : st.l[cb] + p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(x[cb][e], coef[cb], -st.m[cb]));
       pw[cb] = __builtin_bit_cast(h8, make_uint4(pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]),
                                                  pack_f16(p[6], p[7])));
     }
@@ -456,31 +486,35 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       const int ch = 16 * ct + r;
-      const h8 va = *reinterpret_cast<const h8 *>(S.v + ch * 128 + 16 * ((4 * half + rg) ^ (ch & 7)));
+      const h8 va = *reinterpret_cast<const h8 *>(S.v + ch * 128 + 16 * ((4 * half + rg) ^ swz_v(ch)));
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) st.acc[ct][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pw[cb], st.acc[ct][cb], 0, 0, 0);
     }
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) st.sum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(keep8, pw[cb], st.sum[cb], 0, 0, 0);
   }
 }
 
-__global__ void __launch_bounds__(kAttnThreads) pf_attn_kernel(PfArgs a) {
-  __shared__ PfStage stage[2];
+__global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
+  __shared__ PfStage stage[kRing];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, rg = lane >> 4;
   const int n_bh = a.batch * a.hkv;
-  const int qp = kGroupRows / a.g;                     // positions per work group
+  const int hw = a.g / a.hsplit;                       // query heads per work group
+  const int per_head = kColBlocks / hw;                // column blocks per query head
+  const int qp = 16 * per_head;                        // positions per work group
   const int n_blk = (a.n_max + qp - 1) / qp;
-  const int blk = n_blk - 1 - (int)(blockIdx.x / n_bh);  // longest rows first
+  const int rest = (int)(blockIdx.x / n_bh), hs = rest % a.hsplit;
+  const int blk = n_blk - 1 - rest / a.hsplit;         // longest rows first
   const int bh = (int)(blockIdx.x % n_bh), b = bh / a.hkv, h = bh % a.hkv;
   const int32_t p0 = blk * qp;
   int32_t n = checked_n(a, b);
   if (n < 0) n = 0;
-  // Column blocks kCB w + c: query head h g + hg, positions pos0 .. pos0 + 15.
-  const int per_head = 16 / a.g;
+  // Column blocks kCB w + c: query head h g + hs hw + hg, positions pos0 .. pos0 + 15.
   int32_t tq[kCB], jq[kCB], pos0[kCB];
 #pragma unroll
   for (int c = 0; c < kCB; ++c) {
     const int cbg = kCB * w + c;
-    jq[c] = h * a.g + cbg / per_head;
+    jq[c] = h * a.g + hs * hw + cbg / per_head;
     pos0[c] = p0 + 16 * (cbg % per_head);
     tq[c] = pos0[c] + col;
   }
@@ -512,7 +546,7 @@ __global__ void __launch_bounds__(kAttnThreads) pf_attn_kernel(PfArgs a) {
 #pragma unroll
   for (int c = 0; c < kCB; ++c) {
     st.m[c] = -1.0e30f;
-    st.l[c] = 0.0f;
+    st.sum[c] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) st.acc[ct][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -530,27 +564,45 @@ __global__ void __launch_bounds__(kAttnThreads) pf_attn_kernel(PfArgs a) {
   }
   const float *ks = a.k_scales + (int64_t)bh * a.tiles;
 
-  if (total > 0) issue_stage(a, pl, 0, stage[0], b, h, w, lane);
+  // A wave's copies per stage: K and V^T blocks, and the side words on wave 0.  Before
+  // stage s is read, only the copies of the stages after it may still be in flight.
+  auto copies = [&](int sg) {
+    if (sg >= total) return 0;
+    return (sg >= pl.n8 ? 16 : 8) / kAttnWaves + 16 / kAttnWaves + (w == 0 ? 1 : 0);
+  };
+  auto wait_for = [&](int sg) {
+    int later = 0;
+#pragma unroll
+    for (int i = 1; i < kRing - 1; ++i) later += copies(sg + i);
+    switch (later) {
+#define KVQ_WAIT(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+      KVQ_WAIT(1) KVQ_WAIT(2) KVQ_WAIT(3) KVQ_WAIT(4) KVQ_WAIT(5) KVQ_WAIT(6) KVQ_WAIT(7) KVQ_WAIT(8)
+      KVQ_WAIT(9) KVQ_WAIT(10) KVQ_WAIT(11) KVQ_WAIT(12) KVQ_WAIT(13) KVQ_WAIT(14) KVQ_WAIT(15) KVQ_WAIT(16)
+#undef KVQ_WAIT
+      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+    __syncthreads();
+    if (sg + kRing - 1 < total) issue_stage(a, pl, sg + kRing - 1, stage[(sg + kRing - 1) % kRing], b, h, w, lane);
+  };
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i)
+    if (i < total) issue_stage(a, pl, i, stage[i], b, h, w, lane);
   int sigma = 0;
   // INT8 stages: first those whose keys every row reads in INT8, then the ones that
   // reach the window.
   for (; sigma < pl.n8_clean; ++sigma) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
+    wait_for(sigma);
     const float sk = ks[sigma];
 #pragma unroll
     for (int c = 0; c < kCB; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
-    attend_stage<kInt8>(stage[sigma & 1], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
+    attend_stage<kInt8>(stage[sigma % kRing], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
   }
   for (; sigma < pl.n8; ++sigma) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
+    wait_for(sigma);
     const float sk = ks[sigma];
 #pragma unroll
     for (int c = 0; c < kCB; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
-    attend_stage<kInt8Edge>(stage[sigma & 1], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
+    attend_stage<kInt8Edge>(stage[sigma % kRing], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
   }
   // Full-precision segments: bf16 queries (0 for rows past the request's length).
 #pragma unroll
@@ -566,21 +618,17 @@ __global__ void __launch_bounds__(kAttnThreads) pf_attn_kernel(PfArgs a) {
     coef[c] = kScale;
   }
   for (; sigma < pl.n8 + pl.nvl; ++sigma) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
-    attend_stage<kLines>(stage[sigma & 1], st, qi, qf, coef, tq, 0, a.window, lane);
+    wait_for(sigma);
+    attend_stage<kLines>(stage[sigma % kRing], st, qi, qf, coef, tq, 0, a.window, lane);
   }
   for (; sigma < total; ++sigma) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (sigma + 1 < total) issue_stage(a, pl, sigma + 1, stage[(sigma + 1) & 1], b, h, w, lane);
-    attend_stage<kWindow>(stage[sigma & 1], st, qi, qf, coef, tq, (pl.w_first + sigma - pl.n8 - pl.nvl) * kTile,
-                          a.window, lane);
+    wait_for(sigma);
+    attend_stage<kWindow>(stage[sigma % kRing], st, qi, qf, coef, tq,
+                          (pl.w_first + sigma - pl.n8 - pl.nvl) * kTile, a.window, lane);
   }
 #pragma unroll
   for (int c = 0; c < kCB; ++c) {
-    const float l = col_sum(st.l[c]);
+    const float l = __shfl(st.sum[c][0], col);  // lane (col, 0) holds the column's sum
     const bool live = tq[c] < n && l > 0.0f;
     const float inv = live ? 1.0f / l : 0.0f;
     float vals[32];
@@ -598,8 +646,8 @@ kvq_status launched(const char *what) {
   return KVQ_OK;
 }
 
-// Workspace regions (each 256-byte aligned), in this order: vt, keep, vl_pos, vl_cnt,
-// vl_k, vl_vt.
+// Workspace regions (each 256-byte aligned), in this order: vt (fp16), keep (fp16),
+// vl_pos, vl_cnt (int32), vl_k (bf16), vl_vt (fp16).
 struct PfLayout {
   size_t vt, keep, vl_pos, vl_cnt, vl_k, vl_vt, total;
 };
@@ -612,7 +660,7 @@ PfLayout pf_layout(int64_t batch, int64_t n_max, int64_t hkv) {
   L.vt = o;
   o = up(o + bh * kHeadDim * n * 2);
   L.keep = o;
-  o = up(o + bh * n * 4);
+  o = up(o + bh * n * 2);
   L.vl_pos = o;
   o = up(o + bh * n * 4);
   L.vl_cnt = o;
@@ -675,6 +723,7 @@ kvq_status pf_setup(PfArgs &a, const void *q, const void *k, const void *v, int3
   a.hq = hq;
   a.hkv = hkv;
   a.g = g;
+  a.hsplit = g > kColBlocks ? g / kColBlocks : 1;
   a.window = window;
   a.tiles = n_max / kTile;
   a.q_codes = q_codes;
@@ -682,7 +731,7 @@ kvq_status pf_setup(PfArgs &a, const void *q, const void *k, const void *v, int3
   a.q_scales = q_scales;
   a.k_scales = k_scales;
   a.vt = reinterpret_cast<uint16_t *>(ws + L.vt);
-  a.keep = reinterpret_cast<float *>(ws + L.keep);
+  a.keep = reinterpret_cast<uint16_t *>(ws + L.keep);
   a.vl_pos = reinterpret_cast<int32_t *>(ws + L.vl_pos);
   a.vl_cnt = reinterpret_cast<int32_t *>(ws + L.vl_cnt);
   a.vl_k = reinterpret_cast<uint16_t *>(ws + L.vl_k);
@@ -732,8 +781,9 @@ extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, int32_t dty
                            empty);
   if (st != KVQ_OK || empty) return st;
   if (!out) return fail(KVQ_ERR_INVALID_ARG, "NULL out");
-  const int64_t n_blk = (n_max + kGroupRows / a.g - 1) / (kGroupRows / a.g);
-  if (n_blk * batch * hkv > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
-  hipLaunchKernelGGL(pf_attn_kernel, dim3((uint32_t)(n_blk * batch * hkv)), dim3(kAttnThreads), 0, static_cast<hipStream_t>(stream), a);
+  const int64_t qp = 16 * (kColBlocks / (a.g / a.hsplit));
+  const int64_t n_blk = (n_max + qp - 1) / qp, groups = n_blk * a.hsplit * batch * hkv;
+  if (groups > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  hipLaunchKernelGGL(pf_attn_kernel, dim3((uint32_t)groups), dim3(kAttnThreads), 0, static_cast<hipStream_t>(stream), a);
   return launched("pf_attn_kernel");
 }

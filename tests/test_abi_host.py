@@ -179,7 +179,7 @@ def test_balanced_split_counts_minimal_cap(kvq):
 
 
 def test_prefill_workspace_and_validation(kvq):
-    """The prefill scratch size follows its region list (V^T fp16, keep mask, line
+    """The prefill scratch size follows its region list (V^T fp16, fp16 keep mask, line
     positions, per-tile line counts, gathered K and V^T, each 256-byte aligned); the
     entry point rejects g outside {1, 2, 4, 8, 16}, n_max off 64 and a short scratch
     before touching any pointer."""
@@ -188,7 +188,7 @@ def test_prefill_workspace_and_validation(kvq):
     for batch, n_max, hkv in ((1, 64, 1), (2, 1024, 8), (3, 192, 2)):
         bh = batch * hkv
         want = 0
-        for size in (bh * 128 * n_max * 2, bh * n_max * 4, bh * n_max * 4, bh * (n_max // 64) * 4,
+        for size in (bh * 128 * n_max * 2, bh * n_max * 2, bh * n_max * 4, bh * (n_max // 64) * 4,
                      bh * n_max * 128 * 2, bh * 128 * n_max * 2):
             want = up(want + size)
         assert lib.kvq_prefill_workspace_bytes(batch, n_max, hkv) == want
