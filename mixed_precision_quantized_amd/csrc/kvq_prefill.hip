@@ -45,7 +45,8 @@ constexpr int kAttnWaves = 4;   // attention waves per work group
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kCB = kGroupRows / 16 / kAttnWaves;  // 16-row column blocks per wave
 constexpr float kLazy = 8.0f;   // log2 headroom of the running maximum
-constexpr int kRing = 2;        // LDS stages: the copy of stage s + kRing - 1 overlaps stage s
+constexpr int kRing = 2;        // LDS stages: the copy of stage s + 1 overlaps stage s
+static_assert(kRing == 2, "the clean INT8 loop takes its LDS stages in pairs");
 constexpr int kColBlocks = kGroupRows / 16;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -274,70 +275,89 @@ __device__ __forceinline__ void dma_block(uint32_t lds, gbytes base, uint32_t vo
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
 }
 
-__device__ __forceinline__ gbytes uniform(const void *p) {
-  const uint64_t x = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-  return (gbytes)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
 // The work group's stage list: INT8 stages 0 .. n8 - 1 (key tiles 0 ..), line stages
 // (64 list entries each), window stages (key tiles w_first ..).
 struct PfPlan {
   int32_t n8, n8_clean, nvl, nwin, w_first;
 };
 
-__device__ __forceinline__ void issue_stage(const PfArgs &a, const PfPlan &pl, int sigma, PfStage &S, int b, int h,
-                                            int w, int lane) {
-  const int64_t bh = (int64_t)b * a.hkv + h;
-  const void *kp, *vp, *xp;
-  uint32_t krow;
-  int32_t k0;
-  bool wide, lines = false;
-  if (sigma < pl.n8) {
-    k0 = sigma * kTile;
-    wide = false;
-    kp = a.k_codes + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim;
-    krow = (uint32_t)a.hkv * kHeadDim;
-    vp = a.vt + bh * kHeadDim * a.n_max;
-    xp = a.keep + bh * a.n_max;
-  } else if (sigma < pl.n8 + pl.nvl) {
-    k0 = (sigma - pl.n8) * kTile;
-    wide = lines = true;
-    kp = a.vl_k + bh * a.n_max * kHeadDim;
-    krow = kHeadDim * 2;
-    vp = a.vl_vt + bh * kHeadDim * a.n_max;
-    xp = a.vl_pos + bh * a.n_max;
-  } else {
-    k0 = (pl.w_first + sigma - pl.n8 - pl.nvl) * kTile;
-    wide = true;
-    kp = a.k + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim;
-    krow = (uint32_t)a.hkv * kHeadDim * 2;
-    vp = a.vt + bh * kHeadDim * a.n_max;
-    xp = a.keep + bh * a.n_max;
-  }
-  const gbytes kb = uniform(kp), vb = uniform(vp), xb = uniform(xp);
-  const uint32_t kl = lds_addr(S.k), vl = lds_addr(S.v);
-  if (!wide) {
+// A wave-uniform pointer, held in scalar registers.
+__device__ __forceinline__ gbytes uniform(const void *p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (gbytes)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Copies of one stage into LDS.  Each lane's offsets within a stage are fixed, so they
+// are computed once; a stage only moves the (wave-uniform) base pointers.
+struct PfCopier {
+  gbytes kc, kin, kvl, vt, vlvt, keep, vlpos;  // this (request, KV head)'s arrays
+  uint32_t krow8, krow16;                       // K row strides: INT8 codes, bf16 input
+  uint32_t o8[8 / kAttnWaves];                  // INT8 K: key * krow8 + 16 c
+  uint32_t ow[16 / kAttnWaves];                 // bf16 K of the input: key * krow16 + 16 c
+  uint32_t ov[16 / kAttnWaves];                 // V^T: ch * n_max * 2 + 16 c
+  int w, lane;
+
+  __device__ PfCopier(const PfArgs &a, int b, int h, int w_, int lane_) : w(w_), lane(lane_) {
+    const int64_t bh = (int64_t)b * a.hkv + h;
+    kc = uniform(a.k_codes + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim);
+    kin = uniform(a.k + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim);
+    kvl = uniform(a.vl_k + bh * a.n_max * kHeadDim);
+    vt = uniform(a.vt + bh * kHeadDim * a.n_max);
+    vlvt = uniform(a.vl_vt + bh * kHeadDim * a.n_max);
+    keep = uniform(a.keep + bh * a.n_max);
+    vlpos = uniform(a.vl_pos + bh * a.n_max);
+    krow8 = (uint32_t)a.hkv * kHeadDim;
+    krow16 = 2 * krow8;
 #pragma unroll
     for (int i = 0; i < 8 / kAttnWaves; ++i) {  // 1 KB = 8 keys of 128 B
-      const int blk = w + kAttnWaves * i, key = 8 * blk + (lane >> 3), c = (lane & 7) ^ swz_k(key);
-      dma_block(kl + 1024u * blk, kb, (uint32_t)(k0 + key) * krow + 16u * c);
+      const int key = 8 * (w + kAttnWaves * i) + (lane >> 3);
+      o8[i] = (uint32_t)key * krow8 + 16u * (uint32_t)((lane & 7) ^ swz_k(key));
     }
-  } else {
 #pragma unroll
     for (int i = 0; i < 16 / kAttnWaves; ++i) {  // 1 KB = 4 keys of 256 B
-      const int blk = w + kAttnWaves * i, key = 4 * blk + (lane >> 4), c = (lane & 15) ^ swz_w(key);
-      dma_block(kl + 1024u * blk, kb, (uint32_t)(k0 + key) * krow + 16u * c);
+      const int key = 4 * (w + kAttnWaves * i) + (lane >> 4);
+      ow[i] = (uint32_t)key * krow16 + 16u * (uint32_t)((lane & 15) ^ swz_w(key));
+    }
+#pragma unroll
+    for (int i = 0; i < 16 / kAttnWaves; ++i) {  // 1 KB = 8 channels x 64 keys
+      const int ch = 8 * (w + kAttnWaves * i) + (lane >> 3);
+      ov[i] = (uint32_t)ch * (uint32_t)a.n_max * 2u + 16u * (uint32_t)((lane & 7) ^ swz_v(ch));
     }
   }
+
+  __device__ __forceinline__ void issue(const PfPlan &pl, int sigma, PfStage &S) const {
+    const uint32_t kl = lds_addr(S.k), vl = lds_addr(S.v), xl = lds_addr(S.aux);
+    if (sigma < pl.n8) {  // INT8 codes, V^T, keep weights
+      const int32_t k0 = sigma * kTile;
+      const gbytes kb = kc + (uint64_t)k0 * krow8, vb = vt + 2 * k0;
 #pragma unroll
-  for (int i = 0; i < 16 / kAttnWaves; ++i) {  // 1 KB = 8 channels x 64 keys
-    const int blk = w + kAttnWaves * i, ch = 8 * blk + (lane >> 3), c = (lane & 7) ^ swz_v(ch);
-    dma_block(vl + 1024u * blk, vb, ((uint32_t)ch * (uint32_t)a.n_max + (uint32_t)k0 + 8u * c) * 2u);
+      for (int i = 0; i < 8 / kAttnWaves; ++i) dma_block(kl + 1024u * (w + kAttnWaves * i), kb, o8[i]);
+#pragma unroll
+      for (int i = 0; i < 16 / kAttnWaves; ++i) dma_block(vl + 1024u * (w + kAttnWaves * i), vb, ov[i]);
+      if (w == 0 && lane < 8) dma_block(xl, keep + 2 * k0, 16u * lane);
+    } else if (sigma < pl.n8 + pl.nvl) {  // gathered line rows, their V^T, positions
+      const int32_t e0 = (sigma - pl.n8) * kTile;
+      const gbytes kb = kvl + (uint64_t)e0 * (kHeadDim * 2), vb = vlvt + 2 * e0;
+#pragma unroll
+      for (int i = 0; i < 16 / kAttnWaves; ++i) {
+        const int key = 4 * (w + kAttnWaves * i) + (lane >> 4);
+        dma_block(kl + 1024u * (w + kAttnWaves * i), kb, (uint32_t)key * 256u + 16u * (uint32_t)((lane & 15) ^ swz_w(key)));
+      }
+#pragma unroll
+      for (int i = 0; i < 16 / kAttnWaves; ++i) dma_block(vl + 1024u * (w + kAttnWaves * i), vb, ov[i]);
+      if (w == 0 && lane < 16) dma_block(xl, vlpos + 4 * e0, 16u * lane);
+    } else {  // bf16 K rows of the input, V^T, keep weights
+      const int32_t k0 = (pl.w_first + sigma - pl.n8 - pl.nvl) * kTile;
+      const gbytes kb = kin + (uint64_t)k0 * krow16, vb = vt + 2 * k0;
+#pragma unroll
+      for (int i = 0; i < 16 / kAttnWaves; ++i) dma_block(kl + 1024u * (w + kAttnWaves * i), kb, ow[i]);
+#pragma unroll
+      for (int i = 0; i < 16 / kAttnWaves; ++i) dma_block(vl + 1024u * (w + kAttnWaves * i), vb, ov[i]);
+      if (w == 0 && lane < 8) dma_block(xl, keep + 2 * k0, 16u * lane);
+    }
   }
-  // Side data: 64 fp16 keep weights (128 B), or 64 line positions (256 B).
-  if (w == 0 && lane < (lines ? 16 : 8)) dma_block(lds_addr(S.aux), xb, (uint32_t)k0 * (lines ? 4u : 2u) + 16u * lane);
-}
+};
 
 // Per-lane softmax state and output accumulators of the wave's four column blocks.
 // The row sums ride along as a ninth P.V tile whose A operand is the keep weight of each
@@ -442,9 +462,10 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
           x[cb][e] = ok ? x[cb][e] : -INFINITY;
         }
     }
-    // Step maximum per column (coef >= FLT_MIN, so -inf stays -inf); the running
-    // maximum moves only by more than kLazy.
-    float bmax[kCB];
+    // The running maximum moves only when a score passes it by more than kLazy: each
+    // lane tests its own 8 scores (coef >= FLT_MIN, so -inf stays -inf), and only then
+    // do the 4 lanes of a column agree on its new maximum.
+    float lmax[kCB];
     bool grow = false;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
@@ -452,13 +473,13 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
       mx = __builtin_fmaxf(__builtin_fmaxf(mx, x[cb][3]), x[cb][4]);
       mx = __builtin_fmaxf(__builtin_fmaxf(mx, x[cb][5]), x[cb][6]);
       mx = __builtin_fmaxf(mx, x[cb][7]);
-      bmax[cb] = col_max(mx) * coef[cb];
-      grow |= bmax[cb] > st.m[cb] + kLazy;
+      lmax[cb] = mx * coef[cb];
+      grow |= lmax[cb] > st.m[cb] + kLazy;
     }
     if (__any(grow)) {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
-        const float mn = fmaxf(st.m[cb], bmax[cb]);
+        const float mn = fmaxf(st.m[cb], col_max(lmax[cb]));
         const float al = __builtin_amdgcn_exp2f(st.m[cb] - mn);
         st.m[cb] = mn;
         st.sum[cb] *= al;
@@ -497,7 +518,8 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
 
 __global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
   __shared__ PfStage stage[kRing];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, rg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, rg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   const int n_bh = a.batch * a.hkv;
   const int hw = a.g / a.hsplit;                       // query heads per work group
   const int per_head = kColBlocks / hw;                // column blocks per query head
@@ -564,6 +586,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
   }
   const float *ks = a.k_scales + (int64_t)bh * a.tiles;
 
+  const PfCopier cp(a, b, h, w, lane);
   // A wave's copies per stage: K and V^T blocks, and the side words on wave 0.  Before
   // stage s is read, only the copies of the stages after it may still be in flight.
   auto copies = [&](int sg) {
@@ -582,20 +605,30 @@ __global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
       default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
     __syncthreads();
-    if (sg + kRing - 1 < total) issue_stage(a, pl, sg + kRing - 1, stage[(sg + kRing - 1) % kRing], b, h, w, lane);
+    if (sg + kRing - 1 < total) cp.issue(pl, sg + kRing - 1, stage[(sg + kRing - 1) % kRing]);
   };
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i)
-    if (i < total) issue_stage(a, pl, i, stage[i], b, h, w, lane);
+    if (i < total) cp.issue(pl, i, stage[i]);
   int sigma = 0;
   // INT8 stages: first those whose keys every row reads in INT8, then the ones that
   // reach the window.
-  for (; sigma < pl.n8_clean; ++sigma) {
-    wait_for(sigma);
-    const float sk = ks[sigma];
+  // Two stages a pass (stage 2i in LDS stage 0, 2i + 1 in LDS stage 1), so that every
+  // LDS address is a lane base plus a constant.
+  auto clean = [&](int sg, const PfStage &S) {
+    wait_for(sg);
+    const float sk = ks[sg];
 #pragma unroll
     for (int c = 0; c < kCB; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
-    attend_stage<kInt8>(stage[sigma % kRing], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
+    attend_stage<kInt8>(S, st, qi, qf, coef, tq, sg * kTile, a.window, lane);
+  };
+  for (; sigma + 1 < pl.n8_clean; sigma += 2) {
+    clean(sigma, stage[0]);
+    clean(sigma + 1, stage[1]);
+  }
+  if (sigma < pl.n8_clean) {
+    clean(sigma, stage[0]);
+    ++sigma;
   }
   for (; sigma < pl.n8; ++sigma) {
     wait_for(sigma);
