@@ -101,3 +101,49 @@ def test_causality():
     out2, *_ = oracle.prefill_attend(q, k2, v2, [120], cls, window=32)
     assert np.array_equal(out[0, :64], out2[0, :64])                        # same tiles, earlier keys
     assert not np.allclose(out[0, 80:], out2[0, 80:])
+
+
+def test_window_edge_and_lines_on_an_exact_grid():
+    """Which keys each row reads through INT8, pinned exactly.  Q and K sit on INT8 grids
+    (integers times a power of two, 127 reached in every tile), except that a random
+    half of the K entries carry +1/4 of a step: INT8 reads such an entry as the grid
+    value, full precision reads it as it is.  One vertical line is far larger than
+    the tile maximum (left out of K's scale, else the grid would change).  Row t must
+    read key p exactly iff p is a line of its head or p > t - W; the expected rows are
+    plain causal softmax attention with that key set written out per row."""
+    r = np.random.default_rng(9)
+    batch, n, hq, hkv, w = 1, 192, 4, 2, 16
+    g = hq // hkv
+    sq, sk = 2.0 ** -6, 2.0 ** -5
+    qi = r.integers(-126, 127, (batch, n, hq, 128))
+    ki = r.integers(-126, 127, (batch, n, hkv, 128))
+    qi[:, ::64, :, 0] = 127
+    ki[:, ::64, :, 0] = 127
+    off = (r.random((batch, n, hkv, 128)) < 0.5) * 0.25
+    off[:, ::64, :, 0] = 0.0
+    cls = np.zeros((batch, hkv, n), np.uint8)
+    cls[0, 0, 5::13] = 1
+    cls[0, 1, 3::7] = 1
+    ki_line = ki.copy().astype(np.float64)
+    big = 70                                             # a line of head 0 in tile 1, channel 3
+    assert cls[0, 0, big] == 1
+    ki_line[0, big, 0, 3] = 400.0
+    q = (qi * sq).astype(np.float32)
+    k_exact = ((ki_line + off) * sk).astype(np.float32)
+    k_grid = (ki * sk).astype(np.float64)
+    v = r.standard_normal((batch, n, hkv, 128)).astype(np.float32)
+    out, qc, _, kc, ks = oracle.prefill_attend(q, k_exact, v, [n], cls, window=w)
+    assert np.all(ks == np.float32(sk))                  # the big line left every scale alone
+    lines_free = cls[0].T == 0                           # [n, hkv]
+    assert np.array_equal(kc[0][lines_free], ki[0][lines_free])
+    want = np.zeros((n, hq, 128))
+    for t in range(n):
+        p = np.arange(t + 1)
+        for j in range(hq):
+            h = j // g
+            exact = (cls[0, h, p] == 1) | (p > t - w)
+            keys = np.where(exact[:, None], k_exact[0, p, h].astype(np.float64), k_grid[0, p, h])
+            x = keys @ q[0, t, j].astype(np.float64) / np.sqrt(128.0)
+            e = np.exp(x - x.max())
+            want[t, j] = (e / e.sum()) @ v[0, p, h].astype(np.float64)
+    assert np.allclose(out[0], want, rtol=1e-12, atol=1e-12)
