@@ -412,6 +412,26 @@ kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch
 kvq_status kvq_balanced_split_counts(const int64_t *work, int32_t n, int32_t total_work, int32_t *out);
 
 /*
+ * Head groups of ragged tables and their memory [host] (Tangram: the KV heads of one
+ * group share a slot-map table, sized for the group's largest budget, and each head
+ * reads its own prefix of it).  budgets [host] float [hkv], 0 < r_h <= 1;
+ * heads_per_group H divides hkv.  Heads are grouped by budget: order [host] int32
+ * [hkv] receives the head ids by decreasing budget (ties: lower id first), and group
+ * i holds order[i H .. i H + H - 1] (consecutive in that order, which minimises the
+ * summed table lengths).  For a request of n_tokens, head h keeps ceil(r_h n)
+ * tokens and group i's table has table_slots[i] = max over its heads (int32
+ * [hkv / H]).  bytes [host] int64 [3], for the cache class cls (KVQ_INT2 / INT4 /
+ * FP16; kvq_block_bytes(cls) per head-page of 16 slots):
+ *   [0] grouped tables: sum_i ceil(table_slots[i] / 16) H block + 4 table_slots[i];
+ *   [1] a table per head: sum_h ceil(ceil(r_h n) / 16) block + 4 ceil(r_h n);
+ *   [2] no eviction: hkv ceil(n / 16) (block + 4).
+ * Errors: INVALID_ARG.
+ */
+kvq_status kvq_head_group_plan(const float *budgets, int32_t hkv, int32_t heads_per_group,
+                               int64_t n_tokens, int32_t cls, int32_t *order,
+                               int32_t *table_slots, int64_t *bytes);
+
+/*
  * Work groups (one wavefront each) of the decode kernel that fit on the current
  * device at once: *per_cu from the HIP occupancy API, *n_cu the compute-unit
  * count.  g (query heads per KV head) and table_kind select the kernel: page

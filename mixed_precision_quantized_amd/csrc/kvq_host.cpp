@@ -220,6 +220,37 @@ kvq_status kvq_balanced_split_counts(const int64_t *work, int32_t n, int32_t tot
   return KVQ_OK;
 }
 
+kvq_status kvq_head_group_plan(const float *budgets, int32_t hkv, int32_t heads_per_group, int64_t n_tokens,
+                               int32_t cls, int32_t *order, int32_t *table_slots, int64_t *bytes) {
+  if (!budgets || !order || !table_slots || !bytes || hkv <= 0 || heads_per_group <= 0 ||
+      hkv % heads_per_group || n_tokens < 0 || n_tokens > INT32_MAX)
+    return fail(KVQ_ERR_INVALID_ARG, "bad head-group arguments");
+  if (cls != KVQ_INT2 && cls != KVQ_INT4 && cls != KVQ_FP16) return fail(KVQ_ERR_INVALID_ARG, "unknown class %d", cls);
+  std::vector<int64_t> keep((size_t)hkv);
+  for (int32_t h = 0; h < hkv; ++h) {
+    if (!(budgets[h] > 0.0f && budgets[h] <= 1.0f)) return fail(KVQ_ERR_INVALID_ARG, "budget of head %d outside (0, 1]", h);
+    keep[(size_t)h] = (int64_t)std::ceil((double)budgets[h] * (double)n_tokens);
+    order[h] = h;
+  }
+  // Exchange argument: for groups of a fixed size, the padded total sum_i H max_i is
+  // smallest when each group takes the next H heads in decreasing order of budget.
+  std::stable_sort(order, order + hkv, [&](int32_t a, int32_t b) { return budgets[a] > budgets[b]; });
+  const int64_t block = (int64_t)kvq_block_bytes(cls), page = kPage;
+  auto pages = [&](int64_t slots) { return (slots + page - 1) / page; };
+  int64_t grouped = 0, exact = 0;
+  for (int32_t i = 0; i < hkv / heads_per_group; ++i) {
+    int64_t slots = 0;
+    for (int32_t k = 0; k < heads_per_group; ++k) slots = std::max(slots, keep[(size_t)order[i * heads_per_group + k]]);
+    table_slots[i] = (int32_t)slots;
+    grouped += pages(slots) * heads_per_group * block + 4 * slots;
+  }
+  for (int32_t h = 0; h < hkv; ++h) exact += pages(keep[(size_t)h]) * block + 4 * keep[(size_t)h];
+  bytes[0] = grouped;
+  bytes[1] = exact;
+  bytes[2] = (int64_t)hkv * pages(n_tokens) * (block + 4);
+  return KVQ_OK;
+}
+
 kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch, int32_t total_work,
                                 int32_t *out) {
   if (!budgets || !out || hkv <= 0 || batch <= 0 || total_work <= 0)

@@ -504,13 +504,16 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
                                                  pack_f16(p[6], p[7])));
     }
     // O^T += V^T P^T: lane (channel row r, key group rg) reads keys 32 half + 8 rg ...+7.
+    h8 va[8];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       const int ch = 16 * ct + r;
-      const h8 va = *reinterpret_cast<const h8 *>(S.v + ch * 128 + 16 * ((4 * half + rg) ^ swz_v(ch)));
-#pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) st.acc[ct][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pw[cb], st.acc[ct][cb], 0, 0, 0);
+      va[ct] = *reinterpret_cast<const h8 *>(S.v + ch * 128 + 16 * ((4 * half + rg) ^ swz_v(ch)));
     }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) st.acc[ct][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[ct], pw[cb], st.acc[ct][cb], 0, 0, 0);
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) st.sum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(keep8, pw[cb], st.sum[cb], 0, 0, 0);
   }

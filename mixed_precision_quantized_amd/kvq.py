@@ -79,6 +79,7 @@ _SIGS = {
     "kvq_aot_split_counts": ([_P, _i32, _i32, _i32, _P], ctypes.c_int),
     "kvq_balanced_split_counts": ([_P, _i32, _i32, _P], ctypes.c_int),
     "kvq_decode_occupancy": ([_i32, _i32, _P, _P], ctypes.c_int),
+    "kvq_head_group_plan": ([_P, _i32, _i32, _i64, _i32, _P, _P, _P], ctypes.c_int),
     "kvq_status_string": ([_i32], ctypes.c_char_p),
     "kvq_last_error": ([], ctypes.c_char_p),
 }
@@ -370,6 +371,19 @@ def plan_splits(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int,
                                 _hptr(tps), int(target_bytes), _hptr(out), max_out,
                                 ctypes.byref(n_out), _hptr(offsets)), "kvq_plan_splits")
     return out[: n_out.value].copy(), offsets
+
+
+def head_group_plan(budgets: np.ndarray, heads_per_group: int, n_tokens: int, cls: int = 1):
+    """(order int32 [hkv], table_slots int32 [hkv / H], bytes int64 [3]: grouped,
+    per-head, no eviction) for ragged head-group tables (host)."""
+    b = np.ascontiguousarray(budgets, np.float32)
+    hkv = b.shape[0]
+    order = np.zeros(hkv, np.int32)
+    slots = np.zeros(max(hkv // max(heads_per_group, 1), 1), np.int32)
+    nbytes = np.zeros(3, np.int64)
+    _check(_lib.kvq_head_group_plan(_hptr(b), hkv, heads_per_group, n_tokens, cls, _hptr(order), _hptr(slots),
+                                    _hptr(nbytes)), "kvq_head_group_plan")
+    return order, slots, nbytes
 
 
 def aot_split_counts(budgets: np.ndarray, batch: int, total_work: int) -> np.ndarray:
