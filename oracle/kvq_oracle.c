@@ -131,12 +131,50 @@ void orc_quantize(const float *x, int32_t n, int64_t stride, int32_t bits,
  *   pair at 512: 64 fp16 scales then 64 fp16 zeros (the even page of the pair
  *   holds channels 0-63, the odd page 64-127); V codes [16 tok][32 B] at 768;
  *   V meta [4 groups][16 tok][scale, zero] at 1280.
- * FP16 (8192 B): K [16 tok][128] fp16 at 0; V at 4096. */
+ * FP16 (8192 B): K [16 tok][128] fp16 at 0; V at 4096.
+ * FP8 anchors (4160 B, the FP16 class of a cache with anchor_fp8): K codes
+ *   [16 tok][128 B] at 0, K scales [16] fp16 at 2048, V codes [16][128 B] at
+ *   2080, V scales [16] fp16 at 4128. */
 enum {
     I4_KC = 0, I4_KM = 1024, I4_VC = 1280, I4_VM = 2304, I4_BYTES = 2560,
     I2_KC = 0, I2_KS = 512, I2_KZ = 640, I2_VC = 768, I2_VM = 1280, I2_BYTES = 1536,
-    F16_K = 0, F16_V = 4096, F16_BYTES = 8192
+    F16_K = 0, F16_V = 4096, F16_BYTES = 8192,
+    F8_K = 0, F8_KS = 2048, F8_V = 2080, F8_VS = 4128, F8_BYTES = 4160
 };
+
+/* e4m3 by its definition: code s.EEEE.mmm is (-1)^s (1 + m/8) 2^(E-7) for E >= 1,
+ * (-1)^s (m/8) 2^-6 for E = 0; the all-ones magnitude 0x7F is NaN. */
+double orc_e4m3_value(uint8_t code)
+{
+    int E = (code >> 3) & 15, m = code & 7;
+    double mag;
+    if ((code & 0x7F) == 0x7F) return NAN;
+    mag = E == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, E - 7);
+    return (code & 0x80) ? -mag : mag;
+}
+
+/* Nearest e4m3 by trying every finite magnitude; an exact tie goes to the even
+ * code (even mantissa).  Zero results are +0 (0x00). */
+uint8_t orc_e4m3_nearest(double y)
+{
+    double a = fabs(y), best_d = INFINITY;
+    int best = 0;
+    for (int c = 0; c < 0x7F; ++c) {
+        double d = fabs(orc_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) { best_d = d; best = c; }
+    }
+    return (uint8_t)(best != 0 && y < 0 ? (best | 0x80) : best);
+}
+
+void orc_fp8_row(const float *x, int n, uint8_t *codes, uint16_t *scale)
+{
+    double amax = 0.0;
+    int e = -24;
+    for (int i = 0; i < n; ++i) if (fabs((double)x[i]) > amax) amax = fabs((double)x[i]);
+    while (amax > ldexp(448.0, e)) ++e;
+    for (int i = 0; i < n; ++i) codes[i] = orc_e4m3_nearest(ldexp((double)x[i], -e));
+    *scale = orc_f16_nearest((float)ldexp(1.0, e));
+}
 
 /* Bit position of channel ch inside its code row (b bits per code). */
 static int code_bit(int ch, int bits)
@@ -161,7 +199,7 @@ static void put_code(uint8_t *row, int ch, int bits, int code)
 int64_t orc_block_bytes(int32_t cls)
 {
     return cls == ORC_INT2 ? I2_BYTES : cls == ORC_INT4 ? I4_BYTES
-         : cls == ORC_FP16 ? F16_BYTES : 0;
+         : cls == ORC_FP16 ? F16_BYTES : cls == 3 ? F8_BYTES : 0;
 }
 
 static int32_t page_class(const orc_cache *c, int64_t page)
@@ -185,7 +223,8 @@ static uint8_t *block_ptr(const orc_cache *c, int64_t page, int32_t head)
 {
     int32_t cls = page_class(c, page);
     int64_t rel = page - class_base(c, cls);
-    return c->pool[cls] + (rel * c->heads_per_page + head) * orc_block_bytes(cls);
+    int64_t bytes = (cls == ORC_FP16 && c->anchor_fp8) ? F8_BYTES : orc_block_bytes(cls);
+    return c->pool[cls] + (rel * c->heads_per_page + head) * bytes;
 }
 
 static void put_u16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)(v & 255); p[1] = (uint8_t)(v >> 8); }
@@ -327,6 +366,14 @@ int orc_append(orc_cache *c, const void *k, const void *v, int32_t dtype,
             uint8_t *blk = block_ptr(c, page, h);
             load_row(kr, k, dtype, rows16[i], row_stride, head_stride, h);
             load_row(vr, v, dtype, rows16[i], row_stride, head_stride, h);
+            if (c->anchor_fp8) {
+                uint16_t ks, vs;
+                orc_fp8_row(kr, D, blk + F8_K + off * 128, &ks);
+                orc_fp8_row(vr, D, blk + F8_V + off * 128, &vs);
+                put_u16(blk + F8_KS + off * 2, ks);
+                put_u16(blk + F8_VS + off * 2, vs);
+                continue;
+            }
             for (int ch = 0; ch < D; ++ch) {
                 put_u16(blk + F16_K + off * 256 + ch * 2, orc_f16_nearest(kr[ch]));
                 put_u16(blk + F16_V + off * 256 + ch * 2, orc_f16_nearest(vr[ch]));
@@ -598,6 +645,9 @@ int orc_token(const orc_cache *c, int32_t page, int32_t off, int32_t head,
             k[ch] = deq(get_u16(mblk + I2_KS + (ch % 64) * 2), get_u16(mblk + I2_KZ + (ch % 64) * 2),
                         get_code(blk + I2_KC + off * 32, ch, 2));
             v[ch] = deq(get_u16(vm), get_u16(vm + 2), get_code(blk + I2_VC + off * 32, ch, 2));
+        } else if (c->anchor_fp8) {
+            k[ch] = orc_e4m3_value(blk[F8_K + off * 128 + ch]) * orc_f16_value(get_u16(blk + F8_KS + off * 2));
+            v[ch] = orc_e4m3_value(blk[F8_V + off * 128 + ch]) * orc_f16_value(get_u16(blk + F8_VS + off * 2));
         } else {
             k[ch] = orc_f16_value(get_u16(blk + F16_K + off * 256 + ch * 2));
             v[ch] = orc_f16_value(get_u16(blk + F16_V + off * 256 + ch * 2));

@@ -57,6 +57,7 @@ typedef struct {
     int32_t n_pages[3];      /* pages per class; ids: INT2 [0,n2), INT4 [n2,n2+n4), FP16 after */
     uint8_t *pool[3];        /* host byte pools, one per class */
     int32_t sentinel_slot;   /* slot id of the dead slot, or -1 */
+    int32_t anchor_fp8;      /* 0: FP16 anchors; 1: FP8 (e4m3) anchors with a power-of-two scale */
 } orc_cache;
 
 /* A token range of one (table, head): tokens t in [tok_begin, tok_end), where
@@ -71,7 +72,14 @@ uint16_t orc_f16_up(float x);       /* smallest fp16 >= x, never -0           */
 uint16_t orc_f16_nearest(float x);  /* round to nearest, ties to even          */
 double   orc_f16_value(uint16_t h);
 
-/* Page head-block sizes in bytes (per class). */
+/* --- FP8 (OCP e4m3: 4 exponent bits, bias 7, 3 mantissa bits, max 448) --- */
+double  orc_e4m3_value(uint8_t code);   /* NaN for 0x7F / 0xFF                  */
+uint8_t orc_e4m3_nearest(double y);     /* |y| <= 448; ties to the even code; 0 -> 0x00 */
+/* One anchor row: scale 2^e with e the smallest integer >= -24 such that
+ * max |x| <= 448 * 2^e, codes nearest to x / 2^e; *scale is 2^e as fp16 bits. */
+void    orc_fp8_row(const float *x, int n, uint8_t *codes, uint16_t *scale);
+
+/* Page head-block sizes in bytes (per class; 3 = an FP8 anchor block). */
 int64_t orc_block_bytes(int32_t cls);
 
 /* --- quantizer ------------------------------------------------------------

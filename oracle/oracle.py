@@ -20,6 +20,7 @@ PAGES, SLOTS = 0, 1
 PAGE = 16
 HEAD_DIM = 128
 BLOCK_BYTES = {INT2: 1536, INT4: 2560, FP16: 8192}
+FP8_ANCHOR_BYTES = 4160   # an FP16-class block of a cache with FP8 anchors
 
 _lib = None
 
@@ -39,7 +40,8 @@ class _Cache(ctypes.Structure):
     _fields_ = [("heads_per_page", ctypes.c_int32),
                 ("n_pages", ctypes.c_int32 * 3),
                 ("pool", ctypes.c_void_p * 3),
-                ("sentinel_slot", ctypes.c_int32)]
+                ("sentinel_slot", ctypes.c_int32),
+                ("anchor_fp8", ctypes.c_int32)]
 
 
 class _Range(ctypes.Structure):
@@ -65,6 +67,12 @@ def _declare(L):
     L.orc_f16_value.restype = ctypes.c_double
     L.orc_block_bytes.argtypes = [i32]
     L.orc_block_bytes.restype = i64
+    L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+    L.orc_e4m3_value.restype = ctypes.c_double
+    L.orc_e4m3_nearest.argtypes = [ctypes.c_double]
+    L.orc_e4m3_nearest.restype = ctypes.c_uint8
+    L.orc_fp8_row.argtypes = [P, i32, P, P]
+    L.orc_fp8_row.restype = None
     L.orc_quantize.argtypes = [P, i32, i64, i32, P, P, P]
     L.orc_quantize.restype = None
     L.orc_route.argtypes = [P, i32, P, P, P, P]
@@ -98,6 +106,23 @@ def _c_array(a, dtype):
 
 
 # --- fp16 helpers ------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    return float(lib().orc_e4m3_value(int(code)))
+
+
+def e4m3_nearest(y: float) -> int:
+    return int(lib().orc_e4m3_nearest(float(y)))
+
+
+def fp8_row(x):
+    """(codes uint8 [n], scale fp16 bits) of one FP8 anchor row."""
+    x = _c_array(x, np.float32)
+    codes = np.zeros(x.shape[0], np.uint8)
+    scale = np.zeros(1, np.uint16)
+    lib().orc_fp8_row(_ptr(x), x.shape[0], _ptr(codes), _ptr(scale))
+    return codes, int(scale[0])
+
 
 def f16_down(x: float) -> int:
     return int(lib().orc_f16_down(float(x)))
@@ -184,10 +209,12 @@ def prefill_attend(q, k, v, n_tokens, cls=None, window=128):
 class Cache:
     """Host-side pools laid out exactly as the GPU pools (one per class)."""
 
-    def __init__(self, heads_per_page, n_int2, n_int4, n_fp16, sentinel_slot=-1):
+    def __init__(self, heads_per_page, n_int2, n_int4, n_fp16, sentinel_slot=-1, anchor_fp8=False):
         self.heads_per_page = int(heads_per_page)
         self.n_pages = (int(n_int2), int(n_int4), int(n_fp16))
-        self.pools = [np.zeros(max(1, n * self.heads_per_page * BLOCK_BYTES[c]), np.uint8)
+        self.anchor_fp8 = bool(anchor_fp8)
+        self.block_bytes = (BLOCK_BYTES[INT2], BLOCK_BYTES[INT4], FP8_ANCHOR_BYTES if anchor_fp8 else BLOCK_BYTES[FP16])
+        self.pools = [np.zeros(max(1, n * self.heads_per_page * self.block_bytes[c]), np.uint8)
                       for c, n in zip((INT2, INT4, FP16), self.n_pages)]
         self.sentinel_slot = int(sentinel_slot)
 
@@ -198,10 +225,11 @@ class Cache:
             c.n_pages[i] = self.n_pages[i]
             c.pool[i] = self.pools[i].ctypes.data
         c.sentinel_slot = self.sentinel_slot
+        c.anchor_fp8 = 1 if self.anchor_fp8 else 0
         return c
 
     def pool_bytes(self, cls):
-        n = self.n_pages[cls] * self.heads_per_page * BLOCK_BYTES[cls]
+        n = self.n_pages[cls] * self.heads_per_page * self.block_bytes[cls]
         return self.pools[cls][:n]
 
     def append(self, k, v, dtype, row_stride, head_stride, rows4=(), slots4=(),
