@@ -98,7 +98,18 @@ typedef struct {
     int32_t n_pages[3];       /* pages per class (INT2, INT4, FP16)           */
     void *pool[3];            /* [dev] one pool per class (NULL if 0 pages)   */
     int32_t sentinel_slot;    /* slot id of the dead slot, or -1              */
+    int32_t anchor_format;    /* KVQ_ANCHOR_FP16 or KVQ_ANCHOR_FP8: the format
+                                 of the FP16 class's blocks (the anchors)      */
 } kvq_cache;
+
+/* Anchor formats (HyQuant keeps its anchors in FP16 and names FP8 as the smaller
+ * form).  KVQ_ANCHOR_FP8: each token's K and V rows of a head are OCP e4m3 codes
+ * (max 448, nearest with ties to even) times 2^e, e the smallest integer >= -24
+ * with max |x| <= 448 2^e, stored as an fp16 power of two; block of 4160 bytes =
+ * kvq_block_bytes(KVQ_FP8_ANCHOR_BLOCK): K codes [16 tok][128 B] at 0, K scales
+ * [16] fp16 at 2048, V codes at 2080, V scales at 4128. */
+enum { KVQ_ANCHOR_FP16 = 0, KVQ_ANCHOR_FP8 = 1 };
+enum { KVQ_FP8_ANCHOR_BLOCK = 3 };
 
 /* A token range of one (table, head-in-table) in one precision class:
  * tokens t in [tok_begin, tok_end); in a page table token t is entry t/16,

@@ -147,7 +147,18 @@ struct DecodeArgs {
   float *part_o, *part_lse;
   int32_t *err;
   int32_t only_fp16;  // page mode with the LDS-staged kernel present: this kernel takes FP16 splits only
+  int32_t fp8;        // the FP16 class holds FP8 anchors (e4m3 codes and a power-of-two scale per token)
 };
+
+// FP8 anchors: 8 e4m3 codes (two words) to 8 fp16 (one uint4, channel order kept), times
+// the token's power-of-two scale s: exact while the values stay inside fp16's range.
+__device__ __forceinline__ uint4 fp8x8_h(uint32_t w0, uint32_t w1, float s) {
+  typedef _Float16 hv2 __attribute__((ext_vector_type(2)));
+  const hv2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, s, false), b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, s, true);
+  const hv2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, s, false), d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, s, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                    __builtin_bit_cast(uint32_t, d));
+}
 
 // The pages of one class: ids first .. first + count - 1 of the unified numbering,
 // blocks of head `head` at base + (id - first) * stride.  The host keeps every unified
@@ -157,7 +168,7 @@ struct ClassPages {
   gbytes base;
   uint32_t first, count, stride;
   __device__ ClassPages(const DecodeArgs &a, int head) {
-    const uint32_t bytes = CLS == KVQ_INT2 ? kI2Bytes : CLS == KVQ_INT4 ? kI4Bytes : kF16Bytes;
+    const uint32_t bytes = CLS == KVQ_INT2 ? kI2Bytes : CLS == KVQ_INT4 ? kI4Bytes : a.fp8 ? kF8Bytes : kF16Bytes;
     first = CLS == KVQ_INT2 ? 0u : CLS == KVQ_INT4 ? (uint32_t)a.n2 : (uint32_t)(a.n2 + a.n4);
     count = (uint32_t)(CLS == KVQ_INT2 ? a.n2 : CLS == KVQ_INT4 ? a.n4 : a.n16);
     stride = (uint32_t)a.heads * bytes;
@@ -190,6 +201,14 @@ struct Win {
   uint32_t live;     // bit h: the QK token T + 16 h + lr is live
   uint32_t vlive;    // bit q: this lane's P V token q (0..7) is live
 };
+
+// The fp16 scale of token t in a block's scale row (2 bytes each, the row 4-byte
+// aligned), as float bits.
+__device__ __forceinline__ uint32_t scale_bits(gbytes row, int t) {
+  const uint32_t w = ld1(row + 4 * (t >> 1));
+  const uint16_t h = (uint16_t)(t & 1 ? w >> 16 : w & 0xffffu);
+  return __float_as_uint((float)__builtin_bit_cast(_Float16, h));
+}
 
 template <int CLS, bool SLOTS>
 struct Loader {
@@ -249,6 +268,10 @@ struct Loader {
         } else if (CLS == KVQ_INT2) {
           const uint2 x = ld2(bh + kI2KC + lr * 32 + lb * 8);
           w.k[h][0] = make_uint4(x.x, x.y, 0, 0);
+        } else if (a.fp8) {  // raw codes of channels 32 lb .. + 31 and the token's scale
+          w.k[h][0] = ld4(bh + kF8K + lr * 128 + lb * 32);
+          w.k[h][1] = ld4(bh + kF8K + lr * 128 + lb * 32 + 16);
+          w.k[h][2].x = scale_bits(bh + kF8KS, lr);
         } else {
 #pragma unroll
           for (int m = 0; m < 4; ++m) w.k[h][m] = ld4(bh + kF16K + lr * 256 + lb * 64 + m * 16);
@@ -269,7 +292,10 @@ struct Loader {
       for (int q = 0; q < 8; ++q) {
         if (CLS == KVQ_INT4) w.v[q].x = ld1(vb + kI4VC + (o0 + q) * 64 + lr * 4);
         else if (CLS == KVQ_INT2) w.v[q].x = ld1(vb + kI2VC + (o0 + q) * 32 + (lr >> 1) * 4);
-        else w.v[q] = ld4(vb + kF16V + (o0 + q) * 256 + lr * 16);
+        else if (a.fp8) {  // codes of channels 8 lr .. + 7 and the token's scale
+          const uint2 c = ld2(vb + kF8V + (o0 + q) * 128 + lr * 8);
+          w.v[q] = make_uint4(c.x, c.y, scale_bits(vb + kF8VS, o0 + q), 0u);
+        } else w.v[q] = ld4(vb + kF16V + (o0 + q) * 256 + lr * 16);
       }
       if (CLS != KVQ_FP16) {
         const int vm_at = CLS == KVQ_INT4 ? kI4VM : kI2VM;
@@ -287,6 +313,10 @@ struct Loader {
         if (CLS == KVQ_INT4) {
           w.k[h][0] = ld4(b + kI4KC + off * 64 + lb * 16);
           w.km[h] = ld4(b + kI4KM + off * 16);
+        } else if (a.fp8) {
+          w.k[h][0] = ld4(b + kF8K + off * 128 + lb * 32);
+          w.k[h][1] = ld4(b + kF8K + off * 128 + lb * 32 + 16);
+          w.k[h][2].x = scale_bits(b + kF8KS, off);
         } else {
 #pragma unroll
           for (int m = 0; m < 4; ++m) w.k[h][m] = ld4(b + kF16K + off * 256 + lb * 64 + m * 16);
@@ -303,7 +333,12 @@ struct Loader {
           w.v[q].x = ld1(b + kI4VC + off * 64 + lr * 4);
           vm[q] = ld1(b + kI4VM + ((lr & 3) * kPage + off) * 4);
         } else {
-          w.v[q] = ld4(b + kF16V + off * 256 + lr * 16);
+          if (a.fp8) {
+            const uint2 c = ld2(b + kF8V + off * 128 + lr * 8);
+            w.v[q] = make_uint4(c.x, c.y, scale_bits(b + kF8VS, off), 0u);
+          } else {
+            w.v[q] = ld4(b + kF16V + off * 256 + lr * 16);
+          }
         }
       }
       if (CLS == KVQ_INT4) {
@@ -476,6 +511,13 @@ struct SplitRun {
         kb[1] = cvt_k2(v.x >> 8, k) * h8_of(w.kg[1]);
         kb[2] = cvt_k2(v.y, k) * h8_of(w.kg[2]);
         kb[3] = cvt_k2(v.y >> 8, k) * h8_of(w.kg[3]);
+      } else if (a.fp8) {
+        const float sk = __uint_as_float(w.k[h][2].x);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint4 c = w.k[h][m >> 1];
+          kb[m] = h8_of(m & 1 ? fp8x8_h(c.z, c.w, sk) : fp8x8_h(c.x, c.y, sk));
+        }
       } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m) kb[m] = h8_of(w.k[h][m]);
@@ -542,7 +584,11 @@ struct SplitRun {
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint4 ra = w.v[2 * u], rb = w.v[2 * u + 1];
+          uint4 ra = w.v[2 * u], rb = w.v[2 * u + 1];
+          if (a.fp8) {
+            ra = fp8x8_h(ra.x, ra.y, __uint_as_float(ra.z));
+            rb = fp8x8_h(rb.x, rb.y, __uint_as_float(rb.z));
+          }
           const uint32_t da[4] = {ra.x, ra.y, ra.z, ra.w}, db[4] = {rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
           for (int nt = 0; nt < 8; ++nt) {
@@ -1348,6 +1394,7 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
   a.pool4 = (gbytes)c->pool[1];
   a.pool16 = (gbytes)c->pool[2];
   a.sentinel = c->sentinel_slot;
+  a.fp8 = c->anchor_format == KVQ_ANCHOR_FP8 ? 1 : 0;
   a.q = q;
   a.q_dtype = q_dtype;
   a.batch = batch;

@@ -28,6 +28,8 @@ kvq_status check_cache(const kvq_cache *c) {
   if (c->page_size != kPage)
     return fail(KVQ_ERR_UNSUPPORTED, "page_size %d is not supported (only 16)", c->page_size);
   if (c->heads_per_page < 1) return fail(KVQ_ERR_INVALID_ARG, "heads_per_page must be >= 1");
+  if (c->anchor_format != KVQ_ANCHOR_FP16 && c->anchor_format != KVQ_ANCHOR_FP8)
+    return fail(KVQ_ERR_INVALID_ARG, "unknown anchor format %d", c->anchor_format);
   int64_t total = 0;
   for (int i = 0; i < 3; ++i) {
     if (c->n_pages[i] < 0) return fail(KVQ_ERR_INVALID_ARG, "n_pages[%d] is negative", i);
@@ -58,7 +60,8 @@ using namespace kvq;
 extern "C" {
 
 size_t kvq_block_bytes(int32_t cls) {
-  return cls == KVQ_INT2 ? kI2Bytes : cls == KVQ_INT4 ? kI4Bytes : cls == KVQ_FP16 ? kF16Bytes : 0;
+  return cls == KVQ_INT2 ? kI2Bytes : cls == KVQ_INT4 ? kI4Bytes : cls == KVQ_FP16 ? kF16Bytes
+       : cls == KVQ_FP8_ANCHOR_BLOCK ? kF8Bytes : 0;
 }
 
 const char *kvq_status_string(int32_t st) {

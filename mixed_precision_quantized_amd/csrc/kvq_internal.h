@@ -22,6 +22,9 @@ constexpr int kMaxReorderEntries = 8192;
 constexpr int kI4Bytes = 2560, kI4KC = 0, kI4KM = 1024, kI4VC = 1280, kI4VM = 2304;
 constexpr int kI2Bytes = 1536, kI2KC = 0, kI2KS = 512, kI2KZ = 640, kI2VC = 768, kI2VM = 1280;
 constexpr int kF16Bytes = 8192, kF16K = 0, kF16V = 4096;
+// FP8 anchor block (the FP16 class of a cache with FP8 anchors): e4m3 codes and one
+// power-of-two fp16 scale per token, K then V.
+constexpr int kF8Bytes = 4160, kF8K = 0, kF8KS = 2048, kF8V = 2080, kF8VS = 4128;
 
 // Records a formatted message as this thread's last error and returns `st`.
 kvq_status fail(kvq_status st, const char *fmt, ...);

@@ -149,7 +149,50 @@ struct CacheView {
   int32_t heads;
   int32_t n2, n4, n16;
   uint8_t *pool2, *pool4, *pool16;
+  int32_t fp8;  // FP8 anchors instead of FP16
 };
+
+// ---------------------------------------------------------------- fp8 ---------
+// OCP e4m3 code of y, |y| <= 448, rounded to nearest with ties to even (0 -> 0x00).
+// Below 2^-6 the codes are multiples of 2^-9 (subnormals); in the binade 2^E they
+// step by 2^(E-3), and the code of the value q 2^(E-3) (8 <= q <= 16) is 8 (E + 6) + q,
+// so a carry into the next binade lands on the right code.  Scaling by powers of two
+// is exact, so rintf does the only rounding.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const float a = fabsf(y);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    const int E = ilogbf(a);
+    code = (uint32_t)(8 * (E + 6)) + (uint32_t)rintf(ldexpf(a, 3 - E));
+  }
+  return (code != 0 && y < 0.0f) ? (code | 0x80u) : code;
+}
+
+// The e of an anchor row: the smallest e >= -24 with max |x| <= 448 2^e.
+__device__ __forceinline__ int fp8_exponent(float amax) {
+  if (!(amax > 0.0f)) return -24;
+  int E;
+  (void)frexpf(amax, &E);  // amax in [2^(E-1), 2^E)
+  int e = E - 9;           // 448 2^(E-10) < 2^(E-1) <= amax, so e is E - 9 or E - 8
+  if (amax > ldexpf(448.0f, e)) ++e;
+  return e < -24 ? -24 : e;
+}
+
+// fp16 bits of 2^e, -24 <= e <= 15.
+__device__ __forceinline__ uint32_t pow2_half(int e) { return e >= -14 ? (uint32_t)(e + 15) << 10 : 1u << (e + 24); }
+
+// One FP8 anchor row of a wavefront: lane L holds channels 2L, 2L + 1.
+__device__ __forceinline__ void put_fp8_row(uint8_t *blk, int codes_at, int scales_at, int off, float x0, float x1,
+                                            int lane) {
+  float m = fmaxf(fabsf(x0), fabsf(x1));
+  for (int d = 32; d > 0; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+  const int e = fp8_exponent(m);
+  const uint32_t c0 = e4m3_code(ldexpf(x0, -e)), c1 = e4m3_code(ldexpf(x1, -e));
+  *reinterpret_cast<uint16_t *>(blk + codes_at + off * 128 + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+  if (lane == 0) *reinterpret_cast<uint16_t *>(blk + scales_at + off * 2) = (uint16_t)pow2_half(e);
+}
 
 __device__ __forceinline__ int page_class(const CacheView &c, int64_t p) {
   if (p < 0) return -1;
@@ -223,6 +266,10 @@ __global__ void __launch_bounds__(256) append_tokens_kernel(
     uint8_t *blk = c.pool4 + ((page - c.n2) * c.heads + head) * (int64_t)kI4Bytes;
     put_token_row<4, true>(blk, kI4KC, kI4KM, off, k0, k1, lane);
     put_token_row<4, false>(blk, kI4VC, kI4VM, off, v0, v1, lane);
+  } else if (c.fp8) {
+    uint8_t *blk = c.pool16 + ((page - c.n2 - c.n4) * c.heads + head) * (int64_t)kF8Bytes;
+    put_fp8_row(blk, kF8K, kF8KS, off, k0, k1, lane);
+    put_fp8_row(blk, kF8V, kF8VS, off, v0, v1, lane);
   } else {
     uint8_t *blk = c.pool16 + ((page - c.n2 - c.n4) * c.heads + head) * (int64_t)kF16Bytes;
     *reinterpret_cast<uint32_t *>(blk + kF16K + off * 256 + lane * 4) =
@@ -407,6 +454,7 @@ CacheView view_of(const kvq_cache *c) {
   v.pool2 = static_cast<uint8_t *>(c->pool[0]);
   v.pool4 = static_cast<uint8_t *>(c->pool[1]);
   v.pool16 = static_cast<uint8_t *>(c->pool[2]);
+  v.fp8 = c->anchor_format == KVQ_ANCHOR_FP8 ? 1 : 0;
   return v;
 }
 

@@ -24,6 +24,7 @@ F32, BF16, F16 = 0, 1, 2
 TABLE_PAGES, TABLE_SLOTS = 0, 1
 DEVERR_ID, DEVERR_RANGE, DEVERR_PAIR, DEVERR_SPLIT = 1, 2, 4, 8
 HEAD_DIM = 128
+FP8_ANCHOR_BLOCK = 3   # kvq_block_bytes class of an FP8 anchor block
 PAGE = 16
 
 SPLIT_DTYPE = np.dtype([("table", "<i4"), ("head", "<i4"), ("cls", "<i4"),
@@ -46,7 +47,7 @@ class KvqError(RuntimeError):
 class _CacheC(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("heads_per_page", ctypes.c_int32), ("n_pages", ctypes.c_int32 * 3),
-                ("pool", ctypes.c_void_p * 3), ("sentinel_slot", ctypes.c_int32)]
+                ("pool", ctypes.c_void_p * 3), ("sentinel_slot", ctypes.c_int32), ("anchor_format", ctypes.c_int32)]
 
 
 class _SplitC(ctypes.Structure):
@@ -124,12 +125,14 @@ class Cache:
     """Device pools of a mixed-precision paged KV cache (allocated by torch)."""
 
     def __init__(self, heads_per_page: int, n_pages, device="cuda", sentinel_slot: int = -1,
-                 pools=None):
+                 pools=None, anchor_fp8: bool = False):
         self.heads_per_page = int(heads_per_page)
         self.n_pages = tuple(int(n) for n in n_pages)
         self.sentinel_slot = int(sentinel_slot)
+        self.anchor_fp8 = bool(anchor_fp8)
+        self.block_bytes = (block_bytes(0), block_bytes(1), block_bytes(FP8_ANCHOR_BLOCK if anchor_fp8 else 2))
         if pools is None:
-            pools = [torch.zeros(max(1, n * self.heads_per_page * block_bytes(c)), dtype=torch.uint8,
+            pools = [torch.zeros(max(1, n * self.heads_per_page * self.block_bytes[c]), dtype=torch.uint8,
                                  device=device) for c, n in enumerate(self.n_pages)]
         self.pools = pools
         self._c = _CacheC()
@@ -140,13 +143,14 @@ class Cache:
             self._c.n_pages[i] = self.n_pages[i]
             self._c.pool[i] = self.pools[i].data_ptr()
         self._c.sentinel_slot = self.sentinel_slot
+        self._c.anchor_format = 1 if self.anchor_fp8 else 0
 
     @property
     def struct(self):
         return ctypes.byref(self._c)
 
     def pool_bytes(self, cls: int) -> torch.Tensor:
-        return self.pools[cls][: self.n_pages[cls] * self.heads_per_page * block_bytes(cls)]
+        return self.pools[cls][: self.n_pages[cls] * self.heads_per_page * self.block_bytes[cls]]
 
 
 def route_tokens(flags: np.ndarray):

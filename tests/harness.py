@@ -38,11 +38,12 @@ def _ranges(w, after_reorder: bool):
 class DeviceRun:
     """Route (library), place, quantize + append, reorder and decode on the GPU."""
 
-    def __init__(self, w: synth.Workload, device="cuda", reorder=True, compact=False):
+    def __init__(self, w: synth.Workload, device="cuda", reorder=True, compact=False, anchor_fp8=False):
         from mixed_precision_quantized_amd import kvq
         self.kvq, self.w, self.device = kvq, w, device
         self.lists = synth.place_all(w, lambda f: kvq.route_tokens(f)[0])
-        self.cache = kvq.Cache(w.heads_per_page, w.n_pages, device, sentinel_slot=w.sentinel_slot)
+        self.cache = kvq.Cache(w.heads_per_page, w.n_pages, device, sentinel_slot=w.sentinel_slot,
+                               anchor_fp8=anchor_fp8)
         self.err = torch.zeros(1, dtype=torch.int32, device=device)
         self.k = w.k.to(device)
         self.v = w.v.to(device)
@@ -106,11 +107,12 @@ class DeviceRun:
 class OracleRun:
     """Route (oracle), place, quantize + append and reorder on the CPU oracle."""
 
-    def __init__(self, w: synth.Workload, reorder=True, compact=False):
+    def __init__(self, w: synth.Workload, reorder=True, compact=False, anchor_fp8=False):
         from oracle import oracle
         self.orc, self.w = oracle, w
         self.lists = synth.place_all(w, lambda f: oracle.route(f)[0])
-        self.cache = oracle.Cache(w.heads_per_page, *w.n_pages, sentinel_slot=w.sentinel_slot)
+        self.cache = oracle.Cache(w.heads_per_page, *w.n_pages, sentinel_slot=w.sentinel_slot,
+                                  anchor_fp8=anchor_fp8)
         k, v, dt = _host_rows(w)
         self.k, self.v, self.dtype = k, v, dt
         row_stride = w.heads_per_page * 128

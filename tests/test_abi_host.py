@@ -33,7 +33,9 @@ def test_every_declared_symbol_is_exported(kvq):
 
 
 def test_block_bytes(kvq):
-    assert [kvq.block_bytes(c) for c in (0, 1, 2, 3)] == [1536, 2560, 8192, 0]
+    # INT2, INT4, FP16 and an FP8 anchor block (e4m3 K and V rows of 16 tokens plus 16
+    # fp16 scales each: 2 * (2048 + 32)); unknown classes 0
+    assert [kvq.block_bytes(c) for c in (0, 1, 2, 3, 4)] == [1536, 2560, 8192, 4160, 0]
 
 
 def test_route_matches_oracle_and_closed_form(kvq, orc):

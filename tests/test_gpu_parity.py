@@ -29,11 +29,11 @@ def _pools_equal(gpu, orc):
             raise AssertionError(f"class {cls}: {bad.size} bytes differ, first at {bad[:8]}")
 
 
-def _check_case(name, make, plan_kw, reorder=True, out_dtype=torch.float32, compact=False):
-    _say(name, plan_kw, "compacted" if compact else "")
+def _check_case(name, make, plan_kw, reorder=True, out_dtype=torch.float32, compact=False, anchor_fp8=False):
+    _say(name, plan_kw, "compacted" if compact else "", "fp8 anchors" if anchor_fp8 else "")
     wg, wo = make(), make()
-    gpu = DeviceRun(wg, reorder=reorder, compact=compact)
-    orc = OracleRun(wo, reorder=reorder, compact=compact)
+    gpu = DeviceRun(wg, reorder=reorder, compact=compact, anchor_fp8=anchor_fp8)
+    orc = OracleRun(wo, reorder=reorder, compact=compact, anchor_fp8=anchor_fp8)
     torch.cuda.synchronize()
     assert int(gpu.err.item()) == 0, f"device error bits {int(gpu.err.item())}"
     _pools_equal(gpu, orc)
@@ -83,6 +83,13 @@ def test_qwen3_8b_unreordered_table():
 def test_hybrid_anchor_small():
     _check_case("hybrid 2x4096", lambda: synth.hybrid_anchor(batch=2, n_tokens=4096),
                 dict(target_bytes=1 << 17))
+
+
+def test_hybrid_anchor_fp8_small():
+    """FP8 anchors (e4m3 codes, a power-of-two scale per token and head): anchor blocks
+    bit-exact with the oracle, decode within the bar over the dequantized anchors."""
+    _check_case("hybrid fp8 2x4096", lambda: synth.hybrid_anchor(batch=2, n_tokens=4096),
+                dict(target_bytes=1 << 17), anchor_fp8=True)
 
 
 def test_ragged_dead_small():
