@@ -52,12 +52,13 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def effective_bytes(w, q_bytes_per_elem=2, out_bytes_per_elem=2):
-    """Algorithmic bytes of one layer: live token-heads x (96 / 160 / 512 B), 4 B per
-    table entry, q and output; and the decode kernel's share (without the output)."""
+def effective_bytes(w, q_bytes_per_elem=2, out_bytes_per_elem=2, anchor_fp8=False):
+    """Algorithmic bytes of one layer: live token-heads x (96 / 160 / 512 B; FP8 anchors
+    260 B = 2 x (128 codes + 2 B scale)), 4 B per table entry, q and output; and the
+    decode kernel's share (without the output)."""
     import numpy as np
     import synth
-    per_tok = np.array([96, 160, 512], np.int64)
+    per_tok = np.array([96, 160, 260 if anchor_fp8 else 512], np.int64)
     if w.kind == synth.PAGES:
         kv = int((w.alloc.tokens * per_tok).sum()) * w.heads_per_page
         tables = int(w.alloc.n_entries.sum()) * 4
@@ -135,6 +136,8 @@ def main():
                     help="a decode workload; vl_select: vertical-line selection + FREEZE routing at the "
                          "hybrid-anchor prefill shape; prefill: INT8-prefix prefill attention")
     ap.add_argument("--prefill-tokens", type=int, default=16384, help="prompt length of the prefill workload")
+    ap.add_argument("--anchor-fp8", action="store_true",
+                    help="decode workloads: anchors (the FP16 class) stored as e4m3 codes with a power-of-two scale")
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--splits-per-head", type=int, default=0,
                     help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
@@ -179,7 +182,7 @@ def main():
     # reordered tables, ranges and plan serve all layers.
     gpu = DeviceRun(make(device=dev, layer=0), compact=not args.no_compact)
     w0 = gpu.w
-    eff_layer, decode_bytes = effective_bytes(w0)
+    eff_layer, decode_bytes = effective_bytes(w0, anchor_fp8=args.anchor_fp8)
     log(f"workload: {w0.note}; effective bytes per layer {eff_layer}")
     cpu_sample = None
     if not args.no_cpu_baseline and w0.kind == synth.PAGES:
@@ -192,7 +195,8 @@ def main():
     w0.k = w0.v = gpu.k = gpu.v = None
     for L in range(1, layers):
         w = make(device=dev, layer=L)
-        cache = kvq.Cache(w0.heads_per_page, w0.n_pages, dev, sentinel_slot=w0.sentinel_slot)
+        cache = kvq.Cache(w0.heads_per_page, w0.n_pages, dev, sentinel_slot=w0.sentinel_slot,
+                          anchor_fp8=args.anchor_fp8)
         if sent is not None:
             kvq.quantize_append(cache, w.k, w.v, rows4=torch.as_tensor(sent["rows4"], device=dev),
                                 slots4=torch.as_tensor(sent["slots4"], device=dev), dev_err=gpu.err)
@@ -327,10 +331,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u2/u4 codes, fp16 scale/zero" + (", fp16 anchors" if w0.n_pages[2] else "") + ", fp32 math",
+        "dtype": "u2/u4 codes, fp16 scale/zero" + ((", fp8 anchors" if args.anchor_fp8 else ", fp16 anchors")
+                                                   if w0.n_pages[2] else "") + ", fp32 math",
         "data": "synthetic",
         "config": {
-            "workload": description + f", {layers} layers",
+            "workload": description + (" (FP8 anchors)" if args.anchor_fp8 else "") + f", {layers} layers",
             "batch": w0.batch, "hq": w0.hq, "hkv": w0.hkv, "layers": layers, "splits_per_layer": n_splits,
             "effective_bytes_per_layer": eff_layer,
         },
@@ -354,7 +359,7 @@ def main():
             n_threads = min(16, len(os.sched_getaffinity(0)))
         except AttributeError:
             n_threads = min(16, os.cpu_count() or 1)
-        orc = OracleRun(cpu_sample)
+        orc = OracleRun(cpu_sample, anchor_fp8=args.anchor_fp8)
         reps, t = 0, time.perf_counter()
         while True:  # whole passes over the sample until CPU_SECONDS have gone by
             orc.attend(n_threads=n_threads)
@@ -362,7 +367,7 @@ def main():
             dt = time.perf_counter() - t
             if dt >= CPU_SECONDS:
                 break
-        sample_bytes, _ = effective_bytes(cpu_sample)
+        sample_bytes, _ = effective_bytes(cpu_sample, anchor_fp8=args.anchor_fp8)
         result["cpu_baseline"] = {
             "value": round(sample_bytes * reps / dt / 1e9, 3),
             "unit": "GB/s",

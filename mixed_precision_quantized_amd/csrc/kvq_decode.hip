@@ -203,12 +203,13 @@ struct Win {
 };
 
 // The fp16 scale of token t in a block's scale row (2 bytes each, the row 4-byte
-// aligned), as float bits.
-__device__ __forceinline__ uint32_t scale_bits(gbytes row, int t) {
+// aligned): its 16 bits, or as float bits.
+__device__ __forceinline__ uint32_t scale_half(gbytes row, int t) {
   const uint32_t w = ld1(row + 4 * (t >> 1));
-  const uint16_t h = (uint16_t)(t & 1 ? w >> 16 : w & 0xffffu);
-  return __float_as_uint((float)__builtin_bit_cast(_Float16, h));
+  return t & 1 ? w >> 16 : w & 0xffffu;
 }
+__device__ __forceinline__ float half_value(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+__device__ __forceinline__ uint32_t scale_bits(gbytes row, int t) { return __float_as_uint(half_value(scale_half(row, t))); }
 
 template <int CLS, bool SLOTS>
 struct Loader {
@@ -292,11 +293,12 @@ struct Loader {
       for (int q = 0; q < 8; ++q) {
         if (CLS == KVQ_INT4) w.v[q].x = ld1(vb + kI4VC + (o0 + q) * 64 + lr * 4);
         else if (CLS == KVQ_INT2) w.v[q].x = ld1(vb + kI2VC + (o0 + q) * 32 + (lr >> 1) * 4);
-        else if (a.fp8) {  // codes of channels 8 lr .. + 7 and the token's scale
+        else if (a.fp8) {  // codes of channels 8 lr .. + 7
           const uint2 c = ld2(vb + kF8V + (o0 + q) * 128 + lr * 8);
-          w.v[q] = make_uint4(c.x, c.y, scale_bits(vb + kF8VS, o0 + q), 0u);
+          w.v[q] = make_uint4(c.x, c.y, 0u, 0u);
         } else w.v[q] = ld4(vb + kF16V + (o0 + q) * 256 + lr * 16);
       }
+      if (CLS == KVQ_FP16 && a.fp8) w.vm[0] = ld4(vb + kF8VS + 2 * o0);  // the 8 tokens' fp16 scales
       if (CLS != KVQ_FP16) {
         const int vm_at = CLS == KVQ_INT4 ? kI4VM : kI2VM;
         const gbytes m = vb + vm_at + ((lr & 3) * kPage + o0) * 4;
@@ -335,7 +337,8 @@ struct Loader {
         } else {
           if (a.fp8) {
             const uint2 c = ld2(b + kF8V + off * 128 + lr * 8);
-            w.v[q] = make_uint4(c.x, c.y, scale_bits(b + kF8VS, off), 0u);
+            w.v[q] = make_uint4(c.x, c.y, 0u, 0u);
+            vm[q] = scale_half(b + kF8VS, off);
           } else {
             w.v[q] = ld4(b + kF16V + off * 256 + lr * 16);
           }
@@ -344,6 +347,8 @@ struct Loader {
       if (CLS == KVQ_INT4) {
         w.vm[0] = make_uint4(vm[0], vm[1], vm[2], vm[3]);
         w.vm[1] = make_uint4(vm[4], vm[5], vm[6], vm[7]);
+      } else if (a.fp8) {  // the 8 tokens' fp16 scales, two per word
+        w.vm[0] = make_uint4(vm[0] | (vm[1] << 16), vm[2] | (vm[3] << 16), vm[4] | (vm[5] << 16), vm[6] | (vm[7] << 16));
       }
     }
   }
@@ -585,9 +590,10 @@ struct SplitRun {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           uint4 ra = w.v[2 * u], rb = w.v[2 * u + 1];
-          if (a.fp8) {
-            ra = fp8x8_h(ra.x, ra.y, __uint_as_float(ra.z));
-            rb = fp8x8_h(rb.x, rb.y, __uint_as_float(rb.z));
+          if (a.fp8) {  // tokens 2u, 2u + 1: scales in the halves of word u
+            const uint32_t sw = u == 0 ? w.vm[0].x : u == 1 ? w.vm[0].y : u == 2 ? w.vm[0].z : w.vm[0].w;
+            ra = fp8x8_h(ra.x, ra.y, half_value(sw & 0xffffu));
+            rb = fp8x8_h(rb.x, rb.y, half_value(sw >> 16));
           }
           const uint32_t da[4] = {ra.x, ra.y, ra.z, ra.w}, db[4] = {rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
