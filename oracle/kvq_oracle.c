@@ -531,21 +531,15 @@ static int8_t int8_code(float x, float s)
     return (int8_t)c;
 }
 
-int orc_prefill_attend(const float *q, const float *k, const float *v,
-                       int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
-                       const int32_t *n_tokens, const uint8_t *cls, int32_t window,
-                       double *out, int8_t *q_codes, float *q_scales,
-                       int8_t *k_codes, float *k_scales)
-{
-    if (!q || !k || !v || !n_tokens || !out || !q_codes || !q_scales || !k_codes || !k_scales ||
-        batch < 0 || n_max < 0 || hq <= 0 || hkv <= 0 || hq % hkv || window < 0)
-        return ORC_EARG;
-    const int32_t g = hq / hkv, tiles = (n_max + QTILE - 1) / QTILE;
-    for (int32_t b = 0; b < batch; ++b)
-        if (n_tokens[b] < 0 || n_tokens[b] > n_max) return ORC_ERANGE;
 #define QI(b, t, j, c) ((((int64_t)(b) * n_max + (t)) * hq + (j)) * D + (c))
 #define KI(b, t, h, c) ((((int64_t)(b) * n_max + (t)) * hkv + (h)) * D + (c))
-    /* the INT8 tiles: queries per query head, keys per KV head (vertical lines out) */
+
+/* The INT8 tiles: queries per query head, keys per KV head (vertical lines out). */
+static void prefill_quantize(const float *q, const float *k, int32_t batch, int32_t n_max, int32_t hq,
+                             int32_t hkv, const int32_t *n_tokens, const uint8_t *cls, int8_t *q_codes,
+                             float *q_scales, int8_t *k_codes, float *k_scales)
+{
+    const int32_t tiles = (n_max + QTILE - 1) / QTILE;
     for (int32_t b = 0; b < batch; ++b) {
         const int32_t n = n_tokens[b];
         for (int32_t tile = 0; tile < tiles; ++tile) {
@@ -574,46 +568,103 @@ int orc_prefill_attend(const float *q, const float *k, const float *v,
             }
         }
     }
-    /* attention: one softmax per (b, t, j) over the keys k <= t */
+}
+
+/* One output row (request b, position t < n, query head j): one softmax over the keys
+ * kk <= t, each in full precision when it is a vertical line or kk > t - window, else
+ * through INT8.  x: scratch of t + 1 doubles. */
+static void prefill_row(const float *q, const float *k, const float *v, int32_t n_max, int32_t hq, int32_t hkv,
+                        const uint8_t *cls, int32_t window, const int8_t *q_codes, const float *q_scales,
+                        const int8_t *k_codes, const float *k_scales, int32_t b, int32_t t, int32_t j, double *x,
+                        double *o)
+{
+    const int32_t g = hq / hkv, h = j / g, tiles = (n_max + QTILE - 1) / QTILE;
+    const uint8_t *vl = cls ? cls + ((int64_t)b * hkv + h) * n_max : NULL;
     const double inv_sqrt_d = 1.0 / sqrt((double)D);
-    double *x = (double *)malloc(sizeof(double) * (size_t)(n_max > 0 ? n_max : 1));
-    for (int32_t b = 0; b < batch; ++b) {
-        const int32_t n = n_tokens[b];
-        for (int32_t j = 0; j < hq; ++j) {
-            const int32_t h = j / g;
-            const uint8_t *vl = cls ? cls + ((int64_t)b * hkv + h) * n_max : NULL;
-            for (int32_t t = 0; t < n_max; ++t) {
-                double *o = out + QI(b, t, j, 0);
-                for (int c = 0; c < D; ++c) o[c] = 0.0;
-                if (t >= n) continue;
-                const double sq = q_scales[((int64_t)b * hq + j) * tiles + t / QTILE];
-                double mx = -INFINITY;
-                for (int32_t kk = 0; kk <= t; ++kk) {
-                    double dot = 0.0;
-                    if ((vl && vl[kk] == 1) || kk > t - window) {
-                        for (int c = 0; c < D; ++c) dot += (double)q[QI(b, t, j, c)] * (double)k[KI(b, kk, h, c)];
-                    } else {
-                        int64_t idot = 0;
-                        for (int c = 0; c < D; ++c) idot += (int64_t)q_codes[QI(b, t, j, c)] * k_codes[KI(b, kk, h, c)];
-                        dot = sq * (double)k_scales[((int64_t)b * hkv + h) * tiles + kk / QTILE] * (double)idot;
-                    }
-                    x[kk] = dot * inv_sqrt_d;
-                    if (x[kk] > mx) mx = x[kk];
-                }
-                double den = 0.0;
-                for (int32_t kk = 0; kk <= t; ++kk) den += exp(x[kk] - mx);
-                for (int32_t kk = 0; kk <= t; ++kk) {
-                    const double p = exp(x[kk] - mx) / den;
-                    for (int c = 0; c < D; ++c) o[c] += p * (double)v[KI(b, kk, h, c)];
-                }
-            }
+    const double sq = q_scales[((int64_t)b * hq + j) * tiles + t / QTILE];
+    double mx = -INFINITY;
+    for (int c = 0; c < D; ++c) o[c] = 0.0;
+    for (int32_t kk = 0; kk <= t; ++kk) {
+        double dot = 0.0;
+        if ((vl && vl[kk] == 1) || kk > t - window) {
+            for (int c = 0; c < D; ++c) dot += (double)q[QI(b, t, j, c)] * (double)k[KI(b, kk, h, c)];
+        } else {
+            int64_t idot = 0;
+            for (int c = 0; c < D; ++c) idot += (int64_t)q_codes[QI(b, t, j, c)] * k_codes[KI(b, kk, h, c)];
+            dot = sq * (double)k_scales[((int64_t)b * hkv + h) * tiles + kk / QTILE] * (double)idot;
         }
+        x[kk] = dot * inv_sqrt_d;
+        if (x[kk] > mx) mx = x[kk];
     }
-    free(x);
-#undef QI
-#undef KI
+    double den = 0.0;
+    for (int32_t kk = 0; kk <= t; ++kk) den += exp(x[kk] - mx);
+    for (int32_t kk = 0; kk <= t; ++kk) {
+        const double p = exp(x[kk] - mx) / den;
+        for (int c = 0; c < D; ++c) o[c] += p * (double)v[KI(b, kk, h, c)];
+    }
+}
+
+static int prefill_args_ok(const float *q, const float *k, const float *v, int32_t batch, int32_t n_max,
+                           int32_t hq, int32_t hkv, const int32_t *n_tokens, int32_t window)
+{
+    if (!q || !k || !v || !n_tokens || batch < 0 || n_max < 0 || hq <= 0 || hkv <= 0 || hq % hkv || window < 0)
+        return ORC_EARG;
+    for (int32_t b = 0; b < batch; ++b)
+        if (n_tokens[b] < 0 || n_tokens[b] > n_max) return ORC_ERANGE;
     return ORC_OK;
 }
+
+int orc_prefill_attend(const float *q, const float *k, const float *v,
+                       int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
+                       const int32_t *n_tokens, const uint8_t *cls, int32_t window,
+                       double *out, int8_t *q_codes, float *q_scales,
+                       int8_t *k_codes, float *k_scales)
+{
+    int rc = prefill_args_ok(q, k, v, batch, n_max, hq, hkv, n_tokens, window);
+    if (rc != ORC_OK) return rc;
+    if (!out || !q_codes || !q_scales || !k_codes || !k_scales) return ORC_EARG;
+    prefill_quantize(q, k, batch, n_max, hq, hkv, n_tokens, cls, q_codes, q_scales, k_codes, k_scales);
+    double *x = (double *)malloc(sizeof(double) * (size_t)(n_max > 0 ? n_max : 1));
+    for (int32_t b = 0; b < batch; ++b)
+        for (int32_t t = 0; t < n_max; ++t)
+            for (int32_t j = 0; j < hq; ++j) {
+                double *o = out + QI(b, t, j, 0);
+                if (t >= n_tokens[b]) {
+                    for (int c = 0; c < D; ++c) o[c] = 0.0;
+                    continue;
+                }
+                prefill_row(q, k, v, n_max, hq, hkv, cls, window, q_codes, q_scales, k_codes, k_scales, b, t, j, x, o);
+            }
+    free(x);
+    return ORC_OK;
+}
+
+int orc_prefill_attend_rows(const float *q, const float *k, const float *v,
+                            int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
+                            const int32_t *n_tokens, const uint8_t *cls, int32_t window,
+                            int32_t n_rows, const int32_t *row_b, const int32_t *row_t, double *out_rows,
+                            int8_t *q_codes, float *q_scales, int8_t *k_codes, float *k_scales)
+{
+    int rc = prefill_args_ok(q, k, v, batch, n_max, hq, hkv, n_tokens, window);
+    if (rc != ORC_OK) return rc;
+    if (n_rows < 0 || (n_rows > 0 && (!row_b || !row_t || !out_rows)) || !q_codes || !q_scales || !k_codes || !k_scales)
+        return ORC_EARG;
+    for (int32_t r = 0; r < n_rows; ++r)
+        if (row_b[r] < 0 || row_b[r] >= batch || row_t[r] < 0 || row_t[r] >= n_tokens[row_b[r]]) return ORC_ERANGE;
+    prefill_quantize(q, k, batch, n_max, hq, hkv, n_tokens, cls, q_codes, q_scales, k_codes, k_scales);
+    rc = ORC_OK;
+#pragma omp parallel for schedule(dynamic)
+    for (int32_t r = 0; r < n_rows; ++r) {
+        double *x = (double *)malloc(sizeof(double) * (size_t)(row_t[r] + 1));
+        for (int32_t j = 0; j < hq; ++j)
+            prefill_row(q, k, v, n_max, hq, hkv, cls, window, q_codes, q_scales, k_codes, k_scales, row_b[r],
+                        row_t[r], j, x, out_rows + ((int64_t)r * hq + j) * D);
+        free(x);
+    }
+    return rc;
+}
+#undef QI
+#undef KI
 
 /* ------------------------------------------------------------------------ */
 /* Dequantization of one token (fp64, exact)                                 */

@@ -166,6 +166,13 @@ int orc_prefill_attend(const float *q, const float *k, const float *v,
                        const int32_t *n_tokens, const uint8_t *cls, int32_t window,
                        double *out, int8_t *q_codes, float *q_scales,
                        int8_t *k_codes, float *k_scales);
+/* The same for the listed rows only: out_rows [n_rows][hq][128] for (row_b[r],
+ * row_t[r]), row_t[r] < n_tokens[row_b[r]]; the codes and scales in full. */
+int orc_prefill_attend_rows(const float *q, const float *k, const float *v,
+                            int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
+                            const int32_t *n_tokens, const uint8_t *cls, int32_t window,
+                            int32_t n_rows, const int32_t *row_b, const int32_t *row_t, double *out_rows,
+                            int8_t *q_codes, float *q_scales, int8_t *k_codes, float *k_scales);
 
 /* Dequantize one token of one head to fp64 (K and V, 128 channels each). */
 int orc_token(const orc_cache *c, int32_t page, int32_t off, int32_t head,

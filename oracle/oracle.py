@@ -82,11 +82,12 @@ def _declare(L):
     L.orc_token.argtypes = [P, i32, i32, i32, P, P]
     L.orc_select_vl.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, i32, ctypes.c_double, P, P, P]
     L.orc_prefill_attend.argtypes = [P, P, P, i32, i32, i32, i32, P, P, i32, P, P, P, P, P]
+    L.orc_prefill_attend_rows.argtypes = [P, P, P, i32, i32, i32, i32, P, P, i32, i32, P, P, P, P, P, P, P]
     L.orc_attend.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, P, i32, P, P, i32]
     L.orc_attend_ranges.argtypes = [P, P, i32, i32, i32, P, i32, i32, i32, P, i32, P, P, i32]
     L.orc_merge.argtypes = [P, P, P, i32, i32, i32, P, P]
     for name in ("orc_route", "orc_append", "orc_reorder", "orc_compact_slots", "orc_token", "orc_select_vl",
-                 "orc_prefill_attend",
+                 "orc_prefill_attend", "orc_prefill_attend_rows",
                  "orc_attend",
                  "orc_attend_ranges", "orc_merge"):
         getattr(L, name).restype = ctypes.c_int
@@ -203,6 +204,26 @@ def prefill_attend(q, k, v, n_tokens, cls=None, window=128):
     _check(lib().orc_prefill_attend(_ptr(q), _ptr(k), _ptr(v), batch, n_max, hq, hkv,
                                     _ptr(_c_array(n_tokens, np.int32)), _ptr(c), window, _ptr(out),
                                     _ptr(qc), _ptr(qs), _ptr(kc), _ptr(ks)), "prefill_attend")
+    return out, qc, qs, kc, ks
+
+
+def prefill_attend_rows(q, k, v, n_tokens, cls, window, rows):
+    """prefill_attend for the listed (request, position) rows only: (out fp64 [n_rows,
+    hq, 128], q_codes, q_scales, k_codes, k_scales)."""
+    q, k, v = (_c_array(a, np.float32) for a in (q, k, v))
+    batch, n_max, hq = q.shape[:3]
+    hkv = k.shape[2]
+    tiles = (n_max + 63) // 64
+    rows = np.asarray(rows, np.int32).reshape(-1, 2)
+    rb, rt = np.ascontiguousarray(rows[:, 0]), np.ascontiguousarray(rows[:, 1])
+    out = np.zeros((rows.shape[0], hq, HEAD_DIM), np.float64)
+    qc, kc = np.zeros(q.shape, np.int8), np.zeros(k.shape, np.int8)
+    qs, ks = np.zeros((batch, hq, tiles), np.float32), np.zeros((batch, hkv, tiles), np.float32)
+    c = None if cls is None else _c_array(cls, np.uint8)
+    _check(lib().orc_prefill_attend_rows(_ptr(q), _ptr(k), _ptr(v), batch, n_max, hq, hkv,
+                                         _ptr(_c_array(n_tokens, np.int32)), _ptr(c), window, rows.shape[0],
+                                         _ptr(rb), _ptr(rt), _ptr(out), _ptr(qc), _ptr(qs), _ptr(kc), _ptr(ks)),
+           "prefill_attend_rows")
     return out, qc, qs, kc, ks
 
 

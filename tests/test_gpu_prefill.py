@@ -77,3 +77,32 @@ def test_bad_length_is_reported():
                                device="cuda"), None, window=16, dev_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == kvq.DEVERR_RANGE and not out[1].any()
+
+
+def test_full_size_sampled():
+    """The benchmarked workload (1 x 16384 positions, Hq 32 / Hkv 8, 5 % lines, window
+    128) in the benchmarked launch: codes and tile scales bit-exact in full; twelve
+    positions (all 32 query heads each; tile and window edges, the last position)
+    against the oracle's rows."""
+    from mixed_precision_quantized_amd import kvq
+    from oracle import oracle
+    from harness import row_metric
+    n, hq, hkv = 16384, 32, 8
+    _say("full size 1 x 16384, Hq 32 / Hkv 8")
+    q, k, v, lens, cls = synth.prefill_qkv(seed=8, batch=1, n_max=n, hq=hq, hkv=hkv, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qc, qs, kc, ks, _, out = kvq.prefill_attn(q, k, v, torch.as_tensor(lens, device="cuda"),
+                                             torch.as_tensor(cls, device="cuda").contiguous(), window=128,
+                                             dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    pos = [0, 1, 63, 64, 127, 128, 129, 4095, 8191, 12000, 16320, 16383]
+    ref, rqc, rqs, rkc, rks = oracle.prefill_attend_rows(q.float().cpu().numpy(), k.float().cpu().numpy(),
+                                                         v.float().cpu().numpy(), lens, cls, 128,
+                                                         [(0, t) for t in pos])
+    assert np.array_equal(qs.cpu().numpy(), rqs) and np.array_equal(ks.cpu().numpy(), rks)
+    assert np.array_equal(qc.cpu().numpy(), rqc) and np.array_equal(kc.cpu().numpy(), rkc)
+    got = out[0, pos].cpu().numpy()
+    e = row_metric(ref, got)
+    _say(f"  full size: row error {e:.2e} over {len(pos)} positions x {hq} heads")
+    assert e <= TOL

@@ -147,3 +147,17 @@ def test_window_edge_and_lines_on_an_exact_grid():
             e = np.exp(x - x.max())
             want[t, j] = (e / e.sum()) @ v[0, p, h].astype(np.float64)
     assert np.allclose(out[0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_rows_entry_matches_the_full_computation():
+    """The sampled-rows entry (used at sizes the full oracle cannot finish) gives the
+    full computation's rows, codes and scales."""
+    q, k, v = _data(5, batch=2, n=150)
+    cls = np.zeros((2, 2, 150), np.uint8)
+    cls[:, :, 3::11] = 1
+    full, qc, qs, kc, ks = oracle.prefill_attend(q, k, v, [150, 97], cls, window=24)
+    rows = [(0, 0), (0, 63), (0, 64), (0, 149), (1, 50), (1, 96)]
+    part, qc2, qs2, kc2, ks2 = oracle.prefill_attend_rows(q, k, v, [150, 97], cls, 24, rows)
+    for i, (b, t) in enumerate(rows):
+        assert np.array_equal(part[i], full[b, t])
+    assert all(np.array_equal(x, y) for x, y in ((qc, qc2), (qs, qs2), (kc, kc2), (ks, ks2)))
