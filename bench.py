@@ -29,6 +29,8 @@ sys.path.insert(1, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_8b_traffic.md")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_llama8b_16k_traffic.md")
+PREFILL_SOURCES = ("kvq_prefill.hip", "kvq_internal.h")
 CPU_SECONDS = 10.0  # lower bound on the timed oracle work
 
 # name: (metric suffix, default layers, description)
@@ -75,10 +77,10 @@ def effective_bytes(w, q_bytes_per_elem=2, out_bytes_per_elem=2, anchor_fp8=Fals
     return kv + tables + q + w.batch * w.hq * 128 * out_bytes_per_elem, kv + tables + q
 
 
-def kernel_source_sha():
-    """Hash of the decode kernel's source code (comments and layout ignored)."""
+def kernel_source_sha(files=("kvq_decode.hip", "kvq_internal.h")):
+    """Hash of a kernel's source code (comments and layout ignored)."""
     h = hashlib.sha256()
-    for f in ("kvq_decode.hip", "kvq_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "mixed_precision_quantized_amd", "csrc", f)) as fh:
             text = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
@@ -86,11 +88,11 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 PMC summary (its line
-    starting 'bench-traffic:'), if it was taken on the current kernel source; else None."""
+def measured_traffic(path=None, files=("kvq_decode.hip", "kvq_internal.h")):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary (its line starting
+    'bench-traffic:'), if it was taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             for line in f:
                 if line.startswith("bench-traffic:"):
                     t = json.loads(line.split(":", 1)[1])
@@ -99,7 +101,7 @@ def measured_traffic():
                 return None
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha") != kernel_source_sha():
+    if t.get("kernel_sha") != kernel_source_sha(files):
         return None
     return t.get("bytes_per_launch")
 
@@ -530,7 +532,8 @@ def bench_prefill(args):
                                "window 128", "tokens": n, "hq": hq, "hkv": hkv, "flops_per_call": flops},
         "roofline": {"bound": "mfma", "kernel": "pf_attn_kernel", "achieved": round(attn_tflops, 2),
                      "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
-                     "traffic": None, "kernel_ms": round(sec_attn * 1e3, 4),
+                     "traffic": (measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SOURCES)
+                                 if n == 16384 else None), "kernel_ms": round(sec_attn * 1e3, 4),
                      "peak_note": f"blended: {f_q8 / flops:.3f} of the work is INT8 Q K^T at 5.0 POP/s, "
                                   "the rest bf16 / fp16 at 2.5 PFLOP/s"},
         "cpu_baseline": None,
