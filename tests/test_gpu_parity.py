@@ -388,3 +388,55 @@ def test_graph_replay_matches_eager():
             run()
         torch.cuda.synchronize()
     assert int(gpu.err.item()) == 0
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_slot_map_anchors(fp8):
+    """Anchor tokens reached through a slot map (one head-group table holding 2 KV heads,
+    slots shuffled over the anchor pages, sentinel entries among them), FP16 and FP8
+    anchors: the anchor blocks bit-exact with the oracle, both heads' splits within the
+    bar."""
+    from mixed_precision_quantized_amd import kvq
+    from oracle import oracle
+    H, g, T, n_pages = 2, 4, 150, 12
+    hkv, hq = H, H * g
+    sentinel = n_pages * 16 - 1
+    _say("slot-map anchors", "fp8" if fp8 else "fp16")
+    r = np.random.default_rng(21)
+    k = r.standard_normal((T, H, 128)).astype(np.float32)
+    k[:, :, 9] *= 20.0
+    v = r.standard_normal((T, H, 128)).astype(np.float32)
+    slots = r.permutation(sentinel)[:T].astype(np.int32)
+    cache = kvq.Cache(H, (0, 0, n_pages), "cuda", sentinel_slot=sentinel, anchor_fp8=fp8)
+    ocache = oracle.Cache(H, 0, 0, n_pages, sentinel_slot=sentinel, anchor_fp8=fp8)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kvq.quantize_append(cache, torch.as_tensor(k, device="cuda"), torch.as_tensor(v, device="cuda"),
+                        rows16=torch.arange(T, dtype=torch.int32, device="cuda"),
+                        slots16=torch.as_tensor(slots, device="cuda"), dev_err=err)
+    ocache.append(k, v, oracle.F32, H * 128, 128, rows16=np.arange(T, dtype=np.int32), slots16=slots)
+    ocache.append(np.zeros((1, H, 128), np.float32), np.zeros((1, H, 128), np.float32), oracle.F32, H * 128, 128,
+                  rows16=np.zeros(1, np.int32), slots16=np.array([sentinel], np.int32))
+    kvq.quantize_append(cache, torch.zeros((1, H, 128), device="cuda"), torch.zeros((1, H, 128), device="cuda"),
+                        rows16=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                        slots16=torch.full((1,), sentinel, dtype=torch.int32, device="cuda"), dev_err=err)
+    entries = list(slots)
+    for at in sorted(r.choice(T, 6, replace=False), reverse=True):
+        entries.insert(int(at), sentinel)                     # dead entries among the live ones
+    table = np.array([entries], np.int32)
+    L = table.shape[1]
+    splits = np.array([[0, 0, 2, 0, L], [0, 1, 2, 0, L], [0, 0, 2, 7, 61]], np.int32)
+    q = r.standard_normal((1, hq, 128)).astype(np.float32)
+    part_o = torch.empty((3, g, 128), dtype=torch.float32, device="cuda")
+    part_lse = torch.empty((3, g), dtype=torch.float32, device="cuda")
+    kvq.decode_attn(cache, torch.as_tensor(q, device="cuda"), hkv, torch.as_tensor(table, device="cuda"),
+                    kvq.TABLE_SLOTS, torch.as_tensor(splits, device="cuda"), part_o, part_lse, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(cache.pool_bytes(2).cpu().numpy(), ocache.pool_bytes(2))
+    ref, ref_lse = ocache.attend_ranges(q, 1, hq, hkv, table, oracle.SLOTS,
+                                        synth.ranges_array([tuple(s) for s in splits]))
+    got = part_o.cpu().numpy()
+    e = max(row_metric(ref[i], got[i]) for i in range(3))
+    _say(f"  slot-map anchors ({'fp8' if fp8 else 'fp16'}): row error {e:.2e}")
+    assert e <= TOL
+    assert np.allclose(part_lse.cpu().numpy(), ref_lse, atol=1e-3, rtol=1e-4)
