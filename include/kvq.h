@@ -305,8 +305,9 @@ size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_max, int32_t hkv);
  *   (|v| < 65504); n_max a multiple of 64; g = hq / hkv in {1, 2, 4, 8, 16}.
  *   q_codes [dev] int8 like q, q_scales float [batch][hq][n_max/64], k_codes int8
  *   like k, k_scales float [batch][hkv][n_max/64]: written by prepare, read by
- *   attn.  workspace [dev]: at least kvq_prefill_workspace_bytes(batch, n_max,
- *   hkv) bytes, 256-byte aligned, owned by the caller.  out [dev] float
+ *   attn.  q, k, v and the codes 16-byte aligned.  workspace [dev]: at least
+ *   kvq_prefill_workspace_bytes(batch, n_max, hkv) bytes, 256-byte aligned, owned
+ *   by the caller.  out [dev] float
  *   [batch][n_max][hq][128] (0 for t >= n).
  * Errors: INVALID_ARG, UNSUPPORTED (dtype other than KVQ_BF16, another g, sizes
  * past 32-bit offsets), CAPACITY (workspace too small), HIP; a request whose

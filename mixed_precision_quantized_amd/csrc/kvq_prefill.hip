@@ -562,7 +562,8 @@ __global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
   const int32_t q_hi = kmax - a.window;       // the last INT8 key
   pl.n8 = q_hi >= 0 ? q_hi / kTile + 1 : 0;
   pl.n8_clean = min(pl.n8, max(p0 - a.window + 1, 0) / kTile);
-  pl.nvl = a.cls ? (a.vl_cnt[(int64_t)bh * a.tiles + kmax / kTile] + kTile - 1) / kTile : 0;
+  // (clamped, so that a list left by another call cannot send the copies past it)
+  pl.nvl = a.cls ? (min(max(a.vl_cnt[(int64_t)bh * a.tiles + kmax / kTile], 0), a.n_max) + kTile - 1) / kTile : 0;
   pl.w_first = max(p0 - a.window + 1, 0) / kTile;
   pl.nwin = a.window > 0 ? kmax / kTile - pl.w_first + 1 : 0;
   const int total = pl.n8 + pl.nvl + pl.nwin;
@@ -740,6 +741,11 @@ kvq_status pf_setup(PfArgs &a, const void *q, const void *k, const void *v, int3
   }
   if (!q || !k || !n_tokens || !q_codes || !q_scales || !k_codes || !k_scales || !workspace)
     return fail(KVQ_ERR_INVALID_ARG, "NULL buffer");
+  // 16-byte LDS-bound copies read q, k, v, the codes and the workspace regions.
+  auto misaligned = [](const void *p, uintptr_t to) { return p && (reinterpret_cast<uintptr_t>(p) & (to - 1)); };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(q_codes, 16) ||
+      misaligned(k_codes, 16) || misaligned(workspace, 256))
+    return fail(KVQ_ERR_INVALID_ARG, "q, k, v and the codes must be 16-byte aligned, the workspace 256-byte aligned");
   // LDS-bound loads address one (request, head)'s K rows, V^T rows and lists with 32-bit
   // byte offsets.
   if ((int64_t)n_max * hkv * kHeadDim * 2 > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "n_max * hkv too large");

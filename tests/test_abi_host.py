@@ -215,3 +215,9 @@ def test_prefill_workspace_and_validation(kvq):
         assert call(nbytes=need - 1) == -3      # scratch too small
         assert b"workspace" in lib.kvq_last_error()
     assert attn(out=None) == -1 and prepare(v=None) == -1
+    odd = ctypes.c_void_p(0x1008)                     # 8-byte aligned only
+    assert lib.kvq_prefill_attn(odd, fake, 1, 1, 128, 4, 2, fake, None, 16, fake, fake, fake, fake, fake, need,
+                                fake, None, None) == -1
+    assert lib.kvq_prefill_prepare(fake, fake, fake, 1, 1, 128, 4, 2, fake, None, fake, fake, fake, fake,
+                                   ctypes.c_void_p(0x1010), need, None, None) == -1   # workspace off 256
+    assert b"aligned" in lib.kvq_last_error()
