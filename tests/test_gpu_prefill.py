@@ -106,3 +106,32 @@ def test_full_size_sampled():
     e = row_metric(ref, got)
     _say(f"  full size: row error {e:.2e} over {len(pos)} positions x {hq} heads")
     assert e <= TOL
+
+
+def test_empty_and_single_token_requests_and_window_class():
+    """A request of length 0, one of length 1 and a ragged one in one batch; class flags
+    holding 2 (the FREEZE window class the selection writes) besides 0 and 1: only 1
+    marks a vertical line."""
+    from mixed_precision_quantized_amd import kvq
+    from oracle import oracle
+    from harness import row_metric
+    _say("lengths 0 / 1 / 200, classes 0 / 1 / 2")
+    batch, n_max, hq, hkv = 3, 256, 8, 2
+    q, k, v, _, _ = synth.prefill_qkv(13, batch, n_max, hq, hkv)
+    lens = np.array([0, 1, 200], np.int32)
+    cls = np.random.default_rng(13).integers(0, 3, (batch, hkv, n_max)).astype(np.uint8)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qc, qs, kc, ks, _, out = kvq.prefill_attn(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(lens, device="cuda"),
+                                             torch.as_tensor(cls, device="cuda"), window=32, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref, rqc, rqs, rkc, rks = oracle.prefill_attend(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens,
+                                                    cls, 32)
+    assert np.array_equal(qc.cpu().numpy(), rqc) and np.array_equal(kc.cpu().numpy(), rkc)
+    assert np.array_equal(qs.cpu().numpy(), rqs) and np.array_equal(ks.cpu().numpy(), rks)
+    got = out.cpu().numpy()
+    assert not got[0].any() and not got[1, 1:].any() and not got[2, 200:].any()
+    e = row_metric(np.concatenate([ref[1, :1].reshape(-1, 128), ref[2, :200].reshape(-1, 128)]),
+                   np.concatenate([got[1, :1].reshape(-1, 128), got[2, :200].reshape(-1, 128)]))
+    _say(f"  edge batch: row error {e:.2e}")
+    assert e <= TOL
