@@ -381,7 +381,9 @@ kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, int32_t n_s
  *     pieces per (table, head), shared among its non-empty ranges in proportion
  *     to their decode cost, tokens x class_cost[cls] (class_cost [host, may be
  *     NULL]: float [3] per INT2 / INT4 / FP16 token-head, all > 0; NULL =
- *     1.0 / 1.0 / 4.0, the kernel's relative time per token-head on MI355X), at
+ *     1.0 / 1.0 / 8.0: an FP16 token-head costs its kernel about 6x an INT4 one
+ *     on MI355X, and the extra weight gives the anchors' kernel more, shorter
+ *     splits to run in parallel after the INT2 / INT4 kernel), at
  *     least one each, largest remainders first, so a head gets exactly its count
  *     whenever that is at least its number of non-empty ranges;
  *   tokens_per_split[cls] > 0 [host, may be NULL]: ceil(tokens / that);

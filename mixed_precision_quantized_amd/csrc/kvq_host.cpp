@@ -50,8 +50,11 @@ static int64_t token_bytes(int cls) { return cls == KVQ_INT2 ? 96 : cls == KVQ_I
 // Default relative decode time of one token-head per class on MI355X, used to share a
 // head's split count among its ranges.  INT2 windows are bound by dequantization work
 // and INT4 ones by their bytes, which takes about as long per token (measured: a
-// weight of 1.0 for INT4 beat 0.8 and 1.15-1.8); FP16 windows move 512 B per token.
-static const float kDefaultTokenCost[3] = {1.0f, 1.0f, 4.0f};
+// weight of 1.0 for INT4 beat 0.8 and 1.15-1.8); FP16 windows move 512 B per token and
+// run in their own, register-staged kernel after the others (measured on the
+// hybrid-anchor decode: 8.0 gave 600 us per layer against 617-618 us for 4.0 and 6.0,
+// 654 us for 16.0).
+static const float kDefaultTokenCost[3] = {1.0f, 1.0f, 8.0f};
 
 }  // namespace kvq
 
