@@ -165,6 +165,31 @@ def test_g8_and_g1_heads():
         _check_case(f"g={hq // 8}", make, dict(target_bytes=1 << 16))
 
 
+def _with_ratio(w, g, seed):
+    """The workload with g query heads per KV head (bf16 queries of the new shape)."""
+    w.hq = g * w.hkv
+    w.q = synth._bf16(synth.randn((w.batch, w.hq, 128), seed, 78))
+    return w
+
+
+@pytest.mark.parametrize("g", [2, 16])
+def test_gqa_ratios_every_kernel(g):
+    """g = 2 and g = 16 through every decode kernel: INT2 / INT4 pages (LDS-staged, two
+    waves per split at g = 16), FP16 anchor pages (register-staged, four query tiles at
+    g = 16) and slot maps with dead entries (LDS-staged INT4 at g = 2, register-staged
+    for every split at g = 16)."""
+    _check_case(f"qwen3_8b g={g}", lambda: _with_ratio(synth.qwen3_8b(batch=1, n_tokens=1024), g, 5),
+                dict(target_bytes=1 << 16))
+    _check_case(f"hybrid g={g}", lambda: _with_ratio(synth.hybrid_anchor(batch=1, n_tokens=4096), g, 6),
+                dict(target_bytes=1 << 16))
+
+    def make():
+        return _with_ratio(synth.ragged_dead(batch=2, lo=256, hi=1024), g, 7)
+    from mixed_precision_quantized_amd import kvq
+    _check_case(f"ragged g={g}", make,
+                dict(splits_per_head=kvq.aot_split_counts(make().head_budget, 2, 64)))
+
+
 def test_split_count_invariance_on_gpu():
     """Different split plans of the same cache agree to the parity tolerance (fp16 operand
     roundings depend on each split's running maximum, so agreement is not bitwise)."""
