@@ -16,6 +16,7 @@ codes + fp16 scale/zero of every live token-head, 4 B per table entry, q and the
 output), us per step, the roofline of the decode kernel and the CPU oracle's rate on a
 bounded sample of the same workload."""
 import argparse
+import functools
 import hashlib
 import json
 import os
@@ -140,6 +141,8 @@ def main():
     ap.add_argument("--prefill-tokens", type=int, default=16384, help="prompt length of the prefill workload")
     ap.add_argument("--anchor-fp8", action="store_true",
                     help="decode workloads: anchors (the FP16 class) stored as e4m3 codes with a power-of-two scale")
+    ap.add_argument("--ordered-pages", action="store_true",
+                    help="qwen3_8b: physical pages handed out in id order instead of shuffled")
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--splits-per-head", type=int, default=0,
                     help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
@@ -174,6 +177,10 @@ def main():
         return bench_prefill(args)
     suffix, default_layers, description = WORKLOADS[args.workload]
     make = getattr(synth, args.workload)
+    if args.ordered_pages:
+        if args.workload != "qwen3_8b":
+            sys.exit("--ordered-pages applies to the qwen3_8b workload only")
+        make = functools.partial(make, ordered_pages=True)
     layers = args.layers or default_layers
     dev = "cuda"
     torch.cuda.set_device(0)
@@ -337,7 +344,8 @@ def main():
                                                    if w0.n_pages[2] else "") + ", fp32 math",
         "data": "synthetic",
         "config": {
-            "workload": description + (" (FP8 anchors)" if args.anchor_fp8 else "") + f", {layers} layers",
+            "workload": description + (" (FP8 anchors)" if args.anchor_fp8 else "")
+            + (" (pages in id order)" if args.ordered_pages else "") + f", {layers} layers",
             "batch": w0.batch, "hq": w0.hq, "hkv": w0.hkv, "layers": layers, "splits_per_layer": n_splits,
             "effective_bytes_per_layer": eff_layer,
         },

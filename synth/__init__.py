@@ -83,7 +83,7 @@ class PageAllocator:
     Page ids use one id space: INT2 [0, n2), INT4 [n2, n2+n4), FP16 after.  INT2
     pages are handed out as aligned pairs (even, even+1): one 32-token group."""
 
-    def __init__(self, n_pages, heads_per_page, n_tables, max_entries, seed, reserve_int4=0):
+    def __init__(self, n_pages, heads_per_page, n_tables, max_entries, seed, reserve_int4=0, ordered=False):
         self.n_pages = tuple(int(n) for n in n_pages)
         self.heads_per_page = heads_per_page
         r = np_rng(seed, 0xA110C)
@@ -93,6 +93,10 @@ class PageAllocator:
         ids4 = np.arange(n2 + reserve_int4, n2 + n4)
         self.free4 = list(r.permutation(ids4))
         self.free16 = list(r.permutation(np.arange(n2 + n4, n2 + n4 + n16)))
+        if ordered:  # pages handed out in increasing id order (pop() takes the last)
+            self.free2.sort(reverse=True)
+            self.free4.sort(reverse=True)
+            self.free16.sort(reverse=True)
         self.reserved4 = list(range(n2, n2 + reserve_int4))
         self.max_entries = max_entries
         self.tables = np.full((n_tables, max_entries), -1, dtype=np.int32)
@@ -264,7 +268,7 @@ def tiny(seed=0, device="cpu"):
                     n_pages, alloc, [(0, flags, np.arange(T, dtype=np.int32), False)])
 
 
-def qwen3_8b(seed=2, batch=16, n_tokens=32768, device="cpu", frac_int2=0.7, layer=0):
+def qwen3_8b(seed=2, batch=16, n_tokens=32768, device="cpu", frac_int2=0.7, layer=0, ordered_pages=False):
     """Qwen3-8B-shaped decode: Hq 32 / Hkv 8 (g = 4), d 128, one page table per request
     holding all 8 KV heads, 16-token pages.  Per request 70 % INT2 / 30 % INT4 tokens in
     shuffled runs of 32; bf16 K, V ~ N(0,1) with 1 % of K channels (10 of 1024 head
@@ -284,7 +288,7 @@ def qwen3_8b(seed=2, batch=16, n_tokens=32768, device="cpu", frac_int2=0.7, laye
     k, v = _bf16(k), _bf16(v)
     q = _bf16(randn((batch, hq, HEAD_DIM), seed, 15, layer, device=device))
     max_entries = n_tokens // PAGE
-    alloc = PageAllocator((n2, n4, 0), H, batch, max_entries, seed)
+    alloc = PageAllocator((n2, n4, 0), H, batch, max_entries, seed, ordered=ordered_pages)
     calls = [(t, flags[t], np.arange(t * n_tokens, (t + 1) * n_tokens, dtype=np.int32), False)
              for t in range(batch)]
     return Workload("qwen3_8b", seed, batch, hq, hkv, H, PAGES, torch.bfloat16, torch.bfloat16,
