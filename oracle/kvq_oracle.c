@@ -509,12 +509,14 @@ int orc_select_vl(const float *k, const float *q_tail, int32_t batch,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Prefill attention with an INT8 prefix (HyQuant Algorithm 2)               */
+/* Prefill attention with an INT8 prefix (HyQuant: the fused operator of the */
+/* core method, and Algorithm 2)                                             */
 /* ------------------------------------------------------------------------ */
 
 #define QTILE 64
 
-/* Symmetric INT8 scale of a tile: fp32 max |x| / 127 (no contraction: -ffp-contract=off). */
+/* Symmetric INT8 scale of a tile: fp32 max |x| / c_B with c_B = 127 (no contraction:
+ * -ffp-contract=off). */
 static float int8_scale(float amax)
 {
     volatile float q = amax / 127.0f;
@@ -534,64 +536,56 @@ static int8_t int8_code(float x, float s)
 #define QI(b, t, j, c) ((((int64_t)(b) * n_max + (t)) * hq + (j)) * D + (c))
 #define KI(b, t, h, c) ((((int64_t)(b) * n_max + (t)) * hkv + (h)) * D + (c))
 
-/* The INT8 tiles: queries per query head, keys per KV head (vertical lines out). */
-static void prefill_quantize(const float *q, const float *k, int32_t batch, int32_t n_max, int32_t hq,
-                             int32_t hkv, const int32_t *n_tokens, const uint8_t *cls, int8_t *q_codes,
-                             float *q_scales, int8_t *k_codes, float *k_scales)
+/* The quantized prefix of one tensor (K or V): per request, 64-position tile and KV
+ * head, the tile scale over the live positions that are not vertical lines, and every
+ * live position's codes (vertical lines too, clamped; they are never read through
+ * INT8).  Positions at or past the request's length get code 0. */
+static void prefill_quantize(const float *x, int32_t batch, int32_t n_max, int32_t hkv,
+                             const int32_t *n_tokens, const uint8_t *cls, int8_t *codes, float *scales)
 {
     const int32_t tiles = (n_max + QTILE - 1) / QTILE;
     for (int32_t b = 0; b < batch; ++b) {
         const int32_t n = n_tokens[b];
         for (int32_t tile = 0; tile < tiles; ++tile) {
             const int32_t t0 = tile * QTILE, t1 = t0 + QTILE < n ? t0 + QTILE : n;
-            for (int32_t j = 0; j < hq; ++j) {
-                float amax = 0.0f;
-                for (int32_t t = t0; t < t1; ++t)
-                    for (int c = 0; c < D; ++c) amax = fmaxf(amax, fabsf(q[QI(b, t, j, c)]));
-                const float s = int8_scale(amax);
-                q_scales[((int64_t)b * hq + j) * tiles + tile] = s;
-                for (int32_t t = t0; t < t0 + QTILE && t < n_max; ++t)
-                    for (int c = 0; c < D; ++c)
-                        q_codes[QI(b, t, j, c)] = t < n ? int8_code(q[QI(b, t, j, c)], s) : 0;
-            }
             for (int32_t h = 0; h < hkv; ++h) {
                 const uint8_t *vl = cls ? cls + ((int64_t)b * hkv + h) * n_max : NULL;
                 float amax = 0.0f;
                 for (int32_t t = t0; t < t1; ++t)
                     if (!(vl && vl[t] == 1))
-                        for (int c = 0; c < D; ++c) amax = fmaxf(amax, fabsf(k[KI(b, t, h, c)]));
+                        for (int c = 0; c < D; ++c) amax = fmaxf(amax, fabsf(x[KI(b, t, h, c)]));
                 const float s = int8_scale(amax);
-                k_scales[((int64_t)b * hkv + h) * tiles + tile] = s;
+                scales[((int64_t)b * hkv + h) * tiles + tile] = s;
                 for (int32_t t = t0; t < t0 + QTILE && t < n_max; ++t)
                     for (int c = 0; c < D; ++c)
-                        k_codes[KI(b, t, h, c)] = t < n ? int8_code(k[KI(b, t, h, c)], s) : 0;
+                        codes[KI(b, t, h, c)] = t < n ? int8_code(x[KI(b, t, h, c)], s) : 0;
             }
         }
     }
 }
 
 /* One output row (request b, position t < n, query head j): one softmax over the keys
- * kk <= t, each in full precision when it is a vertical line or kk > t - window, else
- * through INT8.  x: scratch of t + 1 doubles. */
+ * kk <= t.  A key that is a vertical line of the head or lies in the window
+ * kk > t - window is read in full precision (K and V as given); every other key is
+ * read through its tile's INT8 codes, K-hat = s_K code_K and V-hat = s_V code_V.  The
+ * query is used as given.  x: scratch of t + 1 doubles. */
 static void prefill_row(const float *q, const float *k, const float *v, int32_t n_max, int32_t hq, int32_t hkv,
-                        const uint8_t *cls, int32_t window, const int8_t *q_codes, const float *q_scales,
-                        const int8_t *k_codes, const float *k_scales, int32_t b, int32_t t, int32_t j, double *x,
+                        const uint8_t *cls, int32_t window, const int8_t *k_codes, const float *k_scales,
+                        const int8_t *v_codes, const float *v_scales, int32_t b, int32_t t, int32_t j, double *x,
                         double *o)
 {
     const int32_t g = hq / hkv, h = j / g, tiles = (n_max + QTILE - 1) / QTILE;
     const uint8_t *vl = cls ? cls + ((int64_t)b * hkv + h) * n_max : NULL;
     const double inv_sqrt_d = 1.0 / sqrt((double)D);
-    const double sq = q_scales[((int64_t)b * hq + j) * tiles + t / QTILE];
     double mx = -INFINITY;
     for (int c = 0; c < D; ++c) o[c] = 0.0;
     for (int32_t kk = 0; kk <= t; ++kk) {
+        const int full = (vl && vl[kk] == 1) || kk > t - window;
+        const double sk = k_scales[((int64_t)b * hkv + h) * tiles + kk / QTILE];
         double dot = 0.0;
-        if ((vl && vl[kk] == 1) || kk > t - window) {
-            for (int c = 0; c < D; ++c) dot += (double)q[QI(b, t, j, c)] * (double)k[KI(b, kk, h, c)];
-        } else {
-            int64_t idot = 0;
-            for (int c = 0; c < D; ++c) idot += (int64_t)q_codes[QI(b, t, j, c)] * k_codes[KI(b, kk, h, c)];
-            dot = sq * (double)k_scales[((int64_t)b * hkv + h) * tiles + kk / QTILE] * (double)idot;
+        for (int c = 0; c < D; ++c) {
+            const double kv = full ? (double)k[KI(b, kk, h, c)] : sk * (double)k_codes[KI(b, kk, h, c)];
+            dot += (double)q[QI(b, t, j, c)] * kv;
         }
         x[kk] = dot * inv_sqrt_d;
         if (x[kk] > mx) mx = x[kk];
@@ -599,8 +593,13 @@ static void prefill_row(const float *q, const float *k, const float *v, int32_t 
     double den = 0.0;
     for (int32_t kk = 0; kk <= t; ++kk) den += exp(x[kk] - mx);
     for (int32_t kk = 0; kk <= t; ++kk) {
+        const int full = (vl && vl[kk] == 1) || kk > t - window;
+        const double sv = v_scales[((int64_t)b * hkv + h) * tiles + kk / QTILE];
         const double p = exp(x[kk] - mx) / den;
-        for (int c = 0; c < D; ++c) o[c] += p * (double)v[KI(b, kk, h, c)];
+        for (int c = 0; c < D; ++c) {
+            const double vv = full ? (double)v[KI(b, kk, h, c)] : sv * (double)v_codes[KI(b, kk, h, c)];
+            o[c] += p * vv;
+        }
     }
 }
 
@@ -617,13 +616,14 @@ static int prefill_args_ok(const float *q, const float *k, const float *v, int32
 int orc_prefill_attend(const float *q, const float *k, const float *v,
                        int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
                        const int32_t *n_tokens, const uint8_t *cls, int32_t window,
-                       double *out, int8_t *q_codes, float *q_scales,
-                       int8_t *k_codes, float *k_scales)
+                       double *out, int8_t *k_codes, float *k_scales,
+                       int8_t *v_codes, float *v_scales)
 {
     int rc = prefill_args_ok(q, k, v, batch, n_max, hq, hkv, n_tokens, window);
     if (rc != ORC_OK) return rc;
-    if (!out || !q_codes || !q_scales || !k_codes || !k_scales) return ORC_EARG;
-    prefill_quantize(q, k, batch, n_max, hq, hkv, n_tokens, cls, q_codes, q_scales, k_codes, k_scales);
+    if (!out || !k_codes || !k_scales || !v_codes || !v_scales) return ORC_EARG;
+    prefill_quantize(k, batch, n_max, hkv, n_tokens, cls, k_codes, k_scales);
+    prefill_quantize(v, batch, n_max, hkv, n_tokens, cls, v_codes, v_scales);
     double *x = (double *)malloc(sizeof(double) * (size_t)(n_max > 0 ? n_max : 1));
     for (int32_t b = 0; b < batch; ++b)
         for (int32_t t = 0; t < n_max; ++t)
@@ -633,7 +633,7 @@ int orc_prefill_attend(const float *q, const float *k, const float *v,
                     for (int c = 0; c < D; ++c) o[c] = 0.0;
                     continue;
                 }
-                prefill_row(q, k, v, n_max, hq, hkv, cls, window, q_codes, q_scales, k_codes, k_scales, b, t, j, x, o);
+                prefill_row(q, k, v, n_max, hq, hkv, cls, window, k_codes, k_scales, v_codes, v_scales, b, t, j, x, o);
             }
     free(x);
     return ORC_OK;
@@ -643,25 +643,26 @@ int orc_prefill_attend_rows(const float *q, const float *k, const float *v,
                             int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
                             const int32_t *n_tokens, const uint8_t *cls, int32_t window,
                             int32_t n_rows, const int32_t *row_b, const int32_t *row_t, double *out_rows,
-                            int8_t *q_codes, float *q_scales, int8_t *k_codes, float *k_scales)
+                            int8_t *k_codes, float *k_scales, int8_t *v_codes, float *v_scales)
 {
     int rc = prefill_args_ok(q, k, v, batch, n_max, hq, hkv, n_tokens, window);
     if (rc != ORC_OK) return rc;
-    if (n_rows < 0 || (n_rows > 0 && (!row_b || !row_t || !out_rows)) || !q_codes || !q_scales || !k_codes || !k_scales)
+    if (n_rows < 0 || (n_rows > 0 && (!row_b || !row_t || !out_rows)) || !k_codes || !k_scales || !v_codes ||
+        !v_scales)
         return ORC_EARG;
     for (int32_t r = 0; r < n_rows; ++r)
         if (row_b[r] < 0 || row_b[r] >= batch || row_t[r] < 0 || row_t[r] >= n_tokens[row_b[r]]) return ORC_ERANGE;
-    prefill_quantize(q, k, batch, n_max, hq, hkv, n_tokens, cls, q_codes, q_scales, k_codes, k_scales);
-    rc = ORC_OK;
+    prefill_quantize(k, batch, n_max, hkv, n_tokens, cls, k_codes, k_scales);
+    prefill_quantize(v, batch, n_max, hkv, n_tokens, cls, v_codes, v_scales);
 #pragma omp parallel for schedule(dynamic)
     for (int32_t r = 0; r < n_rows; ++r) {
         double *x = (double *)malloc(sizeof(double) * (size_t)(row_t[r] + 1));
         for (int32_t j = 0; j < hq; ++j)
-            prefill_row(q, k, v, n_max, hq, hkv, cls, window, q_codes, q_scales, k_codes, k_scales, row_b[r],
+            prefill_row(q, k, v, n_max, hq, hkv, cls, window, k_codes, k_scales, v_codes, v_scales, row_b[r],
                         row_t[r], j, x, out_rows + ((int64_t)r * hq + j) * D);
         free(x);
     }
-    return rc;
+    return ORC_OK;
 }
 #undef QI
 #undef KI

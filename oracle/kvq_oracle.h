@@ -21,9 +21,11 @@
  *       Algorithm 1 (vertical lines: window W excluded, tail-query proxy,
  *       GQA column scores, top rho of the prefix) and Algorithm 4 (FREEZE:
  *       vertical lines and window stay full precision, the rest is quantized);
- *       Algorithm 2 (prefill: per-tile symmetric INT8 scale max|x| / 127 for
- *       the quantized prefix, then the vertical-line and window segments in
- *       full precision, one softmax over all of them).
+ *       the core method's fused prefill operator (the query as given; the
+ *       quantized prefix's keys and values both through their quantized
+ *       forms, vertical lines and window in full precision, one softmax over
+ *       the concatenation) and Algorithm 2 (per-tile symmetric scale
+ *       max|X_T| / c_B, c_B = 127 for INT8).
  *   [IntentKV] technical summary, "layout-preserving eviction": evicted
  *       positions are redirected to one sentinel dead slot (K = -1e4, V = 0)
  *       whose attention contribution is zero.
@@ -145,34 +147,35 @@ int orc_select_vl(const float *k, const float *q_tail, int32_t batch,
                   const int32_t *n_tokens, const int32_t *n_tail, int32_t window,
                   double rho, double *scores, uint8_t *cls, int32_t *n_vl);
 
-/* --- prefill attention with an INT8 prefix (HyQuant Algorithm 2) ---------
+/* --- prefill attention with an INT8 prefix (HyQuant core method, fused
+ * operator O = softmax([Q K-hat_Q^T || Q K_FP^T] / sqrt(d)) [V-hat_Q || V_FP];
+ * Algorithm 2) ---------------------------------------------------------------
  * Per request b (n = n_tokens[b] prompt positions), query head j and query
  * position t, over the keys k <= t of KV head h = j / g: a key is read in full
- * precision when it is a vertical line of h (cls[(b*hkv + h)*n_max + k] == 1) or
- * in the window k > t - window; every other visible key is read through INT8.
- * INT8 tiles are 64 positions: for query head j the tile of t, for KV head h
- * the tile of k (vertical lines left out of K's tile maximum).  Tile scale
- * s = fl32(max |x| / 127) over the tile's values (0 for an empty or zero tile),
- * code = clamp(rint(fl32(x / s)), -127, 127) (0 when s = 0), all fp32.  The
- * logit of an INT8 pair is s_Q s_K (q_code . k_code) / sqrt(128), of a full
- * pair q . k / sqrt(128), in fp64 from the bf16/fp32-exact inputs; the softmax
- * and the sum of V (never quantized) are fp64.  q [batch][n_max][hq][128],
- * k, v [batch][n_max][hkv][128] fp32; out fp64 [batch][n_max][hq][128] (0 for
- * t >= n).  The codes and scales are returned too: q_codes int8 like q,
- * q_scales [batch][hq][n_max/64 rounded up], k_codes int8 like k, k_scales
- * [batch][hkv][n_max/64 rounded up]. */
+ * precision (K and V as given) when it is a vertical line of h
+ * (cls[(b*hkv + h)*n_max + k] == 1) or in the window k > t - window; every other
+ * visible key is read through INT8 (K-hat = s_K code_K, V-hat = s_V code_V).  The
+ * query is never quantized.  INT8 tiles are 64 positions per KV head, separately
+ * for K and V, with the vertical lines left out of the tile maximum.  Tile scale
+ * s = fl32(max |x| / 127) over the tile's live non-line values (0 for an empty or
+ * zero tile), code = clamp(rint(fl32(x / s)), -127, 127) (0 when s = 0), all fp32.
+ * Logits q . k / sqrt(128) and the softmax and its sum of V are fp64 from the
+ * bf16/fp32-exact inputs.  q [batch][n_max][hq][128], k, v
+ * [batch][n_max][hkv][128] fp32; out fp64 [batch][n_max][hq][128] (0 for t >= n).
+ * The codes and scales are returned: k_codes, v_codes int8 like k, k_scales,
+ * v_scales [batch][hkv][n_max/64 rounded up]. */
 int orc_prefill_attend(const float *q, const float *k, const float *v,
                        int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
                        const int32_t *n_tokens, const uint8_t *cls, int32_t window,
-                       double *out, int8_t *q_codes, float *q_scales,
-                       int8_t *k_codes, float *k_scales);
+                       double *out, int8_t *k_codes, float *k_scales,
+                       int8_t *v_codes, float *v_scales);
 /* The same for the listed rows only: out_rows [n_rows][hq][128] for (row_b[r],
  * row_t[r]), row_t[r] < n_tokens[row_b[r]]; the codes and scales in full. */
 int orc_prefill_attend_rows(const float *q, const float *k, const float *v,
                             int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
                             const int32_t *n_tokens, const uint8_t *cls, int32_t window,
                             int32_t n_rows, const int32_t *row_b, const int32_t *row_t, double *out_rows,
-                            int8_t *q_codes, float *q_scales, int8_t *k_codes, float *k_scales);
+                            int8_t *k_codes, float *k_scales, int8_t *v_codes, float *v_scales);
 
 /* Dequantize one token of one head to fp64 (K and V, 128 channels each). */
 int orc_token(const orc_cache *c, int32_t page, int32_t off, int32_t head,

@@ -190,26 +190,27 @@ def select_vl(k, q_tail, n_tokens, n_tail, window=128, rho=0.05):
 
 
 def prefill_attend(q, k, v, n_tokens, cls=None, window=128):
-    """Prefill attention with an INT8 prefix.  q [batch, n_max, hq, 128], k, v
-    [batch, n_max, hkv, 128] float32; cls uint8 [batch, hkv, n_max] (1 = vertical line)
-    or None.  Returns (out fp64 like q, q_codes, q_scales, k_codes, k_scales)."""
+    """Prefill attention with an INT8 prefix (q plain, prefix K and V quantized).  q
+    [batch, n_max, hq, 128], k, v [batch, n_max, hkv, 128] float32; cls uint8 [batch,
+    hkv, n_max] (1 = vertical line) or None.  Returns (out fp64 like q, k_codes,
+    k_scales, v_codes, v_scales)."""
     q, k, v = (_c_array(a, np.float32) for a in (q, k, v))
     batch, n_max, hq = q.shape[:3]
     hkv = k.shape[2]
     tiles = (n_max + 63) // 64
     out = np.zeros(q.shape, np.float64)
-    qc, kc = np.zeros(q.shape, np.int8), np.zeros(k.shape, np.int8)
-    qs, ks = np.zeros((batch, hq, tiles), np.float32), np.zeros((batch, hkv, tiles), np.float32)
+    kc, vc = np.zeros(k.shape, np.int8), np.zeros(k.shape, np.int8)
+    ks, vs = np.zeros((batch, hkv, tiles), np.float32), np.zeros((batch, hkv, tiles), np.float32)
     c = None if cls is None else _c_array(cls, np.uint8)
     _check(lib().orc_prefill_attend(_ptr(q), _ptr(k), _ptr(v), batch, n_max, hq, hkv,
                                     _ptr(_c_array(n_tokens, np.int32)), _ptr(c), window, _ptr(out),
-                                    _ptr(qc), _ptr(qs), _ptr(kc), _ptr(ks)), "prefill_attend")
-    return out, qc, qs, kc, ks
+                                    _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs)), "prefill_attend")
+    return out, kc, ks, vc, vs
 
 
 def prefill_attend_rows(q, k, v, n_tokens, cls, window, rows):
     """prefill_attend for the listed (request, position) rows only: (out fp64 [n_rows,
-    hq, 128], q_codes, q_scales, k_codes, k_scales)."""
+    hq, 128], k_codes, k_scales, v_codes, v_scales)."""
     q, k, v = (_c_array(a, np.float32) for a in (q, k, v))
     batch, n_max, hq = q.shape[:3]
     hkv = k.shape[2]
@@ -217,14 +218,14 @@ def prefill_attend_rows(q, k, v, n_tokens, cls, window, rows):
     rows = np.asarray(rows, np.int32).reshape(-1, 2)
     rb, rt = np.ascontiguousarray(rows[:, 0]), np.ascontiguousarray(rows[:, 1])
     out = np.zeros((rows.shape[0], hq, HEAD_DIM), np.float64)
-    qc, kc = np.zeros(q.shape, np.int8), np.zeros(k.shape, np.int8)
-    qs, ks = np.zeros((batch, hq, tiles), np.float32), np.zeros((batch, hkv, tiles), np.float32)
+    kc, vc = np.zeros(k.shape, np.int8), np.zeros(k.shape, np.int8)
+    ks, vs = np.zeros((batch, hkv, tiles), np.float32), np.zeros((batch, hkv, tiles), np.float32)
     c = None if cls is None else _c_array(cls, np.uint8)
     _check(lib().orc_prefill_attend_rows(_ptr(q), _ptr(k), _ptr(v), batch, n_max, hq, hkv,
                                          _ptr(_c_array(n_tokens, np.int32)), _ptr(c), window, rows.shape[0],
-                                         _ptr(rb), _ptr(rt), _ptr(out), _ptr(qc), _ptr(qs), _ptr(kc), _ptr(ks)),
+                                         _ptr(rb), _ptr(rt), _ptr(out), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs)),
            "prefill_attend_rows")
-    return out, qc, qs, kc, ks
+    return out, kc, ks, vc, vs
 
 
 class Cache:
