@@ -284,46 +284,51 @@ kvq_status kvq_select_vertical_lines(const void *k, int32_t k_dtype, const void 
 size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_max, int32_t hkv);
 
 /*
- * Prefill attention with an INT8 prefix (HyQuant Algorithm 2).  For request b
+ * Prefill attention with an INT8 prefix (HyQuant, core method: the fused operator
+ * O = softmax([Q K-hat_Q^T || Q K_FP^T] / sqrt(d)) [V-hat_Q || V_FP]; Algorithm 2:
+ * per-tile symmetric scale max|X_T| / c_B, c_B = 127 for INT8).  For request b
  * (n = n_tokens[b] <= n_max prompt positions), query head j (KV head h = j / g)
- * and query position t < n, over the keys k <= t: a key is read in full
- * precision when it is a vertical line of h (token_class[b][h][k] == 1, as
- * kvq_select_vertical_lines writes it; NULL = none) or lies in the window
- * k > t - window, and through INT8 otherwise; one softmax over all of them,
- * out[b][t][j] = sum_k p_k v_k (V not quantized).  INT8: tiles of 64 positions,
- * per query head for Q and per KV head for K (vertical lines left out of the
- * maximum); scale s = fl32(max |x| / 127), code = clamp(rint(fl32(x / s)), -127,
- * 127) (0 when s = 0); the logit of an INT8 pair is s_Q s_K (q_code . k_code).
+ * and query position t < n, over the keys k <= t: a key is read in full precision
+ * (K and V as given) when it is a vertical line of h (token_class[b][h][k] == 1,
+ * as kvq_select_vertical_lines writes it; NULL = none) or lies in the window
+ * k > t - window, and through INT8 otherwise (K-hat = s_K code_K, V-hat =
+ * s_V code_V); the query is used as given; one softmax over all of them,
+ * out[b][t][j] = sum_k p_k v_k.  INT8: tiles of 64 positions per KV head,
+ * separately for K and V (vertical lines left out of the maximum); scale
+ * s = fl32(max |x| / 127), code = clamp(rint(fl32(x / s)), -127, 127) (0 when
+ * s = 0, and for t >= n).
+ *
+ * Precision: Q . K-hat and Q . K are bf16 products with fp32 sums (the K codes
+ * enter as exact integers, s_K scales the fp32 logit); V and V-hat enter P.V in
+ * fp16 (V-hat = s_V code_V rounded once to fp16) with fp16 weights; the result is
+ * within the 2e-3 row error of the exact operator for |v| inside fp16's normal
+ * range.
  *
  * Two calls, in stream order on one workspace:
- *   kvq_prefill_prepare: the INT8 codes and tile scales of q and k, and the
- *     scratch the attention reads (V transposed to fp16, the keep mask, the
- *     vertical-line lists and their gathered K and V);
- *   kvq_prefill_attn: the attention, from what prepare left with the same q, k,
+ *   kvq_prefill_prepare: the INT8 codes and tile scales of k and v, and the
+ *     scratch the attention reads (the K codes as bf16, V and V-hat transposed to
+ *     fp16, the keep mask, the vertical-line lists and their gathered K and V);
+ *   kvq_prefill_attn: the attention, from what prepare left with the same k,
  *     n_tokens and token_class.
  *   q [dev] bf16 [batch][n_max][hq][128]; k, v [dev] bf16 [batch][n_max][hkv][128]
  *   (|v| < 65504); n_max a multiple of 64; g = hq / hkv in {1, 2, 4, 8, 16}.
- *   q_codes [dev] int8 like q, q_scales float [batch][hq][n_max/64], k_codes int8
- *   like k, k_scales float [batch][hkv][n_max/64]: written by prepare, read by
- *   attn.  q, k, v and the codes 16-byte aligned.  workspace [dev]: at least
+ *   k_codes, v_codes [dev] int8 like k, k_scales, v_scales float
+ *   [batch][hkv][n_max/64]: written by prepare; attn reads k_scales.  q, k, v and
+ *   the codes 16-byte aligned.  workspace [dev]: at least
  *   kvq_prefill_workspace_bytes(batch, n_max, hkv) bytes, 256-byte aligned, owned
- *   by the caller.  out [dev] float
- *   [batch][n_max][hq][128] (0 for t >= n).
+ *   by the caller.  out [dev] float [batch][n_max][hq][128] (0 for t >= n).
  * Errors: INVALID_ARG, UNSUPPORTED (dtype other than KVQ_BF16, another g, sizes
  * past 32-bit offsets), CAPACITY (workspace too small), HIP; a request whose
  * n_tokens is out of range is treated as empty (KVQ_DEVERR_RANGE).
  */
-kvq_status kvq_prefill_prepare(const void *q, const void *k, const void *v, int32_t dtype,
-                               int32_t batch, int32_t n_max, int32_t hq, int32_t hkv,
-                               const int32_t *n_tokens, const uint8_t *token_class,
-                               int8_t *q_codes, float *q_scales, int8_t *k_codes,
-                               float *k_scales, void *workspace, size_t workspace_bytes,
-                               int32_t *dev_err, void *stream);
+kvq_status kvq_prefill_prepare(const void *k, const void *v, int32_t dtype, int32_t batch,
+                               int32_t n_max, int32_t hkv, const int32_t *n_tokens,
+                               const uint8_t *token_class, int8_t *k_codes, float *k_scales,
+                               int8_t *v_codes, float *v_scales, void *workspace,
+                               size_t workspace_bytes, int32_t *dev_err, void *stream);
 kvq_status kvq_prefill_attn(const void *q, const void *k, int32_t dtype, int32_t batch,
                             int32_t n_max, int32_t hq, int32_t hkv, const int32_t *n_tokens,
-                            const uint8_t *token_class, int32_t window,
-                            const int8_t *q_codes, const float *q_scales,
-                            const int8_t *k_codes, const float *k_scales,
+                            const uint8_t *token_class, int32_t window, const float *k_scales,
                             const void *workspace, size_t workspace_bytes, float *out,
                             int32_t *dev_err, void *stream);
 

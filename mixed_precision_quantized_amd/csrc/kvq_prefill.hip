@@ -1,29 +1,35 @@
-// Prefill attention with an INT8 prefix (HyQuant Algorithm 2).
+// Prefill attention with an INT8 prefix (HyQuant: the fused operator of the core method,
+// softmax([Q K-hat_Q^T || Q K_FP^T] / sqrt(d)) [V-hat_Q || V_FP], and Algorithm 2).
 //
 // For query position t of a request, query head j and its KV head h = j / g, the keys
-// k <= t are read in full precision when k is a vertical line of h or lies in the window
-// k > t - W, and through INT8 otherwise; all of them share one online softmax.  INT8
-// tiles are 64 positions with the symmetric scale max|x| / 127 (queries per query head,
-// keys per KV head with the vertical lines left out of the maximum).  V is not
-// quantized: it enters P.V as fp16 (exact for bf16 values in fp16's normal range), with
-// fp16 weights (bf16 weights would lose too much for the 2e-3 bar).
+// k <= t are read in full precision (K and V as given) when k is a vertical line of h or
+// lies in the window k > t - W, and through INT8 otherwise (K-hat = s_K code_K, V-hat =
+// s_V code_V); the query is used as given; all of them share one online softmax.  INT8
+// tiles are 64 positions per KV head, separately for K and V, with the symmetric scale
+// max|x| / 127 over the tile's live non-line values.
 //
 // The three segments of the scan are three key lists:
-//   INT8    keys k <= t - W that are not vertical lines: K codes, and V^T with the
-//           vertical-line columns zeroed, so their weights drop out of P.V; their
-//           softmax weights enter the row sum through a 0 / 1 keep mask;
+//   INT8    keys k <= t - W that are not vertical lines: K codes as exact bf16 integers
+//           (the tile's s_K scales the fp32 logit), and V-hat^T (s_V code_V in fp16,
+//           formed once per tile) with the vertical-line columns zeroed, so their
+//           weights drop out of P.V; their softmax weights enter the row sum through a
+//           0 / 1 keep mask;
 //   VL      the vertical lines k <= t, gathered per KV head into a compact list (bf16
 //           K rows, fp16 V^T columns, positions);
-//   window  keys t - W < k <= t that are not vertical lines, bf16 K.
-// Their union is every key k <= t, each in the precision the method gives it.
+//   window  keys t - W < k <= t that are not vertical lines, bf16 K and fp16 V^T.
+// Their union is every key k <= t, each in the precision the method gives it.  Q . K
+// is a bf16 product (exact products, fp32 sums) in every segment; V enters P.V in fp16
+// (exact for bf16 values in fp16's normal range; V-hat rounded once to fp16) with fp16
+// weights (bf16 weights would lose too much for the 2e-3 bar).
 //
-// Launches: INT8 codes and scales (one work group per 64-position tile and head); V^T
-// with the keep mask; the vertical-line list (one work group per request and KV head);
-// its gather; the attention.  An attention work group (4 waves, two groups per CU) takes
-// one request, one KV head and 128 / g positions of all g of its query heads (of half of
-// them, for g = 16): 8 column blocks of 16 (position, head) rows, two per wave.  K and V^T stages of 64 keys go to LDS by
-// LDS-bound global loads, double-buffered across all three segments; S^T = K Q^T on
-// MFMA (i32 16x16x64 for INT8, f32 16x16x32 bf16 otherwise) puts a lane's scores where
+// Launches: K codes and scales with their bf16 copy (one work group per 64-position
+// tile and KV head); V codes and scales, V-hat^T and V^T with the keep mask (the same
+// grid); the vertical-line list (one work group per request and KV head); its gather;
+// the attention.  An attention work group (4 waves, two groups per CU) takes one
+// request, one KV head and 128 / g positions of all g of its query heads (of half of
+// them, for g = 16): 8 column blocks of 16 (position, head) rows, two per wave.  K and
+// V^T stages of 64 keys go to LDS by LDS-bound global loads, double-buffered across all
+// three segments; S^T = K Q^T on MFMA (f32 16x16x32 bf16) puts a lane's scores where
 // the P operand of O^T = V^T P^T wants them (f32 16x16x32 f16).  The softmax rescales
 // lazily: the running maximum moves only when a score exceeds it by 2^8.
 #include <hip/hip_runtime.h>
@@ -31,7 +37,6 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
-#include <type_traits>
 
 #include "kvq.h"
 #include "kvq_internal.h"
@@ -68,9 +73,11 @@ struct PfArgs {
   const int32_t *n_tokens;
   int32_t batch, n_max, hq, hkv, g, window, tiles;
   int32_t hsplit;                // attention work groups per (position block, KV head)
-  int8_t *q_codes, *k_codes;     // like q, k
-  float *q_scales, *k_scales;    // [batch][hq][tiles], [batch][hkv][tiles]
-  uint16_t *vt;                  // fp16 [batch][hkv][128][n_max]; vertical lines, t >= n: 0
+  int8_t *k_codes, *v_codes;     // like k, v
+  float *k_scales, *v_scales;    // [batch][hkv][tiles]
+  uint16_t *kq;                  // bf16 [batch][n_max][hkv][128]: K codes as exact bf16 integers
+  uint16_t *vt;                  // fp16 [batch][hkv][128][n_max]: V; vertical lines, t >= n: 0
+  uint16_t *vtq;                 // fp16 [batch][hkv][128][n_max]: V-hat = s_V code_V; lines, t >= n: 0
   uint16_t *keep;                // fp16 [batch][hkv][n_max]: 1 for live keys that are not lines
   int32_t *vl_pos;               // [batch][hkv][n_max]: line positions in order, then INT32_MAX
   int32_t *vl_cnt;               // [batch][hkv][tiles]: lines at positions < 64 (tile + 1)
@@ -85,26 +92,31 @@ __device__ __forceinline__ int32_t checked_n(const PfArgs &a, int b) {
   return (n < 0 || n > a.n_max) ? -1 : n;
 }
 
-// Codes and scale of one 64-position tile of one head (blockIdx.z < hq: query head z,
-// else KV head z - hq).  Thread: row tid / 4, channels 32 (tid % 4) .. + 31.
-__global__ void __launch_bounds__(256) pf_quant_kernel(PfArgs a) {
+// INT8 code of x in a tile of scale s (Algorithm 2's symmetric scale): clamp(rint(x / s),
+// -127, 127) with a correctly rounded fp32 quotient, 0 when s = 0.
+__device__ __forceinline__ float int8_code(float x, float s) {
+  return s != 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(x, s)), -127.0f), 127.0f) : 0.0f;
+}
+
+// K codes and scale of one 64-position tile of one KV head, and the codes as exact bf16
+// integers (the attention's K operand).  Thread: row tid / 4, channels 32 (tid % 4) ..
+// + 31.
+__global__ void __launch_bounds__(256) pf_quant_k_kernel(PfArgs a) {
   __shared__ float wmax[4];
-  const int tid = threadIdx.x, tile = blockIdx.x, b = blockIdx.y, z = blockIdx.z;
-  const bool is_q = z < a.hq;
-  const int heads = is_q ? a.hq : a.hkv, head = is_q ? z : z - a.hq;
+  const int tid = threadIdx.x, tile = blockIdx.x, b = blockIdx.y, head = blockIdx.z;
   int32_t n = checked_n(a, b);
   if (n < 0) {
     if (tid == 0) report(a.err, KVQ_DEVERR_RANGE);
     n = 0;
   }
   const int row = tile * kTile + tid / 4, c0 = 32 * (tid % 4);
-  const uint16_t *src = (is_q ? a.q : a.k) + (((int64_t)b * a.n_max + row) * heads + head) * kHeadDim + c0;
+  const int64_t at = (((int64_t)b * a.n_max + row) * a.hkv + head) * kHeadDim + c0;
   const bool live = row < n;
-  const bool counts = live && (is_q || !a.cls || a.cls[((int64_t)b * a.hkv + head) * a.n_max + row] != 1);
+  const bool counts = live && !(a.cls && a.cls[((int64_t)b * a.hkv + head) * a.n_max + row] == 1);
   float x[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 w = reinterpret_cast<const uint4 *>(src)[i];
+    const uint4 w = live ? reinterpret_cast<const uint4 *>(a.k + at)[i] : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -121,55 +133,95 @@ __global__ void __launch_bounds__(256) pf_quant_kernel(PfArgs a) {
   __syncthreads();
   const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float s = __fdiv_rn(amax, 127.0f);
-  if (tid == 0) (is_q ? a.q_scales : a.k_scales)[((int64_t)b * heads + head) * a.tiles + tile] = s;
-  uint32_t packed[8];
+  if (tid == 0) a.k_scales[((int64_t)b * a.hkv + head) * a.tiles + tile] = s;
+  uint32_t packed[8], wide[16] = {};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t w = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float c = 0.0f;
-      if (live && s != 0.0f) c = fminf(fmaxf(rintf(__fdiv_rn(x[4 * i + e], s)), -127.0f), 127.0f);
+      const float c = live ? int8_code(x[4 * i + e], s) : 0.0f;
       w |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * e);
+      // an integer of at most 8 bits is exact in bf16: the top half of its fp32 bits
+      const uint32_t hb = __float_as_uint(c) >> 16;
+      wide[2 * i + (e >> 1)] |= hb << (16 * (e & 1));
     }
     packed[i] = w;
   }
-  int8_t *dst = (is_q ? a.q_codes : a.k_codes) + (((int64_t)b * a.n_max + row) * heads + head) * kHeadDim + c0;
+  int8_t *dst = a.k_codes + at;
   reinterpret_cast<uint4 *>(dst)[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   reinterpret_cast<uint4 *>(dst)[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  uint4 *kd = reinterpret_cast<uint4 *>(a.kq + at);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kd[i] = make_uint4(wide[4 * i], wide[4 * i + 1], wide[4 * i + 2], wide[4 * i + 3]);
 }
 
-// V [b][t][h][c] (bf16) -> vt [b][h][c][t] (fp16, exact in fp16's normal range) through
-// LDS, 64 positions x 128 channels a group; vertical lines and positions at or past the
-// request's length are written as 0.  Also the keep mask of the INT8 and window
-// segments: 1 for live positions that are not vertical lines.
-__global__ void __launch_bounds__(256) pf_vt_kernel(PfArgs a) {
-  __shared__ uint16_t tileb[kTile][kHeadDim + 2];
-  __shared__ uint8_t kept[kTile];
+// V of one 64-position tile of one KV head, through LDS: its codes and scale (vertical
+// lines left out of the maximum, as for K), then transposed to [channel][position]
+// twice, as given (fp16, exact in fp16's normal range) for the full-precision segments
+// and as V-hat = s_V code_V (rounded once to fp16) for the INT8 segment; vertical lines
+// and positions at or past the request's length are 0 in both.  Also the keep mask of
+// the INT8 and window segments: 1 for live positions that are not vertical lines.
+__global__ void __launch_bounds__(256) pf_quant_v_kernel(PfArgs a) {
+  __shared__ uint16_t tileb[kTile][kHeadDim + 2];  // bf16 bits
+  __shared__ int8_t codes[kTile][kHeadDim + 4];
+  __shared__ uint8_t kept[kTile], live[kTile];
+  __shared__ float wmax[4];
   const int tid = threadIdx.x, tile = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
-  int32_t n = checked_n(a, b);
+  int32_t n = checked_n(a, b);  // (the K kernel reports a bad length)
   if (n < 0) n = 0;
   const int64_t bh = (int64_t)b * a.hkv + h;
   if (tid < kTile) {
     const int t = tile * kTile + tid;
-    const bool k = t < n && !(a.cls && a.cls[bh * a.n_max + t] == 1);
+    const bool lv = t < n;
+    const bool k = lv && !(a.cls && a.cls[bh * a.n_max + t] == 1);
     kept[tid] = k ? 1 : 0;
+    live[tid] = lv ? 1 : 0;
     a.keep[bh * a.n_max + t] = k ? 0x3C00u : 0u;  // fp16 1.0, 0.0
   }
   __syncthreads();
+  float m = 0.0f;
   for (int i = tid; i < kTile * kHeadDim / 2; i += 256) {  // 2 channels per step
     const int r = i / (kHeadDim / 2), c = 2 * (i % (kHeadDim / 2));
     const int t = tile * kTile + r;
     uint32_t w = 0;
-    if (kept[r]) w = *reinterpret_cast<const uint32_t *>(a.v + (((int64_t)b * a.n_max + t) * a.hkv + h) * kHeadDim + c);
-    tileb[r][c] = __builtin_bit_cast(uint16_t, (_Float16)bf16_value((uint16_t)(w & 0xFFFFu)));
-    tileb[r][c + 1] = __builtin_bit_cast(uint16_t, (_Float16)bf16_value((uint16_t)(w >> 16)));
+    if (live[r]) w = *reinterpret_cast<const uint32_t *>(a.v + (((int64_t)b * a.n_max + t) * a.hkv + h) * kHeadDim + c);
+    tileb[r][c] = (uint16_t)(w & 0xFFFFu);
+    tileb[r][c + 1] = (uint16_t)(w >> 16);
+    if (kept[r]) m = fmaxf(m, fmaxf(fabsf(bf16_value((uint16_t)(w & 0xFFFFu))), fabsf(bf16_value((uint16_t)(w >> 16)))));
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = __fdiv_rn(amax, 127.0f);
+  if (tid == 0) a.v_scales[bh * a.tiles + tile] = s;
+  for (int i = tid; i < kTile * kHeadDim / 4; i += 256) {  // 4 channels (one code word) per step
+    const int r = i / (kHeadDim / 4), c = 4 * (i % (kHeadDim / 4));
+    const int t = tile * kTile + r;
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float cd = live[r] ? int8_code(bf16_value(tileb[r][c + e]), s) : 0.0f;
+      codes[r][c + e] = (int8_t)cd;
+      w |= ((uint32_t)(uint8_t)(int8_t)cd) << (8 * e);
+    }
+    *reinterpret_cast<uint32_t *>(a.v_codes + (((int64_t)b * a.n_max + t) * a.hkv + h) * kHeadDim + c) = w;
   }
   __syncthreads();
+  auto f16 = [](float x) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x); };
   for (int i = tid; i < kHeadDim * kTile / 2; i += 256) {  // 2 positions per step
     const int c = i / (kTile / 2), r = 2 * (i % (kTile / 2));
-    const uint32_t w = (uint32_t)tileb[r][c] | ((uint32_t)tileb[r + 1][c] << 16);
-    *reinterpret_cast<uint32_t *>(a.vt + (bh * kHeadDim + c) * a.n_max + tile * kTile + r) = w;
+    uint32_t raw = 0, deq = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if (kept[r + e]) {
+        raw |= f16(bf16_value(tileb[r + e][c])) << (16 * e);
+        deq |= f16(s * (float)codes[r + e][c]) << (16 * e);
+      }
+    const int64_t at = (bh * kHeadDim + c) * a.n_max + tile * kTile + r;
+    *reinterpret_cast<uint32_t *>(a.vt + at) = raw;
+    *reinterpret_cast<uint32_t *>(a.vtq + at) = deq;
   }
 }
 
@@ -245,11 +297,11 @@ __global__ void __launch_bounds__(256) pf_vl_gather_kernel(PfArgs a) {
 
 // ---- attention ----------------------------------------------------------------------
 
-// One stage in LDS: 64 keys of K (INT8 rows of 128 B, or bf16 rows of 256 B), V^T (128
-// channel rows of 64 fp16 keys) and 256 B of side data (fp16 keep weights, or line
-// positions).  16-byte chunks are XOR-swizzled within a row so that the 16 lanes a
-// 16-byte LDS read serves at once hit 16 different banks quads: a key row's chunk c sits
-// at c ^ swz_k(key) (INT8) or c ^ swz_w(key) (bf16), a channel row's at c ^ swz_v(ch).
+// One stage in LDS: 64 keys of K (bf16 rows of 256 B: codes or values), V^T (128 channel
+// rows of 64 fp16 keys) and 256 B of side data (fp16 keep weights, or line positions).
+// 16-byte chunks are XOR-swizzled within a row so that the 16 lanes a 16-byte LDS read
+// serves at once hit 16 different banks quads: a key row's chunk c sits at c ^ swz_w(key),
+// a channel row's at c ^ swz_v(ch).
 struct __align__(16) PfStage {
   uint8_t k[kTile * 256];
   uint8_t v[kHeadDim * kTile * 2];
@@ -257,13 +309,11 @@ struct __align__(16) PfStage {
 };
 
 // The A-operand rows a 16-lane group reads are keys {0..3, 8..11, 16..19, 24..27} (+4,
-// +32): even and odd keys land in different bank halves of a 128-byte row pair, and the
-// swizzle gives the 8 keys of each parity 8 different chunks.
-__device__ __forceinline__ int swz_k(int key) {
-  return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | (((key >> 4) & 1) << 2);
+// +32): the low three bits give the 8 keys of each parity 8 different chunks, and as
+// 256-byte rows span every bank, the parity picks the other half of the 16 chunks.
+__device__ __forceinline__ int swz_w(int key) {
+  return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | (((key >> 4) & 1) << 2) | ((key & 1) << 3);
 }
-// 256-byte rows span every bank: the parity picks the other half of the 16 chunks.
-__device__ __forceinline__ int swz_w(int key) { return swz_k(key) | ((key & 1) << 3); }
 // Channel rows 16 ct .. 16 ct + 15: parity picks the bank half, ch / 2 the chunk.
 __device__ __forceinline__ int swz_v(int ch) { return (ch >> 1) & 7; }
 
@@ -291,29 +341,23 @@ __device__ __forceinline__ gbytes uniform(const void *p) {
 // Copies of one stage into LDS.  Each lane's offsets within a stage are fixed, so they
 // are computed once; a stage only moves the (wave-uniform) base pointers.
 struct PfCopier {
-  gbytes kc, kin, kvl, vt, vlvt, keep, vlpos;  // this (request, KV head)'s arrays
-  uint32_t krow8, krow16;                       // K row strides: INT8 codes, bf16 input
-  uint32_t o8[8 / kAttnWaves];                  // INT8 K: key * krow8 + 16 c
-  uint32_t ow[16 / kAttnWaves];                 // bf16 K of the input: key * krow16 + 16 c
-  uint32_t ov[16 / kAttnWaves];                 // V^T: ch * n_max * 2 + 16 c
+  gbytes kq, kin, kvl, vt, vtq, vlvt, keep, vlpos;  // this (request, KV head)'s arrays
+  uint32_t krow16;                                  // K row stride (codes and input alike)
+  uint32_t ow[16 / kAttnWaves];                     // K rows: key * krow16 + 16 c
+  uint32_t ov[16 / kAttnWaves];                     // V^T: ch * n_max * 2 + 16 c
   int w, lane;
 
   __device__ PfCopier(const PfArgs &a, int b, int h, int w_, int lane_) : w(w_), lane(lane_) {
     const int64_t bh = (int64_t)b * a.hkv + h;
-    kc = uniform(a.k_codes + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim);
+    kq = uniform(a.kq + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim);
     kin = uniform(a.k + ((int64_t)b * a.n_max * a.hkv + h) * kHeadDim);
     kvl = uniform(a.vl_k + bh * a.n_max * kHeadDim);
     vt = uniform(a.vt + bh * kHeadDim * a.n_max);
+    vtq = uniform(a.vtq + bh * kHeadDim * a.n_max);
     vlvt = uniform(a.vl_vt + bh * kHeadDim * a.n_max);
     keep = uniform(a.keep + bh * a.n_max);
     vlpos = uniform(a.vl_pos + bh * a.n_max);
-    krow8 = (uint32_t)a.hkv * kHeadDim;
-    krow16 = 2 * krow8;
-#pragma unroll
-    for (int i = 0; i < 8 / kAttnWaves; ++i) {  // 1 KB = 8 keys of 128 B
-      const int key = 8 * (w + kAttnWaves * i) + (lane >> 3);
-      o8[i] = (uint32_t)key * krow8 + 16u * (uint32_t)((lane & 7) ^ swz_k(key));
-    }
+    krow16 = 2u * (uint32_t)a.hkv * kHeadDim;
 #pragma unroll
     for (int i = 0; i < 16 / kAttnWaves; ++i) {  // 1 KB = 4 keys of 256 B
       const int key = 4 * (w + kAttnWaves * i) + (lane >> 4);
@@ -328,11 +372,11 @@ struct PfCopier {
 
   __device__ __forceinline__ void issue(const PfPlan &pl, int sigma, PfStage &S) const {
     const uint32_t kl = lds_addr(S.k), vl = lds_addr(S.v), xl = lds_addr(S.aux);
-    if (sigma < pl.n8) {  // INT8 codes, V^T, keep weights
+    if (sigma < pl.n8) {  // K codes (bf16), V-hat^T, keep weights
       const int32_t k0 = sigma * kTile;
-      const gbytes kb = kc + (uint64_t)k0 * krow8, vb = vt + 2 * k0;
+      const gbytes kb = kq + (uint64_t)k0 * krow16, vb = vtq + 2 * k0;
 #pragma unroll
-      for (int i = 0; i < 8 / kAttnWaves; ++i) dma_block(kl + 1024u * (w + kAttnWaves * i), kb, o8[i]);
+      for (int i = 0; i < 16 / kAttnWaves; ++i) dma_block(kl + 1024u * (w + kAttnWaves * i), kb, ow[i]);
 #pragma unroll
       for (int i = 0; i < 16 / kAttnWaves; ++i) dma_block(vl + 1024u * (w + kAttnWaves * i), vb, ov[i]);
       if (w == 0 && lane < 8) dma_block(xl, keep + 2 * k0, 16u * lane);
@@ -385,43 +429,29 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {  // round to 
 // cb holds the scores of keys 32 half + 8 rg + e (e = 0 .. 7) for its query: the A
 // operand row r of block u (u = 0, 1) is key 8 (r / 4) + 4 u + r % 4.
 template <int kKind>
-__device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, const v4i (&qi)[kCB][2],
-                                             const bf8 (&qf)[kCB][4], const float (&coef)[kCB], const int32_t (&tq)[kCB],
-                                             int32_t k0, int32_t window, int lane) {
-  constexpr bool kI8 = kKind == kInt8 || kKind == kInt8Edge;
+__device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, const bf8 (&qf)[kCB][4],
+                                             const float (&coef)[kCB], const int32_t (&tq)[kCB], int32_t k0,
+                                             int32_t window, int lane) {
   constexpr bool kMasked = kKind != kInt8;
   const int r = lane & 15, rg = lane >> 4;
   // Scores of both halves first: the second half's products run on the matrix cores
   // while the first half's softmax runs on the vector ALUs.
-  using Raw = typename std::conditional<kI8, v4i, v4f>::type;
-  Raw raw[2][2][kCB];  // [half][u][column block]
+  v4f raw[2][2][kCB];  // [half][u][column block]
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int key = 32 * half + 8 * (r >> 2) + 4 * u + (r & 3);
-      if constexpr (kI8) {
-        v4i ka[2];
+      bf8 ka[4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-          ka[m] = *reinterpret_cast<const v4i *>(S.k + key * 128 + 16 * ((4 * m + rg) ^ swz_k(key)));
+      for (int m = 0; m < 4; ++m)
+        ka[m] = *reinterpret_cast<const bf8 *>(S.k + key * 256 + 16 * ((4 * m + rg) ^ swz_w(key)));
 #pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-          v4i s32 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[0], qi[cb][0], v4i{0, 0, 0, 0}, 0, 0, 0);
-          raw[half][u][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[1], qi[cb][1], s32, 0, 0, 0);
-        }
-      } else {
-        bf8 ka[4];
+      for (int cb = 0; cb < kCB; ++cb) {
+        v4f sf = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          ka[m] = *reinterpret_cast<const bf8 *>(S.k + key * 256 + 16 * ((4 * m + rg) ^ swz_w(key)));
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-          v4f sf = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) sf = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], qf[cb][m], sf, 0, 0, 0);
-          raw[half][u][cb] = sf;
-        }
+        for (int m = 0; m < 4; ++m) sf = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], qf[cb][m], sf, 0, 0, 0);
+        raw[half][u][cb] = sf;
       }
     }
 #pragma unroll
@@ -432,7 +462,7 @@ __device__ __forceinline__ void attend_stage(const PfStage &S, PfState &st, cons
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[cb][4 * u + i] = (float)raw[half][u][cb][i];
+        for (int i = 0; i < 4; ++i) x[cb][4 * u + i] = raw[half][u][cb][i];
     // Side data of this lane's 8 keys: keep weights (INT8 and window stages; the A
     // operand of the row-sum tile), or positions (line stages).
     const int e0 = 32 * half + 8 * rg;
@@ -577,16 +607,19 @@ __global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
     for (int ct = 0; ct < 8; ++ct) st.acc[ct][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   constexpr float kScale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  v4i qi[kCB][2];
+  // The queries as given (bf16; 0 for rows past the request's length), for every segment.
   bf8 qf[kCB][4];
-  float cq[kCB], coef[kCB];
+  float coef[kCB];
 #pragma unroll
   for (int c = 0; c < kCB; ++c) {
+    const bool live = tq[c] < n;
     const int32_t t = min(tq[c], a.n_max - 1);
-    const int8_t *row = a.q_codes + (((int64_t)b * a.n_max + t) * a.hq + jq[c]) * kHeadDim;
+    const uint16_t *row = a.q + (((int64_t)b * a.n_max + t) * a.hq + jq[c]) * kHeadDim;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) qi[c][m] = *reinterpret_cast<const v4i *>(row + 64 * m + 16 * rg);
-    cq[c] = kScale * a.q_scales[((int64_t)b * a.hq + jq[c]) * a.tiles + min(pos0[c], a.n_max - 1) / kTile];
+    for (int m = 0; m < 4; ++m) {
+      const uint4 v = live ? *reinterpret_cast<const uint4 *>(row + 32 * m + 8 * rg) : make_uint4(0u, 0u, 0u, 0u);
+      qf[c][m] = __builtin_bit_cast(bf8, v);
+    }
   }
   const float *ks = a.k_scales + (int64_t)bh * a.tiles;
 
@@ -595,7 +628,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
   // stage s is read, only the copies of the stages after it may still be in flight.
   auto copies = [&](int sg) {
     if (sg >= total) return 0;
-    return (sg >= pl.n8 ? 16 : 8) / kAttnWaves + 16 / kAttnWaves + (w == 0 ? 1 : 0);
+    return 16 / kAttnWaves + 16 / kAttnWaves + (w == 0 ? 1 : 0);
   };
   auto wait_for = [&](int sg) {
     int later = 0;
@@ -619,12 +652,14 @@ __global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
   // reach the window.
   // Two stages a pass (stage 2i in LDS stage 0, 2i + 1 in LDS stage 1), so that every
   // LDS address is a lane base plus a constant.
+  // The logit of an INT8 key is s_K (q . code) / sqrt(128): the tile's scale joins the
+  // softmax scale (kept >= FLT_MIN so that a masked -inf never meets a zero factor).
   auto clean = [&](int sg, const PfStage &S) {
     wait_for(sg);
-    const float sk = ks[sg];
+    const float c8 = fmaxf(kScale * ks[sg], FLT_MIN);
 #pragma unroll
-    for (int c = 0; c < kCB; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
-    attend_stage<kInt8>(S, st, qi, qf, coef, tq, sg * kTile, a.window, lane);
+    for (int c = 0; c < kCB; ++c) coef[c] = c8;
+    attend_stage<kInt8>(S, st, qf, coef, tq, sg * kTile, a.window, lane);
   };
   for (; sigma + 1 < pl.n8_clean; sigma += 2) {
     clean(sigma, stage[0]);
@@ -636,31 +671,21 @@ __global__ void __launch_bounds__(kAttnThreads, 2) pf_attn_kernel(PfArgs a) {
   }
   for (; sigma < pl.n8; ++sigma) {
     wait_for(sigma);
-    const float sk = ks[sigma];
+    const float c8 = fmaxf(kScale * ks[sigma], FLT_MIN);
 #pragma unroll
-    for (int c = 0; c < kCB; ++c) coef[c] = fmaxf(cq[c] * sk, FLT_MIN);
-    attend_stage<kInt8Edge>(stage[sigma % kRing], st, qi, qf, coef, tq, sigma * kTile, a.window, lane);
+    for (int c = 0; c < kCB; ++c) coef[c] = c8;
+    attend_stage<kInt8Edge>(stage[sigma % kRing], st, qf, coef, tq, sigma * kTile, a.window, lane);
   }
-  // Full-precision segments: bf16 queries (0 for rows past the request's length).
+  // Full-precision segments.
 #pragma unroll
-  for (int c = 0; c < kCB; ++c) {
-    const bool live = tq[c] < n;
-    const int32_t t = min(tq[c], a.n_max - 1);
-    const uint16_t *row = a.q + (((int64_t)b * a.n_max + t) * a.hq + jq[c]) * kHeadDim;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint4 v = live ? *reinterpret_cast<const uint4 *>(row + 32 * m + 8 * rg) : make_uint4(0u, 0u, 0u, 0u);
-      qf[c][m] = __builtin_bit_cast(bf8, v);
-    }
-    coef[c] = kScale;
-  }
+  for (int c = 0; c < kCB; ++c) coef[c] = kScale;
   for (; sigma < pl.n8 + pl.nvl; ++sigma) {
     wait_for(sigma);
-    attend_stage<kLines>(stage[sigma % kRing], st, qi, qf, coef, tq, 0, a.window, lane);
+    attend_stage<kLines>(stage[sigma % kRing], st, qf, coef, tq, 0, a.window, lane);
   }
   for (; sigma < total; ++sigma) {
     wait_for(sigma);
-    attend_stage<kWindow>(stage[sigma % kRing], st, qi, qf, coef, tq,
+    attend_stage<kWindow>(stage[sigma % kRing], st, qf, coef, tq,
                           (pl.w_first + sigma - pl.n8 - pl.nvl) * kTile, a.window, lane);
   }
 #pragma unroll
@@ -683,10 +708,10 @@ kvq_status launched(const char *what) {
   return KVQ_OK;
 }
 
-// Workspace regions (each 256-byte aligned), in this order: vt (fp16), keep (fp16),
-// vl_pos, vl_cnt (int32), vl_k (bf16), vl_vt (fp16).
+// Workspace regions (each 256-byte aligned), in this order: vt, vtq (fp16), keep (fp16),
+// vl_pos, vl_cnt (int32), vl_k (bf16), vl_vt (fp16), kq (bf16).
 struct PfLayout {
-  size_t vt, keep, vl_pos, vl_cnt, vl_k, vl_vt, total;
+  size_t vt, vtq, keep, vl_pos, vl_cnt, vl_k, vl_vt, kq, total;
 };
 
 PfLayout pf_layout(int64_t batch, int64_t n_max, int64_t hkv) {
@@ -695,6 +720,8 @@ PfLayout pf_layout(int64_t batch, int64_t n_max, int64_t hkv) {
   PfLayout L;
   size_t o = 0;
   L.vt = o;
+  o = up(o + bh * kHeadDim * n * 2);
+  L.vtq = o;
   o = up(o + bh * kHeadDim * n * 2);
   L.keep = o;
   o = up(o + bh * n * 2);
@@ -706,6 +733,8 @@ PfLayout pf_layout(int64_t batch, int64_t n_max, int64_t hkv) {
   o = up(o + bh * n * kHeadDim * 2);
   L.vl_vt = o;
   o = up(o + bh * kHeadDim * n * 2);
+  L.kq = o;
+  o = up(o + bh * n * kHeadDim * 2);
   L.total = o;
   return L;
 }
@@ -725,7 +754,7 @@ namespace {
 // Validation shared by both entry points, then the argument block.
 kvq_status pf_setup(PfArgs &a, const void *q, const void *k, const void *v, int32_t dtype, int32_t batch,
                     int32_t n_max, int32_t hq, int32_t hkv, const int32_t *n_tokens, const uint8_t *token_class,
-                    int32_t window, int8_t *q_codes, float *q_scales, int8_t *k_codes, float *k_scales,
+                    int32_t window, int8_t *k_codes, float *k_scales, int8_t *v_codes, float *v_scales,
                     void *workspace, size_t workspace_bytes, float *out, int32_t *dev_err, bool &empty) {
   empty = false;
   if (dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "prefill attention takes bf16 q, k, v");
@@ -739,18 +768,17 @@ kvq_status pf_setup(PfArgs &a, const void *q, const void *k, const void *v, int3
     empty = true;
     return KVQ_OK;
   }
-  if (!q || !k || !n_tokens || !q_codes || !q_scales || !k_codes || !k_scales || !workspace)
-    return fail(KVQ_ERR_INVALID_ARG, "NULL buffer");
-  // 16-byte LDS-bound copies read q, k, v, the codes and the workspace regions.
+  if (!k || !n_tokens || !k_scales || !workspace) return fail(KVQ_ERR_INVALID_ARG, "NULL buffer");
+  // 16-byte LDS-bound copies and vector loads read q, k, v, the codes and the workspace
+  // regions.
   auto misaligned = [](const void *p, uintptr_t to) { return p && (reinterpret_cast<uintptr_t>(p) & (to - 1)); };
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(q_codes, 16) ||
-      misaligned(k_codes, 16) || misaligned(workspace, 256))
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(k_codes, 16) ||
+      misaligned(v_codes, 16) || misaligned(workspace, 256))
     return fail(KVQ_ERR_INVALID_ARG, "q, k, v and the codes must be 16-byte aligned, the workspace 256-byte aligned");
   // LDS-bound loads address one (request, head)'s K rows, V^T rows and lists with 32-bit
   // byte offsets.
   if ((int64_t)n_max * hkv * kHeadDim * 2 > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "n_max * hkv too large");
-  if ((int64_t)batch * hq > 65535 || (int64_t)hq + hkv > 65535 || (int64_t)batch * hkv > 65535)
-    return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  if ((int64_t)batch * hq > 65535 || (int64_t)batch * hkv > 65535) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
   const PfLayout L = pf_layout(batch, n_max, hkv);
   if (workspace_bytes < L.total)
     return fail(KVQ_ERR_CAPACITY, "prefill workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
@@ -768,11 +796,13 @@ kvq_status pf_setup(PfArgs &a, const void *q, const void *k, const void *v, int3
   a.hsplit = g > kColBlocks ? g / kColBlocks : 1;
   a.window = window;
   a.tiles = n_max / kTile;
-  a.q_codes = q_codes;
   a.k_codes = k_codes;
-  a.q_scales = q_scales;
+  a.v_codes = v_codes;
   a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.kq = reinterpret_cast<uint16_t *>(ws + L.kq);
   a.vt = reinterpret_cast<uint16_t *>(ws + L.vt);
+  a.vtq = reinterpret_cast<uint16_t *>(ws + L.vtq);
   a.keep = reinterpret_cast<uint16_t *>(ws + L.keep);
   a.vl_pos = reinterpret_cast<int32_t *>(ws + L.vl_pos);
   a.vl_cnt = reinterpret_cast<int32_t *>(ws + L.vl_cnt);
@@ -785,22 +815,22 @@ kvq_status pf_setup(PfArgs &a, const void *q, const void *k, const void *v, int3
 
 }  // namespace
 
-extern "C" kvq_status kvq_prefill_prepare(const void *q, const void *k, const void *v, int32_t dtype, int32_t batch,
-                                          int32_t n_max, int32_t hq, int32_t hkv, const int32_t *n_tokens,
-                                          const uint8_t *token_class, int8_t *q_codes, float *q_scales,
-                                          int8_t *k_codes, float *k_scales, void *workspace, size_t workspace_bytes,
-                                          int32_t *dev_err, void *stream) {
+extern "C" kvq_status kvq_prefill_prepare(const void *k, const void *v, int32_t dtype, int32_t batch, int32_t n_max,
+                                          int32_t hkv, const int32_t *n_tokens, const uint8_t *token_class,
+                                          int8_t *k_codes, float *k_scales, int8_t *v_codes, float *v_scales,
+                                          void *workspace, size_t workspace_bytes, int32_t *dev_err, void *stream) {
   PfArgs a;
   bool empty;
-  kvq_status st = pf_setup(a, q, k, v, dtype, batch, n_max, hq, hkv, n_tokens, token_class, 0, q_codes, q_scales,
-                           k_codes, k_scales, workspace, workspace_bytes, nullptr, dev_err, empty);
+  // (hq = hkv: the query heads play no part in the preparation)
+  kvq_status st = pf_setup(a, nullptr, k, v, dtype, batch, n_max, hkv, hkv, n_tokens, token_class, 0, k_codes,
+                           k_scales, v_codes, v_scales, workspace, workspace_bytes, nullptr, dev_err, empty);
   if (st != KVQ_OK || empty) return st;
-  if (!v) return fail(KVQ_ERR_INVALID_ARG, "NULL v");
+  if (!v || !k_codes || !v_codes || !v_scales) return fail(KVQ_ERR_INVALID_ARG, "NULL buffer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(pf_quant_kernel, dim3(a.tiles, batch, hq + hkv), dim3(256), 0, s, a);
-  if ((st = launched("pf_quant_kernel")) != KVQ_OK) return st;
-  hipLaunchKernelGGL(pf_vt_kernel, dim3(a.tiles, batch, hkv), dim3(256), 0, s, a);
-  if ((st = launched("pf_vt_kernel")) != KVQ_OK) return st;
+  hipLaunchKernelGGL(pf_quant_k_kernel, dim3(a.tiles, batch, hkv), dim3(256), 0, s, a);
+  if ((st = launched("pf_quant_k_kernel")) != KVQ_OK) return st;
+  hipLaunchKernelGGL(pf_quant_v_kernel, dim3(a.tiles, batch, hkv), dim3(256), 0, s, a);
+  if ((st = launched("pf_quant_v_kernel")) != KVQ_OK) return st;
   if (token_class) {
     hipLaunchKernelGGL(pf_vl_scan_kernel, dim3(batch * hkv), dim3(kScanThreads), 0, s, a);
     if ((st = launched("pf_vl_scan_kernel")) != KVQ_OK) return st;
@@ -812,17 +842,15 @@ extern "C" kvq_status kvq_prefill_prepare(const void *q, const void *k, const vo
 
 extern "C" kvq_status kvq_prefill_attn(const void *q, const void *k, int32_t dtype, int32_t batch, int32_t n_max,
                                        int32_t hq, int32_t hkv, const int32_t *n_tokens, const uint8_t *token_class,
-                                       int32_t window, const int8_t *q_codes, const float *q_scales,
-                                       const int8_t *k_codes, const float *k_scales, const void *workspace,
+                                       int32_t window, const float *k_scales, const void *workspace,
                                        size_t workspace_bytes, float *out, int32_t *dev_err, void *stream) {
   PfArgs a;
   bool empty;
-  kvq_status st = pf_setup(a, q, k, nullptr, dtype, batch, n_max, hq, hkv, n_tokens, token_class, window,
-                           const_cast<int8_t *>(q_codes), const_cast<float *>(q_scales), const_cast<int8_t *>(k_codes),
-                           const_cast<float *>(k_scales), const_cast<void *>(workspace), workspace_bytes, out, dev_err,
-                           empty);
+  kvq_status st = pf_setup(a, q, k, nullptr, dtype, batch, n_max, hq, hkv, n_tokens, token_class, window, nullptr,
+                           const_cast<float *>(k_scales), nullptr, nullptr, const_cast<void *>(workspace),
+                           workspace_bytes, out, dev_err, empty);
   if (st != KVQ_OK || empty) return st;
-  if (!out) return fail(KVQ_ERR_INVALID_ARG, "NULL out");
+  if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "NULL q or out");
   const int64_t qp = 16 * (kColBlocks / (a.g / a.hsplit));
   const int64_t n_blk = (n_max + qp - 1) / qp, groups = n_blk * a.hsplit * batch * hkv;
   if (groups > INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");

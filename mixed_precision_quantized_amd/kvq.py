@@ -66,9 +66,9 @@ _SIGS = {
                              _P, _P], ctypes.c_int),
     "kvq_reorder_pages": ([_P, _P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
     "kvq_compact_slots": ([_P, _P, _i32, _i32, _P, _P, _P, _P, _P], ctypes.c_int),
-    "kvq_prefill_prepare": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P,
+    "kvq_prefill_prepare": ([_P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P,
                              ctypes.c_size_t, _P, _P], ctypes.c_int),
-    "kvq_prefill_attn": ([_P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P, _P, _P, _P,
+    "kvq_prefill_attn": ([_P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P,
                           ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
     "kvq_prefill_workspace_bytes": ([_i32, _i32, _i32], ctypes.c_size_t),
     "kvq_select_vertical_lines": ([_P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32,
@@ -272,33 +272,32 @@ def select_vertical_lines(k: torch.Tensor, q_tail: torch.Tensor, n_tokens: torch
 
 
 def prefill_workspace(batch: int, n_max: int, hq: int, hkv: int, device="cuda"):
-    """Outputs and scratch of prefill_attn: (q_codes, q_scales, k_codes, k_scales,
+    """Outputs and scratch of prefill_attn: (k_codes, k_scales, v_codes, v_scales,
     scratch, out); scratch is kvq_prefill_workspace_bytes bytes."""
     tiles = n_max // 64
     nbytes = _lib.kvq_prefill_workspace_bytes(batch, n_max, hkv)
     if nbytes == 0:
         raise KvqError(-1, f"kvq_prefill_workspace_bytes({batch}, {n_max}, {hkv})")
-    return (torch.empty((batch, n_max, hq, HEAD_DIM), dtype=torch.int8, device=device),
-            torch.empty((batch, hq, tiles), dtype=torch.float32, device=device),
+    return (torch.empty((batch, n_max, hkv, HEAD_DIM), dtype=torch.int8, device=device),
+            torch.empty((batch, hkv, tiles), dtype=torch.float32, device=device),
             torch.empty((batch, n_max, hkv, HEAD_DIM), dtype=torch.int8, device=device),
             torch.empty((batch, hkv, tiles), dtype=torch.float32, device=device),
             torch.empty(nbytes, dtype=torch.uint8, device=device),
             torch.empty((batch, n_max, hq, HEAD_DIM), dtype=torch.float32, device=device))
 
 
-def prefill_prepare(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens: torch.Tensor,
+def prefill_prepare(k: torch.Tensor, v: torch.Tensor, n_tokens: torch.Tensor,
                     token_class: Optional[torch.Tensor], ws, dev_err=None, stream=None):
-    """The INT8 codes and scales of q, k and the attention's scratch, into ws
+    """The INT8 codes and scales of k, v and the attention's scratch, into ws
     (prefill_workspace's tuple)."""
-    assert q.dtype == k.dtype == v.dtype == torch.bfloat16
-    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
-    batch, n_max, hq = q.shape[:3]
-    hkv = k.shape[2]
-    qc, qs, kc, ks, scratch, _ = ws
+    assert k.dtype == v.dtype == torch.bfloat16
+    assert k.is_contiguous() and v.is_contiguous()
+    batch, n_max, hkv = k.shape[:3]
+    kc, ks, vc, vs, scratch, _ = ws
     if token_class is not None:
         assert token_class.dtype == torch.uint8 and token_class.is_contiguous()
-    _check(_lib.kvq_prefill_prepare(_dptr(q), _dptr(k), _dptr(v), BF16, batch, n_max, hq, hkv, _dptr(n_tokens),
-                                    _dptr(token_class), _dptr(qc), _dptr(qs), _dptr(kc), _dptr(ks),
+    _check(_lib.kvq_prefill_prepare(_dptr(k), _dptr(v), BF16, batch, n_max, hkv, _dptr(n_tokens),
+                                    _dptr(token_class), _dptr(kc), _dptr(ks), _dptr(vc), _dptr(vs),
                                     _dptr(scratch), scratch.numel(), _dptr(dev_err), _stream(stream)),
            "kvq_prefill_prepare")
 
@@ -306,12 +305,13 @@ def prefill_prepare(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens:
 def prefill_attend(q: torch.Tensor, k: torch.Tensor, n_tokens: torch.Tensor, token_class: Optional[torch.Tensor],
                    window: int, ws, dev_err=None, stream=None):
     """The attention over what prefill_prepare left in ws; fills ws[5]."""
+    assert q.dtype == torch.bfloat16 and q.is_contiguous()
     batch, n_max, hq = q.shape[:3]
     hkv = k.shape[2]
-    qc, qs, kc, ks, scratch, out = ws
+    _, ks, _, _, scratch, out = ws
     _check(_lib.kvq_prefill_attn(_dptr(q), _dptr(k), BF16, batch, n_max, hq, hkv, _dptr(n_tokens),
-                                 _dptr(token_class), window, _dptr(qc), _dptr(qs), _dptr(kc), _dptr(ks),
-                                 _dptr(scratch), scratch.numel(), _dptr(out), _dptr(dev_err), _stream(stream)),
+                                 _dptr(token_class), window, _dptr(ks), _dptr(scratch), scratch.numel(),
+                                 _dptr(out), _dptr(dev_err), _stream(stream)),
            "kvq_prefill_attn")
 
 
@@ -324,7 +324,7 @@ def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens: to
     batch, n_max, hq = q.shape[:3]
     if ws is None:
         ws = prefill_workspace(batch, n_max, hq, k.shape[2], q.device)
-    prefill_prepare(q, k, v, n_tokens, token_class, ws, dev_err, stream)
+    prefill_prepare(k, v, n_tokens, token_class, ws, dev_err, stream)
     prefill_attend(q, k, n_tokens, token_class, window, ws, dev_err, stream)
     return ws
 

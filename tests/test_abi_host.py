@@ -181,17 +181,17 @@ def test_balanced_split_counts_minimal_cap(kvq):
 
 
 def test_prefill_workspace_and_validation(kvq):
-    """The prefill scratch size follows its region list (V^T fp16, fp16 keep mask, line
-    positions, per-tile line counts, gathered K and V^T, each 256-byte aligned); the
-    entry point rejects g outside {1, 2, 4, 8, 16}, n_max off 64 and a short scratch
-    before touching any pointer."""
+    """The prefill scratch size follows its region list (V^T and V-hat^T fp16, fp16 keep
+    mask, line positions, per-tile line counts, gathered K and V^T, K codes as bf16,
+    each 256-byte aligned); the entry points reject g outside {1, 2, 4, 8, 16}, n_max off
+    64 and a short scratch before touching any pointer."""
     lib = kvq.raw_library()
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for batch, n_max, hkv in ((1, 64, 1), (2, 1024, 8), (3, 192, 2)):
         bh = batch * hkv
         want = 0
-        for size in (bh * 128 * n_max * 2, bh * n_max * 2, bh * n_max * 4, bh * (n_max // 64) * 4,
-                     bh * n_max * 128 * 2, bh * 128 * n_max * 2):
+        for size in (bh * 128 * n_max * 2, bh * 128 * n_max * 2, bh * n_max * 2, bh * n_max * 4,
+                     bh * (n_max // 64) * 4, bh * n_max * 128 * 2, bh * 128 * n_max * 2, bh * n_max * 128 * 2):
             want = up(want + size)
         assert lib.kvq_prefill_workspace_bytes(batch, n_max, hkv) == want
     assert lib.kvq_prefill_workspace_bytes(1, 100, 1) == 0
@@ -200,24 +200,24 @@ def test_prefill_workspace_and_validation(kvq):
     need = lib.kvq_prefill_workspace_bytes(1, 128, 2)
 
     def attn(hq=4, hkv=2, n_max=128, nbytes=need, dtype=1, out=fake):
-        return lib.kvq_prefill_attn(fake, fake, dtype, 1, n_max, hq, hkv, fake, None, 16, fake, fake, fake,
-                                    fake, fake, nbytes, out, None, None)
+        return lib.kvq_prefill_attn(fake, fake, dtype, 1, n_max, hq, hkv, fake, None, 16, fake, fake, nbytes, out,
+                                    None, None)
 
-    def prepare(hq=4, hkv=2, n_max=128, nbytes=need, dtype=1, v=fake):
-        return lib.kvq_prefill_prepare(fake, fake, v, dtype, 1, n_max, hq, hkv, fake, None, fake, fake, fake,
-                                       fake, fake, nbytes, None, None)
+    def prepare(hkv=2, n_max=128, nbytes=need, dtype=1, v=fake):
+        return lib.kvq_prefill_prepare(fake, v, dtype, 1, n_max, hkv, fake, None, fake, fake, fake, fake, fake,
+                                       nbytes, None, None)
+    assert attn(hq=6, hkv=2) == -2              # g = 3
+    assert attn(hq=64, hkv=2) == -2             # g = 32
+    assert attn(hq=6, hkv=4) == -1              # hq % hkv != 0
     for call in (attn, prepare):
-        assert call(hq=6, hkv=2) == -2          # g = 3
-        assert call(hq=64, hkv=2) == -2         # g = 32
-        assert call(hq=6, hkv=4) == -1          # hq % hkv != 0
         assert call(n_max=100) == -1            # not a multiple of 64
         assert call(dtype=0) == -2              # fp32 inputs
         assert call(nbytes=need - 1) == -3      # scratch too small
         assert b"workspace" in lib.kvq_last_error()
     assert attn(out=None) == -1 and prepare(v=None) == -1
     odd = ctypes.c_void_p(0x1008)                     # 8-byte aligned only
-    assert lib.kvq_prefill_attn(odd, fake, 1, 1, 128, 4, 2, fake, None, 16, fake, fake, fake, fake, fake, need,
-                                fake, None, None) == -1
-    assert lib.kvq_prefill_prepare(fake, fake, fake, 1, 1, 128, 4, 2, fake, None, fake, fake, fake, fake,
+    assert lib.kvq_prefill_attn(odd, fake, 1, 1, 128, 4, 2, fake, None, 16, fake, fake, need, fake, None,
+                                None) == -1
+    assert lib.kvq_prefill_prepare(fake, fake, 1, 1, 128, 2, fake, None, fake, fake, fake, fake,
                                    ctypes.c_void_p(0x1010), need, None, None) == -1   # workspace off 256
     assert b"aligned" in lib.kvq_last_error()

@@ -1,7 +1,8 @@
-"""GPU prefill attention with an INT8 prefix (HyQuant Algorithm 2) through the C ABI
-against the oracle: INT8 codes and tile scales bit-exact (both sides divide in IEEE
-fp32), outputs within 2e-3 by the per-row metric (rows = (request, position, query
-head) below the request's length)."""
+"""GPU prefill attention with an INT8 prefix (HyQuant, the core method's fused operator
+and Algorithm 2: the query as given, the prefix's K and V through per-tile INT8) through
+the C ABI against the oracle: K and V codes and tile scales bit-exact (both sides divide
+in IEEE fp32), outputs within 2e-3 by the per-row metric (rows = (request, position,
+query head) below the request's length)."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +17,13 @@ def _say(*a):
     print("[gpu-prefill]", *a, flush=True)
 
 
+def _codes_equal(ws, ref):
+    """ws: the binding's (k_codes, k_scales, v_codes, v_scales, ...); ref: the oracle's
+    (k_codes, k_scales, v_codes, v_scales)."""
+    for got, want, what in zip(ws[:4], ref, ("K codes", "K scales", "V codes", "V scales")):
+        assert np.array_equal(got.cpu().numpy(), want), what
+
+
 def _case(name, batch, n_max, hq, hkv, lengths, window, vl_frac=0.05, with_cls=True, seed=7):
     from mixed_precision_quantized_amd import kvq
     from oracle import oracle
@@ -25,15 +33,14 @@ def _case(name, batch, n_max, hq, hkv, lengths, window, vl_frac=0.05, with_cls=T
     dev = "cuda"
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     c_dev = torch.as_tensor(cls, device=dev).contiguous() if with_cls else None
-    qc, qs, kc, ks, vt, out = kvq.prefill_attn(q.to(dev), k.to(dev), v.to(dev), torch.as_tensor(lens, device=dev),
-                                               c_dev, window=window, dev_err=err)
+    ws = kvq.prefill_attn(q.to(dev), k.to(dev), v.to(dev), torch.as_tensor(lens, device=dev), c_dev,
+                          window=window, dev_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    ref, rqc, rqs, rkc, rks = oracle.prefill_attend(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens,
-                                                    cls if with_cls else None, window)
-    assert np.array_equal(qs.cpu().numpy(), rqs) and np.array_equal(ks.cpu().numpy(), rks)
-    assert np.array_equal(qc.cpu().numpy(), rqc) and np.array_equal(kc.cpu().numpy(), rkc)
-    got = out.cpu().numpy()
+    ref, *rcodes = oracle.prefill_attend(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens,
+                                         cls if with_cls else None, window)
+    _codes_equal(ws, rcodes)
+    got = ws[5].cpu().numpy()
     rows_ref, rows_got = [], []
     for b in range(batch):
         rows_ref.append(ref[b, : lens[b]].reshape(-1, 128))
@@ -91,18 +98,15 @@ def test_full_size_sampled():
     _say("full size 1 x 16384, Hq 32 / Hkv 8")
     q, k, v, lens, cls = synth.prefill_qkv(seed=8, batch=1, n_max=n, hq=hq, hkv=hkv, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    qc, qs, kc, ks, _, out = kvq.prefill_attn(q, k, v, torch.as_tensor(lens, device="cuda"),
-                                             torch.as_tensor(cls, device="cuda").contiguous(), window=128,
-                                             dev_err=err)
+    ws = kvq.prefill_attn(q, k, v, torch.as_tensor(lens, device="cuda"),
+                          torch.as_tensor(cls, device="cuda").contiguous(), window=128, dev_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     pos = [0, 1, 63, 64, 127, 128, 129, 4095, 8191, 12000, 16320, 16383]
-    ref, rqc, rqs, rkc, rks = oracle.prefill_attend_rows(q.float().cpu().numpy(), k.float().cpu().numpy(),
-                                                         v.float().cpu().numpy(), lens, cls, 128,
-                                                         [(0, t) for t in pos])
-    assert np.array_equal(qs.cpu().numpy(), rqs) and np.array_equal(ks.cpu().numpy(), rks)
-    assert np.array_equal(qc.cpu().numpy(), rqc) and np.array_equal(kc.cpu().numpy(), rkc)
-    got = out[0, pos].cpu().numpy()
+    ref, *rcodes = oracle.prefill_attend_rows(q.float().cpu().numpy(), k.float().cpu().numpy(),
+                                              v.float().cpu().numpy(), lens, cls, 128, [(0, t) for t in pos])
+    _codes_equal(ws, rcodes)
+    got = ws[5][0, pos].cpu().numpy()
     e = row_metric(ref, got)
     _say(f"  full size: row error {e:.2e} over {len(pos)} positions x {hq} heads")
     assert e <= TOL
@@ -121,15 +125,13 @@ def test_empty_and_single_token_requests_and_window_class():
     lens = np.array([0, 1, 200], np.int32)
     cls = np.random.default_rng(13).integers(0, 3, (batch, hkv, n_max)).astype(np.uint8)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    qc, qs, kc, ks, _, out = kvq.prefill_attn(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(lens, device="cuda"),
-                                             torch.as_tensor(cls, device="cuda"), window=32, dev_err=err)
+    ws = kvq.prefill_attn(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(lens, device="cuda"),
+                          torch.as_tensor(cls, device="cuda"), window=32, dev_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    ref, rqc, rqs, rkc, rks = oracle.prefill_attend(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens,
-                                                    cls, 32)
-    assert np.array_equal(qc.cpu().numpy(), rqc) and np.array_equal(kc.cpu().numpy(), rkc)
-    assert np.array_equal(qs.cpu().numpy(), rqs) and np.array_equal(ks.cpu().numpy(), rks)
-    got = out.cpu().numpy()
+    ref, *rcodes = oracle.prefill_attend(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens, cls, 32)
+    _codes_equal(ws, rcodes)
+    got = ws[5].cpu().numpy()
     assert not got[0].any() and not got[1, 1:].any() and not got[2, 200:].any()
     e = row_metric(np.concatenate([ref[1, :1].reshape(-1, 128), ref[2, :200].reshape(-1, 128)]),
                    np.concatenate([got[1, :1].reshape(-1, 128), got[2, :200].reshape(-1, 128)]))
