@@ -2,7 +2,15 @@
 
 The write path (quantize / pack / reorder) is compiled with -ffp-contract=off and
 fp32 denormals kept, so its fp32 arithmetic rounds exactly as IEEE specifies.
-Every HIP translation unit is compiled without packed fp32 instructions."""
+Every HIP translation unit is compiled without packed fp32 instructions.
+
+`python build.py --sanitize` builds libkvq_san.so instead: the same sources with
+AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (device code is
+built as usual), for the CPU tests of the host entry points:
+
+    KVQ_LIBRARY=mixed_precision_quantized_amd/libkvq_san.so \
+    LD_PRELOAD=$(hipcc -print-file-name=libclang_rt.asan-x86_64.so) ASAN_OPTIONS=detect_leaks=0 \
+    python -m pytest -q tests/test_abi_host.py tests/test_tags_and_widths.py tests/test_head_groups.py"""
 import os
 import subprocess
 import sys
@@ -12,6 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
+LIB_SAN = os.path.join(HERE, "libkvq_san.so")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
@@ -31,12 +40,18 @@ SOURCES = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# Host-side sanitizers (each -fsanitize= right after -Xarch_host: never on device code).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
+    extra = SANITIZE if sanitize else []
     for src, flags in SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        cmd = ["hipcc", *COMMON, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(BUILD, src + (".san.o" if sanitize else ".o"))
+        cmd = ["hipcc", *COMMON, *flags, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,15 +62,18 @@ def build(verbose: bool = False) -> str:
         if err.strip() and verbose:
             print(err, flush=True)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    out = LIB_SAN if sanitize else LIB
+    tmp = out + ".tmp"
     cmd = ["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
+    if sanitize:
+        cmd += ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
     sys.exit(0)

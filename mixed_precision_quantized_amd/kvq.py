@@ -17,7 +17,8 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# KVQ_LIBRARY may name another build of the same sources (the host-sanitizer build).
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(HERE, "libkvq.so")
 
 INT2, INT4, FP16 = 0, 1, 2
 F32, BF16, F16 = 0, 1, 2

@@ -12,7 +12,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# ORACLE_LIBRARY may name another build of the same source (the sanitizer build).
+LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(HERE, "liboracle.so")
 
 INT2, INT4, FP16 = 0, 1, 2
 F32, BF16, F16 = 0, 1, 2
