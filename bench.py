@@ -158,6 +158,9 @@ def main():
                     help="slot maps: decode the tables as they are instead of dropping dead entries ahead of time")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured HIP graph")
+    ap.add_argument("--decode", choices=("static", "shared"), default="static",
+                    help="page-table decode: fixed splits (kvq_decode_attn), or the resident workers of each "
+                         "(request, head) range sharing its windows (kvq_decode_attn_shared)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -216,12 +219,22 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     cost = None if args.class_cost is None else [float(x) for x in args.class_cost.split(",")]
-    splits, offsets, per_cu, n_cu = resident_plan(gpu, kvq, synth, args.splits_per_head, cost, args.ragged_plan)
+    g = w0.g
+    kind = kvq.TABLE_SLOTS if w0.kind == synth.SLOTS else kvq.TABLE_PAGES
+    shared = args.decode == "shared"
+    if shared and (kind != kvq.TABLE_PAGES or g > 8):
+        sys.exit("--decode shared: page tables and g <= 8 only")
+    if shared:
+        per_cu, n_cu = kvq.decode_occupancy(g, kind)
+        wph = args.splits_per_head or max(1, per_cu * n_cu // (w0.batch * w0.hkv))
+        splits, groups, n_groups, offsets = gpu.plan_workers(wph, cost)
+        grp = torch.as_tensor(groups, device=dev).contiguous()
+        work = kvq.decode_work(n_groups, dev)
+    else:
+        splits, offsets, per_cu, n_cu = resident_plan(gpu, kvq, synth, args.splits_per_head, cost, args.ragged_plan)
     n_splits = splits.shape[0]
     sp = torch.as_tensor(splits, device=dev).contiguous()
     off = torch.as_tensor(offsets, device=dev)
-    g = w0.g
-    kind = kvq.TABLE_SLOTS if w0.kind == synth.SLOTS else kvq.TABLE_PAGES
     part_o = torch.empty((n_splits, g, 128), dtype=torch.float32, device=dev)
     part_lse = torch.empty((n_splits, g), dtype=torch.float32, device=dev)
     outs = [torch.empty((w0.batch, w0.hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
@@ -236,8 +249,12 @@ def main():
     stream = torch.cuda.current_stream() if args.eager else torch.cuda.Stream()
 
     def bound(st):
-        d = [kvq.bind_decode_attn(caches[L], qs[L], w0.hkv, gpu.tables, kind, sp, part_o, part_lse, stream=st)
-             for L in range(layers)]
+        if shared:
+            d = [kvq.bind_decode_attn_shared(caches[L], qs[L], w0.hkv, gpu.tables, kind, sp, grp, n_groups, work,
+                                             part_o, part_lse, dev_err=gpu.err, stream=st) for L in range(layers)]
+        else:
+            d = [kvq.bind_decode_attn(caches[L], qs[L], w0.hkv, gpu.tables, kind, sp, part_o, part_lse, stream=st)
+                 for L in range(layers)]
         m = [kvq.bind_lse_merge(part_o, part_lse, n_splits, off, w0.batch, w0.hq, w0.hkv, outs[L], stream=st)
              for L in range(layers)]
         return d, m
@@ -285,13 +302,21 @@ def main():
                 o.zero_()
             g_step.replay()
             torch.cuda.synchronize()
-            assert torch.equal(torch.stack([o.float() for o in outs]), ref), "graph replay differs from eager"
+            got = torch.stack([o.float() for o in outs])
+            if shared:  # the windows a worker takes vary: the same sums in another order
+                dif = (got - ref).abs().amax(-1) / ref.abs().amax(-1).clamp_min(1e-30)
+                assert float(dif.max()) <= 2.0 ** -7, "graph replay differs from eager"
+            else:
+                assert torch.equal(got, ref), "graph replay differs from eager"
+            if shared:
+                assert not work.any().item(), "work counters not reset"
             with torch.cuda.stream(stream):
                 step()
             torch.cuda.synchronize()
         assert int(gpu.err.item()) == 0
         run_step, run_decodes = g_step.replay, g_dec.replay
-        log("step captured as a HIP graph of the decode + merge launches; 3 replays equal to eager")
+        log("step captured as a HIP graph of the decode + merge launches; 3 replays equal to eager"
+            + (" (to bf16 rounding: shared windows sum in another order)" if shared else ""))
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -347,6 +372,7 @@ def main():
             "workload": description + (" (FP8 anchors)" if args.anchor_fp8 else "")
             + (" (pages in id order)" if args.ordered_pages else "") + f", {layers} layers",
             "batch": w0.batch, "hq": w0.hq, "hkv": w0.hkv, "layers": layers, "splits_per_layer": n_splits,
+            "decode": "shared windows (kvq_decode_attn_shared)" if shared else "fixed splits (kvq_decode_attn)",
             "effective_bytes_per_layer": eff_layer,
         },
         "roofline": {

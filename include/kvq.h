@@ -358,6 +358,42 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype,
                            float *part_o, float *part_lse, int32_t *dev_err, void *stream);
 
 /*
+ * Split-K decode attention with shared windows: the same computation as
+ * kvq_decode_attn, but the work items are workers that share the 32-token
+ * windows of their group (the XCDs of one MI355X stream at rates that differ by a
+ * few percent from launch to launch, so a fixed cut leaves the faster ones idle
+ * at the end; shared windows let them take more).  Worker s = workers[s] [dev]
+ * belongs to group worker_group[s] [dev] (0 <= group < n_groups); the workers of
+ * a group carry the same entry (table, head, cls, tok_begin, tok_end): the
+ * group's token range, whose windows start at tok_begin rounded down to a page,
+ * 32 tokens apart.  Each worker takes windows from the group's counter in blocks
+ * (2 windows for INT4, 3 for INT2) and writes the softmax partial of the windows
+ * it took: part_o / part_lse row s, as kvq_decode_attn writes a split's (O = 0,
+ * lse = -inf if it took none), so kvq_lse_merge combines them unchanged (the
+ * workers of a (request, KV head) adjacent).  Page tables only; INT2 and INT4
+ * groups are shared; an FP16 group must have one worker (its kernel reads the
+ * range whole).  g <= 8.
+ *   work [dev]: kvq_decode_work_bytes(n_groups) bytes, all 0 before the first
+ *     call (the caller zeroes it once); every call leaves it 0 again when it
+ *     completes.  Calls that may overlap must not share it.
+ * kvq_plan_workers writes such a plan.  Workers start in a spread order (not in
+ * index order) and n_workers must stay below 2^31 - 1.
+ * Errors: INVALID_ARG, UNSUPPORTED (slot maps, g > 8), HIP; device-side
+ * KVQ_DEVERR_* (a worker whose group is out of range: KVQ_DEVERR_SPLIT).
+ */
+kvq_status kvq_decode_attn_shared(const kvq_cache *c, const void *q, int32_t q_dtype,
+                                  int32_t batch, int32_t hq, int32_t hkv,
+                                  const int32_t *tables, int32_t n_tables, int32_t max_entries,
+                                  int32_t table_kind, const kvq_split *workers,
+                                  const int32_t *worker_group, int32_t n_workers, int32_t n_groups,
+                                  int32_t *work, float *part_o, float *part_lse, int32_t *dev_err,
+                                  void *stream);
+
+/* Bytes of the work counters of kvq_decode_attn_shared for n_groups groups (0 if
+ * n_groups < 1).  Host only. */
+size_t kvq_decode_work_bytes(int32_t n_groups);
+
+/*
  * Log-sum-exp merge of split partials (TriAxialKV key design 4: global online
  * log-sum-exp reduction; HyQuant Algorithm 3: ReduceSoftmax).  The partials of
  * (request b, KV head kvh) are rows split_offsets[b*hkv + kvh] ..
@@ -405,6 +441,24 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
                            const int32_t *tokens_per_split, int64_t target_bytes,
                            kvq_split *out, int32_t max_out, int32_t *n_out,
                            int32_t *split_offsets);
+
+/*
+ * Shared-work plan [host] for kvq_decode_attn_shared.  ranges as for
+ * kvq_plan_splits; every non-empty range is a group.  workers_per_head [host]
+ * int32 [n_tables*heads_per_page] is shared among a (table, head)'s non-empty
+ * ranges in proportion to tokens x class_cost[cls] (NULL = the kvq_plan_splits
+ * default) with at least one worker per range, largest remainders first, at
+ * most one worker per window of the range, and one worker for an FP16 range.
+ * Writes out[0 .. *n_out) [host] (each worker carries its group's range, sorted
+ * by (table, head)), out_group [host] int32 [*n_out], *n_groups, and
+ * split_offsets [host] int32 [batch*hkv + 1] for kvq_lse_merge.
+ * Errors: INVALID_ARG, CAPACITY (max_out).
+ */
+kvq_status kvq_plan_workers(const kvq_split *ranges, int32_t n_ranges, int32_t batch,
+                            int32_t hkv, int32_t heads_per_page, const int32_t *workers_per_head,
+                            const float *class_cost, kvq_split *out, int32_t *out_group,
+                            int32_t max_out, int32_t *n_out, int32_t *n_groups,
+                            int32_t *split_offsets);
 
 /*
  * Ahead-of-time split counts [host] (Tangram steps 6-7: a partition factor per

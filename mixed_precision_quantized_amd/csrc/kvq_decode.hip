@@ -39,6 +39,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "kvq_internal.h"
 
@@ -148,6 +149,9 @@ struct DecodeArgs {
   int32_t *err;
   int32_t only_fp16;  // page mode with the LDS-staged kernel present: this kernel takes FP16 splits only
   int32_t fp8;        // the FP16 class holds FP8 anchors (e4m3 codes and a power-of-two scale per token)
+  int32_t *work;            // shared mode: window counters of the groups, then the count of finished workers
+  const int32_t *wgroup;    // shared mode: group of each worker
+  int32_t n_groups;
 };
 
 // FP8 anchors: 8 e4m3 codes (two words) to 8 fp16 (one uint4, channel order kept), times
@@ -1047,6 +1051,175 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
 }
 
 
+// ------------------------------------------------------------- shared windows -----
+//
+// Shared mode (page tables, INT2 / INT4, one wave per worker): the workers of a group
+// (one token range of one (table, head, class)) take its 32-token windows from the
+// group's counter, kSlots windows per claim, so a worker on a part of the chip that
+// streams faster takes more windows.  A worker's partial is the softmax over the
+// windows it took.  The schedule of run_split_ring is kept: a window's page ids are
+// copied two ring depths before its compute and its data one ring depth before; a block
+// of windows is claimed one block before its page ids are needed, at the start of a
+// block, and its result is read at the start of the next block, where the wait for that
+// block's first window already covers it (vector-memory operations of a wave complete
+// in issue order).  Claims are per block, not per window: atomics on one address
+// serialize (about 250 ns each on MI355X), and a claim per window was measured slower.
+
+// Claims the next n windows of a group: a vector atomic add from lane 0, returning the
+// counter before the add, issued from inline assembly so that it joins the ring copies
+// in the vector-memory counter (the compiler would wait for every copy in flight before
+// the first use of its own atomic's result).  The result register may be read only
+// after a wait that covers the atomic.
+__device__ __forceinline__ uint32_t claim_issue(int32_t *ctr, uint32_t n) {
+  uint32_t old;
+  uint64_t save;
+  asm volatile(
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %0, %2, %3, %4 sc0\n\t"
+      "s_mov_b64 exec, %1"
+      : "=&v"(old), "=&s"(save)
+      : "v"(0u), "v"(n), "s"((uint64_t)(uintptr_t)ctr)
+      : "memory");
+  return old;
+}
+
+// Waits until at most N vector-memory operations of this wave are in flight, then
+// returns lane 0's value of x (a claim result the wait covers) in a scalar register.
+template <int N>
+__device__ __forceinline__ uint32_t wait_take(uint32_t x) {
+  uint32_t r;
+  asm volatile("s_waitcnt vmcnt(%2)\n\tv_readfirstlane_b32 %0, %1" : "=s"(r) : "v"(x), "n"(N) : "memory");
+  return r;
+}
+
+// Issue priority by the progress of the worker's group.  A group's windows are shared by
+// its workers only, so a group whose waves sit behind others on their SIMDs (a SIMD
+// issues the oldest of equal-priority waves first) would end late while the others idle;
+// a wave whose group has handed out more of its windows yields to waves of groups that
+// are further behind: priority 3 below half the windows claimed, 2 below three quarters,
+// 1 below seven eighths, 0 after.
+struct GroupPriority {
+  int level = -1;
+  __device__ __forceinline__ void set(uint32_t claimed, uint32_t nw) {
+    const int want = 8u * claimed < 4u * nw ? 3 : 8u * claimed < 6u * nw ? 2 : 8u * claimed < 7u * nw ? 1 : 0;
+    if (want == level) return;
+    level = want;
+    if (want == 3) __builtin_amdgcn_s_setprio(3);
+    else if (want == 2) __builtin_amdgcn_s_setprio(2);
+    else if (want == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
+};
+
+template <int CLS, int QT>
+__device__ void run_shared_ring(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L, uint8_t *ring,
+                                int32_t *idr, int32_t *win, int32_t *ctr) {
+  using G = RingGeom<CLS, 1>;
+  constexpr int S = G::kSlots;      // windows per claim, per unrolled pass, and in flight
+  constexpr int A = G::kAhead;
+  static_assert(A == S, "one wave refills a slot as soon as its window sits in registers");
+  constexpr int C = G::chunks_of(0);  // data copies per window (plus one id copy)
+  constexpr int kWin = 16;            // window-start ring: window i at i % kWin
+  static_assert(4 * S <= kWin, "window ring too small");
+  constexpr int kIdSlots = 8;
+  static_assert(A < kIdSlots, "id ring too small");
+  RingLoader<CLS, 1> ld(a, sp, ring, idr, 0);
+  const int lane = lane_id();
+  const int32_t T0 = sp.tok_begin & ~15;
+  const uint32_t nw = (uint32_t)((sp.tok_end - T0 + 31) >> 5);  // windows of the group
+  // Window i of this worker starts at token win[i % kWin], or -1 once the group is
+  // exhausted (claims only grow, so every later window is -1 too).
+  auto put = [&](int32_t i, uint32_t k0) {  // windows i .. i + S - 1 are the group's k0 ..
+    if (lane < S) win[(i + lane) & (kWin - 1)] = k0 + (uint32_t)lane < nw ? T0 + 32 * (int32_t)(k0 + lane) : -1;
+  };
+  auto start = [&](int32_t i) { return win[i & (kWin - 1)]; };
+  // The first three blocks in one claim: nothing is in flight yet, so waiting for it
+  // costs its own latency only.
+  uint32_t k0 = 0u;
+  if (lane == 0) k0 = (uint32_t)atomicAdd(ctr, 3 * S);
+  k0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)k0);
+#pragma unroll
+  for (int b = 0; b < 3; ++b) put(b * S, k0 + (uint32_t)(b * S));
+  uint32_t okq = 0;
+#pragma unroll
+  for (int i = 0; i < A; ++i) {
+    const int32_t Ti = start(i), Tn = start(i + A);
+    ld.issue_ids(Tn >= 0 ? Tn : T0, i + A);
+    const int32_t Te = Ti >= 0 ? Ti : T0;
+    okq = (okq << 2) | ld.issue(ld.entry(Te, 0), ld.entry(Te, 1), Ti >= 0, i);
+  }
+  stage_q<QT>(a, sp, L, 0);
+  SplitRun<QT, CLS, false> R(a, sp, L);
+  int id_slot = A;     // id slot of window n + A
+  uint32_t pend = 0u;  // the claim issued at the start of the current block
+  GroupPriority prio;
+  // Window n = block start + r: wait for its data (and, at a block start, for the claim
+  // issued one block earlier), read it, compute it; the copies of window n + A go into
+  // its slot once its words are in registers.  Returns false once the group is
+  // exhausted.
+  auto step = [&](int32_t n, auto rc) -> bool {
+    constexpr int r = decltype(rc)::value;
+    const int32_t Tw = start(n);
+    if (Tw < 0) return false;
+    if (r == 0) {
+      if (n >= S) {
+        const uint32_t k = wait_take<(S - 1) * (C + 1)>(pend);
+        put(n + 2 * S, k);  // the block two ahead
+        prio.set(k, nw);
+      } else {
+        wait_copies<(S - 1) * (C + 1)>();
+      }
+    } else {
+      wait_copies<(S - 1) * (C + 1) + 1>();  // (a claim was issued since window n's copies)
+    }
+    const uint32_t ok = (okq >> (2 * (A - 1))) & 3u;
+    int32_t id0, id1;
+    ld.ids(id_slot, id0, id1);  // window n + A
+    const int id_next = (id_slot + A) & (kIdSlots - 1);
+    Win w;
+    ld.read(Tw, r, ok, w);
+    R.window(w, Tw, [&] {
+      if (r == 0) pend = claim_issue(ctr, S);  // block three ahead
+      const int32_t Tf = start(n + 2 * A);
+      ld.issue_ids(Tf >= 0 ? Tf : T0, id_next);
+      okq = (okq << 2) | ld.issue(id0, id1, start(n + A) >= 0, r);
+    });
+    id_slot = (id_slot + 1) & (kIdSlots - 1);
+    return true;
+  };
+  bool more = true;
+  for (int32_t n0 = 0; more; n0 += S) {
+    more = step(n0, std::integral_constant<int, 0>{});
+    if (more && S > 1) more = step(n0 + 1, std::integral_constant<int, (S > 1 ? 1 : 0)>{});
+    if (more && S > 2) more = step(n0 + 2, std::integral_constant<int, (S > 2 ? 2 : 0)>{});
+  }
+  wait_copies<0>();  // no copy or claim outlives the wave
+  if (ld.errs) report(a.err, (int32_t)ld.errs);
+  R.finish(s_idx);
+}
+
+// Every worker of a shared launch counts itself out, and the last one resets the counters
+// for the next launch (every other worker has stopped claiming by then).  The count is
+// two-level, so that no address takes more than 64 of the workers' atomics, all of
+// which arrive at about the same time: worker s counts into sub-counter s % 64, and the
+// last worker of each sub-counter into the top one.
+constexpr int kDoneSubs = 64;
+
+__device__ void shared_exit(const DecodeArgs &a, int s_idx) {
+  const int lane = lane_id();
+  int32_t *sub = a.work + a.n_groups, *top = sub + kDoneSubs;
+  const int32_t k = s_idx % kDoneSubs;
+  const int32_t members = (a.n_splits - 1 - k) / kDoneSubs + 1;  // workers k, k + 64, ...
+  const int32_t subs = min(a.n_splits, kDoneSubs);
+  int last = 0;
+  if (lane == 0 && atomicAdd(sub + k, 1) == members - 1) last = atomicAdd(top, 1) == subs - 1;
+  last = __builtin_amdgcn_readfirstlane(last);
+  if (last)
+    for (int i = lane; i <= a.n_groups + kDoneSubs; i += 64)
+      __hip_atomic_store(a.work + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Slot maps, INT4 splits, one wave.  Every token of a window may live in a different
 // page, so the window's 32 slot ids are copied into LDS one window ahead of its data
 // (lanes 0-31, 4 B each), and the data copies gather per token into the INT4 window
@@ -1259,15 +1432,38 @@ __global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
 // LDS-staged kernel: page-table mode, INT2 and INT4 splits; W waves per split with 4 QT
 // query heads each; three waves per SIMD at QT = 1 (at most 168 registers a lane), two
 // at QT = 2.
-template <int W, int QT>
+template <int W, int QT, bool SHARED>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 2)))
 decode_ring_kernel(DecodeArgs a) {
   __shared__ Lds<QT> L[W];
   __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes<W>()];
   __shared__ __attribute__((aligned(16))) int32_t idr[W][16];
-  const int s_idx = blockIdx.x;
+  __shared__ int32_t win[SHARED ? 16 : 1];
+  // Shared mode: block b runs worker b P mod n (P the prime 2^31 - 1, so a bijection
+  // for any worker count below it).  Blocks are handed to the SIMDs in order and a SIMD
+  // issues its oldest waves first, so in worker order the early requests' groups would
+  // hold the oldest waves everywhere and end first; spread, every group's workers span
+  // all ages.
+  const int s_idx = SHARED ? (int)(((uint64_t)blockIdx.x * 2147483647ull) % (uint64_t)a.n_splits) : (int)blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   kvq_split sp;
+  if (SHARED) {
+    static_assert(!SHARED || W == 1, "shared windows: one wave per worker");
+    const int32_t grp = a.wgroup[s_idx];
+    if (grp < 0 || grp >= a.n_groups) {  // a worker with no group: O = 0, lse = -inf
+      if (lane_id() == 0) report(a.err, KVQ_DEVERR_SPLIT);
+      for (int j = 0; j < min(4 * QT, a.g); ++j) {
+        *reinterpret_cast<float2 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 2 * lane_id()) =
+            make_float2(0.0f, 0.0f);
+        if (lane_id() == 0) a.part_lse[(int64_t)s_idx * a.g + j] = -INFINITY;
+      }
+    } else if (split_check<QT, false, true>(a, s_idx, sp, 0)) {
+      if (sp.cls == KVQ_INT4) run_shared_ring<KVQ_INT4, QT>(a, sp, s_idx, L[0], ring, idr[0], win, a.work + grp);
+      else if (sp.cls == KVQ_INT2) run_shared_ring<KVQ_INT2, QT>(a, sp, s_idx, L[0], ring, idr[0], win, a.work + grp);
+    }
+    shared_exit(a, s_idx);
+    return;
+  }
   if (!split_check<QT, false, true>(a, s_idx, sp, 4 * QT * wave)) return;
   if (sp.cls == KVQ_INT4) run_split_ring<KVQ_INT4, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
   else if (sp.cls == KVQ_INT2) run_split_ring<KVQ_INT2, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
@@ -1367,11 +1563,12 @@ kvq_status launched(const char *what) {
 
 using namespace kvq;
 
-extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t batch,
-                                      int32_t hq, int32_t hkv, const int32_t *tables, int32_t n_tables,
-                                      int32_t max_entries, int32_t table_kind, const kvq_split *splits,
-                                      int32_t n_splits, float *part_o, float *part_lse, int32_t *dev_err,
-                                      void *stream) {
+namespace {
+
+// Checks shared by both decode entry points; fills the argument block.
+kvq_status decode_setup(DecodeArgs &a, const kvq_cache *c, const void *q, int32_t q_dtype, int32_t batch, int32_t hq,
+                        int32_t hkv, const int32_t *tables, int32_t n_tables, int32_t max_entries, int32_t table_kind,
+                        const kvq_split *splits, int32_t n_splits, float *part_o, float *part_lse, int32_t *dev_err) {
   kvq_status st = check_cache(c);
   if (st != KVQ_OK) return st;
   if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv)
@@ -1388,10 +1585,8 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
     return fail(KVQ_ERR_INVALID_ARG, "n_tables %d != batch * hkv / heads_per_page = %lld", n_tables,
                 (long long)batch * tpr);
   if (n_splits < 0 || max_entries < 0) return fail(KVQ_ERR_INVALID_ARG, "negative size");
-  if (n_splits == 0) return KVQ_OK;
-  if (!q || !tables || !splits || !part_o || !part_lse)
+  if (n_splits > 0 && (!q || !tables || !splits || !part_o || !part_lse))
     return fail(KVQ_ERR_INVALID_ARG, "NULL device array");
-  DecodeArgs a;
   a.heads = c->heads_per_page;
   a.n2 = c->n_pages[0];
   a.n4 = c->n_pages[1];
@@ -1417,6 +1612,36 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
   a.part_lse = part_lse;
   a.err = dev_err;
   a.only_fp16 = 0;
+  a.work = nullptr;
+  a.wgroup = nullptr;
+  a.n_groups = 0;
+  return KVQ_OK;
+}
+
+// The register-staged kernel for the FP16 splits of a page-table launch (when the cache
+// has FP16 pages; the LDS-staged kernel leaves them).
+kvq_status launch_fp16_pages(DecodeArgs a, hipStream_t s) {
+  if (a.n16 == 0) return KVQ_OK;
+  a.only_fp16 = 1;
+  const dim3 grid(a.n_splits), block(64);
+  if (a.g <= 4) hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, s, a);
+  else if (a.g <= 8) hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, s, a);
+  return launched("decode_kernel");
+}
+
+}  // namespace
+
+extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t batch,
+                                      int32_t hq, int32_t hkv, const int32_t *tables, int32_t n_tables,
+                                      int32_t max_entries, int32_t table_kind, const kvq_split *splits,
+                                      int32_t n_splits, float *part_o, float *part_lse, int32_t *dev_err,
+                                      void *stream) {
+  DecodeArgs a;
+  kvq_status st = decode_setup(a, c, q, q_dtype, batch, hq, hkv, tables, n_tables, max_entries, table_kind, splits,
+                               n_splits, part_o, part_lse, dev_err);
+  if (st != KVQ_OK || n_splits == 0) return st;
+  const int g = a.g;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(n_splits), block(64);
   if (table_kind == KVQ_TABLE_SLOTS) {
@@ -1437,16 +1662,38 @@ extern "C" kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t
   }
   // Page mode: INT2 / INT4 splits (and every malformed one) in the LDS-staged kernel,
   // FP16 splits in the register-staged one when the cache has FP16 pages.
-  if (g <= 4) hipLaunchKernelGGL((decode_ring_kernel<1, 1>), grid, dim3(64), 0, s, a);
-  else if (g <= 8) hipLaunchKernelGGL((decode_ring_kernel<1, 2>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((decode_ring_kernel<2, 2>), grid, dim3(128), 0, s, a);
+  if (g <= 4) hipLaunchKernelGGL((decode_ring_kernel<1, 1, false>), grid, dim3(64), 0, s, a);
+  else if (g <= 8) hipLaunchKernelGGL((decode_ring_kernel<1, 2, false>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_ring_kernel<2, 2, false>), grid, dim3(128), 0, s, a);
   st = launched("decode_ring_kernel");
-  if (st != KVQ_OK || a.n16 == 0) return st;
-  a.only_fp16 = 1;
-  if (g <= 4) hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, s, a);
-  else if (g <= 8) hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, s, a);
-  return launched("decode_kernel");
+  if (st != KVQ_OK) return st;
+  return launch_fp16_pages(a, s);
+}
+
+extern "C" kvq_status kvq_decode_attn_shared(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t batch,
+                                             int32_t hq, int32_t hkv, const int32_t *tables, int32_t n_tables,
+                                             int32_t max_entries, int32_t table_kind, const kvq_split *workers,
+                                             const int32_t *worker_group, int32_t n_workers, int32_t n_groups,
+                                             int32_t *work, float *part_o, float *part_lse, int32_t *dev_err,
+                                             void *stream) {
+  DecodeArgs a;
+  kvq_status st = decode_setup(a, c, q, q_dtype, batch, hq, hkv, tables, n_tables, max_entries, table_kind, workers,
+                               n_workers, part_o, part_lse, dev_err);
+  if (st != KVQ_OK) return st;
+  if (table_kind != KVQ_TABLE_PAGES) return fail(KVQ_ERR_UNSUPPORTED, "shared windows need page tables");
+  if (a.g > 8) return fail(KVQ_ERR_UNSUPPORTED, "shared windows: g = %d > 8", a.g);
+  if (n_workers == 0) return KVQ_OK;
+  if (n_groups < 1 || !work || !worker_group) return fail(KVQ_ERR_INVALID_ARG, "shared windows need groups and counters");
+  a.work = work;
+  a.wgroup = worker_group;
+  a.n_groups = n_groups;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(n_workers), block(64);
+  if (a.g <= 4) hipLaunchKernelGGL((decode_ring_kernel<1, 1, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_ring_kernel<1, 2, true>), grid, block, 0, s, a);
+  st = launched("decode_ring_kernel");
+  if (st != KVQ_OK) return st;
+  return launch_fp16_pages(a, s);
 }
 
 extern "C" kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, int32_t n_splits,
@@ -1477,13 +1724,13 @@ extern "C" kvq_status kvq_decode_occupancy(int32_t g, int32_t table_kind, int32_
   const bool slots = table_kind == KVQ_TABLE_SLOTS;
   if (g <= 4)
     e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_slots_ring_kernel<1>, 64, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1, 1>, 64, 0);
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1, 1, false>, 64, 0);
   else if (g <= 8)
     e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_slots_ring_kernel<2>, 64, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1, 2>, 64, 0);
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<1, 2, false>, 64, 0);
   else
     e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, true>, 64, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<2, 2>, 128, 0);
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<2, 2, false>, 128, 0);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(KVQ_ERR_HIP, "CU count query failed");

@@ -204,6 +204,101 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
   return KVQ_OK;
 }
 
+// Shared-work plan: every range is a group whose windows its workers share; a head's
+// worker count is shared among its ranges in proportion to decode cost (largest
+// remainders, at least one worker per range, at most one per 32-token window), FP16
+// ranges get one worker each (their kernel does not share).
+kvq_status kvq_plan_workers(const kvq_split *ranges, int32_t n_ranges, int32_t batch, int32_t hkv,
+                            int32_t heads_per_page, const int32_t *workers_per_head, const float *class_cost,
+                            kvq_split *out, int32_t *out_group, int32_t max_out, int32_t *n_out, int32_t *n_groups,
+                            int32_t *split_offsets) {
+  const float *cost = class_cost ? class_cost : kDefaultTokenCost;
+  for (int c = 0; c < 3; ++c)
+    if (!(cost[c] > 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "class cost %d is not positive", c);
+  if (n_ranges < 0 || batch < 0 || hkv <= 0 || heads_per_page <= 0 || hkv % heads_per_page)
+    return fail(KVQ_ERR_INVALID_ARG, "bad plan shape");
+  if ((n_ranges > 0 && (!ranges || !workers_per_head)) || !n_out || !n_groups || !split_offsets ||
+      (max_out > 0 && (!out || !out_group)))
+    return fail(KVQ_ERR_INVALID_ARG, "NULL plan array");
+  const int32_t tpr = hkv / heads_per_page;
+  const int32_t n_tables = batch * tpr;
+  for (int32_t i = 0; i < n_ranges; ++i) {
+    const kvq_split &r = ranges[i];
+    if (r.table < 0 || r.table >= n_tables || r.head < 0 || r.head >= heads_per_page || r.cls < 0 ||
+        r.cls > 2 || r.tok_begin < 0 || r.tok_end < r.tok_begin)
+      return fail(KVQ_ERR_INVALID_ARG, "malformed range %d", i);
+    if (r.cls == KVQ_INT2 && (r.tok_begin % kGroup || r.tok_end % kGroup))
+      return fail(KVQ_ERR_INVALID_ARG, "INT2 range %d is not on 32-token boundaries", i);
+    if (i > 0) {
+      const kvq_split &p = ranges[i - 1];
+      if (p.table > r.table || (p.table == r.table && p.head > r.head))
+        return fail(KVQ_ERR_INVALID_ARG, "ranges are not sorted by (table, head) at %d", i);
+    }
+  }
+  auto windows = [](const kvq_split &r) -> int64_t {
+    return r.tok_end > r.tok_begin ? (r.tok_end - (r.tok_begin & ~(kPage - 1)) + 31) / 32 : 0;
+  };
+  std::vector<int64_t> workers((size_t)n_ranges, 0);
+  for (int32_t i0 = 0, i1; i0 < n_ranges; i0 = i1) {
+    i1 = i0 + 1;
+    while (i1 < n_ranges && ranges[i1].table == ranges[i0].table && ranges[i1].head == ranges[i0].head) ++i1;
+    const int64_t total = workers_per_head[(size_t)ranges[i0].table * heads_per_page + ranges[i0].head];
+    if (total < 0) return fail(KVQ_ERR_INVALID_ARG, "negative worker count");
+    double cost_sum = 0.0;
+    int32_t n_live = 0;
+    for (int32_t i = i0; i < i1; ++i) {
+      if (windows(ranges[i]) == 0) continue;
+      ++n_live;
+      if (ranges[i].cls != KVQ_FP16)
+        cost_sum += (double)(ranges[i].tok_end - ranges[i].tok_begin) * (double)cost[ranges[i].cls];
+    }
+    if (n_live == 0) continue;
+    const int64_t spare = std::max<int64_t>(0, total - n_live);  // beyond one worker each
+    std::vector<std::pair<double, int32_t>> frac;
+    int64_t given = 0;
+    for (int32_t i = i0; i < i1; ++i) {
+      if (windows(ranges[i]) == 0) continue;
+      workers[i] = 1;
+      if (ranges[i].cls == KVQ_FP16 || cost_sum <= 0.0) continue;
+      const double share =
+          (double)spare * (double)(ranges[i].tok_end - ranges[i].tok_begin) * (double)cost[ranges[i].cls] / cost_sum;
+      const int64_t whole = (int64_t)std::floor(share);
+      workers[i] += whole;
+      given += whole;
+      frac.push_back({share - (double)whole, i});
+    }
+    std::stable_sort(frac.begin(), frac.end(),
+                     [](const std::pair<double, int32_t> &x, const std::pair<double, int32_t> &y) {
+                       return x.first > y.first;
+                     });
+    for (size_t k = 0; given < spare && k < frac.size(); ++k, ++given) ++workers[frac[k].second];
+    for (int32_t i = i0; i < i1; ++i) workers[i] = std::min(workers[i], windows(ranges[i]));
+  }
+  int32_t w = 0, groups = 0;
+  int32_t next_pair = 0;
+  for (int32_t i = 0; i < n_ranges; ++i) {
+    const kvq_split &r = ranges[i];
+    const int32_t pair = (r.table / tpr) * hkv + (r.table % tpr) * heads_per_page + r.head;
+    while (next_pair <= pair) split_offsets[next_pair++] = w;
+    if (workers[i] == 0) continue;
+    for (int64_t p = 0; p < workers[i]; ++p) {
+      if (w >= max_out) return fail(KVQ_ERR_CAPACITY, "more than %d workers", max_out);
+      out_group[w] = groups;
+      out[w++] = r;
+    }
+    ++groups;
+  }
+  while (next_pair <= batch * hkv) split_offsets[next_pair++] = w;
+  *n_out = w;
+  *n_groups = groups;
+  return KVQ_OK;
+}
+
+size_t kvq_decode_work_bytes(int32_t n_groups) {
+  // the groups' window counters, then 64 + 1 counters of finished workers
+  return n_groups > 0 ? (size_t)(n_groups + 65) * sizeof(int32_t) : 0;
+}
+
 kvq_status kvq_balanced_split_counts(const int64_t *work, int32_t n, int32_t total_work, int32_t *out) {
   if (!work || !out || n <= 0 || total_work <= 0) return fail(KVQ_ERR_INVALID_ARG, "bad balanced-count arguments");
   int64_t hi = 1;

@@ -78,6 +78,10 @@ _SIGS = {
                          _P], ctypes.c_int),
     "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
     "kvq_plan_splits": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _i64, _P, _i32, _P, _P], ctypes.c_int),
+    "kvq_plan_workers": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _i32, _P, _P, _P], ctypes.c_int),
+    "kvq_decode_attn_shared": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _P, _i32, _i32, _P, _P,
+                                _P, _P, _P], ctypes.c_int),
+    "kvq_decode_work_bytes": ([_i32], ctypes.c_size_t),
     "kvq_aot_split_counts": ([_P, _i32, _i32, _i32, _P], ctypes.c_int),
     "kvq_balanced_split_counts": ([_P, _i32, _i32, _P], ctypes.c_int),
     "kvq_decode_occupancy": ([_i32, _i32, _P, _P], ctypes.c_int),
@@ -347,6 +351,32 @@ def decode_attn(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, t
                                 _dptr(dev_err), _stream(stream)), "kvq_decode_attn")
 
 
+def decode_attn_shared(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, table_kind: int,
+                       workers: torch.Tensor, groups: torch.Tensor, n_groups: int, work: torch.Tensor,
+                       part_o: torch.Tensor, part_lse: torch.Tensor, dev_err=None, stream=None):
+    """Shared-window decode: workers int32 device [n, 5] (each its group's range), groups
+    int32 device [n], work from decode_work(n_groups) (zero before the first call; zero
+    again after each)."""
+    assert q.is_contiguous() and tables.is_contiguous() and workers.is_contiguous() and groups.is_contiguous()
+    assert workers.dtype == groups.dtype == work.dtype == torch.int32 and workers.shape[-1] == 5
+    batch, hq = q.shape[0], q.shape[1]
+    n = workers.shape[0]
+    assert groups.numel() >= n and work.numel() * 4 >= _lib.kvq_decode_work_bytes(n_groups)
+    assert part_o.numel() >= n * (hq // hkv) * HEAD_DIM and part_lse.numel() >= n * (hq // hkv)
+    _check(_lib.kvq_decode_attn_shared(cache.struct, _dptr(q), _DTYPES[q.dtype], batch, hq, hkv, _dptr(tables),
+                                       tables.shape[0], tables.shape[1], table_kind, _dptr(workers), _dptr(groups),
+                                       n, n_groups, _dptr(work), _dptr(part_o), _dptr(part_lse), _dptr(dev_err),
+                                       _stream(stream)), "kvq_decode_attn_shared")
+
+
+def decode_work(n_groups: int, device="cuda") -> torch.Tensor:
+    """Zeroed work counters for decode_attn_shared."""
+    nbytes = _lib.kvq_decode_work_bytes(n_groups)
+    if nbytes == 0:
+        raise KvqError(-1, f"kvq_decode_work_bytes({n_groups})")
+    return torch.zeros(nbytes // 4, dtype=torch.int32, device=device)
+
+
 def lse_merge(part_o: torch.Tensor, part_lse: torch.Tensor, n_splits: int, split_offsets: torch.Tensor,
               batch: int, hq: int, hkv: int, out: torch.Tensor, out_lse=None, stream=None):
     assert out.is_contiguous() and out.numel() >= batch * hq * HEAD_DIM
@@ -376,6 +406,24 @@ def plan_splits(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int,
                                 _hptr(tps), int(target_bytes), _hptr(out), max_out,
                                 ctypes.byref(n_out), _hptr(offsets)), "kvq_plan_splits")
     return out[: n_out.value].copy(), offsets
+
+
+def plan_workers(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int, workers_per_head: np.ndarray,
+                 class_cost=None):
+    """ranges as for plan_splits.  Returns (workers int32 [n, 5], groups int32 [n], n_groups,
+    split_offsets int32 [batch*hkv + 1])."""
+    r = np.ascontiguousarray(np.asarray(ranges).view(np.int32).reshape(-1, 5))
+    wph = np.ascontiguousarray(workers_per_head, np.int32)
+    max_out = max(1, int(wph.sum()) + len(r))
+    out = np.zeros((max_out, 5), np.int32)
+    grp = np.zeros(max_out, np.int32)
+    offsets = np.zeros(batch * hkv + 1, np.int32)
+    n_out, n_groups = _i32(), _i32()
+    cc = None if class_cost is None else np.ascontiguousarray(class_cost, np.float32)
+    _check(_lib.kvq_plan_workers(_hptr(r), r.shape[0], batch, hkv, heads_per_page, _hptr(wph), _hptr(cc), _hptr(out),
+                                 _hptr(grp), max_out, ctypes.byref(n_out), ctypes.byref(n_groups), _hptr(offsets)),
+           "kvq_plan_workers")
+    return out[: n_out.value].copy(), grp[: n_out.value].copy(), n_groups.value, offsets
 
 
 def head_group_plan(budgets: np.ndarray, heads_per_group: int, n_tokens: int, cls: int = 1):
@@ -451,6 +499,18 @@ def bind_decode_attn(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tens
             tables.shape[1], table_kind, _dptr(splits), splits.shape[0], _dptr(part_o),
             _dptr(part_lse), _dptr(dev_err), _stream(stream))
     return BoundCall("kvq_decode_attn", args, keep=(cache, q, tables, splits, part_o, part_lse, dev_err))
+
+
+def bind_decode_attn_shared(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, table_kind: int,
+                            workers: torch.Tensor, groups: torch.Tensor, n_groups: int, work: torch.Tensor,
+                            part_o: torch.Tensor, part_lse: torch.Tensor, dev_err=None, stream=None) -> BoundCall:
+    assert q.is_contiguous() and tables.is_contiguous() and workers.is_contiguous() and groups.is_contiguous()
+    batch, hq = q.shape[0], q.shape[1]
+    args = (cache.struct, _dptr(q), _DTYPES[q.dtype], batch, hq, hkv, _dptr(tables), tables.shape[0],
+            tables.shape[1], table_kind, _dptr(workers), _dptr(groups), workers.shape[0], n_groups, _dptr(work),
+            _dptr(part_o), _dptr(part_lse), _dptr(dev_err), _stream(stream))
+    return BoundCall("kvq_decode_attn_shared", args,
+                     keep=(cache, q, tables, workers, groups, work, part_o, part_lse, dev_err))
 
 
 def bind_lse_merge(part_o, part_lse, n_splits, split_offsets, batch, hq, hkv, out, out_lse=None,

@@ -86,6 +86,30 @@ class DeviceRun:
         w = self.w
         return self.kvq.plan_splits(self.ranges, w.batch, w.hkv, w.heads_per_page, **kw)
 
+    def plan_workers(self, workers_per_head, class_cost=None):
+        w = self.w
+        wph = np.broadcast_to(np.asarray(workers_per_head, np.int32), (w.n_tables * w.heads_per_page,))
+        return self.kvq.plan_workers(self.ranges, w.batch, w.hkv, w.heads_per_page, wph, class_cost)
+
+    def decode_shared(self, workers, groups, n_groups, offsets, out_dtype=torch.float32, work=None):
+        """Shared-window decode + merge; returns (out, lse, part_o, part_lse, work)."""
+        w, kvq = self.w, self.kvq
+        n = workers.shape[0]
+        wk = torch.as_tensor(workers, device=self.device).contiguous()
+        gr = torch.as_tensor(groups, device=self.device).contiguous()
+        off = torch.as_tensor(offsets, device=self.device)
+        if work is None:
+            work = kvq.decode_work(n_groups, self.device)
+        part_o = torch.empty((max(n, 1), w.g, 128), dtype=torch.float32, device=self.device)
+        part_lse = torch.empty((max(n, 1), w.g), dtype=torch.float32, device=self.device)
+        out = torch.empty((w.batch, w.hq, 128), dtype=out_dtype, device=self.device)
+        out_lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device=self.device)
+        kvq.decode_attn_shared(self.cache, self.q, w.hkv, self.tables, kvq.TABLE_PAGES, wk, gr, n_groups, work,
+                               part_o, part_lse, dev_err=self.err)
+        kvq.lse_merge(part_o, part_lse, n, off, w.batch, w.hq, w.hkv, out, out_lse)
+        torch.cuda.synchronize()
+        return out, out_lse, part_o[:n], part_lse[:n], work
+
     def decode(self, splits: np.ndarray, offsets: np.ndarray, out_dtype=torch.float32):
         w, kvq = self.w, self.kvq
         g = w.g

@@ -221,3 +221,23 @@ def test_prefill_workspace_and_validation(kvq):
     assert lib.kvq_prefill_prepare(fake, fake, 1, 1, 128, 2, fake, None, fake, fake, fake, fake,
                                    ctypes.c_void_p(0x1010), need, None, None) == -1   # workspace off 256
     assert b"aligned" in lib.kvq_last_error()
+
+
+def test_plan_workers_shares_by_cost_and_caps(kvq):
+    """Shared-window plan: a head's workers are shared among its ranges by tokens x cost
+    (largest remainders, one at least each), an FP16 range gets one, no range more than
+    its windows; every worker carries its group's range; groups are numbered in order."""
+    r = _ranges([(0, 0, 0, 0, 640), (0, 0, 1, 640, 1000), (0, 0, 2, 1008, 1100), (0, 1, 1, 0, 96),
+                 (1, 0, 1, 16, 17)], kvq)
+    workers, groups, n_groups, offsets = kvq.plan_workers(r, 2, 2, 2, np.array([10, 50, 4, 4], np.int32))
+    assert n_groups == 5
+    # head (0, 0): 10 = 1 FP16 + 9 shared 640 : 360 -> 5 INT2, 4 INT4 (remainders .48 / .52)
+    counts = np.bincount(groups, minlength=n_groups).tolist()
+    assert counts == [5, 4, 1, 3, 1]          # (0, 1): 3 windows cap 50; (1, 0): one window
+    for gi in range(n_groups):
+        rows = workers[groups == gi]
+        assert (rows == rows[0]).all()
+    assert [tuple(workers[groups == gi][0]) for gi in range(n_groups)] == [tuple(x) for x in np.asarray(r).view(np.int32).reshape(-1, 5)]
+    assert offsets.tolist() == [0, 10, 13, 14, 14]
+    with pytest.raises(kvq.KvqError):
+        kvq.plan_workers(r, 2, 2, 2, np.array([-1, 1, 1, 1], np.int32))
