@@ -389,6 +389,24 @@ kvq_status kvq_decode_attn_shared(const kvq_cache *c, const void *q, int32_t q_d
                                   int32_t *work, float *part_o, float *part_lse, int32_t *dev_err,
                                   void *stream);
 
+/*
+ * kvq_decode_attn_shared for callers that cannot allocate (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same call
+ * without the work argument; the counters live in a file-scope device array of
+ * the library (one per GPU, held until the process ends, about 64 KB), cleared
+ * by a small kernel on the stream at every call.  No allocation, no memset.  At
+ * most 16384 groups (KVQ_ERR_CAPACITY beyond).  Every call on one GPU uses that
+ * GPU's array: calls that may overlap on one GPU (several streams, several
+ * threads) race.  Errors as kvq_decode_attn_shared, plus CAPACITY, NO_DEVICE.
+ */
+kvq_status kvq_decode_attn_shared_noalloc(const kvq_cache *c, const void *q, int32_t q_dtype,
+                                          int32_t batch, int32_t hq, int32_t hkv,
+                                          const int32_t *tables, int32_t n_tables,
+                                          int32_t max_entries, int32_t table_kind,
+                                          const kvq_split *workers, const int32_t *worker_group,
+                                          int32_t n_workers, int32_t n_groups, float *part_o,
+                                          float *part_lse, int32_t *dev_err, void *stream);
+
 /* Bytes of the work counters of kvq_decode_attn_shared for n_groups groups (0 if
  * n_groups < 1).  Host only. */
 size_t kvq_decode_work_bytes(int32_t n_groups);

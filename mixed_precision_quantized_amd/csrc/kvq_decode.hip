@@ -39,6 +39,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "kvq_internal.h"
@@ -1694,6 +1695,77 @@ extern "C" kvq_status kvq_decode_attn_shared(const kvq_cache *c, const void *q, 
   st = launched("decode_ring_kernel");
   if (st != KVQ_OK) return st;
   return launch_fp16_pages(a, s);
+}
+
+namespace kvq {
+namespace {
+
+// ------------------------------------------------------------- no allocation -----
+//
+// The shared-window decode with its counters in a file-scope device array instead of a
+// caller's workspace, for callers that cannot allocate (code under graph capture, tight
+// serving loops).  Each GPU holds its own copy of the array, at its own address, until
+// the process ends; the address is looked up once per device with that device current.
+// Every call on a GPU uses that GPU's array, so calls that overlap on one GPU race.
+
+constexpr int kNoAllocGroups = 16384;  // groups one call may have
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) int32_t scratch[kNoAllocGroups + kDoneSubs + 1];
+
+// Clears n counters (a fill kernel rather than a memset: safe under graph capture).
+__global__ void __launch_bounds__(256) clear_kernel(int32_t *p, int32_t n) {
+  for (int32_t i = (int32_t)(blockIdx.x * 256 + threadIdx.x); i < n; i += (int32_t)(gridDim.x * 256)) p[i] = 0;
+}
+
+int32_t *scratch_address(kvq_status &st) {
+  static std::mutex mu;
+  static int32_t *addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    st = fail(KVQ_ERR_NO_DEVICE, "hipGetDevice failed");
+    return nullptr;
+  }
+  if (dev >= kMaxDevices) {
+    st = fail(KVQ_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      st = fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev] = static_cast<int32_t *>(ptr);
+  }
+  return addr[dev];
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" kvq_status kvq_decode_attn_shared_noalloc(const kvq_cache *c, const void *q, int32_t q_dtype,
+                                                     int32_t batch, int32_t hq, int32_t hkv, const int32_t *tables,
+                                                     int32_t n_tables, int32_t max_entries, int32_t table_kind,
+                                                     const kvq_split *workers, const int32_t *worker_group,
+                                                     int32_t n_workers, int32_t n_groups, float *part_o,
+                                                     float *part_lse, int32_t *dev_err, void *stream) {
+  using namespace kvq;
+  if (n_groups > kNoAllocGroups)
+    return fail(KVQ_ERR_CAPACITY, "%d groups: this entry point holds counters for at most %d", n_groups,
+                kNoAllocGroups);
+  if (n_workers > 0 && n_groups < 1) return fail(KVQ_ERR_INVALID_ARG, "shared windows need groups");
+  kvq_status st = KVQ_OK;
+  int32_t *work = n_workers > 0 ? scratch_address(st) : nullptr;
+  if (st != KVQ_OK) return st;
+  if (work) {
+    const int32_t n = n_groups + kDoneSubs + 1;
+    hipLaunchKernelGGL(clear_kernel, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), work, n);
+    if ((st = launched("clear_kernel")) != KVQ_OK) return st;
+  }
+  return kvq_decode_attn_shared(c, q, q_dtype, batch, hq, hkv, tables, n_tables, max_entries, table_kind, workers,
+                                worker_group, n_workers, n_groups, work, part_o, part_lse, dev_err, stream);
 }
 
 extern "C" kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, int32_t n_splits,

@@ -82,6 +82,8 @@ _SIGS = {
     "kvq_decode_attn_shared": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _P, _i32, _i32, _P, _P,
                                 _P, _P, _P], ctypes.c_int),
     "kvq_decode_work_bytes": ([_i32], ctypes.c_size_t),
+    "kvq_decode_attn_shared_noalloc": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _P, _i32, _i32,
+                                        _P, _P, _P, _P], ctypes.c_int),
     "kvq_aot_split_counts": ([_P, _i32, _i32, _i32, _P], ctypes.c_int),
     "kvq_balanced_split_counts": ([_P, _i32, _i32, _P], ctypes.c_int),
     "kvq_decode_occupancy": ([_i32, _i32, _P, _P], ctypes.c_int),
@@ -367,6 +369,24 @@ def decode_attn_shared(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Te
                                        tables.shape[0], tables.shape[1], table_kind, _dptr(workers), _dptr(groups),
                                        n, n_groups, _dptr(work), _dptr(part_o), _dptr(part_lse), _dptr(dev_err),
                                        _stream(stream)), "kvq_decode_attn_shared")
+
+
+def decode_attn_shared_noalloc(cache: Cache, q: torch.Tensor, hkv: int, tables: torch.Tensor, table_kind: int,
+                               workers: torch.Tensor, groups: torch.Tensor, n_groups: int, part_o: torch.Tensor,
+                               part_lse: torch.Tensor, dev_err=None, stream=None):
+    """decode_attn_shared with the library's own counters (no work argument, nothing
+    allocated by the library)."""
+    assert q.is_contiguous() and tables.is_contiguous() and workers.is_contiguous() and groups.is_contiguous()
+    assert workers.dtype == groups.dtype == torch.int32 and workers.shape[-1] == 5
+    batch, hq = q.shape[0], q.shape[1]
+    n = workers.shape[0]
+    assert groups.numel() >= n
+    assert part_o.numel() >= n * (hq // hkv) * HEAD_DIM and part_lse.numel() >= n * (hq // hkv)
+    _check(_lib.kvq_decode_attn_shared_noalloc(cache.struct, _dptr(q), _DTYPES[q.dtype], batch, hq, hkv,
+                                               _dptr(tables), tables.shape[0], tables.shape[1], table_kind,
+                                               _dptr(workers), _dptr(groups), n, n_groups, _dptr(part_o),
+                                               _dptr(part_lse), _dptr(dev_err), _stream(stream)),
+           "kvq_decode_attn_shared_noalloc")
 
 
 def decode_work(n_groups: int, device="cuda") -> torch.Tensor:
