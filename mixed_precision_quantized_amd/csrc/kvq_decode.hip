@@ -409,6 +409,8 @@ struct SplitRun {
   int qbase = 0;       // first query head (of the g) this wave computes
   float zacc[QT];      // row lr: sum of p z over this lane's tokens (V zero term)
   float asum[QT];      // row lr: sum of the fp16 operand weights p s (V code offset)
+  static constexpr int kFold = 8;  // windows between folds of those two into acc
+  int since = 0;       // windows since the last fold
 
   __device__ SplitRun(const DecodeArgs &a_, const kvq_split &sp_, Lds<QT> &L_)
       : a(a_), sp(sp_), L(L_), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4) {
@@ -671,6 +673,52 @@ struct SplitRun {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = mfma(ap, vb[nt], acc[qt][nt]);
     }
+    if (CLS != KVQ_FP16 && ++since == kFold) {
+      fold();
+      since = 0;
+    }
+  }
+
+  // Row (query lb, group lr / 4) totals of the lanes' V zero-term and code-offset sums
+  // (they are kept per P-operand row, lane (lr, lb) for row lr).
+  __device__ __forceinline__ void row_terms(int qt, float &zrow, float &arow) const {
+    float z = zacc[qt], as = asum[qt];
+    z += __shfl_xor(z, 16);
+    z += __shfl_xor(z, 32);
+    as += __shfl_xor(as, 16);
+    as += __shfl_xor(as, 32);
+    zrow = __shfl(z, 4 * lb + (lr >> 2));
+    arow = __shfl(as, 4 * lb + (lr >> 2));
+  }
+
+  // Code offset of channel 8 lr + nt in the V operand.
+  __device__ __forceinline__ static float v_offset(int nt) {
+    return CLS == KVQ_INT4 ? 64.0f : CLS == KVQ_INT2 ? ((nt >> 1) & 1 ? 16.0f : 64.0f) : 0.0f;
+  }
+
+  // Folds the V zero term and the code offsets into the accumulators every kFold
+  // windows, so that they hold sum p v-hat itself: with the offsets in them, an
+  // accumulator runs some hundreds of times larger than the result (the offset is 64
+  // against codes of 0-15, and the code term cancels most of the zero term), and the
+  // fp32 rounding of a long split's additions would grow with its length (measured:
+  // row error 2.2e-3 for 6,800-token splits, 9.5e-3 for 27,000, against 6e-4 folded
+  // every window's worth).
+  // (Only element lr / 4 of an accumulator is a row this lane reports; the others, rows
+  // of the block-diagonal product that no lane reads, take the same addition.)
+  __device__ __forceinline__ void fold() {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float zrow, arow;
+      row_terms(qt, zrow, arow);
+      const float c64 = fmaf(-64.0f, arow, zrow), c16 = fmaf(-16.0f, arow, zrow);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const float c = v_offset(nt) == 64.0f ? c64 : c16;
+        acc[qt][nt] += f4{c, c, c, c};
+      }
+      zacc[qt] = 0.0f;
+      asum[qt] = 0.0f;
+    }
   }
 
   // Normalize and store: lane (lr, lb) owns query 4 qt + lb, channels 8 lr .. 8 lr + 7.
@@ -678,13 +726,8 @@ struct SplitRun {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float l_tot = row_sum16(l_run[qt]);
-      float z = zacc[qt], as = asum[qt];
-      z += __shfl_xor(z, 16);
-      z += __shfl_xor(z, 32);
-      as += __shfl_xor(as, 16);
-      as += __shfl_xor(as, 32);
-      const float zrow = __shfl(z, 4 * lb + (lr >> 2));  // row (query lb, group lr / 4)
-      const float arow = __shfl(as, 4 * lb + (lr >> 2));
+      float zrow, arow;  // row (query lb, group lr / 4)
+      row_terms(qt, zrow, arow);
       const int j = qbase + 4 * qt + lb;
       const bool any = l_tot > 0.0f;
       const float inv = any ? 1.0f / l_tot : 0.0f;
@@ -694,10 +737,7 @@ struct SplitRun {
       for (int nt = 0; nt < 8; ++nt) {
         const f4 d = acc[qt][nt];
         const float v = r == 0 ? d[0] : r == 1 ? d[1] : r == 2 ? d[2] : d[3];
-        float off = 0.0f;  // code offset of channel 8 lr + nt in the V operand
-        if (CLS == KVQ_INT4) off = 64.0f;
-        if (CLS == KVQ_INT2) off = (nt >> 1) & 1 ? 16.0f : 64.0f;
-        o[nt] = any ? (CLS == KVQ_FP16 ? v : fmaf(-off, arow, v) + zrow) * inv : 0.0f;
+        o[nt] = any ? (CLS == KVQ_FP16 ? v : fmaf(-v_offset(nt), arow, v) + zrow) * inv : 0.0f;
       }
       if (j < a.g) {
         float4 *dst = reinterpret_cast<float4 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 8 * lr);
