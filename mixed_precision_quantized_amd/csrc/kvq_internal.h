@@ -11,7 +11,7 @@ constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 constexpr int kGroup = 32;
 constexpr int kMaxG = 16;             // query heads per KV head handled by the decode kernel
-constexpr int kMaxReorderEntries = 8192;
+constexpr int kMaxReorderEntries = 32768;  // entries per table the reorder stages in LDS (4 B each)
 
 // Head block sizes and region offsets (the written layout; see kvq.h).  Code rows are
 // little-endian 32-bit words; with b bits per code, word w holds channels

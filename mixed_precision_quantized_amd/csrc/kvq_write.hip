@@ -348,15 +348,17 @@ __global__ void __launch_bounds__(64) append_int2_kernel(
 
 // --------------------------------------------------------------- reorder ------
 
-// One wavefront per table: stable partition of the entries by class with
-// ballot + popcount prefix sums.  The entries are staged in LDS (input and
-// output halves), so the write-back is in place and the pair check reads LDS.
+// One wavefront per table: stable partition of the entries by class with ballot +
+// popcount prefix sums.  The table is staged in LDS (4 B per entry) before anything is
+// written, so the partitioned entries can go straight to the table in place: first
+// the class counts, then the INT4 and FP16 entries to their places, then the INT2
+// entries, which are also compacted at the front of the staged copy (an INT2 entry's
+// place is at or before its input index, and every input of a 64-entry chunk is read
+// before any lane writes) for the pair check.
 __global__ void __launch_bounds__(64) reorder_kernel(CacheView c, int32_t *tables, int32_t max_entries,
                                                      const int32_t *n_entries, int32_t *class_counts,
                                                      int32_t *err) {
-  extern __shared__ int32_t lds[];
-  int32_t *ent = lds;                 // [max_entries] input order
-  int32_t *part = lds + max_entries;  // [max_entries] partitioned order
+  extern __shared__ int32_t ent[];  // [max_entries]: the input order; then the INT2 entries in order
   const int lane = threadIdx.x;
   const int32_t t = blockIdx.x;
   int32_t *row = tables + (int64_t)t * max_entries;
@@ -374,28 +376,47 @@ __global__ void __launch_bounds__(64) reorder_kernel(CacheView c, int32_t *table
     if (lane == 0) report(err, KVQ_DEVERR_ID);
     return;
   }
-  int32_t w = 0, counts[3];
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  for (int cls = 0; cls < 3; ++cls) {
-    const int32_t start = w;
-    for (int32_t base = 0; base < n; base += 64) {
-      const int32_t e = base + lane;  // written by this same lane above
-      const bool mine = e < n && page_class(c, ent[e]) == cls;
-      const uint64_t mask = __ballot(mine);
-      if (mine) part[w + __popcll(mask & below)] = ent[e];
-      w += __popcll(mask);
-    }
-    counts[cls] = w - start;
+  int32_t counts[3] = {0, 0, 0};
+  for (int32_t base = 0; base < n; base += 64) {  // each lane reads back what it staged
+    const int32_t e = base + lane;
+    const int cls = e < n ? page_class(c, ent[e]) : 3;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) counts[k] += __popcll(__ballot(cls == k));
   }
-  __syncthreads();  // part[] is read across lanes below
-  for (int32_t e = lane; e < n; e += 64) row[e] = part[e];
+  __syncthreads();  // entries are read across lanes below
+  int32_t w4 = counts[0], w16 = counts[0] + counts[1];
+  for (int32_t base = 0; base < n; base += 64) {
+    const int32_t e = base + lane;
+    const int32_t v = e < n ? ent[e] : 0;
+    const int cls = e < n ? page_class(c, v) : 3;
+    const uint64_t m4 = __ballot(cls == KVQ_INT4), m16 = __ballot(cls == KVQ_FP16);
+    if (cls == KVQ_INT4) row[w4 + __popcll(m4 & below)] = v;
+    if (cls == KVQ_FP16) row[w16 + __popcll(m16 & below)] = v;
+    w4 += __popcll(m4);
+    w16 += __popcll(m16);
+  }
+  int32_t w2 = 0;
+  for (int32_t base = 0; base < n; base += 64) {
+    const int32_t e = base + lane;
+    const int32_t v = e < n ? ent[e] : 0;
+    const bool mine = e < n && page_class(c, v) == KVQ_INT2;
+    const uint64_t m2 = __ballot(mine);
+    if (mine) {
+      const int32_t at = w2 + __popcll(m2 & below);
+      ent[at] = v;
+      row[at] = v;
+    }
+    w2 += __popcll(m2);
+  }
+  __syncthreads();
   if (class_counts && lane == 0)
     for (int cls = 0; cls < 3; ++cls) class_counts[(int64_t)t * 3 + cls] = counts[cls];
   // INT2 entries must now be aligned pairs (even, even + 1).
   bool pair_bad = counts[0] & 1;
   for (int32_t e = 2 * lane; e + 1 < counts[0]; e += 128) {
-    const int32_t p = part[e];
-    pair_bad |= (p & 1) || part[e + 1] != p + 1;
+    const int32_t p = ent[e];
+    pair_bad |= (p & 1) || ent[e + 1] != p + 1;
   }
   if (__any(pair_bad) && lane == 0) report(err, KVQ_DEVERR_PAIR);
 }
@@ -519,9 +540,14 @@ extern "C" kvq_status kvq_reorder_pages(const kvq_cache *c, int32_t *tables, int
   if (!tables || !n_entries) return fail(KVQ_ERR_INVALID_ARG, "NULL tables or n_entries");
   if (max_entries > kMaxReorderEntries)
     return fail(KVQ_ERR_UNSUPPORTED, "max_entries %d exceeds %d", max_entries, kMaxReorderEntries);
-  hipLaunchKernelGGL(reorder_kernel, dim3(n_tables), dim3(64), (size_t)(max_entries > 0 ? max_entries : 1) * 8,
-                     static_cast<hipStream_t>(stream), view_of(c), tables, max_entries, n_entries,
-                     class_counts, dev_err);
+  const size_t lds = (size_t)(max_entries > 0 ? max_entries : 1) * 4;
+  if (lds > 65536) {  // LDS beyond the default dynamic limit (MI355X: 160 KB per CU)
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&reorder_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "reorder LDS of %zu bytes: %s", lds, hipGetErrorString(e));
+  }
+  hipLaunchKernelGGL(reorder_kernel, dim3(n_tables), dim3(64), lds, static_cast<hipStream_t>(stream), view_of(c),
+                     tables, max_entries, n_entries, class_counts, dev_err);
   return launched("reorder_kernel");
 }
 

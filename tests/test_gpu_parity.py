@@ -465,3 +465,12 @@ def test_slot_map_anchors(fp8):
     _say(f"  slot-map anchors ({'fp8' if fp8 else 'fp16'}): row error {e:.2e}")
     assert e <= TOL
     assert np.allclose(part_lse.cpu().numpy(), ref_lse, atol=1e-3, rtol=1e-4)
+
+
+def test_reorder_and_decode_past_131072_tokens():
+    """A request of 163,840 tokens (a 128K prompt plus 32K generated tokens; 10,240
+    table entries, past the 8,192 a 64 KB LDS stage holds): the reordered table and its
+    class counts bit-exact with the oracle, the decode within the bar."""
+    make = lambda: synth.qwen3_8b(batch=1, n_tokens=163840)  # noqa: E731
+    gpu, orc = _check_case("qwen3_8b 1 x 163840", make, dict(splits_per_head=np.full(8, 24, np.int32)))
+    assert int(gpu.w.alloc.n_entries[0]) == 10240
