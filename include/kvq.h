@@ -164,6 +164,14 @@ kvq_status kvq_tag_tokens(const int32_t *tokens, int32_t n, const kvq_tag_marker
                           int32_t n_markers, uint8_t *tags, int32_t *n_turns);
 
 /*
+ * Token counts per tag [host] (the N_k of TriAxialKV key design 2): adds the
+ * histogram of tags [host] uint8 [n] into counts [host] int64 [KVQ_N_TAGS] (not
+ * cleared: calls over several requests accumulate).  Errors: INVALID_ARG (a tag
+ * >= KVQ_N_TAGS, NULL arrays; nothing is added then).
+ */
+kvq_status kvq_count_tags(const uint8_t *tags, int32_t n, int64_t *counts);
+
+/*
  * Greedy width allocation (TriAxialKV key design 2) [host]: minimise sum_k D_k(b_k)
  * over b_k in {2, 4} subject to sum_k N_k b_k <= budget_bits * sum_k N_k.  Every tag
  * starts at 2 bits; tags with N_k > 0 are visited by decreasing
@@ -222,7 +230,8 @@ kvq_status kvq_quantize_append(const kvq_cache *c, const void *k, const void *v,
  * INT4, then FP16 pages.  class_counts [dev] int32 [n_tables][3] receives the
  * number of pages per class (may be NULL).  The INT2 entries must form aligned
  * pairs after the partition (KVQ_DEVERR_PAIR otherwise; the table is still
- * partitioned).  Errors: INVALID_ARG, UNSUPPORTED (max_entries > 8192), HIP.
+ * partitioned).  Errors: INVALID_ARG, UNSUPPORTED (max_entries > 32768: 524,288
+ * tokens of 16-token pages), HIP.
  */
 kvq_status kvq_reorder_pages(const kvq_cache *c, int32_t *tables, int32_t n_tables,
                              int32_t max_entries, const int32_t *n_entries,

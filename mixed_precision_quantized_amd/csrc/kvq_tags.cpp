@@ -115,6 +115,15 @@ kvq_status kvq_allocate_bits(const double *d2, const double *d4, const int64_t *
   return KVQ_OK;
 }
 
+kvq_status kvq_count_tags(const uint8_t *tags, int32_t n, int64_t *counts) {
+  if (n < 0) return fail(KVQ_ERR_INVALID_ARG, "negative count");
+  if (!counts || (n > 0 && !tags)) return fail(KVQ_ERR_INVALID_ARG, "NULL tags or counts");
+  for (int32_t i = 0; i < n; ++i)
+    if (tags[i] >= KVQ_N_TAGS) return fail(KVQ_ERR_INVALID_ARG, "tag %u at %d outside [0, %d)", tags[i], i, KVQ_N_TAGS);
+  for (int32_t i = 0; i < n; ++i) ++counts[tags[i]];  // N_k, the tokens of each tag
+  return KVQ_OK;
+}
+
 kvq_status kvq_tag_flags(const uint8_t *tags, int32_t n, const uint8_t *bits, int32_t n_tags, uint8_t *flags) {
   if (n < 0 || n_tags < 0) return fail(KVQ_ERR_INVALID_ARG, "negative count");
   if (n > 0 && (!tags || !bits || !flags)) return fail(KVQ_ERR_INVALID_ARG, "NULL tags, bits or flags");

@@ -62,6 +62,7 @@ _SIGS = {
     "kvq_route_tokens": ([_P, _i32, _P, _P, _P, _P], ctypes.c_int),
     "kvq_tag_tokens": ([_P, _i32, _P, _i32, _P, _P], ctypes.c_int),
     "kvq_allocate_bits": ([_P, _P, _P, _i32, ctypes.c_double, _P, _P], ctypes.c_int),
+    "kvq_count_tags": ([_P, _i32, _P], ctypes.c_int),
     "kvq_tag_flags": ([_P, _i32, _P, _i32, _P], ctypes.c_int),
     "kvq_quantize_append": ([_P, _P, _P, _i32, _i64, _i64, _i64, _i32, _P, _P, _i32, _P, _P, _i32, _P, _P,
                              _P, _P], ctypes.c_int),
@@ -188,6 +189,16 @@ def tag_tokens(tokens: np.ndarray, markers):
     _check(_lib.kvq_tag_tokens(_hptr(tokens), tokens.shape[0], ctypes.cast(arr, _P), len(markers), _hptr(tags),
                                ctypes.byref(turns)), "kvq_tag_tokens")
     return tags, turns.value
+
+
+def count_tags(tags: np.ndarray, counts: Optional[np.ndarray] = None) -> np.ndarray:
+    """Adds the tokens per tag of tags (uint8) into counts (int64 [N_TAGS], new if None)."""
+    tags = np.ascontiguousarray(tags, np.uint8)
+    if counts is None:
+        counts = np.zeros(N_TAGS, np.int64)
+    assert counts.dtype == np.int64 and counts.flags.c_contiguous and counts.shape[0] >= N_TAGS
+    _check(_lib.kvq_count_tags(_hptr(tags), tags.shape[0], _hptr(counts)), "kvq_count_tags")
+    return counts
 
 
 def allocate_bits(d2, d4, counts, budget_bits: float):

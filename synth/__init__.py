@@ -171,14 +171,16 @@ class PageAllocator:
         return [(t, h, c, b, e) for h in heads for (c, b, e) in out if e > b]
 
 
-    def ranges_after_partition(self, t, heads):
-        """Token ranges of table t once its entries are stably grouped INT2, INT4,
-        FP16 (the order the phase-1 reorder produces): the caller's record of where
-        its tokens now sit."""
-        order = sorted(range(int(self.n_entries[t])), key=lambda e: self.entry_cls[t][e])
+    def ranges_in_order(self, t, pages, heads):
+        """Token ranges of table t when its entries hold `pages` (page ids, e.g. the
+        table as a reorder left it): the caller's record of where its tokens sit, from
+        the fill it gave each page and the class of each page id."""
+        fill_of = {int(self.tables[t, e]): f for e, f in enumerate(self.fill[t])}
+        n2, n4, _ = self.n_pages
         saved = (self.entry_cls[t], self.fill[t])
-        self.entry_cls[t] = [saved[0][e] for e in order]
-        self.fill[t] = [saved[1][e] for e in order]
+        pages = [int(p) for p in pages]
+        self.entry_cls[t] = [INT2 if p < n2 else INT4 if p < n2 + n4 else FP16 for p in pages]
+        self.fill[t] = [fill_of[p] for p in pages]
         try:
             return self.ranges(t, heads)
         finally:
@@ -226,6 +228,11 @@ class Workload:
     dead_entries: Optional[list] = None  # per table: entry indices redirected to the sentinel
     head_tokens: Optional[np.ndarray] = None  # [n_tables, heads_per_page] tokens read per head
     head_budget: Optional[np.ndarray] = None  # [hkv] retained fraction per KV head (ragged tables)
+    call_spans: Optional[list] = None         # per call with flags None: its token span (c0, c1) in the request
+    streams: Optional[list] = None            # per request (table): AgenticStream whose tags give the flags
+    count_streams: Optional[list] = None      # the streams whose aggregate tag counts fix the widths
+    distortion: Optional[tuple] = None        # (d2, d4) per tag
+    budget_bits: float = 0.0
     note: str = ""
 
     @property
@@ -296,109 +303,131 @@ def qwen3_8b(seed=2, batch=16, n_tokens=32768, device="cpu", frac_int2=0.7, laye
                     note=f"{batch}x{n_tokens} tokens, {frac_int2:.0%} INT2 units")
 
 
-# Tag axes of the agentic workload: temporal (by turn from the end), modal, semantic.
+# Tag axes of the agentic workload (TriAxialKV key design 1): temporal (turns from the
+# end: current, one before, two before, older), modal (text, image), semantic role
+# (inst, user, assistant, reasoning, tool_call, obs, delim).  Tag index =
+# (temporal * N_MODAL + modal) * N_SEMANTIC + semantic.  The tags themselves are read
+# from the token streams by the library and by the oracle, each with its own code.
 N_TEMPORAL, N_MODAL, N_SEMANTIC = 4, 2, 7
-# Synthetic 2-bit distortion weights per axis value (semantic axis dominant, its first
-# value highest); 4-bit distortion is 1/25 of it (a 5x finer step).
+N_TAGS = N_TEMPORAL * N_MODAL * N_SEMANTIC
+# Synthetic distortion table (input data of the width allocation, in place of the
+# offline calibration the page describes): per-axis 2-bit weights, semantic axis
+# dominant and its first value (inst) highest; the 4-bit distortion is 1/25 of it.
 _D_SEM = np.array([8.0, 4.0, 2.0, 1.5, 1.0, 0.7, 0.5])
 _D_MOD = np.array([1.0, 0.6])
 _D_TMP = np.array([4.0, 2.0, 1.3, 1.0])
 
 
-def _temporal_bucket(turns_from_end):
-    return np.select([turns_from_end == 0, turns_from_end <= 2, turns_from_end <= 7], [0, 1, 2], 3)
+def agentic_distortion():
+    """(d2, d4) float64 [N_TAGS] in tag-index order."""
+    d2 = (_D_TMP[:, None, None] * _D_MOD[None, :, None] * _D_SEM[None, None, :]).reshape(-1)
+    return d2, d2 / 25.0
 
 
-def agentic_spans(length, rng):
-    """Per-token tag ids (temporal, modal, semantic) of one synthetic multi-turn
-    context: 12-40 turns of near-equal share, each a run of spans with geometric
-    lengths (mean 300); a span is an image span with probability 0.15."""
+@dataclasses.dataclass
+class AgenticStream:
+    """One request's context as template token ids: tokens int32 [n], markers {token id:
+    event name}, and the rows of tokens generated inside image spans (K, V there carry
+    twice the variance)."""
+    tokens: np.ndarray
+    markers: dict
+    image: np.ndarray        # bool [n]
+
+
+def agentic_conversation(length, rng, vocab=900) -> AgenticStream:
+    """A seeded multi-turn agent context of exactly `length` tokens: a system prompt
+    (tool specifications), then 12-40 turns of near-equal share, each a user message
+    (an image span in 30 % of them), an assistant reply with a think span (70 %) and 0-2
+    tool calls each answered by an observation (20 % with an image), text in runs of
+    geometric length; boundary tokens are ids vocab .. vocab + 10.  Truncated at
+    `length` (a span cut there stays open)."""
+    markers = {vocab + i: e for i, e in enumerate(_STREAM_EVENTS)}
+    mid = {e: vocab + i for i, e in enumerate(_STREAM_EVENTS)}
+    toks, img = [], []
+
+    def mark(name):
+        toks.append(np.array([mid[name]], np.int32))
+        img.append(np.zeros(1, bool))
+
+    def text(n, image=False):
+        n = max(1, int(n))
+        toks.append(rng.integers(0, vocab, n).astype(np.int32))
+        img.append(np.full(n, image))
+
+    def span(name, n, image=False):
+        mark(name + "_begin")
+        text(n, image)
+        mark(name + "_end")
+
     n_turns = int(rng.integers(12, 41))
-    cuts = np.sort(rng.choice(np.arange(1, length), n_turns - 1, replace=False))
-    bounds = np.concatenate([[0], cuts, [length]])
-    tmp = np.empty(length, np.int8)
-    mod = np.empty(length, np.int8)
-    sem = np.empty(length, np.int8)
-    sem_p = np.array([0.05, 0.2, 0.25, 0.15, 0.15, 0.1, 0.1])
-    for i in range(n_turns):
-        a, b = int(bounds[i]), int(bounds[i + 1])
-        tmp[a:b] = _temporal_bucket(np.array(n_turns - 1 - i))
-        pos = a
-        while pos < b:
-            n = min(b - pos, int(rng.geometric(1.0 / 300.0)))
-            mod[pos:pos + n] = 1 if rng.random() < 0.15 else 0
-            sem[pos:pos + n] = rng.choice(N_SEMANTIC, p=sem_p)
-            pos += n
-    return tmp, mod, sem
-
-
-def greedy_bits(counts, budget):
-    """2 / 4 bits per tag: start every tag at 2 bits, walk tags by decreasing
-    rho_k = (D_k(2) - D_k(4)) / (2 N_k) (ties by tag index), upgrade a tag while the
-    average width stays within `budget`, stop at the first that would exceed it.
-    counts: tokens per tag [N_TEMPORAL, N_MODAL, N_SEMANTIC]."""
-    d2 = _D_TMP[:, None, None] * _D_MOD[None, :, None] * _D_SEM[None, None, :]
-    d4 = d2 / 25.0
-    n = counts.astype(np.float64).reshape(-1)
-    bits = np.full(n.shape, 2, np.int8)
-    live = np.nonzero(n > 0)[0]
-    rho = (d2.reshape(-1) - d4.reshape(-1))[live] / (2.0 * n[live])
-    order = live[np.lexsort((live, -rho))]
-    total, used = n.sum(), 2.0 * n.sum()
-    for k in order:
-        if used + 2.0 * n[k] > budget * total:
-            break
-        bits[k] = 4
-        used += 2.0 * n[k]
-    return bits.reshape(counts.shape)
+    share = length / (n_turns + 0.5)
+    mark("system"); text(0.5 * share); mark("end")
+    for _ in range(n_turns):
+        mark("user"); text(rng.geometric(1.0 / (0.18 * share)))
+        if rng.random() < 0.3:
+            span("image", rng.geometric(1.0 / (0.15 * share)), image=True)
+        mark("end")
+        mark("assistant")
+        if rng.random() < 0.7:
+            span("think", rng.geometric(1.0 / (0.2 * share)))
+        text(rng.geometric(1.0 / (0.15 * share)))
+        for _ in range(int(rng.integers(0, 3))):
+            span("tool_call", rng.geometric(1.0 / (0.07 * share)))
+            mark("end")
+            mark("observation"); text(rng.geometric(1.0 / (0.1 * share)))
+            if rng.random() < 0.2:
+                span("image", rng.geometric(1.0 / (0.1 * share)), image=True)
+            mark("end")
+            mark("assistant"); text(rng.geometric(1.0 / (0.05 * share)))
+        mark("end")
+    tokens, image = np.concatenate(toks), np.concatenate(img)
+    while tokens.shape[0] < length:  # a long tail of the last reply
+        tokens = np.concatenate([tokens, rng.integers(0, vocab, length - tokens.shape[0]).astype(np.int32)])
+        image = np.concatenate([image, np.zeros(length - image.shape[0], bool)])
+    return AgenticStream(tokens[:length], markers, image[:length])
 
 
 def qwen3_vl_agentic(seed=3, batch=8, lo=65536, hi=131072, device="cpu", chunk=8192,
                      budget_bits=2.6, layer=0):
     """Qwen3-VL-32B-shaped agentic decode: Hq 64 / Hkv 8 (g = 8), d 128, one page table
-    per request holding all 8 KV heads, contexts uniform in [lo, hi].  Tokens carry
-    tri-axis tags (agentic_spans); one tag -> bits map for the batch comes from
-    greedy_bits on the aggregate tag counts at `budget_bits`; tokens are appended in
-    `chunk`-token calls, so every call leaves its own INT4 residual.  bf16 K, V ~ N(0,1),
-    N(0, 2) (variance) on image spans; bf16 q."""
+    per request holding all 8 KV heads, contexts uniform in [lo, hi].  Each request is a
+    synthetic agent conversation (agentic_conversation) whose tri-axis tags, widths at
+    `budget_bits` (one tag -> width map for the batch, from its aggregate tag counts and
+    the agentic_distortion table) and routing flags are made by the side that runs it;
+    tokens are appended in `chunk`-token calls, so every call leaves its own INT4
+    residual.  bf16 K, V ~ N(0,1), N(0, 2) (variance) on image-span tokens; bf16 q.  Pool
+    sizes are upper bounds (every token INT2, or every token INT4)."""
     hq, hkv, H = 64, 8, 8
     rng = np_rng(seed, 31)
     lens = rng.integers(lo, hi + 1, batch)
-    tags = [agentic_spans(int(n), np_rng(seed, 32, b)) for b, n in enumerate(lens)]
-    counts = np.zeros((N_TEMPORAL, N_MODAL, N_SEMANTIC), np.int64)
-    for tmp, mod, sem in tags:
-        np.add.at(counts, (tmp, mod, sem), 1)
-    bits = greedy_bits(counts, budget_bits)
+    streams = [agentic_conversation(int(n), np_rng(seed, 32, b)) for b, n in enumerate(lens)]
     rows_total = int(lens.sum())
     k = randn((rows_total, H, HEAD_DIM), seed, 33, layer, device=device)
     v = randn((rows_total, H, HEAD_DIM), seed, 34, layer, device=device)
-    calls, n2, n4, row = [], 0, 0, 0
+    calls, spans, n2, n4, row = [], [], 0, 0, 0
     image_rows = []
-    for b, (tmp, mod, sem) in enumerate(tags):
+    for b, st in enumerate(streams):
         n = int(lens[b])
-        flags = np.where(bits[tmp, mod, sem] == 4, INT4, INT2).astype(np.uint8)
-        image_rows.append(row + np.nonzero(mod == 1)[0])
-        n4_tab = 0
+        image_rows.append(row + np.nonzero(st.image)[0])
         for c0 in range(0, n, chunk):
-            f = flags[c0:c0 + chunk]
-            calls.append((b, f, np.arange(row + c0, row + c0 + len(f), dtype=np.int32), False))
-            n_int2 = int((f == INT2).sum())
-            n2 += 2 * (n_int2 // GROUP)
-            n4_tab += len(f) - GROUP * (n_int2 // GROUP)
-        n4 += -(-n4_tab // PAGE)
+            c1 = min(n, c0 + chunk)
+            calls.append((b, None, np.arange(row + c0, row + c1, dtype=np.int32), False))
+            spans.append((c0, c1))
+            n2 += 2 * ((c1 - c0) // GROUP)
+            n4 += -(-(c1 - c0) // PAGE)
         row += n
     img = torch.as_tensor(np.concatenate(image_rows), device=device, dtype=torch.long)
     k[img] *= math.sqrt(2.0)
     v[img] *= math.sqrt(2.0)
     k, v = _bf16(k), _bf16(v)
     q = _bf16(randn((batch, hq, HEAD_DIM), seed, 35, layer, device=device))
-    max_entries = -(-int(hi) // PAGE)  # INT2 groups fill whole page pairs, so ceil(n / 16) entries
+    max_entries = -(-int(hi) // PAGE) + -(-int(hi) // chunk)  # every call may end on a partial INT4 page
     alloc = PageAllocator((n2, n4, 0), H, batch, max_entries, seed)
-    int4_frac = float((counts * (bits == 4)).sum()) / float(counts.sum())
     return Workload("qwen3_vl_agentic", seed, batch, hq, hkv, H, PAGES, torch.bfloat16, torch.bfloat16,
-                    k, v, q, (n2, n4, 0), alloc, calls,
+                    k, v, q, (n2, n4, 0), alloc, calls, call_spans=spans, streams=streams,
+                    count_streams=streams, distortion=agentic_distortion(), budget_bits=budget_bits,
                     note=f"{batch} requests of {int(lens.min())}..{int(lens.max())} tokens, "
-                         f"{int4_frac:.0%} INT4 tags at {budget_bits} bits, {chunk}-token appends")
+                         f"tri-axis tags at {budget_bits} bits, {chunk}-token appends")
 
 
 def hybrid_anchor(seed=4, batch=32, n_tokens=65536, device="cpu", window=128, staging=64,
@@ -509,10 +538,11 @@ def subset(w: Workload, requests, device="cpu") -> Workload:
         return _subset_slots(w, requests, device)
     tpr = w.hkv // w.heads_per_page
     tabs = [b * tpr + i for b in requests for i in range(tpr)]
-    rows, calls, new_calls = [], [], []
-    for (t, flags, r, new_page) in w.calls:
+    rows, calls, new_calls, spans = [], [], [], []
+    for i, (t, flags, r, new_page) in enumerate(w.calls):
         if t in tabs:
             calls.append((tabs.index(t), flags, r, new_page))
+            spans.append(w.call_spans[i] if w.call_spans else None)
     all_rows = np.unique(np.concatenate([c[2] for c in calls]))
     remap = {int(r): i for i, r in enumerate(all_rows.tolist())}
     for (t, flags, r, new_page) in calls:
@@ -523,15 +553,22 @@ def subset(w: Workload, requests, device="cpu") -> Workload:
     q = w.q[torch.as_tensor(list(requests), device=w.q.device)].to(device)
     # Pool sizes: upper bounds from the flags alone (whatever the routing decides).
     n2 = n4 = n16 = 0
-    for (_, flags, _, _) in new_calls:
+    for (_, flags, rws, _) in new_calls:
+        if flags is None:  # flags made by the running side: any split of the call's tokens
+            n2 += 2 * (len(rws) // GROUP)
+            n4 += -(-len(rws) // PAGE) + 1
+            continue
         c0, c1, c2 = (int((flags == c).sum()) for c in (INT2, INT4, FP16))
         n2 += 2 * (c0 // GROUP)
         n4 += -(-(c0 + c1) // PAGE) + 1
         n16 += -(-c2 // PAGE) + 1
     n_pages = (n2, n4, n16)
     alloc = PageAllocator(n_pages, w.heads_per_page, len(tabs), w.alloc.max_entries, w.seed + 1000)
+    extra = {}
+    if w.streams is not None:  # the widths stay those of the whole batch
+        extra = dict(call_spans=spans, streams=[w.streams[b] for b in requests], count_streams=w.count_streams)
     return dataclasses.replace(w, batch=len(requests), k=k, v=v, q=q, n_pages=n_pages, alloc=alloc,
-                               calls=new_calls, note=w.note + f" (requests {list(requests)})")
+                               calls=new_calls, note=w.note + f" (requests {list(requests)})", **extra)
 
 
 def _subset_slots(w: Workload, requests, device="cpu") -> Workload:
@@ -561,12 +598,17 @@ def _subset_slots(w: Workload, requests, device="cpu") -> Workload:
 # turning a routed workload into append lists, tables and ranges
 # ----------------------------------------------------------------------------
 
-def place_all(w: Workload, route_fn):
+def place_all(w: Workload, route_fn, flags=None):
     """Route every append call with route_fn(flags) -> classes and give each token a
-    place.  Returns the append lists of the whole workload (one list set)."""
+    place.  A call without flags of its own takes them from flags[table] (the routing
+    flags the running side made for the request, e.g. from its tags) over its span.
+    Returns the append lists of the whole workload (one list set)."""
     lists = AppendLists()
-    for (t, flags, rows, new_page) in w.calls:
-        classes = route_fn(flags)
+    for i, (t, f, rows, new_page) in enumerate(w.calls):
+        if f is None:
+            c0, c1 = w.call_spans[i]
+            f = np.ascontiguousarray(flags[t][c0:c1], np.uint8)
+        classes = route_fn(f)
         w.alloc.place(t, classes, rows, lists, new_page=new_page)
     return lists
 

@@ -25,14 +25,52 @@ def row_metric(ref: np.ndarray, got: np.ndarray) -> float:
     return worst
 
 
-def _ranges(w, after_reorder: bool):
+def _table_ranges(w, tables):
+    """Token ranges of every (table, head), sorted by (table, head), from a side's own
+    tables (as its reorder left them, or as placed) and the fill the caller gave each
+    page."""
     items = []
     for t in range(w.n_tables):
-        heads = list(range(w.heads_per_page))
-        items += (w.alloc.ranges_after_partition(t, heads) if after_reorder else w.alloc.ranges(t, heads))
-    # sorted by (table, head)
+        n = int(w.alloc.n_entries[t])
+        items += w.alloc.ranges_in_order(t, tables[t, :n], list(range(w.heads_per_page)))
     items.sort(key=lambda it: (it[0], it[1]))
     return synth.ranges_array(items)
+
+
+def library_flags(kvq, w):
+    """Routing flags per request of a tagged workload, made by the library: tri-axis
+    tags (kvq_tag_tokens), tokens per tag over the batch (kvq_count_tags), greedy widths
+    (kvq_allocate_bits), flags (kvq_tag_flags)."""
+    ev = {name: getattr(kvq, "EV_" + name.upper()) for name in synth._STREAM_EVENTS}
+    memo = {}
+
+    def tags_of(st):
+        if id(st) not in memo:
+            memo[id(st)] = kvq.tag_tokens(st.tokens, {t: ev[e] for t, e in st.markers.items()})[0]
+        return memo[id(st)]
+    counts = np.zeros(kvq.N_TAGS, np.int64)
+    for st in w.count_streams:
+        kvq.count_tags(tags_of(st), counts)
+    bits, _ = kvq.allocate_bits(w.distortion[0], w.distortion[1], counts, w.budget_bits)
+    return [kvq.tag_flags(tags_of(st), bits) for st in w.streams]
+
+
+def oracle_flags(w):
+    """The same flags made by the oracle's plain-Python tagger and width allocation."""
+    from oracle import tags as ot
+    memo = {}
+
+    def tags_of(st):
+        if id(st) not in memo:
+            names, _ = ot.tag_tokens(st.tokens.tolist(), st.markers)
+            memo[id(st)] = [ot.tag_index(*x) for x in names]
+        return memo[id(st)]
+    counts = [0] * (len(ot.TEMPORAL) * len(ot.MODAL) * len(ot.SEMANTIC))
+    for st in w.count_streams:
+        for k in tags_of(st):
+            counts[k] += 1
+    bits, _ = ot.allocate_bits(list(w.distortion[0]), list(w.distortion[1]), counts, w.budget_bits)
+    return [np.array([0 if bits[k] == 2 else 1 for k in tags_of(st)], np.uint8) for st in w.streams]
 
 
 class DeviceRun:
@@ -41,7 +79,8 @@ class DeviceRun:
     def __init__(self, w: synth.Workload, device="cuda", reorder=True, compact=False, anchor_fp8=False):
         from mixed_precision_quantized_amd import kvq
         self.kvq, self.w, self.device = kvq, w, device
-        self.lists = synth.place_all(w, lambda f: kvq.route_tokens(f)[0])
+        self.flags = library_flags(kvq, w) if w.streams is not None else None
+        self.lists = synth.place_all(w, lambda f: kvq.route_tokens(f)[0], self.flags)
         self.cache = kvq.Cache(w.heads_per_page, w.n_pages, device, sentinel_slot=w.sentinel_slot,
                                anchor_fp8=anchor_fp8)
         self.err = torch.zeros(1, dtype=torch.int32, device=device)
@@ -69,7 +108,7 @@ class DeviceRun:
             if reorder:
                 kvq.reorder_pages(self.cache, self.tables, self.n_entries, self.class_counts,
                                   dev_err=self.err)
-            self.ranges = _ranges(w, after_reorder=reorder)
+            self.ranges = _table_ranges(w, self.tables.cpu().numpy())
         else:
             self.tables = torch.as_tensor(synth.slot_tables(w), device=device).contiguous()
             self.reordered = False
@@ -134,7 +173,8 @@ class OracleRun:
     def __init__(self, w: synth.Workload, reorder=True, compact=False, anchor_fp8=False):
         from oracle import oracle
         self.orc, self.w = oracle, w
-        self.lists = synth.place_all(w, lambda f: oracle.route(f)[0])
+        self.flags = oracle_flags(w) if w.streams is not None else None
+        self.lists = synth.place_all(w, lambda f: oracle.route(f)[0], self.flags)
         self.cache = oracle.Cache(w.heads_per_page, *w.n_pages, sentinel_slot=w.sentinel_slot,
                                   anchor_fp8=anchor_fp8)
         k, v, dt = _host_rows(w)
@@ -147,10 +187,10 @@ class OracleRun:
         if w.kind == synth.PAGES:
             self.tables = w.alloc.tables.copy()
             self.class_counts = None
-            self.ranges_before = _ranges(w, after_reorder=False)
+            self.ranges_before = _table_ranges(w, self.tables)
             if reorder:
                 self.class_counts = self.cache.reorder(self.tables, w.alloc.n_entries)
-            self.ranges = _ranges(w, after_reorder=reorder)
+            self.ranges = _table_ranges(w, self.tables)
             self.kind = oracle.PAGES
         else:
             self.tables = synth.slot_tables(w)

@@ -5,41 +5,49 @@ import synth
 from oracle import oracle
 
 
-def _counts(entries):
-    c = np.zeros((synth.N_TEMPORAL, synth.N_MODAL, synth.N_SEMANTIC), np.int64)
-    for (t, m, s), n in entries.items():
-        c[t, m, s] = n
-    return c
-
-
-def test_greedy_bits_walks_rho_order_and_stops_at_the_first_misfit():
-    # rho = 0.96 D(2) / (2 N): A = 32/20, C = 16/160, B = 0.3/20, so the walk is A, C, B.
-    A, B, C = (0, 0, 0), (3, 1, 6), (0, 0, 1)
-    counts = _counts({A: 10, B: 10, C: 80})
-    bits = synth.greedy_bits(counts, 2.6)       # 200 + 20 (A) fits 260, C would give 380
-    assert bits[A] == 4 and bits[C] == 2 and bits[B] == 2   # B would fit but the walk stopped
-    bits = synth.greedy_bits(counts, 3.9)       # A and C fit 390, B would give 400
-    assert bits[A] == 4 and bits[C] == 4 and bits[B] == 2
-    bits = synth.greedy_bits(counts, 4.0)
-    assert (bits[counts > 0] == 4).all()
-    assert (synth.greedy_bits(counts, 2.0)[counts > 0] == 2).all()
-
-
-def test_agentic_recipe():
+def test_agentic_recipe_and_both_sides_make_the_same_flags():
+    """The agentic workload is token streams (ids, template boundary ids, image-span rows)
+    and a distortion table; the library (kvq_tag_tokens, kvq_count_tags,
+    kvq_allocate_bits, kvq_tag_flags) and the oracle (oracle/tags.py) each turn them into
+    routing flags, and the two agree token for token."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from harness import library_flags, oracle_flags
+    from mixed_precision_quantized_amd import kvq
     w = synth.qwen3_vl_agentic(batch=2, lo=9000, hi=12000, chunk=4096)
     assert w.g == 8 and w.heads_per_page == 8 and w.n_tables == 2
-    total = sum(len(c[1]) for c in w.calls)
-    int4 = sum(int((c[1] == synth.INT4).sum()) for c in w.calls)
-    assert 0.2 < int4 / total < 0.4                      # about 30 % INT4 at 2.6 bits
-    for (t, flags, rows, _) in w.calls:
-        assert len(flags) <= 4096
-        classes = oracle.route(flags)[0]
-        # every call leaves fewer than 32 INT2-flagged tokens to its INT4 residual
-        assert int((flags == synth.INT2).sum()) - int((classes == synth.INT2).sum()) < 32
-    # pools hold what placement needs
-    lists = synth.place_all(w, lambda f: oracle.route(f)[0])
+    assert len(w.streams) == 2 and w.count_streams is w.streams
+    rows = {b: 0 for b in range(2)}
+    for (t, flags, r, _), (c0, c1) in zip(w.calls, w.call_spans):
+        assert flags is None and c1 - c0 == len(r) <= 4096 and c0 == rows[t]
+        rows[t] = c1
+    for b, st in enumerate(w.streams):
+        assert st.tokens.dtype == np.int32 and st.tokens.shape[0] == rows[b] == st.image.shape[0]
+        assert set(st.markers) == set(range(900, 911)) and 0 < st.image.mean() < 0.3
+    lib, orc = library_flags(kvq, w), oracle_flags(w)
+    assert all(np.array_equal(x, y) for x, y in zip(lib, orc))
+    int4 = sum(int(f.sum()) for f in orc) / sum(len(f) for f in orc)
+    assert 0.2 < int4 <= 0.3 + 1e-9                       # at most (2.6 - 2) / 2 upgraded
+    lists = synth.place_all(w, lambda f: oracle.route(f)[0], orc)
     assert len(lists.rows2) == 32 * len(lists.pages2)
     assert int(w.alloc.n_entries.max()) <= w.alloc.max_entries
+    # every call leaves fewer than 32 INT2-flagged tokens to its INT4 residual
+    for (t, _, r, _), (c0, c1) in zip(w.calls, w.call_spans):
+        f = orc[t][c0:c1]
+        assert int((f == 0).sum()) - int((oracle.route(f)[0] == synth.INT2).sum()) < 32
+
+
+def test_subset_keeps_the_batch_widths():
+    """A sampled request of the agentic workload keeps the widths of the whole batch
+    (its flags are the full workload's flags for that request)."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from harness import oracle_flags
+    w = synth.qwen3_vl_agentic(batch=3, lo=3000, hi=5000, chunk=2048)
+    sub = synth.subset(synth.qwen3_vl_agentic(batch=3, lo=3000, hi=5000, chunk=2048), [1])
+    assert np.array_equal(oracle_flags(sub)[0], oracle_flags(w)[1])
 
 
 def _oracle_rows(w, requests=None):
@@ -54,6 +62,7 @@ def test_subset_reproduces_the_sampled_requests():
     """Full-size parity samples requests through subset(): the oracle on the subset must
     equal the oracle on the whole workload for those requests (page and slot maps)."""
     for make, req in ((lambda: synth.qwen3_8b(batch=3, n_tokens=1024), [0, 2]),
+                      (lambda: synth.qwen3_vl_agentic(batch=3, lo=2000, hi=3000, chunk=1024), [1]),
                       (lambda: synth.ragged_dead(batch=4, lo=512, hi=4096), [1, 3]),
                       (lambda: synth.hybrid_anchor(batch=2, n_tokens=2048), [1])):
         full_o, full_l = _oracle_rows(make(), req)

@@ -103,3 +103,15 @@ def test_library_widths_and_flags_match_the_oracle():
         assert np.array_equal(flags, np.array([0 if ref[t] == 2 else 1 for t in tags], np.uint8))
     with pytest.raises(kvq.KvqError):
         kvq.allocate_bits([1.0], [0.0], [5], 4.5)
+
+
+def test_count_tags_accumulates_a_histogram():
+    from mixed_precision_quantized_amd import kvq
+    r = np.random.default_rng(4)
+    a, b = r.integers(0, 56, 1000).astype(np.uint8), r.integers(0, 56, 77).astype(np.uint8)
+    c = kvq.count_tags(a)
+    kvq.count_tags(b, c)
+    assert np.array_equal(c, np.bincount(np.concatenate([a, b]), minlength=56))
+    with pytest.raises(kvq.KvqError):
+        kvq.count_tags(np.array([3, 56], np.uint8), c)
+    assert np.array_equal(c, np.bincount(np.concatenate([a, b]), minlength=56))  # nothing added
