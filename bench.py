@@ -185,6 +185,11 @@ def main():
             sys.exit("--ordered-pages applies to the qwen3_8b workload only")
         make = functools.partial(make, ordered_pages=True)
     layers = args.layers or default_layers
+    base_make = make
+
+    def make(**kw):  # page tables get room for one decode step's INT4 tail page per table
+        w = base_make(**kw)
+        return synth.reserve_tail(w, synth.PAGE) if w.kind == synth.PAGES else w
     dev = "cuda"
     torch.cuda.set_device(0)
     t0 = time.time()
@@ -216,6 +221,22 @@ def main():
         caches.append(cache)
         qs.append(w.q.contiguous())
         del w
+    # One decode step's tail append per layer: a new token per table, placed INT4 at the
+    # table's tail (the reordered table's last INT4 page where it has room, else a fresh
+    # page) and written by kvq_quantize_append.  The decode's ranges stay those of the
+    # prefix: the append is timed beside the step, not inside it.
+    tail_app = []
+    if w0.kind == synth.PAGES:
+        tl = synth.AppendLists()
+        tabs = gpu.tables.cpu().numpy()
+        for t in range(w0.n_tables):
+            n = int(w0.alloc.n_entries[t])
+            w0.alloc.append_tail(t, int(tabs[t, n - 1]) if n else None, [t], tl)
+        ta = tl.arrays()
+        r4, s4 = (torch.as_tensor(ta[x], device=dev) for x in ("rows4", "slots4"))
+        for L in range(layers):
+            tk, tv, _ = synth.tail_rows(w0, L, 1, device=dev)
+            tail_app.append((tk, tv))
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     cost = None if args.class_cost is None else [float(x) for x in args.class_cost.split(",")]
@@ -260,6 +281,12 @@ def main():
         return d, m
 
     dec, mrg = bound(stream)
+    app = [kvq.bind_quantize_append(caches[L], tk, tv, rows4=r4, slots4=s4, dev_err=gpu.err, stream=stream)
+           for L, (tk, tv) in enumerate(tail_app)]
+
+    def appends():
+        for a in app:
+            a()
 
     def step():
         for L in range(layers):
@@ -285,7 +312,11 @@ def main():
     with torch.cuda.stream(stream):
         step()  # first launches (code objects load) outside any capture
     torch.cuda.synchronize()
-    run_step, run_decodes = step, decodes
+    run_step, run_decodes, run_appends = step, decodes, (appends if app else None)
+    if app:
+        with torch.cuda.stream(stream):
+            appends()  # first launch outside any capture
+        torch.cuda.synchronize()
     if not args.eager:
         # The step as one HIP graph (the 2 x layers launches, no allocation, no memset),
         # and the decode launches alone for the kernel's own duration.  Each replay of
@@ -296,6 +327,11 @@ def main():
             step()
         with torch.cuda.graph(g_dec, stream=stream):
             decodes()
+        g_app = None
+        if app:
+            g_app = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_app, stream=stream):
+                appends()
         torch.cuda.synchronize()
         for _ in range(3):
             for o in outs:
@@ -315,6 +351,7 @@ def main():
             torch.cuda.synchronize()
         assert int(gpu.err.item()) == 0
         run_step, run_decodes = g_step.replay, g_dec.replay
+        run_appends = g_app.replay if g_app is not None else None
         log("step captured as a HIP graph of the decode + merge launches; 3 replays equal to eager"
             + (" (to bf16 rounding: shared windows sum in another order)" if shared else ""))
 
@@ -340,6 +377,9 @@ def main():
     # the average launch duration is the span over the number of launches.
     us_decode = timed(run_decodes, args.steps) * 1e6 / layers
     achieved = decode_bytes / (us_decode * 1e-6) / 1e9
+    us_append = timed(run_appends, args.steps) * 1e6 / layers if run_appends else None
+    if us_append is not None:
+        log(f"decode-time tail append {us_append:.1f} us per layer ({w0.n_tables} tokens, one per table)")
     log(f"step {ms_step * 1000:.1f} us ({ms_step * 1000 / layers:.1f} us per layer)")
     log(f"decode kernel {us_decode:.1f} us per launch ({layers} x {args.steps} back-to-back launches), "
         f"{achieved:.0f} GB/s algorithmic")
@@ -361,6 +401,7 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "us_per_step": round(ms_step * 1000, 1),
         "us_per_layer": round(ms_step * 1000 / layers, 2),
+        "append_us_per_layer": None if us_append is None else round(us_append, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",

@@ -544,6 +544,20 @@ def bind_decode_attn_shared(cache: Cache, q: torch.Tensor, hkv: int, tables: tor
                      keep=(cache, q, tables, workers, groups, work, part_o, part_lse, dev_err))
 
 
+def bind_quantize_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, rows4=None, slots4=None,
+                         rows2=None, pages2=None, rows16=None, slots16=None, dev_err=None,
+                         stream=None) -> BoundCall:
+    assert k.shape == v.shape and k.stride() == v.stride() and k.dtype == v.dtype
+    assert k.shape[-1] == HEAD_DIM and k.stride(-1) == 1
+    n = lambda t: 0 if t is None else int(t.numel())  # noqa: E731
+    head_stride = k.stride(1) if k.dim() == 3 else HEAD_DIM
+    args = (cache.struct, _dptr(k), _dptr(v), _DTYPES[k.dtype], k.shape[0], k.stride(0), head_stride,
+            n(rows4), _dptr(rows4), _dptr(slots4), n(pages2), _dptr(rows2), _dptr(pages2),
+            n(rows16), _dptr(rows16), _dptr(slots16), _dptr(dev_err), _stream(stream))
+    return BoundCall("kvq_quantize_append", args,
+                     keep=(cache, k, v, rows4, slots4, rows2, pages2, rows16, slots16, dev_err))
+
+
 def bind_lse_merge(part_o, part_lse, n_splits, split_offsets, batch, hq, hkv, out, out_lse=None,
                    stream=None) -> BoundCall:
     args = (_dptr(part_o), _dptr(part_lse), n_splits, _dptr(split_offsets), batch, hq, hkv, _dptr(out),

@@ -98,6 +98,7 @@ class PageAllocator:
             self.free4.sort(reverse=True)
             self.free16.sort(reverse=True)
         self.reserved4 = list(range(n2, n2 + reserve_int4))
+        self.ordered = ordered
         self.max_entries = max_entries
         self.tables = np.full((n_tables, max_entries), -1, dtype=np.int32)
         self.n_entries = np.zeros(n_tables, dtype=np.int32)
@@ -170,6 +171,27 @@ class PageAllocator:
             out.append((cls_run, start, end))
         return [(t, h, c, b, e) for h in heads for (c, b, e) in out if e > b]
 
+
+    def append_tail(self, t, last_page, rows, lists: AppendLists):
+        """Place decode-time tokens of table t as INT4 at the table's tail: into its
+        last entry while that is an INT4 page with room (last_page: the page id the
+        caller's table ends with now, e.g. as a reorder left it), then into fresh INT4
+        pages pushed at the end of the table.  Returns the page ids pushed, in order."""
+        n2, n4, _ = self.n_pages
+        e = None
+        if last_page is not None and n2 <= last_page < n2 + n4:
+            e = int(np.flatnonzero(self.tables[t, :self.n_entries[t]] == last_page)[0])
+        pushed = []
+        for row in np.asarray(rows).tolist():
+            if e is None or self.fill[t][e] == PAGE:
+                p = int(self.free4.pop())
+                e = self._push(t, p, INT4, 0)
+                pushed.append(p)
+            lists.rows4.append(row)
+            lists.slots4.append(int(self.tables[t, e]) * PAGE + self.fill[t][e])
+            self.fill[t][e] += 1
+            self.tokens[t, INT4] += 1
+        return pushed
 
     def ranges_in_order(self, t, pages, heads):
         """Token ranges of table t when its entries hold `pages` (page ids, e.g. the
@@ -592,6 +614,30 @@ def _subset_slots(w: Workload, requests, device="cpu") -> Workload:
                                dead_entries=[w.dead_entries[t] for t in tabs],
                                head_tokens=w.head_tokens[tabs].copy(),
                                note=w.note + f" (requests {list(requests)})")
+
+
+def reserve_tail(w: Workload, tail_tokens) -> Workload:
+    """The same page-table workload with room for `tail_tokens` decode-time tokens per
+    table: INT4 pool and table width grown by the pages they may open (a fresh
+    allocator, so placement is redone from the start by whoever runs it)."""
+    assert w.kind == PAGES
+    extra = -(-int(tail_tokens) // PAGE)
+    n2, n4, n16 = w.n_pages
+    n_pages = (n2, n4 + extra * w.n_tables, n16)
+    alloc = PageAllocator(n_pages, w.heads_per_page, w.n_tables, w.alloc.max_entries + extra, w.seed,
+                          ordered=w.alloc.ordered)
+    return dataclasses.replace(w, n_pages=n_pages, alloc=alloc)
+
+
+def tail_rows(w: Workload, step, n_new, device="cpu"):
+    """Source rows of one decode step: `n_new` new tokens per table (rows t * n_new + i,
+    all heads of the table) and the step's query.  K, V ~ N(0,1) and q ~ N(0,1) in the
+    workload's dtypes, seeded by the step."""
+    rows = w.n_tables * n_new
+    k = randn((rows, w.heads_per_page, HEAD_DIM), w.seed, 91, step, device=device).to(w.src_dtype)
+    v = randn((rows, w.heads_per_page, HEAD_DIM), w.seed, 92, step, device=device).to(w.src_dtype)
+    q = randn((w.batch, w.hq, HEAD_DIM), w.seed, 93, step, device=device).to(w.q_dtype)
+    return k, v, q
 
 
 # ----------------------------------------------------------------------------

@@ -121,6 +121,29 @@ class DeviceRun:
             else:
                 self.ranges = synth.slot_ranges(w)
 
+    def append_tail(self, k, v, q=None):
+        """One decode step's new tokens (k, v: n_new rows per table, rows t * n_new + i):
+        placed as INT4 at each table's tail (the table as this side's reorder left it),
+        written by kvq_quantize_append; the tables gain the pages the tail opened and
+        the ranges are taken again from them.  q, if given, is the step's query."""
+        w, kvq, dev = self.w, self.kvq, self.device
+        n_new = k.shape[0] // w.n_tables
+        tabs = self.tables.cpu().numpy()
+        lists = synth.AppendLists()
+        for t in range(w.n_tables):
+            n = int(w.alloc.n_entries[t])
+            pushed = w.alloc.append_tail(t, int(tabs[t, n - 1]) if n else None,
+                                         np.arange(t * n_new, (t + 1) * n_new), lists)
+            tabs[t, n:n + len(pushed)] = pushed
+        a = lists.arrays()
+        kvq.quantize_append(self.cache, k.to(dev), v.to(dev), rows4=torch.as_tensor(a["rows4"], device=dev),
+                            slots4=torch.as_tensor(a["slots4"], device=dev), dev_err=self.err)
+        self.tables.copy_(torch.as_tensor(tabs))
+        self.ranges = _table_ranges(w, tabs)
+        if q is not None:
+            self.q = q.to(dev).contiguous()
+        return a
+
     def plan(self, **kw):
         w = self.w
         return self.kvq.plan_splits(self.ranges, w.batch, w.hkv, w.heads_per_page, **kw)
@@ -204,6 +227,25 @@ class OracleRun:
             else:
                 self.ranges = synth.slot_ranges(w)
 
+    def append_tail(self, k, v, q=None):
+        """The same decode step on the oracle: its own tail placement on its own
+        tables, its own append."""
+        w = self.w
+        n_new = k.shape[0] // w.n_tables
+        lists = synth.AppendLists()
+        for t in range(w.n_tables):
+            n = int(w.alloc.n_entries[t])
+            pushed = w.alloc.append_tail(t, int(self.tables[t, n - 1]) if n else None,
+                                         np.arange(t * n_new, (t + 1) * n_new), lists)
+            self.tables[t, n:n + len(pushed)] = pushed
+        a = lists.arrays()
+        kh, vh, dt = _host_pair(k, v)
+        self.cache.append(kh, vh, dt, w.heads_per_page * 128, 128, rows4=a["rows4"], slots4=a["slots4"])
+        self.ranges = _table_ranges(w, self.tables)
+        if q is not None:
+            self.q = q.float().cpu().numpy()
+        return a
+
     def attend(self, n_threads=8):
         w = self.w
         return self.cache.attend(self.q, w.batch, w.hq, w.hkv, self.tables, self.kind, self.ranges,
@@ -212,8 +254,12 @@ class OracleRun:
 
 def _host_rows(w):
     """Source rows as host numpy arrays plus the oracle dtype code (bf16 as uint16 bits)."""
-    if w.src_dtype == torch.bfloat16:
-        k = w.k.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-        v = w.v.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-        return k, v, 1
-    return w.k.float().cpu().contiguous().numpy(), w.v.float().cpu().contiguous().numpy(), 0
+    return _host_pair(w.k, w.v)
+
+
+def _host_pair(k, v):
+    if k.dtype == torch.bfloat16:
+        kh = k.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        vh = v.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        return kh, vh, 1
+    return k.float().cpu().contiguous().numpy(), v.float().cpu().contiguous().numpy(), 0

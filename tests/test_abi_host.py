@@ -141,7 +141,7 @@ def test_validation_fails_before_any_launch(kvq):
                                    None, 0, None, None, None, None) == -1       # bad dtype
     assert lib.kvq_quantize_append(ctypes.byref(c), fake, fake, 0, 1, 128, 128, 3, None, None, 0, None,
                                    None, 0, None, None, None, None) == -1       # NULL list
-    assert lib.kvq_reorder_pages(ctypes.byref(c), fake, 1, 9000, fake, None, None, None) == -2
+    assert lib.kvq_reorder_pages(ctypes.byref(c), fake, 1, 32769, fake, None, None, None) == -2
     assert lib.kvq_lse_merge(fake, fake, 1, fake, 1, 8, 3, fake, 0, None, None) == -1
     assert lib.kvq_lse_merge(fake, fake, 1, fake, 1, 8, 8, fake, 9, None, None) == -1
     assert b"dtype" in lib.kvq_last_error()

@@ -75,3 +75,47 @@ def test_ragged_lengths_match_the_workload():
     lens = synth.ragged_lengths(batch=6, lo=512, hi=4096)
     tl = w.head_tokens.reshape(6, -1).max(axis=1)
     assert np.array_equal(tl, np.ceil(lens * 1.0).astype(np.int64))
+
+
+def test_tail_append_placement():
+    """Decode-time tokens go INT4 at each table's tail: a table that ends on a partly
+    filled INT4 page continues it, then fresh INT4 pages are pushed at the end; every
+    token gets a slot no other token holds, and each head's ranges grow by exactly the
+    new tokens, all of them INT4."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from harness import OracleRun
+    steps = (1, 17, 40)
+    w = synth.reserve_tail(synth.qwen3_vl_agentic(batch=2, lo=9000, hi=12000, chunk=4096), sum(steps))
+    orc = OracleRun(w)
+    n2, n4, _ = w.n_pages
+
+    def per_head(r):
+        out = {}
+        for x in r:
+            key = (int(x["table"]), int(x["head"]), int(x["cls"]))
+            out[key] = out.get(key, 0) + int(x["tok_end"] - x["tok_begin"])
+        return out
+    before = per_head(orc.ranges)
+    used = set(orc.lists.arrays()["slots4"].tolist())
+    last = [int(orc.tables[t, w.alloc.n_entries[t] - 1]) for t in range(w.n_tables)]
+    fill_last = [w.alloc.fill[t][int(np.flatnonzero(w.alloc.tables[t] == p)[0])] for t, p in enumerate(last)]
+    assert any(n2 <= p < n2 + n4 and f < synth.PAGE for p, f in zip(last, fill_last))
+    for i, n_new in enumerate(steps):
+        k, v, q = synth.tail_rows(w, i, n_new)
+        assert k.shape == (w.n_tables * n_new, w.heads_per_page, 128) and q.shape == (w.batch, w.hq, 128)
+        a = orc.append_tail(k, v, q)
+        assert np.array_equal(a["rows4"], np.arange(w.n_tables * n_new))
+        pages = a["slots4"] // synth.PAGE
+        assert ((pages >= n2) & (pages < n2 + n4)).all()
+        assert not used & set(a["slots4"].tolist())
+        used |= set(a["slots4"].tolist())
+        if i == 0:  # the first new token continues the table's last page where it has room
+            for t in range(w.n_tables):
+                p, f = last[t], fill_last[t]
+                if n2 <= p < n2 + n4 and f < synth.PAGE:
+                    assert a["slots4"][t] == p * synth.PAGE + f
+    after = per_head(orc.ranges)
+    for key, n in after.items():
+        assert n - before.get(key, 0) == (sum(steps) if key[2] == synth.INT4 else 0)
