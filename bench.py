@@ -109,7 +109,8 @@ def measured_traffic(path=None, files=("kvq_decode.hip", "kvq_internal.h")):
 
 def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_plan="aot"):
     """One work group per split, as many splits as the decode kernel keeps resident at
-    once (a second, partial round would leave most of the chip idle).  Ragged slot maps
+    once (a second, partial round would leave most of the chip idle); with FP16 pages,
+    one round of each of the two kernels (kvq_plan_splits_per_kernel).  Ragged slot maps
     share the count among heads in proportion to their budgets (Tangram AOT), or, with
     ragged_plan="tokens", so that no piece holds more tokens than it must for the count
     to fit (balanced split counts over the tokens each head reads)."""
@@ -117,6 +118,15 @@ def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_pl
     w = gpu.w
     kind = kvq.TABLE_SLOTS if w.kind == synth.SLOTS else kvq.TABLE_PAGES
     per_cu, n_cu = kvq.decode_occupancy(w.g, kind)
+    if not splits_per_head and w.kind == synth.PAGES and w.n_pages[2]:
+        # FP16 pages: the INT2 / INT4 splits and the FP16 splits run in two kernels; each
+        # kernel gets one resident round of its own
+        per16, _ = kvq.decode_fp16_occupancy(w.g, gpu.cache.anchor_fp8)
+        heads = w.batch * w.hkv
+        splits, offsets = kvq.plan_splits_per_kernel(gpu.ranges, w.batch, w.hkv, w.heads_per_page,
+                                                     max(1, per_cu * n_cu // heads), max(1, per16 * n_cu // heads),
+                                                     class_cost)
+        return splits, offsets, per_cu, n_cu
     if splits_per_head:
         sph = np.full(w.batch * w.hkv, splits_per_head, np.int32)
     elif w.head_tokens is not None and ragged_plan == "tokens":
@@ -128,6 +138,66 @@ def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_pl
         sph = np.full(w.batch * w.hkv, max(1, (per_cu * n_cu) // (w.batch * w.hkv)), np.int32)
     splits, offsets = gpu.plan(splits_per_head=sph, class_cost=class_cost)
     return splits, offsets, per_cu, n_cu
+
+
+def cpu_info():
+    """(CPU model name, processors online, processors this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, allowed
+
+
+def cpu_baseline(cpu_sample, w0, args, make):
+    """The oracle's decode timed on the host: whole passes over a sample of the layer
+    for at least CPU_SECONDS, on all the cores this process may use (at most 16, the
+    host share of one GPU) and on one thread over a smaller sample."""
+    import synth
+    from harness import OracleRun
+
+    def leg(sample, n_threads):
+        orc = OracleRun(sample, anchor_fp8=args.anchor_fp8)
+        reps, t = 0, time.perf_counter()
+        while True:
+            orc.attend(n_threads=n_threads)
+            reps += 1
+            dt = time.perf_counter() - t
+            if dt >= CPU_SECONDS:
+                break
+        nbytes, _ = effective_bytes(sample, anchor_fp8=args.anchor_fp8)
+        return round(nbytes * reps / dt / 1e9, 3), reps, dt
+
+    model, online, allowed = cpu_info()
+    n_threads = min(16, allowed)
+    multi, reps, dt = leg(cpu_sample, n_threads)
+    one_req = list(range(max(1, cpu_sample.batch // 8)))
+    single, reps1, dt1 = leg(synth.subset(make(device="cuda", layer=0), one_req, device="cpu"), 1)
+    log(f"cpu oracle {multi} GB/s on {n_threads} threads ({dt:.1f} s), {single} GB/s on 1 thread ({dt1:.1f} s); "
+        f"{model}, {online} processors online, {allowed} allowed")
+    return {
+        "value": multi,
+        "unit": "GB/s",
+        "cores": n_threads,
+        "kind": "oracle",
+        "sample": f"{cpu_sample.batch} of {w0.batch} requests of one layer (all {w0.hkv} KV heads, "
+                  f"g = {w0.g}), fp64 two-pass softmax, {reps} passes in {dt:.1f} s",
+        "single_thread": {"value": single, "unit": "GB/s", "cores": 1,
+                          "sample": f"{len(one_req)} of {w0.batch} requests of one layer, {reps1} passes in "
+                                    f"{dt1:.1f} s"},
+        "cpu_model": model,
+        "nproc": online,
+        "affinity": allowed,
+    }
 
 
 def main():
@@ -431,30 +501,8 @@ def main():
     }
 
     if cpu_sample is not None:
-        from harness import OracleRun
-        try:
-            n_threads = min(16, len(os.sched_getaffinity(0)))
-        except AttributeError:
-            n_threads = min(16, os.cpu_count() or 1)
-        orc = OracleRun(cpu_sample, anchor_fp8=args.anchor_fp8)
-        reps, t = 0, time.perf_counter()
-        while True:  # whole passes over the sample until CPU_SECONDS have gone by
-            orc.attend(n_threads=n_threads)
-            reps += 1
-            dt = time.perf_counter() - t
-            if dt >= CPU_SECONDS:
-                break
-        sample_bytes, _ = effective_bytes(cpu_sample, anchor_fp8=args.anchor_fp8)
-        result["cpu_baseline"] = {
-            "value": round(sample_bytes * reps / dt / 1e9, 3),
-            "unit": "GB/s",
-            "cores": n_threads,
-            "kind": "oracle",
-            "sample": f"{cpu_sample.batch} of {w0.batch} requests of one layer (all {w0.hkv} KV heads, "
-                      f"g = {w0.g}), fp64 two-pass softmax, {reps} passes in {dt:.1f} s",
-        }
-        log(f"cpu oracle {result['cpu_baseline']['value']} GB/s on {n_threads} threads ({dt:.1f} s)")
-    print(json.dumps(result), flush=True)
+        result["cpu_baseline"] = cpu_baseline(cpu_sample, w0, args, make)
+        print(json.dumps(result), flush=True)
 
 
 def bench_vl(args):

@@ -449,9 +449,9 @@ kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, int32_t n_s
  *     pieces per (table, head), shared among its non-empty ranges in proportion
  *     to their decode cost, tokens x class_cost[cls] (class_cost [host, may be
  *     NULL]: float [3] per INT2 / INT4 / FP16 token-head, all > 0; NULL =
- *     1.0 / 1.0 / 8.0: an FP16 token-head costs its kernel about 6x an INT4 one
- *     on MI355X, and the extra weight gives the anchors' kernel more, shorter
- *     splits to run in parallel after the INT2 / INT4 kernel), at
+ *     1.0 / 1.0 / 6.0: FP16 splits run in their own kernel after the INT2 /
+ *     INT4 one, one wave per SIMD, and the weight gives them about one round
+ *     of that kernel at the hybrid-anchor shape), at
  *     least one each, largest remainders first, so a head gets exactly its count
  *     whenever that is at least its number of non-empty ranges;
  *   tokens_per_split[cls] > 0 [host, may be NULL]: ceil(tokens / that);
@@ -468,6 +468,26 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
                            const int32_t *tokens_per_split, int64_t target_bytes,
                            kvq_split *out, int32_t max_out, int32_t *n_out,
                            int32_t *split_offsets);
+
+/*
+ * Split plan per decode kernel [host] (TriAxialKV key design 4; Tangram steps 6-7):
+ * the splits of a page-table launch run in two kernels, INT2 / INT4 splits in one
+ * and FP16 splits in the other, each best sized to one resident round of its own
+ * (kvq_decode_occupancy, kvq_decode_fp16_occupancy).  ranges, outputs and errors
+ * as for kvq_plan_splits; per (table, head) i:
+ *   int_splits [host] int32 [n_tables*heads_per_page]: pieces shared among its
+ *     INT2 / INT4 ranges in proportion to tokens x class_cost[cls];
+ *   fp16_splits [host] int32 [n_tables*heads_per_page]: pieces shared among its
+ *     FP16 ranges in proportion to tokens;
+ * at least one piece per non-empty range, largest remainders first.
+ * class_cost [host, may be NULL]: as for kvq_plan_splits.
+ */
+kvq_status kvq_plan_splits_per_kernel(const kvq_split *ranges, int32_t n_ranges,
+                                      int32_t batch, int32_t hkv, int32_t heads_per_page,
+                                      const int32_t *int_splits, const int32_t *fp16_splits,
+                                      const float *class_cost, kvq_split *out,
+                                      int32_t max_out, int32_t *n_out,
+                                      int32_t *split_offsets);
 
 /*
  * Shared-work plan [host] for kvq_decode_attn_shared.  ranges as for
@@ -541,6 +561,15 @@ kvq_status kvq_head_group_plan(const float *budgets, int32_t hkv, int32_t heads_
  * Errors: INVALID_ARG, NO_DEVICE, HIP.
  */
 kvq_status kvq_decode_occupancy(int32_t g, int32_t table_kind, int32_t *per_cu, int32_t *n_cu);
+
+/*
+ * Work groups of the kernel that runs the FP16 splits of a page-table
+ * kvq_decode_attn on the current device (as kvq_decode_occupancy): g and the
+ * cache's anchor_format (KVQ_ANCHOR_FP16 / KVQ_ANCHOR_FP8) select it.
+ * Errors: INVALID_ARG, NO_DEVICE, HIP.
+ */
+kvq_status kvq_decode_fp16_occupancy(int32_t g, int32_t anchor_format, int32_t *per_cu,
+                                     int32_t *n_cu);
 
 /* Text of a status code, and a description of this thread's last error. */
 const char *kvq_status_string(int32_t status);

@@ -797,10 +797,12 @@ template <int CLS, int W>
 struct RingGeom {
   // Copies per window, each from one page block (see RingLoader::issue):
   // INT4: K codes x2, V codes x2, metadata x2 (half-wave each); INT2: the first KB of
-  // each page, then the last 512 B of each page (half-wave each).
-  static constexpr int kChunks = CLS == KVQ_INT4 ? 6 : 4;
-  static constexpr int kSlotBytes = CLS == KVQ_INT4 ? 5120 : 3072;
-  static constexpr int kSlots = ring_bytes<W>() / kSlotBytes;
+  // each page, then the last 512 B of each page (half-wave each); FP16 (one wave, its
+  // own kernel with a 32 KB ring): K x4 and V x4 per page.
+  static constexpr int kChunks = CLS == KVQ_INT4 ? 6 : CLS == KVQ_INT2 ? 4 : 16;
+  static constexpr int kSlotBytes = CLS == KVQ_INT4 ? 5120 : CLS == KVQ_INT2 ? 3072 : 16384;
+  static constexpr int kRingBytes = CLS == KVQ_FP16 ? 2 * 16384 : ring_bytes<W>();
+  static constexpr int kSlots = kRingBytes / kSlotBytes;
   // Windows copied ahead of the one computed.  One wave refills a slot as soon as its
   // window sits in registers, so every slot is in flight during a compute; with
   // several waves the slot refilled is the previous window's, which the block barrier
@@ -892,6 +894,10 @@ struct RingLoader {
       voff[0] = kI4KC + lr * 64 + lb * 16;                                 // K codes, reader-lane order
       voff[1] = kI4VC + lane * 16;                                         // V codes, natural
       voff[2] = (lane & 15) * 16 + ((lane >> 4) & 1 ? kI4VM : kI4KM);     // K meta | V meta
+    } else if (CLS == KVQ_FP16) {
+      voff[0] = kF16K + lr * 256 + lb * 64;                                // K rows, reader-lane order
+      voff[1] = kF16V + lane * 16;                                         // V rows, natural
+      voff[2] = 0;
     } else {
       voff[0] = lane * 16;                                                 // bytes 0 .. 1023
       voff[1] = 1024 + (lane & 31) * 16;                                   // bytes 1024 .. 1535
@@ -930,6 +936,13 @@ struct RingLoader {
         case 4: if (lane < 32) dma_block(base + 4096, b0, vo[2]); break;
         default: if (lane >= 32) dma_block(base + 4096, b1, vo[2]); break;
       }
+    } else if (CLS == KVQ_FP16) {
+      // chunk c: region c / 4 (K of page half 0, K of half 1, V of half 0, V of half 1),
+      // part c % 4 (K: channels 8 (c % 4) + 32 lb .. + 7 of every token; V: tokens
+      // 4 (c % 4) .. + 3)
+      const int r = c >> 2, m = c & 3;
+      const gbytes b = (r & 1) ? b1 : b0;
+      dma_block(base + 1024 * c, r < 2 ? b + 16 * m : b + 1024 * m, r < 2 ? vo[0] : vo[1]);
     } else {
       switch (c) {
         case 0: dma_block(base, b0, vo[0]); break;
@@ -992,6 +1005,16 @@ struct RingLoader {
       const uint8_t *VM = M + 512 * (lb >> 1) + 256 + ((lr & 3) * kPage + o0) * 4;
       w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
       w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
+    } else if (CLS == KVQ_FP16) {
+      // [K A][K B] (chunk m of a half: lane L's 16 B of the reader lane L), [V A][V B]
+      // (token rows of 256 B)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w.k[h][m] = *reinterpret_cast<const uint4 *>(S + 4096 * h + 1024 * m + 16 * lane);
+      const uint8_t *V = S + 8192 + 4096 * (lb >> 1) + 256 * o0 + 16 * lr;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w.v[q] = *reinterpret_cast<const uint4 *>(V + 256 * q);
     } else {
       // Page P's bytes 0 .. 1023 at 1024 P, its bytes 1024 .. 1535 at 2048 + 512 P.
       auto at = [S](int P, int byte) { return byte < 1024 ? S + 1024 * P + byte : S + 2048 + 512 * P + (byte - 1024); };
@@ -1458,11 +1481,23 @@ __device__ bool split_prologue(const DecodeArgs &a, int s_idx, kvq_split &sp, Ld
   return true;
 }
 
+// The split block b runs.  With FP16 pages a plan's splits go to two launches, and each
+// launch's blocks of the other kind return at once.  Block b goes to XCD b mod 8, so in
+// plan order (a fixed class pattern per (table, head)) the splits a launch runs can
+// fall unevenly on the XCDs; instead the blocks of XCD x take the x-th eighth of the
+// plan, in order, which holds its even share of every class.
+__device__ __forceinline__ int split_of_block(const DecodeArgs &a) {
+  const int b = (int)blockIdx.x;
+  if (a.n16 == 0) return b;
+  const int q = a.n_splits >> 3, r = a.n_splits & 7, x = b & 7;
+  return x * q + min(x, r) + (b >> 3);
+}
+
 // Register-staged kernel: slot-map mode (all classes), and FP16 splits in page mode.
 template <int QT, bool SLOTS>
 __global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
   __shared__ Lds<QT> L;
-  const int s_idx = blockIdx.x;
+  const int s_idx = split_of_block(a);
   kvq_split sp;
   if (!split_prologue<QT, SLOTS, false>(a, s_idx, sp, L)) return;
   if (sp.cls == KVQ_INT4) run_split<QT, KVQ_INT4, SLOTS>(a, sp, s_idx, L);
@@ -1485,7 +1520,7 @@ decode_ring_kernel(DecodeArgs a) {
   // issues its oldest waves first, so in worker order the early requests' groups would
   // hold the oldest waves everywhere and end first; spread, every group's workers span
   // all ages.
-  const int s_idx = SHARED ? (int)(((uint64_t)blockIdx.x * 2147483647ull) % (uint64_t)a.n_splits) : (int)blockIdx.x;
+  const int s_idx = SHARED ? (int)(((uint64_t)blockIdx.x * 2147483647ull) % (uint64_t)a.n_splits) : split_of_block(a);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   kvq_split sp;
   if (SHARED) {
@@ -1510,6 +1545,22 @@ decode_ring_kernel(DecodeArgs a) {
   else if (sp.cls == KVQ_INT2) run_split_ring<KVQ_INT2, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
 }
 
+// LDS-staged kernel for the FP16 splits of a page-table launch (FP16 anchors, g <= 8):
+// a 32 KB ring of two 16 KB windows per wave, one wave per SIMD; the FP16 window has
+// no unpacking, so one wave's compute keeps ahead of its copies.
+template <int QT>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
+decode_anchor_ring_kernel(DecodeArgs a) {
+  __shared__ Lds<QT> L;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RingGeom<KVQ_FP16, 1>::kRingBytes];
+  __shared__ __attribute__((aligned(16))) int32_t idr[16];
+  const int s_idx = split_of_block(a);
+  kvq_split sp;
+  // (a.only_fp16 is set: this kernel takes the FP16 splits, the other one the rest)
+  if (!split_check<QT, false, false>(a, s_idx, sp, 0)) return;
+  run_split_ring<KVQ_FP16, 1, QT>(a, sp, s_idx, L, ring, idr, 0);
+}
+
 // LDS-staged kernel for slot maps (INT4 splits, g <= 8).
 template <int QT>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 2)))
@@ -1517,7 +1568,7 @@ decode_slots_ring_kernel(DecodeArgs a) {
   __shared__ Lds<QT> L;
   __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes<1>()];
   __shared__ __attribute__((aligned(16))) int32_t id_blocks[SlotRingLoader::kIdBlocks * 32];
-  const int s_idx = blockIdx.x;
+  const int s_idx = split_of_block(a);
   kvq_split sp;
   if (!split_prologue<QT, true, true>(a, s_idx, sp, L)) return;
   if (sp.cls == KVQ_INT4) run_split_slots_ring<QT>(a, sp, s_idx, L, ring, id_blocks);
@@ -1659,12 +1710,18 @@ kvq_status decode_setup(DecodeArgs &a, const kvq_cache *c, const void *q, int32_
   return KVQ_OK;
 }
 
-// The register-staged kernel for the FP16 splits of a page-table launch (when the cache
-// has FP16 pages; the LDS-staged kernel leaves them).
+// The kernel for the FP16 splits of a page-table launch (when the cache has FP16 pages;
+// the INT2 / INT4 kernel leaves them): LDS-staged for FP16 anchors up to g = 8,
+// register-staged for FP8 anchors and g = 16.
 kvq_status launch_fp16_pages(DecodeArgs a, hipStream_t s) {
   if (a.n16 == 0) return KVQ_OK;
   a.only_fp16 = 1;
   const dim3 grid(a.n_splits), block(64);
+  if (!a.fp8 && a.g <= 8) {
+    if (a.g <= 4) hipLaunchKernelGGL((decode_anchor_ring_kernel<1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_anchor_ring_kernel<2>), grid, block, 0, s, a);
+    return launched("decode_anchor_ring_kernel");
+  }
   if (a.g <= 4) hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, s, a);
   else if (a.g <= 8) hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, s, a);
@@ -1843,6 +1900,32 @@ extern "C" kvq_status kvq_decode_occupancy(int32_t g, int32_t table_kind, int32_
   else
     e = slots ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, true>, 64, 0)
               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_ring_kernel<2, 2, false>, 128, 0);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(KVQ_ERR_HIP, "CU count query failed");
+  *per_cu = blocks;
+  *n_cu = cus;
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_decode_fp16_occupancy(int32_t g, int32_t anchor_format, int32_t *per_cu, int32_t *n_cu) {
+  if (!per_cu || !n_cu || g < 1 || g > kMaxG || (anchor_format != KVQ_ANCHOR_FP16 && anchor_format != KVQ_ANCHOR_FP8))
+    return fail(KVQ_ERR_INVALID_ARG, "bad occupancy query");
+  int dev = 0, count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count == 0) return fail(KVQ_ERR_NO_DEVICE, "no HIP device");
+  if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_NO_DEVICE, "hipGetDevice failed");
+  int blocks = 0, cus = 0;
+  hipError_t e;
+  if (anchor_format == KVQ_ANCHOR_FP16 && g <= 4)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_anchor_ring_kernel<1>, 64, 0);
+  else if (anchor_format == KVQ_ANCHOR_FP16 && g <= 8)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_anchor_ring_kernel<2>, 64, 0);
+  else if (g <= 4)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<1, false>, 64, 0);
+  else if (g <= 8)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<2, false>, 64, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, false>, 64, 0);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(KVQ_ERR_HIP, "CU count query failed");

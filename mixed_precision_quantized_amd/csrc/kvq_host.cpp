@@ -51,14 +51,106 @@ static int64_t token_bytes(int cls) { return cls == KVQ_INT2 ? 96 : cls == KVQ_I
 // head's split count among its ranges.  INT2 windows are bound by dequantization work
 // and INT4 ones by their bytes, which takes about as long per token (measured: a
 // weight of 1.0 for INT4 beat 0.8 and 1.15-1.8); FP16 windows move 512 B per token and
-// run in their own, register-staged kernel after the others (measured on the
-// hybrid-anchor decode: 8.0 gave 600 us per layer against 617-618 us for 4.0 and 6.0,
-// 654 us for 16.0).
-static const float kDefaultTokenCost[3] = {1.0f, 1.0f, 8.0f};
+// run in their own kernel after the others, one wave per SIMD (measured on the
+// hybrid-anchor decode at 12 splits per head: 6.0 gave 557 us per layer against 575 us
+// for 8.0 and 606 us for 12.0: four FP16 splits per head, one resident round).
+static const float kDefaultTokenCost[3] = {1.0f, 1.0f, 6.0f};
 
 }  // namespace kvq
 
 using namespace kvq;
+
+namespace {
+
+// Checks a plan's ranges: well formed, INT2 ranges on 32-token boundaries, sorted by
+// (table, head).
+kvq_status check_ranges(const kvq_split *ranges, int32_t n_ranges, int32_t n_tables, int32_t heads_per_page) {
+  for (int32_t i = 0; i < n_ranges; ++i) {
+    const kvq_split &r = ranges[i];
+    if (r.table < 0 || r.table >= n_tables || r.head < 0 || r.head >= heads_per_page || r.cls < 0 ||
+        r.cls > 2 || r.tok_begin < 0 || r.tok_end < r.tok_begin)
+      return fail(KVQ_ERR_INVALID_ARG, "malformed range %d", i);
+    if (r.cls == KVQ_INT2 && (r.tok_begin % kGroup || r.tok_end % kGroup))
+      return fail(KVQ_ERR_INVALID_ARG, "INT2 range %d is not on 32-token boundaries", i);
+    if (i > 0) {
+      const kvq_split &p = ranges[i - 1];
+      if (p.table > r.table || (p.table == r.table && p.head > r.head))
+        return fail(KVQ_ERR_INVALID_ARG, "ranges are not sorted by (table, head) at %d", i);
+    }
+  }
+  return KVQ_OK;
+}
+
+// Shares `total` pieces among the non-empty ranges i0 .. i1 - 1 that `take` accepts, in
+// proportion to tokens x cost[cls]: one piece each, the rest by largest remainders, so
+// the shares add up to `total` whenever it is at least the number of ranges.
+template <typename Take>
+void share_pieces(const kvq_split *ranges, int32_t i0, int32_t i1, int64_t total, const float *cost, Take take,
+                  std::vector<int64_t> &pieces) {
+  double cost_sum = 0.0;
+  int32_t n_live = 0;
+  for (int32_t i = i0; i < i1; ++i) {
+    const int64_t toks = ranges[i].tok_end - ranges[i].tok_begin;
+    if (toks == 0 || !take(ranges[i])) continue;
+    ++n_live;
+    cost_sum += (double)toks * (double)cost[ranges[i].cls];
+  }
+  if (n_live == 0) return;
+  const int64_t spare = std::max<int64_t>(0, total - n_live);  // beyond one piece each
+  std::vector<std::pair<double, int32_t>> frac;
+  int64_t given = 0;
+  for (int32_t i = i0; i < i1; ++i) {
+    const int64_t toks = ranges[i].tok_end - ranges[i].tok_begin;
+    if (toks == 0 || !take(ranges[i])) continue;
+    const double share = (double)spare * (double)toks * (double)cost[ranges[i].cls] / cost_sum;
+    const int64_t whole = (int64_t)std::floor(share);
+    pieces[i] = 1 + whole;
+    given += whole;
+    frac.push_back({share - (double)whole, i});
+  }
+  std::stable_sort(frac.begin(), frac.end(),
+                   [](const std::pair<double, int32_t> &x, const std::pair<double, int32_t> &y) {
+                     return x.first > y.first;
+                   });
+  for (size_t k = 0; given < spare && k < frac.size(); ++k, ++given) ++pieces[frac[k].second];
+}
+
+// Cuts every range into its number of near-equal pieces (INT2 pieces on 32-token
+// boundaries) and writes the splits and the merge offsets.
+kvq_status emit_plan(const kvq_split *ranges, int32_t n_ranges, int32_t batch, int32_t hkv, int32_t heads_per_page,
+                     const std::vector<int64_t> &pieces, kvq_split *out, int32_t max_out, int32_t *n_out,
+                     int32_t *split_offsets) {
+  const int32_t tpr = hkv / heads_per_page;
+  int32_t w = 0;
+  int32_t next_pair = 0;  // next (b*hkv + kvh) whose offset is still unset
+  for (int32_t i = 0; i < n_ranges; ++i) {
+    const kvq_split &r = ranges[i];
+    const int32_t pair = (r.table / tpr) * hkv + (r.table % tpr) * heads_per_page + r.head;
+    while (next_pair <= pair) split_offsets[next_pair++] = w;
+    const int32_t unit = r.cls == KVQ_INT2 ? kGroup : 1;
+    const int64_t units = (r.tok_end - r.tok_begin) / unit;
+    if (units == 0) continue;
+    const int64_t n = std::min(pieces[i], units);
+    for (int64_t p = 0; p < n; ++p) {
+      if (w >= max_out) return fail(KVQ_ERR_CAPACITY, "more than %d splits", max_out);
+      const int64_t a = units * p / n, b = units * (p + 1) / n;
+      out[w++] = kvq_split{r.table, r.head, r.cls, (int32_t)(r.tok_begin + a * unit),
+                           p + 1 == n ? r.tok_end : (int32_t)(r.tok_begin + b * unit)};
+    }
+  }
+  while (next_pair <= batch * hkv) split_offsets[next_pair++] = w;
+  *n_out = w;
+  return KVQ_OK;
+}
+
+// The ranges of one (table, head): i0 .. i1 - 1.
+int32_t head_end(const kvq_split *ranges, int32_t n_ranges, int32_t i0) {
+  int32_t i1 = i0 + 1;
+  while (i1 < n_ranges && ranges[i1].table == ranges[i0].table && ranges[i1].head == ranges[i0].head) ++i1;
+  return i1;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -114,60 +206,20 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
   const float *cost = class_cost ? class_cost : kDefaultTokenCost;
   for (int c = 0; c < 3; ++c)
     if (!(cost[c] > 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "class cost %d is not positive", c);
-  auto token_cost = [cost](int cls) { return (double)cost[cls]; };
   if (n_ranges < 0 || batch < 0 || hkv <= 0 || heads_per_page <= 0 || hkv % heads_per_page)
     return fail(KVQ_ERR_INVALID_ARG, "bad plan shape");
   if ((n_ranges > 0 && !ranges) || !n_out || !split_offsets || (max_out > 0 && !out))
     return fail(KVQ_ERR_INVALID_ARG, "NULL plan array");
-  const int32_t tpr = hkv / heads_per_page;
-  const int32_t n_tables = batch * tpr;
-  for (int32_t i = 0; i < n_ranges; ++i) {
-    const kvq_split &r = ranges[i];
-    if (r.table < 0 || r.table >= n_tables || r.head < 0 || r.head >= heads_per_page || r.cls < 0 ||
-        r.cls > 2 || r.tok_begin < 0 || r.tok_end < r.tok_begin)
-      return fail(KVQ_ERR_INVALID_ARG, "malformed range %d", i);
-    if (r.cls == KVQ_INT2 && (r.tok_begin % kGroup || r.tok_end % kGroup))
-      return fail(KVQ_ERR_INVALID_ARG, "INT2 range %d is not on 32-token boundaries", i);
-    if (i > 0) {
-      const kvq_split &p = ranges[i - 1];
-      if (p.table > r.table || (p.table == r.table && p.head > r.head))
-        return fail(KVQ_ERR_INVALID_ARG, "ranges are not sorted by (table, head) at %d", i);
-    }
-  }
+  const int32_t n_tables = batch * (hkv / heads_per_page);
+  kvq_status st = check_ranges(ranges, n_ranges, n_tables, heads_per_page);
+  if (st != KVQ_OK) return st;
   // Pieces per range.
   std::vector<int64_t> pieces((size_t)n_ranges, 0);
   for (int32_t i0 = 0, i1; i0 < n_ranges; i0 = i1) {
-    i1 = i0 + 1;
-    while (i1 < n_ranges && ranges[i1].table == ranges[i0].table && ranges[i1].head == ranges[i0].head) ++i1;
+    i1 = head_end(ranges, n_ranges, i0);
     if (splits_per_head) {
-      // Share the head's count in proportion to decode cost (largest remainders, so
-      // the shares add up to the count when it is at least the number of ranges).
-      const int64_t total = splits_per_head[(size_t)ranges[i0].table * heads_per_page + ranges[i0].head];
-      double cost_sum = 0.0;
-      int32_t n_live = 0;
-      for (int32_t i = i0; i < i1; ++i) {
-        const int64_t toks = ranges[i].tok_end - ranges[i].tok_begin;
-        if (toks > 0) ++n_live;
-        cost_sum += (double)toks * token_cost(ranges[i].cls);
-      }
-      if (n_live == 0) continue;
-      const int64_t spare = std::max<int64_t>(0, total - n_live);  // beyond one piece each
-      std::vector<std::pair<double, int32_t>> frac;
-      int64_t given = 0;
-      for (int32_t i = i0; i < i1; ++i) {
-        const int64_t toks = ranges[i].tok_end - ranges[i].tok_begin;
-        if (toks == 0) continue;
-        const double share = (double)spare * (double)toks * token_cost(ranges[i].cls) / cost_sum;
-        const int64_t whole = (int64_t)std::floor(share);
-        pieces[i] = 1 + whole;
-        given += whole;
-        frac.push_back({share - (double)whole, i});
-      }
-      std::stable_sort(frac.begin(), frac.end(),
-                       [](const std::pair<double, int32_t> &x, const std::pair<double, int32_t> &y) {
-                         return x.first > y.first;
-                       });
-      for (size_t k = 0; given < spare && k < frac.size(); ++k, ++given) ++pieces[frac[k].second];
+      share_pieces(ranges, i0, i1, splits_per_head[(size_t)ranges[i0].table * heads_per_page + ranges[i0].head],
+                   cost, [](const kvq_split &) { return true; }, pieces);
     } else {
       for (int32_t i = i0; i < i1; ++i) {
         const kvq_split &r = ranges[i];
@@ -182,26 +234,34 @@ kvq_status kvq_plan_splits(const kvq_split *ranges, int32_t n_ranges, int32_t ba
       }
     }
   }
-  int32_t w = 0;
-  int32_t next_pair = 0;  // next (b*hkv + kvh) whose offset is still unset
-  for (int32_t i = 0; i < n_ranges; ++i) {
-    const kvq_split &r = ranges[i];
-    const int32_t pair = (r.table / tpr) * hkv + (r.table % tpr) * heads_per_page + r.head;
-    while (next_pair <= pair) split_offsets[next_pair++] = w;
-    const int32_t unit = r.cls == KVQ_INT2 ? kGroup : 1;
-    const int64_t units = (r.tok_end - r.tok_begin) / unit;
-    if (units == 0) continue;
-    const int64_t n = std::min(pieces[i], units);
-    for (int64_t p = 0; p < n; ++p) {
-      if (w >= max_out) return fail(KVQ_ERR_CAPACITY, "more than %d splits", max_out);
-      const int64_t a = units * p / n, b = units * (p + 1) / n;
-      out[w++] = kvq_split{r.table, r.head, r.cls, (int32_t)(r.tok_begin + a * unit),
-                           p + 1 == n ? r.tok_end : (int32_t)(r.tok_begin + b * unit)};
-    }
+  return emit_plan(ranges, n_ranges, batch, hkv, heads_per_page, pieces, out, max_out, n_out, split_offsets);
+}
+
+kvq_status kvq_plan_splits_per_kernel(const kvq_split *ranges, int32_t n_ranges, int32_t batch, int32_t hkv,
+                                      int32_t heads_per_page, const int32_t *int_splits,
+                                      const int32_t *fp16_splits, const float *class_cost, kvq_split *out,
+                                      int32_t max_out, int32_t *n_out, int32_t *split_offsets) {
+  const float *cost = class_cost ? class_cost : kDefaultTokenCost;
+  for (int c = 0; c < 3; ++c)
+    if (!(cost[c] > 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "class cost %d is not positive", c);
+  if (n_ranges < 0 || batch < 0 || hkv <= 0 || heads_per_page <= 0 || hkv % heads_per_page)
+    return fail(KVQ_ERR_INVALID_ARG, "bad plan shape");
+  if ((n_ranges > 0 && (!ranges || !int_splits || !fp16_splits)) || !n_out || !split_offsets ||
+      (max_out > 0 && !out))
+    return fail(KVQ_ERR_INVALID_ARG, "NULL plan array");
+  const int32_t n_tables = batch * (hkv / heads_per_page);
+  kvq_status st = check_ranges(ranges, n_ranges, n_tables, heads_per_page);
+  if (st != KVQ_OK) return st;
+  std::vector<int64_t> pieces((size_t)n_ranges, 0);
+  for (int32_t i0 = 0, i1; i0 < n_ranges; i0 = i1) {
+    i1 = head_end(ranges, n_ranges, i0);
+    const size_t h = (size_t)ranges[i0].table * heads_per_page + ranges[i0].head;
+    share_pieces(ranges, i0, i1, int_splits[h], cost, [](const kvq_split &r) { return r.cls != KVQ_FP16; },
+                 pieces);
+    share_pieces(ranges, i0, i1, fp16_splits[h], cost, [](const kvq_split &r) { return r.cls == KVQ_FP16; },
+                 pieces);
   }
-  while (next_pair <= batch * hkv) split_offsets[next_pair++] = w;
-  *n_out = w;
-  return KVQ_OK;
+  return emit_plan(ranges, n_ranges, batch, hkv, heads_per_page, pieces, out, max_out, n_out, split_offsets);
 }
 
 // Shared-work plan: every range is a group whose windows its workers share; a head's

@@ -23,6 +23,7 @@ LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(HERE, "libkvq.so")
 INT2, INT4, FP16 = 0, 1, 2
 F32, BF16, F16 = 0, 1, 2
 TABLE_PAGES, TABLE_SLOTS = 0, 1
+ANCHOR_FP16, ANCHOR_FP8 = 0, 1  # kvq_cache.anchor_format
 DEVERR_ID, DEVERR_RANGE, DEVERR_PAIR, DEVERR_SPLIT = 1, 2, 4, 8
 HEAD_DIM = 128
 FP8_ANCHOR_BLOCK = 3   # kvq_block_bytes class of an FP8 anchor block
@@ -88,6 +89,8 @@ _SIGS = {
     "kvq_aot_split_counts": ([_P, _i32, _i32, _i32, _P], ctypes.c_int),
     "kvq_balanced_split_counts": ([_P, _i32, _i32, _P], ctypes.c_int),
     "kvq_decode_occupancy": ([_i32, _i32, _P, _P], ctypes.c_int),
+    "kvq_decode_fp16_occupancy": ([_i32, _i32, _P, _P], ctypes.c_int),
+    "kvq_plan_splits_per_kernel": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _i32, _P, _P], ctypes.c_int),
     "kvq_head_group_plan": ([_P, _i32, _i32, _i64, _i32, _P, _P, _P], ctypes.c_int),
     "kvq_status_string": ([_i32], ctypes.c_char_p),
     "kvq_last_error": ([], ctypes.c_char_p),
@@ -151,7 +154,7 @@ class Cache:
             self._c.n_pages[i] = self.n_pages[i]
             self._c.pool[i] = self.pools[i].data_ptr()
         self._c.sentinel_slot = self.sentinel_slot
-        self._c.anchor_format = 1 if self.anchor_fp8 else 0
+        self._c.anchor_format = ANCHOR_FP8 if self.anchor_fp8 else ANCHOR_FP16
 
     @property
     def struct(self):
@@ -439,6 +442,28 @@ def plan_splits(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int,
     return out[: n_out.value].copy(), offsets
 
 
+def plan_splits_per_kernel(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int,
+                           int_splits: np.ndarray, fp16_splits: np.ndarray, class_cost=None,
+                           max_out: Optional[int] = None):
+    """ranges as for plan_splits; int_splits / fp16_splits int32 [n_tables*heads_per_page]:
+    pieces per (table, head) for its INT2 / INT4 ranges and for its FP16 ranges.
+    Returns (splits int32 [n_out, 5], split_offsets int32 [batch*hkv + 1])."""
+    r = np.ascontiguousarray(np.asarray(ranges).view(np.int32).reshape(-1, 5))
+    n_heads = batch * hkv
+    ints = np.ascontiguousarray(np.broadcast_to(np.asarray(int_splits, np.int32), (n_heads,)))
+    fp16 = np.ascontiguousarray(np.broadcast_to(np.asarray(fp16_splits, np.int32), (n_heads,)))
+    if max_out is None:
+        max_out = max(1, int(ints.sum()) + int(fp16.sum()) + len(r))
+    out = np.zeros((max_out, 5), np.int32)
+    offsets = np.zeros(batch * hkv + 1, np.int32)
+    n_out = _i32()
+    cc = None if class_cost is None else np.ascontiguousarray(class_cost, np.float32)
+    _check(_lib.kvq_plan_splits_per_kernel(_hptr(r), r.shape[0], batch, hkv, heads_per_page, _hptr(ints),
+                                           _hptr(fp16), _hptr(cc), _hptr(out), max_out, ctypes.byref(n_out),
+                                           _hptr(offsets)), "kvq_plan_splits_per_kernel")
+    return out[: n_out.value].copy(), offsets
+
+
 def plan_workers(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int, workers_per_head: np.ndarray,
                  class_cost=None):
     """ranges as for plan_splits.  Returns (workers int32 [n, 5], groups int32 [n], n_groups,
@@ -492,6 +517,13 @@ def decode_occupancy(g: int, table_kind: int = 0):
     per_cu, n_cu = _i32(), _i32()
     _check(_lib.kvq_decode_occupancy(g, table_kind, ctypes.byref(per_cu), ctypes.byref(n_cu)),
            "kvq_decode_occupancy")
+    return per_cu.value, n_cu.value
+
+
+def decode_fp16_occupancy(g: int, anchor_fp8: bool = False):
+    per_cu, n_cu = _i32(), _i32()
+    _check(_lib.kvq_decode_fp16_occupancy(g, ANCHOR_FP8 if anchor_fp8 else ANCHOR_FP16, ctypes.byref(per_cu),
+                                          ctypes.byref(n_cu)), "kvq_decode_fp16_occupancy")
     return per_cu.value, n_cu.value
 
 

@@ -161,6 +161,32 @@ def test_plan_splits_class_cost_shares_a_head_count(kvq):
         kvq.plan_splits(rng, 1, 1, 1, splits_per_head=sph, class_cost=[1.0, 0.0, 1.0])
 
 
+def test_plan_splits_per_kernel(kvq):
+    """Per (table, head): the INT2 / INT4 ranges share int_splits by tokens x cost and
+    the FP16 ranges share fp16_splits by tokens, each at least one piece per range;
+    every range covered exactly once; with no FP16 range it is kvq_plan_splits."""
+    items = [(0, 0, 1, 0, 6000), (0, 0, 2, 6000, 6320), (0, 0, 2, 6336, 6400),       # INT4, VL, window
+             (0, 1, 0, 0, 640), (0, 1, 1, 640, 960), (0, 1, 2, 960, 1000)]
+    rng = _ranges(items, kvq)
+    s, off = kvq.plan_splits_per_kernel(rng, 1, 2, 2, np.array([5, 9], np.int32), np.array([3, 2], np.int32),
+                                        class_cost=[1.0, 1.0, 1.0])
+    count = lambda h, c: int(((s[:, 1] == h) & (s[:, 2] == c)).sum())  # noqa: E731
+    assert count(0, 1) == 5 and count(0, 2) == 3          # 320 + 64 FP16 tokens: 1 + 2 * 320 / 384 -> 2 + 1
+    assert [len(s[(s[:, 1] == 0) & (s[:, 3] >= 6000) & (s[:, 4] <= 6320)]),
+            len(s[(s[:, 1] == 0) & (s[:, 3] >= 6336)])] == [2, 1]
+    assert count(1, 0) == 6 and count(1, 1) == 3 and count(1, 2) == 2   # 640 / 320 INT2 / INT4; one FP16 range
+    for (t, h, c, b, e) in items:
+        mine = s[(s[:, 1] == h) & (s[:, 2] == c) & (s[:, 3] >= b) & (s[:, 4] <= e)]
+        assert mine[0, 3] == b and mine[-1, 4] == e and np.all(mine[1:, 3] == mine[:-1, 4])
+    assert off.tolist() == [0, 8, 8 + 11]
+    no16 = _ranges([it for it in items if it[2] != 2], kvq)
+    a, oa = kvq.plan_splits_per_kernel(no16, 1, 2, 2, np.array([5, 9], np.int32), np.array([3, 2], np.int32))
+    b, ob = kvq.plan_splits(no16, 1, 2, 2, splits_per_head=np.array([5, 9], np.int32))
+    assert np.array_equal(a, b) and np.array_equal(oa, ob)
+    with pytest.raises(kvq.KvqError):
+        kvq.plan_splits_per_kernel(_ranges([(0, 0, 0, 0, 40)], kvq), 1, 1, 1, [1], [1])
+
+
 def test_balanced_split_counts_minimal_cap(kvq):
     """Counts fit the work groups, and no smaller cap on one piece's work would."""
     r = np.random.default_rng(8)

@@ -263,6 +263,11 @@ def _resident_plan(gpu, ragged_plan="aot"):
     "tokens") by balanced split counts over the tokens each head reads."""
     w = gpu.w
     per_cu, n_cu = gpu.kvq.decode_occupancy(w.g, gpu.kvq.TABLE_SLOTS if w.kind == synth.SLOTS else 0)
+    if w.kind == synth.PAGES and w.n_pages[2]:  # one round of each of the two kernels
+        per16, _ = gpu.kvq.decode_fp16_occupancy(w.g, gpu.cache.anchor_fp8)
+        heads = w.batch * w.hkv
+        return gpu.kvq.plan_splits_per_kernel(gpu.ranges, w.batch, w.hkv, w.heads_per_page,
+                                              max(1, per_cu * n_cu // heads), max(1, per16 * n_cu // heads))
     if w.head_tokens is not None and ragged_plan == "tokens":
         read = w.head_tokens if gpu.live_tokens is None else gpu.live_tokens.cpu().numpy()
         return gpu.plan(splits_per_head=gpu.kvq.balanced_split_counts(read, per_cu * n_cu))
