@@ -502,7 +502,7 @@ def main():
 
     if cpu_sample is not None:
         result["cpu_baseline"] = cpu_baseline(cpu_sample, w0, args, make)
-        print(json.dumps(result), flush=True)
+    print(json.dumps(result), flush=True)
 
 
 def bench_vl(args):
