@@ -1051,8 +1051,8 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
   // Window i is copied into slot i mod kSlots, A windows ahead of its compute; the page
   // ids of window i are copied into id slot i mod kIdSlots another A windows earlier
   // (before the copies of window i - A, so they have landed when those have).
-  constexpr int kIdSlots = 8;
-  static_assert(A < kIdSlots, "id ring too small");
+  constexpr int kIdSlots = 8;  // ids of windows n + A .. n + 2A are live; the first A go to slots A .. 2A - 1
+  static_assert(2 * A <= kIdSlots, "id ring too small");
   uint32_t okq = 0;  // validity bits of the windows in flight, 2 per window, newest lowest
 #pragma unroll
   for (int i = 0; i < A; ++i) {
@@ -1186,8 +1186,8 @@ __device__ void run_shared_ring(const DecodeArgs &a, const kvq_split &sp, int s_
   constexpr int C = G::chunks_of(0);  // data copies per window (plus one id copy)
   constexpr int kWin = 16;            // window-start ring: window i at i % kWin
   static_assert(4 * S <= kWin, "window ring too small");
-  constexpr int kIdSlots = 8;
-  static_assert(A < kIdSlots, "id ring too small");
+  constexpr int kIdSlots = 8;  // ids of windows n + A .. n + 2A are live; the first A go to slots A .. 2A - 1
+  static_assert(2 * A <= kIdSlots, "id ring too small");
   RingLoader<CLS, 1> ld(a, sp, ring, idr, 0);
   const int lane = lane_id();
   const int32_t T0 = sp.tok_begin & ~15;
