@@ -187,8 +187,11 @@ struct ClassPages {
 
 template <int QT>
 struct Lds {
-  float q[4 * QT][kHeadDim];         // queries (rows beyond g are zero)
-  _Float16 p[QT][4][32];             // softmax weights of the current 32 tokens
+  _Float16 q[4 * QT][kHeadDim];      // queries, rounded to fp16 (rows beyond g are zero)
+  _Float16 zero[32];                 // zeros: the off-diagonal blocks of the query operand
+  // softmax weights of the current 32 tokens: [query tile][query][token] for one tile;
+  // for two tiles [query][token] over 16 rows (rows 8-15 zero: the weights operand)
+  _Float16 p[QT == 2 ? 1 : QT][QT == 2 ? 16 : 4][32];
 };
 
 // ------------------------------------------------------------- per window -----
@@ -226,11 +229,15 @@ struct Loader {
   const ClassPages<CLS> pages;
   int32_t e_first, e_last;    // page-table entries of the split
   mutable uint32_t errs = 0;  // KVQ_DEVERR_* met so far (reported once, after the loop)
+  const int vg;               // channel group whose V scale / zero this lane loads
 
-  __device__ Loader(const DecodeArgs &a_, const kvq_split &s_, int lane)
+  // vg_by_channel: the group of the lane's V channels (lr / 4) instead of the group of
+  // its weights row (lr % 4), for the P V form that scales the codes.
+  __device__ Loader(const DecodeArgs &a_, const kvq_split &s_, int lane, bool vg_by_channel = false)
       : a(a_), sp(s_), lr(lane & 15), lb(lane >> 4),
         trow(a_.tables + (int64_t)s_.table * a_.max_entries), crow((cints)trow), pages(a_, s_.head),
-        e_first(s_.tok_begin >> 4), e_last((s_.tok_end - 1) >> 4) {}
+        e_first(s_.tok_begin >> 4), e_last((s_.tok_end - 1) >> 4),
+        vg(vg_by_channel ? (lane & 15) >> 2 : lane & 3) {}
 
   // Page-table mode: the block of a 16-token page half, clamped to the split's entries
   // (a bad id reads the class's first block and is flagged).
@@ -306,7 +313,7 @@ struct Loader {
       if (CLS == KVQ_FP16 && a.fp8) w.vm[0] = ld4(vb + kF8VS + 2 * o0);  // the 8 tokens' fp16 scales
       if (CLS != KVQ_FP16) {
         const int vm_at = CLS == KVQ_INT4 ? kI4VM : kI2VM;
-        const gbytes m = vb + vm_at + ((lr & 3) * kPage + o0) * 4;
+        const gbytes m = vb + vm_at + (vg * kPage + o0) * 4;
         w.vm[0] = ld4(m);
         w.vm[1] = ld4(m + 16);
       }
@@ -338,7 +345,7 @@ struct Loader {
         if (live) w.vlive |= 1u << q;
         if (CLS == KVQ_INT4) {
           w.v[q].x = ld1(b + kI4VC + off * 64 + lr * 4);
-          vm[q] = ld1(b + kI4VM + ((lr & 3) * kPage + off) * 4);
+          vm[q] = ld1(b + kI4VM + (vg * kPage + off) * 4);
         } else {
           if (a.fp8) {
             const uint2 c = ld2(b + kF8V + off * 128 + lr * 8);
@@ -404,7 +411,11 @@ struct SplitRun {
   h2 qn[QT][4];        // natural-order q pairs: query 4 qt + lb, channels 8 lr .. 8 lr + 7
   float qsum[QT][4];   // per-group sum of q of query 4 qt + lb (INT4 zero term)
   f4 qoff[QT];         // minus the per-group sum of q x code offset (1024 / 64) of query 4 qt + lb
-  f4 acc[QT][8];       // P V accumulators
+  // Two query tiles (g = 5..8) form P V with the weights as they are (rows = the 8
+  // queries) and the V scale and zero applied to the codes: one set of accumulators
+  // for both tiles instead of one per tile with the weights scaled per channel group.
+  static constexpr bool kVS = QT == 2;
+  f4 acc[kVS ? 1 : QT][8];  // P V accumulators
   float m_run[QT], l_run[QT];
   int qbase = 0;       // first query head (of the g) this wave computes
   float zacc[QT];      // row lr: sum of p z over this lane's tokens (V zero term)
@@ -419,21 +430,17 @@ struct SplitRun {
     sel2[1] = pair_sel((lr & 1) + 2);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
+      // lanes of query row jr hold its channels 32 lb .. 32 lb + 31 where lb is the
+      // lane's group (lr % 4), zeros (L.zero) elsewhere
       const int jr = 4 * qt + (lr >> 2), gi = lr & 3;
+      const _Float16 *src = lb == gi ? &L.q[jr][32 * lb] : L.zero;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint32_t w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const h2 hv = {(_Float16)L.q[jr][32 * lb + 8 * m + 2 * u], (_Float16)L.q[jr][32 * lb + 8 * m + 2 * u + 1]};
-          w[u] = lb == gi ? as_u32(hv) : 0u;
-        }
-        Aq[qt][m] = h8_of(w[0], w[1], w[2], w[3]);
-      }
+      for (int m = 0; m < 4; ++m) Aq[qt][m] = *reinterpret_cast<const h8 *>(src + 8 * m);
       float ps = 0.0f, po = 0.0f;
+      const h2 *qrow = reinterpret_cast<const h2 *>(&L.q[4 * qt + lb][8 * lr]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        qn[qt][u] = h2{(_Float16)L.q[4 * qt + lb][8 * lr + 2 * u], (_Float16)L.q[4 * qt + lb][8 * lr + 2 * u + 1]};
+        qn[qt][u] = qrow[u];
         const float pair = (float)qn[qt][u][0] + (float)qn[qt][u][1];
         ps += pair;
         po += (u & 1 ? 64.0f : 1024.0f) * pair;  // channels 8 lr + 2 u, + 1: (ch & 2) == 2 u & 2
@@ -449,8 +456,13 @@ struct SplitRun {
       l_run[qt] = 0.0f;
       zacc[qt] = 0.0f;
       asum[qt] = 0.0f;
+      if (!kVS || qt == 0) {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int nt = 0; nt < 8; ++nt) acc[kVS ? 0 : qt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+    if (kVS) {  // weight rows 8-15 of the P V operand stay zero
+      for (int i = lane; i < 8 * 32; i += 64) L.p[0][8 + i / 32][i % 32] = (_Float16)0.0f;
     }
   }
 
@@ -619,40 +631,79 @@ struct SplitRun {
           }
         }
       }
+      if (kVS && CLS != KVQ_FP16) {
+        // v = s c + z (fp16, one rounding) with the scale and zero of this lane's channel
+        // group (lr / 4) for each token; c = (offset + c) - offset exactly
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const h2 s2 = as_h2(__builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x05040100u));
+          const h2 z2 = as_h2(__builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x07060302u));
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            const _Float16 o = (_Float16)v_offset(nt);
+            const h2 c = as_h2(t[nt][u]) - h2{o, o};
+            t[nt][u] = as_u32(__builtin_elementwise_fma(c, s2, z2));
+          }
+        }
+      }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) vb[nt] = h8_of(t[nt][0], t[nt][1], t[nt][2], t[nt][3]);
     }
     mid();
 
     // Online softmax per query (the 16 lanes of row lb).
+    float alpha_q[QT];  // (kVS) this window's rescale of query 4 qt + lb
+    bool rescaled = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float bm = row_max16(fmaxf(x[qt][0], x[qt][1]));
       const float mn = fmaxf(m_run[qt], bm);
+      alpha_q[qt] = 1.0f;
       if (__any(mn > m_run[qt])) {  // rare after the first windows
         const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mn);
         l_run[qt] *= alpha;
+        if (kVS) {
+          alpha_q[qt] = alpha;
+          rescaled = true;
+        } else {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
-        const float alpha_row = __shfl(alpha, 16 * (lr >> 2));  // rows lr belong to query lr / 4
-        zacc[qt] *= alpha_row;
-        asum[qt] *= alpha_row;
+          for (int nt = 0; nt < 8; ++nt) acc[kVS ? 0 : qt][nt] *= alpha;
+          const float alpha_row = __shfl(alpha, 16 * (lr >> 2));  // rows lr belong to query lr / 4
+          zacc[qt] *= alpha_row;
+          asum[qt] *= alpha_row;
+        }
         m_run[qt] = mn;
       }
       // v_exp_f32: exp2(-inf) = 0; results below 2^-126 may flush to zero, which no
       // softmax weight of consequence is.
       const float p0 = __builtin_amdgcn_exp2f(x[qt][0] - m_run[qt]), p1 = __builtin_amdgcn_exp2f(x[qt][1] - m_run[qt]);
       l_run[qt] += p0 + p1;
-      L.p[qt][lb][lr] = (_Float16)p0;
-      L.p[qt][lb][16 + lr] = (_Float16)p1;
+      L.p[kVS ? 0 : qt][kVS ? 4 * qt + lb : lb][lr] = (_Float16)p0;
+      L.p[kVS ? 0 : qt][kVS ? 4 * qt + lb : lb][16 + lr] = (_Float16)p1;
+    }
+    if (kVS && rescaled) {  // accumulator row 4 lb + r is query 4 lb + r: tile lb, row r
+      f4 ar;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a0 = __shfl(alpha_q[0], 16 * r), a1 = __shfl(alpha_q[kVS ? 1 : 0], 16 * r);
+        ar[r] = lb == 0 ? a0 : a1;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[0][nt] *= ar;
     }
 
     __syncthreads();  // the weights of this window are in LDS
 
     // P V.
+    if (kVS) {  // weights of query lr (rows 8-15 zero), tokens 8 lb .. 8 lb + 7
+      const h8 ap = h8_of(*reinterpret_cast<const uint4 *>(&L.p[0][lr][8 * lb]));
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[0][nt] = mfma(ap, vb[nt], acc[0][nt]);
+      return;
+    }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const uint4 pw = *reinterpret_cast<const uint4 *>(&L.p[qt][lr >> 2][8 * lb]);
+      const uint4 pw = *reinterpret_cast<const uint4 *>(&L.p[kVS ? 0 : qt][lr >> 2][8 * lb]);
       h8 ap;
       if (CLS == KVQ_FP16) {
         ap = h8_of(pw);
@@ -671,7 +722,7 @@ struct SplitRun {
         ap = h8_of(aw[0], aw[1], aw[2], aw[3]);
       }
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = mfma(ap, vb[nt], acc[qt][nt]);
+      for (int nt = 0; nt < 8; ++nt) acc[kVS ? 0 : qt][nt] = mfma(ap, vb[nt], acc[kVS ? 0 : qt][nt]);
     }
     if (CLS != KVQ_FP16 && ++since == kFold) {
       fold();
@@ -714,15 +765,40 @@ struct SplitRun {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const float c = v_offset(nt) == 64.0f ? c64 : c16;
-        acc[qt][nt] += f4{c, c, c, c};
+        acc[kVS ? 0 : qt][nt] += f4{c, c, c, c};
       }
       zacc[qt] = 0.0f;
       asum[qt] = 0.0f;
     }
   }
 
-  // Normalize and store: lane (lr, lb) owns query 4 qt + lb, channels 8 lr .. 8 lr + 7.
+  // Normalize and store: lane (lr, lb) owns query 4 qt + lb, channels 8 lr .. 8 lr + 7
+  // (kVS: queries 4 lb .. 4 lb + 3 of the wave's eight, for lb < 2).
   __device__ void finish(int s_idx) {
+    if (kVS) {
+      float lt[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) lt[qt] = row_sum16(l_run[qt]);  // query 4 qt + lb, every lane of row lb
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float l0 = __shfl(lt[0], 16 * r), l1 = __shfl(lt[QT - 1], 16 * r);
+        const float m0 = __shfl(m_run[0], 16 * r), m1 = __shfl(m_run[QT - 1], 16 * r);
+        const float l_tot = lb == 0 ? l0 : l1, m = lb == 0 ? m0 : m1;
+        const int j = qbase + 4 * lb + r;
+        const bool any = l_tot > 0.0f;
+        const float inv = any ? 1.0f / l_tot : 0.0f;
+        float o[8];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) o[nt] = any ? acc[0][nt][r] * inv : 0.0f;
+        if (lb < 2 && j < a.g) {
+          float4 *dst = reinterpret_cast<float4 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 8 * lr);
+          dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+          dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+          if (lr == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float l_tot = row_sum16(l_run[qt]);
@@ -735,7 +811,7 @@ struct SplitRun {
       float o[8];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const f4 d = acc[qt][nt];
+        const f4 d = acc[kVS ? 0 : qt][nt];
         const float v = r == 0 ? d[0] : r == 1 ? d[1] : r == 2 ? d[2] : d[3];
         o[nt] = any ? (CLS == KVQ_FP16 ? v : fmaf(-v_offset(nt), arow, v) + zrow) * inv : 0.0f;
       }
@@ -751,7 +827,7 @@ struct SplitRun {
 
 template <int QT, int CLS, bool SLOTS>
 __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, Lds<QT> &L) {
-  const Loader<CLS, SLOTS> ld(a, sp, lane_id());
+  const Loader<CLS, SLOTS> ld(a, sp, lane_id(), QT == 2);
   SplitRun<QT, CLS, SLOTS> R(a, sp, L);
   // Two window buffers used alternately: the loads of the next 32 tokens are issued
   // before the current 32 are computed, unconditionally (the last step reloads the
@@ -885,11 +961,14 @@ struct RingLoader {
   const int32_t *lds_idr;
   uint32_t voff[3];     // per-lane source offsets of this class's copies (within a block)
   uint32_t errs = 0;
+  const int vg;         // channel group whose V scale / zero this lane reads (see Loader)
 
-  __device__ RingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_, int32_t *idr_, int wave_)
+  __device__ RingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_, int32_t *idr_, int wave_,
+                        bool vg_by_channel = false)
       : sp(s_), crow((cints)(a.tables + (int64_t)s_.table * a.max_entries)), pages(a, s_.head),
         e_last((s_.tok_end - 1) >> 4), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4), wave(wave_),
-        ring((uint32_t)(uintptr_t)ring_), lds(ring_), idr((uint32_t)(uintptr_t)idr_), lds_idr(idr_) {
+        ring((uint32_t)(uintptr_t)ring_), lds(ring_), idr((uint32_t)(uintptr_t)idr_), lds_idr(idr_),
+        vg(vg_by_channel ? (lane_id() & 15) >> 2 : lane_id() & 3) {
     if (CLS == KVQ_INT4) {
       voff[0] = kI4KC + lr * 64 + lb * 16;                                 // K codes, reader-lane order
       voff[1] = kI4VC + lane * 16;                                         // V codes, natural
@@ -1002,7 +1081,7 @@ struct RingLoader {
       const uint8_t *V = S + 2048 + 1024 * (lb >> 1) + 64 * o0 + 4 * lr;
 #pragma unroll
       for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 64 * q);
-      const uint8_t *VM = M + 512 * (lb >> 1) + 256 + ((lr & 3) * kPage + o0) * 4;
+      const uint8_t *VM = M + 512 * (lb >> 1) + 256 + (vg * kPage + o0) * 4;
       w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
       w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
     } else if (CLS == KVQ_FP16) {
@@ -1033,7 +1112,7 @@ struct RingLoader {
       const uint8_t *V = at(lb >> 1, kI2VC + 32 * o0) + 4 * (lr >> 1);
 #pragma unroll
       for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 32 * q);
-      const uint8_t *VM = at(lb >> 1, kI2VM) + ((lr & 3) * kPage + o0) * 4;
+      const uint8_t *VM = at(lb >> 1, kI2VM) + (vg * kPage + o0) * 4;
       w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
       w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
     }
@@ -1045,7 +1124,7 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
                                int32_t *idr, int wave) {
   using G = RingGeom<CLS, W>;
   constexpr int A = G::kAhead;
-  RingLoader<CLS, W> ld(a, sp, ring, idr, wave);
+  RingLoader<CLS, W> ld(a, sp, ring, idr, wave, QT == 2);
   const int32_t T0 = sp.tok_begin & ~15;  // INT2 splits start on 32-token pairs
   const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
   // Window i is copied into slot i mod kSlots, A windows ahead of its compute; the page
@@ -1188,7 +1267,7 @@ __device__ void run_shared_ring(const DecodeArgs &a, const kvq_split &sp, int s_
   static_assert(4 * S <= kWin, "window ring too small");
   constexpr int kIdSlots = 8;  // ids of windows n + A .. n + 2A are live; the first A go to slots A .. 2A - 1
   static_assert(2 * A <= kIdSlots, "id ring too small");
-  RingLoader<CLS, 1> ld(a, sp, ring, idr, 0);
+  RingLoader<CLS, 1> ld(a, sp, ring, idr, 0, QT == 2);
   const int lane = lane_id();
   const int32_t T0 = sp.tok_begin & ~15;
   const uint32_t nw = (uint32_t)((sp.tok_end - T0 + 31) >> 5);  // windows of the group
@@ -1303,11 +1382,14 @@ struct SlotRingLoader {
   const uint8_t *lds_ring;
   const int32_t *lds_ids;
   uint32_t errs = 0;
+  const int vg;  // channel group whose V scale / zero this lane reads (see Loader)
 
-  __device__ SlotRingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_, int32_t *ids_)
+  __device__ SlotRingLoader(const DecodeArgs &a, const kvq_split &s_, uint8_t *ring_, int32_t *ids_,
+                            bool vg_by_channel = false)
       : sp(s_), trow((gbytes)(a.tables + (int64_t)s_.table * a.max_entries)), pages(a, s_.head),
         sentinel(a.sentinel), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4),
-        ring((uint32_t)(uintptr_t)ring_), ids((uint32_t)(uintptr_t)ids_), lds_ring(ring_), lds_ids(ids_) {}
+        ring((uint32_t)(uintptr_t)ring_), ids((uint32_t)(uintptr_t)ids_), lds_ring(ring_), lds_ids(ids_),
+        vg(vg_by_channel ? (lane_id() & 15) >> 2 : lane_id() & 3) {}
 
   // Slot ids of window T (entries clamped into the split) into id block `blk`.
   __device__ __forceinline__ void issue_ids(int32_t T, int blk) {
@@ -1374,7 +1456,7 @@ struct SlotRingLoader {
     const uint8_t *V = S + 2048 + 1024 * (lb >> 1) + 64 * o0 + 4 * lr;
 #pragma unroll
     for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 64 * q);
-    const uint8_t *VM = M + 512 + 256 * (lb >> 1) + ((lr & 3) * kPage + o0) * 4;
+    const uint8_t *VM = M + 512 + 256 * (lb >> 1) + (vg * kPage + o0) * 4;
     w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
     w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
   }
@@ -1386,7 +1468,7 @@ __device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, i
   using G = RingGeom<KVQ_INT4, 1>;
   static_assert(G::kSlots == 2, "two data slots");
   constexpr int C = SlotRingLoader::kCopies - 1;  // data copies per window (the eighth: its ids)
-  SlotRingLoader ld(a, sp, ring, id_blocks);
+  SlotRingLoader ld(a, sp, ring, id_blocks, QT == 2);
   SplitRun<QT, KVQ_INT4, true> R(a, sp, L);
   const int32_t T0 = sp.tok_begin;
   const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
@@ -1469,8 +1551,9 @@ __device__ void stage_q(const DecodeArgs &a, const kvq_split &sp, Lds<QT> &L, in
           v = a.q_dtype == KVQ_BF16 ? __uint_as_float(h << 16) : h2f(h);
         }
       }
-      L.q[j][c] = v;
+      L.q[j][c] = (_Float16)v;
     }
+  if (lane < 32) L.zero[lane] = (_Float16)0.0f;
   __syncthreads();
 }
 
