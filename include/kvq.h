@@ -348,7 +348,13 @@ kvq_status kvq_prefill_attn(const void *q, const void *k, int32_t dtype, int32_t
  * request b = t / (hkv / heads_per_page) and KV head
  * kvh = (t % (hkv / heads_per_page)) * heads_per_page + head, whose query heads
  * are kvh*g .. kvh*g + g - 1 (g = hq / hkv; 1 <= g <= 16).
- *   q [dev]: [batch][hq][128] of q_dtype (KVQ_F32 / KVQ_BF16 / KVQ_F16).
+ *   q [dev]: [batch][hq][128] of q_dtype (KVQ_F32 / KVQ_BF16 / KVQ_F16), finite.
+ *     Each query head's row enters the products as fp16 after an exact scaling
+ *     by a power of two that puts its largest magnitude in [2^14, 2^15): any
+ *     finite magnitude fits, BF16 and F16 rows are carried exactly (bf16's 8
+ *     significant bits fit fp16's 11), F32 rows are rounded to 11 significant
+ *     bits, and channels far below the row's largest keep only their share of
+ *     those bits.
  *   tables [dev]: int32 [n_tables][max_entries]: page ids (KVQ_TABLE_PAGES) or
  *     slot ids (KVQ_TABLE_SLOTS); a slot equal to c->sentinel_slot is dead and
  *     excluded from the softmax.  n_tables must equal batch * hkv / heads_per_page.

@@ -187,7 +187,8 @@ struct ClassPages {
 
 template <int QT>
 struct Lds {
-  _Float16 q[4 * QT][kHeadDim];      // queries, rounded to fp16 (rows beyond g are zero)
+  _Float16 q[4 * QT][kHeadDim];      // queries x 2^k (per row), rounded to fp16 (rows beyond g zero)
+  float qs[4 * QT];                  // 2^-k of each row: back onto its logits
   _Float16 zero[32];                 // zeros: the off-diagonal blocks of the query operand
   // softmax weights of the current 32 tokens: [query tile][query][token] for one tile;
   // for two tiles [query][token] over 16 rows (rows 8-15 zero: the weights operand)
@@ -406,7 +407,8 @@ struct SplitRun {
   const int lane, lr, lb;
   const Consts k;
   uint32_t sel2[2];    // INT2 V: byte pairs of this lane's even / odd channels
-  float scale;
+  float scale;         // softmax scale (base 2)
+  float qscale[QT];    // and with the staged row's 2^-k: logits of query 4 qt + lb
   h8 Aq[QT][4];        // block-diagonal query operand
   h2 qn[QT][4];        // natural-order q pairs: query 4 qt + lb, channels 8 lr .. 8 lr + 7
   float qsum[QT][4];   // per-group sum of q of query 4 qt + lb (INT4 zero term)
@@ -426,6 +428,8 @@ struct SplitRun {
   __device__ SplitRun(const DecodeArgs &a_, const kvq_split &sp_, Lds<QT> &L_)
       : a(a_), sp(sp_), L(L_), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4) {
     scale = kLog2e / sqrtf((float)kHeadDim);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) qscale[qt] = scale * L.qs[4 * qt + lb];
     sel2[0] = pair_sel(lr & 1);  // byte lr & 1: even channels of the lane's half word
     sel2[1] = pair_sel((lr & 1) + 2);
 #pragma unroll
@@ -564,7 +568,7 @@ struct SplitRun {
         } else {
           s = (d[0] + d[1]) + (d[2] + d[3]);
         }
-        x[qt][h] = s * scale;
+        x[qt][h] = s * qscale[qt];
       }
     }
     if (partial) {  // tokens that do not count get logit -inf (weight 0)
@@ -1532,27 +1536,43 @@ __device__ bool split_check(const DecodeArgs &a, int s_idx, kvq_split &sp, int q
   return true;
 }
 
-// Stages the split's query heads q_first .. q_first + 4 QT - 1, unscaled, in LDS rows
-// 0 .. 4 QT - 1 (rows past g zero).  Every wave of the work group calls it alike.
+// Stages the split's query heads q_first .. q_first + 4 QT - 1 in LDS rows 0 .. 4 QT - 1
+// (rows past g zero) as fp16, each row multiplied by the power of two 2^k that brings
+// its largest magnitude into [2^14, 2^15): exact, so any finite query fits fp16's range
+// and keeps 11 significant bits relative to its largest channel; L.qs holds 2^-k, which
+// the row's logits take back.  Every wave of the work group calls it alike.
 template <int QT>
 __device__ void stage_q(const DecodeArgs &a, const kvq_split &sp, Lds<QT> &L, int q_first) {
   const int lane = lane_id();
   const int b = sp.table / a.tpr;
   const int kvh = (sp.table % a.tpr) * a.heads + sp.head;
-  for (int j = 0; j < 4 * QT; ++j)
-    for (int c = lane; c < kHeadDim; c += 64) {
-      float v = 0.0f;
+  for (int j = 0; j < 4 * QT; ++j) {
+    float v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v[i] = 0.0f;
       if (q_first + j < a.g) {
-        const int64_t idx = ((int64_t)b * a.hq + kvh * a.g + q_first + j) * kHeadDim + c;
+        const int64_t idx = ((int64_t)b * a.hq + kvh * a.g + q_first + j) * kHeadDim + lane + 64 * i;
         if (a.q_dtype == KVQ_F32) {
-          v = static_cast<const float *>(a.q)[idx];
+          v[i] = static_cast<const float *>(a.q)[idx];
         } else {
           const uint32_t h = static_cast<const uint16_t *>(a.q)[idx];
-          v = a.q_dtype == KVQ_BF16 ? __uint_as_float(h << 16) : h2f(h);
+          v[i] = a.q_dtype == KVQ_BF16 ? __uint_as_float(h << 16) : h2f(h);
         }
       }
-      L.q[j][c] = (_Float16)v;
     }
+    float mx = fmaxf(fabsf(v[0]), fabsf(v[1]));
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    int k = 0;
+    if (mx > 0.0f) {  // mx = f 2^e with f in [0.5, 1)
+      int e;
+      (void)frexpf(mx, &e);
+      k = min(15 - e, 100);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) L.q[j][lane + 64 * i] = (_Float16)ldexpf(v[i], k);
+    if (lane == 0) L.qs[j] = ldexpf(1.0f, -k);
+  }
   if (lane < 32) L.zero[lane] = (_Float16)0.0f;
   __syncthreads();
 }

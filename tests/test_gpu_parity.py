@@ -74,6 +74,34 @@ def test_qwen3_8b_bf16_output():
                 dict(target_bytes=1 << 16), out_dtype=torch.bfloat16)
 
 
+def _scaled(q_factor=1.0, k_factor=1.0, channels=None):
+    """The small Qwen3-8B-shaped case with its bf16 queries (all channels, or the given
+    ones) and keys scaled."""
+    def make():
+        w = synth.qwen3_8b(batch=2, n_tokens=2048)
+        q = w.q.float()
+        if channels is None:
+            q *= q_factor
+        else:
+            q[..., channels] *= q_factor
+        w.q = q.to(torch.bfloat16)
+        w.k = (w.k.float() * k_factor).to(torch.bfloat16)
+        return w
+    return make
+
+
+@pytest.mark.parametrize("case", ["beyond_fp16", "outlier_channels", "below_fp16_normal"])
+def test_query_magnitudes(case):
+    """Queries are staged as fp16 after a power-of-two scaling per row: queries beyond
+    fp16's range (every channel x 1e5), four outlier channels x 3e4 beside ordinary ones,
+    and queries in fp16's subnormal range (x 2^-16, keys x 2^10 so that the logits still
+    matter) all stay within the bar."""
+    make = {"beyond_fp16": _scaled(1e5),
+            "outlier_channels": _scaled(3e4, channels=[3, 40, 77, 120]),
+            "below_fp16_normal": _scaled(2.0 ** -16, 2.0 ** 10)}[case]
+    _check_case(f"q {case}", make, dict(target_bytes=1 << 16))
+
+
 def test_qwen3_8b_unreordered_table():
     """Mixed-class page order without the phase-1 reorder: many short pure ranges."""
     _check_case("qwen3_8b no reorder", lambda: synth.qwen3_8b(batch=1, n_tokens=1024),
