@@ -218,8 +218,8 @@ def main():
                     help="splits per (request, KV head); 0 = as many as the decode kernel keeps resident")
     ap.add_argument("--class-cost", default=None,
                     help="per-token decode cost INT2,INT4,FP16 for sharing splits (default: the library's)")
-    ap.add_argument("--ragged-plan", choices=("aot", "tokens"), default="aot",
-                    help="split counts of ragged slot maps: by budget (Tangram AOT) or balanced by tokens read")
+    ap.add_argument("--ragged-plan", choices=("aot", "tokens"), default="tokens",
+                    help="split counts of ragged slot maps: balanced by the tokens each head reads, or by budget (Tangram AOT)")
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (reference for HBM byte counters)")

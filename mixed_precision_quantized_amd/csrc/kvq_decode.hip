@@ -1476,26 +1476,29 @@ __device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, i
   SplitRun<QT, KVQ_INT4, true> R(a, sp, L);
   const int32_t T0 = sp.tok_begin;
   const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
-  // Window i: slot ids copied at iteration i - 3 into id block i mod 4, data at
+  // Window i: slot ids copied at iteration i - 4 into id block i mod 4, data at
   // iteration i - 2 into data slot i mod 2 (as soon as window i - 2 sits in registers),
-  // computed at iteration i, so two windows are in flight during every compute.  Per
-  // iteration: (wait: data of i), read i, ids of i + 3, (wait: ids of i + 2), data of
-  // i + 2, compute i.  Copies complete in issue order; the waits count what follows.
+  // computed at iteration i, so two windows are in flight during every compute and a
+  // window's ids have two iterations to land before its data copies need them.  Per
+  // iteration: (wait: data of i, and so the ids of i + 2, copied before it), read i,
+  // ids of i + 4, data of i + 2, compute i.  Copies complete in issue order; the wait
+  // counts what follows: the ids of i + 3 and the data of i + 1.
+  static_assert(SlotRingLoader::kIdBlocks == 4, "ids of windows i + 2 .. i + 4 are live");
   ld.issue_ids(T0, 0);
   ld.issue_ids(T0 + 32, 1);
-  wait_copies<1>();  // ids of window 0
-  uint32_t mask0 = ld.issue_data(T0, 0, true, 0);
   ld.issue_ids(T0 + 64, 2);
-  wait_copies<C + 1>();  // ids of window 1
+  wait_copies<2>();  // ids of window 0
+  uint32_t mask0 = ld.issue_data(T0, 0, true, 0);
+  ld.issue_ids(T0 + 96, 3);
+  wait_copies<C + 2>();  // ids of window 1 (then: ids of 2, data of 0, ids of 3)
   uint32_t mask1 = ld.issue_data(T0 + 32, 1, 1 < nw, 1);
   ProgressPriority prio(nw);
   for (int32_t n = 0; n < nw; ++n) {
     prio.step(n);
-    wait_copies<C + 1>();  // the data of window n (then: ids of n + 2, data of n + 1)
+    wait_copies<C + 1>();  // the data of window n and the ids of n + 2 (then: ids of n + 3, data of n + 1)
     Win w;
     ld.read(n & 1, mask0, w);
-    ld.issue_ids(T0 + 32 * (n + 3), (n + 3) & 3);
-    wait_copies<C + 1>();  // the ids of window n + 2 (then: data of n + 1, ids of n + 3)
+    ld.issue_ids(T0 + 32 * (n + 4), (n + 4) & 3);
     const uint32_t mask2 = ld.issue_data(T0 + 32 * (n + 2), (n + 2) & 3, n + 2 < nw, n & 1);
     R.window(w, T0 + 32 * n);
     mask0 = mask1;
