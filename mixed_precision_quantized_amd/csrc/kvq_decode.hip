@@ -873,15 +873,23 @@ __device__ void run_split(const DecodeArgs &a, const kvq_split &sp, int s_idx, L
 template <int W>
 constexpr int ring_bytes() { return W == 1 ? 10240 : 15360; }
 
+// Ring geometry tag of the FP16 class when a cache stores its anchors as FP8 (a copy
+// layout of its own; the window compute is the FP16 class's).
+constexpr int kAnchorF8 = 3;
+template <int CLS>
+constexpr int compute_class() { return CLS == kAnchorF8 ? KVQ_FP16 : CLS; }
+
 template <int CLS, int W>
 struct RingGeom {
   // Copies per window, each from one page block (see RingLoader::issue):
   // INT4: K codes x2, V codes x2, metadata x2 (half-wave each); INT2: the first KB of
   // each page, then the last 512 B of each page (half-wave each); FP16 (one wave, its
   // own kernel with a 32 KB ring): K x4 and V x4 per page.
-  static constexpr int kChunks = CLS == KVQ_INT4 ? 6 : CLS == KVQ_INT2 ? 4 : 16;
-  static constexpr int kSlotBytes = CLS == KVQ_INT4 ? 5120 : CLS == KVQ_INT2 ? 3072 : 16384;
-  static constexpr int kRingBytes = CLS == KVQ_FP16 ? 2 * 16384 : ring_bytes<W>();
+  // FP8 anchors: K codes x2 and V codes x2 per page, then each page's K and V scales
+  // (lanes 0-3).
+  static constexpr int kChunks = CLS == KVQ_INT4 ? 6 : CLS == KVQ_INT2 ? 4 : CLS == kAnchorF8 ? 10 : 16;
+  static constexpr int kSlotBytes = CLS == KVQ_INT4 ? 5120 : CLS == KVQ_INT2 ? 3072 : CLS == kAnchorF8 ? 8320 : 16384;
+  static constexpr int kRingBytes = CLS == KVQ_FP16 ? 2 * 16384 : CLS == kAnchorF8 ? 2 * 8320 : ring_bytes<W>();
   static constexpr int kSlots = kRingBytes / kSlotBytes;
   // Windows copied ahead of the one computed.  One wave refills a slot as soon as its
   // window sits in registers, so every slot is in flight during a compute; with
@@ -956,7 +964,7 @@ struct RingLoader {
   static constexpr int kAhead = G::kAhead;
   const kvq_split sp;
   cints crow;
-  const ClassPages<CLS> pages;
+  const ClassPages<compute_class<CLS>()> pages;
   const int32_t e_last;
   const int lane, lr, lb, wave;
   const uint32_t ring;  // LDS byte address of the ring
@@ -981,6 +989,10 @@ struct RingLoader {
       voff[0] = kF16K + lr * 256 + lb * 64;                                // K rows, reader-lane order
       voff[1] = kF16V + lane * 16;                                         // V rows, natural
       voff[2] = 0;
+    } else if (CLS == kAnchorF8) {
+      voff[0] = kF8K + lr * 128 + lb * 32;                                 // K codes, reader-lane order
+      voff[1] = kF8V + lane * 16;                                          // V codes, natural
+      voff[2] = (lane & 1) * 16 + ((lane & 2) ? kF8VS : kF8KS);            // lanes 0-3: K, V scales
     } else {
       voff[0] = lane * 16;                                                 // bytes 0 .. 1023
       voff[1] = 1024 + (lane & 31) * 16;                                   // bytes 1024 .. 1535
@@ -1026,6 +1038,17 @@ struct RingLoader {
       const int r = c >> 2, m = c & 3;
       const gbytes b = (r & 1) ? b1 : b0;
       dma_block(base + 1024 * c, r < 2 ? b + 16 * m : b + 1024 * m, r < 2 ? vo[0] : vo[1]);
+    } else if (CLS == kAnchorF8) {
+      // chunks 0-3: K codes of half c / 2, part c % 2 (channels 32 lb + 16 (c % 2) .. + 15
+      // of every token); 4-7: V codes of half (c - 4) / 2, tokens 8 ((c - 4) % 2) .. + 7;
+      // 8, 9: the scales of half c - 8 (lanes 0-3)
+      if (c < 4) {
+        dma_block(base + 1024 * c, ((c >> 1) ? b1 : b0) + 16 * (c & 1), vo[0]);
+      } else if (c < 8) {
+        dma_block(base + 4096 + 1024 * (c - 4), (((c - 4) >> 1) ? b1 : b0) + 1024 * (c & 1), vo[1]);
+      } else if (lane < 4) {
+        dma_block(base + 8192 + 64 * (c - 8), c == 8 ? b0 : b1, vo[2]);
+      }
     } else {
       switch (c) {
         case 0: dma_block(base, b0, vo[0]); break;
@@ -1088,6 +1111,22 @@ struct RingLoader {
       const uint8_t *VM = M + 512 * (lb >> 1) + 256 + (vg * kPage + o0) * 4;
       w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
       w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
+    } else if (CLS == kAnchorF8) {
+      // [K A][K B] (2 chunks each, reader-lane order), [V A][V B] (rows of 128 B),
+      // [K scales A, V scales A][K scales B, V scales B] (32 B each)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        w.k[h][0] = *reinterpret_cast<const uint4 *>(S + 2048 * h + 16 * lane);
+        w.k[h][1] = *reinterpret_cast<const uint4 *>(S + 2048 * h + 1024 + 16 * lane);
+        w.k[h][2].x = __float_as_uint(half_value(*reinterpret_cast<const uint16_t *>(S + 8192 + 64 * h + 2 * lr)));
+      }
+      const uint8_t *V = S + 4096 + 2048 * (lb >> 1) + 128 * o0 + 8 * lr;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint2 c = *reinterpret_cast<const uint2 *>(V + 128 * q);
+        w.v[q] = make_uint4(c.x, c.y, 0u, 0u);
+      }
+      w.vm[0] = *reinterpret_cast<const uint4 *>(S + 8192 + 64 * (lb >> 1) + 32 + 2 * o0);
     } else if (CLS == KVQ_FP16) {
       // [K A][K B] (chunk m of a half: lane L's 16 B of the reader lane L), [V A][V B]
       // (token rows of 256 B)
@@ -1145,7 +1184,7 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
   }
   // The queries are fetched while the first windows are on their way.
   stage_q<QT>(a, sp, L, 4 * QT * wave);
-  SplitRun<QT, CLS, false> R(a, sp, L);
+  SplitRun<QT, compute_class<CLS>(), false> R(a, sp, L);
   R.qbase = 4 * QT * wave;
   int id_slot = A;  // id slot of window n + A
   ProgressPriority prio(nw);
@@ -1654,17 +1693,19 @@ decode_ring_kernel(DecodeArgs a) {
 // LDS-staged kernel for the FP16 splits of a page-table launch (FP16 anchors, g <= 8):
 // a 32 KB ring of two 16 KB windows per wave, one wave per SIMD; the FP16 window has
 // no unpacking, so one wave's compute keeps ahead of its copies.
-template <int QT>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
+// FP8 anchors: 8.3 KB windows, two per wave, two waves per SIMD.
+template <int QT, bool F8>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(F8 ? 2 : 1)))
 decode_anchor_ring_kernel(DecodeArgs a) {
+  constexpr int RC = F8 ? kAnchorF8 : KVQ_FP16;
   __shared__ Lds<QT> L;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[RingGeom<KVQ_FP16, 1>::kRingBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RingGeom<RC, 1>::kRingBytes];
   __shared__ __attribute__((aligned(16))) int32_t idr[16];
   const int s_idx = split_of_block(a);
   kvq_split sp;
   // (a.only_fp16 is set: this kernel takes the FP16 splits, the other one the rest)
   if (!split_check<QT, false, false>(a, s_idx, sp, 0)) return;
-  run_split_ring<KVQ_FP16, 1, QT>(a, sp, s_idx, L, ring, idr, 0);
+  run_split_ring<RC, 1, QT>(a, sp, s_idx, L, ring, idr, 0);
 }
 
 // LDS-staged kernel for slot maps (INT4 splits, g <= 8).
@@ -1817,15 +1858,17 @@ kvq_status decode_setup(DecodeArgs &a, const kvq_cache *c, const void *q, int32_
 }
 
 // The kernel for the FP16 splits of a page-table launch (when the cache has FP16 pages;
-// the INT2 / INT4 kernel leaves them): LDS-staged for FP16 anchors up to g = 8,
-// register-staged for FP8 anchors and g = 16.
+// the INT2 / INT4 kernel leaves them): LDS-staged up to g = 8 (FP16 or FP8 anchors),
+// register-staged at g = 16.
 kvq_status launch_fp16_pages(DecodeArgs a, hipStream_t s) {
   if (a.n16 == 0) return KVQ_OK;
   a.only_fp16 = 1;
   const dim3 grid(a.n_splits), block(64);
-  if (!a.fp8 && a.g <= 8) {
-    if (a.g <= 4) hipLaunchKernelGGL((decode_anchor_ring_kernel<1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_anchor_ring_kernel<2>), grid, block, 0, s, a);
+  if (a.g <= 8) {
+    if (a.fp8 && a.g <= 4) hipLaunchKernelGGL((decode_anchor_ring_kernel<1, true>), grid, block, 0, s, a);
+    else if (a.fp8) hipLaunchKernelGGL((decode_anchor_ring_kernel<2, true>), grid, block, 0, s, a);
+    else if (a.g <= 4) hipLaunchKernelGGL((decode_anchor_ring_kernel<1, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_anchor_ring_kernel<2, false>), grid, block, 0, s, a);
     return launched("decode_anchor_ring_kernel");
   }
   if (a.g <= 4) hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, s, a);
@@ -2022,14 +2065,13 @@ extern "C" kvq_status kvq_decode_fp16_occupancy(int32_t g, int32_t anchor_format
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVQ_ERR_NO_DEVICE, "hipGetDevice failed");
   int blocks = 0, cus = 0;
   hipError_t e;
-  if (anchor_format == KVQ_ANCHOR_FP16 && g <= 4)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_anchor_ring_kernel<1>, 64, 0);
-  else if (anchor_format == KVQ_ANCHOR_FP16 && g <= 8)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_anchor_ring_kernel<2>, 64, 0);
-  else if (g <= 4)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<1, false>, 64, 0);
+  const bool f8 = anchor_format == KVQ_ANCHOR_FP8;
+  if (g <= 4)
+    e = f8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_anchor_ring_kernel<1, true>, 64, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_anchor_ring_kernel<1, false>, 64, 0);
   else if (g <= 8)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<2, false>, 64, 0);
+    e = f8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_anchor_ring_kernel<2, true>, 64, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_anchor_ring_kernel<2, false>, 64, 0);
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<4, false>, 64, 0);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
