@@ -150,6 +150,7 @@ struct DecodeArgs {
   int32_t *err;
   int32_t only_fp16;  // page mode with the LDS-staged kernel present: this kernel takes FP16 splits only
   int32_t fp8;        // the FP16 class holds FP8 anchors (e4m3 codes and a power-of-two scale per token)
+  int32_t q_lds;      // 16-bit queries on a 16-byte boundary: the LDS-staged kernels copy them in (stage_q_issue)
   int32_t *work;            // shared mode: window counters of the groups, then the count of finished workers
   const int32_t *wgroup;    // shared mode: group of each worker
   int32_t n_groups;
@@ -191,8 +192,9 @@ struct Lds {
   float qs[4 * QT];                  // 2^-k of each row: back onto its logits
   _Float16 zero[32];                 // zeros: the off-diagonal blocks of the query operand
   // softmax weights of the current 32 tokens: [query tile][query][token] for one tile;
-  // for two tiles [query][token] over 16 rows (rows 8-15 zero: the weights operand)
-  _Float16 p[QT == 2 ? 1 : QT][QT == 2 ? 16 : 4][32];
+  // for two tiles [query][token] over the 8 queries (the weights operand's rows 8-15
+  // are zero, read from `zero`)
+  _Float16 p[QT == 2 ? 1 : QT][QT == 2 ? 8 : 4][32];
 };
 
 // ------------------------------------------------------------- per window -----
@@ -465,9 +467,6 @@ struct SplitRun {
         for (int nt = 0; nt < 8; ++nt) acc[kVS ? 0 : qt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
-    if (kVS) {  // weight rows 8-15 of the P V operand stay zero
-      for (int i = lane; i < 8 * 32; i += 64) L.p[0][8 + i / 32][i % 32] = (_Float16)0.0f;
-    }
   }
 
   __device__ __forceinline__ void window(const Win &w, int32_t T) {
@@ -700,7 +699,8 @@ struct SplitRun {
 
     // P V.
     if (kVS) {  // weights of query lr (rows 8-15 zero), tokens 8 lb .. 8 lb + 7
-      const h8 ap = h8_of(*reinterpret_cast<const uint4 *>(&L.p[0][lr][8 * lb]));
+      const _Float16 *prow = lr < 8 ? &L.p[0][lr & 7][8 * lb] : L.zero;
+      const h8 ap = h8_of(*reinterpret_cast<const uint4 *>(prow));
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc[0][nt] = mfma(ap, vb[nt], acc[0][nt]);
       return;
@@ -914,6 +914,21 @@ __device__ __forceinline__ void dma_block(uint32_t lds, gbytes base, uint32_t vo
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
 }
 
+// Half of a chunk: lanes 0-31 (HI false) or 32-63 (HI true) copy 16 B from base + voff
+// to LDS byte lds + 16 L.  The other half is masked off by clearing its half of EXEC
+// around the copy (restored after it), with no lane test: every lane of the wave is
+// active where this is called.
+template <bool HI>
+__device__ __forceinline__ void dma_block_half(uint32_t lds, gbytes base, uint32_t voff) {
+  uint64_t saved;
+  if (HI)
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b32 exec_lo, 0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
+  else
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b32 exec_hi, 0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
+}
+
 // One 256 B chunk: lane L copies 4 B from src to LDS byte lds + 4 L.
 __device__ __forceinline__ void dma_dword(uint32_t lds, gbytes src) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"((uint64_t)src), "{m0}"(lds) : "memory");
@@ -935,6 +950,10 @@ __device__ __forceinline__ void wait_copies() {
 
 template <int QT>
 __device__ void stage_q(const DecodeArgs &a, const kvq_split &sp, Lds<QT> &L, int q_first);
+template <int QT>
+__device__ void stage_q_issue(const DecodeArgs &a, const kvq_split &sp, Lds<QT> &L, int q_first);
+template <int QT>
+__device__ void stage_q_convert(const DecodeArgs &a, Lds<QT> &L, int q_first);
 
 // Issue priority by progress.  A SIMD's waves issue oldest first among equal
 // priorities, so waves given equal work would finish one after another and leave the
@@ -994,8 +1013,8 @@ struct RingLoader {
       voff[1] = kF8V + lane * 16;                                          // V codes, natural
       voff[2] = (lane & 1) * 16 + ((lane & 2) ? kF8VS : kF8KS);            // lanes 0-3: K, V scales
     } else {
-      voff[0] = lane * 16;                                                 // bytes 0 .. 1023
-      voff[1] = 1024 + (lane & 31) * 16;                                   // bytes 1024 .. 1535
+      voff[0] = lane * 16;                                                 // bytes 0 .. 1023 (and 1024 ..)
+      voff[1] = 0;
       voff[2] = 0;
     }
   }
@@ -1028,8 +1047,8 @@ struct RingLoader {
         case 1: dma_block(base + 1024, b1, vo[0]); break;
         case 2: dma_block(base + 2048, b0, vo[1]); break;
         case 3: dma_block(base + 3072, b1, vo[1]); break;
-        case 4: if (lane < 32) dma_block(base + 4096, b0, vo[2]); break;
-        default: if (lane >= 32) dma_block(base + 4096, b1, vo[2]); break;
+        case 4: dma_block_half<false>(base + 4096, b0, vo[2]); break;
+        default: dma_block_half<true>(base + 4096, b1, vo[2]); break;
       }
     } else if (CLS == KVQ_FP16) {
       // chunk c: region c / 4 (K of page half 0, K of half 1, V of half 0, V of half 1),
@@ -1053,8 +1072,10 @@ struct RingLoader {
       switch (c) {
         case 0: dma_block(base, b0, vo[0]); break;
         case 1: dma_block(base + 1024, b1, vo[0]); break;
-        case 2: if (lane < 32) dma_block(base + 2048, b0, vo[1]); break;
-        default: if (lane >= 32) dma_block(base + 2048, b1, vo[1]); break;
+        // bytes 1024 .. 1535 of page half 0 (lanes 0-31), then of half 1 (lanes 32-63):
+        // lane L reads base + 16 L of a base moved by 1024, or by 1024 - 512
+        case 2: dma_block_half<false>(base + 2048, b0 + 1024, vo[0]); break;
+        default: dma_block_half<true>(base + 2048, b1 + 512, vo[0]); break;
       }
     }
   }
@@ -1090,6 +1111,15 @@ struct RingLoader {
     else if (wave == 1) wait_copies<(kAhead - 1) * (G::chunks_of(1) + 1)>();
     else if (wave == 2) wait_copies<(kAhead - 1) * (G::chunks_of(2) + 1)>();
     else wait_copies<(kAhead - 1) * (G::chunks_of(3) + 1)>();
+  }
+
+  // Waits for the copies this wave issued before the prologue's windows (the query rows
+  // of stage_q_issue): the kAhead windows and their id copies may still be in flight.
+  __device__ __forceinline__ void wait_before_windows() const {
+    if (W == 1 || wave == 0) wait_copies<kAhead * (G::chunks_of(0) + 1)>();
+    else if (wave == 1) wait_copies<kAhead * (G::chunks_of(1) + 1)>();
+    else if (wave == 2) wait_copies<kAhead * (G::chunks_of(2) + 1)>();
+    else wait_copies<kAhead * (G::chunks_of(3) + 1)>();
   }
 
   // Reads window T from slot `slot` into the register window of the compute.
@@ -1176,14 +1206,30 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
   constexpr int kIdSlots = 8;  // ids of windows n + A .. n + 2A are live; the first A go to slots A .. 2A - 1
   static_assert(2 * A <= kIdSlots, "id ring too small");
   uint32_t okq = 0;  // validity bits of the windows in flight, 2 per window, newest lowest
+  // The start is a chain of dependent memory round trips (split, page ids, data), each
+  // long while every wave of the launch starts at once: the query rows are copied first
+  // and the page ids of the first windows loaded together, before any window's copies.
+  const bool q_lds = a.q_lds != 0;
+  if (q_lds) stage_q_issue<QT>(a, sp, L, 4 * QT * wave);
+  int32_t pid[A][2];
+#pragma unroll
+  for (int i = 0; i < A; ++i) {
+    pid[i][0] = ld.entry(T0 + 32 * i, 0);
+    pid[i][1] = ld.entry(T0 + 32 * i, 1);
+  }
 #pragma unroll
   for (int i = 0; i < A; ++i) {
     const int32_t Ti = T0 + 32 * i;
     ld.issue_ids(Ti + 32 * A, i + A);
-    okq = (okq << 2) | ld.issue(ld.entry(Ti, 0), ld.entry(Ti, 1), i < nw, i);
+    okq = (okq << 2) | ld.issue(pid[i][0], pid[i][1], i < nw, i);
   }
-  // The queries are fetched while the first windows are on their way.
-  stage_q<QT>(a, sp, L, 4 * QT * wave);
+  // The queries are staged while the first windows are on their way.
+  if (q_lds) {
+    ld.wait_before_windows();
+    stage_q_convert<QT>(a, L, 4 * QT * wave);
+  } else {
+    stage_q<QT>(a, sp, L, 4 * QT * wave);
+  }
   SplitRun<QT, compute_class<CLS>(), false> R(a, sp, L);
   R.qbase = 4 * QT * wave;
   int id_slot = A;  // id slot of window n + A
@@ -1322,20 +1368,36 @@ __device__ void run_shared_ring(const DecodeArgs &a, const kvq_split &sp, int s_
   auto start = [&](int32_t i) { return win[i & (kWin - 1)]; };
   // The first three blocks in one claim: nothing is in flight yet, so waiting for it
   // costs its own latency only.
+  // (the query rows are copied first, alongside the claim; the first windows' page ids
+  // are loaded together, as in run_split_ring)
+  const bool q_lds = a.q_lds != 0;
+  if (q_lds) stage_q_issue<QT>(a, sp, L, 0);
   uint32_t k0 = 0u;
   if (lane == 0) k0 = (uint32_t)atomicAdd(ctr, 3 * S);
   k0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)k0);
 #pragma unroll
   for (int b = 0; b < 3; ++b) put(b * S, k0 + (uint32_t)(b * S));
   uint32_t okq = 0;
+  int32_t pid[A][2];
+#pragma unroll
+  for (int i = 0; i < A; ++i) {
+    const int32_t Ti = start(i);
+    const int32_t Te = Ti >= 0 ? Ti : T0;
+    pid[i][0] = ld.entry(Te, 0);
+    pid[i][1] = ld.entry(Te, 1);
+  }
 #pragma unroll
   for (int i = 0; i < A; ++i) {
     const int32_t Ti = start(i), Tn = start(i + A);
     ld.issue_ids(Tn >= 0 ? Tn : T0, i + A);
-    const int32_t Te = Ti >= 0 ? Ti : T0;
-    okq = (okq << 2) | ld.issue(ld.entry(Te, 0), ld.entry(Te, 1), Ti >= 0, i);
+    okq = (okq << 2) | ld.issue(pid[i][0], pid[i][1], Ti >= 0, i);
   }
-  stage_q<QT>(a, sp, L, 0);
+  if (q_lds) {
+    ld.wait_before_windows();
+    stage_q_convert<QT>(a, L, 0);
+  } else {
+    stage_q<QT>(a, sp, L, 0);
+  }
   SplitRun<QT, CLS, false> R(a, sp, L);
   int id_slot = A;     // id slot of window n + A
   uint32_t pend = 0u;  // the claim issued at the start of the current block
@@ -1512,7 +1574,6 @@ __device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, i
   static_assert(G::kSlots == 2, "two data slots");
   constexpr int C = SlotRingLoader::kCopies - 1;  // data copies per window (the eighth: its ids)
   SlotRingLoader ld(a, sp, ring, id_blocks, QT == 2);
-  SplitRun<QT, KVQ_INT4, true> R(a, sp, L);
   const int32_t T0 = sp.tok_begin;
   const int32_t nw = (sp.tok_end - T0 + 31) >> 5;
   // Window i: slot ids copied at iteration i - 4 into id block i mod 4, data at
@@ -1523,6 +1584,10 @@ __device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, i
   // ids of i + 4, data of i + 2, compute i.  Copies complete in issue order; the wait
   // counts what follows: the ids of i + 3 and the data of i + 1.
   static_assert(SlotRingLoader::kIdBlocks == 4, "ids of windows i + 2 .. i + 4 are live");
+  // The query rows are copied before the first ids (a.q_lds), so the wait for the ids
+  // of window 0 covers them (copies complete in issue order).
+  const bool q_lds = a.q_lds != 0;
+  if (q_lds) stage_q_issue<QT>(a, sp, L, 0);
   ld.issue_ids(T0, 0);
   ld.issue_ids(T0 + 32, 1);
   ld.issue_ids(T0 + 64, 2);
@@ -1531,6 +1596,9 @@ __device__ void run_split_slots_ring(const DecodeArgs &a, const kvq_split &sp, i
   ld.issue_ids(T0 + 96, 3);
   wait_copies<C + 2>();  // ids of window 1 (then: ids of 2, data of 0, ids of 3)
   uint32_t mask1 = ld.issue_data(T0 + 32, 1, 1 < nw, 1);
+  if (q_lds) stage_q_convert<QT>(a, L, 0);
+  else stage_q<QT>(a, sp, L, 0);
+  SplitRun<QT, KVQ_INT4, true> R(a, sp, L);
   ProgressPriority prio(nw);
   for (int32_t n = 0; n < nw; ++n) {
     prio.step(n);
@@ -1583,38 +1651,105 @@ __device__ bool split_check(const DecodeArgs &a, int s_idx, kvq_split &sp, int q
 // its largest magnitude into [2^14, 2^15): exact, so any finite query fits fp16's range
 // and keeps 11 significant bits relative to its largest channel; L.qs holds 2^-k, which
 // the row's logits take back.  Every wave of the work group calls it alike.
+// Row j of the staged queries from its channels lane and lane + 64 (v), given the
+// row's largest magnitude mx.
+template <int QT>
+__device__ __forceinline__ void stage_row(Lds<QT> &L, int j, const float (&v)[2], float mx) {
+  const int lane = lane_id();
+  int k = 0;
+  if (mx > 0.0f) {  // mx = f 2^e with f in [0.5, 1)
+    int e;
+    (void)frexpf(mx, &e);
+    k = min(15 - e, 100);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) L.q[j][lane + 64 * i] = (_Float16)ldexpf(v[i], k);
+  if (lane == 0) L.qs[j] = ldexpf(1.0f, -k);
+}
+
 template <int QT>
 __device__ void stage_q(const DecodeArgs &a, const kvq_split &sp, Lds<QT> &L, int q_first) {
   const int lane = lane_id();
   const int b = sp.table / a.tpr;
   const int kvh = (sp.table % a.tpr) * a.heads + sp.head;
-  for (int j = 0; j < 4 * QT; ++j) {
-    float v[2];
+  // Every load is issued before any value is used (rows at or past g read row g - 1).
+  float v[4 * QT][2], mx[4 * QT];
+  const int64_t row0 = (int64_t)b * a.hq + (int64_t)kvh * a.g;
+  if (a.q_dtype == KVQ_F32) {
+    const float *q = static_cast<const float *>(a.q);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      v[i] = 0.0f;
-      if (q_first + j < a.g) {
-        const int64_t idx = ((int64_t)b * a.hq + kvh * a.g + q_first + j) * kHeadDim + lane + 64 * i;
-        if (a.q_dtype == KVQ_F32) {
-          v[i] = static_cast<const float *>(a.q)[idx];
-        } else {
-          const uint32_t h = static_cast<const uint16_t *>(a.q)[idx];
-          v[i] = a.q_dtype == KVQ_BF16 ? __uint_as_float(h << 16) : h2f(h);
-        }
-      }
-    }
-    float mx = fmaxf(fabsf(v[0]), fabsf(v[1]));
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    int k = 0;
-    if (mx > 0.0f) {  // mx = f 2^e with f in [0.5, 1)
-      int e;
-      (void)frexpf(mx, &e);
-      k = min(15 - e, 100);
-    }
+    for (int j = 0; j < 4 * QT; ++j)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) L.q[j][lane + 64 * i] = (_Float16)ldexpf(v[i], k);
-    if (lane == 0) L.qs[j] = ldexpf(1.0f, -k);
+      for (int i = 0; i < 2; ++i) v[j][i] = q[(row0 + min(q_first + j, a.g - 1)) * kHeadDim + lane + 64 * i];
+  } else {
+    const uint16_t *q = static_cast<const uint16_t *>(a.q);
+    uint32_t h[4 * QT][2];
+#pragma unroll
+    for (int j = 0; j < 4 * QT; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) h[j][i] = q[(row0 + min(q_first + j, a.g - 1)) * kHeadDim + lane + 64 * i];
+#pragma unroll
+    for (int j = 0; j < 4 * QT; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) v[j][i] = a.q_dtype == KVQ_BF16 ? __uint_as_float(h[j][i] << 16) : h2f(h[j][i]);
   }
+#pragma unroll
+  for (int j = 0; j < 4 * QT; ++j) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v[j][i] = q_first + j < a.g ? v[j][i] : 0.0f;
+    mx[j] = fmaxf(fabsf(v[j][0]), fabsf(v[j][1]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)  // the rows' reductions side by side
+#pragma unroll
+    for (int j = 0; j < 4 * QT; ++j) mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], off));
+#pragma unroll
+  for (int j = 0; j < 4 * QT; ++j) stage_row(L, j, v[j], mx[j]);
+  if (lane < 32) L.zero[lane] = (_Float16)0.0f;
+  __syncthreads();
+}
+
+// The same in two steps for 16-bit queries on a 16-byte boundary (a.q_lds): the raw
+// rows go to L.q by LDS-bound copies (one per four rows: lane L takes row 4 c + L / 16,
+// bytes 16 (L % 16) .. + 15), issued before the split's first windows; rows at or past g
+// copy row g - 1, a valid row of the same head (they are staged as zeros).  Once the
+// copies have landed, stage_q_convert stages the rows in place.
+template <int QT>
+__device__ void stage_q_issue(const DecodeArgs &a, const kvq_split &sp, Lds<QT> &L, int q_first) {
+  const int lane = lane_id();
+  const int b = sp.table / a.tpr;
+  const int kvh = (sp.table % a.tpr) * a.heads + sp.head;
+  const gbytes base = (gbytes)a.q + ((int64_t)b * a.hq + (int64_t)kvh * a.g) * (kHeadDim * 2);
+  const uint32_t lds = (uint32_t)(uintptr_t)&L.q[0][0];
+#pragma unroll
+  for (int c = 0; c < QT; ++c) {
+    const int row = min(q_first + 4 * c + (lane >> 4), a.g - 1);
+    dma_block(lds + 1024u * (uint32_t)c, base, (uint32_t)row * (kHeadDim * 2) + 16u * (uint32_t)(lane & 15));
+  }
+}
+
+template <int QT>
+__device__ void stage_q_convert(const DecodeArgs &a, Lds<QT> &L, int q_first) {
+  const int lane = lane_id();
+  uint32_t raw[4 * QT][2];
+#pragma unroll
+  for (int j = 0; j < 4 * QT; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) raw[j][i] = reinterpret_cast<const uint16_t *>(&L.q[j][0])[lane + 64 * i];
+  float v[4 * QT][2], mx[4 * QT];
+#pragma unroll
+  for (int j = 0; j < 4 * QT; ++j) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      v[j][i] = q_first + j >= a.g ? 0.0f : a.q_dtype == KVQ_BF16 ? __uint_as_float(raw[j][i] << 16) : h2f(raw[j][i]);
+    mx[j] = fmaxf(fabsf(v[j][0]), fabsf(v[j][1]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)  // the rows' reductions side by side
+#pragma unroll
+    for (int j = 0; j < 4 * QT; ++j) mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], off));
+#pragma unroll
+  for (int j = 0; j < 4 * QT; ++j) stage_row(L, j, v[j], mx[j]);
   if (lane < 32) L.zero[lane] = (_Float16)0.0f;
   __syncthreads();
 }
@@ -1652,7 +1787,8 @@ __global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
 
 // LDS-staged kernel: page-table mode, INT2 and INT4 splits; W waves per split with 4 QT
 // query heads each; three waves per SIMD at QT = 1 (at most 168 registers a lane), two
-// at QT = 2.
+// at QT = 2 (three, with the query operand read from LDS at each window to fit the
+// registers, measured slower: 208 against 187 us on the agentic shape).
 template <int W, int QT, bool SHARED>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 2)))
 decode_ring_kernel(DecodeArgs a) {
@@ -1717,7 +1853,7 @@ decode_slots_ring_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) int32_t id_blocks[SlotRingLoader::kIdBlocks * 32];
   const int s_idx = split_of_block(a);
   kvq_split sp;
-  if (!split_prologue<QT, true, true>(a, s_idx, sp, L)) return;
+  if (!split_check<QT, true, true>(a, s_idx, sp)) return;
   if (sp.cls == KVQ_INT4) run_split_slots_ring<QT>(a, sp, s_idx, L, ring, id_blocks);
 }
 
@@ -1837,6 +1973,7 @@ kvq_status decode_setup(DecodeArgs &a, const kvq_cache *c, const void *q, int32_
   a.fp8 = c->anchor_format == KVQ_ANCHOR_FP8 ? 1 : 0;
   a.q = q;
   a.q_dtype = q_dtype;
+  a.q_lds = q_dtype != KVQ_F32 && ((uintptr_t)q & 15u) == 0 ? 1 : 0;
   a.batch = batch;
   a.hq = hq;
   a.hkv = hkv;
