@@ -107,6 +107,17 @@ template <int P>
 __device__ __forceinline__ uint32_t quad_perm(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, P, 0xf, 0xf, true);
 }
+// Lane n of each 16-lane row to every lane of the row (n a constant once unrolled).
+__device__ __forceinline__ float row_bcast(float x, int n) {
+#define KVQ_BC(N) \
+  case N: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xf, 0xf, false));
+  switch (n) {
+    KVQ_BC(0) KVQ_BC(1) KVQ_BC(2) KVQ_BC(3) KVQ_BC(4) KVQ_BC(5) KVQ_BC(6) KVQ_BC(7)
+    KVQ_BC(8) KVQ_BC(9) KVQ_BC(10) KVQ_BC(11) KVQ_BC(12) KVQ_BC(13) KVQ_BC(14)
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + 15, 0xf, 0xf, false));
+  }
+#undef KVQ_BC
+}
 
 // Min and max over the 16 lanes of a group (one DPP row); every lane gets both.
 __device__ __forceinline__ void group16_minmax(float &mn, float &mx) {
@@ -336,14 +347,37 @@ __global__ void __launch_bounds__(64) append_int2_kernel(
     *reinterpret_cast<uint32_t *>(m + kI2KZ + at) = q0.zb | (q1.zb << 16);
   }
 
-  // V, per token: all 32 rows loaded first, then quantized independently.
-  float2 vx[kGroup];
+  // V, per token, one page (16 tokens) at a time.  The group of 32 channels (16 lanes)
+  // of token t has its minimum and maximum in every lane of the group after the row
+  // reduction; lane 16 g + i keeps token i's, forms its scale and zero (one of the 64
+  // (token, group) pairs of the page per lane, not every pair in every lane), stores
+  // them, and lends them to its group for the codes.
+  const int li = lane & 15;
 #pragma unroll
-  for (int t = 0; t < kGroup; ++t)
-    vx[t] = load_pair(v, dtype, (int64_t)rows[t] * row_stride + (int64_t)head * head_stride + 2 * lane);
+  for (int h = 0; h < 2; ++h) {
+    float2 vx[kPage];
 #pragma unroll
-  for (int t = 0; t < kGroup; ++t)
-    put_token_row<2, false>(blk[t >> 4], kI2VC, kI2VM, t & 15, vx[t].x, vx[t].y, lane);
+    for (int t = 0; t < kPage; ++t)
+      vx[t] = load_pair(v, dtype, (int64_t)rows[16 * h + t] * row_stride + (int64_t)head * head_stride + 2 * lane);
+    float kmn = 0.f, kmx = 0.f;
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      float mn = fminf(canon(vx[t].x), canon(vx[t].y)), mx = fmaxf(canon(vx[t].x), canon(vx[t].y));
+      group16_minmax(mn, mx);
+      kmn = li == t ? mn : kmn;
+      kmx = li == t ? mx : kmx;
+    }
+    const Quant qv = quant_params(kmn, kmx, 3.0f);
+    // group-major [4][16][s, z]: entry (lane / 16) 16 + token = lane
+    *reinterpret_cast<uint32_t *>(blk[h] + kI2VM + lane * 4) = qv.sb | (qv.zb << 16);
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      Quant q;
+      q.s = row_bcast(qv.s, t);
+      q.z = row_bcast(qv.z, t);
+      put_code_pair<2>(blk[h] + kI2VC + t * 32, quant_code(vx[t].x, q, 3.0f), quant_code(vx[t].y, q, 3.0f), lane);
+    }
+  }
 }
 
 // --------------------------------------------------------------- reorder ------
