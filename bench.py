@@ -113,7 +113,9 @@ def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_pl
     one round of each of the two kernels (kvq_plan_splits_per_kernel).  Ragged slot maps
     share the count among heads in proportion to their budgets (Tangram AOT), or, with
     ragged_plan="tokens", so that no piece holds more tokens than it must for the count
-    to fit (balanced split counts over the tokens each head reads)."""
+    to fit (balanced split counts over the tokens each head reads).  Page tables without
+    FP16 pages get counts balanced over each head's tokens x class cost
+    (kvq_plan_balanced)."""
     import numpy as np
     w = gpu.w
     kind = kvq.TABLE_SLOTS if w.kind == synth.SLOTS else kvq.TABLE_PAGES
@@ -135,7 +137,11 @@ def resident_plan(gpu, kvq, synth, splits_per_head=0, class_cost=None, ragged_pl
     elif w.head_budget is not None:
         sph = kvq.aot_split_counts(w.head_budget, w.batch, per_cu * n_cu)
     else:
-        sph = np.full(w.batch * w.hkv, max(1, (per_cu * n_cu) // (w.batch * w.hkv)), np.int32)
+        # page tables: counts by each head's tokens x class cost, so that long requests
+        # get more splits and one resident round ends together
+        splits, offsets, _ = kvq.plan_balanced(gpu.ranges, w.batch, w.hkv, w.heads_per_page, w.g, per_cu * n_cu,
+                                               class_cost)
+        return splits, offsets, per_cu, n_cu
     splits, offsets = gpu.plan(splits_per_head=sph, class_cost=class_cost)
     return splits, offsets, per_cu, n_cu
 

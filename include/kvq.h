@@ -538,6 +538,29 @@ kvq_status kvq_aot_split_counts(const float *budgets, int32_t hkv, int32_t batch
 kvq_status kvq_balanced_split_counts(const int64_t *work, int32_t n, int32_t total_work, int32_t *out);
 
 /*
+ * Balanced split plan [host] (TriAxialKV key design 4: splits of one precision each;
+ * Tangram steps 6-7: split counts fixed ahead of the decode by each head's work).
+ * ranges, out, max_out, n_out and split_offsets as for kvq_plan_splits.  The work
+ * of a (table, head) is the sum over its ranges of tokens x class_cost[cls]
+ * (class_cost [host, may be NULL]: float [3], all > 0; NULL = the default for g:
+ * 1.0 / 1.0 / 6.0 per INT2 / INT4 / FP16 token-head, and 1.0 / 0.82 / 6.0 for
+ * 4 < g <= 8, where a wave computes two query tiles and an INT4 window costs less
+ * than an INT2 one).  The heads' split counts are kvq_balanced_split_counts of
+ * those works over total_splits work groups (so requests of different lengths end
+ * together instead of the longest straggling), each shared among the head's ranges
+ * as kvq_plan_splits shares splits_per_head.  g [in]: query heads per KV head (the
+ * default costs only).  splits_per_head [host, may be NULL]: int32
+ * [n_tables*heads_per_page] receives the counts.
+ * Errors: INVALID_ARG (as kvq_plan_splits; g or total_splits not positive),
+ * CAPACITY (max_out).
+ */
+kvq_status kvq_plan_balanced(const kvq_split *ranges, int32_t n_ranges, int32_t batch,
+                             int32_t hkv, int32_t heads_per_page, int32_t g,
+                             int32_t total_splits, const float *class_cost, kvq_split *out,
+                             int32_t max_out, int32_t *n_out, int32_t *split_offsets,
+                             int32_t *splits_per_head);
+
+/*
  * Head groups of ragged tables and their memory [host] (Tangram: the KV heads of one
  * group share a slot-map table, sized for the group's largest budget, and each head
  * reads its own prefix of it).  budgets [host] float [hkv], 0 < r_h <= 1;

@@ -55,6 +55,14 @@ static int64_t token_bytes(int cls) { return cls == KVQ_INT2 ? 96 : cls == KVQ_I
 // hybrid-anchor decode at 12 splits per head: 6.0 gave 557 us per layer against 575 us
 // for 8.0 and 606 us for 12.0: four FP16 splits per head, one resident round).
 static const float kDefaultTokenCost[3] = {1.0f, 1.0f, 6.0f};
+// With two query tiles per wave (g = 5 .. 8) an INT2 window costs more than an INT4 one:
+// its key build and the two tiles' zero terms take more dequantization work, while the
+// INT4 window's extra bytes hide behind it.  Measured on the Qwen3-VL-32B-shaped decode
+// (g = 8): INT4 splits given the same tokens x cost as INT2 splits of their head took
+// 0.82 of their time (per-split timestamps, 136 against 167 us).
+static const float kTwoTileTokenCost[3] = {1.0f, 0.82f, 6.0f};
+
+static const float *default_token_cost(int32_t g) { return g > 4 && g <= 8 ? kTwoTileTokenCost : kDefaultTokenCost; }
 
 }  // namespace kvq
 
@@ -141,6 +149,24 @@ kvq_status emit_plan(const kvq_split *ranges, int32_t n_ranges, int32_t batch, i
   while (next_pair <= batch * hkv) split_offsets[next_pair++] = w;
   *n_out = w;
   return KVQ_OK;
+}
+
+// The smallest cap c >= 1 on one piece's work such that sum_i ceil(work[i] / c) fits
+// total (the largest work when nothing fits).
+int64_t balanced_cap(const int64_t *work, int32_t n, int64_t total) {
+  int64_t lo = 1, hi = 1;
+  for (int32_t i = 0; i < n; ++i) hi = std::max(hi, work[i]);
+  auto pieces = [&](int64_t cap) {  // non-increasing in cap; at cap = max work, one per entry
+    int64_t sum = 0;
+    for (int32_t i = 0; i < n; ++i) sum += (work[i] + cap - 1) / cap;
+    return sum;
+  };
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (pieces(mid) <= total) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
 }
 
 // The ranges of one (table, head): i0 .. i1 - 1.
@@ -361,24 +387,50 @@ size_t kvq_decode_work_bytes(int32_t n_groups) {
 
 kvq_status kvq_balanced_split_counts(const int64_t *work, int32_t n, int32_t total_work, int32_t *out) {
   if (!work || !out || n <= 0 || total_work <= 0) return fail(KVQ_ERR_INVALID_ARG, "bad balanced-count arguments");
-  int64_t hi = 1;
-  for (int32_t i = 0; i < n; ++i) {
+  for (int32_t i = 0; i < n; ++i)
     if (work[i] < 0) return fail(KVQ_ERR_INVALID_ARG, "work[%d] is negative", i);
-    hi = std::max(hi, work[i]);
-  }
-  auto pieces = [&](int64_t cap) {  // non-increasing in cap; at cap = max work, one per entry
-    int64_t sum = 0;
-    for (int32_t i = 0; i < n; ++i) sum += (work[i] + cap - 1) / cap;
-    return sum;
-  };
-  int64_t lo = 1;  // smallest cap whose pieces fit (or the largest work, when nothing fits)
-  while (lo < hi) {
-    const int64_t mid = lo + (hi - lo) / 2;
-    if (pieces(mid) <= total_work) hi = mid;
-    else lo = mid + 1;
-  }
-  for (int32_t i = 0; i < n; ++i) out[i] = (int32_t)((work[i] + lo - 1) / lo);
+  const int64_t cap = balanced_cap(work, n, total_work);
+  for (int32_t i = 0; i < n; ++i) out[i] = (int32_t)((work[i] + cap - 1) / cap);
   return KVQ_OK;
+}
+
+kvq_status kvq_plan_balanced(const kvq_split *ranges, int32_t n_ranges, int32_t batch, int32_t hkv,
+                             int32_t heads_per_page, int32_t g, int32_t total_splits, const float *class_cost,
+                             kvq_split *out, int32_t max_out, int32_t *n_out, int32_t *split_offsets,
+                             int32_t *splits_per_head) {
+  if (g <= 0 || total_splits <= 0) return fail(KVQ_ERR_INVALID_ARG, "g and total_splits must be positive");
+  const float *cost = class_cost ? class_cost : default_token_cost(g);
+  for (int c = 0; c < 3; ++c)
+    if (!(cost[c] > 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "class cost %d is not positive", c);
+  if (n_ranges < 0 || batch < 0 || hkv <= 0 || heads_per_page <= 0 || hkv % heads_per_page)
+    return fail(KVQ_ERR_INVALID_ARG, "bad plan shape");
+  if ((n_ranges > 0 && !ranges) || !n_out || !split_offsets || (max_out > 0 && !out))
+    return fail(KVQ_ERR_INVALID_ARG, "NULL plan array");
+  const int32_t n_tables = batch * (hkv / heads_per_page);
+  kvq_status st = check_ranges(ranges, n_ranges, n_tables, heads_per_page);
+  if (st != KVQ_OK) return st;
+  // Work of every (table, head): its tokens x class cost, in 1/256 token units.
+  const size_t n_heads = (size_t)n_tables * heads_per_page;
+  std::vector<int64_t> work(n_heads, 0);
+  for (int32_t i = 0; i < n_ranges; ++i) {
+    const kvq_split &r = ranges[i];
+    work[(size_t)r.table * heads_per_page + r.head] +=
+        std::llround(256.0 * (double)(r.tok_end - r.tok_begin) * (double)cost[r.cls]);
+  }
+  std::vector<int32_t> counts(n_heads, 0);
+  if (n_heads > 0) {
+    const int64_t cap = balanced_cap(work.data(), (int32_t)n_heads, total_splits);
+    for (size_t h = 0; h < n_heads; ++h) counts[h] = (int32_t)((work[h] + cap - 1) / cap);
+  }
+  if (splits_per_head)
+    for (size_t h = 0; h < n_heads; ++h) splits_per_head[h] = counts[h];
+  std::vector<int64_t> pieces((size_t)n_ranges, 0);
+  for (int32_t i0 = 0, i1; i0 < n_ranges; i0 = i1) {
+    i1 = head_end(ranges, n_ranges, i0);
+    share_pieces(ranges, i0, i1, counts[(size_t)ranges[i0].table * heads_per_page + ranges[i0].head], cost,
+                 [](const kvq_split &) { return true; }, pieces);
+  }
+  return emit_plan(ranges, n_ranges, batch, hkv, heads_per_page, pieces, out, max_out, n_out, split_offsets);
 }
 
 kvq_status kvq_head_group_plan(const float *budgets, int32_t hkv, int32_t heads_per_group, int64_t n_tokens,

@@ -76,6 +76,7 @@ _SIGS = {
     "kvq_prefill_workspace_bytes": ([_i32, _i32, _i32], ctypes.c_size_t),
     "kvq_select_vertical_lines": ([_P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32,
                                    ctypes.c_float, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "kvq_plan_balanced": ([_P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P, _P], ctypes.c_int),
     "kvq_decode_attn": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P, _P,
                          _P], ctypes.c_int),
     "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
@@ -501,6 +502,26 @@ def aot_split_counts(budgets: np.ndarray, batch: int, total_work: int) -> np.nda
     _check(_lib.kvq_aot_split_counts(_hptr(b), b.shape[0], batch, total_work, _hptr(out)),
            "kvq_aot_split_counts")
     return out
+
+
+def plan_balanced(ranges: np.ndarray, batch: int, hkv: int, heads_per_page: int, g: int, total_splits: int,
+                  class_cost=None, max_out: Optional[int] = None):
+    """Split counts per (table, head) balanced over tokens x class cost (kvq_plan_balanced).
+    Returns (splits int32 [n_out, 5], split_offsets int32 [batch*hkv + 1],
+    splits_per_head int32 [n_tables*heads_per_page])."""
+    r = np.ascontiguousarray(np.asarray(ranges).view(np.int32).reshape(-1, 5))
+    n_heads = batch * hkv  # n_tables * heads_per_page
+    if max_out is None:  # a head may get one piece per non-empty range beyond its count
+        max_out = max(int(total_splits), n_heads) + len(r) + 1
+    out = np.zeros((max_out, 5), np.int32)
+    offsets = np.zeros(batch * hkv + 1, np.int32)
+    sph = np.zeros(n_heads, np.int32)
+    n_out = _i32()
+    cc = None if class_cost is None else np.ascontiguousarray(class_cost, np.float32)
+    _check(_lib.kvq_plan_balanced(_hptr(r), r.shape[0], batch, hkv, heads_per_page, g, total_splits, _hptr(cc),
+                                  _hptr(out), max_out, ctypes.byref(n_out), _hptr(offsets), _hptr(sph)),
+           "kvq_plan_balanced")
+    return out[: n_out.value].copy(), offsets, sph
 
 
 def balanced_split_counts(work, total_work: int) -> np.ndarray:

@@ -206,6 +206,47 @@ def test_balanced_split_counts_minimal_cap(kvq):
         kvq.balanced_split_counts(np.array([3, -1], np.int64), 4)
 
 
+def test_plan_balanced_counts_follow_cost_weighted_work(kvq):
+    """kvq_plan_balanced: a head's split count is the balanced count of its tokens x class
+    cost (in 1/256 token units), its pieces are kvq_plan_splits' pieces for that count,
+    equal heads get equal counts, and the default INT4 weight is 0.82 only for 4 < g <= 8."""
+    rng = np.random.default_rng(11)
+    batch, hkv, hpp = 4, 2, 2
+    items = []
+    for t in range(batch * hkv // hpp):
+        for h in range(hpp):
+            n2 = 32 * int(rng.integers(0, 200))
+            n4 = int(rng.integers(0, 5000))
+            if n2:
+                items.append((t, h, 0, 0, n2))
+            if n4:
+                items.append((t, h, 1, n2, n2 + n4))
+    ranges = _ranges(items, kvq)
+    r = np.asarray(ranges).view(np.int32).reshape(-1, 5)
+    for g, w4 in ((4, 1.0), (8, 0.82), (16, 1.0)):
+        total = 40
+        splits, offsets, sph = kvq.plan_balanced(ranges, batch, hkv, hpp, g, total)
+        work = np.zeros(batch * hkv, np.int64)
+        for t, h, c, b, e in r:
+            work[t * hpp + h] += int(round(256.0 * (e - b) * (1.0 if c == 0 else w4)))
+        assert np.array_equal(sph, kvq.balanced_split_counts(work, total))
+        ref, ref_off = kvq.plan_splits(ranges, batch, hkv, hpp, splits_per_head=sph,
+                                       class_cost=[1.0, w4, 6.0])
+        assert np.array_equal(splits, ref) and np.array_equal(offsets, ref_off)
+    # equal heads: equal counts, the same plan as a fixed count per head
+    eq = _ranges([(t, h, 0, 0, 4096) for t in range(4) for h in range(2)], kvq)
+    splits, offsets, sph = kvq.plan_balanced(eq, 4, 2, 2, 4, 64)
+    ref, ref_off = kvq.plan_splits(eq, 4, 2, 2, splits_per_head=np.full(8, 8, np.int32))
+    assert np.all(sph == 8) and np.array_equal(splits, ref) and np.array_equal(offsets, ref_off)
+    # a long head gets more splits than a short one, in proportion
+    two = _ranges([(0, 0, 1, 0, 30000), (0, 1, 1, 0, 10000)], kvq)
+    _, _, sph = kvq.plan_balanced(two, 1, 2, 2, 4, 8)
+    assert sph.tolist() == [6, 2]
+    for bad in ((0, 8), (4, 0)):
+        with pytest.raises(kvq.KvqError):
+            kvq.plan_balanced(two, 1, 2, 2, *bad)
+
+
 def test_prefill_workspace_and_validation(kvq):
     """The prefill scratch size follows its region list (V^T and V-hat^T fp16, fp16 keep
     mask, line positions, per-tile line counts, gathered K and V^T, K codes as bf16,

@@ -301,8 +301,8 @@ def _resident_plan(gpu, ragged_plan="aot"):
         return gpu.plan(splits_per_head=gpu.kvq.balanced_split_counts(read, per_cu * n_cu))
     if w.head_budget is not None:
         return gpu.plan(splits_per_head=gpu.kvq.aot_split_counts(w.head_budget, w.batch, per_cu * n_cu))
-    sph = max(1, (per_cu * n_cu) // (w.batch * w.hkv))
-    return gpu.plan(splits_per_head=np.full(w.batch * w.hkv, sph, np.int32))
+    splits, offsets, _ = gpu.kvq.plan_balanced(gpu.ranges, w.batch, w.hkv, w.heads_per_page, w.g, per_cu * n_cu)
+    return splits, offsets
 
 
 def _full_size_sampled(name, make, requests, compact=False, ragged_plan="aot"):
