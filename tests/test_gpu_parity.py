@@ -325,10 +325,39 @@ def _full_size_sampled(name, make, requests, compact=False, ragged_plan="aot"):
     assert np.allclose(lse[requests], ref_lse, rtol=0, atol=1e-3)
 
 
-def test_full_size_hybrid_anchor_sampled():
+def _full_size_full(name, make, compact=False, ragged_plan="aot"):
+    """A full-size workload on both sides, each from its own seeded copy, with the
+    benchmark's plan on the GPU: every pool byte, the tables (and class counts or live
+    counts) bit-exact, and every request's rows against the oracle."""
+    _say(f"full-size {name}: generating on the GPU" + (" (compacted slot maps)" if compact else "")
+         + f", {ragged_plan} plan, compared in full")
+    gpu = DeviceRun(make(), compact=compact)
+    orc = OracleRun(make(), compact=compact)
+    torch.cuda.synchronize()
+    assert int(gpu.err.item()) == 0
+    _pools_equal(gpu, orc)
+    assert np.array_equal(gpu.tables.cpu().numpy(), orc.tables)
+    if gpu.w.kind == synth.PAGES:
+        assert np.array_equal(gpu.class_counts.cpu().numpy(), orc.class_counts)
+    if compact:
+        assert np.array_equal(gpu.live_tokens.cpu().numpy(), orc.live_tokens)
+    _say(f"  {gpu.w.note}; pools (every byte) and tables bit-exact")
+    splits, offsets = _resident_plan(gpu, ragged_plan)
+    out, lse, _, _ = gpu.decode(splits, offsets)
+    assert int(gpu.err.item()) == 0
+    ref, ref_lse = orc.attend(n_threads=16)
+    err = row_metric(ref, out.cpu().numpy())
+    _say(f"  {splits.shape[0]} splits decoded; row error over all {gpu.w.batch} requests {err:.2e}")
+    assert err <= TOL
+    assert np.allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+def test_full_size_hybrid_anchor():
     """FP16 anchors at full size (32 requests x 8 heads x 65536 tokens, INT4 prefix and
-    FP16 vertical-line / staging / window segments): two launches (INT4, FP16)."""
-    _full_size_sampled("hybrid_anchor", lambda: synth.hybrid_anchor(device="cuda"), [7])
+    FP16 vertical-line / staging / window segments; two launches, INT4 and FP16) against
+    the oracle in full: every pool byte, the reordered tables and class counts, and the
+    rows of all 32 requests."""
+    _full_size_full("hybrid_anchor", lambda: synth.hybrid_anchor(device="cuda"))
 
 
 def test_full_size_ragged_dead_sampled():
@@ -347,15 +376,12 @@ def test_full_size_ragged_dead_compacted_sampled():
     _full_size_sampled("ragged_dead", lambda: synth.ragged_dead(device="cuda"), pick, compact=True)
 
 
-def test_full_size_ragged_dead_balanced_sampled():
-    """The full-size ragged workload, compacted, under balanced split counts over the
-    tokens each head reads (kvq_balanced_split_counts); four requests sampled: the
-    shortest, the longest and two between."""
-    lens = synth.ragged_lengths()
-    order = np.argsort(lens, kind="stable")
-    pick = sorted({int(order[0]), int(order[len(order) // 3]), int(order[2 * len(order) // 3]), int(order[-1])})
-    _full_size_sampled("ragged_dead", lambda: synth.ragged_dead(device="cuda"), pick, compact=True,
-                       ragged_plan="tokens")
+def test_full_size_ragged_dead_balanced():
+    """The full-size ragged workload (64 requests, 4K-128K tokens, 20 % dead slots),
+    compacted, under balanced split counts over the tokens each head reads (the
+    benchmark's plan), against the oracle in full: every pool byte, the compacted slot
+    maps and live counts, and the rows of all 64 requests."""
+    _full_size_full("ragged_dead", lambda: synth.ragged_dead(device="cuda"), compact=True, ragged_plan="tokens")
 
 
 def test_qwen3_vl_agentic_small():
