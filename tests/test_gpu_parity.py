@@ -535,6 +535,49 @@ def test_slot_map_anchors(fp8):
     assert np.allclose(part_lse.cpu().numpy(), ref_lse, atol=1e-3, rtol=1e-4)
 
 
+def test_reorder_at_the_entry_limit():
+    """kvq_reorder_pages at its limit of 32,768 entries per table (a 128 KB LDS stage):
+    tables of 32,768, 32,767, 1 and 0 entries mixing INT2 page pairs, INT4 and FP16
+    pages, bit-exact with the oracle's stable partition and class counts; one entry
+    more is rejected before any launch."""
+    from mixed_precision_quantized_amd import kvq
+    from oracle import oracle
+    limit = 32768
+    rng = np.random.default_rng(41)
+    n2, n4, n16 = 2 * 6000, 9000, 3000
+    tabs = np.full((4, limit), -1, np.int32)
+    fill = [limit, limit - 1, 1, 0]
+    for t, n in enumerate(fill):
+        row = []
+        while len(row) < n:
+            kind = rng.integers(0, 3) if n - len(row) >= 2 else rng.integers(1, 3)
+            if kind == 0:  # an INT2 page pair, its two pages one after the other
+                p = 2 * int(rng.integers(0, n2 // 2))
+                row += [p, p + 1]
+            elif kind == 1:
+                row.append(n2 + int(rng.integers(0, n4)))
+            else:
+                row.append(n2 + n4 + int(rng.integers(0, n16)))
+        tabs[t, :n] = row
+    n_entries = np.array(fill, np.int32)
+    orc_tabs = tabs.copy()
+    orc_counts = oracle.Cache(1, n2, n4, n16).reorder(orc_tabs, n_entries)
+    cache = kvq.Cache(1, (n2, n4, n16), "cuda")
+    g_tabs = torch.as_tensor(tabs, device="cuda").contiguous()
+    g_n = torch.as_tensor(n_entries, device="cuda")
+    counts = torch.zeros((4, 3), dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kvq.reorder_pages(cache, g_tabs, g_n, counts, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(g_tabs.cpu().numpy(), orc_tabs)
+    assert np.array_equal(counts.cpu().numpy(), orc_counts)
+    _say(f"reorder at {limit} entries per table: tables and counts bit-exact {orc_counts[0].tolist()}")
+    wide = torch.full((1, limit + 1), n2, dtype=torch.int32, device="cuda")
+    with pytest.raises(kvq.KvqError):
+        kvq.reorder_pages(cache, wide, torch.ones(1, dtype=torch.int32, device="cuda"), dev_err=err)
+
+
 def test_reorder_and_decode_past_131072_tokens():
     """A request of 163,840 tokens (a 128K prompt plus 32K generated tokens; 10,240
     table entries, past the 8,192 a 64 KB LDS stage holds): the reordered table and its
