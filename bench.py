@@ -237,7 +237,16 @@ def main():
     ap.add_argument("--decode", choices=("static", "shared"), default="static",
                     help="page-table decode: fixed splits (kvq_decode_attn), or the resident workers of each "
                          "(request, head) range sharing its windows (kvq_decode_attn_shared)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="profiling: run the profiling build libkvq_timeline.so and print a per-wave timeline "
+                         "summary of the fixed-split decode (graph replays) instead of the result line")
+    ap.add_argument("--timeline-samples", type=int, default=5, help="launches summarized by --timeline")
     args = ap.parse_args()
+    if args.timeline:
+        # before the binding is imported: it loads the library named here
+        os.environ["KVQ_LIBRARY"] = os.path.join(ROOT, "mixed_precision_quantized_amd", "libkvq_timeline.so")
+        if args.decode != "static" or args.eager:
+            sys.exit("--timeline records the fixed-split decode replayed as a graph")
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(requests and KV heads shard with no exchange; see the design notes)", file=sys.stderr)
@@ -278,7 +287,9 @@ def main():
     eff_layer, decode_bytes = effective_bytes(w0, anchor_fp8=args.anchor_fp8)
     log(f"workload: {w0.note}; effective bytes per layer {eff_layer}")
     cpu_sample = None
-    if not args.no_cpu_baseline and w0.kind == synth.PAGES:
+    if args.timeline and (w0.kind != synth.PAGES or w0.n_pages[2]):
+        sys.exit("--timeline records the page-table decode of INT2 / INT4 splits (no slot maps, no FP16 pages)")
+    if not args.no_cpu_baseline and not args.timeline and w0.kind == synth.PAGES:
         req = list(range(min(args.cpu_requests, w0.batch)))
         cpu_sample = synth.subset(make(device=dev, layer=0), req, device="cpu")
     lists = {n: torch.as_tensor(a, device=dev) for n, a in gpu.lists.arrays().items()}
@@ -435,6 +446,8 @@ def main():
         for _ in range(args.warmup):
             run_step()
     torch.cuda.synchronize()
+    if args.timeline:
+        return wave_timeline(args, kvq, run_decodes, stream, splits, layers, description)
 
     def timed(fn, reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -509,6 +522,56 @@ def main():
     if cpu_sample is not None:
         result["cpu_baseline"] = cpu_baseline(cpu_sample, w0, args, make)
     print(json.dumps(result), flush=True)
+
+
+def wave_timeline(args, kvq, run_decodes, stream, splits, layers, description):
+    """Per-wave timeline of the decode kernel (profiling build): after three back-to-back
+    replays of the layers' decode launches the buffer holds the last launch; repeated
+    --timeline-samples times.  Prints one JSON line of per-launch summaries."""
+    import numpy as np
+    import torch
+    n = splits.shape[0]
+    buf = torch.zeros((n, 8), dtype=torch.int64, device="cuda")
+    kvq.wave_timeline(buf)
+    cls = np.asarray(splits).view(np.int32).reshape(n, 5)[:, 2]
+    samples = []
+    for _ in range(args.timeline_samples):
+        buf.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                run_decodes()
+        torch.cuda.synchronize()
+        r = buf.cpu().numpy().astype(np.int64)
+        assert (r[:, 2] > 0).all(), "a split recorded no end"
+        t0 = r[:, 0].min()
+        st, fw, en = ((r[:, k] - t0) / 100.0 for k in (0, 1, 2))  # us (100 MHz)
+        mhz = (r[:, 4] - r[:, 3]) / np.maximum(r[:, 2] - r[:, 0], 1) * 100.0
+        xcc = r[:, 5] & 0xF
+        hw = r[:, 6]
+        cu = xcc * 4096 + ((hw >> 13) & 7) * 32 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 15)
+        per_cu = [float(np.mean(en[cu == c])) for c in np.unique(cu)]
+        per_xcd = [float(np.mean(en[xcc == x])) for x in range(8) if (xcc == x).any()]
+        rate = r[:, 7] / np.maximum(en - fw, 1e-3)
+        samples.append({
+            "span_us": round(float(en.max()), 1),
+            "start_max_us": round(float(st.max()), 2),
+            "first_window_us": {"median": round(float(np.median(fw)), 1), "p90": round(float(np.percentile(fw, 90)), 1)},
+            "end_us": {q: round(float(np.percentile(en, p)), 1) for q, p in (("p50", 50), ("p90", 90), ("p99", 99))},
+            "mean_wave_us": round(float(np.mean(en - st)), 1),
+            "end_median_per_xcd_us": [round(float(np.median(en[xcc == x])), 1) for x in range(8) if (xcc == x).any()],
+            "clock_mhz_median_per_xcd": [round(float(np.median(mhz[xcc == x]))) for x in range(8) if (xcc == x).any()],
+            "max_cu_mean_end_us": round(max(per_cu), 1),
+            "max_xcd_mean_end_us": round(max(per_xcd), 1),
+            "windows_per_us_median": {c: round(float(np.median(rate[cls == k])), 3)
+                                      for c, k in (("int2", 0), ("int4", 1)) if (cls == k).any()},
+        })
+        log(f"timeline: span {samples[-1]['span_us']} us, median end {samples[-1]['end_us']['p50']} us, "
+            f"mean wave {samples[-1]['mean_wave_us']} us")
+    kvq.wave_timeline(None)
+    print(json.dumps({"kind": "wave_timeline", "workload": description + f", {layers} layers",
+                      "splits": n, "launch": "the last of three back-to-back replays of the layers' decode launches",
+                      "samples": samples}), flush=True)
 
 
 def bench_vl(args):

@@ -581,6 +581,19 @@ kvq_status kvq_head_group_plan(const float *budgets, int32_t hkv, int32_t heads_
                                int32_t *table_slots, int64_t *bytes);
 
 /*
+ * Per-wave timeline [profiling builds only] for measuring where a decode launch's
+ * time goes (not part of the method).  In a build compiled with KVQ_WAVE_TIMELINE
+ * (libkvq_timeline.so), every later fixed-split page-table decode launch on the current
+ * device writes, for split s, 8 uint64 words at buffer[8 s ..] [dev, caller-owned,
+ * at least 64 B per split]: the wave's start, the landing of its first window and its
+ * end (s_memrealtime, 100 MHz), the shader clock (s_memtime) at its start and end, the
+ * hardware XCC_ID and HW_ID registers, and its window count.  NULL stops the
+ * recording.  Launches that overlap on one device write the same buffer.  Other builds
+ * return UNSUPPORTED.  Errors: UNSUPPORTED, HIP.
+ */
+kvq_status kvq_wave_timeline(void *buffer);
+
+/*
  * Work groups (one wavefront each) of the decode kernel that fit on the current
  * device at once: *per_cu from the HIP occupancy API, *n_cu the compute-unit
  * count.  g (query heads per KV head) and table_kind select the kernel: page

@@ -4,6 +4,10 @@ The write path (quantize / pack / reorder) is compiled with -ffp-contract=off an
 fp32 denormals kept, so its fp32 arithmetic rounds exactly as IEEE specifies.
 Every HIP translation unit is compiled without packed fp32 instructions.
 
+`python build.py --timeline` builds libkvq_timeline.so: the same sources with the decode
+kernel's per-wave timeline compiled in (KVQ_WAVE_TIMELINE; kvq_wave_timeline records
+it), for `bench.py --timeline`.
+
 `python build.py --sanitize` builds libkvq_san.so instead: the same sources with
 AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (device code is
 built as usual), for the CPU tests of the host entry points:
@@ -21,6 +25,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 LIB_SAN = os.path.join(HERE, "libkvq_san.so")
+LIB_TIMELINE = os.path.join(HERE, "libkvq_timeline.so")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
@@ -45,13 +50,15 @@ SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=unde
             "-fno-omit-frame-pointer", "-g"]
 
 
-def build(verbose: bool = False, sanitize: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False, timeline: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     extra = SANITIZE if sanitize else []
     for src, flags in SOURCES:
-        obj = os.path.join(BUILD, src + (".san.o" if sanitize else ".o"))
-        cmd = ["hipcc", *COMMON, *flags, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        probe = timeline and src == "kvq_decode.hip"  # the other objects are shared
+        obj = os.path.join(BUILD, src + (".san.o" if sanitize else ".timeline.o" if probe else ".o"))
+        defs = ["-DKVQ_WAVE_TIMELINE"] if probe else []
+        cmd = ["hipcc", *COMMON, *flags, *defs, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,7 +69,7 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
         if err.strip() and verbose:
             print(err, flush=True)
         objs.append(obj)
-    out = LIB_SAN if sanitize else LIB
+    out = LIB_SAN if sanitize else LIB_TIMELINE if timeline else LIB
     tmp = out + ".tmp"
     cmd = ["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
     if sanitize:
@@ -75,5 +82,5 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:], timeline="--timeline" in sys.argv[1:])
     sys.exit(0)

@@ -58,6 +58,22 @@ typedef const __attribute__((address_space(1))) uint8_t *gbytes;
 typedef const __attribute__((address_space(4))) int32_t *cints;
 
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+
+// Per-wave timeline of the fixed-split page-table decode, compiled in only when
+// KVQ_WAVE_TIMELINE is defined (the profiling build libkvq_timeline.so): per split, 8
+// words: the wave's start, its first window landed and its end (s_memrealtime, 100 MHz),
+// the shader clock (s_memtime) at start and end, XCC_ID, HW_ID and the split's window
+// count.  Every lane stores the same value.
+#ifdef KVQ_WAVE_TIMELINE
+__device__ uint64_t *g_timeline = nullptr;
+__device__ __forceinline__ void timeline_put(int s_idx, int k, uint64_t v) {
+  uint64_t *p = g_timeline;
+  if (p) p[(size_t)s_idx * 8 + k] = v;
+}
+#define KVQ_TIMELINE(s_idx, k, v) timeline_put((s_idx), (k), (v))
+#else
+#define KVQ_TIMELINE(s_idx, k, v) ((void)0)
+#endif
 __device__ __forceinline__ uint4 ld4(gbytes p) {
   const u4v v = *reinterpret_cast<const __attribute__((address_space(1))) u4v *>(p);
   return make_uint4(v[0], v[1], v[2], v[3]);
@@ -1240,6 +1256,7 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
   auto step = [&](int32_t n, int slot_c, int slot_i) {
     if (W == 1) prio.step(n);  // (the waves of one block move in step anyway)
     ld.wait();
+    if (n == 0) KVQ_TIMELINE(s_idx, 1, __builtin_amdgcn_s_memrealtime());
     if (W > 1) __syncthreads();  // every wave's chunks of window n have landed, window n - 1 is read
     const uint32_t ok = (okq >> (2 * (A - 1))) & 3u;
     const int32_t Tn = T0 + 32 * (n + A);
@@ -1280,6 +1297,9 @@ __device__ void run_split_ring(const DecodeArgs &a, const kvq_split &sp, int s_i
   wait_copies<0>();  // no copy outlives the wave
   if (ld.errs) report(a.err, (int32_t)ld.errs);
   R.finish(s_idx);
+  KVQ_TIMELINE(s_idx, 2, __builtin_amdgcn_s_memrealtime());
+  KVQ_TIMELINE(s_idx, 4, __builtin_amdgcn_s_memtime());
+  KVQ_TIMELINE(s_idx, 7, (uint64_t)nw);
 }
 
 
@@ -1821,6 +1841,17 @@ decode_ring_kernel(DecodeArgs a) {
     shared_exit(a, s_idx);
     return;
   }
+#ifdef KVQ_WAVE_TIMELINE
+  {
+    KVQ_TIMELINE(s_idx, 0, __builtin_amdgcn_s_memrealtime());
+    KVQ_TIMELINE(s_idx, 3, __builtin_amdgcn_s_memtime());
+    uint32_t xcc, hwid;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hwid));
+    KVQ_TIMELINE(s_idx, 5, xcc);
+    KVQ_TIMELINE(s_idx, 6, hwid);
+  }
+#endif
   if (!split_check<QT, false, true>(a, s_idx, sp, 4 * QT * wave)) return;
   if (sp.cls == KVQ_INT4) run_split_ring<KVQ_INT4, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
   else if (sp.cls == KVQ_INT2) run_split_ring<KVQ_INT2, W, QT>(a, sp, s_idx, L[wave], ring, idr[wave], wave);
@@ -2166,6 +2197,18 @@ extern "C" kvq_status kvq_lse_merge(const float *part_o, const float *part_lse, 
   hipLaunchKernelGGL(lse_merge_kernel, dim3(batch * hq), dim3(64), 0, static_cast<hipStream_t>(stream), part_o,
                      part_lse, n_splits, split_offsets, hq, hkv, out, out_dtype, out_lse);
   return launched("lse_merge_kernel");
+}
+
+extern "C" kvq_status kvq_wave_timeline(void *buffer) {
+#ifdef KVQ_WAVE_TIMELINE
+  uint64_t *p = static_cast<uint64_t *>(buffer);
+  const hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), &p, sizeof p);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "timeline buffer: %s", hipGetErrorString(e));
+  return KVQ_OK;
+#else
+  (void)buffer;
+  return fail(KVQ_ERR_UNSUPPORTED, "this build records no wave timeline (build with KVQ_WAVE_TIMELINE)");
+#endif
 }
 
 extern "C" kvq_status kvq_decode_occupancy(int32_t g, int32_t table_kind, int32_t *per_cu, int32_t *n_cu) {

@@ -77,6 +77,7 @@ _SIGS = {
     "kvq_select_vertical_lines": ([_P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32,
                                    ctypes.c_float, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "kvq_plan_balanced": ([_P, _i32, _i32, _i32, _i32, _i32, _i32, _P, _P, _i32, _P, _P, _P], ctypes.c_int),
+    "kvq_wave_timeline": ([_P], ctypes.c_int),
     "kvq_decode_attn": ([_P, _P, _i32, _i32, _i32, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P, _P,
                          _P], ctypes.c_int),
     "kvq_lse_merge": ([_P, _P, _i32, _P, _i32, _i32, _i32, _P, _i32, _P, _P], ctypes.c_int),
@@ -532,6 +533,15 @@ def balanced_split_counts(work, total_work: int) -> np.ndarray:
     _check(_lib.kvq_balanced_split_counts(_hptr(w), w.shape[0], total_work, _hptr(out)),
            "kvq_balanced_split_counts")
     return out
+
+
+def wave_timeline(buffer: Optional[torch.Tensor]):
+    """Profiling builds (libkvq_timeline.so) only: later fixed-split page-table decode
+    launches record 8 uint64 words per split into buffer (int64 [n_splits, 8], device);
+    None stops the recording."""
+    if buffer is not None:
+        assert buffer.dtype == torch.int64 and buffer.is_contiguous() and buffer.shape[-1] == 8
+    _check(_lib.kvq_wave_timeline(_dptr(buffer)), "kvq_wave_timeline")
 
 
 def decode_occupancy(g: int, table_kind: int = 0):

@@ -247,6 +247,19 @@ def test_plan_balanced_counts_follow_cost_weighted_work(kvq):
             kvq.plan_balanced(two, 1, 2, 2, *bad)
 
 
+def test_wave_timeline_only_in_the_profiling_build(kvq):
+    """The production library records no timeline: kvq_wave_timeline says UNSUPPORTED
+    (no device call is made); the profiling build exports the same symbols."""
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.wave_timeline(None)
+    assert e.value.status == -2  # KVQ_ERR_UNSUPPORTED
+    path = os.path.join(ROOT, "mixed_precision_quantized_amd", "libkvq_timeline.so")
+    if os.path.exists(path):
+        lib = ctypes.CDLL(path)
+        for n in kvq.EXPORTED:
+            assert hasattr(lib, n), n
+
+
 def test_prefill_workspace_and_validation(kvq):
     """The prefill scratch size follows its region list (V^T and V-hat^T fp16, fp16 keep
     mask, line positions, per-tile line counts, gathered K and V^T, K codes as bf16,
