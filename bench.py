@@ -243,8 +243,9 @@ def main():
     ap.add_argument("--timeline-samples", type=int, default=5, help="launches summarized by --timeline")
     args = ap.parse_args()
     if args.timeline:
-        # before the binding is imported: it loads the library named here
-        os.environ["KVQ_LIBRARY"] = os.path.join(ROOT, "mixed_precision_quantized_amd", "libkvq_timeline.so")
+        # before the binding is imported: it loads the library named here (another
+        # profiling build of the same sources may be named by KVQ_LIBRARY)
+        os.environ.setdefault("KVQ_LIBRARY", os.path.join(ROOT, "mixed_precision_quantized_amd", "libkvq_timeline.so"))
         if args.decode != "static" or args.eager:
             sys.exit("--timeline records the fixed-split decode replayed as a graph")
     if args.gpus != 1:
