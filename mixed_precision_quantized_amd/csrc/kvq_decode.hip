@@ -22,7 +22,7 @@
 //   product is removed per group together with the zero term z * sum(q).  INT2 K has
 //   per-channel scales: the code operand becomes s * (c - 2), exact in fp16 because
 //   c - 2 is in {-2, -1, 0, 1}, and the zero term sum q (z + 2 s) of the 32-token pair
-//   enters through the accumulator start.
+//   is added to the logits.
 //   Online softmax in base 2 per query with 16-lane DPP row reductions; the running
 //   state is rescaled only when a row maximum grows.
 //   P V on MFMA.  Rows (query j', group i); the weight operand is p * s (fp16) for
@@ -444,10 +444,13 @@ struct SplitRun {
   // for both tiles instead of one per tile with the weights scaled per channel group.
   static constexpr bool kVS = QT == 2;
   f4 acc[kVS ? 1 : QT][8];  // P V accumulators
-  float m_run[QT], l_run[QT];
+  float m_run[QT], l_run[QT];  // running maximum of the raw logits, sum of the weights
+  float mq[QT];        // m_run qscale (the base-2 maximum the weights are taken against)
   int qbase = 0;       // first query head (of the g) this wave computes
   float zacc[QT];      // row lr: sum of p z over this lane's tokens (V zero term)
-  float asum[QT];      // row lr: sum of the fp16 operand weights p s (V code offset)
+  f4 aone[QT];         // rows 4 lb + e: sums of the fp16 operand weights p s (V code offset),
+                       // the product of the weights operand with a ones operand
+  h8 ones;             // that operand
   static constexpr int kFold = 16;  // windows between folds of those two into acc
   int since = 0;       // windows since the last fold
 
@@ -456,6 +459,10 @@ struct SplitRun {
     scale = kLog2e / sqrtf((float)kHeadDim);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) qscale[qt] = scale * L.qs[4 * qt + lb];
+    {
+      const uint32_t one = in_vgpr(0x3C003C00u);
+      ones = h8_of(one, one, one, one);
+    }
     sel2[0] = pair_sel(lr & 1);  // byte lr & 1: even channels of the lane's half word
     sel2[1] = pair_sel((lr & 1) + 2);
 #pragma unroll
@@ -483,9 +490,10 @@ struct SplitRun {
         qoff[qt][r] = -__shfl(po, 16 * lb + 4 * r);
       }
       m_run[qt] = kNegBig;
+      mq[qt] = kNegBig;
       l_run[qt] = 0.0f;
       zacc[qt] = 0.0f;
-      asum[qt] = 0.0f;
+      aone[qt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
       if (!kVS || qt == 0) {
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[kVS ? 0 : qt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -591,7 +599,7 @@ struct SplitRun {
         } else {
           s = (d[0] + d[1]) + (d[2] + d[3]);
         }
-        x[qt][h] = s * qscale[qt];
+        x[qt][h] = s;  // raw: the softmax applies qscale
       }
     }
     if (partial) {  // tokens that do not count get logit -inf (weight 0)
@@ -681,16 +689,23 @@ struct SplitRun {
     }
     mid();
 
-    // Online softmax per query (the 16 lanes of row lb).
+    // Online softmax per query (the 16 lanes of row lb) on the raw logits: the base-2
+    // logit is x qscale.  The row maximum is taken only when a logit of the wave exceeds
+    // its row's running maximum m_run (rare after the first windows); the weights are
+    // exp2(x qscale - mq) with mq = m_run qscale, one rounding (fma), so at most 1 up
+    // to that rounding.
     float alpha_q[QT];  // (kVS) this window's rescale of query 4 qt + lb
     bool rescaled = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float bm = row_max16(fmaxf(x[qt][0], x[qt][1]));
-      const float mn = fmaxf(m_run[qt], bm);
+      const float t = fmaxf(x[qt][0], x[qt][1]);
       alpha_q[qt] = 1.0f;
-      if (__any(mn > m_run[qt])) {  // rare after the first windows
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mn);
+      if (__any(t > m_run[qt])) {
+        const float mn = fmaxf(m_run[qt], row_max16(t));
+        const float mqn = mn * qscale[qt];
+        // rows whose maximum stays keep alpha 1 (no -inf - -inf); the first rise from
+        // the start values gives 0, which meets an empty state
+        const float alpha = mn > m_run[qt] ? __builtin_amdgcn_exp2f(mq[qt] - mqn) : 1.0f;
         l_run[qt] *= alpha;
         if (kVS) {
           alpha_q[qt] = alpha;
@@ -698,15 +713,18 @@ struct SplitRun {
         } else {
 #pragma unroll
           for (int nt = 0; nt < 8; ++nt) acc[kVS ? 0 : qt][nt] *= alpha;
-          const float alpha_row = __shfl(alpha, 16 * (lr >> 2));  // rows lr belong to query lr / 4
-          zacc[qt] *= alpha_row;
-          asum[qt] *= alpha_row;
+          if (CLS != KVQ_FP16) {
+            aone[qt] *= alpha;  // rows 4 lb .. 4 lb + 3: query lb, this lane's own
+            zacc[qt] *= __shfl(alpha, 16 * (lr >> 2));  // row lr belongs to query lr / 4
+          }
         }
+        mq[qt] = mn > m_run[qt] ? mqn : mq[qt];
         m_run[qt] = mn;
       }
       // v_exp_f32: exp2(-inf) = 0; results below 2^-126 may flush to zero, which no
       // softmax weight of consequence is.
-      const float p0 = __builtin_amdgcn_exp2f(x[qt][0] - m_run[qt]), p1 = __builtin_amdgcn_exp2f(x[qt][1] - m_run[qt]);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[qt][0], qscale[qt], -mq[qt]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[qt][1], qscale[qt], -mq[qt]));
       l_run[qt] += p0 + p1;
       L.p[kVS ? 0 : qt][kVS ? 4 * qt + lb : lb][lr] = (_Float16)p0;
       L.p[kVS ? 0 : qt][kVS ? 4 * qt + lb : lb][16 + lr] = (_Float16)p1;
@@ -748,9 +766,9 @@ struct SplitRun {
           const h2 pp = as_h2(p2[u]), ap2 = pp * as_h2(s2);
           aw[u] = as_u32(ap2);
           zacc[qt] = dot2(pp, as_h2(z2), zacc[qt]);
-          asum[qt] = dot2(ap2, h2{(_Float16)1.0f, (_Float16)1.0f}, asum[qt]);
         }
         ap = h8_of(aw[0], aw[1], aw[2], aw[3]);
+        aone[qt] = mfma(ap, ones, aone[qt]);
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc[kVS ? 0 : qt][nt] = mfma(ap, vb[nt], acc[kVS ? 0 : qt][nt]);
@@ -761,16 +779,13 @@ struct SplitRun {
     }
   }
 
-  // Row (query lb, group lr / 4) totals of the lanes' V zero-term and code-offset sums
-  // (they are kept per P-operand row, lane (lr, lb) for row lr).
-  __device__ __forceinline__ void row_terms(int qt, float &zrow, float &arow) const {
-    float z = zacc[qt], as = asum[qt];
+  // Row (query lb, group lr / 4) total of the lanes' V zero-term sums (they are kept per
+  // P-operand row, lane (lr, lb) for row lr).
+  __device__ __forceinline__ float row_zero(int qt) const {
+    float z = zacc[qt];
     z += __shfl_xor(z, 16);
     z += __shfl_xor(z, 32);
-    as += __shfl_xor(as, 16);
-    as += __shfl_xor(as, 32);
-    zrow = __shfl(z, 4 * lb + (lr >> 2));
-    arow = __shfl(as, 4 * lb + (lr >> 2));
+    return __shfl(z, 4 * lb + (lr >> 2));
   }
 
   // Code offset of channel 8 lr + nt in the V operand.
@@ -787,20 +802,21 @@ struct SplitRun {
   // every 8 windows).  Every 16 windows (512 tokens) the 32K-token Qwen3-8B-shaped rows
   // measure 8.2e-4 against 7.6e-4 at 8, and a launch takes about 0.5 % less time.
   // (Only element lr / 4 of an accumulator is a row this lane reports; the others, rows
-  // of the block-diagonal product that no lane reads, take the same addition.)
+  // of the block-diagonal product that no lane reads, take additions of no meaning.)
   __device__ __forceinline__ void fold() {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float zrow, arow;
-      row_terms(qt, zrow, arow);
-      const float c64 = fmaf(-64.0f, arow, zrow), c16 = fmaf(-16.0f, arow, zrow);
+      const float zrow = row_zero(qt);
+      f4 c64, c16;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const float c = v_offset(nt) == 64.0f ? c64 : c16;
-        acc[kVS ? 0 : qt][nt] += f4{c, c, c, c};
+      for (int e = 0; e < 4; ++e) {
+        c64[e] = fmaf(-64.0f, aone[qt][e], zrow);
+        c16[e] = fmaf(-16.0f, aone[qt][e], zrow);
       }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[kVS ? 0 : qt][nt] += v_offset(nt) == 64.0f ? c64 : c16;
       zacc[qt] = 0.0f;
-      asum[qt] = 0.0f;
+      aone[qt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
 
@@ -814,7 +830,7 @@ struct SplitRun {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float l0 = __shfl(lt[0], 16 * r), l1 = __shfl(lt[QT - 1], 16 * r);
-        const float m0 = __shfl(m_run[0], 16 * r), m1 = __shfl(m_run[QT - 1], 16 * r);
+        const float m0 = __shfl(mq[0], 16 * r), m1 = __shfl(mq[QT - 1], 16 * r);
         const float l_tot = lb == 0 ? l0 : l1, m = lb == 0 ? m0 : m1;
         const int j = qbase + 4 * lb + r;
         const bool any = l_tot > 0.0f;
@@ -834,8 +850,7 @@ struct SplitRun {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float l_tot = row_sum16(l_run[qt]);
-      float zrow, arow;  // row (query lb, group lr / 4)
-      row_terms(qt, zrow, arow);
+      const float zrow = CLS == KVQ_FP16 ? 0.0f : row_zero(qt);  // row (query lb, group lr / 4)
       const int j = qbase + 4 * qt + lb;
       const bool any = l_tot > 0.0f;
       const float inv = any ? 1.0f / l_tot : 0.0f;
@@ -845,13 +860,15 @@ struct SplitRun {
       for (int nt = 0; nt < 8; ++nt) {
         const f4 d = acc[kVS ? 0 : qt][nt];
         const float v = r == 0 ? d[0] : r == 1 ? d[1] : r == 2 ? d[2] : d[3];
+        const f4 ao = aone[qt];
+        const float arow = r == 0 ? ao[0] : r == 1 ? ao[1] : r == 2 ? ao[2] : ao[3];
         o[nt] = any ? (CLS == KVQ_FP16 ? v : fmaf(-v_offset(nt), arow, v) + zrow) * inv : 0.0f;
       }
       if (j < a.g) {
         float4 *dst = reinterpret_cast<float4 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 8 * lr);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-        if (lr == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (m_run[qt] + log2f(l_tot)) * kLn2 : -INFINITY;
+        if (lr == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (mq[qt] + log2f(l_tot)) * kLn2 : -INFINITY;
       }
     }
   }
