@@ -1034,6 +1034,13 @@ struct ProgressPriority {
   }
 };
 
+// 1 if a < b, else 0 (unsigned), computed on the scalar unit: a and b are wave-uniform.
+__device__ __forceinline__ uint32_t s_below(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("s_cmp_lt_u32 %1, %2\n\ts_cselect_b32 %0, 1, 0" : "=s"(r) : "s"(a), "s"(b) : "scc");
+  return r;
+}
+
 template <int CLS, int W>
 struct RingLoader {
   using G = RingGeom<CLS, W>;
@@ -1145,14 +1152,17 @@ struct RingLoader {
     const uint32_t base = ring + (uint32_t)slot * G::kSlotBytes;
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // this wave's reads of the slot are done
     if (real) {
+      // Validity bits on the scalar unit (a comparison the compiler keeps as a lane mask
+      // would be turned into an integer by vector instructions); an invalid id reads the
+      // class's first block.
       const uint32_t r0 = pages.rel(id0), r1 = pages.rel(id1);
-      const bool ok0 = r0 < pages.count, ok1 = r1 < pages.count;
-      const gbytes b0 = pages.block(ok0 ? r0 : 0u), b1 = pages.block(ok1 ? r1 : 0u);
+      const uint32_t ok0 = s_below(r0, pages.count), ok1 = s_below(r1, pages.count);
+      const gbytes b0 = pages.block(r0 & (0u - ok0)), b1 = pages.block(r1 & (0u - ok1));
 #pragma unroll
       for (int c = 0; c < G::kChunks; ++c)
         if (c % W == wave) copy(c, base, b0, b1, voff);
-      if (!(ok0 && ok1)) errs |= KVQ_DEVERR_ID;
-      return (ok0 ? 1u : 0u) | (ok1 ? 2u : 0u);
+      errs |= (ok0 & ok1) ^ 1u;  // KVQ_DEVERR_ID (1) unless both halves are valid
+      return ok0 | (ok1 << 1);
     }
     const uint32_t zero[3] = {0u, 0u, 0u};
 #pragma unroll
