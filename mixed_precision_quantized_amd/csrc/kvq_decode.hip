@@ -445,7 +445,7 @@ struct SplitRun {
   static constexpr bool kVS = QT == 2;
   f4 acc[kVS ? 1 : QT][8];  // P V accumulators
   float m_run[QT], l_run[QT];  // running maximum of the raw logits, sum of the weights
-  float mq[QT];        // m_run qscale (the base-2 maximum the weights are taken against)
+  float nmq[QT];       // -m_run qscale (minus the base-2 maximum the weights are taken against)
   int qbase = 0;       // first query head (of the g) this wave computes
   float zacc[QT];      // row lr: sum of p z over this lane's tokens (V zero term)
   f4 aone[QT];         // rows 4 lb + e: sums of the fp16 operand weights p s (V code offset),
@@ -490,7 +490,7 @@ struct SplitRun {
         qoff[qt][r] = -__shfl(po, 16 * lb + 4 * r);
       }
       m_run[qt] = kNegBig;
-      mq[qt] = kNegBig;
+      nmq[qt] = -kNegBig;
       l_run[qt] = 0.0f;
       zacc[qt] = 0.0f;
       aone[qt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -692,8 +692,8 @@ struct SplitRun {
     // Online softmax per query (the 16 lanes of row lb) on the raw logits: the base-2
     // logit is x qscale.  The row maximum is taken only when a logit of the wave exceeds
     // its row's running maximum m_run (rare after the first windows); the weights are
-    // exp2(x qscale - mq) with mq = m_run qscale, one rounding (fma), so at most 1 up
-    // to that rounding.
+    // exp2(x qscale - m_run qscale), one rounding (fma), so at most 1 up to that
+    // rounding.
     float alpha_q[QT];  // (kVS) this window's rescale of query 4 qt + lb
     bool rescaled = false;
 #pragma unroll
@@ -705,7 +705,7 @@ struct SplitRun {
         const float mqn = mn * qscale[qt];
         // rows whose maximum stays keep alpha 1 (no -inf - -inf); the first rise from
         // the start values gives 0, which meets an empty state
-        const float alpha = mn > m_run[qt] ? __builtin_amdgcn_exp2f(mq[qt] - mqn) : 1.0f;
+        const float alpha = mn > m_run[qt] ? __builtin_amdgcn_exp2f(-mqn - nmq[qt]) : 1.0f;
         l_run[qt] *= alpha;
         if (kVS) {
           alpha_q[qt] = alpha;
@@ -718,13 +718,13 @@ struct SplitRun {
             zacc[qt] *= __shfl(alpha, 16 * (lr >> 2));  // row lr belongs to query lr / 4
           }
         }
-        mq[qt] = mn > m_run[qt] ? mqn : mq[qt];
+        nmq[qt] = mn > m_run[qt] ? -mqn : nmq[qt];
         m_run[qt] = mn;
       }
       // v_exp_f32: exp2(-inf) = 0; results below 2^-126 may flush to zero, which no
       // softmax weight of consequence is.
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[qt][0], qscale[qt], -mq[qt]));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[qt][1], qscale[qt], -mq[qt]));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[qt][0], qscale[qt], nmq[qt]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[qt][1], qscale[qt], nmq[qt]));
       l_run[qt] += p0 + p1;
       L.p[kVS ? 0 : qt][kVS ? 4 * qt + lb : lb][lr] = (_Float16)p0;
       L.p[kVS ? 0 : qt][kVS ? 4 * qt + lb : lb][16 + lr] = (_Float16)p1;
@@ -830,7 +830,7 @@ struct SplitRun {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float l0 = __shfl(lt[0], 16 * r), l1 = __shfl(lt[QT - 1], 16 * r);
-        const float m0 = __shfl(mq[0], 16 * r), m1 = __shfl(mq[QT - 1], 16 * r);
+        const float m0 = -__shfl(nmq[0], 16 * r), m1 = -__shfl(nmq[QT - 1], 16 * r);
         const float l_tot = lb == 0 ? l0 : l1, m = lb == 0 ? m0 : m1;
         const int j = qbase + 4 * lb + r;
         const bool any = l_tot > 0.0f;
@@ -868,7 +868,7 @@ struct SplitRun {
         float4 *dst = reinterpret_cast<float4 *>(a.part_o + ((int64_t)s_idx * a.g + j) * kHeadDim + 8 * lr);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-        if (lr == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (mq[qt] + log2f(l_tot)) * kLn2 : -INFINITY;
+        if (lr == 0) a.part_lse[(int64_t)s_idx * a.g + j] = any ? (log2f(l_tot) - nmq[qt]) * kLn2 : -INFINITY;
       }
     }
   }
