@@ -960,7 +960,8 @@ __device__ __forceinline__ void dma_block(uint32_t lds, gbytes base, uint32_t vo
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
 }
 
-// The same with the default cache policy (query rows, read by every split of a head).
+// The same with the default cache policy (query rows, read by every split of a head, and
+// anchor rows, whose lines several copies share).
 __device__ __forceinline__ void dma_block_keep(uint32_t lds, gbytes base, uint32_t voff) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"((uint64_t)base), "{m0}"(lds) : "memory");
 }
@@ -1115,22 +1116,25 @@ struct RingLoader {
         default: dma_block_half<true>(base + 4096, b1, vo[2]); break;
       }
     } else if (CLS == KVQ_FP16) {
+      // (anchor copies keep the default cache policy: a K row's 128-byte lines are read by
+      // four of these copies, 16 B of every 64 at a time, and non-temporal reads fetched
+      // them again for each: 119 against 88 us per hybrid-anchor layer)
       // chunk c: region c / 4 (K of page half 0, K of half 1, V of half 0, V of half 1),
       // part c % 4 (K: channels 8 (c % 4) + 32 lb .. + 7 of every token; V: tokens
       // 4 (c % 4) .. + 3)
       const int r = c >> 2, m = c & 3;
       const gbytes b = (r & 1) ? b1 : b0;
-      dma_block(base + 1024 * c, r < 2 ? b + 16 * m : b + 1024 * m, r < 2 ? vo[0] : vo[1]);
+      dma_block_keep(base + 1024 * c, r < 2 ? b + 16 * m : b + 1024 * m, r < 2 ? vo[0] : vo[1]);
     } else if (CLS == kAnchorF8) {
       // chunks 0-3: K codes of half c / 2, part c % 2 (channels 32 lb + 16 (c % 2) .. + 15
       // of every token); 4-7: V codes of half (c - 4) / 2, tokens 8 ((c - 4) % 2) .. + 7;
       // 8, 9: the scales of half c - 8 (lanes 0-3)
       if (c < 4) {
-        dma_block(base + 1024 * c, ((c >> 1) ? b1 : b0) + 16 * (c & 1), vo[0]);
+        dma_block_keep(base + 1024 * c, ((c >> 1) ? b1 : b0) + 16 * (c & 1), vo[0]);
       } else if (c < 8) {
-        dma_block(base + 4096 + 1024 * (c - 4), (((c - 4) >> 1) ? b1 : b0) + 1024 * (c & 1), vo[1]);
+        dma_block_keep(base + 4096 + 1024 * (c - 4), (((c - 4) >> 1) ? b1 : b0) + 1024 * (c & 1), vo[1]);
       } else if (lane < 4) {
-        dma_block(base + 8192 + 64 * (c - 8), c == 8 ? b0 : b1, vo[2]);
+        dma_block_keep(base + 8192 + 64 * (c - 8), c == 8 ? b0 : b1, vo[2]);
       }
     } else {
       switch (c) {
