@@ -20,9 +20,9 @@
 //   softmax scale is applied to the fp32 result.  INT4 K codes enter as exact
 //   offset-coded fp16 values (2^e + c, see below) and the offset's share of the dot
 //   product is removed per group together with the zero term z * sum(q).  INT2 K has
-//   per-channel scales: the code operand becomes s * (c - 2), exact in fp16 because
-//   c - 2 is in {-2, -1, 0, 1}, and the zero term sum q (z + 2 s) of the 32-token pair
-//   is added to the logits.
+//   per-channel scales of at most 9 significant bits: the code operand becomes
+//   2^-9 c s, exact in fp16 (one fma per pair of values, see k2_field), and the zero
+//   term sum q z of the 32-token pair is added to the logits.
 //   Online softmax in base 2 per query with 16-lane DPP row reductions; the running
 //   state is rescaled only when a row maximum grows.
 //   P V on MFMA.  Rows (query j', group i); the weight operand is p * s (fp16) for
@@ -228,7 +228,7 @@ struct Lds {
 struct Win {
   uint4 k[2][4];     // K codes: [page half][up to 64 B]
   uint4 km[2];       // INT4 K meta of token lr (per page half)
-  uint4 ks, kz;      // INT2 per-channel scales / zeros of channels 8 lr .. 8 lr + 7
+  uint4 kz;          // INT2 per-channel zeros of channels 8 lr .. 8 lr + 7
   uint4 kg[4];       // INT2 per-channel scales of channels 32 lb .. 32 lb + 31
   uint4 v[8];        // V words / FP16 rows of this lane's 8 tokens
   uint4 vm[2];       // V meta (scale, zero) of this lane's 8 tokens, group lr & 3
@@ -319,7 +319,6 @@ struct Loader {
       }
       if (CLS == KVQ_INT2) {  // per-channel meta of the pair: even page ch 0-63, odd 64-127
         const gbytes mb = (lr >> 3) ? blk1 : blk0;
-        w.ks = ld4(mb + kI2KS + (lr & 7) * 16);
         w.kz = ld4(mb + kI2KZ + (lr & 7) * 16);
         const gbytes g = ((lb >> 1) ? blk1 : blk0) + kI2KS + (lb & 1) * 64;
 #pragma unroll
@@ -414,13 +413,19 @@ __device__ __forceinline__ h8 cvt_k4(uint32_t x, const Consts &k) {
   return h8_of((x & k.m000F) | 0x64006400u, (x & k.m00F0) | 0x54005400u, (y & k.m000F) | 0x64006400u,
                (y & k.m00F0) | 0x54005400u);
 }
-// INT2 byte pair (bits 0-7 and 16-23) -> c - 2 of its 8 codes, exact.
-__device__ __forceinline__ h8 cvt_k2(uint32_t x, const Consts &k) {
-  return h8_of(as_u32(as_h2((x & k.m0003) | 0x64006400u) - h2{(_Float16)1026.0f, (_Float16)1026.0f}),
-               as_u32(as_h2((x & k.m000C) | 0x5C005C00u) - h2{(_Float16)258.0f, (_Float16)258.0f}),
-               as_u32(as_h2((x & k.m0030) | 0x54005400u) - h2{(_Float16)66.0f, (_Float16)66.0f}),
-               as_u32(as_h2((x & k.m00C0) | 0x4C004C00u) - h2{(_Float16)18.0f, (_Float16)18.0f}));
+// INT2 byte pair (bits 0-7 and 16-23) -> its 8 codes c as off + 2^-9 c: each 2-bit
+// field OR-ed into the mantissa of off = 2, 1/2, 1/8, 1/32 (bits 0-1, 2-3, 4-5, 6-7),
+// whose last place is 2^-9 where the field lands.  The K operand is then
+// fma(off + 2^-9 c, s, -off s) = 2^-9 c s, exact: -off s is s times a power of two, and
+// an INT2 key scale has at most 9 significant bits (the write path rounds it so), so
+// c s is an fp16 value for c = 0..3; both are finite while 2 s is.  (For scales below
+// 2^-7 the operand lies on fp16's subnormal grid and may round, by at most 2^-24 in all,
+// 2^-15 of a key value.)
+__device__ __forceinline__ h8 k2_field(uint32_t x, const Consts &k) {
+  return h8_of((x & k.m0003) | 0x40004000u, (x & k.m000C) | 0x38003800u, (x & k.m0030) | 0x30003000u,
+               (x & k.m00C0) | 0x28002800u);
 }
+constexpr float kI2Unit = 0x1p-9f;  // unit of the INT2 K operand (above)
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so no exp2 ever sees -inf - -inf
 
@@ -458,7 +463,8 @@ struct SplitRun {
       : a(a_), sp(sp_), L(L_), lane(lane_id()), lr(lane_id() & 15), lb(lane_id() >> 4) {
     scale = kLog2e / sqrtf((float)kHeadDim);
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) qscale[qt] = scale * L.qs[4 * qt + lb];
+    for (int qt = 0; qt < QT; ++qt)  // (INT2 logits come in the K operand's unit 2^-9)
+      qscale[qt] = scale * L.qs[4 * qt + lb] * (CLS == KVQ_INT2 ? 1.0f / kI2Unit : 1.0f);
     {
       const uint32_t one = in_vgpr(0x3C003C00u);
       ones = h8_of(one, one, one, one);
@@ -535,22 +541,24 @@ struct SplitRun {
       for (int q = 0; q < 8; ++q) mv[q] = (vlive >> q & 1) ? mv[q] : 0u;
     }
 
-    // INT2: zero term of the pair, q . (z + 2 s) summed over the 128 channels (the 16
-    // lanes of row lb hold 8 channels each); added to the logits of query 4 qt + lb.
+    // INT2: zero term of the pair, q . z summed over the 128 channels (the 16 lanes of
+    // row lb hold 8 channels each), in the K operand's unit 2^-9; added to the logits of
+    // query 4 qt + lb.  And -off s for the 8 values of each K operand register (k2_field).
     float c2[QT];
+    h8 nofs[4];
     if (CLS == KVQ_INT2) {
-      const uint32_t ks[4] = {w.ks.x, w.ks.y, w.ks.z, w.ks.w};
       const uint32_t kz[4] = {w.kz.x, w.kz.y, w.kz.z, w.kz.w};
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        float bz = 0.0f, bs = 0.0f;
+        float bz = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          bz = dot2(qn[qt][u], as_h2(kz[u]), bz);
-          bs = dot2(qn[qt][u], as_h2(ks[u]), bs);
-        }
-        c2[qt] = row_sum16(fmaf(2.0f, bs, bz));
+        for (int u = 0; u < 4; ++u) bz = dot2(qn[qt][u], as_h2(kz[u]), bz);
+        c2[qt] = row_sum16(bz) * kI2Unit;
       }
+      const h8 noff = {(_Float16)-2.0f, (_Float16)-2.0f, (_Float16)-0.5f, (_Float16)-0.5f,
+                       (_Float16)-0.125f, (_Float16)-0.125f, (_Float16)-0.03125f, (_Float16)-0.03125f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) nofs[m] = h8_of(w.kg[m]) * noff;
     }
 
     // QK^T: logit (base 2) of query 4 qt + lb and token T + 16 h + lr.
@@ -566,10 +574,10 @@ struct SplitRun {
         kb[3] = cvt_k4(v.w, k);
       } else if (CLS == KVQ_INT2) {
         const uint4 v = w.k[h][0];
-        kb[0] = cvt_k2(v.x, k) * h8_of(w.kg[0]);  // s (c - 2): exact in fp16
-        kb[1] = cvt_k2(v.x >> 8, k) * h8_of(w.kg[1]);
-        kb[2] = cvt_k2(v.y, k) * h8_of(w.kg[2]);
-        kb[3] = cvt_k2(v.y >> 8, k) * h8_of(w.kg[3]);
+        kb[0] = __builtin_elementwise_fma(k2_field(v.x, k), h8_of(w.kg[0]), nofs[0]);  // 2^-9 c s
+        kb[1] = __builtin_elementwise_fma(k2_field(v.x >> 8, k), h8_of(w.kg[1]), nofs[1]);
+        kb[2] = __builtin_elementwise_fma(k2_field(v.y, k), h8_of(w.kg[2]), nofs[2]);
+        kb[3] = __builtin_elementwise_fma(k2_field(v.y >> 8, k), h8_of(w.kg[3]), nofs[3]);
       } else if (a.fp8) {
         const float sk = __uint_as_float(w.k[h][2].x);
 #pragma unroll
@@ -1246,9 +1254,7 @@ struct RingLoader {
         const uint2 x = *reinterpret_cast<const uint2 *>(S + 1024 * h + kI2KC + 32 * lr + 8 * lb);
         w.k[h][0] = make_uint4(x.x, x.y, 0, 0);
       }
-      const uint8_t *KS = S + 1024 * (lr >> 3) + kI2KS + 16 * (lr & 7);  // scales; zeros 128 B on
-      w.ks = *reinterpret_cast<const uint4 *>(KS);
-      w.kz = *reinterpret_cast<const uint4 *>(KS + (kI2KZ - kI2KS));
+      w.kz = *reinterpret_cast<const uint4 *>(S + 1024 * (lr >> 3) + kI2KZ + 16 * (lr & 7));  // zeros
       const uint8_t *KG = S + 1024 * (lb >> 1) + kI2KS + 64 * (lb & 1);
 #pragma unroll
       for (int m = 0; m < 4; ++m) w.kg[m] = *reinterpret_cast<const uint4 *>(KG + 16 * m);

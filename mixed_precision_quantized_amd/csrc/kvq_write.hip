@@ -147,6 +147,17 @@ __device__ __forceinline__ Quant quant_params(float mn, float mx, float levels) 
   return q;
 }
 
+// INT2 key groups (one channel over 32 tokens): the scale is rounded up further, to the
+// next fp16 value whose two lowest mantissa bits are zero (at most 9 significant bits;
+// a carry into the exponent field is correct), so that c s is an fp16 value for every
+// code c = 0..3 and the decode can form its key operand with one fused multiply-add.
+__device__ __forceinline__ Quant quant_params_k2(float mn, float mx) {
+  Quant q = quant_params(mn, mx, 3.0f);
+  q.sb = (q.sb + 3u) & ~3u;
+  q.s = half_bits_to_float(q.sb);
+  return q;
+}
+
 __device__ __forceinline__ uint32_t quant_code(float x, const Quant &q, float levels) {
   if (q.s == 0.0f) return 0;
   const float t = __fdiv_rn(__fsub_rn(x, q.z), q.s);
@@ -334,7 +345,7 @@ __global__ void __launch_bounds__(64) append_int2_kernel(
     if (lane == 0) report(err, KVQ_DEVERR_ID);
     return;
   }
-  const Quant q0 = quant_params(mn0, mx0, 3.0f), q1 = quant_params(mn1, mx1, 3.0f);
+  const Quant q0 = quant_params_k2(mn0, mx0), q1 = quant_params_k2(mn1, mx1);
 #pragma unroll
   for (int t = 0; t < kGroup; ++t)
     put_code_pair<2>(blk[t >> 4] + kI2KC + (t & 15) * 32, quant_code(kx[t][0], q0, 3.0f),

@@ -73,6 +73,16 @@ uint16_t orc_f16_up(float x)
     return f16_encode(ceil(d / q) * q);
 }
 
+/* INT2 key scales: the smallest fp16 value >= x whose two lowest mantissa bits are
+ * zero (a multiple of four units in the last place at x's fp16 exponent). */
+uint16_t orc_f16_up4(float x)
+{
+    double d = (double)x;
+    if (d == 0.0) return 0;
+    double q = 4.0 * f16_quantum(d);
+    return f16_encode(ceil(d / q) * q);
+}
+
 uint16_t orc_f16_nearest(float x)
 {
     double d = (double)x;
@@ -85,8 +95,8 @@ uint16_t orc_f16_nearest(float x)
 /* Quantizer (TriAxialKV key design 3: asymmetric groups, scale and zero)   */
 /* ------------------------------------------------------------------------ */
 
-void orc_quantize(const float *x, int32_t n, int64_t stride, int32_t bits,
-                  uint8_t *codes, uint16_t *scale, uint16_t *zero)
+static void quantize_with(const float *x, int32_t n, int64_t stride, int32_t bits,
+                          uint16_t (*scale_up)(float), uint8_t *codes, uint16_t *scale, uint16_t *zero)
 {
     const int levels = (1 << bits) - 1;
     float mn = 0.0f, mx = 0.0f;
@@ -100,7 +110,7 @@ void orc_quantize(const float *x, int32_t n, int64_t stride, int32_t bits,
     float z = (float)orc_f16_value(zb);
     float range = mx - z;                      /* fp32 subtract */
     float step = range / (float)levels;        /* fp32 correctly rounded divide */
-    uint16_t sb = orc_f16_up(step);
+    uint16_t sb = scale_up(step);
     float s = (float)orc_f16_value(sb);
     for (int32_t i = 0; i < n; ++i) {
         int code = 0;
@@ -115,6 +125,18 @@ void orc_quantize(const float *x, int32_t n, int64_t stride, int32_t bits,
     }
     *scale = sb;
     *zero = zb;
+}
+
+void orc_quantize(const float *x, int32_t n, int64_t stride, int32_t bits,
+                  uint8_t *codes, uint16_t *scale, uint16_t *zero)
+{
+    quantize_with(x, n, stride, bits, orc_f16_up, codes, scale, zero);
+}
+
+void orc_quantize_k2(const float *x, int32_t n, int64_t stride,
+                     uint8_t *codes, uint16_t *scale, uint16_t *zero)
+{
+    quantize_with(x, n, stride, 2, orc_f16_up4, codes, scale, zero);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -344,7 +366,7 @@ int orc_append(orc_cache *c, const void *k, const void *v, int32_t dtype,
                     col[t] = src_value(k, dtype, rows[t] * row_stride + h * head_stride + ch);
                 uint8_t codes[GRP];
                 uint16_t s, z;
-                orc_quantize(col, GRP, 1, 2, codes, &s, &z);
+                orc_quantize_k2(col, GRP, 1, codes, &s, &z);
                 for (int t = 0; t < GRP; ++t)
                     put_code(blk[t / PAGE] + I2_KC + (t % PAGE) * 32, ch, 2, codes[t]);
                 put_u16(blk[ch / 64] + I2_KS + (ch % 64) * 2, s);

@@ -72,6 +72,8 @@ typedef struct {
 uint16_t orc_f16_down(float x);     /* largest fp16 <= x, never -0            */
 uint16_t orc_f16_up(float x);       /* smallest fp16 >= x, never -0           */
 uint16_t orc_f16_nearest(float x);  /* round to nearest, ties to even          */
+uint16_t orc_f16_up4(float x);      /* smallest fp16 >= x with its two lowest mantissa
+                                       bits zero (INT2 key scales), never -0   */
 double   orc_f16_value(uint16_t h);
 
 /* --- FP8 (OCP e4m3: 4 exponent bits, bias 7, 3 mantissa bits, max 448) --- */
@@ -91,6 +93,11 @@ int64_t orc_block_bytes(int32_t cls);
  *   gives all-zero codes.  Dequantization is z + code * s. */
 void orc_quantize(const float *x, int32_t n, int64_t stride, int32_t bits,
                   uint8_t *codes, uint16_t *scale, uint16_t *zero);
+/* The same with bits = 2 and s = orc_f16_up4(fl32(fl32(max - z) / 3)): the INT2 key
+ * groups (one channel over 32 tokens).  s has at most 9 significant bits, so every
+ * c s (c = 0..3) is an fp16 value. */
+void orc_quantize_k2(const float *x, int32_t n, int64_t stride,
+                     uint8_t *codes, uint16_t *scale, uint16_t *zero);
 
 /* --- routing (TriAxialKV key design 3) -------------------------------------
  * flags: 0 = wants INT2, 1 = INT4, 2 = FP16 anchor.  INT2-flagged tokens, in

@@ -62,6 +62,8 @@ def _declare(L):
     L.orc_f16_down.restype = ctypes.c_uint16
     L.orc_f16_up.argtypes = [ctypes.c_float]
     L.orc_f16_up.restype = ctypes.c_uint16
+    L.orc_f16_up4.argtypes = [ctypes.c_float]
+    L.orc_f16_up4.restype = ctypes.c_uint16
     L.orc_f16_nearest.argtypes = [ctypes.c_float]
     L.orc_f16_nearest.restype = ctypes.c_uint16
     L.orc_f16_value.argtypes = [ctypes.c_uint16]
@@ -76,6 +78,8 @@ def _declare(L):
     L.orc_fp8_row.restype = None
     L.orc_quantize.argtypes = [P, i32, i64, i32, P, P, P]
     L.orc_quantize.restype = None
+    L.orc_quantize_k2.argtypes = [P, i32, i64, P, P, P]
+    L.orc_quantize_k2.restype = None
     L.orc_route.argtypes = [P, i32, P, P, P, P]
     L.orc_append.argtypes = [P, P, P, i32, i64, i64, i32, P, P, i32, P, P, i32, P, P]
     L.orc_reorder.argtypes = [P, P, i32, i32, P, P]
@@ -140,6 +144,21 @@ def f16_nearest(x: float) -> int:
 
 def f16_value(bits: int) -> float:
     return float(lib().orc_f16_value(int(bits)))
+
+
+def f16_up4(x: float) -> int:
+    return int(lib().orc_f16_up4(float(x)))
+
+
+def quantize_k2(x):
+    """Quantize one INT2 key group (one channel over 32 tokens); returns (codes, scale
+    bits, zero bits)."""
+    x = _c_array(x, np.float32)
+    codes = np.zeros(x.shape[0], np.uint8)
+    s = ctypes.c_uint16()
+    z = ctypes.c_uint16()
+    lib().orc_quantize_k2(_ptr(x), x.shape[0], 1, _ptr(codes), ctypes.byref(s), ctypes.byref(z))
+    return codes, int(s.value), int(z.value)
 
 
 def quantize(x, bits: int):

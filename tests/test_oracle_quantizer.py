@@ -148,3 +148,67 @@ def test_quantizer_golden_examples(orc):
         codes, sb, zb = orc.quantize(x, bits)
         assert (sb, zb) == (s, z), name
         assert np.array_equal(codes, c), name
+
+
+# ---------------------------------------------------------------- INT2 key scales ----
+# INT2 key groups (one channel over 32 tokens) round their scale up once more, to the
+# next fp16 value whose two lowest mantissa bits are zero (at most 9 significant bits),
+# so that c s (c = 0..3) is an fp16 value and the decode forms its key operand exactly
+# with one fused multiply-add.
+
+def _candidates4():
+    """Every finite fp16 value whose two lowest mantissa bits are zero, ascending
+    (numpy's float16 decoding of the bit patterns)."""
+    bits = np.arange(0, 0x10000, 4, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    vals = vals[np.isfinite(vals)]
+    return np.unique(vals)
+
+
+def test_f16_up4_is_the_next_value_with_two_zero_low_bits(orc):
+    cand = _candidates4()
+    for x in _sample_floats(4000, 5):
+        if x > cand[-1]:  # (above 65408 the next such value is past fp16's range)
+            continue
+        want = cand[np.searchsorted(cand, float(x), side="left")]
+        got = orc.f16_value(orc.f16_up4(x))
+        assert got == want, (x, got, want)
+        assert orc.f16_up4(x) & 3 == 0 and orc.f16_up4(x) != 0x8000
+
+
+def test_quantize_k2_is_the_quantizer_with_the_coarser_scale(orc):
+    """Same zero as the plain quantizer; scale = the next value with two zero low bits at
+    or above the plain scale; codes nearest on that grid; |x - x_hat| <= s/2."""
+    cand = _candidates4()
+    for x in _groups(31):
+        codes, sb, zb = orc.quantize_k2(x)
+        _, sb0, zb0 = orc.quantize(x, 2)
+        assert zb == zb0
+        s0 = orc.f16_value(sb0)
+        s, z = orc.f16_value(sb), orc.f16_value(zb)
+        assert s == cand[np.searchsorted(cand, s0, side="left")], (s, s0)
+        assert sb & 3 == 0 and s0 <= s <= s0 * (1 + 2.0 ** -8) + 2.0 ** -22
+        xd = x.astype(np.float64)
+        if s == 0:
+            assert not codes.any()
+            continue
+        assert codes.max() <= 3
+        eps = 2.0 ** -18 * (np.abs(xd - z) + s)
+        assert np.all(np.abs(xd - (z + codes * s)) <= s / 2 + eps)
+        levels = z + np.arange(4) * s
+        dist = np.abs(xd[:, None] - levels[None, :])
+        assert np.all(dist[np.arange(32), codes] <= dist.min(axis=1) + eps)
+
+
+def test_int2_key_operand_is_exact_for_every_such_scale():
+    """For every fp16 scale with two zero low mantissa bits in [2^-7, 32752): c s 2^-9
+    (c = 0..3) and s times 2, 1/2, 1/8, 1/32 are fp16 values (numpy float16 round trip),
+    which is what makes the decode's fma(off + 2^-9 c, s, -off s) exact."""
+    cand = _candidates4()
+    s = cand[(cand >= 2.0 ** -7) & (cand < 32752.0)]
+    for c in range(4):
+        v = c * s * 2.0 ** -9
+        assert np.array_equal(v.astype(np.float16).astype(np.float64), v), c
+    for off in (2.0, 0.5, 0.125, 0.03125):
+        v = off * s
+        assert np.array_equal(v.astype(np.float16).astype(np.float64), v), off
