@@ -208,7 +208,10 @@ kvq_status kvq_tag_flags(const uint8_t *tags, int32_t n, const uint8_t *bits, in
  *   FP16:  fp16_rows[i] [dev] -> slot fp16_slots[i] [dev]   (i < n_fp16)
  * Quantizer (bit-exact, IEEE fp32): z = largest fp16 <= min, s = smallest fp16
  * >= (max - z) / L, code = clamp(rint((x - z) / s), 0, L), L = 2^b - 1; s = 0
- * gives all-zero codes.  FP16 anchors are rounded to nearest even.  Destinations
+ * gives all-zero codes.  INT2 key groups (one channel over 32 tokens) round s up
+ * once more, to the next fp16 value whose two lowest mantissa bits are zero (at
+ * most 9 significant bits, so every code times s is an fp16 value).  FP16
+ * anchors are rounded to nearest even.  Destinations
  * of one call must be distinct.
  * Errors: INVALID_ARG (bad cache, NULL arrays with nonzero counts, bad dtype,
  * negative counts or strides), UNSUPPORTED (head_dim != 128, page_size != 16),
