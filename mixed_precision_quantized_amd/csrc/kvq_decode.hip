@@ -517,33 +517,37 @@ struct SplitRun {
   __device__ __forceinline__ void window(const Win &w, int32_t T, F &&mid) {
     const bool partial = (T < sp.tok_begin) || (T + 32 > sp.tok_end) || w.ok != 3u;  // (slot maps: ok = 0)
     // live bit h: QK token T + 16 h + lr counts; vlive bit q: P V token T + 8 lb + q counts.
-    uint32_t live = 3u, vlive = 0xFFu;
-    if (SLOTS) {
-      live = w.live;
-      vlive = w.vlive;
-    } else if (partial) {
-      live = 0u;
+    // Formed inside each branch of a partial window that needs them, so that a full
+    // window carries no masks.
+    auto live_bits = [&]() -> uint32_t {
+      if (SLOTS) return w.live;
+      uint32_t l = 0u;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int32_t t = T + 16 * h + lr;
-        if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> h & 1)) live |= 1u << h;
+        if (t >= sp.tok_begin && t < sp.tok_end && (w.ok >> h & 1)) l |= 1u << h;
       }
+      return l;
+    };
+    auto vlive_bits = [&]() -> uint32_t {
+      if (SLOTS) return w.vlive;
       const int32_t t0 = T + 8 * lb;
       const int32_t lo = min(max(sp.tok_begin - t0, 0), 8), hi = min(max(sp.tok_end - t0, 0), 8);
-      vlive = (w.ok >> (lb >> 1) & 1) ? (0xFFu >> (8 - hi)) & (0xFFu << lo) & 0xFFu : 0u;
-    }
+      return (w.ok >> (lb >> 1) & 1) ? (0xFFu >> (8 - hi)) & (0xFFu << lo) & 0xFFu : 0u;
+    };
     // V metadata (scale, zero) of this lane's 8 P V tokens; a token that does not count
     // may sit in an unwritten slot, so its pair is cleared (its weight is 0, and 0 times
     // a non-finite scale would not be).
     uint32_t mv[8] = {w.vm[0].x, w.vm[0].y, w.vm[0].z, w.vm[0].w, w.vm[1].x, w.vm[1].y, w.vm[1].z, w.vm[1].w};
     if (CLS != KVQ_FP16 && partial) {
+      const uint32_t vlive = vlive_bits();
 #pragma unroll
       for (int q = 0; q < 8; ++q) mv[q] = (vlive >> q & 1) ? mv[q] : 0u;
     }
 
     // INT2: zero term of the pair, q . z summed over the 128 channels (the 16 lanes of
-    // row lb hold 8 channels each), in the K operand's unit 2^-9; added to the logits of
-    // query 4 qt + lb.  And -off s for the 8 values of each K operand register (k2_field).
+    // row lb hold 8 channels each); added to the logits of query 4 qt + lb in the K
+    // operand's unit 2^-9.  And -off s for the 8 values of each K operand register (k2_field).
     float c2[QT];
     h8 nofs[4];
     if (CLS == KVQ_INT2) {
@@ -553,7 +557,7 @@ struct SplitRun {
         float bz = 0.0f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) bz = dot2(qn[qt][u], as_h2(kz[u]), bz);
-        c2[qt] = row_sum16(bz) * kI2Unit;
+        c2[qt] = row_sum16(bz);
       }
       const h8 noff = {(_Float16)-2.0f, (_Float16)-2.0f, (_Float16)-0.5f, (_Float16)-0.5f,
                        (_Float16)-0.125f, (_Float16)-0.125f, (_Float16)-0.03125f, (_Float16)-0.03125f};
@@ -603,7 +607,7 @@ struct SplitRun {
           for (int r = 0; r < 4; ++r)  // s (q . (offset + c) - q . offset) + z sum(q)
             s = fmaf(h2f(mm[r]), d[r], fmaf(h2f(mm[r] >> 16), qsum[qt][r], s));
         } else if (CLS == KVQ_INT2) {
-          s = ((d[0] + d[1]) + (d[2] + d[3])) + c2[qt];
+          s = fmaf(c2[qt], kI2Unit, (d[0] + d[1]) + (d[2] + d[3]));
         } else {
           s = (d[0] + d[1]) + (d[2] + d[3]);
         }
@@ -614,6 +618,7 @@ struct SplitRun {
       // (partial is wave-uniform and rare: the empty asm keeps this a branch instead of
       // selects that every window would execute)
       asm volatile("" ::: "memory");
+      const uint32_t live = live_bits();
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -668,6 +673,7 @@ struct SplitRun {
           }
         }
         if (partial) {  // absent or dead tokens: keep the operand finite
+          const uint32_t vlive = vlive_bits();
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const uint32_t mk = ((vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) |
