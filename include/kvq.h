@@ -86,8 +86,9 @@ enum {
  *     [scale, zero] @2304.
  *   INT2 (1536 B): K codes [16 tok][32 B] @0; K per-channel meta of the page
  *     pair @512: 64 fp16 scales then 64 fp16 zeros @640 (even page: channels
- *     0-63, odd page: 64-127); V codes [16 tok][32 B] @768; V meta [4 groups]
- *     [16 tok][scale, zero] @1280.  INT2 pages are used in aligned pairs (even,
+ *     0-63, odd page: 64-127); V codes [16 tok][32 B] @768; V meta @1280: per
+ *     group (4 x 64 B) the 16 tokens' fp16 scales, then their 16 fp16 zeros.
+ *     INT2 pages are used in aligned pairs (even,
  *     even+1) holding one 32-token group; n_pages[KVQ_INT2] must be even.
  *   FP16 (8192 B): K [16 tok][128] fp16 @0; V @4096.
  */

@@ -231,7 +231,8 @@ struct Win {
   uint4 kz;          // INT2 per-channel zeros of channels 8 lr .. 8 lr + 7
   uint4 kg[4];       // INT2 per-channel scales of channels 32 lb .. 32 lb + 31
   uint4 v[8];        // V words / FP16 rows of this lane's 8 tokens
-  uint4 vm[2];       // V meta (scale, zero) of this lane's 8 tokens, group lr & 3
+  uint4 vm[2];       // V meta of this lane's 8 tokens, group lr & 3: INT4 (scale, zero) pairs;
+                     // INT2 the 8 scales, then the 8 zeros
   uint32_t ok;       // bit h: page half h exists and has the right class
   uint32_t live;     // bit h: the QK token T + 16 h + lr is live
   uint32_t vlive;    // bit q: this lane's P V token q (0..7) is live
@@ -337,11 +338,14 @@ struct Loader {
         } else w.v[q] = ld4(vb + kF16V + (o0 + q) * 256 + lr * 16);
       }
       if (CLS == KVQ_FP16 && a.fp8) w.vm[0] = ld4(vb + kF8VS + 2 * o0);  // the 8 tokens' fp16 scales
-      if (CLS != KVQ_FP16) {
-        const int vm_at = CLS == KVQ_INT4 ? kI4VM : kI2VM;
-        const gbytes m = vb + vm_at + (vg * kPage + o0) * 4;
+      if (CLS == KVQ_INT4) {  // (scale, zero) pairs of the 8 tokens
+        const gbytes m = vb + kI4VM + (vg * kPage + o0) * 4;
         w.vm[0] = ld4(m);
         w.vm[1] = ld4(m + 16);
+      } else if (CLS == KVQ_INT2) {  // the 8 tokens' scales, then their zeros
+        const gbytes m = vb + kI2VM + 64 * vg + 2 * o0;
+        w.vm[0] = ld4(m);
+        w.vm[1] = ld4(m + 32);
       }
     } else {
 #pragma unroll
@@ -539,11 +543,29 @@ struct SplitRun {
     // may sit in an unwritten slot, so its pair is cleared (its weight is 0, and 0 times
     // a non-finite scale would not be).
     uint32_t mv[8] = {w.vm[0].x, w.vm[0].y, w.vm[0].z, w.vm[0].w, w.vm[1].x, w.vm[1].y, w.vm[1].z, w.vm[1].w};
-    if (CLS != KVQ_FP16 && partial) {
+    if (CLS == KVQ_INT4 && partial) {  // word q: token q's (scale, zero)
       const uint32_t vlive = vlive_bits();
 #pragma unroll
       for (int q = 0; q < 8; ++q) mv[q] = (vlive >> q & 1) ? mv[q] : 0u;
+    } else if (CLS == KVQ_INT2 && partial) {  // words u and 4 + u: tokens 2 u, 2 u + 1 in the halves
+      const uint32_t vlive = vlive_bits();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t mk = ((vlive >> (2 * u) & 1) ? 0x0000ffffu : 0u) | ((vlive >> (2 * u + 1) & 1) ? 0xffff0000u : 0u);
+        mv[u] &= mk;
+        mv[4 + u] &= mk;
+      }
     }
+    // The scales and the zeros of tokens 2 u, 2 u + 1 as fp16 pairs.
+    auto meta_pair = [&](int u, uint32_t &s2, uint32_t &z2) {
+      if (CLS == KVQ_INT2) {
+        s2 = mv[u];
+        z2 = mv[4 + u];
+      } else {
+        s2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x05040100u);
+        z2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x07060302u);
+      }
+    };
 
     // INT2: zero term of the pair, q . z summed over the 128 channels (the 16 lanes of
     // row lb hold 8 channels each); added to the logits of query 4 qt + lb in the K
@@ -688,8 +710,9 @@ struct SplitRun {
         // group (lr / 4) for each token; c = (offset + c) - offset exactly
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const h2 s2 = as_h2(__builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x05040100u));
-          const h2 z2 = as_h2(__builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x07060302u));
+          uint32_t s2w, z2w;
+          meta_pair(u, s2w, z2w);
+          const h2 s2 = as_h2(s2w), z2 = as_h2(z2w);
 #pragma unroll
           for (int nt = 0; nt < 8; ++nt) {
             const _Float16 o = (_Float16)v_offset(nt);
@@ -775,8 +798,8 @@ struct SplitRun {
         uint32_t aw[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t s2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x05040100u);  // scales
-          const uint32_t z2 = __builtin_amdgcn_perm(mv[2 * u + 1], mv[2 * u], 0x07060302u);  // zeros
+          uint32_t s2, z2;  // scales, zeros
+          meta_pair(u, s2, z2);
           const h2 pp = as_h2(p2[u]), ap2 = pp * as_h2(s2);
           aw[u] = as_u32(ap2);
           zacc[qt] = dot2(pp, as_h2(z2), zacc[qt]);
@@ -1268,9 +1291,9 @@ struct RingLoader {
       const uint8_t *V = at(lb >> 1, kI2VC + 32 * o0) + 4 * (lr >> 1);
 #pragma unroll
       for (int q = 0; q < 8; ++q) w.v[q].x = *reinterpret_cast<const uint32_t *>(V + 32 * q);
-      const uint8_t *VM = at(lb >> 1, kI2VM) + (vg * kPage + o0) * 4;
+      const uint8_t *VM = at(lb >> 1, kI2VM + 64 * vg + 2 * o0);  // 8 scales, the zeros 32 B on
       w.vm[0] = *reinterpret_cast<const uint4 *>(VM);
-      w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 16);
+      w.vm[1] = *reinterpret_cast<const uint4 *>(VM + 32);
     }
   }
 };

@@ -379,8 +379,11 @@ __global__ void __launch_bounds__(64) append_int2_kernel(
       kmx = li == t ? mx : kmx;
     }
     const Quant qv = quant_params(kmn, kmx, 3.0f);
-    // group-major [4][16][s, z]: entry (lane / 16) 16 + token = lane
-    *reinterpret_cast<uint32_t *>(blk[h] + kI2VM + lane * 4) = qv.sb | (qv.zb << 16);
+    // per group (64 B) the 16 tokens' scales, then their 16 zeros: lane 16 g + t holds
+    // group g, token t
+    uint8_t *vm = blk[h] + kI2VM + 64 * (lane >> 4) + 2 * li;
+    *reinterpret_cast<uint16_t *>(vm) = (uint16_t)qv.sb;
+    *reinterpret_cast<uint16_t *>(vm + 32) = (uint16_t)qv.zb;
 #pragma unroll
     for (int t = 0; t < kPage; ++t) {
       Quant q;

@@ -152,7 +152,8 @@ void orc_quantize_k2(const float *x, int32_t n, int64_t stride,
  * INT2 (1536 B): K codes [16 tok][32 B] at 0; K per-channel meta of the page
  *   pair at 512: 64 fp16 scales then 64 fp16 zeros (the even page of the pair
  *   holds channels 0-63, the odd page 64-127); V codes [16 tok][32 B] at 768;
- *   V meta [4 groups][16 tok][scale, zero] at 1280.
+ *   V meta at 1280: per group (4 x 64 B) the 16 tokens' fp16 scales, then their
+ *   16 fp16 zeros.
  * FP16 (8192 B): K [16 tok][128] fp16 at 0; V at 4096.
  * FP8 anchors (4160 B, the FP16 class of a cache with anchor_fp8): K codes
  *   [16 tok][128 B] at 0, K scales [16] fp16 at 2048, V codes [16][128 B] at
@@ -310,9 +311,12 @@ int orc_route(const uint8_t *flags, int32_t n, uint8_t *cls_out,
 /* Write path                                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Per-token groups of 32 channels (INT4 K and V, INT2 V); the metadata of
- * (group g, token off) sits at meta_at + 4 * (token_major ? off*4 + g : g*16 + off). */
-static void put_token_groups(uint8_t *blk, int codes_at, int meta_at, int token_major, int bits,
+/* Per-token groups of 32 channels (INT4 K and V, INT2 V); the (scale, zero) of
+ * (group g, token off) sits at meta_at + 4 * (off*4 + g) (META_TOKEN_MAJOR) or
+ * 4 * (g*16 + off) (META_GROUP_MAJOR); META_GROUP_RUNS puts the scale at
+ * meta_at + 64*g + 2*off and the zero 32 bytes after it. */
+enum { META_TOKEN_MAJOR, META_GROUP_MAJOR, META_GROUP_RUNS };
+static void put_token_groups(uint8_t *blk, int codes_at, int meta_at, int meta_kind, int bits,
                              int off, const float *row)
 {
     const int row_bytes = D * bits / 8;
@@ -322,9 +326,14 @@ static void put_token_groups(uint8_t *blk, int codes_at, int meta_at, int token_
         orc_quantize(row + g * GRP, GRP, 1, bits, codes, &s, &z);
         for (int i = 0; i < GRP; ++i)
             put_code(blk + codes_at + off * row_bytes, g * GRP + i, bits, codes[i]);
-        uint8_t *m = blk + meta_at + 4 * (token_major ? off * 4 + g : g * PAGE + off);
-        put_u16(m, s);
-        put_u16(m + 2, z);
+        if (meta_kind == META_GROUP_RUNS) {
+            put_u16(blk + meta_at + 64 * g + 2 * off, s);
+            put_u16(blk + meta_at + 64 * g + 32 + 2 * off, z);
+        } else {
+            uint8_t *m = blk + meta_at + 4 * (meta_kind == META_TOKEN_MAJOR ? off * 4 + g : g * PAGE + off);
+            put_u16(m, s);
+            put_u16(m + 2, z);
+        }
     }
 }
 
@@ -347,8 +356,8 @@ int orc_append(orc_cache *c, const void *k, const void *v, int32_t dtype,
             uint8_t *blk = block_ptr(c, page, h);
             load_row(kr, k, dtype, rows4[i], row_stride, head_stride, h);
             load_row(vr, v, dtype, rows4[i], row_stride, head_stride, h);
-            put_token_groups(blk, I4_KC, I4_KM, 1, 4, off, kr);
-            put_token_groups(blk, I4_VC, I4_VM, 0, 4, off, vr);
+            put_token_groups(blk, I4_KC, I4_KM, META_TOKEN_MAJOR, 4, off, kr);
+            put_token_groups(blk, I4_VC, I4_VM, META_GROUP_MAJOR, 4, off, vr);
         }
     }
 
@@ -375,7 +384,7 @@ int orc_append(orc_cache *c, const void *k, const void *v, int32_t dtype,
             /* V: per-token groups. */
             for (int t = 0; t < GRP; ++t) {
                 load_row(vr, v, dtype, rows[t], row_stride, head_stride, h);
-                put_token_groups(blk[t / PAGE], I2_VC, I2_VM, 0, 2, t % PAGE, vr);
+                put_token_groups(blk[t / PAGE], I2_VC, I2_VM, META_GROUP_RUNS, 2, t % PAGE, vr);
             }
         }
     }
@@ -715,10 +724,10 @@ int orc_token(const orc_cache *c, int32_t page, int32_t off, int32_t head,
         } else if (cls == ORC_INT2) {
             int32_t even = page & ~1;               /* INT2 ids start at 0 */
             const uint8_t *mblk = block_ptr(c, even + ch / 64, head);
-            const uint8_t *vm = blk + I2_VM + (g * PAGE + off) * 4;
+            const uint8_t *vs = blk + I2_VM + g * 64 + off * 2;   /* the zero 32 bytes on */
             k[ch] = deq(get_u16(mblk + I2_KS + (ch % 64) * 2), get_u16(mblk + I2_KZ + (ch % 64) * 2),
                         get_code(blk + I2_KC + off * 32, ch, 2));
-            v[ch] = deq(get_u16(vm), get_u16(vm + 2), get_code(blk + I2_VC + off * 32, ch, 2));
+            v[ch] = deq(get_u16(vs), get_u16(vs + 32), get_code(blk + I2_VC + off * 32, ch, 2));
         } else if (c->anchor_fp8) {
             k[ch] = orc_e4m3_value(blk[F8_K + off * 128 + ch]) * orc_f16_value(get_u16(blk + F8_KS + off * 2));
             v[ch] = orc_e4m3_value(blk[F8_V + off * 128 + ch]) * orc_f16_value(get_u16(blk + F8_VS + off * 2));

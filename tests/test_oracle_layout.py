@@ -79,10 +79,29 @@ def test_int2_layout_golden(orc):
         assert bytes(blk[off * 32:off * 32 + 32]) == g[f"int2 token_t%4={tt % 4} krow"]
         assert bytes(blk[768 + off * 32:768 + off * 32 + 32]) == g["int2 vrow"]
         for gi in range(4):
-            m = 1280 + (gi * 16 + off) * 4
-            assert bytes(blk[m:m + 4]) == g["int2 vmeta"]
+            m = 1280 + gi * 64 + off * 2
+            assert bytes(blk[m:m + 2]) == g["int2 vscale"] and bytes(blk[m + 32:m + 34]) == g["int2 vzero"]
     for page in (even, odd):
         assert bytes(page[512:640]) == g["int2 kscales"] and bytes(page[640:768]) == g["int2 kzeros"]
+
+
+def test_int2_v_meta_runs_golden(orc):
+    """INT2 V metadata: per group the 16 tokens' scales, then their 16 zeros."""
+    g = _golden()
+    c = orc.Cache(1, 4, 0, 0)
+    t = np.arange(32)[:, None]
+    ch = np.arange(128)[None, :]
+    k = np.zeros((32, 128), np.float32)
+    v = ((ch % 4) * (t + 1)).astype(np.float32)
+    c.append(k, v, orc.F32, 128, 128, rows2=np.arange(32), pages2=[0])
+    pool = c.pool_bytes(orc.INT2)
+    for page, key in ((pool[:1536], "int2 vscale run even"), (pool[1536:3072], "int2 vscale run odd")):
+        for gi in range(4):
+            m = 1280 + gi * 64
+            assert bytes(page[m:m + 32]) == g[key], (key, gi)
+            assert not page[m + 32:m + 64].any()
+        for off in range(16):
+            assert bytes(page[768 + off * 32:768 + off * 32 + 32]) == g["int2 vrow"]
 
 
 def test_fp16_layout_golden(orc):
